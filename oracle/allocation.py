@@ -1,0 +1,118 @@
+"""Decay-aware per-row bit allocation for one head.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__``).
+
+[LBRS] "State bit allocation", "Range normalization", "Approximate erasure rate",
+"Allocation units", "Levels and storage"; [LBRS-x] (the cost c = Gamma-hat * R~^2 and
+the rule "mean budget plus half log2 of cost over its geometric mean"):
+
+  R_i     row absolute maximum of the currently stored (dequantized) state;
+  R~_i    R_i / RMS_j R_j over the normalisation group (one head for KDA);
+  Gamma_i 1 / expm1(2 (s_i + r_i))   (rho_i = 1, C = 1);
+  c_i     Gamma_i * R~_i^2;
+  b*_i    bbar + 0.5 * log2(c_i / GM(c))  -- the real-valued minimiser of
+          sum_i c_i 2^{-2 b_i} at mean bbar (the displayed equation is missing from
+          the extracted page; the explainer states the rule in words);
+  b_i     round (ties to even), clip to [bmin, bmax], then adjust one bit at a time
+          until sum b_i = bbar * dk: while short, +1 to the row of largest marginal
+          gain (3/4) c_i 2^{-2 b_i} among b_i < bmax; while over, -1 to the row of
+          smallest marginal loss 3 c_i 2^{-2 b_i} among b_i > bmin; ties go to the
+          lower row index (the page says only "adjust widths to meet the budget").
+  fit     for each row, f_k = 1/4 + k/20 (k = 0..15); Delta_k = f16(f_k R_i / n_i);
+          squared error of rounding the row to {-n..n} Delta_k; the smallest error
+          wins, ties to the larger f ("fit f over 16 values in [1/4, 1] by squared
+          error per scale group").
+
+Guards (the pages are silent): every b_i = bbar when all R_i = 0; c_i is floored at
+1e-300 before logarithms; Delta_k = 0 stores level 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import f16, rne
+from .quantizers import fit_fraction, levels_n
+from .recurrence import erasure_rate_approx
+
+C_FLOOR = 1e-300
+
+
+def proxy_cost(c, b):
+    """Distortion proxy sum_i c_i 2^{-2 b_i}."""
+    return float(np.sum(np.asarray(c, np.float64) * 2.0 ** (-2.0 * np.asarray(b, np.float64))))
+
+
+def real_widths(c, bbar: float):
+    """b*_i = bbar + 0.5 log2(c_i / GM(c))."""
+    c = np.maximum(np.asarray(c, dtype=np.float64), C_FLOOR)
+    gm = np.exp(np.mean(np.log(c)))
+    return bbar + 0.5 * np.log2(c / gm)
+
+
+def integer_widths(c, bstar, bbar: int, bmin: int, bmax: int):
+    """Round, clip and greedily adjust to the budget sum b_i = bbar * len(c)."""
+    c = np.maximum(np.asarray(c, dtype=np.float64), C_FLOOR)
+    b = np.clip(rne(bstar), bmin, bmax).astype(np.int64)
+    target = bbar * len(c)
+    while b.sum() < target:
+        gain = np.where(b < bmax, 0.75 * c * 2.0 ** (-2.0 * b), -np.inf)
+        b[int(np.argmax(gain))] += 1
+    while b.sum() > target:
+        loss = np.where(b > bmin, 3.0 * c * 2.0 ** (-2.0 * b), np.inf)
+        b[int(np.argmin(loss))] -= 1
+    return b
+
+
+def row_costs(Y, s_rows, r_rows):
+    """(R, R~, Gamma-hat, c) of one head from its stored values Y [dk][dv]."""
+    Y = np.asarray(Y, dtype=np.float64)
+    R = np.max(np.abs(Y), axis=1)
+    rms = np.sqrt(np.mean(R ** 2))
+    Rt = R / rms if rms > 0 else np.zeros_like(R)
+    G = erasure_rate_approx(s_rows, r_rows)
+    return R, Rt, G, G * Rt ** 2
+
+
+def fit_row(x, R: float, b: int):
+    """Clipping-fit index k and the row's squared errors for all 16 candidates."""
+    x = np.asarray(x, dtype=np.float64)
+    n = levels_n(b)
+    errs = np.zeros(16)
+    for k in range(16):
+        d = float(f16(fit_fraction(k) * R / n))
+        if d == 0.0:
+            kap = np.zeros_like(x)
+        else:
+            kap = np.clip(rne(x / d), -n, n)
+        errs[k] = np.sum((x - d * kap) ** 2)
+    best = 15
+    for k in range(14, -1, -1):        # ties go to the larger f
+        if errs[k] < errs[best]:
+            best = k
+    return best, errs
+
+
+def allocate_head(Y, s_rows, r_rows, bbar=4, bmin=2, bmax=8):
+    """Widths, fit indices and diagnostics for one head's stored values Y."""
+    Y = np.asarray(Y, dtype=np.float64)
+    dk = Y.shape[0]
+    R, Rt, G, c = row_costs(Y, s_rows, r_rows)
+    if np.all(R == 0):
+        bstar = np.full(dk, float(bbar))
+        b = np.full(dk, bbar, dtype=np.int64)
+    else:
+        bstar = real_widths(c, bbar)
+        b = integer_widths(c, bstar, bbar, bmin, bmax)
+    fits = np.zeros(dk, dtype=np.int64)
+    errs = np.zeros((dk, 16))
+    for i in range(dk):
+        fits[i], errs[i] = fit_row(Y[i], R[i], int(b[i]))
+    return {"widths": b, "fit": fits, "bstar": bstar, "c": np.maximum(c, C_FLOOR),
+            "R": R, "Rt": Rt, "Gamma": G, "fit_err": errs}
+
+
+def default_r(dk: int) -> float:
+    """Closed form of r_i for the synthetic stream: beta ~ U(0,1) and unit keys of
+    isotropic direction give E[beta (2 - beta)] = 2/3 and E[k_i^2] = 1/dk, so
+    r_i = (1/2)(2/3)(1/dk) = 1/(3 dk)."""
+    return 1.0 / (3.0 * dk)

@@ -1,0 +1,136 @@
+"""Write-back rules and the grids they round onto.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__``).
+
+Write-back maps the computed state h_t to the stored q_t ([WB] "Post-training
+write-back interventions and diagnostics"; [WB-zh] "Core method" 核心方法 and
+"Method steps" 方法步骤详情):
+  * continuous propagation (identity): q_t = h_t;
+  * deterministic B-bit: nearest level of a grid of spacing Delta_B, half-step ties
+    to the even index, clipped at the grid rails ([WB-zh] "Reproduction assessment"
+    复现评估);
+  * stochastic rounding: one of the two adjacent levels, chosen with probability
+    given by the relative position, so unbiased in expectation ([WB-zh] "Error
+    feedback and stochastic rounding" 误差反馈与随机舍入);
+  * error feedback: q_t = Q_B(h_t + e_{t-1}) with the residual e_t clipped to
+    +-Delta_B (same section of [WB-zh]); e is an auxiliary write-back state.
+
+Every grid here is "offset + kappa * step" with integer kappa in [lo, hi]; a rule
+works on the grid coordinate tau = (x - offset) / step.
+  * uniform B-bit grid: offset 0, step Delta_B = 2^(1-B), kappa in
+    [-2^(B-1), 2^(B-1) - 1]; Delta_4 = 0.125 ([WB-zh] "Core method").
+  * per-block asymmetric affine INT8 ([DAMP] "Quantization & calibration details"):
+    offset = f16(min), step = f16((max - min) / 255), kappa in [0, 255].
+  * symmetric per-row levels {-n..n} Delta, n = 2^(b-1) - 1, Delta = f16(f R / n)
+    ([LBRS] "Levels and storage").
+Stochastic rounding compares a 16-bit uniform draw r with the fractional part:
+kappa = floor(tau) + [r < frac(tau) * 2^16]; the rounding boundary is floor(tau) +
+r / 2^16. A zero step (degenerate block or all-zero row) stores kappa = 0 and, with
+error feedback, a zero residual.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .numerics import f16, rne
+
+RTN, SR, EF = "rtn", "sr", "ef"
+
+
+@dataclass
+class Rounded:
+    kappa: np.ndarray      # integer level index (int64)
+    xhat: np.ndarray       # dequantized value offset + kappa * step (float64)
+    e_new: np.ndarray      # new error-feedback residual (zeros unless EF)
+    tau: np.ndarray        # pre-rounding grid coordinate
+    boundary: np.ndarray   # distance of tau to the rule's rounding boundary (grid units)
+
+
+def round_on_grid(x, step, offset, lo, hi, mode, e=None, r16=None) -> Rounded:
+    """Apply one write-back rule to values ``x`` on the grid offset + kappa * step.
+
+    ``step`` and ``offset`` broadcast against ``x``; ``e`` is the incoming
+    error-feedback residual (EF only); ``r16`` the 16-bit draws (SR only).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    step = np.broadcast_to(np.asarray(step, dtype=np.float64), x.shape)
+    offset = np.broadcast_to(np.asarray(offset, dtype=np.float64), x.shape)
+    target = x + (np.asarray(e, dtype=np.float64) if mode == EF else 0.0)
+    zero_step = step == 0.0
+    safe = np.where(zero_step, 1.0, step)
+    tau = (target - offset) / safe
+    if mode == SR:
+        r = np.asarray(r16, dtype=np.float64).reshape(x.shape)
+        fl = np.floor(tau)
+        frac = tau - fl
+        kappa = fl + (r < frac * 65536.0)
+        boundary = np.abs(frac - r / 65536.0)
+    else:
+        kappa = rne(tau)
+        boundary = np.abs(np.abs(tau - np.floor(tau) - 0.5))
+    kappa = np.clip(kappa, lo, hi)
+    kappa = np.where(zero_step, 0.0, kappa)
+    boundary = np.where(zero_step, np.inf, boundary)
+    xhat = offset + kappa * step
+    if mode == EF:
+        e_new = np.clip(target - xhat, -step, step)
+    else:
+        e_new = np.zeros_like(x)
+    return Rounded(kappa.astype(np.int64), xhat, e_new, tau, boundary)
+
+
+# ----- uniform B-bit grid ---------------------------------------------------
+
+def uniform_step(B: int) -> float:
+    return 2.0 ** (1 - B)
+
+
+def uniform_round(x, B: int, mode: str, e=None, r16=None) -> Rounded:
+    lo, hi = -(2 ** (B - 1)), 2 ** (B - 1) - 1
+    return round_on_grid(x, uniform_step(B), 0.0, lo, hi, mode, e, r16)
+
+
+def write_margin(h, q_prev, B: int):
+    """M = 2 |h - q_prev| / Delta_B ([WB] "Methods", Diagnostics; [WB-zh] the margin
+    M_{t,j} = 2|delta| / Delta_B of "Core method")."""
+    return 2.0 * np.abs(np.asarray(h, np.float64) - np.asarray(q_prev, np.float64)) / uniform_step(B)
+
+
+# ----- per-block asymmetric affine INT8 ---------------------------------------
+
+def affine_metadata(x_block):
+    """Returns (scale, zero, scale_pre, zero_pre): float16 values and their float64
+    pre-rounding values, for one block of values."""
+    x_block = np.asarray(x_block, dtype=np.float64)
+    mn = float(np.min(x_block))
+    mx = float(np.max(x_block))
+    scale_pre = max(mx - mn, 0.0) / 255.0
+    return float(f16(scale_pre)), float(f16(mn)), scale_pre, mn
+
+
+def affine_round(x, scale, zero, mode, e=None, r16=None) -> Rounded:
+    return round_on_grid(x, scale, zero, 0, 255, mode, e, r16)
+
+
+# ----- symmetric per-row levels (decay-aware allocation) ---------------------
+
+def fit_fraction(kfit: int) -> float:
+    """Clipping fraction f_k = 1/4 + k/20, k = 0..15: sixteen values on [1/4, 1]
+    ([LBRS] "Levels and storage")."""
+    return 0.25 + kfit / 20.0
+
+
+def levels_n(b: int) -> int:
+    return 2 ** (b - 1) - 1
+
+
+def row_step(R: float, b: int, kfit: int):
+    """Delta = f16(f R / n) and its float64 pre-rounding value."""
+    pre = fit_fraction(kfit) * R / levels_n(b)
+    return float(f16(pre)), pre
+
+
+def sym_round(x, step, n, mode, e=None, r16=None) -> Rounded:
+    return round_on_grid(x, step, 0.0, -n, n, mode, e, r16)

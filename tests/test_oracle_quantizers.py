@@ -1,0 +1,126 @@
+"""Pins of the write-back rules and grids."""
+import json
+import os
+
+import numpy as np
+
+from oracle.numerics import f16
+from oracle.quantizers import (affine_metadata, affine_round, fit_fraction, levels_n,
+                               row_step, sym_round, uniform_round, uniform_step,
+                               write_margin)
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_uniform_grid_constants():
+    with open(os.path.join(GOLD, "layout_accounting.json")) as f:
+        g = json.load(f)
+    assert uniform_step(4) == g["delta_4"]
+    assert uniform_step(4) / 2 == g["half_step_4"]
+    # rails: two's-complement 4-bit levels cover [-1, 1 - Delta]
+    r = uniform_round(np.array([1.0, 5.0, -1.0, -7.0, 0.875]), 4, "rtn")
+    assert list(r.kappa) == [7, 7, -8, -8, 7]
+    assert list(r.xhat) == [0.875, 0.875, -1.0, -1.0, 0.875]
+
+
+def test_uniform_ties_go_to_even_index():
+    d = uniform_step(4)
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, 3.5]) * d
+    assert list(uniform_round(x, 4, "rtn").kappa) == [0, 2, 2, 0, -2, 4]
+
+
+def test_dead_zone():
+    """Margin M = 2|h - q_prev| / Delta < 1 keeps an interior stored level; M > 1
+    moves it (When Quantization Breaks Memory, Methods / Diagnostics)."""
+    rng = np.random.default_rng(9)
+    B = 4
+    d = uniform_step(B)
+    kprev = rng.integers(-7, 7, 20000)                 # interior levels
+    qprev = kprev * d
+    h = qprev + rng.uniform(-1.5, 1.5, kprev.size) * d
+    M = write_margin(h, qprev, B)
+    k_new = uniform_round(h, B, "rtn").kappa
+    inside = M < 1
+    assert np.all(k_new[inside] == kprev[inside])
+    assert np.all(k_new[M > 1] != kprev[M > 1])
+
+
+def test_error_feedback_bounds_and_telescoping():
+    rng = np.random.default_rng(10)
+    B = 4
+    d = uniform_step(B)
+    e = np.zeros(50)
+    total = np.zeros(50)
+    for _ in range(300):
+        h = rng.uniform(-0.6, 0.6, 50)          # away from the rails: no clip fires
+        r = uniform_round(h, B, "ef", e=e)
+        assert np.all(np.abs(r.e_new) <= d)
+        total += h - r.xhat
+        e = r.e_new
+    assert np.allclose(total, e, atol=1e-12)      # sum (h_t - q_t) = e_T - e_0
+
+
+def test_error_feedback_clips_at_rails():
+    r = uniform_round(np.array([3.0]), 4, "ef", e=np.array([0.05]))
+    assert r.kappa[0] == 7 and r.e_new[0] == uniform_step(4)
+
+
+def test_stochastic_rounding_unbiased():
+    rng = np.random.default_rng(11)
+    x = rng.uniform(-0.8, 0.8, 64)
+    n = 4000
+    acc = np.zeros_like(x)
+    up = np.zeros_like(x)
+    for _ in range(n):
+        r16 = rng.integers(0, 65536, x.size)
+        rr = uniform_round(x, 4, "sr", r16=r16)
+        acc += rr.xhat
+        up += rr.kappa > np.floor(rr.tau)
+    d = uniform_step(4)
+    frac = x / d - np.floor(x / d)
+    # E[q] = x and P(up) = frac (binomial error bars, 5 sigma)
+    sig = np.sqrt(frac * (1 - frac) / n)
+    assert np.all(np.abs(up / n - frac) <= 5 * sig + 2 ** -16)
+    assert np.all(np.abs(acc / n - x) <= 5 * sig * d + d * 2 ** -16)
+
+
+def test_affine_block_metadata_and_idempotence():
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        blk = rng.standard_normal(32) * 10.0 ** rng.uniform(-3, 1)
+        scale, zero, spre, zpre = affine_metadata(blk)
+        assert scale == f16(spre) and zero == f16(zpre)
+        r = affine_round(blk, scale, zero, "rtn")
+        assert r.kappa.min() == 0 and r.kappa.max() == 255
+        assert np.all(np.abs(r.xhat - blk) <= scale / 2 * (1 + 1e-9) + abs(zero - zpre) + 1e-300)
+        s2, z2, _, _ = affine_metadata(r.xhat)
+        assert (s2, z2) == (scale, zero)
+        r2 = affine_round(r.xhat, s2, z2, "rtn")
+        assert np.array_equal(r2.kappa, r.kappa)
+
+
+def test_affine_degenerate_block():
+    blk = np.full(32, 0.3)
+    scale, zero, _, _ = affine_metadata(blk)
+    assert scale == 0.0
+    r = affine_round(blk, scale, zero, "ef", e=np.full(32, 0.01))
+    assert np.all(r.kappa == 0) and np.all(r.xhat == zero) and np.all(r.e_new == 0)
+
+
+def test_symmetric_row_levels():
+    assert [levels_n(b) for b in range(2, 9)] == [1, 3, 7, 15, 31, 63, 127]
+    fr = [fit_fraction(k) for k in range(16)]
+    assert fr[0] == 0.25 and fr[-1] == 1.0 and len(set(fr)) == 16
+    rng = np.random.default_rng(13)
+    for b in range(2, 9):
+        x = rng.standard_normal(128)
+        R = np.max(np.abs(x))
+        d, pre = row_step(R, b, 15)
+        r = sym_round(x, d, levels_n(b), "rtn")
+        assert np.abs(r.kappa).max() == levels_n(b)
+        # idempotence at f = 1: the extreme value maps to +-n, so the refit is equal
+        d2, _ = row_step(np.max(np.abs(r.xhat)), b, 15)
+        assert d2 == d
+        assert np.array_equal(sym_round(r.xhat, d2, levels_n(b), "rtn").kappa, r.kappa)
+    z = sym_round(np.zeros(8), 0.0, 7, "rtn")
+    assert np.all(z.kappa == 0)
