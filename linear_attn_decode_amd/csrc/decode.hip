@@ -1,0 +1,608 @@
+// Fused decode write-back kernel and its import/export variants (gfx950, wave64).
+//
+// One workgroup owns one head state (b, h) and updates its region in place:
+//   load + unpack codes -> dequantize -> decay -> u = k^T D S -> w = beta (v - u)
+//   -> S' = D S + k w^T -> o = S'^T q (before quantization) -> metadata -> round
+//   under the write-back rule -> pack -> store
+// ([LBRS] "Accumulated readout error"; [DAMP] "Implementation": reconstruct the INT8
+// channels, update in FP32, re-quantize, write back).
+//
+// Lane tile. Lane `tid` owns 8 rows x 8 consecutive columns: columns 8*cg .. 8*cg+7 with
+// cg = tid % (dv/8), rows rg + (dk/8)*m for m = 0..7 with rg = tid / (dv/8). For
+// dk = dv = 128 a wavefront covers 4 consecutive rows per m (512 contiguous bytes of
+// INT8 codes per load instruction), and every lane holds exactly one of the first
+// dk/8 physical rows (m = 0) -- the float16 rows of the mixed layout -- so the two
+// storage tiers never diverge inside a wavefront.
+//
+// Hadamard rows stay in the rotated domain ([DAMP] "Key Points": the transform runs
+// along the value dimension of each key channel): with Y = S H,
+//   u = sum_P k_i a_i S_i + H sum_Q k_i a_i Y_i,   w = beta (v - u),
+//   S_i' = a_i S_i + k_i w (float16 rows P),   Y_i' = a_i Y_i + k_i (H w) (rows Q),
+//   o = sum_P q_i a_i S_i + H sum_Q q_i a_i Y_i + (q . k) w,
+// so a step costs three 128-point vector transforms instead of one per row.
+//
+// Arithmetic. Layouts with Hadamard INT8 rows (HAD_INT8, MIXED) run the per-element
+// path and the u/p reductions in float64: their stored codes must agree with a float64
+// evaluation to within 1e-5 of a quantization step, and the float16 rows within 1e-5
+// of a float16 spacing (~1e-8 relative), below float32 resolution. FP32, UNIFORM and
+// BITALLOC run in float32.
+#include <type_traits>
+
+#include "wb_device.hpp"
+#include "wb_kernels.hpp"
+
+namespace wb {
+namespace {
+
+constexpr double kInvSqrt128 = 0.08838834764831844055;  // 1/sqrt(128)
+
+template <int DK, int DV>
+struct Shape {
+    static constexpr int NCG = DV / 8;                 // column groups (lanes per row)
+    static constexpr int RS = DK / 8;                  // row groups (row stride between m)
+    static constexpr int NACT = NCG * RS;              // lanes holding a tile
+    static constexpr int NT = NACT < 64 ? 64 : NACT;   // workgroup size
+    static constexpr int NW = NT / 64;
+};
+
+template <typename Real>
+__device__ __forceinline__ Real rexp(Real x);
+template <>
+__device__ __forceinline__ double rexp<double>(double x) { return exp(x); }
+template <>
+__device__ __forceinline__ float rexp<float>(float x) { return expf(x); }
+
+// 128-point orthonormal Walsh-Hadamard transform of one row held by 16 consecutive
+// lanes (8 values each, lane cg holding elements 8*cg .. 8*cg+7).
+template <typename Real>
+__device__ __forceinline__ void row_wht128(Real v[8], int cg) {
+#pragma unroll
+    for (int span = 1; span < 8; span <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if ((i & span) == 0) {
+                const Real a = v[i], b = v[i + span];
+                v[i] = a + b;
+                v[i + span] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const Real o = xor_shfl(v[i], d);
+            v[i] = (cg & d) ? (o - v[i]) : (v[i] + o);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= Real(kInvSqrt128);
+}
+
+// 128-point transform of two vectors held by one wavefront, lane l holding elements
+// l and l + 64 of each.
+template <typename Real>
+__device__ __forceinline__ void vec_wht128(Real& a0, Real& a1, int lane) {
+    Real x = a0 + a1, y = a0 - a1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const Real ox = xor_shfl(x, d), oy = xor_shfl(y, d);
+        x = (lane & d) ? (ox - x) : (x + ox);
+        y = (lane & d) ? (oy - y) : (y + oy);
+    }
+    a0 = x * Real(kInvSqrt128);
+    a1 = y * Real(kInvSqrt128);
+}
+
+template <int DK, int DV, int KIND>
+struct Smem {
+    static constexpr bool ROT = KIND == WB_HAD_INT8 || KIND == WB_MIXED;
+    using Real = typename std::conditional<ROT, double, float>::type;
+    static constexpr int NQ = ROT ? 4 : 2;             // reduced quantities: uP, pP (, uQ, pQ)
+    static constexpr int BA_WORDS = (KIND == WB_BITALLOC) ? (DK * DV + 3 * DK) / 4 + 4 : 1;
+    Real k[DK], q[DK], a[DK];
+    Real red[Shape<DK, DV>::NW][NQ][DV];
+    Real vec[NQ][DV];
+    Real w[DV], wr[DV];
+    int perm[DK];
+    // BITALLOC: the region's bytes, and per-row width, fit, byte offset and Delta
+    uint32_t reg[BA_WORDS];
+    int width[KIND == WB_BITALLOC ? DK : 1];
+    int fit[KIND == WB_BITALLOC ? DK : 1];
+    int off[KIND == WB_BITALLOC ? DK : 1];
+    float delta[KIND == WB_BITALLOC ? DK : 1];
+};
+
+template <int KIND, int MODE, int OP, int DK, int DV>
+__global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) {
+    using Sh = Shape<DK, DV>;
+    using SM = Smem<DK, DV, KIND>;
+    using Real = typename SM::Real;
+    constexpr bool ROT = SM::ROT;
+    constexpr int NCG = Sh::NCG, RS = Sh::RS, NT = Sh::NT;
+    constexpr int EMODE = (OP == OP_IMPORT) ? WB_RTN : MODE;    // import rounds to nearest
+    constexpr bool USE_SIDE = (MODE == WB_EF) && (KIND != WB_FP32);
+
+    __shared__ SM sm;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int head = blockIdx.x;
+    const int b = head / A.H, h = head - b * A.H;
+    const bool act = tid < Sh::NACT;
+    const int cg = tid % NCG, rg = act ? tid / NCG : 0;
+    uint8_t* region = A.state + (size_t)head * A.region_stride;
+    const int mhi = (KIND == WB_MIXED) ? A.k_hi / RS : 0;     // m < mhi: float16 rows
+
+    // ---- per-head vectors, in physical row order -------------------------------
+    for (int i = tid; i < DK; i += NT) {
+        const int lr = (KIND == WB_MIXED) ? int(A.perm[h * DK + i]) : i;
+        sm.perm[i] = lr;
+        if (OP == OP_STEP) {
+            sm.k[i] = Real(A.k[(size_t)head * DK + lr]);
+            sm.q[i] = Real(A.q[(size_t)head * DK + lr]);
+            const float sv = A.s_per_row ? A.s[(size_t)head * DK + lr] : A.s[head];
+            sm.a[i] = rexp<Real>(-Real(sv));
+        }
+    }
+
+    // ---- BITALLOC: stage the region in LDS, derive widths and row offsets --------
+    if (KIND == WB_BITALLOC) {
+        const int code_bytes = DK * DV * A.bbar / 8;
+        const int total = code_bytes + 3 * DK;
+        const uint4* src = reinterpret_cast<const uint4*>(region);
+        for (int i = tid; i * 16 < total; i += NT) {
+            reinterpret_cast<uint4*>(sm.reg)[i] = src[i];
+        }
+        __syncthreads();
+        const uint8_t* bytes = reinterpret_cast<const uint8_t*>(sm.reg);
+        if (wave == 0) {
+            constexpr int RPL = (DK + 63) / 64;     // rows per lane in the scan
+            int local = 0;
+            int wv[RPL];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int row = lane * RPL + r;
+                int wdt = 0;
+                if (row < DK) {
+                    const int meta = bytes[code_bytes + 2 * DK + row];
+                    wdt = (meta & 7) + 1;
+                    sm.width[row] = wdt;
+                    sm.fit[row] = meta >> 4;
+                    const uint32_t db = uint32_t(bytes[code_bytes + 2 * row]) |
+                                        (uint32_t(bytes[code_bytes + 2 * row + 1]) << 8);
+                    sm.delta[row] = f16_bits_to_f32(db);
+                }
+                wv[r] = wdt * (DV / 8);
+                local += wv[r];
+            }
+            int incl = local;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int o = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += o;
+            }
+            int run = incl - local;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int row = lane * RPL + r;
+                if (row < DK) sm.off[row] = run;
+                run += wv[r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- load the lane's tile (stored domain) ------------------------------------
+    Real x[8][8];
+    float e[8][8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            x[m][c] = Real(0);
+            e[m][c] = 0.f;
+        }
+    }
+    if (act) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int row = rg + RS * m;
+            if (OP == OP_IMPORT) {
+                const float* src = A.S_in + ((size_t)head * DK + sm.perm[row]) * DV + 8 * cg;
+                const float4 v0 = reinterpret_cast<const float4*>(src)[0];
+                const float4 v1 = reinterpret_cast<const float4*>(src)[1];
+                const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[m][c] = Real(f[c]);
+                if (ROT && (KIND == WB_HAD_INT8 || m >= mhi)) row_wht128<Real>(x[m], cg);
+                continue;
+            }
+            if (KIND == WB_FP32) {
+                const float* src = reinterpret_cast<const float*>(region) + row * DV + 8 * cg;
+                const float4 v0 = reinterpret_cast<const float4*>(src)[0];
+                const float4 v1 = reinterpret_cast<const float4*>(src)[1];
+                const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[m][c] = Real(f[c]);
+            } else if (KIND == WB_UNIFORM) {
+                const int B = A.bits;
+                const Real step = Real(1) / Real(1 << (B - 1));
+                const size_t boff = ((size_t)row * DV / 8 + cg) * B;   // 8 fields = B bytes
+                uint64_t fld;
+                if (B == 2) fld = *reinterpret_cast<const uint16_t*>(region + boff);
+                else if (B == 4) fld = *reinterpret_cast<const uint32_t*>(region + boff);
+                else fld = *reinterpret_cast<const uint64_t*>(region + boff);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    int kap = int((fld >> (c * B)) & ((1u << B) - 1));
+                    if (kap >= (1 << (B - 1))) kap -= (1 << B);
+                    x[m][c] = Real(kap) * step;
+                }
+            } else if (KIND == WB_MIXED && m < mhi) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(region + ((size_t)row * DV + 8 * cg) * 2);
+                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    x[m][c] = Real(f16_bits_to_f32((w4[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu));
+            } else if (ROT) {
+                const int k_hi = (KIND == WB_MIXED) ? A.k_hi : 0;
+                const int qrow = row - k_hi;
+                const size_t code_base = (size_t)k_hi * DV * 2;
+                const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV;
+                const uint2 raw = *reinterpret_cast<const uint2*>(region + code_base + (size_t)qrow * DV + 8 * cg);
+                const int nb = DV / A.block;
+                const int g = (8 * cg) / A.block;
+                const uint32_t sz = *reinterpret_cast<const uint32_t*>(region + meta_base + ((size_t)qrow * nb + g) * 4);
+                const Real scale = Real(f16_bits_to_f32(sz & 0xFFFFu));
+                const Real zero = Real(f16_bits_to_f32(sz >> 16));
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t code = ((c < 4 ? raw.x : raw.y) >> ((c & 3) * 8)) & 0xFFu;
+                    x[m][c] = zero + Real(code) * scale;
+                }
+            } else if (KIND == WB_BITALLOC) {
+                const int bw = sm.width[row];
+                const int n = (1 << (bw - 1)) - 1;
+                const int off = sm.off[row] + cg * bw;
+                const int wi = off >> 2, sh = (off & 3) * 8;
+                const uint64_t lo = uint64_t(sm.reg[wi]) | (uint64_t(sm.reg[wi + 1]) << 32);
+                uint64_t fld = lo >> sh;
+                if (sh) fld |= uint64_t(sm.reg[wi + 2]) << (64 - sh);
+                const float dl = sm.delta[row];
+                const uint64_t mask = (1ull << bw) - 1;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int kap = int((fld >> (c * bw)) & mask) - n;
+                    x[m][c] = Real(float(kap) * dl);
+                }
+            }
+            if (USE_SIDE && OP == OP_STEP && !(KIND == WB_MIXED && m < mhi)) {
+                const float* src = A.side + ((size_t)head * DK + row) * DV + 8 * cg;
+                const float4 v0 = reinterpret_cast<const float4*>(src)[0];
+                const float4 v1 = reinterpret_cast<const float4*>(src)[1];
+                e[m][0] = v0.x; e[m][1] = v0.y; e[m][2] = v0.z; e[m][3] = v0.w;
+                e[m][4] = v1.x; e[m][5] = v1.y; e[m][6] = v1.z; e[m][7] = v1.w;
+            }
+        }
+    }
+
+    // ---- export: back to the original domain, logical order ---------------------
+    if (OP == OP_EXPORT) {
+        if (act) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int row = rg + RS * m;
+                if (ROT && (KIND == WB_HAD_INT8 || m >= mhi)) row_wht128<Real>(x[m], cg);
+                float* dst = A.S_out + ((size_t)head * DK + sm.perm[row]) * DV + 8 * cg;
+                reinterpret_cast<float4*>(dst)[0] = make_float4(float(x[m][0]), float(x[m][1]), float(x[m][2]), float(x[m][3]));
+                reinterpret_cast<float4*>(dst)[1] = make_float4(float(x[m][4]), float(x[m][5]), float(x[m][6]), float(x[m][7]));
+            }
+        }
+        return;
+    }
+
+    if (OP == OP_STEP) {
+        // ---- u, p partial sums over the lane's rows -----------------------------
+        Real acc[SM::NQ][8];
+#pragma unroll
+        for (int qn = 0; qn < SM::NQ; ++qn)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[qn][c] = Real(0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int row = rg + RS * m;
+            const Real ka = sm.k[row] * sm.a[row];
+            const Real qa = sm.q[row] * sm.a[row];
+            const bool rot = ROT && (KIND == WB_HAD_INT8 || m >= mhi);
+            const int base = rot ? 2 : 0;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (rot) {
+                    acc[SM::NQ - 2][c] += ka * x[m][c];
+                    acc[SM::NQ - 1][c] += qa * x[m][c];
+                } else {
+                    acc[0][c] += ka * x[m][c];
+                    acc[1][c] += qa * x[m][c];
+                }
+            }
+            (void)base;
+        }
+        // reduce over the row groups of this wavefront, then across wavefronts
+#pragma unroll
+        for (int qn = 0; qn < SM::NQ; ++qn)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int d = NCG; d < 64; d <<= 1) acc[qn][c] += xor_shfl(acc[qn][c], d);
+        if (act && lane < NCG) {
+#pragma unroll
+            for (int qn = 0; qn < SM::NQ; ++qn)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) sm.red[wave][qn][8 * cg + c] = acc[qn][c];
+        }
+        __syncthreads();
+        for (int i = tid; i < SM::NQ * DV; i += NT) {
+            const int qn = i / DV, j = i - qn * DV;
+            Real sum = Real(0);
+#pragma unroll
+            for (int w = 0; w < Sh::NW; ++w) sum += sm.red[w][qn][j];
+            sm.vec[qn][j] = sum;
+        }
+        __syncthreads();
+
+        // ---- vector phase: u, w, H w, o (one wavefront) -------------------------
+        if (wave == 0) {
+            Real qk = Real(0);
+            for (int i = lane; i < DK; i += 64) qk += sm.q[i] * sm.k[i];
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) qk += xor_shfl(qk, d);
+            const Real beta = Real(A.beta[head]);
+            if constexpr (ROT) {
+                // DV == 128: lane holds elements lane and lane + 64
+                Real uq0 = sm.vec[2][lane], uq1 = sm.vec[2][lane + 64];
+                Real pq0 = sm.vec[3][lane], pq1 = sm.vec[3][lane + 64];
+                vec_wht128<Real>(uq0, uq1, lane);
+                vec_wht128<Real>(pq0, pq1, lane);
+                const Real u0 = sm.vec[0][lane] + uq0, u1 = sm.vec[0][lane + 64] + uq1;
+                const Real p0 = sm.vec[1][lane] + pq0, p1 = sm.vec[1][lane + 64] + pq1;
+                const Real w0 = beta * (Real(A.v[(size_t)head * DV + lane]) - u0);
+                const Real w1 = beta * (Real(A.v[(size_t)head * DV + lane + 64]) - u1);
+                A.o[(size_t)head * DV + lane] = float(p0 + qk * w0);
+                A.o[(size_t)head * DV + lane + 64] = float(p1 + qk * w1);
+                sm.w[lane] = w0;
+                sm.w[lane + 64] = w1;
+                Real r0 = w0, r1 = w1;
+                vec_wht128<Real>(r0, r1, lane);
+                sm.wr[lane] = r0;
+                sm.wr[lane + 64] = r1;
+            } else {
+                for (int j = lane; j < DV; j += 64) {
+                    const Real u = sm.vec[0][j];
+                    const Real p = sm.vec[1][j];
+                    const Real w = beta * (Real(A.v[(size_t)head * DV + j]) - u);
+                    A.o[(size_t)head * DV + j] = float(p + qk * w);
+                    sm.w[j] = w;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- update: S' = D S + k w^T (rotated rows take H w) --------------------
+        if (act) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int row = rg + RS * m;
+                const Real am = sm.a[row], km = sm.k[row];
+                const bool rot = ROT && (KIND == WB_HAD_INT8 || m >= mhi);
+                const Real* wv = rot ? sm.wr : sm.w;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[m][c] = am * x[m][c] + km * wv[8 * cg + c];
+            }
+        }
+    }
+
+    // ---- requantize and store ------------------------------------------------------
+    if (KIND == WB_BITALLOC) {
+        // clear the code area of the LDS copy; codes are OR-ed in, then copied out
+        __syncthreads();
+        const int code_words = DK * DV * A.bbar / 32;
+        for (int i = tid; i < code_words; i += NT) sm.reg[i] = 0u;
+        __syncthreads();
+    }
+    if (act) {
+        const uint32_t bh = uint32_t(head);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int row = rg + RS * m;
+            uint32_t r16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            const bool hi_row = (KIND == WB_MIXED && m < mhi);
+            if (EMODE == WB_SR && KIND != WB_FP32 && !hi_row) sr_draws8(A.seed, bh, A.t, row, cg, r16);
+            float en[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (KIND == WB_FP32) {
+                float* dst = reinterpret_cast<float*>(region) + row * DV + 8 * cg;
+                reinterpret_cast<float4*>(dst)[0] = make_float4(float(x[m][0]), float(x[m][1]), float(x[m][2]), float(x[m][3]));
+                reinterpret_cast<float4*>(dst)[1] = make_float4(float(x[m][4]), float(x[m][5]), float(x[m][6]), float(x[m][7]));
+                continue;
+            } else if (KIND == WB_UNIFORM) {
+                const int B = A.bits;
+                const Real step = Real(1) / Real(1 << (B - 1));
+                const int lo = -(1 << (B - 1)), hi = (1 << (B - 1)) - 1;
+                uint64_t fld = 0;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int kap = round_rule<EMODE, Real>(x[m][c], Real(e[m][c]), step, Real(0), lo, hi, r16[c], &en[c]);
+                    fld |= uint64_t(uint32_t(kap) & ((1u << B) - 1)) << (c * B);
+                }
+                const size_t boff = ((size_t)row * DV / 8 + cg) * B;
+                if (B == 2) *reinterpret_cast<uint16_t*>(region + boff) = uint16_t(fld);
+                else if (B == 4) *reinterpret_cast<uint32_t*>(region + boff) = uint32_t(fld);
+                else *reinterpret_cast<uint64_t*>(region + boff) = fld;
+            } else if (hi_row) {
+                uint32_t w4[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int c = 0; c < 8; ++c) w4[c >> 1] |= uint32_t(to_f16_bits<Real>(x[m][c])) << ((c & 1) * 16);
+                *reinterpret_cast<uint4*>(region + ((size_t)row * DV + 8 * cg) * 2) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                continue;
+            } else if (ROT) {
+                const int k_hi = (KIND == WB_MIXED) ? A.k_hi : 0;
+                const int qrow = row - k_hi;
+                const size_t code_base = (size_t)k_hi * DV * 2;
+                const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV;
+                const int LB = A.block / 8;               // lanes per block
+                Real mn = x[m][0], mx = x[m][0];
+#pragma unroll
+                for (int c = 1; c < 8; ++c) {
+                    mn = fmin(mn, x[m][c]);
+                    mx = fmax(mx, x[m][c]);
+                }
+                for (int d = 1; d < LB; d <<= 1) {
+                    mn = fmin(mn, xor_shfl(mn, d));
+                    mx = fmax(mx, xor_shfl(mx, d));
+                }
+                const Real spre = fmax(mx - mn, Real(0)) / Real(255);
+                const uint16_t sbits = to_f16_bits<Real>(spre);
+                const uint16_t zbits = to_f16_bits<Real>(mn);
+                const Real scale = Real(f16_bits_to_f32(sbits));
+                const Real zero = Real(f16_bits_to_f32(zbits));
+                uint32_t lo4 = 0, hi4 = 0;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int code = round_rule<EMODE, Real>(x[m][c], Real(e[m][c]), scale, zero, 0, 255, r16[c], &en[c]);
+                    if (c < 4) lo4 |= uint32_t(code) << (c * 8);
+                    else hi4 |= uint32_t(code) << ((c - 4) * 8);
+                }
+                *reinterpret_cast<uint2*>(region + code_base + (size_t)qrow * DV + 8 * cg) = make_uint2(lo4, hi4);
+                if ((cg % LB) == 0) {
+                    const int nb = DV / A.block;
+                    const int g = (8 * cg) / A.block;
+                    *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * nb + g) * 4) =
+                        uint32_t(sbits) | (uint32_t(zbits) << 16);
+                }
+            } else if (KIND == WB_BITALLOC) {
+                const int bw = sm.width[row];
+                const int n = (1 << (bw - 1)) - 1;
+                float R = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) R = fmaxf(R, fabsf(float(x[m][c])));
+#pragma unroll
+                for (int d = 1; d < NCG; d <<= 1) R = fmaxf(R, xor_shfl(R, d));
+                const double f = 0.25 + double(sm.fit[row]) / 20.0;
+                const uint16_t dbits = f64_to_f16_bits(f * double(R) / double(n));
+                const float dl = f16_bits_to_f32(dbits);
+                uint64_t fld = 0;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int kap = round_rule<EMODE, float>(float(x[m][c]), e[m][c], dl, 0.f, -n, n, r16[c], &en[c]);
+                    fld |= uint64_t(uint32_t(kap + n)) << (c * bw);
+                }
+                const int off = sm.off[row] + cg * bw;
+                const int wi = off >> 2, sh = (off & 3) * 8;
+                const uint64_t lo = fld << sh;
+                atomicOr(&sm.reg[wi], uint32_t(lo));
+                atomicOr(&sm.reg[wi + 1], uint32_t(lo >> 32));
+                if (sh) {
+                    const uint32_t top = uint32_t(fld >> (64 - sh));
+                    if (top) atomicOr(&sm.reg[wi + 2], top);
+                }
+                if (cg == 0) {
+                    const int code_bytes = DK * DV * A.bbar / 8;
+                    reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(sm.reg) + code_bytes)[row] = dbits;
+                }
+            }
+            if (USE_SIDE) {
+                float* dst = A.side + ((size_t)head * DK + row) * DV + 8 * cg;
+                reinterpret_cast<float4*>(dst)[0] = make_float4(en[0], en[1], en[2], en[3]);
+                reinterpret_cast<float4*>(dst)[1] = make_float4(en[4], en[5], en[6], en[7]);
+            }
+        }
+    }
+    if (KIND == WB_BITALLOC) {
+        __syncthreads();
+        const int total = DK * DV * A.bbar / 8 + 2 * DK;     // codes + Delta (meta unchanged)
+        uint4* dst = reinterpret_cast<uint4*>(region);
+        for (int i = tid; i * 16 < total; i += NT) dst[i] = reinterpret_cast<const uint4*>(sm.reg)[i];
+    }
+}
+
+template <int KIND, int MODE, int OP, int DK, int DV>
+hipError_t launch_one(const KArgs& a, int heads, hipStream_t stream) {
+    hipLaunchKernelGGL((wb_kernel<KIND, MODE, OP, DK, DV>), dim3(heads), dim3(Shape<DK, DV>::NT), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <int KIND, int OP, int DK, int DV>
+hipError_t launch_mode(int mode, const KArgs& a, int heads, hipStream_t stream) {
+    if (KIND == WB_FP32 || OP == OP_EXPORT) return launch_one<KIND, WB_RTN, OP, DK, DV>(a, heads, stream);
+    switch (mode) {
+        case WB_RTN: return launch_one<KIND, WB_RTN, OP, DK, DV>(a, heads, stream);
+        case WB_SR: return launch_one<KIND, WB_SR, OP, DK, DV>(a, heads, stream);
+        default: return launch_one<KIND, WB_EF, OP, DK, DV>(a, heads, stream);
+    }
+}
+
+template <int KIND, int DK, int DV>
+hipError_t launch_op(int op, int mode, const KArgs& a, int heads, hipStream_t stream) {
+    switch (op) {
+        case OP_STEP: return launch_mode<KIND, OP_STEP, DK, DV>(mode, a, heads, stream);
+        case OP_IMPORT: return launch_mode<KIND, OP_IMPORT, DK, DV>(mode, a, heads, stream);
+        default: return launch_mode<KIND, OP_EXPORT, DK, DV>(mode, a, heads, stream);
+    }
+}
+
+__global__ void fill_kernel(uint8_t* dst, size_t n, uint4 p0, int period) {
+    const uint8_t* pat = reinterpret_cast<const uint8_t*>(&p0);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = pat[i % period];
+}
+
+__global__ void init_bitalloc_kernel(uint8_t* state, uint64_t stride, int code_bytes, uint4 p0, int period,
+                                    int dk, uint8_t meta) {
+    const uint8_t* pat = reinterpret_cast<const uint8_t*>(&p0);
+    uint8_t* reg = state + (size_t)blockIdx.x * stride;
+    for (int i = threadIdx.x; i < code_bytes; i += blockDim.x) reg[i] = pat[i % period];
+    for (int i = threadIdx.x; i < 2 * dk; i += blockDim.x) reg[code_bytes + i] = 0;
+    for (int i = threadIdx.x; i < dk; i += blockDim.x) reg[code_bytes + 2 * dk + i] = meta;
+}
+
+}  // namespace
+
+hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes, const uint8_t* pattern,
+                                int period, int dk, uint8_t meta, hipStream_t stream) {
+    uint4 p{0, 0, 0, 0};
+    uint8_t* pb = reinterpret_cast<uint8_t*>(&p);
+    for (int i = 0; i < period && i < 16; ++i) pb[i] = pattern[i];
+    hipLaunchKernelGGL(init_bitalloc_kernel, dim3(heads), dim3(256), 0, stream, state, stride, code_bytes, p, period,
+                       dk, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_t stream) {
+    const int heads = d.B * d.H;
+    const bool small = d.dk == 16;
+    switch (d.kind) {
+        case WB_FP32:
+            return small ? launch_op<WB_FP32, 16, 16>(op, d.mode, a, heads, stream)
+                         : launch_op<WB_FP32, 128, 128>(op, d.mode, a, heads, stream);
+        case WB_UNIFORM:
+            return small ? launch_op<WB_UNIFORM, 16, 16>(op, d.mode, a, heads, stream)
+                         : launch_op<WB_UNIFORM, 128, 128>(op, d.mode, a, heads, stream);
+        case WB_HAD_INT8: return launch_op<WB_HAD_INT8, 128, 128>(op, d.mode, a, heads, stream);
+        case WB_MIXED: return launch_op<WB_MIXED, 128, 128>(op, d.mode, a, heads, stream);
+        default: return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
+    }
+}
+
+hipError_t launch_fill(void* dst, size_t n, const uint8_t* pattern, int period, hipStream_t stream) {
+    uint4 p{0, 0, 0, 0};
+    uint8_t* pb = reinterpret_cast<uint8_t*>(&p);
+    for (int i = 0; i < period && i < 16; ++i) pb[i] = pattern[i];
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<uint8_t*>(dst), n, p, period);
+    return hipGetLastError();
+}
+
+}  // namespace wb

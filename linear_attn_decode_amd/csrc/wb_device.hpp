@@ -1,0 +1,125 @@
+// Device helpers shared by the write-back kernels (gfx950, wave64).
+//
+// Pages cited: see include/wbstate.h for the list ([WB], [WB-zh], [LBRS], [LBRS-x],
+// [DAMP]).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wbstate.h"
+
+namespace wb {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64
+// multiplies with the published constants, the key bumped by the two Weyl constants
+// between rounds. Source of the 16-bit uniform draws of stochastic rounding.
+struct Ctr4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ Ctr4 philox4x32_10(Ctr4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = Ctr4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    }
+    return c;
+}
+
+// 16-bit draws for the 8 consecutive columns 8*cg .. 8*cg+7 of one stored row.
+__device__ __forceinline__ void sr_draws8(uint64_t seed, uint32_t bh, uint64_t t, int row, int cg,
+                                          uint32_t r16[8]) {
+    const Ctr4 w = philox4x32_10(Ctr4{uint32_t(16 * row + cg), bh, uint32_t(t), uint32_t(t >> 32)},
+                                 uint32_t(seed), uint32_t(seed >> 32));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) r16[c] = (c & 1) ? (ws[c >> 1] >> 16) : (ws[c >> 1] & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// float16 conversions. float64 -> float16 is rounded once, to nearest with ties to
+// even, by integer arithmetic on the float64 fields (a float64 -> float32 -> float16
+// chain can round twice and land on the wrong side of a float16 midpoint).
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
+    const uint64_t bits = (uint64_t)__double_as_longlong(x);
+    const uint16_t sign = uint16_t((bits >> 48) & 0x8000u);
+    const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
+    if (mag >= 0x7FF0000000000000ull) return sign | (mag > 0x7FF0000000000000ull ? 0x7E00u : 0x7C00u);
+    const int biased = int(mag >> 52);
+    if (biased == 0) return sign;                       // float64 subnormal: far below float16
+    const int e = biased - 1023;
+    if (e >= 16) return sign | 0x7C00u;                 // overflow to infinity
+    const uint64_t m = (mag & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+    const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+    if (shift >= 64) return sign;
+    uint64_t q = m >> shift;
+    const uint64_t rem = m & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+    const uint32_t h = (e >= -14) ? (uint32_t(e + 14) << 10) + uint32_t(q) : uint32_t(q);
+    return uint16_t(sign | h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __half_as_ushort(__float2half_rn(x));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
+    return __half2float(__ushort_as_half(uint16_t(bits)));
+}
+
+template <typename Real>
+__device__ __forceinline__ uint16_t to_f16_bits(Real x);
+template <>
+__device__ __forceinline__ uint16_t to_f16_bits<double>(double x) { return f64_to_f16_bits(x); }
+template <>
+__device__ __forceinline__ uint16_t to_f16_bits<float>(float x) { return f32_to_f16_bits(x); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (xor butterflies inside a wavefront).
+template <typename T>
+__device__ __forceinline__ T xor_shfl(T v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+// ---------------------------------------------------------------------------
+// One write-back rule on the grid offset + kappa * step, kappa in [lo, hi]
+// ([WB] / [WB-zh] write-back rules; ties to even and rail clamp per [WB-zh]
+// "Reproduction assessment"). Returns kappa; writes the new EF residual.
+template <int MODE, typename Real>
+__device__ __forceinline__ int round_rule(Real x, Real e, Real step, Real offset, int lo, int hi,
+                                          uint32_t r16, float* e_new) {
+    if (step == Real(0)) {
+        if (MODE == WB_EF) *e_new = 0.f;
+        return 0;
+    }
+    const Real target = (MODE == WB_EF) ? x + e : x;
+    const Real tau = (target - offset) / step;
+    Real kf;
+    if (MODE == WB_SR) {
+        const Real fl = floor(tau);
+        kf = fl + ((Real(r16) < (tau - fl) * Real(65536)) ? Real(1) : Real(0));
+    } else {
+        kf = rint(tau);
+    }
+    kf = fmin(fmax(kf, Real(lo)), Real(hi));
+    if (MODE == WB_EF) {
+        const Real xhat = offset + kf * step;
+        Real r = target - xhat;
+        r = fmin(fmax(r, -step), step);
+        *e_new = float(r);
+    }
+    return int(kf);
+}
+
+}  // namespace wb

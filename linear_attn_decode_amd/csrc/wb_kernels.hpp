@@ -1,0 +1,80 @@
+// Kernel argument blocks and launch entry points of the write-back kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wbstate.h"
+
+namespace wb {
+
+enum Op : int { OP_STEP = 0, OP_IMPORT = 1, OP_EXPORT = 2 };
+
+struct KArgs {
+    uint8_t* state = nullptr;         // first region
+    float* side = nullptr;            // error-feedback residuals [B*H][dk][dv]
+    const uint8_t* perm = nullptr;    // [H][dk] (MIXED)
+    const float* q = nullptr;
+    const float* k = nullptr;
+    const float* v = nullptr;
+    const float* beta = nullptr;
+    const float* s = nullptr;
+    float* o = nullptr;
+    const float* S_in = nullptr;      // import: [B*H][dk][dv] logical order
+    float* S_out = nullptr;           // export
+    uint64_t t = 0;
+    uint64_t seed = 0;
+    uint64_t region_stride = 0;
+    int H = 1;
+    int s_per_row = 1;
+    int bits = 4;
+    int block = 32;
+    int k_hi = 0;
+    int bbar = 4;
+};
+
+// One launch of the decode / import / export kernel for every head of the layout.
+hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_t stream);
+
+// Fills `n` bytes at dst with the repeating `period`-byte pattern (period <= 16).
+hipError_t launch_fill(void* dst, size_t n, const uint8_t* pattern, int period, hipStream_t stream);
+
+// Writes the zero state of every BITALLOC region: codes of width bbar holding level 0
+// (the `period`-byte pattern), Delta = 0 and the given meta byte.
+hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes,
+                                const uint8_t* pattern, int period, int dk, uint8_t meta, hipStream_t stream);
+
+struct AllocArgs {
+    uint8_t* state = nullptr;
+    const float* s = nullptr;         // [B*H][dk]
+    const float* r = nullptr;         // [B*H][dk] or null
+    uint64_t region_stride = 0;
+    float r_default = 0.f;
+    int bbar = 4, bmin = 2, bmax = 8;
+};
+hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
+
+struct DampArgs {
+    const float* samples = nullptr;   // [N][H][dk][dv]
+    const float* s = nullptr;         // [H][dk]
+    float* cost = nullptr;            // [H][dk] or null
+    uint8_t* perm = nullptr;          // [H][dk]
+    int N = 0, H = 0, block = 32, k_hi = 16;
+    float tau = 0.01f;
+};
+hipError_t launch_damp_select(const DampArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+    KArgs base;                       // state, side, perm, seed, region_stride, H, ...
+    const uint16_t* q = nullptr;      // [B][T][H][dk] bf16
+    const uint16_t* k = nullptr;
+    const uint16_t* v = nullptr;
+    const float* beta = nullptr;      // [B][T][H]
+    const float* s = nullptr;         // [B][T][H][dk] or [B][T][H]
+    float* o = nullptr;               // [B][T][H][dv]
+    int T = 0, chunk = 64, C = 8;
+    uint64_t t0 = 0;
+};
+hipError_t launch_prefill(const wb_layout_desc& d, const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace wb

@@ -1,0 +1,178 @@
+"""Teacher-forced comparison of one GPU write-back step against the oracle.
+
+Protocol (the tolerances are those fixed for the decode write-back step):
+  1. The oracle starts from the GPU's stored bytes before the step (decoded by the
+     oracle's own reader) and the GPU's residuals, and runs one float64 step on the same
+     inputs.
+  2. Metadata first: every float16 scale, zero point and row step must equal the
+     oracle's, except that the adjacent float16 value is accepted where the oracle's
+     float64 pre-rounding value lies within 1e-6 (relative) of the midpoint between the
+     two. BITALLOC widths and fit indices must be unchanged by a decode step.
+  3. Codes, given the GPU's accepted metadata: the oracle re-rounds its float64
+     pre-rounding values on the GPU's grid. Codes must be bit-equal, except that at most
+     a 1e-4 fraction of the elements may differ by exactly one step, and only where the
+     oracle's pre-rounding value lies within 1e-5 of a step of the rounding boundary
+     (for float16 rows the step is the float16 spacing at the value).
+  4. Outputs: relative L2 error of o per head <= 1e-4.
+Error-feedback residuals are compared where the codes agree, within the rounding of
+the GPU's arithmetic (float32 storage of the residual; float32 values for the float32
+layouts).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from oracle import layouts as L
+from oracle.numerics import f16_value
+from oracle.step import decode_step, write_back
+
+WINDOW = 1e-5
+MAX_FRAC = 1e-4
+META_REL = 1e-6
+O_REL = 1e-4
+
+
+@dataclass
+class Tally:
+    elems: int = 0
+    mismatch: int = 0
+    bad: list = field(default_factory=list)
+    meta_blocks: int = 0
+    meta_adjacent: int = 0
+    o_worst: float = 0.0
+    o_num: float = 0.0
+    o_den: float = 0.0
+    e_worst: float = 0.0
+
+    def ok(self):
+        return (not self.bad and self.mismatch <= MAX_FRAC * max(self.elems, 1)
+                and self.o_worst <= O_REL)
+
+    def summary(self):
+        return (f"elems={self.elems} mismatch={self.mismatch} ({self.mismatch / max(self.elems, 1):.2e}) "
+                f"bad={len(self.bad)} meta_adjacent={self.meta_adjacent}/{self.meta_blocks} "
+                f"o_worst={self.o_worst:.2e} e_worst={self.e_worst:.2e} first_bad={self.bad[:3]}")
+
+
+def _adjacent_f16(a_bits, b_bits):
+    a = np.asarray(a_bits, np.uint16).view(np.float16)
+    b = np.asarray(b_bits, np.uint16).view(np.float16)
+    return (np.nextafter(a, b) == b) | (a == b)
+
+
+def _meta_ok(gpu_bits, orc_bits, pre, tally, what):
+    gpu_bits = np.asarray(gpu_bits, np.uint16)
+    orc_bits = np.asarray(orc_bits, np.uint16)
+    tally.meta_blocks += gpu_bits.size
+    diff = gpu_bits != orc_bits
+    if not diff.any():
+        return
+    gv = f16_value(gpu_bits[diff])
+    ov = f16_value(orc_bits[diff])
+    mid = 0.5 * (gv + ov)
+    pre_d = np.asarray(pre)[diff]
+    adj = _adjacent_f16(gpu_bits[diff], orc_bits[diff])
+    near = np.abs(pre_d - mid) <= META_REL * np.maximum(np.abs(mid), 1e-300)
+    good = adj & near
+    tally.meta_adjacent += int(good.sum())
+    if not good.all():
+        idx = np.argwhere(diff)[~good][:3]
+        tally.bad.append((what, "metadata", idx.tolist(), gv[~good][:3].tolist(), ov[~good][:3].tolist(),
+                          pre_d[~good][:3].tolist()))
+
+
+def check_head(lay: L.Layout, reg_in, reg_gpu, e_in, e_gpu, o_gpu, q, k, v, beta, s, t, b, h, perm,
+               tally: Tally):
+    """Compare one head's GPU step against the oracle; accumulate into ``tally``."""
+    reg_in = np.asarray(reg_in, np.uint8)[: lay.region_size()]
+    reg_gpu = np.asarray(reg_gpu, np.uint8)[: lay.region_size()]
+    r = decode_step(lay, reg_in, e_in, q, k, v, beta, s, t, b, h, perm)
+    o = np.asarray(o_gpu, np.float64)
+    den = np.linalg.norm(r.o)
+    rel = np.linalg.norm(o - r.o) / max(den, 1e-30)
+    tally.o_worst = max(tally.o_worst, rel)
+    tally.o_num += float(np.sum((o - r.o) ** 2))
+    tally.o_den += float(den ** 2)
+    where = (b, h, t)
+    cin = L.decode_region(lay, reg_in)
+    g = L.decode_region(lay, reg_gpu)
+    X = r.wb.X
+    if lay.kind == L.FP32:
+        err = np.abs(g.S32 - X)
+        tol = 4 * 2.0 ** -24 * (np.abs(X) + np.max(np.abs(X)))
+        tally.elems += X.size
+        if np.any(err > tol):
+            i = np.unravel_index(np.argmax(err - tol), err.shape)
+            tally.bad.append((where, "fp32 value", i, g.S32[i], X[i]))
+        return r
+    override = None
+    if lay.kind in (L.HAD_INT8, L.MIXED):
+        o_scale_bits = L.decode_region(lay, r.wb.region).scale_bits
+        o_zero_bits = L.decode_region(lay, r.wb.region).zero_bits
+        _meta_ok(g.scale_bits, o_scale_bits, r.wb.meta_pre["scale"], tally, (where, "scale"))
+        _meta_ok(g.zero_bits, o_zero_bits, r.wb.meta_pre["zero"], tally, (where, "zero"))
+        override = {"scale": g.scale, "zero": g.zero}
+    elif lay.kind == L.BITALLOC:
+        if not (np.array_equal(g.widths, cin.widths) and np.array_equal(g.fit, cin.fit)):
+            tally.bad.append((where, "widths/fit changed by a decode step"))
+        o_delta_bits = L.decode_region(lay, r.wb.region).delta_bits
+        _meta_ok(g.delta_bits, o_delta_bits, r.wb.meta_pre["delta"], tally, (where, "delta"))
+        override = {"delta": g.delta}
+    wb2 = write_back(lay, X, e_in, t, b, h, prev=cin, meta_override=override)
+    req = L.decode_region(lay, wb2.region)
+    if lay.kind == L.UNIFORM:
+        gc, oc = g.kappa, req.kappa
+        step = np.full(X.shape, 2.0 ** (1 - lay.bits))
+    elif lay.kind == L.BITALLOC:
+        gc, oc = g.kappa, req.kappa
+        step = np.repeat(g.delta[:, None], lay.dv, axis=1)
+    else:
+        q0 = lay.dk - lay.int8_rows
+        gc = np.zeros(X.shape, np.int64)
+        oc = np.zeros(X.shape, np.int64)
+        gc[q0:], oc[q0:] = g.codes, req.codes
+        if lay.kind == L.MIXED:
+            # float16 rows: codes are the bit patterns; adjacency by one float16 step
+            gb = g.hi_bits.astype(np.int64)
+            ob = req.hi_bits.astype(np.int64)
+            gc[:q0], oc[:q0] = gb, ob
+        step = np.zeros(X.shape)
+        step[q0:] = np.repeat(g.scale, lay.block, axis=1)
+        if lay.kind == L.MIXED:
+            step[:q0] = 1.0
+    tally.elems += X.size
+    diff = gc != oc
+    if diff.any():
+        d = np.abs(gc - oc)
+        if lay.kind == L.MIXED:
+            q0 = lay.dk - lay.int8_rows
+            adj = np.zeros(X.shape, bool)
+            adj[:q0] = _adjacent_f16(g.hi_bits, req.hi_bits)
+            adj[q0:] = d[q0:] == 1
+        else:
+            adj = d == 1
+        near = wb2.boundary <= WINDOW
+        ok = ~diff | (adj & near)
+        tally.mismatch += int(diff.sum())
+        if not ok.all():
+            idx = np.argwhere(~ok)[:3]
+            tally.bad.append((where, "codes", idx.tolist(), gc[~ok][:3].tolist(), oc[~ok][:3].tolist(),
+                              wb2.boundary[~ok][:3].tolist(), wb2.tau[~ok][:3].tolist()))
+    if lay.mode == "ef":
+        eg = np.asarray(e_gpu, np.float64)
+        eo = wb2.e_new
+        same = ~diff
+        if lay.kind == L.MIXED:
+            same[: lay.dk - lay.int8_rows] = False
+        if lay.kind in (L.HAD_INT8, L.MIXED):
+            tol = 2.0 ** -22 * np.abs(eo) + 1e-9 * step
+        else:
+            tol = 1e-6 * (np.abs(X) + np.abs(np.asarray(e_in))) + 1e-7 * step
+        err = np.where(same, np.abs(eg - eo) - tol, -np.inf)
+        tally.e_worst = max(tally.e_worst, float(np.max(np.where(same, np.abs(eg - eo), 0))))
+        if np.any(err > 0):
+            i = np.unravel_index(np.argmax(err), err.shape)
+            tally.bad.append((where, "residual", i, eg[i], eo[i]))
+    return r

@@ -1,0 +1,285 @@
+"""GPU parity of the fused decode write-back step (every layout x write-back rule),
+import/export, the allocation pass and DAMP selection, against the CPU oracle.
+
+Each test prints the case it runs before launching GPU work."""
+import numpy as np
+import pytest
+
+from oracle import layouts as L
+from oracle.allocation import allocate_head
+from oracle.damp import risk_scores, select_permutation
+from oracle.numerics import f16_value
+from oracle.step import allocate_region, export_state, import_state, write_back
+from synth import decode_inputs
+from tests.parity import Tally, check_head
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _wb():
+    import linear_attn_decode_amd as wb
+    return wb
+
+
+def _layout(kind, mode, B, H, dk, per_row=True, **kw):
+    args = dict(kind=kind, B=B, H=H, dk=dk, dv=dk, mode=mode, per_row_decay=per_row, seed=0x5EED_1234_ABCD)
+    if kind == L.HAD_INT8:
+        args["block"] = 128
+    args.update(kw)
+    return L.Layout(**args)
+
+
+def _state(lay, perm=None):
+    wb = _wb()
+    return wb.WriteBackState(lay.kind, lay.mode, lay.B, lay.H, lay.dk, lay.dv, lay.per_row_decay,
+                             bits=lay.bits, block=lay.block, k_hi=lay.k_hi, bbar=lay.bbar, bmin=lay.bmin,
+                             bmax=lay.bmax, seed=lay.seed, perm=perm)
+
+
+def _warm_state(rng, B, H, dk, dv):
+    """A realistic stored state: rows of very different ranges."""
+    scale = np.exp(rng.uniform(-3.0, 0.5, (B, H, dk, 1)))
+    return (rng.standard_normal((B, H, dk, dv)) * scale).astype(np.float32)
+
+
+def _to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_decode(lay, T, heads=None, warm=True, seed=1, perm=None, steps_checked=None, alloc_every=None):
+    print(f"\n[case] kind={lay.kind} mode={lay.mode} B={lay.B} H={lay.H} dk={lay.dk} T={T}", flush=True)
+    B, H, dk, dv = lay.B, lay.H, lay.dk, lay.dv
+    rng = np.random.default_rng(seed)
+    if lay.kind == L.MIXED and perm is None:
+        perm = np.stack([rng.permutation(dk) for _ in range(H)])
+    st = _state(lay, perm)
+    inp = decode_inputs(seed, B, H, dk, dv, T, lay.per_row_decay)
+    dev = {k: _to_dev(v) for k, v in inp.items()}
+    o = torch.zeros((B, H, dv), dtype=torch.float32, device="cuda")
+    if warm:
+        st.quantize(_to_dev(_warm_state(rng, B, H, dk, dv)))
+    heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    tally = Tally()
+    s_all = inp["s"]
+    for t in range(T):
+        check = steps_checked is None or t in steps_checked
+        if alloc_every and t % alloc_every == 0 and t > 0:
+            st.allocate_bits(dev["s"] if s_all.ndim == 3 else None)
+        if check:
+            regs = st.regions()
+            reg_in = {bh: regs[bh[0] * H + bh[1]].cpu().numpy() for bh in heads}
+            res = st.residuals()
+            e_in = {bh: res[bh[0], bh[1]].cpu().numpy() for bh in heads} if res is not None else None
+        st.step_decode(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, t)
+        if not check:
+            continue
+        torch.cuda.synchronize()
+        regs = st.regions()
+        res = st.residuals()
+        o_np = o.cpu().numpy()
+        for (b, h) in heads:
+            check_head(lay, reg_in[(b, h)], regs[b * H + h].cpu().numpy(),
+                       None if e_in is None else e_in[(b, h)],
+                       None if res is None else res[b, h].cpu().numpy(), o_np[b, h],
+                       inp["q"][t, b, h], inp["k"][t, b, h], inp["v"][t, b, h], inp["beta"][t, b, h],
+                       s_all[b, h], t, b, h, None if perm is None else perm[h], tally)
+    print("[tally]", tally.summary(), flush=True)
+    assert tally.ok(), tally.summary()
+    return tally
+
+
+def test_tiny_uniform_4bit_rtn_every_step():
+    lay = _layout(L.UNIFORM, "rtn", 1, 1, 16, bits=4)
+    run_decode(lay, 256, warm=False, seed=0)
+
+
+def test_tiny_uniform_4bit_error_feedback_every_step():
+    lay = _layout(L.UNIFORM, "ef", 1, 1, 16, bits=4)
+    run_decode(lay, 256, warm=False, seed=0)
+
+
+def test_tiny_fp32_identity():
+    lay = _layout(L.FP32, "rtn", 1, 1, 16)
+    run_decode(lay, 64, warm=False, seed=0)
+
+
+CASES = [
+    (L.FP32, {}), (L.UNIFORM, {"bits": 4}), (L.UNIFORM, {"bits": 2}), (L.UNIFORM, {"bits": 8}),
+    (L.HAD_INT8, {"block": 128}), (L.HAD_INT8, {"block": 32}), (L.MIXED, {"block": 32, "k_hi": 16}),
+    (L.BITALLOC, {}),
+]
+
+
+@pytest.mark.parametrize("kind,kw", CASES, ids=[f"{k}-{'-'.join(map(str, v.values()))}" for k, v in CASES])
+@pytest.mark.parametrize("mode", ["rtn", "sr", "ef"])
+def test_decode_matrix(kind, kw, mode):
+    if kind == L.FP32 and mode != "rtn":
+        pytest.skip("identity write-back has no rounding rule")
+    lay = _layout(kind, mode, 2, 3, 128, **kw)
+    run_decode(lay, 4, warm=True, seed=11)
+
+
+def test_decode_per_head_decay_had_int8():
+    lay = _layout(L.HAD_INT8, "rtn", 2, 2, 128, per_row=False, block=128)
+    run_decode(lay, 3, warm=True, seed=12)
+
+
+def test_bitalloc_after_allocation_rtn_and_sr():
+    for mode in ("rtn", "sr"):
+        lay = _layout(L.BITALLOC, mode, 2, 2, 128)
+        run_decode(lay, 7, warm=True, seed=13, alloc_every=3)
+
+
+# ---------------------------------------------------------------------------- import / export
+
+
+@pytest.mark.parametrize("kind,kw", CASES, ids=[f"{k}-{'-'.join(map(str, v.values()))}" for k, v in CASES])
+def test_import_export(kind, kw):
+    print(f"\n[case] import/export kind={kind} {kw}", flush=True)
+    B, H, dk = 2, 2, 128
+    lay = _layout(kind, "rtn", B, H, dk, **kw)
+    rng = np.random.default_rng(21)
+    perm = np.stack([rng.permutation(dk) for _ in range(H)]) if kind == L.MIXED else None
+    st = _state(lay, perm)
+    S = _warm_state(rng, B, H, dk, dk)
+    st.quantize(_to_dev(S))
+    out = torch.zeros((B, H, dk, dk), dtype=torch.float32, device="cuda")
+    st.dequant(out)
+    torch.cuda.synchronize()
+    regs = st.regions().cpu().numpy()
+    S_gpu = out.cpu().numpy()
+    init = L.initial_region(lay)
+    tally = Tally()
+    for b in range(B):
+        for h in range(H):
+            p = None if perm is None else perm[h]
+            reg = regs[b * H + h][: lay.region_size()]
+            # export: the oracle's decoder on the GPU bytes, to float32
+            ref = export_state(lay, reg, p)
+            assert np.allclose(S_gpu[b, h], ref, rtol=2 ** -23, atol=1e-7 * np.abs(ref).max())
+            # import: one nearest write-back of S from the zero state's metadata
+            X = L.to_stored(lay, S[b, h].astype(np.float64), p)
+            cin = L.decode_region(lay, init)
+            orc = write_back(lay, X, None, 0, b, h, prev=cin)
+            g = L.decode_region(lay, reg)
+            o_reg = orc.region
+            if kind == L.FP32:
+                assert np.array_equal(reg, o_reg)
+                continue
+            if kind in (L.HAD_INT8, L.MIXED):
+                oc = L.decode_region(lay, o_reg)
+                from tests.parity import _meta_ok
+                _meta_ok(g.scale_bits, oc.scale_bits, orc.meta_pre["scale"], tally, ("scale", b, h))
+                _meta_ok(g.zero_bits, oc.zero_bits, orc.meta_pre["zero"], tally, ("zero", b, h))
+                override = {"scale": g.scale, "zero": g.zero}
+            elif kind == L.BITALLOC:
+                from tests.parity import _meta_ok
+                oc = L.decode_region(lay, o_reg)
+                _meta_ok(g.delta_bits, oc.delta_bits, orc.meta_pre["delta"], tally, ("delta", b, h))
+                override = {"delta": g.delta}
+            else:
+                override = None
+            req = write_back(lay, X, None, 0, b, h, prev=cin, meta_override=override)
+            diff = req.region != reg
+            if diff.any():
+                # element-level check through the decoded codes
+                rc = L.decode_region(lay, req.region)
+                if kind == L.UNIFORM or kind == L.BITALLOC:
+                    d = rc.kappa != g.kappa
+                    assert np.all(req.boundary[d] <= 1e-5), (kind, np.argwhere(d)[:3])
+                    tally.mismatch += int(d.sum())
+                else:
+                    q0 = dk - lay.int8_rows
+                    d = rc.codes != g.codes
+                    assert np.all(req.boundary[q0:][d] <= 1e-5)
+                    tally.mismatch += int(d.sum())
+                    if kind == L.MIXED:
+                        dh = rc.hi_bits != g.hi_bits
+                        assert np.all(req.boundary[:q0][dh] <= 1e-5)
+                        tally.mismatch += int(dh.sum())
+            tally.elems += dk * dk
+    print("[tally]", tally.summary(), flush=True)
+    assert not tally.bad and tally.mismatch <= 1e-4 * tally.elems, tally.summary()
+
+
+# ---------------------------------------------------------------------------- allocation pass
+
+
+def test_allocate_bits_matches_oracle():
+    print("\n[case] allocate_bits B=2 H=4", flush=True)
+    B, H, dk = 2, 4, 128
+    lay = _layout(L.BITALLOC, "rtn", B, H, dk)
+    rng = np.random.default_rng(31)
+    st = _state(lay)
+    st.quantize(_to_dev(_warm_state(rng, B, H, dk, dk)))
+    s = np.exp(rng.uniform(np.log(1e-3), 0.0, (B, H, dk))).astype(np.float32)
+    r = np.full((B, H, dk), 1.0 / (3 * dk), dtype=np.float32)
+    torch.cuda.synchronize()
+    before = st.regions().cpu().numpy()
+    st.allocate_bits(_to_dev(s), _to_dev(r))
+    torch.cuda.synchronize()
+    after = st.regions().cpu().numpy()
+    st2 = _state(lay)
+    st2.state.copy_(st.state)
+    for b in range(B):
+        for h in range(H):
+            reg_in = before[b * H + h][: lay.region_size()]
+            reg_gpu = after[b * H + h][: lay.region_size()]
+            reg_orc, alloc = allocate_region(lay, reg_in, s[b, h].astype(np.float64), r[b, h].astype(np.float64))
+            g = L.decode_region(lay, reg_gpu)
+            o = L.decode_region(lay, reg_orc)
+            assert g.widths.sum() == 512
+            if not np.array_equal(g.widths, o.widths):
+                # only near-ties of the real widths may differ
+                bad = np.argwhere(g.widths != o.widths).ravel()
+                frac = np.abs(alloc["bstar"][bad] - np.floor(alloc["bstar"][bad]) - 0.5)
+                assert np.all(frac < 1e-5), (b, h, bad, alloc["bstar"][bad])
+                continue
+            if not np.array_equal(g.fit, o.fit):
+                bad = np.argwhere(g.fit != o.fit).ravel()
+                for i in bad:
+                    e = alloc["fit_err"][i]
+                    assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (b, h, i)
+                continue
+            assert np.array_equal(reg_gpu, reg_orc), (b, h)
+
+
+def test_allocation_then_decode_full_budget_zero_state():
+    # a zero state keeps every row at the mean width
+    lay = _layout(L.BITALLOC, "rtn", 1, 2, 128)
+    st = _state(lay)
+    s = _to_dev(np.full((1, 2, 128), 0.01, np.float32))
+    st.allocate_bits(s)
+    torch.cuda.synchronize()
+    regs = st.regions().cpu().numpy()
+    for h in range(2):
+        c = L.decode_region(lay, regs[h][: lay.region_size()])
+        assert np.all(c.widths == 4) and np.all(c.kappa == 0)
+
+
+# ---------------------------------------------------------------------------- DAMP selection
+
+
+def test_damp_select_matches_oracle():
+    print("\n[case] damp_select N=6 H=3", flush=True)
+    wb = _wb()
+    rng = np.random.default_rng(41)
+    N, H, dk = 6, 3, 128
+    samples = (rng.standard_normal((N, H, dk, dk)) * np.exp(rng.uniform(-3, 1, (1, H, dk, 1)))).astype(np.float32)
+    s = np.exp(rng.uniform(np.log(1e-3), 0, (H, dk))).astype(np.float32)
+    perm, cost = wb.damp_select(_to_dev(samples), _to_dev(s), k_hi=16, block=32, tau=0.01)
+    torch.cuda.synchronize()
+    perm = perm.cpu().numpy()
+    cost = cost.cpu().numpy()
+    for h in range(H):
+        E, P, C = risk_scores(samples[:, h].astype(np.float64), s[h].astype(np.float64), 0.01, 32)
+        assert np.allclose(cost[h], C, rtol=1e-5)
+        ref = select_permutation(C, 16)
+        if not np.array_equal(perm[h], ref):
+            # only rows whose costs tie to 1e-6 at the selection boundary may swap
+            thr = np.sort(C)[::-1][15]
+            diff = set(perm[h][:16]) ^ set(ref[:16])
+            assert all(abs(C[u] - thr) <= 1e-6 * thr for u in diff), h
+        assert sorted(perm[h]) == list(range(dk))
