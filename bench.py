@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the fused quantized write-back decode step on one MI355X.
+
+A step is one decode token through one layer: every head state of a B x H layer is
+dequantized, advanced by the gated delta rule, read out and requantized in place
+(one kernel launch), and the layer's decay-aware allocation pass runs on its cadence
+(every 64 of that layer's tokens). L independent layer states are cycled so that the
+working set is several times the 256 MB last-level cache; q, k, v, beta, s and o
+cycle through a 64-token ring on the device. Inputs are synthetic (seeded), with the
+distributions of the decode studies, and resident in HBM before timing starts.
+
+Prints ONE JSON line: tokens/s (value), the achieved HBM bandwidth of the decode
+kernel against the 8 TB/s peak (roofline), and the CPU oracle timed on a bounded sample
+of the same work (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "kda-bitalloc": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
+                         extra=dict(bbar=4, bmin=2, bmax=8)),
+    "kda-mixed": dict(cfg=2, kind="mixed", B=256, H=32, per_row=True, layers=7, alloc_every=0,
+                      extra=dict(block=32, k_hi=16)),
+    "gdn-had-int8": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
+                         extra=dict(block=128)),
+    "kda-fp32": dict(cfg=None, kind="fp32", B=256, H=32, per_row=True, layers=3, alloc_every=0, extra={}),
+}
+DEFAULT = "kda-bitalloc"
+DK = DV = 128
+
+
+def region_bytes(kind, extra):
+    dk, dv = DK, DV
+    if kind == "fp32":
+        return 4 * dk * dv, 4 * dk * dv
+    if kind == "had_int8":
+        n = dk * dv + dk * (dv // extra["block"]) * 4
+        return n, n
+    if kind == "mixed":
+        qr = dk - extra["k_hi"]
+        n = extra["k_hi"] * dv * 2 + qr * dv + qr * (dv // extra["block"]) * 4
+        return n, n
+    code = dk * dv * extra["bbar"] // 8
+    return code + 3 * dk, code + 2 * dk          # read: codes + Delta + meta; write: codes + Delta
+
+
+def algorithmic_bytes_per_head(kind, extra, per_row):
+    rd, wr = region_bytes(kind, extra)
+    io = 2 * DK * 4 + DV * 4 + 4 + (DK * 4 if per_row else 4) + DV * 4
+    return rd + wr + io
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "linear_attn_decode_amd", "csrc"))):
+        with open(os.path.join(ROOT, "linear_attn_decode_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def warm_states(wb, torch, w, seed):
+    """L layer states holding a realistic state: rows of widely different ranges,
+    slow-decay rows larger; BITALLOC states get one allocation pass."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 100)
+    B, H = w["B"], w["H"]
+    perm = None
+    if w["kind"] == "mixed":
+        import numpy as np
+        rng = np.random.default_rng(seed)
+        perm = np.stack([rng.permutation(DK) for _ in range(H)])
+    states = []
+    for layer in range(w["layers"]):
+        st = wb.WriteBackState(w["kind"], "rtn", B, H, DK, DV, w["per_row"], seed=seed + layer, perm=perm,
+                               **w["extra"])
+        scale = torch.exp(torch.rand((B, H, DK, 1), generator=g, device="cuda") * 3.5 - 3.0)
+        S = torch.randn((B, H, DK, DV), generator=g, device="cuda") * scale
+        st.quantize(S.contiguous())
+        states.append(st)
+        del S
+    return states
+
+
+def run_gpu(args, w):
+    import torch
+
+    import linear_attn_decode_amd as wb
+    from synth import device_inputs
+
+    torch.cuda.set_device(0)
+    B, H = w["B"], w["H"]
+    R = 64
+    inp = device_inputs(args.seed, B, H, DK, DV, R, w["per_row"])
+    s_ring = inp["s"].unsqueeze(0).expand((R,) + tuple(inp["s"].shape)).contiguous()
+    s_alloc = inp["s"] if w["per_row"] else None
+    o_ring = torch.zeros((R, B, H, DV), dtype=torch.float32, device="cuda")
+    states = warm_states(wb, torch, w, args.seed)
+    if w["kind"] == "bitalloc":
+        for st in states:
+            st.allocate_bits(s_alloc)
+    torch.cuda.synchronize()
+    counts = [0] * len(states)
+    alloc_every = w["alloc_every"]
+
+    def one(i, ev=None, ev_alloc=None):
+        layer = i % len(states)
+        r = i % R
+        st = states[layer]
+        if ev is not None:
+            ev[0].record()
+        st.step_decode(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r], counts[layer])
+        if ev is not None:
+            ev[1].record()
+        counts[layer] += 1
+        if alloc_every and counts[layer] % alloc_every == 0:
+            if ev_alloc is not None:
+                ev_alloc[0].record()
+            st.allocate_bits(s_alloc)
+            if ev_alloc is not None:
+                ev_alloc[1].record()
+                return True
+        return False
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    aevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    used_alloc = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        if one(args.warmup + i, evs[i], aevs[i]):
+            used_alloc.append(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    alloc_ms = [aevs[i][0].elapsed_time(aevs[i][1]) for i in used_alloc]
+    return {"total_ms": total_ms, "wall_s": wall, "decode_ms": dec_ms, "alloc_ms": alloc_ms, "states": states,
+            "inputs": inp}
+
+
+def cpu_baseline(w, gpu, budget_s):
+    """The oracle, single-threaded, on a bounded sample of the same decode work: the
+    stored regions of sampled heads after the GPU warm-up, one step each."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    from oracle import layouts as L
+    from oracle.step import decode_step
+
+    st = gpu["states"][0]
+    inp = gpu["inputs"]
+    lay = L.Layout(kind=w["kind"], B=w["B"], H=w["H"], dk=DK, dv=DV, per_row_decay=w["per_row"], mode="rtn",
+                   **{k: v for k, v in w["extra"].items()})
+    regs = st.regions()
+    perm = st._perm
+    q = inp["q"][0].cpu().numpy()
+    k = inp["k"][0].cpu().numpy()
+    v = inp["v"][0].cpu().numpy()
+    beta = inp["beta"][0].cpu().numpy()
+    s = inp["s"].cpu().numpy()
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w["B"] * w["H"])
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    n = 0
+    t0 = time.perf_counter()
+    try:
+        if ctx:
+            ctx.__enter__()
+        while True:
+            idx = int(order[n % order.size])
+            b, h = divmod(idx, w["H"])
+            reg = regs[idx].cpu().numpy()[: lay.region_size()]
+            decode_step(lay, reg, None, q[b, h], k[b, h], v[b, h], beta[b, h], s[b, h], 0, b, h,
+                        None if perm is None else perm[h])
+            n += 1
+            if time.perf_counter() - t0 >= budget_s and n >= 4:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    el = time.perf_counter() - t0
+    per_head = el / n
+    tok_s = 1.0 / (per_head * w["H"])          # one token of a sequence = H heads
+    return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {w['B'] * w['H']} head states of one decode step, float64 numpy, "
+                      f"{el:.1f} s, extrapolated to the full step (host has {os.cpu_count()} logical CPUs)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported on this build "
+              f"(every head state is independent, see the design notes on sharding).", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    gpu = run_gpu(args, w)
+    B, H = w["B"], w["H"]
+    K = args.steps
+    total_s = gpu["total_ms"] / 1e3
+    tokens = B * K
+    dec = sorted(gpu["decode_ms"])
+    avg_dec_ms = sum(dec) / len(dec)
+    bytes_launch = algorithmic_bytes_per_head(w["kind"], w["extra"], w["per_row"]) * B * H
+    achieved = bytes_launch / (avg_dec_ms / 1e3) / 1e9
+    traffic = load_traffic(args.workload)
+    out = {
+        "metric": "write-back decode tokens/s + effective HBM GB/s (% peak), 32h x 128x128, B=256",
+        "value": tokens / total_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": gpu["total_ms"] / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w["kind"] in ("bitalloc", "fp32") else "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: decode write-back, {w['kind']} layout, B={B}, H={H}, "
+                               f"dk=dv=128, {'per-row' if w['per_row'] else 'per-head'} decay, RTN, "
+                               f"{w['layers']} layer states cycled"
+                               + (f", allocation pass every {w['alloc_every']} tokens per layer" if w["alloc_every"] else ""),
+                   "global_batch": B, "heads": H, "layers_cycled": w["layers"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "wb_kernel (decode step)", "bytes_per_launch": bytes_launch,
+                     "avg_launch_us": avg_dec_ms * 1e3, "median_launch_us": dec[len(dec) // 2] * 1e3},
+        "allocation_pass": {"launches": len(gpu["alloc_ms"]),
+                            "avg_us": (sum(gpu["alloc_ms"]) / len(gpu["alloc_ms"]) * 1e3) if gpu["alloc_ms"] else None},
+        "wall_s": gpu["wall_s"],
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, gpu, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
