@@ -36,6 +36,9 @@ struct KArgs {
 // One launch of the decode / import / export kernel for every head of the layout.
 hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_t stream);
 
+// Decode step of the BITALLOC layout with round-to-nearest (the tuned kernel).
+hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
+
 // Fills `n` bytes at dst with the repeating `period`-byte pattern (period <= 16).
 hipError_t launch_fill(void* dst, size_t n, const uint8_t* pattern, int period, hipStream_t stream);
 

@@ -283,3 +283,27 @@ def test_damp_select_matches_oracle():
             diff = set(perm[h][:16]) ^ set(ref[:16])
             assert all(abs(C[u] - thr) <= 1e-6 * thr for u in diff), h
         assert sorted(perm[h]) == list(range(dk))
+
+
+# ---------------------------------------------------------------------------- full-size shapes
+
+
+FULL = [
+    ("gdn-had-int8", dict(kind=L.HAD_INT8, B=64, H=16, per_row=False, block=128), ["rtn"]),
+    ("kda-mixed", dict(kind=L.MIXED, B=256, H=32, per_row=True, block=32, k_hi=16), ["rtn"]),
+    ("kda-bitalloc", dict(kind=L.BITALLOC, B=256, H=32, per_row=True), ["rtn", "sr"]),
+]
+
+
+@pytest.mark.parametrize("name,cfg,modes", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled_heads(name, cfg, modes):
+    """The benchmark's launch configuration (all heads of a full layer per launch),
+    checked on sampled heads over a few teacher-forced steps; BITALLOC after an
+    allocation pass."""
+    rng = np.random.default_rng(51)
+    for mode in modes:
+        c = dict(cfg)
+        kind, B, H, per_row = c.pop("kind"), c.pop("B"), c.pop("H"), c.pop("per_row")
+        lay = _layout(kind, mode, B, H, 128, per_row=per_row, **c)
+        picks = sorted({(int(rng.integers(B)), int(rng.integers(H))) for _ in range(12)})
+        run_decode(lay, 4, heads=picks, warm=True, seed=52, steps_checked={1, 3}, alloc_every=1 if kind == L.BITALLOC else None)
