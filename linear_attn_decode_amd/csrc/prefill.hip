@@ -1,14 +1,438 @@
-// Chunked prefill with deferred write-back.
+// Prefill with deferred write-back (chunked gated delta rule on MFMA).
+//
+// [LBRS] "Accumulated readout error": write-back happens once every C tokens (per
+// prefill chunk, per token in decode, or deferred with C = 8); outputs are read from
+// the unquantized state before each write-back. Between two write-backs the state
+// evolves exactly, so each call is cut into segments of at most 8 tokens that end at
+// every write-back point; a segment of L tokens starting from state S_0 is evaluated
+// in closed form (a WY-style rewrite of L delta-rule steps):
+//   g_t = sum_{tau<=t} s_tau (per key row), Gamma_t = e^{-g_t};
+//   k^_t = Gamma_t k_t,  q^_t = Gamma_t q_t,  k-_t = k_t / Gamma_t;
+//   w_t  = beta_t (v_t - S_0^T k^_t - sum_{tau<t} (k^_t . k-_tau) w_tau)   (forward solve)
+//   o_t  = S_0^T q^_t + sum_{tau<=t} (q^_t . k-_tau) w_tau
+//   S_L  = Gamma_L S_0 + sum_tau (Gamma_L k-_tau) w_tau^T.
+// The dense contractions [k^; q^] S_0 (16 x 128 x 128) and the rank-8 update run on
+// v_mfma_f32_16x16x4_f32 in float32 (inputs q, k, v are bfloat16); the triangular
+// solve and the small dot products run on the vector ALUs.
+//
+// State placement: the 128 x 128 state lives in registers in the MFMA accumulator
+// layout. Wave w owns columns 32w .. 32w+31 (2 column tiles of 16) and all 8 row tiles;
+// lane l holds rows 16*rt + 4*(l/16) + r (r = 0..3) of columns 32w + 16*ct + l%16. The
+// same registers serve as the B operand of the [k^; q^] S_0 contraction (K index =
+// row), so no state data moves between waves. Hadamard rows stay rotated (Y = S H):
+// the contraction over rotated rows is transformed back with one 128-point transform
+// per output vector, and rotated rows are updated with H w.
+//
+// Write-back (every C tokens and after the last token) rounds the register state in
+// place: float16 rows to nearest float16; Hadamard INT8 rows per block of 32 columns
+// (= one wave's columns) with an asymmetric affine grid ([DAMP] "Quantization &
+// calibration details"); uniform rows on the B-bit grid. The last write-back is also
+// encoded into the stored region. Supported here: FP32, UNIFORM, HAD_INT8 and MIXED
+// with affine blocks of 32 values, round-to-nearest.
 #include "wb_device.hpp"
 #include "wb_kernels.hpp"
 
 namespace wb {
+namespace {
+
+constexpr int DK = 128, DV = 128, NT = 256, SEG = 8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));   // MFMA accumulator fragment
+constexpr float kInvSqrt128f = 0.08838834764831845f;
+
+struct PfSmem {
+    float khat[SEG][DK];      // rows 0..7 of the contraction operand
+    float qhat[SEG][DK];      // rows 8..15 (must follow khat)
+    float kbar[SEG][DK];      // k_tau / Gamma_tau
+    float kbarL[SEG][DK];     // Gamma_L k_tau / Gamma_tau
+    float gl[DK];             // Gamma_L per row
+    float v[SEG][DV];
+    float ks[2 * SEG][DV];    // [k^; q^] S_0 (and the rotated-part exchange)
+    float w[SEG][DV];
+    float hw[SEG][DV];
+    float A[SEG][SEG], QK[SEG][SEG];
+    float beta[SEG];
+    int perm[DK];
+};
+
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// 128-point orthonormal transform of a vector held by one wavefront as v[lane], v[lane + 64]
+__device__ __forceinline__ void wave_wht128(float& a0, float& a1, int lane) {
+    float x = a0 + a1, y = a0 - a1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float ox = __shfl_xor(x, d, 64), oy = __shfl_xor(y, d, 64);
+        x = (lane & d) ? (ox - x) : (x + ox);
+        y = (lane & d) ? (oy - y) : (y + oy);
+    }
+    a0 = x * kInvSqrt128f;
+    a1 = y * kInvSqrt128f;
+}
+
+// min / max over the 16 lanes of a DPP row
+__device__ __forceinline__ float dpp_min16(float v) {
+    v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+__device__ __forceinline__ float dpp_max16(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+template <int KIND>
+struct PfLayout {
+    static constexpr bool ROT = KIND == WB_HAD_INT8 || KIND == WB_MIXED;
+    // row tile rt is rotated (Hadamard) for these layouts; MIXED keeps row tile 0
+    // (physical rows 0..15, the float16 rows with k_hi = 16) unrotated
+    __device__ static bool rotated(int rt) { return KIND == WB_HAD_INT8 || (KIND == WB_MIXED && rt > 0); }
+};
+
+template <int KIND>
+__global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
+    __shared__ PfSmem sm;
+    using LY = PfLayout<KIND>;
+    const KArgs& A = P.base;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int head = blockIdx.x;
+    const int H = A.H;
+    const int b = head / H, h = head - b * H;
+    const int lc = lane & 15, lg = lane >> 4;          // column within tile, row group
+    uint8_t* region = A.state + (size_t)head * A.region_stride;
+    const int k_hi = (KIND == WB_MIXED) ? A.k_hi : 0;
+    const size_t code_base = (size_t)k_hi * DV * 2;
+    const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV;
+    const int ub = A.bits;
+    const float ustep = 1.f / float(1 << (ub - 1));
+
+    for (int i = tid; i < DK; i += NT) sm.perm[i] = (KIND == WB_MIXED) ? int(A.perm[h * DK + i]) : i;
+
+    // ---- load and dequantize the stored state into the accumulator layout ----------
+    f32x4 S[8][2];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            float e[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rt + 4 * lg + r;
+                const int col = 32 * wave + 16 * ct + lc;
+                float x = 0.f;
+                if (KIND == WB_FP32) {
+                    x = reinterpret_cast<const float*>(region)[row * DV + col];
+                } else if (KIND == WB_UNIFORM) {
+                    const int bit = (row * DV + col) * ub;
+                    const uint32_t byte = region[bit >> 3];
+                    int kap = int((byte >> (bit & 7)) & ((1u << ub) - 1));
+                    if (kap >= (1 << (ub - 1))) kap -= (1 << ub);
+                    x = float(kap) * ustep;
+                } else if (KIND == WB_MIXED && row < k_hi) {
+                    x = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(region)[row * DV + col]);
+                } else {
+                    const int qrow = row - k_hi;
+                    const uint32_t code = region[code_base + (size_t)qrow * DV + col];
+                    const uint32_t sz = *reinterpret_cast<const uint32_t*>(
+                        region + meta_base + ((size_t)qrow * (DV / 32) + col / 32) * 4);
+                    x = f16_bits_to_f32(sz >> 16) + float(code) * f16_bits_to_f32(sz & 0xFFFFu);
+                }
+                e[r] = x;
+            }
+            S[rt][ct] = f32x4{e[0], e[1], e[2], e[3]};
+        }
+    __syncthreads();
+
+    const int T = P.T;
+    int t = 0;
+    while (t < T) {
+        // segment: up to SEG tokens, ending at the next write-back point or the last token
+        const int to_wb = P.C - int((t) % P.C);
+        int L = SEG < to_wb ? SEG : to_wb;
+        if (L > T - t) L = T - t;
+        const bool write_back = ((t + L) % P.C == 0) || (t + L == T);
+
+        // ---- stage inputs (physical row order) and the decay products ---------------
+        for (int i = tid; i < SEG * DV; i += NT) {
+            const int tt = i / DV, j = i - tt * DV;
+            sm.v[tt][j] = tt < L ? bf16f(P.v[(((size_t)b * T + t + tt) * H + h) * DV + j]) : 0.f;
+        }
+        if (tid < SEG) sm.beta[tid] = tid < L ? P.beta[((size_t)b * T + t + tid) * H + h] : 0.f;
+        if (tid < DK) {
+            const int p = tid, lr = sm.perm[p];
+            float g[SEG], kk[SEG], qq[SEG];
+            float acc = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < SEG; ++tt) {
+                if (tt < L) {
+                    const size_t base = ((size_t)b * T + t + tt) * H + h;
+                    const float sv = A.s_per_row ? P.s[base * DK + lr] : P.s[base];
+                    acc += sv;
+                    kk[tt] = bf16f(P.k[base * DK + lr]);
+                    qq[tt] = bf16f(P.q[base * DK + lr]);
+                } else {
+                    kk[tt] = 0.f;
+                    qq[tt] = 0.f;
+                }
+                g[tt] = acc;
+            }
+            const float gL = g[L - 1];
+#pragma unroll
+            for (int tt = 0; tt < SEG; ++tt) {
+                const float dec = expf(-g[tt]);
+                sm.khat[tt][p] = kk[tt] * dec;
+                sm.qhat[tt][p] = qq[tt] * dec;
+                sm.kbar[tt][p] = kk[tt] * expf(g[tt]);
+                sm.kbarL[tt][p] = kk[tt] * expf(g[tt] - gL);
+            }
+            sm.gl[p] = expf(-gL);
+        }
+        __syncthreads();
+        // small Gram matrices: A[t][tau] = k^_t . k-_tau (tau < t), QK[t][tau] (tau <= t)
+        if (tid < SEG * SEG) {
+            const int tt = tid / SEG, ta = tid - tt * SEG;
+            float a = 0.f, q = 0.f;
+            if (ta <= tt && tt < L) {
+                for (int i = 0; i < DK; ++i) {
+                    const float kb = sm.kbar[ta][i];
+                    a = __builtin_fmaf(sm.khat[tt][i], kb, a);
+                    q = __builtin_fmaf(sm.qhat[tt][i], kb, q);
+                }
+            }
+            sm.A[tt][ta] = (ta < tt) ? a : 0.f;
+            sm.QK[tt][ta] = q;
+        }
+
+        // ---- [k^; q^] S_0 on MFMA (16 x 32 per wave), rotated rows kept apart --------
+        f32x4 accP[2], accQ[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            accP[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accQ[ct] = accP[ct];
+        }
+        const float* kq = &sm.khat[0][0];      // 16 x DK: khat rows then qhat rows
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = kq[lc * DK + 16 * rt + 4 * lg + r];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const float bv = (r == 0) ? S[rt][ct].x : (r == 1) ? S[rt][ct].y : (r == 2) ? S[rt][ct].z : S[rt][ct].w;
+                    if (LY::rotated(rt))
+                        accQ[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, accQ[ct], 0, 0, 0);
+                    else
+                        accP[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, accP[ct], 0, 0, 0);
+                }
+            }
+        }
+        // accumulator element (M = 4*lg + r, column 32w + 16ct + lc)
+        if (LY::ROT) {
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int col = 32 * wave + 16 * ct + lc;
+                sm.ks[4 * lg + 0][col] = accQ[ct].x;
+                sm.ks[4 * lg + 1][col] = accQ[ct].y;
+                sm.ks[4 * lg + 2][col] = accQ[ct].z;
+                sm.ks[4 * lg + 3][col] = accQ[ct].w;
+            }
+            __syncthreads();
+            // wave w transforms vectors 4w .. 4w+3 back from the rotated domain
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                const int m = 4 * wave + vv;
+                float a0 = sm.ks[m][lane], a1 = sm.ks[m][lane + 64];
+                wave_wht128(a0, a1, lane);
+                sm.ks[m][lane] = a0;
+                sm.ks[m][lane + 64] = a1;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int col = 32 * wave + 16 * ct + lc;
+                accP[ct].x += sm.ks[4 * lg + 0][col];
+                accP[ct].y += sm.ks[4 * lg + 1][col];
+                accP[ct].z += sm.ks[4 * lg + 2][col];
+                accP[ct].w += sm.ks[4 * lg + 3][col];
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int col = 32 * wave + 16 * ct + lc;
+            sm.ks[4 * lg + 0][col] = accP[ct].x;
+            sm.ks[4 * lg + 1][col] = accP[ct].y;
+            sm.ks[4 * lg + 2][col] = accP[ct].z;
+            sm.ks[4 * lg + 3][col] = accP[ct].w;
+        }
+        __syncthreads();
+
+        // ---- per column: forward solve for w, outputs o ------------------------------
+        if (tid < DV) {
+            const int j = tid;
+            float wv[SEG];
+#pragma unroll
+            for (int tt = 0; tt < SEG; ++tt) {
+                float u = sm.v[tt][j] - sm.ks[tt][j];
+#pragma unroll
+                for (int ta = 0; ta < tt; ++ta) u = __builtin_fmaf(-sm.A[tt][ta], wv[ta], u);
+                wv[tt] = sm.beta[tt] * u;
+                sm.w[tt][j] = wv[tt];
+            }
+#pragma unroll
+            for (int tt = 0; tt < SEG; ++tt) {
+                if (tt < L) {
+                    float o = sm.ks[SEG + tt][j];
+#pragma unroll
+                    for (int ta = 0; ta <= tt; ++ta) o = __builtin_fmaf(sm.QK[tt][ta], wv[ta], o);
+                    P.o[(((size_t)b * T + t + tt) * H + h) * DV + j] = o;
+                }
+            }
+        }
+        __syncthreads();
+        if (LY::ROT) {
+            // H w for the rotated rows: two vectors per wave
+#pragma unroll
+            for (int vv = 0; vv < 2; ++vv) {
+                const int m = 2 * wave + vv;
+                float a0 = sm.w[m][lane], a1 = sm.w[m][lane + 64];
+                wave_wht128(a0, a1, lane);
+                sm.hw[m][lane] = a0;
+                sm.hw[m][lane + 64] = a1;
+            }
+            __syncthreads();
+        }
+
+        // ---- S_L = Gamma_L S_0 + sum_tau (Gamma_L k-_tau) w_tau^T  (MFMA, K = 8) ------
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const float g0 = sm.gl[16 * rt + 4 * lg + 0], g1 = sm.gl[16 * rt + 4 * lg + 1];
+            const float g2 = sm.gl[16 * rt + 4 * lg + 2], g3 = sm.gl[16 * rt + 4 * lg + 3];
+            const float* wsrc = LY::rotated(rt) ? &sm.hw[0][0] : &sm.w[0][0];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x4 c = S[rt][ct];
+                c.x *= g0;
+                c.y *= g1;
+                c.z *= g2;
+                c.w *= g3;
+                const int col = 32 * wave + 16 * ct + lc;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int tok = 4 * kk + lg;
+                    const float a = sm.kbarL[tok][16 * rt + lc];
+                    const float bv = wsrc[tok * DV + col];
+                    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, c, 0, 0, 0);
+                }
+                S[rt][ct] = c;
+            }
+        }
+
+        // ---- write-back: round the register state in place ---------------------------
+        if (write_back && KIND != WB_FP32) {
+            const bool last = (t + L == T);
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * rt + 4 * lg + r;
+                    float x0 = (r == 0) ? S[rt][0].x : (r == 1) ? S[rt][0].y : (r == 2) ? S[rt][0].z : S[rt][0].w;
+                    float x1 = (r == 0) ? S[rt][1].x : (r == 1) ? S[rt][1].y : (r == 2) ? S[rt][1].z : S[rt][1].w;
+                    const int c0 = 32 * wave + lc, c1 = c0 + 16;
+                    if (KIND == WB_UNIFORM) {
+                        const float lo = -float(1 << (ub - 1)), hi = float((1 << (ub - 1)) - 1);
+                        const float k0 = fminf(fmaxf(rintf(x0 / ustep), lo), hi);
+                        const float k1 = fminf(fmaxf(rintf(x1 / ustep), lo), hi);
+                        x0 = k0 * ustep;
+                        x1 = k1 * ustep;
+                        if (last) {
+                            // bits of element (row, col) at ub*(row*DV + col); ub in {2,4,8}
+                            const uint32_t m = (1u << ub) - 1;
+                            const int b0 = (row * DV + c0) * ub, b1 = (row * DV + c1) * ub;
+                            atomicAnd(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), ~(m << (b0 & 31)));
+                            atomicOr(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), (uint32_t(int(k0)) & m) << (b0 & 31));
+                            atomicAnd(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), ~(m << (b1 & 31)));
+                            atomicOr(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), (uint32_t(int(k1)) & m) << (b1 & 31));
+                        }
+                    } else if (KIND == WB_MIXED && row < k_hi) {
+                        const uint16_t h0 = f32_to_f16_bits(x0), h1 = f32_to_f16_bits(x1);
+                        x0 = f16_bits_to_f32(h0);
+                        x1 = f16_bits_to_f32(h1);
+                        if (last) {
+                            reinterpret_cast<uint16_t*>(region)[row * DV + c0] = h0;
+                            reinterpret_cast<uint16_t*>(region)[row * DV + c1] = h1;
+                        }
+                    } else {
+                        // affine INT8 block of 32 columns = this wave's columns
+                        const float mn = dpp_min16(fminf(x0, x1));
+                        const float mx = dpp_max16(fmaxf(x0, x1));
+                        const uint16_t sb = f32_to_f16_bits(fmaxf(mx - mn, 0.f) / 255.f);
+                        const uint16_t zb = f32_to_f16_bits(mn);
+                        const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
+                        float q0 = 0.f, q1 = 0.f;
+                        if (sc > 0.f) {
+                            q0 = fminf(fmaxf(rintf((x0 - ze) / sc), 0.f), 255.f);
+                            q1 = fminf(fmaxf(rintf((x1 - ze) / sc), 0.f), 255.f);
+                        }
+                        x0 = ze + q0 * sc;
+                        x1 = ze + q1 * sc;
+                        if (last) {
+                            const int qrow = row - k_hi;
+                            region[code_base + (size_t)qrow * DV + c0] = uint8_t(q0);
+                            region[code_base + (size_t)qrow * DV + c1] = uint8_t(q1);
+                            if (lc == 0)
+                                *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + wave) * 4) =
+                                    uint32_t(sb) | (uint32_t(zb) << 16);
+                        }
+                    }
+                    if (r == 0) { S[rt][0].x = x0; S[rt][1].x = x1; }
+                    else if (r == 1) { S[rt][0].y = x0; S[rt][1].y = x1; }
+                    else if (r == 2) { S[rt][0].z = x0; S[rt][1].z = x1; }
+                    else { S[rt][0].w = x0; S[rt][1].w = x1; }
+                }
+            }
+        }
+        if (KIND == WB_FP32 && t + L == T) {
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int col = 32 * wave + 16 * ct + lc;
+                    float* dst = reinterpret_cast<float*>(region);
+                    dst[(16 * rt + 4 * lg + 0) * DV + col] = S[rt][ct].x;
+                    dst[(16 * rt + 4 * lg + 1) * DV + col] = S[rt][ct].y;
+                    dst[(16 * rt + 4 * lg + 2) * DV + col] = S[rt][ct].z;
+                    dst[(16 * rt + 4 * lg + 3) * DV + col] = S[rt][ct].w;
+                }
+        }
+        __syncthreads();
+        t += L;
+    }
+}
+
+}  // namespace
 
 hipError_t launch_prefill(const wb_layout_desc& d, const PrefillArgs& a, hipStream_t stream) {
-    (void)d;
-    (void)a;
-    (void)stream;
-    return hipErrorNotSupported;
+    if (d.dk != 128 || d.dv != 128 || d.mode != WB_RTN) return hipErrorNotSupported;
+    const dim3 grid(d.B * d.H), block(NT);
+    switch (d.kind) {
+        case WB_FP32: hipLaunchKernelGGL(prefill_kernel<WB_FP32>, grid, block, 0, stream, a); break;
+        case WB_UNIFORM: hipLaunchKernelGGL(prefill_kernel<WB_UNIFORM>, grid, block, 0, stream, a); break;
+        case WB_HAD_INT8:
+            if (d.block != 32) return hipErrorNotSupported;
+            hipLaunchKernelGGL(prefill_kernel<WB_HAD_INT8>, grid, block, 0, stream, a);
+            break;
+        case WB_MIXED:
+            if (d.block != 32 || d.k_hi != 16) return hipErrorNotSupported;
+            hipLaunchKernelGGL(prefill_kernel<WB_MIXED>, grid, block, 0, stream, a);
+            break;
+        default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace wb

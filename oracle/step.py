@@ -205,15 +205,17 @@ def allocate_region(lay: L.Layout, region, s_rows, r_rows):
 
 
 def prefill(lay: L.Layout, region, e_in, q, k, v, beta, s, t0: int, C: int, b: int, h: int,
-            perm=None):
+            perm=None, return_last=False):
     """Token-by-token prefill of one head with write-back after every C-th token of
     the call and after the last one. q, k, v, beta, s are per-token arrays for this
-    head ([T][d], [T], [T][dk] or [T]). Returns (region, e, outputs [T][dv])."""
+    head ([T][d], [T], [T][dk] or [T]). Returns (region, e, outputs [T][dv]) and, with
+    ``return_last``, the record of the last write-back (its pre-rounding values)."""
     T = len(beta)
     content = L.decode_region(lay, region)
     S = L.to_logical(lay, L.stored_values(lay, content), perm)
     e = e_in
     outs = np.zeros((T, lay.dv))
+    wb = None
     for i in range(T):
         S, outs[i] = delta_step(S, q[i], k[i], v[i], beta[i], s[i])
         if (i + 1) % C == 0 or i == T - 1:
@@ -223,4 +225,6 @@ def prefill(lay: L.Layout, region, e_in, q, k, v, beta, s, t0: int, C: int, b: i
             e = wb.e_new
             content = L.decode_region(lay, region)
             S = L.to_logical(lay, L.stored_values(lay, content), perm)
+    if return_last:
+        return region, e, outs, wb
     return region, e, outs

@@ -62,7 +62,7 @@ def _adjacent_f16(a_bits, b_bits):
     return (np.nextafter(a, b) == b) | (a == b)
 
 
-def _meta_ok(gpu_bits, orc_bits, pre, tally, what):
+def _meta_ok(gpu_bits, orc_bits, pre, tally, what, meta_rel=META_REL):
     gpu_bits = np.asarray(gpu_bits, np.uint16)
     orc_bits = np.asarray(orc_bits, np.uint16)
     tally.meta_blocks += gpu_bits.size
@@ -74,7 +74,7 @@ def _meta_ok(gpu_bits, orc_bits, pre, tally, what):
     mid = 0.5 * (gv + ov)
     pre_d = np.asarray(pre)[diff]
     adj = _adjacent_f16(gpu_bits[diff], orc_bits[diff])
-    near = np.abs(pre_d - mid) <= META_REL * np.maximum(np.abs(mid), 1e-300)
+    near = np.abs(pre_d - mid) <= meta_rel * np.maximum(np.abs(mid), 1e-300)
     good = adj & near
     tally.meta_adjacent += int(good.sum())
     if not good.all():
@@ -95,30 +95,43 @@ def check_head(lay: L.Layout, reg_in, reg_gpu, e_in, e_gpu, o_gpu, q, k, v, beta
     tally.o_worst = max(tally.o_worst, rel)
     tally.o_num += float(np.sum((o - r.o) ** 2))
     tally.o_den += float(den ** 2)
+    compare_write_back(lay, reg_in, reg_gpu, r.wb, e_in, e_gpu, t, b, h, tally)
+    return r
+
+
+def compare_write_back(lay: L.Layout, reg_in, reg_gpu, wb, e_in, e_gpu, t, b, h, tally: Tally,
+                       window=WINDOW, meta_rel=META_REL, fp32_rel=4 * 2.0 ** -24, abs_rel=None):
+    """Compare a GPU-written region with the oracle's write-back record ``wb`` of the
+    same pre-rounding values (metadata first, then codes on the GPU's grid).
+
+    With ``abs_rel`` (GPU paths whose arithmetic error is bounded relative to the row's
+    magnitude rather than to the value), a differing code is accepted when the GPU's
+    stored value lies within half a step plus abs_rel * max|row| of the oracle's value;
+    otherwise the boundary window (in steps) applies."""
+    reg_in = np.asarray(reg_in, np.uint8)[: lay.region_size()]
+    reg_gpu = np.asarray(reg_gpu, np.uint8)[: lay.region_size()]
     where = (b, h, t)
     cin = L.decode_region(lay, reg_in)
     g = L.decode_region(lay, reg_gpu)
-    X = r.wb.X
+    X = wb.X
     if lay.kind == L.FP32:
         err = np.abs(g.S32 - X)
-        tol = 4 * 2.0 ** -24 * (np.abs(X) + np.max(np.abs(X)))
+        tol = fp32_rel * (np.abs(X) + np.max(np.abs(X)))
         tally.elems += X.size
         if np.any(err > tol):
             i = np.unravel_index(np.argmax(err - tol), err.shape)
             tally.bad.append((where, "fp32 value", i, g.S32[i], X[i]))
-        return r
+        return
     override = None
+    owb = L.decode_region(lay, wb.region)
     if lay.kind in (L.HAD_INT8, L.MIXED):
-        o_scale_bits = L.decode_region(lay, r.wb.region).scale_bits
-        o_zero_bits = L.decode_region(lay, r.wb.region).zero_bits
-        _meta_ok(g.scale_bits, o_scale_bits, r.wb.meta_pre["scale"], tally, (where, "scale"))
-        _meta_ok(g.zero_bits, o_zero_bits, r.wb.meta_pre["zero"], tally, (where, "zero"))
+        _meta_ok(g.scale_bits, owb.scale_bits, wb.meta_pre["scale"], tally, (where, "scale"), meta_rel)
+        _meta_ok(g.zero_bits, owb.zero_bits, wb.meta_pre["zero"], tally, (where, "zero"), meta_rel)
         override = {"scale": g.scale, "zero": g.zero}
     elif lay.kind == L.BITALLOC:
         if not (np.array_equal(g.widths, cin.widths) and np.array_equal(g.fit, cin.fit)):
             tally.bad.append((where, "widths/fit changed by a decode step"))
-        o_delta_bits = L.decode_region(lay, r.wb.region).delta_bits
-        _meta_ok(g.delta_bits, o_delta_bits, r.wb.meta_pre["delta"], tally, (where, "delta"))
+        _meta_ok(g.delta_bits, owb.delta_bits, wb.meta_pre["delta"], tally, (where, "delta"), meta_rel)
         override = {"delta": g.delta}
     wb2 = write_back(lay, X, e_in, t, b, h, prev=cin, meta_override=override)
     req = L.decode_region(lay, wb2.region)
@@ -135,9 +148,7 @@ def check_head(lay: L.Layout, reg_in, reg_gpu, e_in, e_gpu, o_gpu, q, k, v, beta
         gc[q0:], oc[q0:] = g.codes, req.codes
         if lay.kind == L.MIXED:
             # float16 rows: codes are the bit patterns; adjacency by one float16 step
-            gb = g.hi_bits.astype(np.int64)
-            ob = req.hi_bits.astype(np.int64)
-            gc[:q0], oc[:q0] = gb, ob
+            gc[:q0], oc[:q0] = g.hi_bits.astype(np.int64), req.hi_bits.astype(np.int64)
         step = np.zeros(X.shape)
         step[q0:] = np.repeat(g.scale, lay.block, axis=1)
         if lay.kind == L.MIXED:
@@ -153,8 +164,23 @@ def check_head(lay: L.Layout, reg_in, reg_gpu, e_in, e_gpu, o_gpu, q, k, v, beta
             adj[q0:] = d[q0:] == 1
         else:
             adj = d == 1
-        near = wb2.boundary <= WINDOW
-        ok = ~diff | (adj & near)
+        if abs_rel is None:
+            near = wb2.boundary <= window
+            ok = ~diff | (adj & near)
+        else:
+            gv = L.stored_values(lay, g)
+            rowmax = np.max(np.abs(X), axis=1, keepdims=True)
+            if lay.kind == L.MIXED:
+                q0 = lay.dk - lay.int8_rows
+                a = np.abs(X[:q0])
+                r = a.astype(np.float16)
+                lower = np.where(r.astype(np.float64) <= a, r.astype(np.float64),
+                                 np.nextafter(r, np.float16(0)).astype(np.float64))
+                upper = np.where(r.astype(np.float64) >= a, r.astype(np.float64),
+                                 np.nextafter(r, np.float16(np.inf)).astype(np.float64))
+                step = step.copy()
+                step[:q0] = np.maximum(upper - lower, 2.0 ** -24)
+            ok = ~diff | (np.abs(gv - X) <= 0.5 * step * (1 + 1e-9) + abs_rel * rowmax)
         tally.mismatch += int(diff.sum())
         if not ok.all():
             idx = np.argwhere(~ok)[:3]
@@ -178,4 +204,3 @@ def check_head(lay: L.Layout, reg_in, reg_gpu, e_in, e_gpu, o_gpu, q, k, v, beta
         if np.any(err > 0):
             i = np.unravel_index(np.argmax(err), err.shape)
             tally.bad.append((where, "residual", i, eg[i], eo[i]))
-    return r
