@@ -36,7 +36,25 @@ WORKLOADS = {
     "gdn-had-int8": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
                          extra=dict(block=128)),
     "kda-fp32": dict(cfg=None, kind="fp32", B=256, H=32, per_row=True, layers=3, alloc_every=0, extra={}),
+    "kda-prefill": dict(cfg=4, kind="mixed", B=8, H=32, per_row=True, layers=1, alloc_every=0, T=8192, C=8,
+                        extra=dict(block=32, k_hi=16)),
 }
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def prefill_flops_per_segment(L=8):
+    """Float operations of one L-token segment of one head, as the prefill kernel
+    evaluates it: [k^; q^] S_0 (2L x 128 x 128), the two Gram matrices (L x L x 128),
+    the forward solve and outputs, the rank-L update and its decay scaling, and the
+    three 128-point transforms per output vector of the rotated rows."""
+    d = 128
+    contraction = 2 * (2 * L) * d * d
+    update = 2 * d * d * L + d * d
+    gram = 2 * 2 * L * L * d
+    solve = 2 * d * (L * (L - 1) // 2 + L * (L + 1) // 2) + 2 * d * L
+    transforms = (2 * L + L) * d * 7
+    mfma = contraction + update - d * d
+    return contraction + update + gram + solve + transforms, mfma
 DEFAULT = "kda-bitalloc"
 DK = DV = 128
 
@@ -168,6 +186,51 @@ def run_gpu(args, w):
             "inputs": inp}
 
 
+def run_prefill(args, w):
+    import numpy as np
+    import torch
+
+    import linear_attn_decode_amd as wb
+    from synth import device_inputs
+
+    torch.cuda.set_device(0)
+    B, H, T, C = w["B"], w["H"], w["T"], w["C"]
+    rng = np.random.default_rng(args.seed)
+    perm = np.stack([rng.permutation(DK) for _ in range(H)])
+    st = wb.WriteBackState(w["kind"], "rtn", B, H, DK, DV, w["per_row"], perm=perm, **w["extra"])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 7)
+
+    def bf16(x):
+        return x.to(torch.bfloat16).view(torch.int16)
+
+    def unit(shape):
+        x = torch.randn(shape, generator=g, device="cuda")
+        return x / x.norm(dim=-1, keepdim=True)
+
+    q = bf16(unit((B, T, H, DK)))
+    k = bf16(unit((B, T, H, DK)))
+    v = bf16(torch.randn((B, T, H, DV), generator=g, device="cuda"))
+    beta = torch.rand((B, T, H), generator=g, device="cuda")
+    s_h = device_inputs(args.seed, 1, H, DK, DV, 1, True)["s"][0]
+    s = s_h.view(1, 1, H, DK).expand(B, T, H, DK).contiguous()
+    o = torch.zeros((B, T, H, DV), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        st.prefill(q, k, v, beta, s, o, T, 64, C, 0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        st.prefill(q, k, v, beta, s, o, T, 64, C, 0)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return {"ms": ms, "wall_s": wall, "state": st, "perm": perm}
+
+
 def cpu_baseline(w, gpu, budget_s):
     """The oracle, single-threaded, on a bounded sample of the same decode work: the
     stored regions of sampled heads after the GPU warm-up, one step each."""
@@ -233,6 +296,8 @@ def main():
               f"(every head state is independent, see the design notes on sharding).", file=sys.stderr)
         sys.exit(2)
     w = WORKLOADS[args.workload]
+    if args.workload == "kda-prefill":
+        return main_prefill(args, w)
     gpu = run_gpu(args, w)
     B, H = w["B"], w["H"]
     K = args.steps
@@ -271,6 +336,33 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, gpu, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def main_prefill(args, w):
+    gpu = run_prefill(args, w)
+    B, H, T, C = w["B"], w["H"], w["T"], w["C"]
+    ms = sorted(gpu["ms"])
+    avg = sum(ms) / len(ms)
+    seg = T // 8
+    flops, mfma_flops = prefill_flops_per_segment(8)
+    total = flops * seg * B * H
+    achieved = total / (avg / 1e3) / 1e12
+    out = {
+        "metric": "chunked prefill with deferred write-back tokens/s",
+        "value": B * T / (avg / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": avg,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"kda-prefill: B={B}, H={H}, T={T}, dk=dv=128, per-row decay, mixed layout "
+                               f"(16 float16 rows + Hadamard INT8, 32-value blocks), write-back every {C} tokens",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None, "kernel": "prefill_kernel",
+                     "flops_per_launch": total, "mfma_flops_per_launch": mfma_flops * seg * B * H,
+                     "avg_launch_us": avg * 1e3},
+        "wall_s": gpu["wall_s"],
+    }
     print(json.dumps(out), flush=True)
 
 
