@@ -4,18 +4,21 @@
 // Same computation as the generic decode kernel (dequantize -> decay -> u = k^T D S ->
 // w = beta (v - u) -> S' = D S + k w^T -> o -> Delta_i = f16(f_i R_i / n_i) -> nearest
 // level -> pack), organised so that each stored element costs few vector instructions:
-//   * rows are visited in order of increasing width (a counting sort in the prologue),
-//     so the 4 rows a wavefront handles per step nearly always share one width: the
-//     unpack and pack code is specialised per width (static bit positions, aligned LDS
-//     accesses for 2/4/8-bit rows) and branches are wavefront-uniform;
-//   * per-row constants (byte offset, decayed step, offset term, k_i, q_i, f_i / n_i)
-//     are computed once per row, not once per lane;
+//   * rows are visited in order of increasing width, so the 4 rows a wavefront handles
+//     per step nearly always share one width; that width is read into a scalar register
+//     and the unpack / pack code is chosen by a scalar branch and specialised per width
+//     (static bit positions); a group of mixed widths is walked one width at a time;
+//   * the sort, the byte offsets of the rows and their ranks come from wavefront ballots
+//     (every wavefront derives them for all 128 rows, so no cross-wave scan is needed);
+//   * per-row constants (decayed step, offset term, k_i, q_i, f_i / n_i, rounding
+//     constants, byte offset, width) sit in LDS tables indexed by sorted position;
 //   * dequantize + decay is one FMA: a_i Delta_i (code - n_i) = code * (a_i Delta_i) +
 //     (-n_i a_i Delta_i);
 //   * rounding to the nearest level adds 1.5 * 2^23 + n_i in the same FMA as the scaling
 //     (x * (1/Delta) + magic rounds the exact product once, ties to even), clamps with
-//     one integer med3 on the bit pattern, and packs with shift-adds whose constant
-//     high bits are removed once per 32-bit word;
+//     one med3, and packs with shift-adds whose constant high bits are removed once per
+//     32-bit word;
+//   * row maxima use DPP integer max on the bits of |x| (ordered like the values);
 //   * the packed codes of a lane (8 elements = b bytes) go to a staging copy of the
 //     region in LDS at their final byte offset, then the region is written to HBM with
 //     16-byte stores.
@@ -26,75 +29,97 @@
 namespace wb {
 namespace {
 
-constexpr int DK = 128, DV = 128, NT = 256, NCG = 16;
+constexpr int DK = 128, DV = 128, NT = 256;
 constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
 constexpr uint32_t kMagicBits = 0x4B400000u;
 
-struct BaSmem {
-    uint32_t reg[(DK * DV + 3 * DK) / 4 + 8];  // staged region (codes, Delta, meta)
-    int order[DK];                             // physical row at sorted position
-    int off[DK];                               // byte offset of each row's codes
-    int width[DK];
-    float alpha[DK];                           // a_i * Delta_i (old)
-    float beta0[DK];                           // -n_i * a_i * Delta_i
-    float kk[DK], qq[DK];
-    float fn[DK];                              // f_i / n_i
-    float red[4][2][DV];
-    float w[DV];
-    int hist[16];
-    float qk;
+struct TabA {                                   // dequantize constants, by sorted position
+    float alpha, beta0, k, q;                   // a Delta, -n a Delta, k_i, q_i
+};
+struct TabB {                                   // requantize constants, by sorted position
+    float fn;                                   // f / n
+    uint32_t loc;                               // byte offset | width << 16 | row << 24
 };
 
-// 8 codes of `B` bits starting at byte `boff` of the staged region, as integers.
+struct BaFixed {
+    TabA ta[DK];
+    TabB tb[DK];
+    float red[2][16][DV];                      // u / p partials of the 16 row groups
+    float w[DV];
+    float qk[4];
+};
+// the staged region follows BaFixed in dynamic LDS
+constexpr int kRegOffset = (int(sizeof(BaFixed)) + 15) / 16 * 16;
+
+// f_k / n_b for fit index k (f_k = 1/4 + k/20) and width b (n_b = 2^(b-1) - 1)
+struct FnTable {
+    float v[16][9];
+    constexpr FnTable() : v() {
+        for (int k = 0; k < 16; ++k)
+            for (int b = 2; b <= 8; ++b) v[k][b] = (0.25f + 0.05f * float(k)) / float((1 << (b - 1)) - 1);
+    }
+};
+__constant__ FnTable kFn = FnTable();
+
+// The three 32-bit words of the staged region that hold a lane's 8 codes (at most 64
+// bits starting anywhere in the first word).
+struct Raw {
+    uint32_t w0, w1, w2;
+};
+__device__ __forceinline__ Raw load_raw(const uint32_t* reg, int boff) {
+    const int wi = boff >> 2;
+    return Raw{reg[wi], reg[wi + 1], reg[wi + 2]};
+}
+
+// 0x0F0F0F0F mask kept opaque, so the byte conversions below stay byte conversions
+__device__ __forceinline__ uint32_t low_nibbles(uint32_t v) {
+    uint32_t r;
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// 8 codes of `B` bits starting at bit 8 * (boff & 3) of the raw words.
 template <int B>
-__device__ __forceinline__ void unpack8(const BaSmem& sm, int boff, uint32_t code[8]) {
-    const uint8_t* bytes = reinterpret_cast<const uint8_t*>(sm.reg);
-    if constexpr (B == 2) {
-        const uint32_t v = *reinterpret_cast<const uint16_t*>(bytes + boff);
+__device__ __forceinline__ void unpack8(const Raw& raw, int boff, float code[8]) {
+    if constexpr (B == 4) {                            // 4-byte aligned
+        const uint32_t lo = low_nibbles(raw.w0), hi = low_nibbles(raw.w0 >> 4);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) code[c] = (v >> (2 * c)) & 3u;
-    } else if constexpr (B == 4) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(bytes + boff);
+        for (int c = 0; c < 4; ++c) {
+            code[2 * c] = float((lo >> (8 * c)) & 255u);
+            code[2 * c + 1] = float((hi >> (8 * c)) & 255u);
+        }
+    } else if constexpr (B == 8) {                     // 8-byte aligned
 #pragma unroll
-        for (int c = 0; c < 8; ++c) code[c] = (v >> (4 * c)) & 15u;
-    } else if constexpr (B == 8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(bytes + boff);
+        for (int c = 0; c < 4; ++c) code[c] = float((raw.w0 >> (8 * c)) & 255u);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) code[c] = (v.x >> (8 * c)) & 255u;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) code[4 + c] = (v.y >> (8 * c)) & 255u;
+        for (int c = 0; c < 4; ++c) code[4 + c] = float((raw.w1 >> (8 * c)) & 255u);
     } else {
-        // B bytes at an arbitrary byte offset: three aligned words, funnel-shifted
-        const int wi = boff >> 2, sh = (boff & 3) * 8;
-        const uint32_t w0 = sm.reg[wi], w1 = sm.reg[wi + 1], w2 = sm.reg[wi + 2];
-        const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
-        const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
+        const int sh = (boff & 3) * 8;
+        const uint32_t lo = __builtin_amdgcn_alignbit(raw.w1, raw.w0, sh);
+        const uint32_t hi = __builtin_amdgcn_alignbit(raw.w2, raw.w1, sh);
         constexpr uint32_t M = (1u << B) - 1;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const int p = c * B;
-            if (p + B <= 32) code[c] = (lo >> p) & M;
-            else if (p >= 32) code[c] = (hi >> (p - 32)) & M;
-            else code[c] = __builtin_amdgcn_alignbit(hi, lo, p) & M;
+            uint32_t v;
+            if (p + B <= 32) v = (lo >> p) & M;
+            else if (p >= 32) v = (hi >> (p - 32)) & M;
+            else v = __builtin_amdgcn_alignbit(hi, lo, p) & M;
+            code[c] = float(v);
         }
     }
 }
 
-// Round 8 values on the row grid and write the packed B-bit codes (b bytes) at byte
-// `boff` of the staging copy.
+// Round 8 values on the row grid (magic-number FMA, med3 clamp) and write the packed
+// B-bit codes (B bytes) at byte `boff` of the staging copy.
 template <int B>
-__device__ __forceinline__ void pack8_store(BaSmem& sm, int boff, const float x[8], float inv, int n) {
-    const float magic = kMagic + float(n);
-    const float hi_f = kMagic + float(2 * n);
+__device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8], float inv) {
+    constexpr float n = float((1 << (B - 1)) - 1);
     uint32_t y[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const float t = __builtin_fmaf(x[c], inv, magic);       // kMagic + n + rne(x / Delta)
-        y[c] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic, hi_f));
-    }
-    // shift-add the biased patterns, then remove the constant bias once per word
-    uint32_t w0 = 0, w1 = 0;
-    uint32_t g0 = 0, g1 = 0;
+    for (int c = 0; c < 8; ++c)
+        y[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
+    uint32_t w0 = 0, w1 = 0, g0 = 0, g1 = 0;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int p = c * B;
@@ -112,7 +137,7 @@ __device__ __forceinline__ void pack8_store(BaSmem& sm, int boff, const float x[
     }
     w0 -= g0;
     w1 -= g1;
-    uint8_t* bytes = reinterpret_cast<uint8_t*>(sm.reg);
+    uint8_t* bytes = reinterpret_cast<uint8_t*>(reg);
     if constexpr (B == 2) {
         *reinterpret_cast<uint16_t*>(bytes + boff) = uint16_t(w0);
     } else if constexpr (B == 4) {
@@ -120,251 +145,282 @@ __device__ __forceinline__ void pack8_store(BaSmem& sm, int boff, const float x[
     } else if constexpr (B == 8) {
         *reinterpret_cast<uint2*>(bytes + boff) = make_uint2(w0, w1);
     } else if constexpr (B == 6) {
-        uint16_t* h = reinterpret_cast<uint16_t*>(bytes + boff);   // 2-byte aligned
-        h[0] = uint16_t(w0);
-        h[1] = uint16_t(w0 >> 16);
-        h[2] = uint16_t(w1);
+        uint16_t* hw = reinterpret_cast<uint16_t*>(bytes + boff);   // 2-byte aligned
+        hw[0] = uint16_t(w0);
+        hw[1] = uint16_t(w0 >> 16);
+        hw[2] = uint16_t(w1);
     } else {
 #pragma unroll
         for (int i = 0; i < B; ++i) bytes[boff + i] = uint8_t(i < 4 ? (w0 >> (8 * i)) : (w1 >> (8 * (i - 4))));
     }
 }
 
-// Row maximum over the 16 lanes of a row group (DPP inside a row of 16 lanes).
-__device__ __forceinline__ float rowmax16(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // xor 1
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // xor 2
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false))); // half mirror
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false))); // mirror
+// Generic unpack / pack for a per-lane width (a group of rows of mixed widths).
+__device__ __forceinline__ void unpack8_any(const Raw& raw, int boff, int bw, float code[8]) {
+    const int sh = (boff & 3) * 8;
+    const uint32_t lo = __builtin_amdgcn_alignbit(raw.w1, raw.w0, sh);
+    const uint32_t hi = __builtin_amdgcn_alignbit(raw.w2, raw.w1, sh);
+    const uint64_t fld = uint64_t(lo) | (uint64_t(hi) << 32);
+    const uint32_t mask = (1u << bw) - 1;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) code[c] = float(uint32_t(fld >> (c * bw)) & mask);
+}
+
+__device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const float x[8], float inv) {
+    const float n = float((1 << (bw - 1)) - 1);
+    uint64_t fld = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t y =
+            __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
+        fld |= uint64_t(y - kMagicBits) << (c * bw);
+    }
+    uint8_t* bytes = reinterpret_cast<uint8_t*>(reg);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < bw) bytes[boff + i] = uint8_t(fld >> (8 * i));
+}
+
+// Unpack / pack with the width held per lane. When the lanes share one width (rows
+// handled together are adjacent in the width order, so this is the common case), the
+// width is a scalar and the specialised code is chosen by a scalar branch; otherwise
+// the generic per-lane code runs.
+__device__ __forceinline__ void unpack_rows(const Raw& raw, int boff, int bw, float code[8]) {
+    const int bu = __builtin_amdgcn_readfirstlane(bw);
+    if (__ballot(bw != bu) == 0ull) {
+        switch (bu) {
+            case 2: unpack8<2>(raw, boff, code); break;
+            case 3: unpack8<3>(raw, boff, code); break;
+            case 4: unpack8<4>(raw, boff, code); break;
+            case 5: unpack8<5>(raw, boff, code); break;
+            case 6: unpack8<6>(raw, boff, code); break;
+            case 7: unpack8<7>(raw, boff, code); break;
+            default: unpack8<8>(raw, boff, code); break;
+        }
+    } else {
+        unpack8_any(raw, boff, bw, code);
+    }
+}
+
+__device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const float x[8], float inv) {
+    const int bu = __builtin_amdgcn_readfirstlane(bw);
+    if (__ballot(bw != bu) == 0ull) {
+        switch (bu) {
+            case 2: pack8<2>(reg, boff, x, inv); break;
+            case 3: pack8<3>(reg, boff, x, inv); break;
+            case 4: pack8<4>(reg, boff, x, inv); break;
+            case 5: pack8<5>(reg, boff, x, inv); break;
+            case 6: pack8<6>(reg, boff, x, inv); break;
+            case 7: pack8<7>(reg, boff, x, inv); break;
+            default: pack8<8>(reg, boff, x, inv); break;
+        }
+    } else {
+        pack8_any(reg, boff, bw, x, inv);
+    }
+}
+
+// max over the 16 lanes of a DPP row, of non-negative floats given as bit patterns
+__device__ __forceinline__ uint32_t rowmax16_bits(uint32_t v) {
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));   // xor 1
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));   // xor 2
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));  // half mirror
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));  // mirror
     return v;
 }
 
-// One workgroup per head state. The region and the per-row inputs are fetched into
-// registers first, then written to LDS.
-template <int MODE>
-__global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A, int num_heads) {
-    __shared__ BaSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cg = lane & 15, rq = lane >> 4;            // rq: row within the wave's quad
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+}
+
+__global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
+    extern __shared__ __align__(16) uint8_t smraw[];
+    BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw);
+    uint32_t* reg = reinterpret_cast<uint32_t*>(smraw + kRegOffset);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int head = blockIdx.x;
+    const int cg = lane & 15, rq = lane >> 4;
+    uint8_t* region = A.state + (size_t)head * A.region_stride;
     const int code_bytes = DK * DV * A.bbar / 8;
-    const int total = code_bytes + 3 * DK;
-    const int nvec = (total + 15) / 16;
+    const int nvec = (code_bytes + 3 * DK) / 16;
 
+    // ---- loads: the region (staged through registers), metadata, per-row inputs ------
     uint4 pf0 = make_uint4(0, 0, 0, 0), pf1 = pf0, pf2 = pf0;
-    float pk = 0.f, pq = 0.f, ps = 0.f, pv = 0.f;
-#define WB_PREFETCH(hd)                                                                         \
-    do {                                                                                        \
-        const uint4* src_ = reinterpret_cast<const uint4*>(A.state + (size_t)(hd) * A.region_stride); \
-        if (tid < nvec) pf0 = src_[tid];                                                        \
-        if (tid + NT < nvec) pf1 = src_[tid + NT];                                              \
-        if (tid + 2 * NT < nvec) pf2 = src_[tid + 2 * NT];                                      \
-        if (tid < DK) {                                                                         \
-            const size_t vb_ = (size_t)(hd) * DK + tid;                                         \
-            pk = A.k[vb_];                                                                      \
-            pq = A.q[vb_];                                                                      \
-            ps = A.s_per_row ? A.s[vb_] : A.s[hd];                                              \
-            pv = A.v[(size_t)(hd) * DV + tid];                                                  \
-        }                                                                                       \
-    } while (0)
-    int head = blockIdx.x;
-    WB_PREFETCH(head);
-
     {
-        uint8_t* region = A.state + (size_t)head * A.region_stride;
-        __syncthreads();                              // previous head is out of LDS
-        {
-            uint4* dst = reinterpret_cast<uint4*>(sm.reg);
-            if (tid < nvec) dst[tid] = pf0;
-            if (tid + NT < nvec) dst[tid + NT] = pf1;
-            if (tid + 2 * NT < nvec) dst[tid + 2 * NT] = pf2;
-        }
-        if (tid < 16) sm.hist[tid] = 0;
-        const float kv_row = pk, qv_row = pq, s_row = ps, v_col = pv;
-        const float beta = A.beta[head];
-        __syncthreads();
-
-        // ---- per-row constants (threads 0..127 own row = tid) -----------------------
-        const uint8_t* bytes = reinterpret_cast<const uint8_t*>(sm.reg);
-        int my_w = 0;
-        if (tid < DK) {
-            const int r = tid;
-            const int meta = bytes[code_bytes + 2 * DK + r];
-            my_w = (meta & 7) + 1;
-            const int fit = meta >> 4;
-            const int n = (1 << (my_w - 1)) - 1;
-            const float dl = f16_bits_to_f32(uint32_t(bytes[code_bytes + 2 * r]) |
-                                             (uint32_t(bytes[code_bytes + 2 * r + 1]) << 8));
-            const float a = expf(-s_row);
-            sm.width[r] = my_w;
-            sm.alpha[r] = a * dl;
-            sm.beta0[r] = -float(n) * (a * dl);
-            sm.kk[r] = kv_row;
-            sm.qq[r] = qv_row;
-            sm.fn[r] = float((0.25 + double(fit) / 20.0) / double(n));
-            atomicAdd(&sm.hist[my_w], 1);
-            int incl = my_w * (DV / 8);
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int o = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += o;
-            }
-            sm.off[r] = incl - my_w * (DV / 8);
-            float pqk = qv_row * kv_row;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) pqk += __shfl_xor(pqk, d, 64);
-            if (lane == 63) sm.red[wave][0][0] = float(incl);
-            if (lane == 0) sm.red[wave][1][0] = pqk;
-        }
-        __syncthreads();
-        if (tid < DK) {
-            const int r = tid;
-            if (wave == 1) sm.off[r] += int(sm.red[0][0][0]);
-            int base = 0;
-            for (int v = 2; v < my_w; ++v) base += sm.hist[v];
-            int rank = 0;
-            for (int v = 2; v <= 8; ++v) {
-                const unsigned long long m = __ballot(my_w == v);
-                if (my_w == v) rank = __popcll(m & ((1ull << lane) - 1));
-            }
-            if (wave == 1) {
-                int c0 = 0;
-                for (int rr = 0; rr < 64; ++rr) c0 += (sm.width[rr] == my_w) ? 1 : 0;
-                rank += c0;
-            }
-            sm.order[base + rank] = r;
-            if (tid == 0) sm.qk = sm.red[0][1][0] + sm.red[1][1][0];
-        }
-        __syncthreads();
-
-        // ---- dequantize the lane's 8 rows x 8 columns; u, p partial sums ------------
-        // (the sorted-position base is re-materialised every head: keeping per-m LDS
-        // addresses live across the head loop costs registers the tile needs)
-        int pos0;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(pos0));
-        pos0 += 4 * wave + rq;
-        float x[8][8];
-        float up[8], pp[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            up[c] = 0.f;
-            pp[c] = 0.f;
-        }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int r = sm.order[16 * m + pos0];
-            const int bw = sm.width[r];
-            const int boff = sm.off[r] + cg * bw;
-            uint32_t code[8];
-            switch (bw) {
-                case 2: unpack8<2>(sm, boff, code); break;
-                case 3: unpack8<3>(sm, boff, code); break;
-                case 4: unpack8<4>(sm, boff, code); break;
-                case 5: unpack8<5>(sm, boff, code); break;
-                case 6: unpack8<6>(sm, boff, code); break;
-                case 7: unpack8<7>(sm, boff, code); break;
-                default: unpack8<8>(sm, boff, code); break;
-            }
-            const float al = sm.alpha[r], b0 = sm.beta0[r], kv = sm.kk[r], qv = sm.qq[r];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                x[m][c] = __builtin_fmaf(float(code[c]), al, b0);
-                up[c] = __builtin_fmaf(kv, x[m][c], up[c]);
-                pp[c] = __builtin_fmaf(qv, x[m][c], pp[c]);
-            }
-            __builtin_amdgcn_sched_barrier(0);       // keep one row's temporaries live at a time
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            up[c] += __shfl_xor(up[c], 16, 64);
-            up[c] += __shfl_xor(up[c], 32, 64);
-            pp[c] += __shfl_xor(pp[c], 16, 64);
-            pp[c] += __shfl_xor(pp[c], 32, 64);
-        }
-        if (rq == 0) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                sm.red[wave][0][8 * cg + c] = up[c];
-                sm.red[wave][1][8 * cg + c] = pp[c];
-            }
-        }
-        __syncthreads();
-
-        // ---- w = beta (v - u), o = p + (q . k) w ---------------------------------------
-        if (tid < DV) {
-            const int j = tid;
-            const float u = (sm.red[0][0][j] + sm.red[1][0][j]) + (sm.red[2][0][j] + sm.red[3][0][j]);
-            const float p = (sm.red[0][1][j] + sm.red[1][1][j]) + (sm.red[2][1][j] + sm.red[3][1][j]);
-            const float wj = beta * (v_col - u);
-            sm.w[j] = wj;
-            A.o[(size_t)head * DV + j] = __builtin_fmaf(sm.qk, wj, p);
-        }
-        __syncthreads();
-
-        // ---- update, row maxima ---------------------------------------------------------
-        float wv[8];
-        {
-            const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[8 * cg]);
-            const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[8 * cg + 4]);
-            wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-            wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
-        }
-        float R[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float kv = sm.kk[sm.order[16 * m + pos0]];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) x[m][c] = __builtin_fmaf(kv, wv[c], x[m][c]);
-            float mx = fmaxf(fmaxf(fabsf(x[m][0]), fabsf(x[m][1])), fabsf(x[m][2]));
-            mx = fmaxf(fmaxf(mx, fabsf(x[m][3])), fabsf(x[m][4]));
-            mx = fmaxf(fmaxf(mx, fabsf(x[m][5])), fabsf(x[m][6]));
-            R[m] = rowmax16(fmaxf(mx, fabsf(x[m][7])));
-        }
-
-        // ---- round and pack into the staging copy (every code byte is rewritten) --------
-        uint16_t* dout = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(sm.reg) + code_bytes);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int r = sm.order[16 * m + pos0];
-            const int bw = sm.width[r];
-            const int n = (1 << (bw - 1)) - 1;
-            const uint16_t dbits = f32_to_f16_bits(R[m] * sm.fn[r]);
-            const float dl = f16_bits_to_f32(dbits);
-            const float inv = dl > 0.f ? __builtin_amdgcn_rcpf(dl) : 0.f;
-            const int boff = sm.off[r] + cg * bw;
-            if (cg == 0) dout[r] = dbits;
-            switch (bw) {
-                case 2: pack8_store<2>(sm, boff, x[m], inv, n); break;
-                case 3: pack8_store<3>(sm, boff, x[m], inv, n); break;
-                case 4: pack8_store<4>(sm, boff, x[m], inv, n); break;
-                case 5: pack8_store<5>(sm, boff, x[m], inv, n); break;
-                case 6: pack8_store<6>(sm, boff, x[m], inv, n); break;
-                case 7: pack8_store<7>(sm, boff, x[m], inv, n); break;
-                default: pack8_store<8>(sm, boff, x[m], inv, n); break;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __syncthreads();
-        {
-            const int out_vec = (code_bytes + 2 * DK) / 16;
-            uint4* dst = reinterpret_cast<uint4*>(region);
-            const uint4* src = reinterpret_cast<const uint4*>(sm.reg);
-            for (int i = tid; i < out_vec; i += NT) dst[i] = src[i];
-        }
+        const uint4* src = reinterpret_cast<const uint4*>(region);
+        if (tid < nvec) pf0 = src[tid];
+        if (tid + NT < nvec) pf1 = src[tid + NT];
+        if (tid + 2 * NT < nvec) pf2 = src[tid + 2 * NT];
     }
-#undef WB_PREFETCH
+    // every wavefront reads the widths of all rows: rows lane and lane + 64
+    const uint8_t* meta = region + code_bytes + 2 * DK;
+    const int meta0 = meta[lane], meta1 = meta[lane + 64];
+    // this lane writes the table entry of row `trow` when `writer`
+    const int trow = lane + 64 * (wave >> 1);
+    const bool writer = (lane >> 5) == (wave & 1);
+    const size_t rb = (size_t)head * DK + trow;
+    const float kr = A.k[rb], qr = A.q[rb];
+    const float sr = A.s_per_row ? A.s[rb] : A.s[head];
+    const uint32_t dold = reinterpret_cast<const uint16_t*>(region + code_bytes)[trow];
+    const float vj = A.v[(size_t)head * DV + (tid & (DV - 1))];
+    const float beta = A.beta[head];
+
+    // ---- sorted positions and byte offsets from ballots --------------------------------
+    const int bw0 = (meta0 & 7) + 1, bw1 = (meta1 & 7) + 1;
+    const bool hi_half = wave >> 1;                  // table rows 64..127 (uniform)
+    const int bwt = hi_half ? bw1 : bw0;
+    int off = 0, pos = 0, before = 0, sum_lo = 0;
+#pragma unroll
+    for (int v = 2; v <= 8; ++v) {
+        const unsigned long long ma = __ballot(bw0 == v), mb = __ballot(bw1 == v);
+        const int ca = __popcll(ma), cb = __popcll(mb);
+        const int bt = lanes_below(hi_half ? mb : ma);
+        off += v * bt;
+        if (bwt == v) pos = before + (hi_half ? ca : 0) + bt;
+        before += ca + cb;
+        sum_lo += v * ca;
+    }
+    if (hi_half) off += sum_lo;
+    if (writer) {
+        const int fit = (hi_half ? meta1 : meta0) >> 4;
+        const float n = float((1 << (bwt - 1)) - 1);
+        const float ad = expf(-sr) * f16_bits_to_f32(dold);
+        sm.ta[pos] = TabA{ad, -n * ad, kr, qr};
+        sm.tb[pos] = TabB{kFn.v[fit][bwt], uint32_t(off * (DV / 8)) | (uint32_t(bwt) << 16) | (uint32_t(trow) << 24)};
+    }
+    {
+        float pq = writer ? qr * kr : 0.f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) pq += __shfl_xor(pq, d, 64);
+        if (lane == 0) sm.qk[wave] = pq;
+    }
+    {
+        uint4* dst = reinterpret_cast<uint4*>(reg);
+        if (tid < nvec) dst[tid] = pf0;
+        if (tid + NT < nvec) dst[tid + NT] = pf1;
+        if (tid + 2 * NT < nvec) dst[tid + 2 * NT] = pf2;
+    }
+    __syncthreads();
+
+    // ---- dequantize the lane's 8 rows x 8 columns; u, p partial sums ------------------
+    // The code words of row m + 1 are requested (and the location of row m + 2 read)
+    // before row m is unpacked, so their LDS latency overlaps the arithmetic.
+    auto boff_of = [&](uint32_t l) { return int(l & 0xFFFFu) + cg * int((l >> 16) & 15u); };
+    float x[8][8];
+    float up[8], pp[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        up[c] = 0.f;
+        pp[c] = 0.f;
+    }
+    uint32_t loc_cur = sm.tb[4 * wave + rq].loc;
+    uint32_t loc_next = sm.tb[16 + 4 * wave + rq].loc;
+    Raw raw_next = load_raw(reg, boff_of(loc_cur));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const Raw raw = raw_next;
+        const uint32_t loc = loc_cur;
+        if (m + 1 < 8) {
+            raw_next = load_raw(reg, boff_of(loc_next));
+            loc_cur = loc_next;
+        }
+        if (m + 2 < 8) loc_next = sm.tb[16 * (m + 2) + 4 * wave + rq].loc;
+        const TabA ta = sm.ta[16 * m + 4 * wave + rq];
+        float code[8];
+        unpack_rows(raw, boff_of(loc), int((loc >> 16) & 15u), code);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            x[m][c] = __builtin_fmaf(code[c], ta.alpha, ta.beta0);
+            up[c] = __builtin_fmaf(ta.k, x[m][c], up[c]);
+            pp[c] = __builtin_fmaf(ta.q, x[m][c], pp[c]);
+        }
+        // finish this row here (keeps the codes of one row live at a time)
+        asm volatile("" ::"v"(x[m][0]), "v"(x[m][1]), "v"(x[m][2]), "v"(x[m][3]), "v"(x[m][4]), "v"(x[m][5]),
+                     "v"(x[m][6]), "v"(x[m][7]));
+        asm volatile("" ::"v"(up[0]), "v"(up[1]), "v"(up[2]), "v"(up[3]), "v"(up[4]), "v"(up[5]), "v"(up[6]),
+                     "v"(up[7]), "v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(pp[4]), "v"(pp[5]), "v"(pp[6]),
+                     "v"(pp[7]));
+    }
+    // partials as red[q][row group][column]: a lane's 8 columns are two float4 stores
+    {
+        const int rg = 4 * wave + rq;
+        float4* u4 = reinterpret_cast<float4*>(&sm.red[0][rg][8 * cg]);
+        float4* p4 = reinterpret_cast<float4*>(&sm.red[1][rg][8 * cg]);
+        u4[0] = make_float4(up[0], up[1], up[2], up[3]);
+        u4[1] = make_float4(up[4], up[5], up[6], up[7]);
+        p4[0] = make_float4(pp[0], pp[1], pp[2], pp[3]);
+        p4[1] = make_float4(pp[4], pp[5], pp[6], pp[7]);
+    }
+    __syncthreads();
+
+    // ---- w = beta (v - u) (threads 0..127); p kept by threads 128..255 for o ----------
+    const int jq = tid >> 7, j = tid & (DV - 1);
+    float pj = 0.f;
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) acc += sm.red[jq][g][j];
+        if (jq == 0) sm.w[j] = beta * (vj - acc);
+        else pj = acc;
+    }
+    __syncthreads();
+    if (jq == 1) {
+        const float qk = (sm.qk[0] + sm.qk[1]) + (sm.qk[2] + sm.qk[3]);
+        A.o[(size_t)head * DV + j] = __builtin_fmaf(qk, sm.w[j], pj);
+    }
+
+    // ---- update and requantize into the staging copy -----------------------------------
+    float wv[8];
+    {
+        const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[8 * cg]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[8 * cg + 4]);
+        wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+        wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+    }
+    uint16_t* dout = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(reg) + code_bytes);
+    // row maxima and steps first (no branches, so the 8 rows interleave) ...
+    float inv[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int pos = 16 * m + 4 * wave + rq;
+        const float kk = sm.ta[pos].k;
+        const TabB tb = sm.tb[pos];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[m][c] = __builtin_fmaf(kk, wv[c], x[m][c]);
+        float mx = fmaxf(fmaxf(fabsf(x[m][0]), fabsf(x[m][1])), fabsf(x[m][2]));
+        mx = fmaxf(fmaxf(mx, fabsf(x[m][3])), fabsf(x[m][4]));
+        mx = fmaxf(fmaxf(mx, fabsf(x[m][5])), fabsf(x[m][6]));
+        mx = fmaxf(mx, fabsf(x[m][7]));
+        const float R = __uint_as_float(rowmax16_bits(__float_as_uint(mx)));
+        const uint16_t dbits = f32_to_f16_bits(R * tb.fn);
+        const float dl = f16_bits_to_f32(dbits);
+        // reciprocal refined by one Newton step (near correctly rounded)
+        float r = __builtin_amdgcn_rcpf(dl);
+        r = __builtin_fmaf(__builtin_fmaf(-dl, r, 1.f), r, r);
+        inv[m] = dl > 0.f ? r : 0.f;
+        if (cg == 0) dout[tb.loc >> 24] = dbits;
+    }
+    // ... then the rounding and packing, specialised per width
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const uint32_t l = sm.tb[16 * m + 4 * wave + rq].loc;
+        pack_rows(reg, boff_of(l), int((l >> 16) & 15u), x[m], inv[m]);
+    }
+    __syncthreads();
+    {
+        const int out_vec = (code_bytes + 2 * DK) / 16;
+        uint4* dst = reinterpret_cast<uint4*>(region);
+        const uint4* src = reinterpret_cast<const uint4*>(reg);
+        for (int i = tid; i < out_vec; i += NT) dst[i] = src[i];
+    }
 }
 
 }  // namespace
 
 hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-    }
-    const int heads = d.B * d.H;
-    hipLaunchKernelGGL(bitalloc_step_kernel<WB_RTN>, dim3(heads), dim3(NT), 0, stream, a, heads);
+    const size_t region = size_t(DK) * DV * d.bbar / 8 + 3 * DK;
+    const size_t smem = kRegOffset + (region + 15) / 16 * 16 + 16;
+    hipLaunchKernelGGL(bitalloc_step_kernel, dim3(d.B * d.H), dim3(NT), smem, stream, a);
     return hipGetLastError();
 }
 
