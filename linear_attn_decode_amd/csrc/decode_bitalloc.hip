@@ -252,47 +252,53 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         if (tid + NT < nvec) pf1 = src[tid + NT];
         if (tid + 2 * NT < nvec) pf2 = src[tid + 2 * NT];
     }
-    // every wavefront reads the widths of all rows: rows lane and lane + 64
-    const uint8_t* meta = region + code_bytes + 2 * DK;
-    const int meta0 = meta[lane], meta1 = meta[lane + 64];
-    // this lane writes the table entry of row `trow` when `writer`
-    const int trow = lane + 64 * (wave >> 1);
-    const bool writer = (lane >> 5) == (wave & 1);
-    const size_t rb = (size_t)head * DK + trow;
-    const float kr = A.k[rb], qr = A.q[rb];
-    const float sr = A.s_per_row ? A.s[rb] : A.s[head];
-    const uint32_t dold = reinterpret_cast<const uint16_t*>(region + code_bytes)[trow];
     const float vj = A.v[(size_t)head * DV + (tid & (DV - 1))];
     const float beta = A.beta[head];
 
-    // ---- sorted positions and byte offsets from ballots --------------------------------
-    const int bw0 = (meta0 & 7) + 1, bw1 = (meta1 & 7) + 1;
-    const bool hi_half = wave >> 1;                  // table rows 64..127 (uniform)
-    const int bwt = hi_half ? bw1 : bw0;
-    int off = 0, pos = 0, before = 0, sum_lo = 0;
+    // ---- per-row tables: wavefronts 0 and 1 own rows lane and lane + 64 ---------------
+    // The width order, the byte offsets and the ranks come from ballots over the width
+    // bytes of all 128 rows, which both wavefronts read.
+    if (wave < 2) {
+        const uint8_t* meta = region + code_bytes + 2 * DK;
+        const int meta0 = meta[lane], meta1 = meta[lane + 64];
+        const int trow = lane + 64 * wave;
+        const size_t rb = (size_t)head * DK + trow;
+        const float kr = A.k[rb], qr = A.q[rb];
+        const float sr = A.s_per_row ? A.s[rb] : A.s[head];
+        const uint32_t dold = reinterpret_cast<const uint16_t*>(region + code_bytes)[trow];
+        const int bw0 = (meta0 & 7) + 1, bw1 = (meta1 & 7) + 1;
+        const bool hi_half = wave == 1;
+        const int bwt = hi_half ? bw1 : bw0;
+        int off = 0, pos = 0, before = 0, sum_lo = 0;
 #pragma unroll
-    for (int v = 2; v <= 8; ++v) {
-        const unsigned long long ma = __ballot(bw0 == v), mb = __ballot(bw1 == v);
-        const int ca = __popcll(ma), cb = __popcll(mb);
-        const int bt = lanes_below(hi_half ? mb : ma);
-        off += v * bt;
-        if (bwt == v) pos = before + (hi_half ? ca : 0) + bt;
-        before += ca + cb;
-        sum_lo += v * ca;
-    }
-    if (hi_half) off += sum_lo;
-    if (writer) {
+        for (int v = 2; v <= 8; ++v) {
+            const unsigned long long ma = __ballot(bw0 == v), mb = __ballot(bw1 == v);
+            const int ca = __popcll(ma), cb = __popcll(mb);
+            const int bt = lanes_below(hi_half ? mb : ma);
+            off += v * bt;
+            if (bwt == v) pos = before + (hi_half ? ca : 0) + bt;
+            before += ca + cb;
+            sum_lo += v * ca;
+        }
+        if (hi_half) off += sum_lo;
         const int fit = (hi_half ? meta1 : meta0) >> 4;
         const float n = float((1 << (bwt - 1)) - 1);
         const float ad = expf(-sr) * f16_bits_to_f32(dold);
         sm.ta[pos] = TabA{ad, -n * ad, kr, qr};
         sm.tb[pos] = TabB{kFn.v[fit][bwt], uint32_t(off * (DV / 8)) | (uint32_t(bwt) << 16) | (uint32_t(trow) << 24)};
-    }
-    {
-        float pq = writer ? qr * kr : 0.f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) pq += __shfl_xor(pq, d, 64);
-        if (lane == 0) sm.qk[wave] = pq;
+        // q . k over the wavefront's 64 rows: DPP sums inside each row of 16 lanes, then
+        // the four row sums
+        float pq = qr * kr;
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0xB1, 0xF, 0xF, false));
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x4E, 0xF, 0xF, false));
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x141, 0xF, 0xF, false));
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x140, 0xF, 0xF, false));
+        // (read the row sums with every lane active; only the store is predicated)
+        const float qsum = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 0)) +
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 16))) +
+                           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 32)) +
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 48)));
+        if (lane == 0) sm.qk[wave] = qsum;
     }
     {
         uint4* dst = reinterpret_cast<uint4*>(reg);
@@ -365,7 +371,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     }
     __syncthreads();
     if (jq == 1) {
-        const float qk = (sm.qk[0] + sm.qk[1]) + (sm.qk[2] + sm.qk[3]);
+        const float qk = sm.qk[0] + sm.qk[1];
         A.o[(size_t)head * DV + j] = __builtin_fmaf(qk, sm.w[j], pj);
     }
 
