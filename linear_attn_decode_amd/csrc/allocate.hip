@@ -11,8 +11,13 @@
 //   fit: f_k = 1/4 + k/20, Delta_k = f16(f_k R_i / n_i), the smallest squared rounding
 //   error wins, ties to the larger f;
 //   repack: the stored values rounded to nearest on the new grid, new prefix offsets.
-// Everything that decides a width or a fit index runs in float64; the pass is rare
-// (every 64 tokens in the decay-aware decode study), so it favours exactness.
+// Widths are decided in float64. The stored values are exact in float32 (|kappa| <=
+// 127 times a float16 step), the 16 candidate steps per row come from float64 exactly
+// as defined, and the candidates' squared errors are summed in float32: an element
+// whose rounding is a near-tie contributes (almost) the same error either way, so
+// only errors within ~1e-7 of each other can be ordered differently. The rounding that
+// is stored (the repack) is exact: float32 where the quotient is clear of a
+// half-integer, float64 division otherwise.
 #include "wb_device.hpp"
 #include "wb_kernels.hpp"
 
@@ -20,32 +25,72 @@ namespace wb {
 namespace {
 
 constexpr int DK = 128, DV = 128, NT = 256, NCG = 16, RS = 16;
+constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
 
 struct AllocSmem {
     uint32_t reg[(DK * DV + 3 * DK) / 4 + 4];
     int width[DK], fit[DK], off[DK], newoff[DK];
     float delta[DK];
     double R[DK], c[DK];
+    float2 cand[DK][16];                       // (Delta_k, 1 / Delta_k) per row and fit index
     int newwidth[DK];
     int newfit[DK];
     uint16_t newdelta[DK];
 };
 
-__device__ __forceinline__ void argbest(double& val, int& idx, bool want_max) {
-    // wave-wide arg-max (or arg-min) with ties to the lower index
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const double ov = __shfl_xor(val, d, 64);
-        const int oi = __shfl_xor(idx, d, 64);
-        const bool better = want_max ? (ov > val || (ov == val && oi < idx)) : (ov < val || (ov == val && oi < idx));
-        if (better) {
-            val = ov;
-            idx = oi;
-        }
+// sum over the 16 lanes of a DPP row (the 16 column groups of one state row)
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // xor 1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // xor 2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // mirror
+    return v;
+}
+
+// wave-wide arg-max (or arg-min) with ties to the lower index: DPP inside each row of
+// 16 lanes, then the four row winners; every lane must be active. The result is the
+// same in every lane.
+__device__ __forceinline__ bool better_than(double ov, int oi, double v, int i, bool want_max) {
+    return want_max ? (ov > v || (ov == v && oi < i)) : (ov < v || (ov == v && oi < i));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argbest_step(double& val, int& idx, bool want_max) {
+    const uint64_t b = __double_as_longlong(val);
+    const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, idx, CTRL, 0xF, 0xF, false);
+    const double ov = __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+    if (better_than(ov, oi, val, idx, want_max)) {
+        val = ov;
+        idx = oi;
     }
 }
 
-__global__ void __launch_bounds__(NT) allocate_kernel(const AllocArgs A) {
+__device__ __forceinline__ void argbest(double& val, int& idx, bool want_max) {
+    argbest_step<0xB1>(val, idx, want_max);    // xor 1
+    argbest_step<0x4E>(val, idx, want_max);    // xor 2
+    argbest_step<0x141>(val, idx, want_max);   // half mirror
+    argbest_step<0x140>(val, idx, want_max);   // mirror
+    const uint64_t b = __double_as_longlong(val);
+    double bv = 0.0;
+    int bi = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(b)), 16 * r);
+        const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(b >> 32)), 16 * r);
+        const int ri = __builtin_amdgcn_readlane(idx, 16 * r);
+        const double rv = __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+        if (r == 0 || better_than(rv, ri, bv, bi, want_max)) {
+            bv = rv;
+            bi = ri;
+        }
+    }
+    val = bv;
+    idx = bi;
+}
+
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) allocate_kernel(const AllocArgs A) {
     __shared__ AllocSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int head = blockIdx.x;
@@ -84,7 +129,7 @@ __global__ void __launch_bounds__(NT) allocate_kernel(const AllocArgs A) {
     __syncthreads();
 
     // stored values (exact in float32: |kappa| <= 127 times a float16 Delta)
-    double x[8][8];
+    float x[8][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int row = rg + RS * m;
@@ -95,16 +140,16 @@ __global__ void __launch_bounds__(NT) allocate_kernel(const AllocArgs A) {
         uint64_t fld = (uint64_t(sm.reg[wi]) | (uint64_t(sm.reg[wi + 1]) << 32)) >> sh;
         if (sh) fld |= uint64_t(sm.reg[wi + 2]) << (64 - sh);
         const float dl = sm.delta[row];
-        double R = 0.0;
+        float R = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const int kap = int((fld >> (c * bw)) & ((1ull << bw) - 1)) - n;
-            x[m][c] = double(float(kap) * dl);
-            R = fmax(R, fabs(x[m][c]));
+            x[m][c] = float(kap) * dl;
+            R = fmaxf(R, fabsf(x[m][c]));
         }
 #pragma unroll
-        for (int d = 1; d < NCG; d <<= 1) R = fmax(R, __shfl_xor(R, d, 64));
-        if (cg == 0) sm.R[row] = R;
+        for (int d = 1; d < NCG; d <<= 1) R = fmaxf(R, __shfl_xor(R, d, 64));
+        if (cg == 0) sm.R[row] = double(R);
     }
     __syncthreads();
 
@@ -141,12 +186,14 @@ __global__ void __launch_bounds__(NT) allocate_kernel(const AllocArgs A) {
             b0 = int(fmin(fmax(rint(bs0), double(A.bmin)), double(A.bmax)));
             b1 = int(fmin(fmax(rint(bs1), double(A.bmin)), double(A.bmax)));
             const int target = A.bbar * DK;
-            for (int iter = 0; iter < 4 * DK * 8; ++iter) {   // each pass moves one bit toward the budget
-                int tot = b0 + b1;
+            int tot = b0 + b1;
 #pragma unroll
-                for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d, 64);
-                if (tot == target) break;
-                const bool grow = tot < target;
+            for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d, 64);
+            // each pass moves one bit toward the budget (there is always a row that can
+            // move: bmin * dk <= target <= bmax * dk)
+            const bool grow = tot < target;
+            const int moves = grow ? target - tot : tot - target;
+            for (int iter = 0; iter < moves; ++iter) {
                 double v0, v1;
                 if (grow) {
                     v0 = b0 < A.bmax ? (0.75 * c0) * exp2(-2.0 * b0) : -INFINITY;
@@ -183,6 +230,13 @@ __global__ void __launch_bounds__(NT) allocate_kernel(const AllocArgs A) {
     }
     __syncthreads();
 
+    // candidate steps: thread t fills fit index t % 16 of rows t / 16 + 16 m
+    for (int i = tid; i < DK * 16; i += NT) {
+        const int row = i >> 4, kf = i & 15;
+        const int n = (1 << (sm.newwidth[row] - 1)) - 1;
+        const float d = f16_bits_to_f32(f64_to_f16_bits((0.25 + kf / 20.0) * sm.R[row] / n));
+        sm.cand[row][kf] = make_float2(d, d > 0.f ? 1.f / d : 0.f);
+    }
     // clipping fit and repack
     for (int i = tid; i < code_bytes / 4; i += NT) sm.reg[i] = 0u;
     __syncthreads();
@@ -191,41 +245,49 @@ __global__ void __launch_bounds__(NT) allocate_kernel(const AllocArgs A) {
         const int row = rg + RS * m;
         const int bw = sm.newwidth[row];
         const int n = (1 << (bw - 1)) - 1;
-        const double R = sm.R[row];
-        double err[16];
+        const float lo = kMagic - float(n), hi = kMagic + float(n);
+        float err[16];
 #pragma unroll
         for (int kf = 0; kf < 16; ++kf) {
-            const double d = double(__half2float(__ushort_as_half(f64_to_f16_bits((0.25 + kf / 20.0) * R / n))));
-            double e = 0.0;
+            const float2 dk = sm.cand[row][kf];
+            float e = 0.f;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                double kap = 0.0;
-                if (d != 0.0) kap = fmin(fmax(rint(x[m][c] / d), double(-n)), double(n));
-                const double r = x[m][c] - d * kap;
-                e += r * r;
+                const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[m][c], dk.y, kMagic), lo, hi);
+                const float r = __builtin_fmaf(-dk.x, y - kMagic, x[m][c]);
+                e = __builtin_fmaf(r, r, e);
             }
-#pragma unroll
-            for (int dd = 1; dd < NCG; dd <<= 1) e += __shfl_xor(e, dd, 64);
-            err[kf] = e;
+            err[kf] = row16_sum(e);
         }
         int best = 15;
+        float be = err[15];
 #pragma unroll
-        for (int kf = 14; kf >= 0; --kf)
-            if (err[kf] < err[best]) best = kf;
-        const uint16_t dbits = f64_to_f16_bits((0.25 + best / 20.0) * R / n);
-        const double d = double(f16_bits_to_f32(dbits));
+        for (int kf = 14; kf >= 0; --kf)     // ties go to the larger f
+            if (err[kf] < be) {
+                be = err[kf];
+                best = kf;
+            }
+        const float2 dk = sm.cand[row][best];
+        const uint16_t dbits = f32_to_f16_bits(dk.x);
         uint64_t fld = 0;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            double kap = 0.0;
-            if (d != 0.0) kap = fmin(fmax(rint(x[m][c] / d), double(-n)), double(n));
+            // nearest level, ties to even, of the exact quotient x / Delta
+            float kap = 0.f;
+            if (dk.x != 0.f) {
+                const float t = x[m][c] * dk.y;
+                kap = rintf(t);
+                if (fabsf(fabsf(t - kap) - 0.5f) <= 0x1.0p-10f)
+                    kap = float(rint(double(x[m][c]) / double(dk.x)));
+                kap = fminf(fmaxf(kap, float(-n)), float(n));
+            }
             fld |= uint64_t(int(kap) + n) << (c * bw);
         }
         const int off = sm.newoff[row] + cg * bw;
         const int wi = off >> 2, sh = (off & 3) * 8;
-        const uint64_t lo = fld << sh;
-        atomicOr(&sm.reg[wi], uint32_t(lo));
-        atomicOr(&sm.reg[wi + 1], uint32_t(lo >> 32));
+        const uint64_t lo64 = fld << sh;
+        atomicOr(&sm.reg[wi], uint32_t(lo64));
+        atomicOr(&sm.reg[wi + 1], uint32_t(lo64 >> 32));
         if (sh) {
             const uint32_t top = uint32_t(fld >> (64 - sh));
             if (top) atomicOr(&sm.reg[wi + 2], top);
