@@ -587,8 +587,12 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
         case WB_UNIFORM:
             return small ? launch_op<WB_UNIFORM, 16, 16>(op, d.mode, a, heads, stream)
                          : launch_op<WB_UNIFORM, 128, 128>(op, d.mode, a, heads, stream);
-        case WB_HAD_INT8: return launch_op<WB_HAD_INT8, 128, 128>(op, d.mode, a, heads, stream);
-        case WB_MIXED: return launch_op<WB_MIXED, 128, 128>(op, d.mode, a, heads, stream);
+        case WB_HAD_INT8:
+            if (op == OP_STEP && rot_step_supported(d)) return launch_rot_step(d, a, stream);
+            return launch_op<WB_HAD_INT8, 128, 128>(op, d.mode, a, heads, stream);
+        case WB_MIXED:
+            if (op == OP_STEP && rot_step_supported(d)) return launch_rot_step(d, a, stream);
+            return launch_op<WB_MIXED, 128, 128>(op, d.mode, a, heads, stream);
         default:
             if (op == OP_STEP && d.mode == WB_RTN) return launch_bitalloc_step(d, a, stream);
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);

@@ -1,0 +1,297 @@
+// Decode write-back step of the Hadamard-rotated layouts, round to nearest: HAD_INT8
+// (every row in the rotated domain, per-block affine INT8) and MIXED (the first k_hi
+// physical rows in float16, the rest Hadamard INT8, rows permuted per head).
+// [DAMP] "Implementation" (reconstruct, update, re-quantize, write back), "Key
+// Points" (transform along the value dimension); [LBRS] "Accumulated readout error".
+//
+// Same computation as the generic decode kernel (rotated domain: u = sum_P k a S +
+// H sum_Q k a Y, w = beta (v - u), S_P' = a S_P + k w, Y_Q' = a Y_Q + k (H w),
+// o = sum_P q a S + H sum_Q q a Y + (q . k) w), organised for throughput:
+//   * the region is staged in LDS with 16-byte loads, updated there, and written back
+//     with 16-byte stores;
+//   * u and p (contractions over rows) run column-parallel: thread (j, half) walks
+//     half of the rows of column j, so the only cross-thread step is adding two
+//     halves; the float64 step and offset of every INT8 block are tabulated once;
+//   * the three 128-point transforms (H uQ, H pQ, H w) run on one wavefront;
+//   * the update and the requantization run row-parallel (lane = 8 rows x 8 columns)
+//     with float64 element arithmetic and the block minimum / maximum by DPP;
+//   * float64 -> float16 goes through float32 rounded to odd, then the hardware
+//     conversion: rounding to odd at 24 bits followed by a rounding to 11 bits gives
+//     the correctly rounded result (Boldo & Melquiond, IEEE Trans. Computers 2008).
+// Float64 is used wherever a stored code or float16 value is decided: the codes must
+// agree with a float64 evaluation to within 1e-5 of a step, and float16 rows to within
+// 1e-5 of a float16 spacing.
+#include "wb_device.hpp"
+#include "wb_kernels.hpp"
+
+namespace wb {
+namespace {
+
+constexpr int DK = 128, DV = 128, NT = 256;
+constexpr double kInvSqrt128 = 0.08838834764831844055;
+
+template <int KHI, int BLOCK>
+struct RotLayout {
+    static constexpr int NQ = DK - KHI;                     // INT8 rows
+    static constexpr int NB = DV / BLOCK;                   // blocks per INT8 row
+    static constexpr int CODE_BASE = KHI * DV * 2;
+    static constexpr int META_BASE = CODE_BASE + NQ * DV;
+    static constexpr int REGION = META_BASE + NQ * NB * 4;  // bytes (a multiple of 16)
+    static_assert(REGION % 16 == 0, "region must be a whole number of 16-byte words");
+};
+
+template <int KHI, int BLOCK>
+struct RotSmem {
+    using LY = RotLayout<KHI, BLOCK>;
+    double2 kq[DK];                  // (k a, q a) per physical row
+    double2 ak[DK];                  // (a, k)
+    double2 sz[LY::NQ * LY::NB];     // float64 (step, offset) of every INT8 block
+    double part[4][DV];              // (uP, pP, uQ, pQ) of the second half, then the sums
+    double w[DV], hw[DV];
+    double qk[2];
+    uint32_t reg[LY::REGION / 4];
+};
+
+__device__ __forceinline__ uint16_t f64_to_f16_rto(double x) {
+    const float f = float(x);
+    uint32_t fb = __float_as_uint(f);
+    const double back = double(f);
+    if (back != x) {
+        if (fabs(back) > fabs(x)) fb -= 1u;   // one step toward zero: the truncation
+        fb |= 1u;                             // sticky bit: round to odd
+    }
+    return __half_as_ushort(__float2half_rn(__uint_as_float(fb)));
+}
+
+__device__ __forceinline__ double f16_to_f64(uint32_t bits) { return double(f16_bits_to_f32(bits)); }
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __double_as_longlong(v);
+    const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false));
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+// min and max over the lanes of one block (BLOCK / 8 consecutive lanes of a DPP row)
+template <int BLOCK>
+__device__ __forceinline__ void block_minmax(double& mn, double& mx) {
+    mn = fmin(mn, dpp_f64<0xB1>(mn));     // xor 1
+    mx = fmax(mx, dpp_f64<0xB1>(mx));
+    mn = fmin(mn, dpp_f64<0x4E>(mn));     // xor 2
+    mx = fmax(mx, dpp_f64<0x4E>(mx));
+    if constexpr (BLOCK == 128) {
+        mn = fmin(mn, dpp_f64<0x141>(mn));    // half mirror
+        mx = fmax(mx, dpp_f64<0x141>(mx));
+        mn = fmin(mn, dpp_f64<0x140>(mn));    // mirror
+        mx = fmax(mx, dpp_f64<0x140>(mx));
+    }
+}
+
+// 128-point orthonormal transform of a vector held by one wavefront (lane l holds
+// elements l and l + 64)
+__device__ __forceinline__ void wht128(double& a0, double& a1, int lane) {
+    double x = a0 + a1, y = a0 - a1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const double ox = __shfl_xor(x, d, 64), oy = __shfl_xor(y, d, 64);
+        x = (lane & d) ? (ox - x) : (x + ox);
+        y = (lane & d) ? (oy - y) : (y + oy);
+    }
+    a0 = x * kInvSqrt128;
+    a1 = y * kInvSqrt128;
+}
+
+template <int KHI, int BLOCK>
+__global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
+    using LY = RotLayout<KHI, BLOCK>;
+    __shared__ RotSmem<KHI, BLOCK> sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int head = blockIdx.x;
+    const int h = head % A.H;
+    uint8_t* region = A.state + (size_t)head * A.region_stride;
+    uint8_t* lb = reinterpret_cast<uint8_t*>(sm.reg);
+
+    // ---- stage the region; per-row tables in physical row order -----------------------
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(region);
+        uint4* dst = reinterpret_cast<uint4*>(sm.reg);
+#pragma unroll
+        for (int i = tid; i < LY::REGION / 16; i += NT) dst[i] = src[i];
+    }
+    if (wave < 2) {
+        const int p = tid;
+        const int lr = KHI > 0 ? int(A.perm[h * DK + p]) : p;
+        const double kd = double(A.k[(size_t)head * DK + lr]);
+        const double qd = double(A.q[(size_t)head * DK + lr]);
+        const float sv = A.s_per_row ? A.s[(size_t)head * DK + lr] : A.s[head];
+        const double ad = exp(-double(sv));
+        sm.kq[p] = make_double2(kd * ad, qd * ad);
+        sm.ak[p] = make_double2(ad, kd);
+        double pq = qd * kd;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) pq += __shfl_xor(pq, d, 64);
+        if (lane == 0) sm.qk[wave] = pq;
+    }
+    __syncthreads();
+    for (int i = tid; i < LY::NQ * LY::NB; i += NT) {
+        const uint32_t m = sm.reg[LY::META_BASE / 4 + i];
+        sm.sz[i] = make_double2(f16_to_f64(m & 0xFFFFu), f16_to_f64(m >> 16));
+    }
+    __syncthreads();
+
+    // ---- u, p: thread (j, half) sums half of the rows of column j -----------------------
+    {
+        const int j = tid & (DV - 1), half = tid >> 7;
+        double uP = 0.0, pP = 0.0, uQ = 0.0, pQ = 0.0;
+        if constexpr (KHI > 0) {
+            const uint16_t* f16rows = reinterpret_cast<const uint16_t*>(lb);
+#pragma unroll 4
+            for (int p = half * (KHI / 2); p < (half + 1) * (KHI / 2); ++p) {
+                const double x = f16_to_f64(f16rows[p * DV + j]);
+                const double2 c = sm.kq[p];
+                uP = fma(c.x, x, uP);
+                pP = fma(c.y, x, pP);
+            }
+        }
+        const int g = j / BLOCK;
+#pragma unroll 4
+        for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
+            const double2 s = sm.sz[qr * LY::NB + g];
+            const double y = fma(double(lb[LY::CODE_BASE + qr * DV + j]), s.x, s.y);
+            const double2 c = sm.kq[qr + KHI];
+            uQ = fma(c.x, y, uQ);
+            pQ = fma(c.y, y, pQ);
+        }
+        if (half == 1) {
+            sm.part[0][j] = uP;
+            sm.part[1][j] = pP;
+            sm.part[2][j] = uQ;
+            sm.part[3][j] = pQ;
+        }
+        __syncthreads();
+        if (half == 0) {
+            sm.part[0][j] += uP;
+            sm.part[1][j] += pP;
+            sm.part[2][j] += uQ;
+            sm.part[3][j] += pQ;
+        }
+        __syncthreads();
+    }
+
+    // ---- w = beta (v - u), o = p + (q . k) w, H w (one wavefront) ----------------------
+    if (wave == 0) {
+        double uq0 = sm.part[2][lane], uq1 = sm.part[2][lane + 64];
+        double pq0 = sm.part[3][lane], pq1 = sm.part[3][lane + 64];
+        wht128(uq0, uq1, lane);
+        wht128(pq0, pq1, lane);
+        const double qk = sm.qk[0] + sm.qk[1];
+        const double beta = double(A.beta[head]);
+        const double u0 = sm.part[0][lane] + uq0, u1 = sm.part[0][lane + 64] + uq1;
+        const double p0 = sm.part[1][lane] + pq0, p1 = sm.part[1][lane + 64] + pq1;
+        const double w0 = beta * (double(A.v[(size_t)head * DV + lane]) - u0);
+        const double w1 = beta * (double(A.v[(size_t)head * DV + lane + 64]) - u1);
+        A.o[(size_t)head * DV + lane] = float(p0 + qk * w0);
+        A.o[(size_t)head * DV + lane + 64] = float(p1 + qk * w1);
+        sm.w[lane] = w0;
+        sm.w[lane + 64] = w1;
+        double r0 = w0, r1 = w1;
+        wht128(r0, r1, lane);
+        sm.hw[lane] = r0;
+        sm.hw[lane + 64] = r1;
+    }
+    __syncthreads();
+
+    // ---- update and requantize in place (lane = 8 rows x 8 columns) --------------------
+    {
+        const int rg = tid >> 4, cg = tid & 15;
+        double hwv[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) hwv[c] = sm.hw[8 * cg + c];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int p = rg + 16 * m;
+            const double2 ak = sm.ak[p];
+            if (KHI > 0 && m == 0) {
+                // float16 row (p < 16 <= k_hi): original domain, w itself
+                uint4* ptr = reinterpret_cast<uint4*>(lb + (p * DV + 8 * cg) * 2);
+                const uint4 raw = *ptr;
+                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+                uint32_t o4[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const double x = f16_to_f64((w4[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu);
+                    const double xn = fma(ak.x, x, ak.y * sm.w[8 * cg + c]);
+                    o4[c >> 1] |= uint32_t(f64_to_f16_rto(xn)) << ((c & 1) * 16);
+                }
+                *ptr = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+                continue;
+            }
+            const int qr = p - KHI;
+            const int g = (8 * cg) / BLOCK;
+            uint2* ptr = reinterpret_cast<uint2*>(lb + LY::CODE_BASE + qr * DV + 8 * cg);
+            const uint2 raw = *ptr;
+            const double2 s = sm.sz[qr * LY::NB + g];
+            double y[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t code = ((c < 4 ? raw.x : raw.y) >> ((c & 3) * 8)) & 0xFFu;
+                y[c] = fma(ak.x, fma(double(code), s.x, s.y), ak.y * hwv[c]);
+            }
+            double mn = y[0], mx = y[0];
+#pragma unroll
+            for (int c = 1; c < 8; ++c) {
+                mn = fmin(mn, y[c]);
+                mx = fmax(mx, y[c]);
+            }
+            block_minmax<BLOCK>(mn, mx);
+            const uint16_t sbits = f64_to_f16_rto(fmax(mx - mn, 0.0) / 255.0);
+            const uint16_t zbits = f64_to_f16_rto(mn);
+            const double scale = f16_to_f64(sbits), zero = f16_to_f64(zbits);
+            uint32_t lo4 = 0, hi4 = 0;
+            if (scale != 0.0) {
+                const double inv = 1.0 / scale;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const double kf = fmin(fmax(rint((y[c] - zero) * inv), 0.0), 255.0);
+                    const uint32_t code = uint32_t(kf);
+                    if (c < 4) lo4 |= code << (c * 8);
+                    else hi4 |= code << ((c - 4) * 8);
+                }
+            }
+            *ptr = make_uint2(lo4, hi4);
+            if ((cg % (BLOCK / 8)) == 0)
+                sm.reg[LY::META_BASE / 4 + qr * LY::NB + g] = uint32_t(sbits) | (uint32_t(zbits) << 16);
+        }
+    }
+    __syncthreads();
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(sm.reg);
+        uint4* dst = reinterpret_cast<uint4*>(region);
+#pragma unroll
+        for (int i = tid; i < LY::REGION / 16; i += NT) dst[i] = src[i];
+    }
+}
+
+template <int KHI, int BLOCK>
+hipError_t launch_rot(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool rot_step_supported(const wb_layout_desc& d) {
+    if (d.mode != WB_RTN || d.dk != DK || d.dv != DV) return false;
+    if (d.kind == WB_HAD_INT8) return d.block == 32 || d.block == 128;
+    if (d.kind == WB_MIXED) return d.k_hi == 16 && d.block == 32;
+    return false;
+}
+
+hipError_t launch_rot_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
+    if (d.kind == WB_MIXED) return launch_rot<16, 32>(d, a, stream);
+    return d.block == 32 ? launch_rot<0, 32>(d, a, stream) : launch_rot<0, 128>(d, a, stream);
+}
+
+}  // namespace wb

@@ -39,6 +39,11 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
 // Decode step of the BITALLOC layout with round-to-nearest (the tuned kernel).
 hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
 
+// Decode step of the Hadamard-rotated layouts with round-to-nearest (the tuned kernel),
+// for the shapes rot_step_supported() accepts.
+bool rot_step_supported(const wb_layout_desc& d);
+hipError_t launch_rot_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
+
 // Fills `n` bytes at dst with the repeating `period`-byte pattern (period <= 16).
 hipError_t launch_fill(void* dst, size_t n, const uint8_t* pattern, int period, hipStream_t stream);
 
