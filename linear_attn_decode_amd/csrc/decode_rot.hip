@@ -233,11 +233,13 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             uint2* ptr = reinterpret_cast<uint2*>(lb + LY::CODE_BASE + qr * DV + 8 * cg);
             const uint2 raw = *ptr;
             const double2 s = sm.sz[qr * LY::NB + g];
+            // a (zero + code * scale) + k (H w)_c = code * (a scale) + (a zero + k (H w)_c)
+            const double as = ak.x * s.x, az = ak.x * s.y;
             double y[8];
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const uint32_t code = ((c < 4 ? raw.x : raw.y) >> ((c & 3) * 8)) & 0xFFu;
-                y[c] = fma(ak.x, fma(double(code), s.x, s.y), ak.y * hwv[c]);
+                y[c] = fma(double(code), as, fma(ak.y, hwv[c], az));
             }
             double mn = y[0], mx = y[0];
 #pragma unroll
@@ -246,18 +248,38 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                 mx = fmax(mx, y[c]);
             }
             block_minmax<BLOCK>(mn, mx);
-            const uint16_t sbits = f64_to_f16_rto(fmax(mx - mn, 0.0) / 255.0);
+            // (a product with 1/255 instead of the quotient: the two differ by at most one
+            // float64 unit, which moves a float16 rounding only at a midpoint)
+            const uint16_t sbits = f64_to_f16_rto(fmax(mx - mn, 0.0) * (1.0 / 255.0));
             const uint16_t zbits = f64_to_f16_rto(mn);
             const double scale = f16_to_f64(sbits), zero = f16_to_f64(zbits);
             uint32_t lo4 = 0, hi4 = 0;
             if (scale != 0.0) {
-                const double inv = 1.0 / scale;
+                // reciprocal of the step refined by one Newton step
+                double inv = __builtin_amdgcn_rcp(scale);
+                inv = fma(fma(-scale, inv, 1.0), inv, inv);
+                const double nz = -zero * inv;
+                // levels t = (y - zero) / scale lie within +-2^30 unless the offset is far
+                // outside the block's range (then the float64 path below is taken)
+                const double span = fmax(fabs(mx - zero), fabs(mn - zero)) * inv;
+                if (span < 1073741824.0) {
+                    // t + 1.5 * 2^52 rounds t to the nearest integer (ties to even); its
+                    // low 32 bits are that integer, clamped to [0, 255] in integer form
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const double kf = fmin(fmax(rint((y[c] - zero) * inv), 0.0), 255.0);
-                    const uint32_t code = uint32_t(kf);
-                    if (c < 4) lo4 |= code << (c * 8);
-                    else hi4 |= code << ((c - 4) * 8);
+                    for (int c = 0; c < 8; ++c) {
+                        const double r = fma(y[c], inv, nz) + 6755399441055744.0;
+                        const int kk = min(max(int(uint32_t(__double_as_longlong(r))), 0), 255);
+                        if (c < 4) lo4 |= uint32_t(kk) << (c * 8);
+                        else hi4 |= uint32_t(kk) << ((c - 4) * 8);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const double kf = fmin(fmax(rint((y[c] - zero) / scale), 0.0), 255.0);
+                        const uint32_t code = uint32_t(kf);
+                        if (c < 4) lo4 |= code << (c * 8);
+                        else hi4 |= code << ((c - 4) * 8);
+                    }
                 }
             }
             *ptr = make_uint2(lo4, hi4);
