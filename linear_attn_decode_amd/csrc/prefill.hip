@@ -93,6 +93,50 @@ struct PfLayout {
     __device__ static bool rotated(int rt) { return KIND == WB_HAD_INT8 || (KIND == WB_MIXED && rt > 0); }
 };
 
+// One segment's inputs as this thread reads them: threads 0..127 own physical row
+// `tid` (k, q and the decay of every token), every thread owns 4 values of v, and
+// threads 0..7 one beta each. Loaded a segment ahead into registers.
+struct SegIn {
+    uint16_t kk[SEG], qq[SEG];
+    float sv[SEG];
+    uint16_t vv[SEG * DV / NT];
+    float beta;
+};
+
+__device__ __forceinline__ void load_segment(const PrefillArgs& P, int b, int h, int t, int L, int tid, int lr,
+                                             SegIn& in) {
+    const KArgs& A = P.base;
+    const int H = A.H, T = P.T;
+    if (tid < DK) {
+#pragma unroll
+        for (int tt = 0; tt < SEG; ++tt) {
+            in.kk[tt] = 0;
+            in.qq[tt] = 0;
+            in.sv[tt] = 0.f;
+            if (tt < L) {
+                const size_t base = ((size_t)b * T + t + tt) * H + h;
+                in.sv[tt] = A.s_per_row ? P.s[base * DK + lr] : P.s[base];
+                in.kk[tt] = P.k[base * DK + lr];
+                in.qq[tt] = P.q[base * DK + lr];
+            }
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < SEG * DV / NT; ++n) {
+        const int i = tid + n * NT, tt = i / DV, j = i - tt * DV;
+        in.vv[n] = tt < L ? P.v[(((size_t)b * T + t + tt) * H + h) * DV + j] : uint16_t(0);
+    }
+    in.beta = (tid < SEG && tid < L) ? P.beta[((size_t)b * T + t + tid) * H + h] : 0.f;
+}
+
+// length of the segment starting at t: up to SEG tokens, ending at the next
+// write-back point or the last token
+__device__ __forceinline__ int segment_length(int t, int T, int C) {
+    const int to_wb = C - (t % C);
+    int L = SEG < to_wb ? SEG : to_wb;
+    return L > T - t ? T - t : L;
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
     __shared__ PfSmem sm;
@@ -148,63 +192,72 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
     __syncthreads();
 
     const int T = P.T;
+    const int my_lr = tid < DK ? sm.perm[tid] : 0;
+    SegIn nxt;
+    load_segment(P, b, h, 0, segment_length(0, T, P.C), tid, my_lr, nxt);
     int t = 0;
     while (t < T) {
-        // segment: up to SEG tokens, ending at the next write-back point or the last token
-        const int to_wb = P.C - int((t) % P.C);
-        int L = SEG < to_wb ? SEG : to_wb;
-        if (L > T - t) L = T - t;
+        const int L = segment_length(t, T, P.C);
         const bool write_back = ((t + L) % P.C == 0) || (t + L == T);
+        const SegIn cur = nxt;
+        if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C), tid, my_lr, nxt);
 
         // ---- stage inputs (physical row order) and the decay products ---------------
-        for (int i = tid; i < SEG * DV; i += NT) {
-            const int tt = i / DV, j = i - tt * DV;
-            sm.v[tt][j] = tt < L ? bf16f(P.v[(((size_t)b * T + t + tt) * H + h) * DV + j]) : 0.f;
+#pragma unroll
+        for (int n = 0; n < SEG * DV / NT; ++n) {
+            const int i = tid + n * NT, tt = i / DV, j = i - tt * DV;
+            sm.v[tt][j] = bf16f(cur.vv[n]);
         }
-        if (tid < SEG) sm.beta[tid] = tid < L ? P.beta[((size_t)b * T + t + tid) * H + h] : 0.f;
+        if (tid < SEG) sm.beta[tid] = cur.beta;
         if (tid < DK) {
-            const int p = tid, lr = sm.perm[p];
-            float g[SEG], kk[SEG], qq[SEG];
+            const int p = tid;
+            float g[SEG];
             float acc = 0.f;
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
-                if (tt < L) {
-                    const size_t base = ((size_t)b * T + t + tt) * H + h;
-                    const float sv = A.s_per_row ? P.s[base * DK + lr] : P.s[base];
-                    acc += sv;
-                    kk[tt] = bf16f(P.k[base * DK + lr]);
-                    qq[tt] = bf16f(P.q[base * DK + lr]);
-                } else {
-                    kk[tt] = 0.f;
-                    qq[tt] = 0.f;
-                }
+                acc += cur.sv[tt];
                 g[tt] = acc;
             }
             const float gL = g[L - 1];
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
+                const float kk = bf16f(cur.kk[tt]), qq = bf16f(cur.qq[tt]);
                 const float dec = expf(-g[tt]);
-                sm.khat[tt][p] = kk[tt] * dec;
-                sm.qhat[tt][p] = qq[tt] * dec;
-                sm.kbar[tt][p] = kk[tt] * expf(g[tt]);
-                sm.kbarL[tt][p] = kk[tt] * expf(g[tt] - gL);
+                sm.khat[tt][p] = kk * dec;
+                sm.qhat[tt][p] = qq * dec;
+                sm.kbar[tt][p] = kk * expf(g[tt]);
+                sm.kbarL[tt][p] = kk * expf(g[tt] - gL);
             }
             sm.gl[p] = expf(-gL);
         }
         __syncthreads();
-        // small Gram matrices: A[t][tau] = k^_t . k-_tau (tau < t), QK[t][tau] (tau <= t)
-        if (tid < SEG * SEG) {
-            const int tt = tid / SEG, ta = tid - tt * SEG;
+        // small Gram matrices: A[t][tau] = k^_t . k-_tau (tau < t), QK[t][tau] (tau <= t);
+        // four lanes (a DPP quad) per entry, 32 rows each
+        {
+            const int pair = tid >> 2, part = tid & 3;
+            const int tt = pair / SEG, ta = pair - tt * SEG;
             float a = 0.f, q = 0.f;
             if (ta <= tt && tt < L) {
-                for (int i = 0; i < DK; ++i) {
-                    const float kb = sm.kbar[ta][i];
-                    a = __builtin_fmaf(sm.khat[tt][i], kb, a);
-                    q = __builtin_fmaf(sm.qhat[tt][i], kb, q);
+                const float4* kh = reinterpret_cast<const float4*>(&sm.khat[tt][32 * part]);
+                const float4* qh = reinterpret_cast<const float4*>(&sm.qhat[tt][32 * part]);
+                const float4* kb = reinterpret_cast<const float4*>(&sm.kbar[ta][32 * part]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 x = kh[i], y = qh[i], z = kb[i];
+                    a = __builtin_fmaf(x.x, z.x, a); a = __builtin_fmaf(x.y, z.y, a);
+                    a = __builtin_fmaf(x.z, z.z, a); a = __builtin_fmaf(x.w, z.w, a);
+                    q = __builtin_fmaf(y.x, z.x, q); q = __builtin_fmaf(y.y, z.y, q);
+                    q = __builtin_fmaf(y.z, z.z, q); q = __builtin_fmaf(y.w, z.w, q);
                 }
             }
-            sm.A[tt][ta] = (ta < tt) ? a : 0.f;
-            sm.QK[tt][ta] = q;
+            a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false));
+            q += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(q), 0xB1, 0xF, 0xF, false));
+            a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false));
+            q += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(q), 0x4E, 0xF, 0xF, false));
+            if (part == 0) {
+                sm.A[tt][ta] = (ta < tt) ? a : 0.f;
+                sm.QK[tt][ta] = (ta <= tt) ? q : 0.f;
+            }
         }
 
         // ---- [k^; q^] S_0 on MFMA (16 x 32 per wave), rotated rows kept apart --------
@@ -375,8 +428,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                         const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
                         float q0 = 0.f, q1 = 0.f;
                         if (sc > 0.f) {
-                            q0 = fminf(fmaxf(rintf((x0 - ze) / sc), 0.f), 255.f);
-                            q1 = fminf(fmaxf(rintf((x1 - ze) / sc), 0.f), 255.f);
+                            const float inv = 1.f / sc;
+                            q0 = fminf(fmaxf(rintf((x0 - ze) * inv), 0.f), 255.f);
+                            q1 = fminf(fmaxf(rintf((x1 - ze) * inv), 0.f), 255.f);
                         }
                         x0 = ze + q0 * sc;
                         x1 = ze + q1 * sc;
