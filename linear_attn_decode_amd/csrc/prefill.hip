@@ -219,16 +219,18 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 g[tt] = acc;
             }
             const float gL = g[L - 1];
+            const float decL = expf(-gL);
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
                 const float kk = bf16f(cur.kk[tt]), qq = bf16f(cur.qq[tt]);
                 const float dec = expf(-g[tt]);
+                const float inc = __builtin_amdgcn_rcpf(dec);      // e^{g}, within an ulp or two
                 sm.khat[tt][p] = kk * dec;
                 sm.qhat[tt][p] = qq * dec;
-                sm.kbar[tt][p] = kk * expf(g[tt]);
-                sm.kbarL[tt][p] = kk * expf(g[tt] - gL);
+                sm.kbar[tt][p] = kk * inc;
+                sm.kbarL[tt][p] = kk * (inc * decL);
             }
-            sm.gl[p] = expf(-gL);
+            sm.gl[p] = decL;
         }
         __syncthreads();
         // small Gram matrices: A[t][tau] = k^_t . k-_tau (tau < t), QK[t][tau] (tau <= t);
@@ -423,14 +425,18 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                         // affine INT8 block of 32 columns = this wave's columns
                         const float mn = dpp_min16(fminf(x0, x1));
                         const float mx = dpp_max16(fmaxf(x0, x1));
-                        const uint16_t sb = f32_to_f16_bits(fmaxf(mx - mn, 0.f) / 255.f);
+                        const uint16_t sb = f32_to_f16_bits(fmaxf(mx - mn, 0.f) * (1.f / 255.f));
                         const uint16_t zb = f32_to_f16_bits(mn);
                         const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
                         float q0 = 0.f, q1 = 0.f;
                         if (sc > 0.f) {
-                            const float inv = 1.f / sc;
-                            q0 = fminf(fmaxf(rintf((x0 - ze) * inv), 0.f), 255.f);
-                            q1 = fminf(fmaxf(rintf((x1 - ze) * inv), 0.f), 255.f);
+                            // reciprocal refined by one Newton step; rounding by adding
+                            // 1.5 * 2^23 (ties to even), clamp by med3
+                            float inv = __builtin_amdgcn_rcpf(sc);
+                            inv = __builtin_fmaf(__builtin_fmaf(-sc, inv, 1.f), inv, inv);
+                            constexpr float M = 12582912.0f;
+                            q0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0 - ze, inv, M), M, M + 255.f) - M;
+                            q1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1 - ze, inv, M), M, M + 255.f) - M;
                         }
                         x0 = ze + q0 * sc;
                         x1 = ze + q1 * sc;
