@@ -16,7 +16,6 @@ of the same work (cpu_baseline).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,12 +29,13 @@ PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {
     "kda-bitalloc": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
-                         extra=dict(bbar=4, bmin=2, bmax=8)),
+                         extra=dict(bbar=4, bmin=2, bmax=8), kernel="bitalloc_step_kernel"),
     "kda-mixed": dict(cfg=2, kind="mixed", B=256, H=32, per_row=True, layers=7, alloc_every=0,
-                      extra=dict(block=32, k_hi=16)),
+                      extra=dict(block=32, k_hi=16), kernel="rot_step_kernel"),
     "gdn-had-int8": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
-                         extra=dict(block=128)),
-    "kda-fp32": dict(cfg=None, kind="fp32", B=256, H=32, per_row=True, layers=3, alloc_every=0, extra={}),
+                         extra=dict(block=128), kernel="rot_step_kernel"),
+    "kda-fp32": dict(cfg=None, kind="fp32", B=256, H=32, per_row=True, layers=3, alloc_every=0, extra={},
+                     kernel="wb_kernel"),
     "kda-prefill": dict(cfg=4, kind="mixed", B=8, H=32, per_row=True, layers=1, alloc_every=0, T=8192, C=8,
                         extra=dict(block=32, k_hi=16)),
 }
@@ -80,20 +80,13 @@ def algorithmic_bytes_per_head(kind, extra, per_row):
     return rd + wr + io
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "linear_attn_decode_amd", "csrc"))):
-        with open(os.path.join(ROOT, "linear_attn_decode_amd", "csrc", f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload):
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
+    from linear_attn_decode_amd.traffic import kernel_source_hash
     if t.get("kernel_hash") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
@@ -143,15 +136,11 @@ def run_gpu(args, w):
     counts = [0] * len(states)
     alloc_every = w["alloc_every"]
 
-    def one(i, ev=None, ev_alloc=None):
+    def one(i, ev_alloc=None):
         layer = i % len(states)
         r = i % R
         st = states[layer]
-        if ev is not None:
-            ev[0].record()
         st.step_decode(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r], counts[layer])
-        if ev is not None:
-            ev[1].record()
         counts[layer] += 1
         if alloc_every and counts[layer] % alloc_every == 0:
             if ev_alloc is not None:
@@ -159,29 +148,44 @@ def run_gpu(args, w):
             st.allocate_bits(s_alloc)
             if ev_alloc is not None:
                 ev_alloc[1].record()
-                return True
+            return True
         return False
 
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    aevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    used_alloc = []
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # Decode launches are timed in groups of G back-to-back launches (HIP events on the
+    # stream the kernels run on); groups that contain an allocation pass are left out
+    # of the per-launch figure, and the allocation passes are timed on their own.
+    G = 16
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    groups = []
+    alloc_evs = []
+    start, end = ev(), ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
+    g0, n, dirty = None, 0, False
     for i in range(args.steps):
-        if one(args.warmup + i, evs[i], aevs[i]):
-            used_alloc.append(i)
+        if i % G == 0:
+            g0, n, dirty = ev(), 0, False
+            g0.record()
+        ae = (ev(), ev())
+        if one(args.warmup + i, ae):
+            alloc_evs.append(ae)
+            dirty = True
+        n += 1
+        if i % G == G - 1 or i == args.steps - 1:
+            g1 = ev()
+            g1.record()
+            groups.append((g0, g1, n, dirty))
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    alloc_ms = [aevs[i][0].elapsed_time(aevs[i][1]) for i in used_alloc]
+    clean = [(a.elapsed_time(b), n) for a, b, n, d in groups if not d]
+    dec_ms = [t / n for t, n in clean for _ in range(n)]
+    alloc_ms = [a.elapsed_time(b) for a, b in alloc_evs]
     return {"total_ms": total_ms, "wall_s": wall, "decode_ms": dec_ms, "alloc_ms": alloc_ms, "states": states,
             "inputs": inp}
 
@@ -281,6 +285,28 @@ def cpu_baseline(w, gpu, budget_s):
                       f"{el:.1f} s, extrapolated to the full step (host has {os.cpu_count()} logical CPUs)"}
 
 
+CALIB_BYTES = 256 * 1024 * 1024
+
+
+def profile_run(args, w):
+    """For the memory-counter runs: one elementwise negation of a 256 MiB buffer (reads
+    and writes CALIB_BYTES each; the traffic reducer scales the counters by it), then
+    `profile_steps` decode steps of the workload, cycling the layer states as the
+    timed run does."""
+    import torch
+
+    args.steps, args.warmup = args.profile_steps, 0
+    x = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    run_gpu(args, w)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_steps": args.profile_steps, "workload": args.workload, "kernel": w["kernel"],
+                      "calib_bytes": CALIB_BYTES}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,12 +316,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="counter run: a calibration kernel of known traffic, then this many decode steps "
+                         "(no timing, no JSON result line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported on this build "
               f"(every head state is independent, see the design notes on sharding).", file=sys.stderr)
         sys.exit(2)
     w = WORKLOADS[args.workload]
+    if args.profile_steps:
+        return profile_run(args, w)
     if args.workload == "kda-prefill":
         return main_prefill(args, w)
     gpu = run_gpu(args, w)
@@ -328,8 +359,9 @@ def main():
                    "global_batch": B, "heads": H, "layers_cycled": w["layers"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "wb_kernel (decode step)", "bytes_per_launch": bytes_launch,
-                     "avg_launch_us": avg_dec_ms * 1e3, "median_launch_us": dec[len(dec) // 2] * 1e3},
+                     "kernel": w["kernel"], "bytes_per_launch": bytes_launch,
+                     "avg_launch_us": avg_dec_ms * 1e3, "median_launch_us": dec[len(dec) // 2] * 1e3,
+                     "timing": "HIP events around groups of 16 back-to-back decode launches"},
         "allocation_pass": {"launches": len(gpu["alloc_ms"]),
                             "avg_us": (sum(gpu["alloc_ms"]) / len(gpu["alloc_ms"]) * 1e3) if gpu["alloc_ms"] else None},
         "wall_s": gpu["wall_s"],
