@@ -47,47 +47,25 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// wave-wide arg-max (or arg-min) with ties to the lower index: DPP inside each row of
-// 16 lanes, then the four row winners; every lane must be active. The result is the
-// same in every lane.
-__device__ __forceinline__ bool better_than(double ov, int oi, double v, int i, bool want_max) {
-    return want_max ? (ov > v || (ov == v && oi < i)) : (ov < v || (ov == v && oi < i));
+// maximum / minimum of a 32-bit value over the wavefront (DPP inside rows of 16 lanes,
+// then the four row results); every lane must be active; the result is uniform
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));
+    const uint32_t a = __builtin_amdgcn_readlane(int(v), 0), b = __builtin_amdgcn_readlane(int(v), 16);
+    const uint32_t c = __builtin_amdgcn_readlane(int(v), 32), d = __builtin_amdgcn_readlane(int(v), 48);
+    return max(max(a, b), max(c, d));
 }
-
-template <int CTRL>
-__device__ __forceinline__ void argbest_step(double& val, int& idx, bool want_max) {
-    const uint64_t b = __double_as_longlong(val);
-    const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xF, 0xF, false));
-    const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false));
-    const int oi = __builtin_amdgcn_update_dpp(0, idx, CTRL, 0xF, 0xF, false);
-    const double ov = __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
-    if (better_than(ov, oi, val, idx, want_max)) {
-        val = ov;
-        idx = oi;
-    }
-}
-
-__device__ __forceinline__ void argbest(double& val, int& idx, bool want_max) {
-    argbest_step<0xB1>(val, idx, want_max);    // xor 1
-    argbest_step<0x4E>(val, idx, want_max);    // xor 2
-    argbest_step<0x141>(val, idx, want_max);   // half mirror
-    argbest_step<0x140>(val, idx, want_max);   // mirror
-    const uint64_t b = __double_as_longlong(val);
-    double bv = 0.0;
-    int bi = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(b)), 16 * r);
-        const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(b >> 32)), 16 * r);
-        const int ri = __builtin_amdgcn_readlane(idx, 16 * r);
-        const double rv = __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
-        if (r == 0 || better_than(rv, ri, bv, bi, want_max)) {
-            bv = rv;
-            bi = ri;
-        }
-    }
-    val = bv;
-    idx = bi;
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));
+    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));
+    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));
+    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));
+    const uint32_t a = __builtin_amdgcn_readlane(int(v), 0), b = __builtin_amdgcn_readlane(int(v), 16);
+    const uint32_t c = __builtin_amdgcn_readlane(int(v), 32), d = __builtin_amdgcn_readlane(int(v), 48);
+    return min(min(a, b), min(c, d));
 }
 
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) allocate_kernel(const AllocArgs A) {
@@ -193,27 +171,35 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             // move: bmin * dk <= target <= bmax * dk)
             const bool grow = tot < target;
             const int moves = grow ? target - tot : tot - target;
+            // Each row's marginal value is kept as it changes: one more bit scales
+            // 3/4 c 2^{-2b} by exactly 1/4, one bit less scales 3 c 2^{-2b} by 4. The
+            // row to move is the arg-max of an order-preserving 64-bit key (the value's
+            // bits for a maximum, their complement for a minimum, 0 for a row that cannot
+            // move), ties to the lower row.
+            double v0 = grow ? (0.75 * c0) * exp2(-2.0 * b0) : (3.0 * c0) * exp2(-2.0 * b0);
+            double v1 = grow ? (0.75 * c1) * exp2(-2.0 * b1) : (3.0 * c1) * exp2(-2.0 * b1);
+            const double scale = grow ? 0.25 : 4.0;
             for (int iter = 0; iter < moves; ++iter) {
-                double v0, v1;
-                if (grow) {
-                    v0 = b0 < A.bmax ? (0.75 * c0) * exp2(-2.0 * b0) : -INFINITY;
-                    v1 = b1 < A.bmax ? (0.75 * c1) * exp2(-2.0 * b1) : -INFINITY;
-                } else {
-                    v0 = b0 > A.bmin ? (3.0 * c0) * exp2(-2.0 * b0) : INFINITY;
-                    v1 = b1 > A.bmin ? (3.0 * c1) * exp2(-2.0 * b1) : INFINITY;
+                const bool ok0 = grow ? b0 < A.bmax : b0 > A.bmin;
+                const bool ok1 = grow ? b1 < A.bmax : b1 > A.bmin;
+                const uint64_t raw0 = uint64_t(__double_as_longlong(v0)), raw1 = uint64_t(__double_as_longlong(v1));
+                const uint64_t k0 = ok0 ? (grow ? raw0 : ~raw0) : 0ull;
+                const uint64_t k1 = ok1 ? (grow ? raw1 : ~raw1) : 0ull;
+                const bool second = k1 > k0;
+                const uint64_t kl = second ? k1 : k0;
+                const int il = second ? r1 : r0;
+                const uint32_t hi = uint32_t(kl >> 32), lo = uint32_t(kl);
+                const uint32_t mh = wave_max_u32(hi);
+                const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+                const int bi = int(wave_min_u32((hi == mh && lo == ml) ? uint32_t(il) : 0xFFFFu));
+                if (bi == r0) {
+                    b0 += grow ? 1 : -1;
+                    v0 *= scale;
                 }
-                double bv;
-                int bi;
-                if (grow) {
-                    bv = (v1 > v0) ? v1 : v0;
-                    bi = (v1 > v0) ? r1 : r0;
-                } else {
-                    bv = (v1 < v0) ? v1 : v0;
-                    bi = (v1 < v0) ? r1 : r0;
+                if (bi == r1) {
+                    b1 += grow ? 1 : -1;
+                    v1 *= scale;
                 }
-                argbest(bv, bi, grow);
-                if (bi == r0) b0 += grow ? 1 : -1;
-                if (bi == r1) b1 += grow ? 1 : -1;
             }
         }
         sm.newwidth[r0] = b0;
