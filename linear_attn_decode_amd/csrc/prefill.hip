@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
                 const float kk = bf16f(cur.kk[tt]), qq = bf16f(cur.qq[tt]);
-                const float dec = expf(-g[tt]);
+                const float dec = __expf(-g[tt]);    // hardware exp2 of the scaled argument
                 const float inc = __builtin_amdgcn_rcpf(dec);      // e^{g}, within an ulp or two
                 sm.khat[tt][p] = kk * dec;
                 sm.qhat[tt][p] = qq * dec;
@@ -388,72 +388,115 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         }
 
         // ---- write-back: round the register state in place ---------------------------
+        // Two row tiles (8 rows of the lane) at a time, each phase over all 8 rows, so
+        // the rows' dependency chains (block extrema by DPP, float16 metadata, rounding)
+        // interleave.
         if (write_back && KIND != WB_FP32) {
             const bool last = (t + L == T);
 #pragma unroll
-            for (int rt = 0; rt < 8; ++rt) {
+            for (int pr = 0; pr < 4; ++pr) {
+                float x[2][4][2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * rt + 4 * lg + r;
-                    float x0 = (r == 0) ? S[rt][0].x : (r == 1) ? S[rt][0].y : (r == 2) ? S[rt][0].z : S[rt][0].w;
-                    float x1 = (r == 0) ? S[rt][1].x : (r == 1) ? S[rt][1].y : (r == 2) ? S[rt][1].z : S[rt][1].w;
-                    const int c0 = 32 * wave + lc, c1 = c0 + 16;
-                    if (KIND == WB_UNIFORM) {
-                        const float lo = -float(1 << (ub - 1)), hi = float((1 << (ub - 1)) - 1);
-                        const float k0 = fminf(fmaxf(rintf(x0 / ustep), lo), hi);
-                        const float k1 = fminf(fmaxf(rintf(x1 / ustep), lo), hi);
-                        x0 = k0 * ustep;
-                        x1 = k1 * ustep;
-                        if (last) {
-                            // bits of element (row, col) at ub*(row*DV + col); ub in {2,4,8}
-                            const uint32_t m = (1u << ub) - 1;
-                            const int b0 = (row * DV + c0) * ub, b1 = (row * DV + c1) * ub;
-                            atomicAnd(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), ~(m << (b0 & 31)));
-                            atomicOr(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), (uint32_t(int(k0)) & m) << (b0 & 31));
-                            atomicAnd(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), ~(m << (b1 & 31)));
-                            atomicOr(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), (uint32_t(int(k1)) & m) << (b1 & 31));
-                        }
-                    } else if (KIND == WB_MIXED && row < k_hi) {
-                        const uint16_t h0 = f32_to_f16_bits(x0), h1 = f32_to_f16_bits(x1);
-                        x0 = f16_bits_to_f32(h0);
-                        x1 = f16_bits_to_f32(h1);
-                        if (last) {
-                            reinterpret_cast<uint16_t*>(region)[row * DV + c0] = h0;
-                            reinterpret_cast<uint16_t*>(region)[row * DV + c1] = h1;
-                        }
-                    } else {
-                        // affine INT8 block of 32 columns = this wave's columns
-                        const float mn = dpp_min16(fminf(x0, x1));
-                        const float mx = dpp_max16(fmaxf(x0, x1));
-                        const uint16_t sb = f32_to_f16_bits(fmaxf(mx - mn, 0.f) * (1.f / 255.f));
-                        const uint16_t zb = f32_to_f16_bits(mn);
-                        const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
-                        float q0 = 0.f, q1 = 0.f;
-                        if (sc > 0.f) {
-                            // reciprocal refined by one Newton step; rounding by adding
-                            // 1.5 * 2^23 (ties to even), clamp by med3
-                            float inv = __builtin_amdgcn_rcpf(sc);
-                            inv = __builtin_fmaf(__builtin_fmaf(-sc, inv, 1.f), inv, inv);
-                            constexpr float M = 12582912.0f;
-                            q0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0 - ze, inv, M), M, M + 255.f) - M;
-                            q1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1 - ze, inv, M), M, M + 255.f) - M;
-                        }
-                        x0 = ze + q0 * sc;
-                        x1 = ze + q1 * sc;
-                        if (last) {
-                            const int qrow = row - k_hi;
-                            region[code_base + (size_t)qrow * DV + c0] = uint8_t(q0);
-                            region[code_base + (size_t)qrow * DV + c1] = uint8_t(q1);
-                            if (lc == 0)
-                                *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + wave) * 4) =
-                                    uint32_t(sb) | (uint32_t(zb) << 16);
-                        }
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const f32x4 v = S[2 * pr + i][ct];
+                        x[i][0][ct] = v.x;
+                        x[i][1][ct] = v.y;
+                        x[i][2][ct] = v.z;
+                        x[i][3][ct] = v.w;
                     }
-                    if (r == 0) { S[rt][0].x = x0; S[rt][1].x = x1; }
-                    else if (r == 1) { S[rt][0].y = x0; S[rt][1].y = x1; }
-                    else if (r == 2) { S[rt][0].z = x0; S[rt][1].z = x1; }
-                    else { S[rt][0].w = x0; S[rt][1].w = x1; }
+                const int c0 = 32 * wave + lc, c1 = c0 + 16;
+                if constexpr (KIND == WB_UNIFORM) {
+                    const float lo = -float(1 << (ub - 1)), hi = float((1 << (ub - 1)) - 1);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = 16 * (2 * pr + i) + 4 * lg + r;
+                            const float k0 = fminf(fmaxf(rintf(x[i][r][0] / ustep), lo), hi);
+                            const float k1 = fminf(fmaxf(rintf(x[i][r][1] / ustep), lo), hi);
+                            x[i][r][0] = k0 * ustep;
+                            x[i][r][1] = k1 * ustep;
+                            if (last) {
+                                // bits of element (row, col) at ub*(row*DV + col); ub in {2,4,8}
+                                const uint32_t m = (1u << ub) - 1;
+                                const int b0 = (row * DV + c0) * ub, b1 = (row * DV + c1) * ub;
+                                atomicAnd(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), ~(m << (b0 & 31)));
+                                atomicOr(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), (uint32_t(int(k0)) & m) << (b0 & 31));
+                                atomicAnd(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), ~(m << (b1 & 31)));
+                                atomicOr(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), (uint32_t(int(k1)) & m) << (b1 & 31));
+                            }
+                        }
+                } else {
+                    // block minima / maxima of the INT8 rows (a block = this wave's 32 columns)
+                    float mn[2][4], mx[2][4];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            mn[i][r] = fminf(x[i][r][0], x[i][r][1]);
+                            mx[i][r] = fmaxf(x[i][r][0], x[i][r][1]);
+                        }
+#define WB_PF_DPP_STEP(CTRL)                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int r = 0; r < 4; ++r) {             \
+        mn[i][r] = fminf(mn[i][r], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn[i][r]), CTRL, 0xF, 0xF, false))); \
+        mx[i][r] = fmaxf(mx[i][r], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx[i][r]), CTRL, 0xF, 0xF, false))); \
+    }
+                    WB_PF_DPP_STEP(0xB1)
+                    WB_PF_DPP_STEP(0x4E)
+                    WB_PF_DPP_STEP(0x141)
+                    WB_PF_DPP_STEP(0x140)
+#undef WB_PF_DPP_STEP
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int rt = 2 * pr + i;
+                            const int row = 16 * rt + 4 * lg + r;
+                            float& x0 = x[i][r][0];
+                            float& x1 = x[i][r][1];
+                            if (KIND == WB_MIXED && rt == 0) {
+                                // float16 rows (physical rows 0..15 = row tile 0)
+                                const uint16_t h0 = f32_to_f16_bits(x0), h1 = f32_to_f16_bits(x1);
+                                x0 = f16_bits_to_f32(h0);
+                                x1 = f16_bits_to_f32(h1);
+                                if (last) {
+                                    reinterpret_cast<uint16_t*>(region)[row * DV + c0] = h0;
+                                    reinterpret_cast<uint16_t*>(region)[row * DV + c1] = h1;
+                                }
+                                continue;
+                            }
+                            const uint16_t sb = f32_to_f16_bits(fmaxf(mx[i][r] - mn[i][r], 0.f) * (1.f / 255.f));
+                            const uint16_t zb = f32_to_f16_bits(mn[i][r]);
+                            const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
+                            float q0 = 0.f, q1 = 0.f;
+                            if (sc > 0.f) {
+                                // reciprocal refined by one Newton step; rounding by adding
+                                // 1.5 * 2^23 (ties to even), clamp by med3
+                                float inv = __builtin_amdgcn_rcpf(sc);
+                                inv = __builtin_fmaf(__builtin_fmaf(-sc, inv, 1.f), inv, inv);
+                                constexpr float M = 12582912.0f;
+                                q0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0 - ze, inv, M), M, M + 255.f) - M;
+                                q1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1 - ze, inv, M), M, M + 255.f) - M;
+                            }
+                            x0 = ze + q0 * sc;
+                            x1 = ze + q1 * sc;
+                            if (last) {
+                                const int qrow = row - k_hi;
+                                region[code_base + (size_t)qrow * DV + c0] = uint8_t(q0);
+                                region[code_base + (size_t)qrow * DV + c1] = uint8_t(q1);
+                                if (lc == 0)
+                                    *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + wave) * 4) =
+                                        uint32_t(sb) | (uint32_t(zb) << 16);
+                            }
+                        }
                 }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        S[2 * pr + i][ct] = f32x4{x[i][0][ct], x[i][1][ct], x[i][2][ct], x[i][3][ct]};
             }
         }
         if (KIND == WB_FP32 && t + L == T) {
