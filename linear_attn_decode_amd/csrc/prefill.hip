@@ -46,7 +46,8 @@ struct PfSmem {
     float kbarL[SEG][DK];     // Gamma_L k_tau / Gamma_tau
     float gl[DK];             // Gamma_L per row
     float v[SEG][DV];
-    float ks[2 * SEG][DV];    // [k^; q^] S_0 (and the rotated-part exchange)
+    float ks[2 * SEG][DV];    // [k^; q^] S_0 over the unrotated rows, then the whole contraction
+    float ksq[2 * SEG][DV];   // the same over the rotated rows
     float w[SEG][DV];
     float hw[SEG][DV];
     float A[SEG][SEG], QK[SEG][SEG];
@@ -200,7 +201,6 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         const int L = segment_length(t, T, P.C);
         const bool write_back = ((t + L) % P.C == 0) || (t + L == T);
         const SegIn cur = nxt;
-        if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C), tid, my_lr, nxt);
 
         // ---- stage inputs (physical row order) and the decay products ---------------
 #pragma unroll
@@ -286,36 +286,6 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             }
         }
         // accumulator element (M = 4*lg + r, column 32w + 16ct + lc)
-        if (LY::ROT) {
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int col = 32 * wave + 16 * ct + lc;
-                sm.ks[4 * lg + 0][col] = accQ[ct].x;
-                sm.ks[4 * lg + 1][col] = accQ[ct].y;
-                sm.ks[4 * lg + 2][col] = accQ[ct].z;
-                sm.ks[4 * lg + 3][col] = accQ[ct].w;
-            }
-            __syncthreads();
-            // wave w transforms vectors 4w .. 4w+3 back from the rotated domain
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv) {
-                const int m = 4 * wave + vv;
-                float a0 = sm.ks[m][lane], a1 = sm.ks[m][lane + 64];
-                wave_wht128(a0, a1, lane);
-                sm.ks[m][lane] = a0;
-                sm.ks[m][lane + 64] = a1;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int col = 32 * wave + 16 * ct + lc;
-                accP[ct].x += sm.ks[4 * lg + 0][col];
-                accP[ct].y += sm.ks[4 * lg + 1][col];
-                accP[ct].z += sm.ks[4 * lg + 2][col];
-                accP[ct].w += sm.ks[4 * lg + 3][col];
-            }
-            __syncthreads();
-        }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const int col = 32 * wave + 16 * ct + lc;
@@ -323,8 +293,27 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             sm.ks[4 * lg + 1][col] = accP[ct].y;
             sm.ks[4 * lg + 2][col] = accP[ct].z;
             sm.ks[4 * lg + 3][col] = accP[ct].w;
+            if (LY::ROT) {
+                sm.ksq[4 * lg + 0][col] = accQ[ct].x;
+                sm.ksq[4 * lg + 1][col] = accQ[ct].y;
+                sm.ksq[4 * lg + 2][col] = accQ[ct].z;
+                sm.ksq[4 * lg + 3][col] = accQ[ct].w;
+            }
         }
         __syncthreads();
+        if (LY::ROT) {
+            // wave w transforms vectors 4w .. 4w+3 back from the rotated domain and adds
+            // the unrotated part
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                const int m = 4 * wave + vv;
+                float a0 = sm.ksq[m][lane], a1 = sm.ksq[m][lane + 64];
+                wave_wht128(a0, a1, lane);
+                sm.ks[m][lane] += a0;
+                sm.ks[m][lane + 64] += a1;
+            }
+            __syncthreads();
+        }
 
         // ---- per column: forward solve for w, outputs o ------------------------------
         if (tid < DV) {
@@ -348,6 +337,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 }
             }
         }
+        // inputs of the next segment: requested after this segment's output stores, so
+        // that waiting for them never waits for those stores
+        if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C), tid, my_lr, nxt);
         __syncthreads();
         if (LY::ROT) {
             // H w for the rotated rows: two vectors per wave
