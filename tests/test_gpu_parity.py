@@ -48,7 +48,8 @@ def _to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_decode(lay, T, heads=None, warm=True, seed=1, perm=None, steps_checked=None, alloc_every=None):
+def run_decode(lay, T, heads=None, warm=True, seed=1, perm=None, steps_checked=None, alloc_every=None,
+               edit=None):
     print(f"\n[case] kind={lay.kind} mode={lay.mode} B={lay.B} H={lay.H} dk={lay.dk} T={T}", flush=True)
     B, H, dk, dv = lay.B, lay.H, lay.dk, lay.dv
     rng = np.random.default_rng(seed)
@@ -56,6 +57,8 @@ def run_decode(lay, T, heads=None, warm=True, seed=1, perm=None, steps_checked=N
         perm = np.stack([rng.permutation(dk) for _ in range(H)])
     st = _state(lay, perm)
     inp = decode_inputs(seed, B, H, dk, dv, T, lay.per_row_decay)
+    if edit is not None:
+        edit(inp)
     dev = {k: _to_dev(v) for k, v in inp.items()}
     o = torch.zeros((B, H, dv), dtype=torch.float32, device="cuda")
     if warm:
@@ -202,6 +205,47 @@ def test_import_export(kind, kw):
             tally.elems += dk * dk
     print("[tally]", tally.summary(), flush=True)
     assert not tally.bad and tally.mismatch <= 1e-4 * tally.elems, tally.summary()
+
+
+# ---------------------------------------------------------------------------- degenerate inputs
+
+def _zero_keys(inp):
+    inp["k"][:] = 0.0
+
+
+def _no_write(inp):
+    inp["beta"][:] = 0.0
+
+
+def _no_decay(inp):
+    inp["s"][:] = 0.0
+
+
+def _one_hot_overwrite(inp):
+    # unit keys e_i with beta = 1: the delta rule replaces row i by v ([LBRS] recurrence)
+    T, B, H, dk = inp["k"].shape
+    inp["k"][:] = 0.0
+    for t in range(T):
+        inp["k"][t, :, :, (7 * t + 3) % dk] = 1.0
+    inp["beta"][:] = 1.0
+
+
+DEGENERATE = [
+    ("zero-state-zero-keys", _zero_keys, False),   # every stored value stays 0: Delta = 0, zero-range blocks
+    ("pure-decay", _no_write, True),
+    ("no-decay", _no_decay, True),
+    ("one-hot-overwrite", _one_hot_overwrite, True),
+]
+
+
+@pytest.mark.parametrize("case,edit,warm", DEGENERATE, ids=[c[0] for c in DEGENERATE])
+@pytest.mark.parametrize("kind,kw,mode", [
+    (L.UNIFORM, dict(bits=4), "rtn"), (L.HAD_INT8, dict(block=128), "rtn"), (L.MIXED, dict(block=32, k_hi=16), "rtn"),
+    (L.BITALLOC, {}, "rtn"), (L.MIXED, dict(block=32, k_hi=16), "ef"), (L.BITALLOC, {}, "sr"),
+], ids=["uniform4-rtn", "had128-rtn", "mixed-rtn", "bitalloc-rtn", "mixed-ef", "bitalloc-sr"])
+def test_decode_degenerate_inputs(case, edit, warm, kind, kw, mode):
+    lay = _layout(kind, mode, 2, 2, 128, **kw)
+    run_decode(lay, 3, warm=warm, edit=edit, seed=11)
 
 
 # ---------------------------------------------------------------------------- allocation pass
