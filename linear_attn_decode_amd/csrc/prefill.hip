@@ -53,6 +53,8 @@ struct PfSmem {
     float A[SEG][SEG], QK[SEG][SEG];
     float beta[SEG];
     int perm[DK];
+    float wbuf[DK][DV + 4];   // the state in row-major order for the write-back (row stride
+                              // padded to 132 floats: both transposes are conflict-free)
 };
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
@@ -379,117 +381,117 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             }
         }
 
-        // ---- write-back: round the register state in place ---------------------------
-        // Two row tiles (8 rows of the lane) at a time, each phase over all 8 rows, so
-        // the rows' dependency chains (block extrema by DPP, float16 metadata, rounding)
-        // interleave.
+        // ---- write-back ---------------------------------------------------------------
+        // The state goes through LDS in row-major order: each thread then rounds two
+        // whole 32-value row blocks (one INT8 block each: extrema, float16 metadata and
+        // levels without cross-lane steps), and the call's last write-back stores its
+        // codes contiguously.
         if (write_back && KIND != WB_FP32) {
             const bool last = (t + L == T);
 #pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-                float x[2][4][2];
+            for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int col = 32 * wave + 16 * ct + lc;
+                    const f32x4 v = S[rt][ct];
+                    sm.wbuf[16 * rt + 4 * lg + 0][col] = v.x;
+                    sm.wbuf[16 * rt + 4 * lg + 1][col] = v.y;
+                    sm.wbuf[16 * rt + 4 * lg + 2][col] = v.z;
+                    sm.wbuf[16 * rt + 4 * lg + 3][col] = v.w;
+                }
+            __syncthreads();
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const f32x4 v = S[2 * pr + i][ct];
-                        x[i][0][ct] = v.x;
-                        x[i][1][ct] = v.y;
-                        x[i][2][ct] = v.z;
-                        x[i][3][ct] = v.w;
-                    }
-                const int c0 = 32 * wave + lc, c1 = c0 + 16;
-                if constexpr (KIND == WB_UNIFORM) {
+            for (int unit = 0; unit < 2; ++unit) {
+                const int u = tid + NT * unit;
+                const int row = u >> 2, cb = u & 3;          // row block: columns 32 cb .. +31
+                float4* rp = reinterpret_cast<float4*>(&sm.wbuf[row][32 * cb]);
+                float x[32];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 f = rp[i];
+                    x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+                }
+                if (KIND == WB_UNIFORM) {
                     const float lo = -float(1 << (ub - 1)), hi = float((1 << (ub - 1)) - 1);
+                    const float inv = float(1 << (ub - 1));
+                    uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // 32 fields of ub <= 8 bits
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int c = 0; c < 32; ++c) {
+                        const float k = fminf(fmaxf(rintf(x[c] * inv), lo), hi);
+                        x[c] = k * ustep;
+                        const int bit = c * ub;
+                        wd[bit >> 5] |= (uint32_t(int(k)) & ((1u << ub) - 1)) << (bit & 31);
+                    }
+                    if (last) {
+                        // element (row, col) at bit ub (row DV + col): this block is 4 ub
+                        // contiguous bytes, 4-byte aligned
+                        uint32_t* dst = reinterpret_cast<uint32_t*>(region + ((row * DV + 32 * cb) * ub) / 8);
+                        for (int i = 0; i < ub; ++i) dst[i] = wd[i];
+                    }
+                } else if (KIND == WB_MIXED && row < k_hi) {
+                    uint32_t hw2[16];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = 16 * (2 * pr + i) + 4 * lg + r;
-                            const float k0 = fminf(fmaxf(rintf(x[i][r][0] / ustep), lo), hi);
-                            const float k1 = fminf(fmaxf(rintf(x[i][r][1] / ustep), lo), hi);
-                            x[i][r][0] = k0 * ustep;
-                            x[i][r][1] = k1 * ustep;
-                            if (last) {
-                                // bits of element (row, col) at ub*(row*DV + col); ub in {2,4,8}
-                                const uint32_t m = (1u << ub) - 1;
-                                const int b0 = (row * DV + c0) * ub, b1 = (row * DV + c1) * ub;
-                                atomicAnd(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), ~(m << (b0 & 31)));
-                                atomicOr(reinterpret_cast<unsigned int*>(region + ((b0 >> 5) << 2)), (uint32_t(int(k0)) & m) << (b0 & 31));
-                                atomicAnd(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), ~(m << (b1 & 31)));
-                                atomicOr(reinterpret_cast<unsigned int*>(region + ((b1 >> 5) << 2)), (uint32_t(int(k1)) & m) << (b1 & 31));
-                            }
-                        }
+                    for (int c = 0; c < 32; c += 2) {
+                        const uint16_t h0 = f32_to_f16_bits(x[c]), h1 = f32_to_f16_bits(x[c + 1]);
+                        x[c] = f16_bits_to_f32(h0);
+                        x[c + 1] = f16_bits_to_f32(h1);
+                        hw2[c >> 1] = uint32_t(h0) | (uint32_t(h1) << 16);
+                    }
+                    if (last) {
+                        uint4* dst = reinterpret_cast<uint4*>(region + (row * DV + 32 * cb) * 2);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dst[i] = make_uint4(hw2[4 * i], hw2[4 * i + 1], hw2[4 * i + 2], hw2[4 * i + 3]);
+                    }
                 } else {
-                    // block minima / maxima of the INT8 rows (a block = this wave's 32 columns)
-                    float mn[2][4], mx[2][4];
+                    // affine INT8 block of 32 values
+                    float mn = x[0], mx = x[0];
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int c = 1; c < 32; ++c) {
+                        mn = fminf(mn, x[c]);
+                        mx = fmaxf(mx, x[c]);
+                    }
+                    const uint16_t sb = f32_to_f16_bits(fmaxf(mx - mn, 0.f) * (1.f / 255.f));
+                    const uint16_t zb = f32_to_f16_bits(mn);
+                    const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
+                    uint32_t cw4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (sc > 0.f) {
+                        // reciprocal refined by one Newton step; rounding by adding 1.5 * 2^23
+                        // (ties to even), clamp by med3
+                        float inv = __builtin_amdgcn_rcpf(sc);
+                        inv = __builtin_fmaf(__builtin_fmaf(-sc, inv, 1.f), inv, inv);
+                        constexpr float M = 12582912.0f;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            mn[i][r] = fminf(x[i][r][0], x[i][r][1]);
-                            mx[i][r] = fmaxf(x[i][r][0], x[i][r][1]);
+                        for (int c = 0; c < 32; ++c) {
+                            const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c] - ze, inv, M), M, M + 255.f);
+                            cw4[c >> 2] |= (__float_as_uint(y) & 0xFFu) << (8 * (c & 3));
+                            x[c] = __builtin_fmaf(y - M, sc, ze);
                         }
-#define WB_PF_DPP_STEP(CTRL)                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int r = 0; r < 4; ++r) {             \
-        mn[i][r] = fminf(mn[i][r], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn[i][r]), CTRL, 0xF, 0xF, false))); \
-        mx[i][r] = fmaxf(mx[i][r], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx[i][r]), CTRL, 0xF, 0xF, false))); \
-    }
-                    WB_PF_DPP_STEP(0xB1)
-                    WB_PF_DPP_STEP(0x4E)
-                    WB_PF_DPP_STEP(0x141)
-                    WB_PF_DPP_STEP(0x140)
-#undef WB_PF_DPP_STEP
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int rt = 2 * pr + i;
-                            const int row = 16 * rt + 4 * lg + r;
-                            float& x0 = x[i][r][0];
-                            float& x1 = x[i][r][1];
-                            if (KIND == WB_MIXED && rt == 0) {
-                                // float16 rows (physical rows 0..15 = row tile 0)
-                                const uint16_t h0 = f32_to_f16_bits(x0), h1 = f32_to_f16_bits(x1);
-                                x0 = f16_bits_to_f32(h0);
-                                x1 = f16_bits_to_f32(h1);
-                                if (last) {
-                                    reinterpret_cast<uint16_t*>(region)[row * DV + c0] = h0;
-                                    reinterpret_cast<uint16_t*>(region)[row * DV + c1] = h1;
-                                }
-                                continue;
-                            }
-                            const uint16_t sb = f32_to_f16_bits(fmaxf(mx[i][r] - mn[i][r], 0.f) * (1.f / 255.f));
-                            const uint16_t zb = f32_to_f16_bits(mn[i][r]);
-                            const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
-                            float q0 = 0.f, q1 = 0.f;
-                            if (sc > 0.f) {
-                                // reciprocal refined by one Newton step; rounding by adding
-                                // 1.5 * 2^23 (ties to even), clamp by med3
-                                float inv = __builtin_amdgcn_rcpf(sc);
-                                inv = __builtin_fmaf(__builtin_fmaf(-sc, inv, 1.f), inv, inv);
-                                constexpr float M = 12582912.0f;
-                                q0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0 - ze, inv, M), M, M + 255.f) - M;
-                                q1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1 - ze, inv, M), M, M + 255.f) - M;
-                            }
-                            x0 = ze + q0 * sc;
-                            x1 = ze + q1 * sc;
-                            if (last) {
-                                const int qrow = row - k_hi;
-                                region[code_base + (size_t)qrow * DV + c0] = uint8_t(q0);
-                                region[code_base + (size_t)qrow * DV + c1] = uint8_t(q1);
-                                if (lc == 0)
-                                    *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + wave) * 4) =
-                                        uint32_t(sb) | (uint32_t(zb) << 16);
-                            }
-                        }
+                        for (int c = 0; c < 32; ++c) x[c] = ze;
+                    }
+                    if (last) {
+                        const int qrow = row - k_hi;
+                        uint4* dst = reinterpret_cast<uint4*>(region + code_base + (size_t)qrow * DV + 32 * cb);
+                        dst[0] = make_uint4(cw4[0], cw4[1], cw4[2], cw4[3]);
+                        dst[1] = make_uint4(cw4[4], cw4[5], cw4[6], cw4[7]);
+                        *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + cb) * 4) =
+                            uint32_t(sb) | (uint32_t(zb) << 16);
+                    }
                 }
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct)
-                        S[2 * pr + i][ct] = f32x4{x[i][0][ct], x[i][1][ct], x[i][2][ct], x[i][3][ct]};
+                for (int i = 0; i < 8; ++i) rp[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
             }
+            __syncthreads();
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int col = 32 * wave + 16 * ct + lc;
+                    S[rt][ct] = f32x4{sm.wbuf[16 * rt + 4 * lg + 0][col], sm.wbuf[16 * rt + 4 * lg + 1][col],
+                                      sm.wbuf[16 * rt + 4 * lg + 2][col], sm.wbuf[16 * rt + 4 * lg + 3][col]};
+                }
         }
         if (KIND == WB_FP32 && t + L == T) {
 #pragma unroll
