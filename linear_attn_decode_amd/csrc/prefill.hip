@@ -45,6 +45,8 @@ struct PfSmem {
     float kbar[SEG][DK];      // k_tau / Gamma_tau
     float kbarL[SEG][DK];     // Gamma_L k_tau / Gamma_tau
     float gl[DK];             // Gamma_L per row
+    float kqt[DK][20];        // [k^; q^] transposed (16 used): the MFMA A operand, read
+                              // without bank conflicts (row stride 20 floats)
     float v[SEG][DV];
     float ks[2 * SEG][DV];    // [k^; q^] S_0 over the unrotated rows, then the whole contraction
     float ksq[2 * SEG][DV];   // the same over the rotated rows
@@ -229,6 +231,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 const float inc = __builtin_amdgcn_rcpf(dec);      // e^{g}, within an ulp or two
                 sm.khat[tt][p] = kk * dec;
                 sm.qhat[tt][p] = qq * dec;
+                sm.kqt[p][tt] = kk * dec;
+                sm.kqt[p][SEG + tt] = qq * dec;
                 sm.kbar[tt][p] = kk * inc;
                 sm.kbarL[tt][p] = kk * (inc * decL);
             }
@@ -271,12 +275,11 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             accP[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
             accQ[ct] = accP[ct];
         }
-        const float* kq = &sm.khat[0][0];      // 16 x DK: khat rows then qhat rows
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float a = kq[lc * DK + 16 * rt + 4 * lg + r];
+                const float a = sm.kqt[16 * rt + 4 * lg + r][lc];
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     const float bv = (r == 0) ? S[rt][ct].x : (r == 1) ? S[rt][ct].y : (r == 2) ? S[rt][ct].z : S[rt][ct].w;
