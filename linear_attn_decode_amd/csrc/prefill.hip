@@ -61,15 +61,41 @@ struct PfSmem {
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// Butterfly partner at lane ^ d for d = 1, 2, 4, 8 (DPP inside a row of 16 lanes),
+// 16 (swizzle inside 32 lanes) and 32 (permute).
+template <int D>
+__device__ __forceinline__ float xor_partner(float v, int lane) {
+    const int b = __float_as_int(v);
+    if constexpr (D == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false));
+    if constexpr (D == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false));
+    if constexpr (D == 4) {
+        // row_ror:n hands lane i the value of lane i - n (mod 16)
+        const int up = __builtin_amdgcn_mov_dpp(b, 0x12C, 0xF, 0xF, false);     // row_ror:12 (i + 4)
+        const int dn = __builtin_amdgcn_mov_dpp(b, 0x124, 0xF, 0xF, false);     // row_ror:4  (i - 4)
+        return __int_as_float((lane & 4) ? dn : up);
+    }
+    if constexpr (D == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, false));   // row_ror:8
+    if constexpr (D == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x401F));   // xor 16 in 32 lanes
+    return __shfl_xor(v, 32, 64);
+}
+
+template <int D>
+__device__ __forceinline__ void butterfly(float& x, float& y, int lane) {
+    const float sg = (lane & D) ? -1.f : 1.f;     // lane with bit D set: partner - self
+    const float ox = xor_partner<D>(x, lane), oy = xor_partner<D>(y, lane);
+    x = __builtin_fmaf(sg, x, ox);
+    y = __builtin_fmaf(sg, y, oy);
+}
+
 // 128-point orthonormal transform of a vector held by one wavefront as v[lane], v[lane + 64]
 __device__ __forceinline__ void wave_wht128(float& a0, float& a1, int lane) {
     float x = a0 + a1, y = a0 - a1;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float ox = __shfl_xor(x, d, 64), oy = __shfl_xor(y, d, 64);
-        x = (lane & d) ? (ox - x) : (x + ox);
-        y = (lane & d) ? (oy - y) : (y + oy);
-    }
+    butterfly<1>(x, y, lane);
+    butterfly<2>(x, y, lane);
+    butterfly<4>(x, y, lane);
+    butterfly<8>(x, y, lane);
+    butterfly<16>(x, y, lane);
+    butterfly<32>(x, y, lane);
     a0 = x * kInvSqrt128f;
     a1 = y * kInvSqrt128f;
 }
