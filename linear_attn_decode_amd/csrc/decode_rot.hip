@@ -88,16 +88,48 @@ __device__ __forceinline__ void block_minmax(double& mn, double& mx) {
     }
 }
 
+// Butterfly partner at lane ^ D of a float64 value: DPP inside a row of 16 lanes for
+// D = 1, 2, 4, 8 (row_ror:n hands lane i the value of lane i - n mod 16), swizzle inside
+// 32 lanes for D = 16, permute for D = 32.
+template <int D>
+__device__ __forceinline__ uint32_t xor_partner32(uint32_t b, int lane) {
+    if constexpr (D == 1) return uint32_t(__builtin_amdgcn_mov_dpp(int(b), 0xB1, 0xF, 0xF, false));
+    if constexpr (D == 2) return uint32_t(__builtin_amdgcn_mov_dpp(int(b), 0x4E, 0xF, 0xF, false));
+    if constexpr (D == 4) {
+        const int up = __builtin_amdgcn_mov_dpp(int(b), 0x12C, 0xF, 0xF, false);   // lane i + 4
+        const int dn = __builtin_amdgcn_mov_dpp(int(b), 0x124, 0xF, 0xF, false);   // lane i - 4
+        return uint32_t((lane & 4) ? dn : up);
+    }
+    if constexpr (D == 8) return uint32_t(__builtin_amdgcn_mov_dpp(int(b), 0x128, 0xF, 0xF, false));
+    if constexpr (D == 16) return uint32_t(__builtin_amdgcn_ds_swizzle(int(b), 0x401F));
+    return uint32_t(__shfl_xor(int(b), 32, 64));
+}
+
+template <int D>
+__device__ __forceinline__ double xor_partner(double v, int lane) {
+    const uint64_t b = __double_as_longlong(v);
+    const uint32_t lo = xor_partner32<D>(uint32_t(b), lane), hi = xor_partner32<D>(uint32_t(b >> 32), lane);
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+template <int D>
+__device__ __forceinline__ void butterfly(double& x, double& y, int lane) {
+    const double sg = (lane & D) ? -1.0 : 1.0;    // lane with bit D set: partner - self
+    const double ox = xor_partner<D>(x, lane), oy = xor_partner<D>(y, lane);
+    x = fma(sg, x, ox);
+    y = fma(sg, y, oy);
+}
+
 // 128-point orthonormal transform of a vector held by one wavefront (lane l holds
 // elements l and l + 64)
 __device__ __forceinline__ void wht128(double& a0, double& a1, int lane) {
     double x = a0 + a1, y = a0 - a1;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const double ox = __shfl_xor(x, d, 64), oy = __shfl_xor(y, d, 64);
-        x = (lane & d) ? (ox - x) : (x + ox);
-        y = (lane & d) ? (oy - y) : (y + oy);
-    }
+    butterfly<1>(x, y, lane);
+    butterfly<2>(x, y, lane);
+    butterfly<4>(x, y, lane);
+    butterfly<8>(x, y, lane);
+    butterfly<16>(x, y, lane);
+    butterfly<32>(x, y, lane);
     a0 = x * kInvSqrt128;
     a1 = y * kInvSqrt128;
 }
