@@ -8,8 +8,13 @@
 //     per step nearly always share one width; that width is read into a scalar register
 //     and the unpack / pack code is chosen by a scalar branch and specialised per width
 //     (static bit positions); a group of mixed widths is walked one width at a time;
+//   * eight wavefronts per head; a lane holds 4 rows x 8 columns of the state (32
+//     values, which keeps the register count low enough for 6 wavefronts per SIMD), and
+//     the u / p partial sums of a wavefront are combined in registers by lane swaps
+//     before one LDS store;
 //   * the sort, the byte offsets of the rows and their ranks come from wavefront ballots
-//     (every wavefront derives them for all 128 rows, so no cross-wave scan is needed);
+//     (each of the two wavefronts that build the tables reads the widths of all 128
+//     rows, so no cross-wave scan is needed);
 //   * per-row constants (decayed step, offset term, k_i, q_i, f_i / n_i, rounding
 //     constants, byte offset, width) sit in LDS tables indexed by sorted position;
 //   * dequantize + decay is one FMA: a_i Delta_i (code - n_i) = code * (a_i Delta_i) +
@@ -29,7 +34,10 @@
 namespace wb {
 namespace {
 
-constexpr int DK = 128, DV = 128, NT = 256;
+constexpr int DK = 128, DV = 128;
+constexpr int NW = 8, NT = 64 * NW;            // wavefronts per head
+constexpr int NG = 4 * NW;                     // row groups: a wavefront step covers 4 rows
+constexpr int MR = DK / NG;                    // rows per lane
 constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
 constexpr uint32_t kMagicBits = 0x4B400000u;
 
@@ -44,7 +52,7 @@ struct TabB {                                   // requantize constants, by sort
 struct BaFixed {
     TabA ta[DK];
     TabB tb[DK];
-    float red[2][16][DV];                      // u / p partials of the 16 row groups
+    float red[2][NW][DV];                      // u / p partials of the wavefronts
     float w[DV];
     float qk[4];
 };
@@ -308,11 +316,11 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     }
     __syncthreads();
 
-    // ---- dequantize the lane's 8 rows x 8 columns; u, p partial sums ------------------
+    // ---- dequantize the lane's 4 rows x 8 columns; u, p partial sums ------------------
     // The code words of row m + 1 are requested (and the location of row m + 2 read)
     // before row m is unpacked, so their LDS latency overlaps the arithmetic.
     auto boff_of = [&](uint32_t l) { return int(l & 0xFFFFu) + cg * int((l >> 16) & 15u); };
-    float x[8][8];
+    float x[MR][8];
     float up[8], pp[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -320,18 +328,18 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         pp[c] = 0.f;
     }
     uint32_t loc_cur = sm.tb[4 * wave + rq].loc;
-    uint32_t loc_next = sm.tb[16 + 4 * wave + rq].loc;
+    uint32_t loc_next = sm.tb[NG + 4 * wave + rq].loc;
     Raw raw_next = load_raw(reg, boff_of(loc_cur));
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < MR; ++m) {
         const Raw raw = raw_next;
         const uint32_t loc = loc_cur;
-        if (m + 1 < 8) {
+        if (m + 1 < MR) {
             raw_next = load_raw(reg, boff_of(loc_next));
             loc_cur = loc_next;
         }
-        if (m + 2 < 8) loc_next = sm.tb[16 * (m + 2) + 4 * wave + rq].loc;
-        const TabA ta = sm.ta[16 * m + 4 * wave + rq];
+        if (m + 2 < MR) loc_next = sm.tb[NG * (m + 2) + 4 * wave + rq].loc;
+        const TabA ta = sm.ta[NG * m + 4 * wave + rq];
         float code[8];
         unpack_rows(raw, boff_of(loc), int((loc >> 16) & 15u), code);
 #pragma unroll
@@ -347,25 +355,39 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
                      "v"(up[7]), "v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(pp[4]), "v"(pp[5]), "v"(pp[6]),
                      "v"(pp[7]));
     }
-    // partials as red[q][row group][column]: a lane's 8 columns are two float4 stores
+    // Sum the four row groups of the wavefront in registers (a reduce-scatter by lane
+    // swaps): exchanging lanes 32..63 of u with lanes 0..31 of p and adding leaves the
+    // u sums over row groups (0, 2) and (1, 3) in the low half and the p sums in the
+    // high half; exchanging odd 16-lane rows of columns c with even rows of columns
+    // c + 4 and adding completes the sums. Lane (cg, rq) then holds quantity rq / 2 of
+    // columns 8 cg + 4 (rq % 2) + 0..3.
     {
-        const int rg = 4 * wave + rq;
-        float4* u4 = reinterpret_cast<float4*>(&sm.red[0][rg][8 * cg]);
-        float4* p4 = reinterpret_cast<float4*>(&sm.red[1][rg][8 * cg]);
-        u4[0] = make_float4(up[0], up[1], up[2], up[3]);
-        u4[1] = make_float4(up[4], up[5], up[6], up[7]);
-        p4[0] = make_float4(pp[0], pp[1], pp[2], pp[3]);
-        p4[1] = make_float4(pp[4], pp[5], pp[6], pp[7]);
+        float t[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(up[c]), __float_as_uint(pp[c]), false,
+                                                            false);
+            t[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        float s4[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t[c]), __float_as_uint(t[c + 4]), false,
+                                                            false);
+            s4[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        *reinterpret_cast<float4*>(&sm.red[rq >> 1][wave][8 * cg + 4 * (rq & 1)]) =
+            make_float4(s4[0], s4[1], s4[2], s4[3]);
     }
     __syncthreads();
 
-    // ---- w = beta (v - u) (threads 0..127); p kept by threads 128..255 for o ----------
+    // ---- w = beta (v - u) (threads 0..127); p summed by threads 128..255 for o --------
     const int jq = tid >> 7, j = tid & (DV - 1);
     float pj = 0.f;
-    {
+    if (jq < 2) {
         float acc = 0.f;
 #pragma unroll
-        for (int g = 0; g < 16; ++g) acc += sm.red[jq][g][j];
+        for (int g = 0; g < NW; ++g) acc += sm.red[jq][g][j];
         if (jq == 0) sm.w[j] = beta * (vj - acc);
         else pj = acc;
     }
@@ -384,11 +406,11 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
     }
     uint16_t* dout = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(reg) + code_bytes);
-    // row maxima and steps first (no branches, so the 8 rows interleave) ...
-    float inv[8];
+    // row maxima and steps first (no branches, so the lane's rows interleave) ...
+    float inv[MR];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int pos = 16 * m + 4 * wave + rq;
+    for (int m = 0; m < MR; ++m) {
+        const int pos = NG * m + 4 * wave + rq;
         const float kk = sm.ta[pos].k;
         const TabB tb = sm.tb[pos];
 #pragma unroll
@@ -408,8 +430,8 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     }
     // ... then the rounding and packing, specialised per width
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const uint32_t l = sm.tb[16 * m + 4 * wave + rq].loc;
+    for (int m = 0; m < MR; ++m) {
+        const uint32_t l = sm.tb[NG * m + 4 * wave + rq].loc;
         pack_rows(reg, boff_of(l), int((l >> 16) & 15u), x[m], inv[m]);
     }
     __syncthreads();
