@@ -13,8 +13,9 @@
 //     half of the rows of column j, so the only cross-thread step is adding two
 //     halves; the float64 step and offset of every INT8 block are tabulated once;
 //   * the three 128-point transforms (H uQ, H pQ, H w) run on one wavefront;
-//   * the update and the requantization run row-parallel (lane = 8 rows x 8 columns)
-//     with float64 element arithmetic and the block minimum / maximum by DPP;
+//   * the update and the requantization run row-parallel (lane = 4 rows x 16 columns,
+//     so a block of 32 values spans 2 lanes) with float64 element arithmetic and the
+//     block minimum / maximum by DPP;
 //   * float64 -> float16 goes through float32 rounded to odd, then the hardware
 //     conversion: rounding to odd at 24 bits followed by a rounding to 11 bits gives
 //     the correctly rounded result (Boldo & Melquiond, IEEE Trans. Computers 2008).
@@ -73,18 +74,16 @@ __device__ __forceinline__ double dpp_f64(double v) {
     return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
 }
 
-// min and max over the lanes of one block (BLOCK / 8 consecutive lanes of a DPP row)
+// min and max over the lanes of one block (BLOCK / 16 consecutive lanes of a DPP row)
 template <int BLOCK>
 __device__ __forceinline__ void block_minmax(double& mn, double& mx) {
     mn = fmin(mn, dpp_f64<0xB1>(mn));     // xor 1
     mx = fmax(mx, dpp_f64<0xB1>(mx));
-    mn = fmin(mn, dpp_f64<0x4E>(mn));     // xor 2
-    mx = fmax(mx, dpp_f64<0x4E>(mx));
     if constexpr (BLOCK == 128) {
-        mn = fmin(mn, dpp_f64<0x141>(mn));    // half mirror
+        mn = fmin(mn, dpp_f64<0x4E>(mn));     // xor 2
+        mx = fmax(mx, dpp_f64<0x4E>(mx));
+        mn = fmin(mn, dpp_f64<0x141>(mn));    // half mirror (8 lanes)
         mx = fmax(mx, dpp_f64<0x141>(mx));
-        mn = fmin(mn, dpp_f64<0x140>(mn));    // mirror
-        mx = fmax(mx, dpp_f64<0x140>(mx));
     }
 }
 
@@ -235,47 +234,55 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     }
     __syncthreads();
 
-    // ---- update and requantize in place (lane = 8 rows x 8 columns) --------------------
+    // ---- update and requantize in place (lane = 4 rows x 16 columns) -------------------
+    // A block of BLOCK columns of a row spans BLOCK / 16 lanes, so its range, step and
+    // offset are derived by few lanes (the per-block work is repeated on each of them).
     {
-        const int rg = tid >> 4, cg = tid & 15;
-        double hwv[8];
+        const int rg = tid >> 3, cg = tid & 7;
+        constexpr int LPB = BLOCK / 16;                     // lanes per block
+        double hwv[16];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) hwv[c] = sm.hw[8 * cg + c];
+        for (int c = 0; c < 16; ++c) hwv[c] = sm.hw[16 * cg + c];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int p = rg + 16 * m;
+        for (int m = 0; m < 4; ++m) {
+            const int p = rg + 32 * m;
             const double2 ak = sm.ak[p];
-            if (KHI > 0 && m == 0) {
-                // float16 row (p < 16 <= k_hi): original domain, w itself
-                uint4* ptr = reinterpret_cast<uint4*>(lb + (p * DV + 8 * cg) * 2);
-                const uint4 raw = *ptr;
-                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-                uint32_t o4[4] = {0, 0, 0, 0};
+            if (KHI > 0 && p < KHI) {
+                // float16 row (original domain, updated with w itself); the rows below
+                // k_hi are those of whole wavefronts at m = 0
+                uint4* ptr = reinterpret_cast<uint4*>(lb + (p * DV + 16 * cg) * 2);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const double x = f16_to_f64((w4[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu);
-                    const double xn = fma(ak.x, x, ak.y * sm.w[8 * cg + c]);
-                    o4[c >> 1] |= uint32_t(f64_to_f16_rto(xn)) << ((c & 1) * 16);
+                for (int hv = 0; hv < 2; ++hv) {
+                    const uint4 raw = ptr[hv];
+                    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+                    uint32_t o4[4] = {0, 0, 0, 0};
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const double x = f16_to_f64((w4[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu);
+                        const double xn = fma(ak.x, x, ak.y * sm.w[16 * cg + 8 * hv + c]);
+                        o4[c >> 1] |= uint32_t(f64_to_f16_rto(xn)) << ((c & 1) * 16);
+                    }
+                    ptr[hv] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
                 }
-                *ptr = make_uint4(o4[0], o4[1], o4[2], o4[3]);
                 continue;
             }
             const int qr = p - KHI;
-            const int g = (8 * cg) / BLOCK;
-            uint2* ptr = reinterpret_cast<uint2*>(lb + LY::CODE_BASE + qr * DV + 8 * cg);
-            const uint2 raw = *ptr;
+            const int g = (16 * cg) / BLOCK;
+            uint4* ptr = reinterpret_cast<uint4*>(lb + LY::CODE_BASE + qr * DV + 16 * cg);
+            const uint4 raw = *ptr;
+            const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
             const double2 s = sm.sz[qr * LY::NB + g];
             // a (zero + code * scale) + k (H w)_c = code * (a scale) + (a zero + k (H w)_c)
             const double as = ak.x * s.x, az = ak.x * s.y;
-            double y[8];
+            double y[16];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint32_t code = ((c < 4 ? raw.x : raw.y) >> ((c & 3) * 8)) & 0xFFu;
+            for (int c = 0; c < 16; ++c) {
+                const uint32_t code = (rw[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
                 y[c] = fma(double(code), as, fma(ak.y, hwv[c], az));
             }
             double mn = y[0], mx = y[0];
 #pragma unroll
-            for (int c = 1; c < 8; ++c) {
+            for (int c = 1; c < 16; ++c) {
                 mn = fmin(mn, y[c]);
                 mx = fmax(mx, y[c]);
             }
@@ -285,7 +292,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             const uint16_t sbits = f64_to_f16_rto(fmax(mx - mn, 0.0) * (1.0 / 255.0));
             const uint16_t zbits = f64_to_f16_rto(mn);
             const double scale = f16_to_f64(sbits), zero = f16_to_f64(zbits);
-            uint32_t lo4 = 0, hi4 = 0;
+            uint32_t o4[4] = {0, 0, 0, 0};
             if (scale != 0.0) {
                 // reciprocal of the step refined by one Newton step
                 double inv = __builtin_amdgcn_rcp(scale);
@@ -298,24 +305,21 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                     // t + 1.5 * 2^52 rounds t to the nearest integer (ties to even); its
                     // low 32 bits are that integer, clamped to [0, 255] in integer form
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
+                    for (int c = 0; c < 16; ++c) {
                         const double r = fma(y[c], inv, nz) + 6755399441055744.0;
                         const int kk = min(max(int(uint32_t(__double_as_longlong(r))), 0), 255);
-                        if (c < 4) lo4 |= uint32_t(kk) << (c * 8);
-                        else hi4 |= uint32_t(kk) << ((c - 4) * 8);
+                        o4[c >> 2] |= uint32_t(kk) << ((c & 3) * 8);
                     }
                 } else {
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
+                    for (int c = 0; c < 16; ++c) {
                         const double kf = fmin(fmax(rint((y[c] - zero) / scale), 0.0), 255.0);
-                        const uint32_t code = uint32_t(kf);
-                        if (c < 4) lo4 |= code << (c * 8);
-                        else hi4 |= code << ((c - 4) * 8);
+                        o4[c >> 2] |= uint32_t(kf) << ((c & 3) * 8);
                     }
                 }
             }
-            *ptr = make_uint2(lo4, hi4);
-            if ((cg % (BLOCK / 8)) == 0)
+            *ptr = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            if ((cg % LPB) == 0)
                 sm.reg[LY::META_BASE / 4 + qr * LY::NB + g] = uint32_t(sbits) | (uint32_t(zbits) << 16);
         }
     }
