@@ -47,25 +47,9 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// maximum / minimum of a 32-bit value over the wavefront (DPP inside rows of 16 lanes,
-// then the four row results); every lane must be active; the result is uniform
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));
-    const uint32_t a = __builtin_amdgcn_readlane(int(v), 0), b = __builtin_amdgcn_readlane(int(v), 16);
-    const uint32_t c = __builtin_amdgcn_readlane(int(v), 32), d = __builtin_amdgcn_readlane(int(v), 48);
-    return max(max(a, b), max(c, d));
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));
-    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));
-    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));
-    v = min(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));
-    const uint32_t a = __builtin_amdgcn_readlane(int(v), 0), b = __builtin_amdgcn_readlane(int(v), 16);
-    const uint32_t c = __builtin_amdgcn_readlane(int(v), 32), d = __builtin_amdgcn_readlane(int(v), 48);
-    return min(min(a, b), min(c, d));
+// number of set bits of a wavefront mask below the calling lane
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
 }
 
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) allocate_kernel(const AllocArgs A) {
@@ -167,39 +151,62 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             int tot = b0 + b1;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d, 64);
-            // each pass moves one bit toward the budget (there is always a row that can
-            // move: bmin * dk <= target <= bmax * dk)
+            // One bit at a time toward the budget, each time to the row of largest gain
+            // (3/4) c 2^{-2b} (b < bmax) or, when over, from the row of smallest loss
+            // 3 c 2^{-2b} (b > bmin), ties to the lower row. A row's successive gains
+            // shrink by exactly 1/4 (losses grow by 4), so the moves made are the
+            // `moves` first candidates (row, step) in the order (value, then row): with
+            // an order-preserving 64-bit key per candidate (the value's bits for gains,
+            // their complement for losses), the key of the last move made is found by a
+            // bitwise search on the count of keys at or above it (ballots), and of the
+            // candidates equal to it the lowest rows are taken.
             const bool grow = tot < target;
             const int moves = grow ? target - tot : tot - target;
-            // Each row's marginal value is kept as it changes: one more bit scales
-            // 3/4 c 2^{-2b} by exactly 1/4, one bit less scales 3 c 2^{-2b} by 4. The
-            // row to move is the arg-max of an order-preserving 64-bit key (the value's
-            // bits for a maximum, their complement for a minimum, 0 for a row that cannot
-            // move), ties to the lower row.
-            double v0 = grow ? (0.75 * c0) * exp2(-2.0 * b0) : (3.0 * c0) * exp2(-2.0 * b0);
-            double v1 = grow ? (0.75 * c1) * exp2(-2.0 * b1) : (3.0 * c1) * exp2(-2.0 * b1);
-            const double scale = grow ? 0.25 : 4.0;
-            for (int iter = 0; iter < moves; ++iter) {
-                const bool ok0 = grow ? b0 < A.bmax : b0 > A.bmin;
-                const bool ok1 = grow ? b1 < A.bmax : b1 > A.bmin;
-                const uint64_t raw0 = uint64_t(__double_as_longlong(v0)), raw1 = uint64_t(__double_as_longlong(v1));
-                const uint64_t k0 = ok0 ? (grow ? raw0 : ~raw0) : 0ull;
-                const uint64_t k1 = ok1 ? (grow ? raw1 : ~raw1) : 0ull;
-                const bool second = k1 > k0;
-                const uint64_t kl = second ? k1 : k0;
-                const int il = second ? r1 : r0;
-                const uint32_t hi = uint32_t(kl >> 32), lo = uint32_t(kl);
-                const uint32_t mh = wave_max_u32(hi);
-                const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
-                const int bi = int(wave_min_u32((hi == mh && lo == ml) ? uint32_t(il) : 0xFFFFu));
-                if (bi == r0) {
-                    b0 += grow ? 1 : -1;
+            if (moves > 0) {
+                constexpr int MS = 8;                         // bmax - bmin < 8
+                const int lim0 = grow ? A.bmax - b0 : b0 - A.bmin;
+                const int lim1 = grow ? A.bmax - b1 : b1 - A.bmin;
+                double v0 = grow ? (0.75 * c0) * exp2(-2.0 * b0) : (3.0 * c0) * exp2(-2.0 * b0);
+                double v1 = grow ? (0.75 * c1) * exp2(-2.0 * b1) : (3.0 * c1) * exp2(-2.0 * b1);
+                const double scale = grow ? 0.25 : 4.0;
+                uint64_t key0[MS], key1[MS];                  // 0: no such candidate
+#pragma unroll
+                for (int st = 0; st < MS; ++st) {
+                    const uint64_t r0b = uint64_t(__double_as_longlong(v0)), r1b = uint64_t(__double_as_longlong(v1));
+                    key0[st] = st < lim0 ? (grow ? r0b : ~r0b) : 0ull;
+                    key1[st] = st < lim1 ? (grow ? r1b : ~r1b) : 0ull;
                     v0 *= scale;
-                }
-                if (bi == r1) {
-                    b1 += grow ? 1 : -1;
                     v1 *= scale;
                 }
+                auto count_ge = [&](uint64_t t) {
+                    int cnt = 0;
+#pragma unroll
+                    for (int st = 0; st < MS; ++st)
+                        cnt += __popcll(__ballot(key0[st] >= t)) + __popcll(__ballot(key1[st] >= t));
+                    return cnt;
+                };
+                // largest T with at least `moves` keys >= T: the key of the last move
+                uint64_t T = 0;
+                for (int bit = 63; bit >= 0; --bit) {
+                    const uint64_t cand = T | (1ull << bit);
+                    if (count_ge(cand) >= moves) T = cand;
+                }
+                const int rem = moves - count_ge(T + 1);      // equal keys still to take
+                int a0 = 0, a1 = 0;
+                bool t0 = false, t1 = false;
+#pragma unroll
+                for (int st = 0; st < MS; ++st) {
+                    a0 += key0[st] > T;
+                    a1 += key1[st] > T;
+                    t0 |= key0[st] == T;
+                    t1 |= key1[st] == T;
+                }
+                // rank of each tied row among the tied rows (rows 2 lane, 2 lane + 1)
+                const int below = lanes_below(__ballot(t0)) + lanes_below(__ballot(t1));
+                if (t0 && below < rem) ++a0;
+                if (t1 && below + int(t0) < rem) ++a1;
+                b0 += grow ? a0 : -a0;
+                b1 += grow ? a1 : -a1;
             }
         }
         sm.newwidth[r0] = b0;

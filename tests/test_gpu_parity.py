@@ -251,22 +251,42 @@ def test_decode_degenerate_inputs(case, edit, warm, kind, kw, mode):
 # ---------------------------------------------------------------------------- allocation pass
 
 
-def test_allocate_bits_matches_oracle():
-    print("\n[case] allocate_bits B=2 H=4", flush=True)
+def _alloc_case(case, rng, B, H, dk):
+    """(state, s) for an allocation case. "warm": rows of very different ranges;
+    "groups": three groups of identical rows (magnitudes 1, 1e-2, 1e-5) with one decay,
+    so that clipping forces over a hundred one-bit moves per head that end inside a group of
+    exactly tied rows; "spread": row magnitudes and decays both spread over several
+    decades (many rows clipped at both ends)."""
+    if case == "warm":
+        S = _warm_state(rng, B, H, dk, dk)
+        s = np.exp(rng.uniform(np.log(1e-3), 0.0, (B, H, dk))).astype(np.float32)
+    elif case == "groups":
+        base = rng.standard_normal((B, H, 1, dk)).astype(np.float32)
+        mag = np.array([1.0, 1e-2, 1e-5], np.float32)[np.arange(dk) % 3]
+        S = np.ascontiguousarray(np.broadcast_to(base, (B, H, dk, dk)) * mag[None, None, :, None])
+        s = np.full((B, H, dk), 0.05, np.float32)
+    else:
+        S = (rng.standard_normal((B, H, dk, dk)) * np.exp(rng.uniform(-8.0, 2.0, (B, H, dk, 1)))).astype(np.float32)
+        s = np.exp(rng.uniform(np.log(1e-4), np.log(2.0), (B, H, dk))).astype(np.float32)
+    return S, s
+
+
+@pytest.mark.parametrize("case", ["warm", "groups", "spread"])
+def test_allocate_bits_matches_oracle(case):
+    print(f"\n[case] allocate_bits {case} B=2 H=4", flush=True)
     B, H, dk = 2, 4, 128
     lay = _layout(L.BITALLOC, "rtn", B, H, dk)
     rng = np.random.default_rng(31)
     st = _state(lay)
-    st.quantize(_to_dev(_warm_state(rng, B, H, dk, dk)))
-    s = np.exp(rng.uniform(np.log(1e-3), 0.0, (B, H, dk))).astype(np.float32)
+    S, s = _alloc_case(case, rng, B, H, dk)
+    st.quantize(_to_dev(S))
     r = np.full((B, H, dk), 1.0 / (3 * dk), dtype=np.float32)
     torch.cuda.synchronize()
     before = st.regions().cpu().numpy()
     st.allocate_bits(_to_dev(s), _to_dev(r))
     torch.cuda.synchronize()
     after = st.regions().cpu().numpy()
-    st2 = _state(lay)
-    st2.state.copy_(st.state)
+    moved = 0
     for b in range(B):
         for h in range(H):
             reg_in = before[b * H + h][: lay.region_size()]
@@ -275,6 +295,7 @@ def test_allocate_bits_matches_oracle():
             g = L.decode_region(lay, reg_gpu)
             o = L.decode_region(lay, reg_orc)
             assert g.widths.sum() == 512
+            moved += int(np.abs(np.clip(np.rint(alloc["bstar"]), lay.bmin, lay.bmax) - o.widths).sum())
             if not np.array_equal(g.widths, o.widths):
                 # only near-ties of the real widths may differ
                 bad = np.argwhere(g.widths != o.widths).ravel()
@@ -288,6 +309,9 @@ def test_allocate_bits_matches_oracle():
                     assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (b, h, i)
                 continue
             assert np.array_equal(reg_gpu, reg_orc), (b, h)
+    print(f"[alloc] one-bit moves over the heads: {moved}", flush=True)
+    if case != "warm":
+        assert moved >= 50 * B * H
 
 
 def test_allocation_then_decode_full_budget_zero_state():
