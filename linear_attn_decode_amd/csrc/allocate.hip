@@ -158,12 +158,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             // `moves` first candidates (row, step) in the order (value, then row): with
             // an order-preserving 64-bit key per candidate (the value's bits for gains,
             // their complement for losses), the key of the last move made is found by a
-            // bitwise search on the count of keys at or above it (ballots), and of the
-            // candidates equal to it the lowest rows are taken.
+            // bitwise search on the count of keys at or above it (ballots) -- first on
+            // the high 32 bits, then on the low 32 bits of the keys that share the high
+            // word found (skipped when only one does) -- and of the candidates equal to it
+            // the lowest rows are taken.
             const bool grow = tot < target;
             const int moves = grow ? target - tot : tot - target;
             if (moves > 0) {
-                constexpr int MS = 8;                         // bmax - bmin < 8
+                constexpr int MS = 6;                         // bmax - bmin <= 6
                 const int lim0 = grow ? A.bmax - b0 : b0 - A.bmin;
                 const int lim1 = grow ? A.bmax - b1 : b1 - A.bmin;
                 double v0 = grow ? (0.75 * c0) * exp2(-2.0 * b0) : (3.0 * c0) * exp2(-2.0 * b0);
@@ -178,20 +180,51 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
                     v0 *= scale;
                     v1 *= scale;
                 }
-                auto count_ge = [&](uint64_t t) {
+                auto count_gt = [&](uint64_t t) {
                     int cnt = 0;
 #pragma unroll
                     for (int st = 0; st < MS; ++st)
-                        cnt += __popcll(__ballot(key0[st] >= t)) + __popcll(__ballot(key1[st] >= t));
+                        cnt += __popcll(__ballot(key0[st] > t)) + __popcll(__ballot(key1[st] > t));
                     return cnt;
                 };
-                // largest T with at least `moves` keys >= T: the key of the last move
-                uint64_t T = 0;
-                for (int bit = 63; bit >= 0; --bit) {
-                    const uint64_t cand = T | (1ull << bit);
-                    if (count_ge(cand) >= moves) T = cand;
+                // high word: the largest H with at least `moves` keys whose high word >= H
+                uint32_t H = 0;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t cand = H | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int st = 0; st < MS; ++st)
+                        cnt += __popcll(__ballot(uint32_t(key0[st] >> 32) >= cand)) +
+                               __popcll(__ballot(uint32_t(key1[st] >> 32) >= cand));
+                    if (cnt >= moves) H = cand;
                 }
-                const int rem = moves - count_ge(T + 1);      // equal keys still to take
+                // keys with high word H: `need` of them are taken, the largest low words
+                const int need = moves - count_gt((uint64_t(H) << 32) | 0xFFFFFFFFull);
+                int neq = 0;
+                uint32_t L = 0;
+#pragma unroll
+                for (int st = 0; st < MS; ++st) {
+                    const unsigned long long e0 = __ballot(uint32_t(key0[st] >> 32) == H);
+                    const unsigned long long e1 = __ballot(uint32_t(key1[st] >> 32) == H);
+                    neq += __popcll(e0) + __popcll(e1);
+                    // (the low word of one of them, kept when it is the only one)
+                    if (e0) L = __builtin_amdgcn_readlane(uint32_t(key0[st]), __builtin_ctzll(e0));
+                    if (e1) L = __builtin_amdgcn_readlane(uint32_t(key1[st]), __builtin_ctzll(e1));
+                }
+                if (neq > 1) {
+                    L = 0;
+                    for (int bit = 31; bit >= 0; --bit) {
+                        const uint32_t cand = L | (1u << bit);
+                        int cnt = 0;
+#pragma unroll
+                        for (int st = 0; st < MS; ++st)
+                            cnt += __popcll(__ballot(uint32_t(key0[st] >> 32) == H && uint32_t(key0[st]) >= cand)) +
+                                   __popcll(__ballot(uint32_t(key1[st] >> 32) == H && uint32_t(key1[st]) >= cand));
+                        if (cnt >= need) L = cand;
+                    }
+                }
+                const uint64_t T = (uint64_t(H) << 32) | L;   // the key of the last move
+                const int rem = moves - count_gt(T);          // equal keys still to take
                 int a0 = 0, a1 = 0;
                 bool t0 = false, t1 = false;
 #pragma unroll
