@@ -118,6 +118,14 @@ __device__ __forceinline__ void unpack8(const Raw& raw, int boff, float code[8])
     }
 }
 
+// (y << s) + a as one instruction (the compiler otherwise splits such chains into
+// shifts and three-input adds)
+__device__ __forceinline__ uint32_t lshl_add(uint32_t y, int s, uint32_t a) {
+    uint32_t r;
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(y), "i"(s), "v"(a));
+    return r;
+}
+
 // Round 8 values on the row grid (magic-number FMA, med3 clamp) and write the packed
 // B-bit codes (B bytes) at byte `boff` of the staging copy.
 template <int B>
@@ -127,24 +135,32 @@ __device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8],
 #pragma unroll
     for (int c = 0; c < 8; ++c)
         y[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
-    uint32_t w0 = 0, w1 = 0, g0 = 0, g1 = 0;
+    // the constant high bits of every shifted y are removed once per word
+    uint32_t g0 = 0, g1 = 0;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int p = c * B;
+        if (p + B <= 32) g0 += kMagicBits << p;
+        else if (p >= 32) g1 += kMagicBits << (p - 32);
+    }
+    uint32_t w0 = y[0] - g0, w1 = 0u - g1;
+    bool w1_started = false;
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+        const int p = c * B;
         if (p + B <= 32) {
-            w0 += y[c] << p;
-            g0 += kMagicBits << p;
+            w0 = lshl_add(y[c], p, w0);
         } else if (p >= 32) {
-            w1 += y[c] << (p - 32);
-            g1 += kMagicBits << (p - 32);
+            if (!w1_started && p == 32) w1 = y[c] + w1;
+            else w1 = lshl_add(y[c], p - 32, w1);
+            w1_started = true;
         } else {
             const uint32_t code = y[c] - kMagicBits;
-            w0 += code << p;
+            w0 = lshl_add(code, p, w0);
             w1 += code >> (32 - p);
+            w1_started = true;
         }
     }
-    w0 -= g0;
-    w1 -= g1;
     uint8_t* bytes = reinterpret_cast<uint8_t*>(reg);
     if constexpr (B == 2) {
         *reinterpret_cast<uint16_t*>(bytes + boff) = uint16_t(w0);
