@@ -33,6 +33,7 @@ struct AllocSmem {
     float delta[DK];
     double R[DK], c[DK];
     float2 cand[DK][16];                       // (Delta_k, 1 / Delta_k) per row and fit index
+    int order[DK];                             // rows by increasing stored width
     int newwidth[DK];
     int newfit[DK];
     uint16_t newdelta[DK];
@@ -45,6 +46,16 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half mirror
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // mirror
     return v;
+}
+
+// one step of a (smallest error, then largest fit index) reduction over a DPP row
+template <int CTRL>
+__device__ __forceinline__ void argmin_step(float& be, int& best) {
+    const float oe = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(be), CTRL, 0xF, 0xF, false));
+    const int ob = __builtin_amdgcn_update_dpp(0, best, CTRL, 0xF, 0xF, false);
+    const bool take = oe < be || (oe == be && ob > best);
+    be = take ? oe : be;
+    best = take ? ob : best;
 }
 
 // number of set bits of a wavefront mask below the calling lane
@@ -87,14 +98,29 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         }
         sm.off[2 * lane] = incl - local;
         sm.off[2 * lane + 1] = incl - local + wv[0];
+        // rank of rows 2 lane and 2 lane + 1 in (stored width, row) order (ballots)
+        const int w0 = wv[0] / (DV / 8), w1 = wv[1] / (DV / 8);
+        int before = 0, pos0 = 0, pos1 = 0;
+#pragma unroll
+        for (int v = 1; v <= 8; ++v) {
+            const unsigned long long m0 = __ballot(w0 == v), m1 = __ballot(w1 == v);
+            const int below = lanes_below(m0) + lanes_below(m1);
+            if (w0 == v) pos0 = before + below;
+            if (w1 == v) pos1 = before + below + int(w0 == v);
+            before += __popcll(m0) + __popcll(m1);
+        }
+        sm.order[pos0] = 2 * lane;
+        sm.order[pos1] = 2 * lane + 1;
     }
     __syncthreads();
 
-    // stored values (exact in float32: |kappa| <= 127 times a float16 Delta)
+    // stored values (exact in float32: |kappa| <= 127 times a float16 Delta); the rows
+    // are visited in stored-width order, so the 4 rows of a wavefront step nearly
+    // always share a width
     float x[8][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const int row = rg + RS * m;
+        const int row = sm.order[rg + RS * m];
         const int bw = sm.width[row];
         const int n = (1 << (bw - 1)) - 1;
         const int off = sm.off[row] + cg * bw;
@@ -268,31 +294,79 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const int row = rg + RS * m;
+        const int row = sm.order[rg + RS * m];
         const int bw = sm.newwidth[row];
         const int n = (1 << (bw - 1)) - 1;
         const float lo = kMagic - float(n), hi = kMagic + float(n);
-        float err[16];
-#pragma unroll
-        for (int kf = 0; kf < 16; ++kf) {
-            const float2 dk = sm.cand[row][kf];
-            float e = 0.f;
+        const int bwo = sm.width[row];
+        int best;
+        if (bwo <= 5) {
+            // Stored values lie on the old grid (kappa Delta_old) and a value's error
+            // depends only on a = |kappa| <= n_old <= 15: count the levels over the
+            // row (4-bit fields per lane, then 8-bit fields summed over its 16 lanes)
+            // and let lane cg evaluate fit index cg as a sum over the levels.
+            const float dl = sm.delta[row];
+            const float inv4 = dl > 0.f ? 4.f / dl : 0.f;
+            uint64_t h = 0;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[m][c], dk.y, kMagic), lo, hi);
-                const float r = __builtin_fmaf(-dk.x, y - kMagic, x[m][c]);
-                e = __builtin_fmaf(r, r, e);
+                const uint32_t a4 = uint32_t(__builtin_fmaf(fabsf(x[m][c]), inv4, 0.5f));   // 4 a
+                h += 1ull << a4;
             }
-            err[kf] = row16_sum(e);
-        }
-        int best = 15;
-        float be = err[15];
+            uint32_t cnt[4] = {uint32_t(h) & 0x0F0F0F0Fu, uint32_t(h >> 4) & 0x0F0F0F0Fu,
+                               uint32_t(h >> 32) & 0x0F0F0F0Fu, uint32_t(h >> 36) & 0x0F0F0F0Fu};
 #pragma unroll
-        for (int kf = 14; kf >= 0; --kf)     // ties go to the larger f
-            if (err[kf] < be) {
-                be = err[kf];
-                best = kf;
+            for (int i = 0; i < 4; ++i) {
+                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0xB1, 0xF, 0xF, false));
+                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x4E, 0xF, 0xF, false));
+                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x141, 0xF, 0xF, false));
+                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x140, 0xF, 0xF, false));
             }
+            // cnt[0]: levels 0, 2, 4, 6; cnt[1]: 1, 3, 5, 7; cnt[2]: 8, 10, ..; cnt[3]: 9, 11, ..
+            const float2 dk = sm.cand[row][cg];
+            const int nold = (1 << (bwo - 1)) - 1;
+            float e = 0.f;
+#pragma unroll
+            for (int a = 1; a < 16; ++a) {
+                if (a <= nold) {
+                    const uint32_t word = cnt[(a & 1) + 2 * (a >> 3)];
+                    const float ca = float((word >> (8 * ((a >> 1) & 3))) & 255u);
+                    const float xa = float(a) * dl;                          // exact
+                    const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(xa, dk.y, kMagic), lo, hi);
+                    const float r = __builtin_fmaf(-dk.x, y - kMagic, xa);
+                    e = __builtin_fmaf(ca * r, r, e);
+                }
+            }
+            // smallest error over the 16 lanes of the row, ties to the larger f
+            float be = e;
+            best = cg;
+            argmin_step<0xB1>(be, best);
+            argmin_step<0x4E>(be, best);
+            argmin_step<0x141>(be, best);
+            argmin_step<0x140>(be, best);
+        } else {
+            float err[16];
+#pragma unroll
+            for (int kf = 0; kf < 16; ++kf) {
+                const float2 dk = sm.cand[row][kf];
+                float e = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[m][c], dk.y, kMagic), lo, hi);
+                    const float r = __builtin_fmaf(-dk.x, y - kMagic, x[m][c]);
+                    e = __builtin_fmaf(r, r, e);
+                }
+                err[kf] = row16_sum(e);
+            }
+            best = 15;
+            float be = err[15];
+#pragma unroll
+            for (int kf = 14; kf >= 0; --kf)     // ties go to the larger f
+                if (err[kf] < be) {
+                    be = err[kf];
+                    best = kf;
+                }
+        }
         const float2 dk = sm.cand[row][best];
         const uint16_t dbits = f32_to_f16_bits(dk.x);
         uint64_t fld = 0;

@@ -273,6 +273,9 @@ def _alloc_case(case, rng, B, H, dk):
 
 @pytest.mark.parametrize("case", ["warm", "groups", "spread"])
 def test_allocate_bits_matches_oracle(case):
+    """Two allocation passes per head: the first from the imported state (every row at
+    the mean width), the second, with the decays reversed across rows, from the mixed
+    widths the first one left (rows stored with 2 to 8 bits)."""
     print(f"\n[case] allocate_bits {case} B=2 H=4", flush=True)
     B, H, dk = 2, 4, 128
     lay = _layout(L.BITALLOC, "rtn", B, H, dk)
@@ -281,37 +284,44 @@ def test_allocate_bits_matches_oracle(case):
     S, s = _alloc_case(case, rng, B, H, dk)
     st.quantize(_to_dev(S))
     r = np.full((B, H, dk), 1.0 / (3 * dk), dtype=np.float32)
-    torch.cuda.synchronize()
-    before = st.regions().cpu().numpy()
-    st.allocate_bits(_to_dev(s), _to_dev(r))
-    torch.cuda.synchronize()
-    after = st.regions().cpu().numpy()
     moved = 0
-    for b in range(B):
-        for h in range(H):
-            reg_in = before[b * H + h][: lay.region_size()]
-            reg_gpu = after[b * H + h][: lay.region_size()]
-            reg_orc, alloc = allocate_region(lay, reg_in, s[b, h].astype(np.float64), r[b, h].astype(np.float64))
-            g = L.decode_region(lay, reg_gpu)
-            o = L.decode_region(lay, reg_orc)
-            assert g.widths.sum() == 512
-            moved += int(np.abs(np.clip(np.rint(alloc["bstar"]), lay.bmin, lay.bmax) - o.widths).sum())
-            if not np.array_equal(g.widths, o.widths):
-                # only near-ties of the real widths may differ
-                bad = np.argwhere(g.widths != o.widths).ravel()
-                frac = np.abs(alloc["bstar"][bad] - np.floor(alloc["bstar"][bad]) - 0.5)
-                assert np.all(frac < 1e-5), (b, h, bad, alloc["bstar"][bad])
-                continue
-            if not np.array_equal(g.fit, o.fit):
-                bad = np.argwhere(g.fit != o.fit).ravel()
-                for i in bad:
-                    e = alloc["fit_err"][i]
-                    assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (b, h, i)
-                continue
-            assert np.array_equal(reg_gpu, reg_orc), (b, h)
-    print(f"[alloc] one-bit moves over the heads: {moved}", flush=True)
+    wide_rows = 0
+    for pas, s_pass in enumerate((s, np.ascontiguousarray(s[..., ::-1]))):
+        torch.cuda.synchronize()
+        before = st.regions().cpu().numpy()
+        st.allocate_bits(_to_dev(s_pass), _to_dev(r))
+        torch.cuda.synchronize()
+        after = st.regions().cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                reg_in = before[b * H + h][: lay.region_size()]
+                reg_gpu = after[b * H + h][: lay.region_size()]
+                reg_orc, alloc = allocate_region(lay, reg_in, s_pass[b, h].astype(np.float64),
+                                                 r[b, h].astype(np.float64))
+                if pas == 1:
+                    wide_rows += int((L.decode_region(lay, reg_in).widths >= 6).sum())
+                g = L.decode_region(lay, reg_gpu)
+                o = L.decode_region(lay, reg_orc)
+                assert g.widths.sum() == 512
+                moved += int(np.abs(np.clip(np.rint(alloc["bstar"]), lay.bmin, lay.bmax) - o.widths).sum())
+                if not np.array_equal(g.widths, o.widths):
+                    # only near-ties of the real widths may differ
+                    bad = np.argwhere(g.widths != o.widths).ravel()
+                    frac = np.abs(alloc["bstar"][bad] - np.floor(alloc["bstar"][bad]) - 0.5)
+                    assert np.all(frac < 1e-5), (pas, b, h, bad, alloc["bstar"][bad])
+                    continue
+                if not np.array_equal(g.fit, o.fit):
+                    bad = np.argwhere(g.fit != o.fit).ravel()
+                    for i in bad:
+                        e = alloc["fit_err"][i]
+                        assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (pas, b, h, i)
+                    continue
+                assert np.array_equal(reg_gpu, reg_orc), (pas, b, h)
+    print(f"[alloc] one-bit moves over the heads: {moved}; rows stored with 6+ bits before the second pass: "
+          f"{wide_rows}", flush=True)
     if case != "warm":
         assert moved >= 50 * B * H
+    assert wide_rows > 0
 
 
 def test_allocation_then_decode_full_budget_zero_state():
