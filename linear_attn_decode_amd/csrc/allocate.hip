@@ -26,6 +26,31 @@ namespace {
 
 constexpr int DK = 128, DV = 128, NT = 256, NCG = 16, RS = 16;
 constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
+constexpr uint32_t kMagicBits = 0x4B400000u;
+
+// float64 -> float16 bits, correctly rounded (nearest, ties to even): rounding to odd
+// at float32 precision, then the hardware conversion (Boldo & Melquiond, IEEE Trans.
+// Computers 2008: a rounding to odd with at least two more bits than the target
+// followed by the final rounding is the correct rounding)
+__device__ __forceinline__ uint16_t f64_to_f16_rto(double x) {
+    const float f = float(x);
+    uint32_t fb = __float_as_uint(f);
+    const double back = double(f);
+    if (back != x) {
+        if (fabs(back) > fabs(x)) fb -= 1u;   // one step toward zero: the truncation
+        fb |= 1u;                             // sticky bit: round to odd
+    }
+    return __half_as_ushort(__float2half_rn(__uint_as_float(fb)));
+}
+
+// fit fractions f_k = 1/4 + k/20 in float64 (the same operations, at compile time)
+struct FitTable {
+    double f[16];
+    constexpr FitTable() : f() {
+        for (int k = 0; k < 16; ++k) f[k] = 0.25 + k / 20.0;
+    }
+};
+__constant__ FitTable kFit = FitTable();
 
 struct AllocSmem {
     uint32_t reg[(DK * DV + 3 * DK) / 4 + 4];
@@ -56,6 +81,69 @@ __device__ __forceinline__ void argmin_step(float& be, int& best) {
     const bool take = oe < be || (oe == be && ob > best);
     be = take ? oe : be;
     best = take ? ob : best;
+}
+
+// Clipping fit of one row from level counts. The row's stored values lie on its old
+// grid (kappa Delta_old) and a value's rounding error depends only on a = |kappa| <=
+// n_old < 16 NWD: each lane counts the levels of its 8 values in 4-bit fields (NWD
+// 64-bit words), the counts are widened to 8-bit fields and summed over the row's 16
+// lanes, lane cg evaluates fit index cg (step dk.x, reciprocal dk.y, levels clamped to
+// [lo, hi] in magic-number form) as a sum over the levels, and the row's smallest error
+// (ties to the larger f) is found over the 16 lanes.
+template <int NWD>
+__device__ __forceinline__ int level_fit(const float x[8], float dl, int nold, float2 dk, float lo, float hi,
+                                         int cg) {
+    const float inv4 = dl > 0.f ? 4.f / dl : 0.f;
+    uint64_t h[NWD];
+#pragma unroll
+    for (int w = 0; w < NWD; ++w) h[w] = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t a4 = uint32_t(__builtin_fmaf(fabsf(x[c]), inv4, 0.5f));     // 4 a
+        const uint64_t one = 1ull << (a4 & 63);
+        if constexpr (NWD == 1) {
+            h[0] += one;
+        } else {
+            h[0] += a4 < 64 ? one : 0ull;
+            h[1] += a4 < 64 ? 0ull : one;
+        }
+    }
+    // cnt[4 w + 0]: levels 16 w + 0, 2, 4, 6; + 1: 1, 3, 5, 7; + 2: 8, 10, ..; + 3: 9, 11, ..
+    uint32_t cnt[4 * NWD];
+#pragma unroll
+    for (int w = 0; w < NWD; ++w) {
+        cnt[4 * w + 0] = uint32_t(h[w]) & 0x0F0F0F0Fu;
+        cnt[4 * w + 1] = uint32_t(h[w] >> 4) & 0x0F0F0F0Fu;
+        cnt[4 * w + 2] = uint32_t(h[w] >> 32) & 0x0F0F0F0Fu;
+        cnt[4 * w + 3] = uint32_t(h[w] >> 36) & 0x0F0F0F0Fu;
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * NWD; ++i) {
+        cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0xB1, 0xF, 0xF, false));
+        cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x4E, 0xF, 0xF, false));
+        cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x141, 0xF, 0xF, false));
+        cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x140, 0xF, 0xF, false));
+    }
+    float e = 0.f;
+#pragma unroll
+    for (int a = 1; a < 16 * NWD; ++a) {
+        if (a <= nold) {
+            const int l = a & 15;
+            const uint32_t word = cnt[4 * (a >> 4) + (l & 1) + 2 * (l >> 3)];
+            const float ca = float((word >> (8 * ((l >> 1) & 3))) & 255u);
+            const float xa = float(a) * dl;                                  // exact
+            const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(xa, dk.y, kMagic), lo, hi);
+            const float r = __builtin_fmaf(-dk.x, y - kMagic, xa);
+            e = __builtin_fmaf(ca * r, r, e);
+        }
+    }
+    float be = e;
+    int best = cg;
+    argmin_step<0xB1>(be, best);
+    argmin_step<0x4E>(be, best);
+    argmin_step<0x141>(be, best);
+    argmin_step<0x140>(be, best);
+    return best;
 }
 
 // number of set bits of a wavefront mask below the calling lane
@@ -286,13 +374,17 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     for (int i = tid; i < DK * 16; i += NT) {
         const int row = i >> 4, kf = i & 15;
         const int n = (1 << (sm.newwidth[row] - 1)) - 1;
-        const float d = f16_bits_to_f32(f64_to_f16_bits((0.25 + kf / 20.0) * sm.R[row] / n));
-        sm.cand[row][kf] = make_float2(d, d > 0.f ? 1.f / d : 0.f);
+        const float d = f16_bits_to_f32(f64_to_f16_rto(kFit.f[kf] * sm.R[row] / n));
+        // reciprocal refined by one Newton step: it only orders candidate errors and
+        // pre-rounds the repack, which falls back to an exact quotient near half-integers
+        float r = __builtin_amdgcn_rcpf(d);
+        r = __builtin_fmaf(__builtin_fmaf(-d, r, 1.f), r, r);
+        sm.cand[row][kf] = make_float2(d, d > 0.f ? r : 0.f);
     }
     // clipping fit and repack
     for (int i = tid; i < code_bytes / 4; i += NT) sm.reg[i] = 0u;
     __syncthreads();
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int m = 0; m < 8; ++m) {
         const int row = sm.order[rg + RS * m];
         const int bw = sm.newwidth[row];
@@ -301,49 +393,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         const int bwo = sm.width[row];
         int best;
         if (bwo <= 5) {
-            // Stored values lie on the old grid (kappa Delta_old) and a value's error
-            // depends only on a = |kappa| <= n_old <= 15: count the levels over the
-            // row (4-bit fields per lane, then 8-bit fields summed over its 16 lanes)
-            // and let lane cg evaluate fit index cg as a sum over the levels.
-            const float dl = sm.delta[row];
-            const float inv4 = dl > 0.f ? 4.f / dl : 0.f;
-            uint64_t h = 0;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint32_t a4 = uint32_t(__builtin_fmaf(fabsf(x[m][c]), inv4, 0.5f));   // 4 a
-                h += 1ull << a4;
-            }
-            uint32_t cnt[4] = {uint32_t(h) & 0x0F0F0F0Fu, uint32_t(h >> 4) & 0x0F0F0F0Fu,
-                               uint32_t(h >> 32) & 0x0F0F0F0Fu, uint32_t(h >> 36) & 0x0F0F0F0Fu};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0xB1, 0xF, 0xF, false));
-                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x4E, 0xF, 0xF, false));
-                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x141, 0xF, 0xF, false));
-                cnt[i] += uint32_t(__builtin_amdgcn_update_dpp(0, int(cnt[i]), 0x140, 0xF, 0xF, false));
-            }
-            // cnt[0]: levels 0, 2, 4, 6; cnt[1]: 1, 3, 5, 7; cnt[2]: 8, 10, ..; cnt[3]: 9, 11, ..
-            const float2 dk = sm.cand[row][cg];
-            const int nold = (1 << (bwo - 1)) - 1;
-            float e = 0.f;
-#pragma unroll
-            for (int a = 1; a < 16; ++a) {
-                if (a <= nold) {
-                    const uint32_t word = cnt[(a & 1) + 2 * (a >> 3)];
-                    const float ca = float((word >> (8 * ((a >> 1) & 3))) & 255u);
-                    const float xa = float(a) * dl;                          // exact
-                    const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(xa, dk.y, kMagic), lo, hi);
-                    const float r = __builtin_fmaf(-dk.x, y - kMagic, xa);
-                    e = __builtin_fmaf(ca * r, r, e);
-                }
-            }
-            // smallest error over the 16 lanes of the row, ties to the larger f
-            float be = e;
-            best = cg;
-            argmin_step<0xB1>(be, best);
-            argmin_step<0x4E>(be, best);
-            argmin_step<0x141>(be, best);
-            argmin_step<0x140>(be, best);
+            best = level_fit<1>(x[m], sm.delta[row], (1 << (bwo - 1)) - 1, sm.cand[row][cg], lo, hi, cg);
+        } else if (bwo == 6) {
+            best = level_fit<2>(x[m], sm.delta[row], (1 << (bwo - 1)) - 1, sm.cand[row][cg], lo, hi, cg);
         } else {
             float err[16];
 #pragma unroll
@@ -372,16 +424,17 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         uint64_t fld = 0;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            // nearest level, ties to even, of the exact quotient x / Delta
-            float kap = 0.f;
-            if (dk.x != 0.f) {
-                const float t = x[m][c] * dk.y;
-                kap = rintf(t);
-                if (fabsf(fabsf(t - kap) - 0.5f) <= 0x1.0p-10f)
-                    kap = float(rint(double(x[m][c]) / double(dk.x)));
-                kap = fminf(fmaxf(kap, float(-n)), float(n));
-            }
-            fld |= uint64_t(int(kap) + n) << (c * bw);
+            // nearest level, ties to even, of the exact quotient x / Delta: x / Delta +
+            // 1.5 * 2^23 rounded once (its fraction, x / Delta - level, one more FMA);
+            // within 2^-10 of a half-integer the quotient is recomputed in float64
+            float q = __builtin_fmaf(x[m][c], dk.y, kMagic);
+            const float lev = q - kMagic;
+            const float fr = __builtin_fmaf(x[m][c], dk.y, -lev);
+            if (__builtin_expect(fabsf(fabsf(fr) - 0.5f) <= 0x1.0p-10f, 0) && dk.x != 0.f)
+                q = float(rint(double(x[m][c]) / double(dk.x))) + kMagic;
+            q = __builtin_amdgcn_fmed3f(q, lo, hi);
+            const uint32_t code = __float_as_uint(q) - (kMagicBits - uint32_t(n));   // level + n
+            fld |= uint64_t(code) << (c * bw);
         }
         const int off = sm.newoff[row] + cg * bw;
         const int wi = off >> 2, sh = (off & 3) * 8;
