@@ -50,6 +50,7 @@ struct RotSmem {
     double part[4][DV];              // (uP, pP, uQ, pQ) of the second half, then the sums
     double w[DV], hw[DV];
     double qk[2];
+    double zoff[2][2];               // (sum k a zero, sum q a zero) per wavefront (one block per row)
     uint32_t reg[LY::REGION / 4];
 };
 
@@ -166,9 +167,31 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         if (lane == 0) sm.qk[wave] = pq;
     }
     __syncthreads();
-    for (int i = tid; i < LY::NQ * LY::NB; i += NT) {
-        const uint32_t m = sm.reg[LY::META_BASE / 4 + i];
-        sm.sz[i] = make_double2(f16_to_f64(m & 0xFFFFu), f16_to_f64(m >> 16));
+    constexpr bool kRowBlocks = KHI == 0 && BLOCK == DV;   // one INT8 block per row
+    if constexpr (kRowBlocks) {
+        // one block per row: the contraction over rows folds the step into the row
+        // weights, sum_r c_r (zero_r + code scale_r) = sum_r (c_r scale_r) code +
+        // sum_r c_r zero_r, and the offsets are summed once
+        if (wave < 2) {
+            const int i = tid;
+            const uint32_t m = sm.reg[LY::META_BASE / 4 + i];
+            const double sc = f16_to_f64(m & 0xFFFFu), zr = f16_to_f64(m >> 16);
+            sm.sz[i] = make_double2(sc, zr);
+            const double2 c = sm.kq[i];
+            sm.kq[i] = make_double2(c.x * sc, c.y * sc);
+            double zu = c.x * zr, zp = c.y * zr;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                zu += __shfl_xor(zu, d, 64);
+                zp += __shfl_xor(zp, d, 64);
+            }
+            if (lane == 0) sm.zoff[wave][0] = zu, sm.zoff[wave][1] = zp;
+        }
+    } else {
+        for (int i = tid; i < LY::NQ * LY::NB; i += NT) {
+            const uint32_t m = sm.reg[LY::META_BASE / 4 + i];
+            sm.sz[i] = make_double2(f16_to_f64(m & 0xFFFFu), f16_to_f64(m >> 16));
+        }
     }
     __syncthreads();
 
@@ -187,13 +210,27 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             }
         }
         const int g = j / BLOCK;
+        if constexpr (kRowBlocks) {
 #pragma unroll 4
-        for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
-            const double2 s = sm.sz[qr * LY::NB + g];
-            const double y = fma(double(lb[LY::CODE_BASE + qr * DV + j]), s.x, s.y);
-            const double2 c = sm.kq[qr + KHI];
-            uQ = fma(c.x, y, uQ);
-            pQ = fma(c.y, y, pQ);
+            for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
+                const double code = double(lb[LY::CODE_BASE + qr * DV + j]);
+                const double2 c = sm.kq[qr];             // (k a scale, q a scale)
+                uQ = fma(c.x, code, uQ);
+                pQ = fma(c.y, code, pQ);
+            }
+            if (half == 0) {
+                uQ += sm.zoff[0][0] + sm.zoff[1][0];
+                pQ += sm.zoff[0][1] + sm.zoff[1][1];
+            }
+        } else {
+#pragma unroll 4
+            for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
+                const double2 s = sm.sz[qr * LY::NB + g];
+                const double y = fma(double(lb[LY::CODE_BASE + qr * DV + j]), s.x, s.y);
+                const double2 c = sm.kq[qr + KHI];
+                uQ = fma(c.x, y, uQ);
+                pQ = fma(c.y, y, pQ);
+            }
         }
         if (half == 1) {
             sm.part[0][j] = uP;
