@@ -12,7 +12,8 @@
 //   * u and p (contractions over rows) run column-parallel: thread (j, half) walks
 //     half of the rows of column j, so the only cross-thread step is adding two
 //     halves; the float64 step and offset of every INT8 block are tabulated once;
-//   * the three 128-point transforms (H uQ, H pQ, H w) run on one wavefront;
+//   * the three 128-point transforms run on wavefronts (H uQ then H w on one, H pQ on
+//     another);
 //   * the update and the requantization run row-parallel (lane = 4 rows x 16 columns,
 //     so a block of 32 values spans 2 lanes) with float64 element arithmetic and the
 //     block minimum / maximum by DPP;
@@ -145,6 +146,14 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     uint8_t* region = A.state + (size_t)head * A.region_stride;
     uint8_t* lb = reinterpret_cast<uint8_t*>(sm.reg);
 
+    // v and beta for the vector phase, requested first
+    float v_lo = 0.f, v_hi = 0.f, beta_in = 0.f;
+    if (wave == 0) {
+        v_lo = A.v[(size_t)head * DV + lane];
+        v_hi = A.v[(size_t)head * DV + lane + 64];
+        beta_in = A.beta[head];
+    }
+
     // ---- stage the region; per-row tables in physical row order -----------------------
     {
         const uint4* src = reinterpret_cast<const uint4*>(region);
@@ -249,27 +258,30 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     }
 
     // ---- w = beta (v - u), o = p + (q . k) w, H w (one wavefront) ----------------------
+    // (wavefront 0: u, w and H w; wavefront 1: p, in parallel; o after the barrier)
     if (wave == 0) {
         double uq0 = sm.part[2][lane], uq1 = sm.part[2][lane + 64];
-        double pq0 = sm.part[3][lane], pq1 = sm.part[3][lane + 64];
         wht128(uq0, uq1, lane);
-        wht128(pq0, pq1, lane);
-        const double qk = sm.qk[0] + sm.qk[1];
-        const double beta = double(A.beta[head]);
         const double u0 = sm.part[0][lane] + uq0, u1 = sm.part[0][lane + 64] + uq1;
-        const double p0 = sm.part[1][lane] + pq0, p1 = sm.part[1][lane + 64] + pq1;
-        const double w0 = beta * (double(A.v[(size_t)head * DV + lane]) - u0);
-        const double w1 = beta * (double(A.v[(size_t)head * DV + lane + 64]) - u1);
-        A.o[(size_t)head * DV + lane] = float(p0 + qk * w0);
-        A.o[(size_t)head * DV + lane + 64] = float(p1 + qk * w1);
+        const double w0 = double(beta_in) * (double(v_lo) - u0);
+        const double w1 = double(beta_in) * (double(v_hi) - u1);
         sm.w[lane] = w0;
         sm.w[lane + 64] = w1;
         double r0 = w0, r1 = w1;
         wht128(r0, r1, lane);
         sm.hw[lane] = r0;
         sm.hw[lane + 64] = r1;
+    } else if (wave == 1) {
+        double pq0 = sm.part[3][lane], pq1 = sm.part[3][lane + 64];
+        wht128(pq0, pq1, lane);
+        sm.part[3][lane] = sm.part[1][lane] + pq0;
+        sm.part[3][lane + 64] = sm.part[1][lane + 64] + pq1;
     }
     __syncthreads();
+    if (tid >= NT - DV) {
+        const int j = tid - (NT - DV);
+        A.o[(size_t)head * DV + j] = float(sm.part[3][j] + (sm.qk[0] + sm.qk[1]) * sm.w[j]);
+    }
 
     // ---- update and requantize in place (lane = 4 rows x 16 columns) -------------------
     // A block of BLOCK columns of a row spans BLOCK / 16 lanes, so its range, step and
