@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             __syncthreads();
         }
 
-        // ---- per column: forward solve for w, outputs o ------------------------------
+        // ---- per column: forward solve for w (threads 0..127) ------------------------
         if (tid < DV) {
             const int j = tid;
             float wv[SEG];
@@ -358,6 +358,16 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 wv[tt] = sm.beta[tt] * u;
                 sm.w[tt][j] = wv[tt];
             }
+        }
+        // inputs of the next segment (requested before this segment's output stores)
+        if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C), tid, my_lr, nxt);
+        __syncthreads();
+        // ---- outputs o (threads 128..255) beside H w (threads 0..127) ------------------
+        if (tid >= NT - DV) {
+            const int j = tid - (NT - DV);
+            float wv[SEG];
+#pragma unroll
+            for (int tt = 0; tt < SEG; ++tt) wv[tt] = sm.w[tt][j];
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
                 if (tt < L) {
@@ -367,23 +377,18 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                     P.o[(((size_t)b * T + t + tt) * H + h) * DV + j] = o;
                 }
             }
-        }
-        // inputs of the next segment: requested after this segment's output stores, so
-        // that waiting for them never waits for those stores
-        if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C), tid, my_lr, nxt);
-        __syncthreads();
-        if (LY::ROT) {
-            // H w for the rotated rows: two vectors per wave
+        } else if (LY::ROT) {
+            // H w for the rotated rows: four vectors per wave
 #pragma unroll
-            for (int vv = 0; vv < 2; ++vv) {
-                const int m = 2 * wave + vv;
+            for (int vv = 0; vv < 4; ++vv) {
+                const int m = 4 * wave + vv;
                 float a0 = sm.w[m][lane], a1 = sm.w[m][lane + 64];
                 wave_wht128(a0, a1, lane);
                 sm.hw[m][lane] = a0;
                 sm.hw[m][lane + 64] = a1;
             }
-            __syncthreads();
         }
+        if (LY::ROT) __syncthreads();
 
         // ---- S_L = Gamma_L S_0 + sum_tau (Gamma_L k-_tau) w_tau^T  (MFMA, K = 8) ------
 #pragma unroll
