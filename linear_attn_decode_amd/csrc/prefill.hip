@@ -124,11 +124,12 @@ struct PfLayout {
     __device__ static bool rotated(int rt) { return KIND == WB_HAD_INT8 || (KIND == WB_MIXED && rt > 0); }
 };
 
-// One segment's inputs as this thread reads them: threads 0..127 own physical row
-// `tid` (k, q and the decay of every token), every thread owns 4 values of v, and
-// threads 0..7 one beta each. Loaded a segment ahead into registers.
+// One segment's inputs as this thread reads them: thread t owns physical row t % 128
+// for the tokens 4 (t / 128) .. +3 (k and q; the decays of all the segment's tokens),
+// every thread owns 4 values of v, and threads 0..7 one beta each. Loaded a segment
+// ahead into registers.
 struct SegIn {
-    uint16_t kk[SEG], qq[SEG];
+    uint16_t kk[SEG / 2], qq[SEG / 2];
     float sv[SEG];
     uint16_t vv[SEG * DV / NT];
     float beta;
@@ -138,18 +139,24 @@ __device__ __forceinline__ void load_segment(const PrefillArgs& P, int b, int h,
                                              SegIn& in) {
     const KArgs& A = P.base;
     const int H = A.H, T = P.T;
-    if (tid < DK) {
+    const int half = tid / DK;
 #pragma unroll
-        for (int tt = 0; tt < SEG; ++tt) {
-            in.kk[tt] = 0;
-            in.qq[tt] = 0;
-            in.sv[tt] = 0.f;
-            if (tt < L) {
-                const size_t base = ((size_t)b * T + t + tt) * H + h;
-                in.sv[tt] = A.s_per_row ? P.s[base * DK + lr] : P.s[base];
-                in.kk[tt] = P.k[base * DK + lr];
-                in.qq[tt] = P.q[base * DK + lr];
-            }
+    for (int tt = 0; tt < SEG; ++tt) {
+        in.sv[tt] = 0.f;
+        if (tt < L) {
+            const size_t base = ((size_t)b * T + t + tt) * H + h;
+            in.sv[tt] = A.s_per_row ? P.s[base * DK + lr] : P.s[base];
+        }
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < SEG / 2; ++t4) {
+        const int tt = (SEG / 2) * half + t4;
+        in.kk[t4] = 0;
+        in.qq[t4] = 0;
+        if (tt < L) {
+            const size_t base = ((size_t)b * T + t + tt) * H + h;
+            in.kk[t4] = P.k[base * DK + lr];
+            in.qq[t4] = P.q[base * DK + lr];
         }
     }
 #pragma unroll
@@ -223,7 +230,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
     __syncthreads();
 
     const int T = P.T;
-    const int my_lr = tid < DK ? sm.perm[tid] : 0;
+    const int my_lr = sm.perm[tid & (DK - 1)];
     SegIn nxt;
     load_segment(P, b, h, 0, segment_length(0, T, P.C), tid, my_lr, nxt);
     int t = 0;
@@ -239,8 +246,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             sm.v[tt][j] = bf16f(cur.vv[n]);
         }
         if (tid < SEG) sm.beta[tid] = cur.beta;
-        if (tid < DK) {
-            const int p = tid;
+        {
+            // thread t: row t % 128, tokens 4 (t / 128) .. +3
+            const int p = tid & (DK - 1), half = tid / DK;
             float g[SEG];
             float acc = 0.f;
 #pragma unroll
@@ -251,9 +259,11 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             const float gL = g[L - 1];
             const float decL = expf(-gL);
 #pragma unroll
-            for (int tt = 0; tt < SEG; ++tt) {
-                const float kk = bf16f(cur.kk[tt]), qq = bf16f(cur.qq[tt]);
-                const float dec = __expf(-g[tt]);    // hardware exp2 of the scaled argument
+            for (int t4 = 0; t4 < SEG / 2; ++t4) {
+                const int tt = (SEG / 2) * half + t4;
+                const float gt = half ? g[SEG / 2 + t4] : g[t4];
+                const float kk = bf16f(cur.kk[t4]), qq = bf16f(cur.qq[t4]);
+                const float dec = __expf(-gt);       // hardware exp2 of the scaled argument
                 const float inc = __builtin_amdgcn_rcpf(dec);      // e^{g}, within an ulp or two
                 sm.khat[tt][p] = kk * dec;
                 sm.qhat[tt][p] = qq * dec;
@@ -262,7 +272,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 sm.kbar[tt][p] = kk * inc;
                 sm.kbarL[tt][p] = kk * (inc * decL);
             }
-            sm.gl[p] = decL;
+            if (half == 0) sm.gl[p] = decL;
         }
         __syncthreads();
         // small Gram matrices: A[t][tau] = k^_t . k-_tau (tau < t), QK[t][tau] (tau <= t);
