@@ -45,13 +45,17 @@ struct RotLayout {
 template <int KHI, int BLOCK>
 struct RotSmem {
     using LY = RotLayout<KHI, BLOCK>;
-    double2 kq[DK];                  // (k a, q a) per physical row
+    // (uP, pP, uQ, pQ) of the second half, then the sums; before the contraction its
+    // first half holds (k a, q a) per physical row
+    double part[4][DV];
+    double2 kqh[KHI > 0 ? KHI : 1];  // (k a, q a) of the float16 rows
     double2 ak[DK];                  // (a, k)
-    double2 sz[LY::NQ * LY::NB];     // float64 (step, offset) of every INT8 block
-    double part[4][DV];              // (uP, pP, uQ, pQ) of the second half, then the sums
+    float2 sz[LY::NQ * LY::NB];      // (step, offset) of every INT8 block (float16 values)
+    double2 kqs[LY::NQ * LY::NB];    // (k a step, q a step) of every INT8 block
+    double zsum[4][LY::NB][2];       // per wavefront and block column: (sum k a offset, sum q a offset)
+    static constexpr int ZW = (LY::NQ * LY::NB + 63) / 64 < 4 ? (LY::NQ * LY::NB + 63) / 64 : 4;
     double w[DV], hw[DV];
     double qk[2];
-    double zoff[2][2];               // (sum k a zero, sum q a zero) per wavefront (one block per row)
     uint32_t reg[LY::REGION / 4];
 };
 
@@ -145,6 +149,8 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     const int h = head % A.H;
     uint8_t* region = A.state + (size_t)head * A.region_stride;
     uint8_t* lb = reinterpret_cast<uint8_t*>(sm.reg);
+    double2* kq = reinterpret_cast<double2*>(&sm.part[0][0]);
+    constexpr int kZW = RotSmem<KHI, BLOCK>::ZW;     // wavefronts that hold INT8 blocks
 
     // v and beta for the vector phase, requested first
     float v_lo = 0.f, v_hi = 0.f, beta_in = 0.f;
@@ -168,7 +174,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         const double qd = double(A.q[(size_t)head * DK + lr]);
         const float sv = A.s_per_row ? A.s[(size_t)head * DK + lr] : A.s[head];
         const double ad = exp(-double(sv));
-        sm.kq[p] = make_double2(kd * ad, qd * ad);
+        kq[p] = make_double2(kd * ad, qd * ad);
         sm.ak[p] = make_double2(ad, kd);
         double pq = qd * kd;
 #pragma unroll
@@ -176,31 +182,35 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         if (lane == 0) sm.qk[wave] = pq;
     }
     __syncthreads();
-    constexpr bool kRowBlocks = KHI == 0 && BLOCK == DV;   // one INT8 block per row
-    if constexpr (kRowBlocks) {
-        // one block per row: the contraction over rows folds the step into the row
-        // weights, sum_r c_r (zero_r + code scale_r) = sum_r (c_r scale_r) code +
-        // sum_r c_r zero_r, and the offsets are summed once
-        if (wave < 2) {
-            const int i = tid;
+    // The contraction over rows folds each INT8 block's step into the row weights:
+    // sum_r c_r (offset_rg + code step_rg) = sum_r (c_r step_rg) code + sum_r c_r offset_rg,
+    // with the offset sums (one per block column g) formed here once. Thread t handles
+    // the blocks t, t + 256, .. (all of block column t % NB).
+    {
+        double zu = 0.0, zp = 0.0;
+        for (int i = tid; i < LY::NQ * LY::NB; i += NT) {
             const uint32_t m = sm.reg[LY::META_BASE / 4 + i];
-            const double sc = f16_to_f64(m & 0xFFFFu), zr = f16_to_f64(m >> 16);
-            sm.sz[i] = make_double2(sc, zr);
-            const double2 c = sm.kq[i];
-            sm.kq[i] = make_double2(c.x * sc, c.y * sc);
-            double zu = c.x * zr, zp = c.y * zr;
+            const float sc = f16_bits_to_f32(m & 0xFFFFu), zr = f16_bits_to_f32(m >> 16);
+            sm.sz[i] = make_float2(sc, zr);
+            const double2 c = kq[i / LY::NB + KHI];
+            sm.kqs[i] = make_double2(c.x * double(sc), c.y * double(sc));
+            zu = fma(c.x, double(zr), zu);
+            zp = fma(c.y, double(zr), zp);
+        }
+        // sum over the lanes of one block column (lanes equal modulo NB), on the
+        // wavefronts that hold blocks
+        if (wave < kZW) {
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
+            for (int d = LY::NB; d < 64; d <<= 1) {
                 zu += __shfl_xor(zu, d, 64);
                 zp += __shfl_xor(zp, d, 64);
             }
-            if (lane == 0) sm.zoff[wave][0] = zu, sm.zoff[wave][1] = zp;
+            if (lane < LY::NB) {
+                sm.zsum[wave][lane][0] = zu;
+                sm.zsum[wave][lane][1] = zp;
+            }
         }
-    } else {
-        for (int i = tid; i < LY::NQ * LY::NB; i += NT) {
-            const uint32_t m = sm.reg[LY::META_BASE / 4 + i];
-            sm.sz[i] = make_double2(f16_to_f64(m & 0xFFFFu), f16_to_f64(m >> 16));
-        }
+        if (tid < KHI) sm.kqh[tid] = kq[tid];
     }
     __syncthreads();
 
@@ -213,32 +223,24 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
 #pragma unroll 4
             for (int p = half * (KHI / 2); p < (half + 1) * (KHI / 2); ++p) {
                 const double x = f16_to_f64(f16rows[p * DV + j]);
-                const double2 c = sm.kq[p];
+                const double2 c = sm.kqh[p];
                 uP = fma(c.x, x, uP);
                 pP = fma(c.y, x, pP);
             }
         }
         const int g = j / BLOCK;
-        if constexpr (kRowBlocks) {
 #pragma unroll 4
-            for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
-                const double code = double(lb[LY::CODE_BASE + qr * DV + j]);
-                const double2 c = sm.kq[qr];             // (k a scale, q a scale)
-                uQ = fma(c.x, code, uQ);
-                pQ = fma(c.y, code, pQ);
-            }
-            if (half == 0) {
-                uQ += sm.zoff[0][0] + sm.zoff[1][0];
-                pQ += sm.zoff[0][1] + sm.zoff[1][1];
-            }
-        } else {
-#pragma unroll 4
-            for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
-                const double2 s = sm.sz[qr * LY::NB + g];
-                const double y = fma(double(lb[LY::CODE_BASE + qr * DV + j]), s.x, s.y);
-                const double2 c = sm.kq[qr + KHI];
-                uQ = fma(c.x, y, uQ);
-                pQ = fma(c.y, y, pQ);
+        for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
+            const double code = double(lb[LY::CODE_BASE + qr * DV + j]);
+            const double2 c = sm.kqs[qr * LY::NB + g];  // (k a step, q a step)
+            uQ = fma(c.x, code, uQ);
+            pQ = fma(c.y, code, pQ);
+        }
+        if (half == 0) {
+#pragma unroll
+            for (int wv = 0; wv < kZW; ++wv) {
+                uQ += sm.zsum[wv][g][0];
+                pQ += sm.zsum[wv][g][1];
             }
         }
         if (half == 1) {
@@ -320,9 +322,9 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             uint4* ptr = reinterpret_cast<uint4*>(lb + LY::CODE_BASE + qr * DV + 16 * cg);
             const uint4 raw = *ptr;
             const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-            const double2 s = sm.sz[qr * LY::NB + g];
+            const float2 s = sm.sz[qr * LY::NB + g];
             // a (zero + code * scale) + k (H w)_c = code * (a scale) + (a zero + k (H w)_c)
-            const double as = ak.x * s.x, az = ak.x * s.y;
+            const double as = ak.x * double(s.x), az = ak.x * double(s.y);
             double y[16];
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
