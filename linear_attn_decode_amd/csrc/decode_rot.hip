@@ -229,12 +229,23 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             }
         }
         const int g = j / BLOCK;
+        {
+            // two interleaved partial sums per quantity (shorter dependency chains)
+            double uQ1 = 0.0, pQ1 = 0.0;
+            static_assert(LY::NQ % 4 == 0, "rows are taken two at a time per half");
 #pragma unroll 4
-        for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); ++qr) {
-            const double code = double(lb[LY::CODE_BASE + qr * DV + j]);
-            const double2 c = sm.kqs[qr * LY::NB + g];  // (k a step, q a step)
-            uQ = fma(c.x, code, uQ);
-            pQ = fma(c.y, code, pQ);
+            for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); qr += 2) {
+                const double code0 = double(lb[LY::CODE_BASE + qr * DV + j]);
+                const double code1 = double(lb[LY::CODE_BASE + (qr + 1) * DV + j]);
+                const double2 c0 = sm.kqs[qr * LY::NB + g];         // (k a step, q a step)
+                const double2 c1 = sm.kqs[(qr + 1) * LY::NB + g];
+                uQ = fma(c0.x, code0, uQ);
+                pQ = fma(c0.y, code0, pQ);
+                uQ1 = fma(c1.x, code1, uQ1);
+                pQ1 = fma(c1.y, code1, pQ1);
+            }
+            uQ += uQ1;
+            pQ += pQ1;
         }
         if (half == 0) {
 #pragma unroll
