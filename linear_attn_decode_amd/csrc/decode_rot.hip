@@ -80,6 +80,39 @@ __device__ __forceinline__ double dpp_f64(double v) {
     return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
 }
 
+// v + (the value lanes 32 apart / 16 apart hold): the two halves of the wavefront (odd
+// and even DPP rows) exchanged by one lane swap per 32-bit half
+__device__ __forceinline__ double add_xor32_f64(double v) {
+    const uint64_t b = __double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+    return __longlong_as_double((long long)((uint64_t(hi[0]) << 32) | lo[0])) +
+           __longlong_as_double((long long)((uint64_t(hi[1]) << 32) | lo[1]));
+}
+__device__ __forceinline__ double add_xor16_f64(double v) {
+    const uint64_t b = __double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+    return __longlong_as_double((long long)((uint64_t(hi[0]) << 32) | lo[0])) +
+           __longlong_as_double((long long)((uint64_t(hi[1]) << 32) | lo[1]));
+}
+
+// Sum over the lanes of the wavefront that are equal modulo NB (1 or 4), returned in
+// every lane: DPP inside rows of 16 lanes (xor 1, xor 2; rotations by 8 and 4 combine
+// the four lanes of a residue class), then the rows by lane swaps.
+template <int NB>
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    static_assert(NB == 1 || NB == 4, "residue classes of 1 or 4 lanes");
+    if constexpr (NB == 1) {
+        v += dpp_f64<0xB1>(v);     // xor 1
+        v += dpp_f64<0x4E>(v);     // xor 2
+    }
+    v += dpp_f64<0x128>(v);        // row_ror:8
+    v += dpp_f64<0x124>(v);        // row_ror:4
+    v = add_xor16_f64(v);
+    return add_xor32_f64(v);
+}
+
 // min and max over the lanes of one block (BLOCK / 16 consecutive lanes of a DPP row)
 template <int BLOCK>
 __device__ __forceinline__ void block_minmax(double& mn, double& mx) {
@@ -94,8 +127,10 @@ __device__ __forceinline__ void block_minmax(double& mn, double& mx) {
 }
 
 // Butterfly partner at lane ^ D of a float64 value: DPP inside a row of 16 lanes for
-// D = 1, 2, 4, 8 (row_ror:n hands lane i the value of lane i - n mod 16), swizzle inside
-// 32 lanes for D = 16, permute for D = 32.
+// D = 1, 2, 4, 8 (row_ror:n hands lane i the value of lane i - n mod 16), lane swaps of
+// the odd and even rows (D = 16) or of the two halves (D = 32): swapping a register with
+// itself leaves the even rows' (low half's) values in the first result and the odd
+// rows' (high half's) in the second, everywhere.
 template <int D>
 __device__ __forceinline__ uint32_t xor_partner32(uint32_t b, int lane) {
     if constexpr (D == 1) return uint32_t(__builtin_amdgcn_mov_dpp(int(b), 0xB1, 0xF, 0xF, false));
@@ -106,8 +141,12 @@ __device__ __forceinline__ uint32_t xor_partner32(uint32_t b, int lane) {
         return uint32_t((lane & 4) ? dn : up);
     }
     if constexpr (D == 8) return uint32_t(__builtin_amdgcn_mov_dpp(int(b), 0x128, 0xF, 0xF, false));
-    if constexpr (D == 16) return uint32_t(__builtin_amdgcn_ds_swizzle(int(b), 0x401F));
-    return uint32_t(__shfl_xor(int(b), 32, 64));
+    if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    }
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return (lane & 32) ? r[0] : r[1];
 }
 
 template <int D>
@@ -177,8 +216,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         kq[p] = make_double2(kd * ad, qd * ad);
         sm.ak[p] = make_double2(ad, kd);
         double pq = qd * kd;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) pq += __shfl_xor(pq, d, 64);
+        pq = wave_sum_f64<1>(pq);
         if (lane == 0) sm.qk[wave] = pq;
     }
     __syncthreads();
@@ -200,11 +238,8 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         // sum over the lanes of one block column (lanes equal modulo NB), on the
         // wavefronts that hold blocks
         if (wave < kZW) {
-#pragma unroll
-            for (int d = LY::NB; d < 64; d <<= 1) {
-                zu += __shfl_xor(zu, d, 64);
-                zp += __shfl_xor(zp, d, 64);
-            }
+            zu = wave_sum_f64<LY::NB>(zu);
+            zp = wave_sum_f64<LY::NB>(zp);
             if (lane < LY::NB) {
                 sm.zsum[wave][lane][0] = zu;
                 sm.zsum[wave][lane][1] = zp;
