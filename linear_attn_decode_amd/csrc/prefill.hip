@@ -62,7 +62,9 @@ struct PfSmem {
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // Butterfly partner at lane ^ d for d = 1, 2, 4, 8 (DPP inside a row of 16 lanes),
-// 16 (swizzle inside 32 lanes) and 32 (permute).
+// 16 and 32 (lane swaps of the odd and even rows or of the two halves: swapping a
+// register with itself leaves the even rows' (low half's) values in the first result
+// and the odd rows' (high half's) in the second, everywhere).
 template <int D>
 __device__ __forceinline__ float xor_partner(float v, int lane) {
     const int b = __float_as_int(v);
@@ -75,8 +77,12 @@ __device__ __forceinline__ float xor_partner(float v, int lane) {
         return __int_as_float((lane & 4) ? dn : up);
     }
     if constexpr (D == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, false));   // row_ror:8
-    if constexpr (D == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x401F));   // xor 16 in 32 lanes
-    return __shfl_xor(v, 32, 64);
+    if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    }
+    const auto r = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
 }
 
 template <int D>
