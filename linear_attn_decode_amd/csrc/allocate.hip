@@ -223,8 +223,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             x[m][c] = float(kap) * dl;
             R = fmaxf(R, fabsf(x[m][c]));
         }
-#pragma unroll
-        for (int d = 1; d < NCG; d <<= 1) R = fmaxf(R, __shfl_xor(R, d, 64));
+        // maximum over the row's 16 lanes (a DPP row; non-negative values)
+        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0xB1, 0xF, 0xF, false)));
+        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x4E, 0xF, 0xF, false)));
+        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x141, 0xF, 0xF, false)));
+        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x140, 0xF, 0xF, false)));
         if (cg == 0) sm.R[row] = double(R);
     }
     __syncthreads();
@@ -233,16 +236,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     if (wave == 0) {
         const int r0 = 2 * lane, r1 = r0 + 1;
         const double R0 = sm.R[r0], R1 = sm.R[r1];
-        double sq = R0 * R0 + R1 * R1;
-        double anyR = fmax(R0, R1);
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            sq += __shfl_xor(sq, d, 64);
-            anyR = fmax(anyR, __shfl_xor(anyR, d, 64));
-        }
+        // (the squares of float32 maxima cannot underflow in float64: some R > 0 iff sq > 0)
+        const double sq = wave_sum_f64<1>(R0 * R0 + R1 * R1);
         int b0 = A.bbar, b1 = A.bbar;
         double c0 = 0.0, c1 = 0.0;
-        if (anyR > 0.0) {
+        if (sq > 0.0) {
             const double rms = sqrt(sq / double(DK));
             const size_t base = (size_t)head * DK;
             const double s0 = A.s[base + r0], s1 = A.s[base + r1];
@@ -253,18 +251,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             const double rt0 = R0 / rms, rt1 = R1 / rms;
             c0 = fmax(g0 * (rt0 * rt0), 1e-300);
             c1 = fmax(g1 * (rt1 * rt1), 1e-300);
-            double lsum = log(c0) + log(c1);
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) lsum += __shfl_xor(lsum, d, 64);
+            const double lsum = wave_sum_f64<1>(log(c0) + log(c1));
             const double gm = exp(lsum / double(DK));
             const double bs0 = double(A.bbar) + 0.5 * log2(c0 / gm);
             const double bs1 = double(A.bbar) + 0.5 * log2(c1 / gm);
             b0 = int(fmin(fmax(rint(bs0), double(A.bmin)), double(A.bmax)));
             b1 = int(fmin(fmax(rint(bs1), double(A.bmin)), double(A.bmax)));
             const int target = A.bbar * DK;
-            int tot = b0 + b1;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d, 64);
+            const int tot = int(wave_sum_f64<1>(double(b0 + b1)));      // exact: small integers
             // One bit at a time toward the budget, each time to the row of largest gain
             // (3/4) c 2^{-2b} (b < bmax) or, when over, from the row of smallest loss
             // 3 c 2^{-2b} (b > bmin), ties to the lower row. A row's successive gains

@@ -72,47 +72,6 @@ __device__ __forceinline__ uint16_t f64_to_f16_rto(double x) {
 
 __device__ __forceinline__ double f16_to_f64(uint32_t bits) { return double(f16_bits_to_f32(bits)); }
 
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-    const uint64_t b = __double_as_longlong(v);
-    const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xF, 0xF, false));
-    const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false));
-    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
-}
-
-// v + (the value lanes 32 apart / 16 apart hold): the two halves of the wavefront (odd
-// and even DPP rows) exchanged by one lane swap per 32-bit half
-__device__ __forceinline__ double add_xor32_f64(double v) {
-    const uint64_t b = __double_as_longlong(v);
-    const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
-    return __longlong_as_double((long long)((uint64_t(hi[0]) << 32) | lo[0])) +
-           __longlong_as_double((long long)((uint64_t(hi[1]) << 32) | lo[1]));
-}
-__device__ __forceinline__ double add_xor16_f64(double v) {
-    const uint64_t b = __double_as_longlong(v);
-    const auto lo = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
-    return __longlong_as_double((long long)((uint64_t(hi[0]) << 32) | lo[0])) +
-           __longlong_as_double((long long)((uint64_t(hi[1]) << 32) | lo[1]));
-}
-
-// Sum over the lanes of the wavefront that are equal modulo NB (1 or 4), returned in
-// every lane: DPP inside rows of 16 lanes (xor 1, xor 2; rotations by 8 and 4 combine
-// the four lanes of a residue class), then the rows by lane swaps.
-template <int NB>
-__device__ __forceinline__ double wave_sum_f64(double v) {
-    static_assert(NB == 1 || NB == 4, "residue classes of 1 or 4 lanes");
-    if constexpr (NB == 1) {
-        v += dpp_f64<0xB1>(v);     // xor 1
-        v += dpp_f64<0x4E>(v);     // xor 2
-    }
-    v += dpp_f64<0x128>(v);        // row_ror:8
-    v += dpp_f64<0x124>(v);        // row_ror:4
-    v = add_xor16_f64(v);
-    return add_xor32_f64(v);
-}
-
 // min and max over the lanes of one block (BLOCK / 16 consecutive lanes of a DPP row)
 template <int BLOCK>
 __device__ __forceinline__ void block_minmax(double& mn, double& mx) {
