@@ -464,15 +464,20 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 if (KIND == WB_UNIFORM) {
                     const float lo = -float(1 << (ub - 1)), hi = float((1 << (ub - 1)) - 1);
                     const float inv = float(1 << (ub - 1));
-                    uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // 32 fields of ub <= 8 bits
+                    float kv[32];
 #pragma unroll
                     for (int c = 0; c < 32; ++c) {
-                        const float k = fminf(fmaxf(rintf(x[c] * inv), lo), hi);
-                        x[c] = k * ustep;
-                        const int bit = c * ub;
-                        wd[bit >> 5] |= (uint32_t(int(k)) & ((1u << ub) - 1)) << (bit & 31);
+                        kv[c] = fminf(fmaxf(rintf(x[c] * inv), lo), hi);
+                        x[c] = kv[c] * ustep;
                     }
                     if (last) {
+                        // codes are packed only where they are stored
+                        uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // 32 fields of ub <= 8 bits
+#pragma unroll
+                        for (int c = 0; c < 32; ++c) {
+                            const int bit = c * ub;
+                            wd[bit >> 5] |= (uint32_t(int(kv[c])) & ((1u << ub) - 1)) << (bit & 31);
+                        }
                         // element (row, col) at bit ub (row DV + col): this block is 4 ub
                         // contiguous bytes, 4-byte aligned
                         uint32_t* dst = reinterpret_cast<uint32_t*>(region + ((row * DV + 32 * cb) * ub) / 8);
@@ -504,24 +509,32 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                     const uint16_t sb = f32_to_f16_bits(fmaxf(mx - mn, 0.f) * (1.f / 255.f));
                     const uint16_t zb = f32_to_f16_bits(mn);
                     const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
-                    uint32_t cw4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    // levels in magic-number form (1.5 * 2^23 + level); level 0 if the
+                    // block is constant
+                    constexpr float M = 12582912.0f;
+                    float yv[32];
                     if (sc > 0.f) {
                         // reciprocal refined by one Newton step; rounding by adding 1.5 * 2^23
                         // (ties to even), clamp by med3
                         float inv = __builtin_amdgcn_rcpf(sc);
                         inv = __builtin_fmaf(__builtin_fmaf(-sc, inv, 1.f), inv, inv);
-                        constexpr float M = 12582912.0f;
 #pragma unroll
                         for (int c = 0; c < 32; ++c) {
-                            const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c] - ze, inv, M), M, M + 255.f);
-                            cw4[c >> 2] |= (__float_as_uint(y) & 0xFFu) << (8 * (c & 3));
-                            x[c] = __builtin_fmaf(y - M, sc, ze);
+                            yv[c] = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c] - ze, inv, M), M, M + 255.f);
+                            x[c] = __builtin_fmaf(yv[c] - M, sc, ze);
                         }
                     } else {
 #pragma unroll
-                        for (int c = 0; c < 32; ++c) x[c] = ze;
+                        for (int c = 0; c < 32; ++c) {
+                            yv[c] = M;
+                            x[c] = ze;
+                        }
                     }
                     if (last) {
+                        // codes are packed only where they are stored
+                        uint32_t cw4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                        for (int c = 0; c < 32; ++c) cw4[c >> 2] |= (__float_as_uint(yv[c]) & 0xFFu) << (8 * (c & 3));
                         const int qrow = row - k_hi;
                         uint4* dst = reinterpret_cast<uint4*>(region + code_base + (size_t)qrow * DV + 32 * cb);
                         dst[0] = make_uint4(cw4[0], cw4[1], cw4[2], cw4[3]);
