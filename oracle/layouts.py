@@ -55,6 +55,7 @@ class Layout:
     bmax: int = 8
     mode: str = "rtn"
     seed: int = 0
+    mem_bits: int = 0      # k of the temporal-memory rules (direction / residual memory)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -80,8 +81,10 @@ class Layout:
         return (self.region_size() + 255) // 256 * 256
 
     def side_elems(self) -> int:
-        """Error-feedback residuals per head (0 unless EF on a rounding layout)."""
-        if self.mode != "ef" or self.kind == FP32:
+        """Auxiliary write-back values per head: the error-feedback residual (EF on a
+        rounding layout), the k-bit residual (residual memory) or the direction counter
+        (direction memory), one per element; 0 otherwise."""
+        if self.mode not in ("ef", "dir", "resq") or self.kind == FP32:
             return 0
         return self.dk * self.dv
 

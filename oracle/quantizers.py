@@ -15,6 +15,23 @@ write-back interventions and diagnostics"; [WB-zh] "Core method" 核心方法 an
   * error feedback: q_t = Q_B(h_t + e_{t-1}) with the residual e_t clipped to
     +-Delta_B (same section of [WB-zh]); e is an auxiliary write-back state.
 
+Temporal-memory rules on the fixed uniform grid ([WB] "Interventions", "Post-training
+write-back interventions and diagnostics", "Trajectory analysis"; [WB-zh] "Core
+method"), the readings of this module:
+  * quantized residual memory (k bits): error feedback whose carried residual is itself
+    stored on a k-bit grid -- the clipped residual r in [-Delta_B, Delta_B] rounds to
+    the nearest of j * Delta_B / 2^(k-1), j in [-2^(k-1), 2^(k-1) - 1] (ties to even j);
+  * direction memory (k bits): a signed counter c per element. With q_{t-1} on level
+    kappa_{t-1} and delta = h_t - q_{t-1}: if the nearest level of h_t differs from
+    kappa_{t-1} the write is ordinary (stored, counter reset); otherwise a proposal with
+    Delta_B/8 < |delta| < Delta_B/2 votes c += sign(delta) and, when |c| reaches
+    T = 2^(k-1), the stored level moves one step in that direction (clipped at the grid
+    rails) and the counter resets; smaller proposals leave level and counter unchanged.
+    The counter therefore takes the 2^k - 1 values -(T-1) .. T-1.
+Write activity of one step (per head): dead-zone elements (write margin M < 1),
+elements whose stored level changed, eligible sub-threshold proposals (Delta_B/8 <
+|delta| < Delta_B/2) and direction-memory triggers (a trigger at a rail moves nothing).
+
 Every grid here is "offset + kappa * step" with integer kappa in [lo, hi]; a rule
 works on the grid coordinate tau = (x - offset) / step.
   * uniform B-bit grid: offset 0, step Delta_B = 2^(1-B), kappa in
@@ -36,7 +53,7 @@ import numpy as np
 
 from .numerics import f16, rne
 
-RTN, SR, EF = "rtn", "sr", "ef"
+RTN, SR, EF, DIR, RESQ = "rtn", "sr", "ef", "dir", "resq"
 
 
 @dataclass
@@ -90,6 +107,82 @@ def uniform_step(B: int) -> float:
 def uniform_round(x, B: int, mode: str, e=None, r16=None) -> Rounded:
     lo, hi = -(2 ** (B - 1)), 2 ** (B - 1) - 1
     return round_on_grid(x, uniform_step(B), 0.0, lo, hi, mode, e, r16)
+
+
+def residual_quantize(r, step, kbits: int):
+    """Nearest point of the k-bit residual grid j * step / 2^(k-1), j in
+    [-2^(k-1), 2^(k-1) - 1], ties to even j. Returns (value, j, distance of r /
+    (step / 2^(k-1)) to the rounding boundary)."""
+    r = np.asarray(r, dtype=np.float64)
+    step = np.broadcast_to(np.asarray(step, dtype=np.float64), r.shape)
+    h = 2 ** (kbits - 1)
+    sub = np.where(step == 0.0, 1.0, step / h)
+    u = r / sub
+    j = np.clip(rne(u), -h, h - 1)
+    j = np.where(step == 0.0, 0.0, j)
+    bnd = np.where(step == 0.0, np.inf, np.abs(np.abs(u - np.floor(u)) - 0.5))
+    return j * np.where(step == 0.0, 0.0, sub), j.astype(np.int64), bnd
+
+
+@dataclass
+class MemoryRounded:
+    kappa: np.ndarray       # stored level index (int64)
+    side_new: np.ndarray    # new residual value (residual memory) or counter (direction memory)
+    tau: np.ndarray         # grid coordinate of the value rounded (h or h + e)
+    boundary: np.ndarray    # distance (grid units) to the nearest decision boundary
+    activity: np.ndarray    # [dead-zone, level changes, votes, direction-memory triggers]
+
+
+def uniform_memory_round(x, B: int, mode: str, kappa_prev, side, kbits: int) -> MemoryRounded:
+    """Residual memory (mode RESQ, ``side`` = carried k-bit residual value) or direction
+    memory (mode DIR, ``side`` = counter) on the uniform B-bit grid; ``kappa_prev`` are
+    the stored levels entering the step."""
+    x = np.asarray(x, dtype=np.float64)
+    step = uniform_step(B)
+    lo, hi = -(2 ** (B - 1)), 2 ** (B - 1) - 1
+    kp = np.asarray(kappa_prev, dtype=np.int64)
+    side = np.asarray(side, dtype=np.float64)
+    q_prev = kp * step
+    delta = x - q_prev
+    ad = np.abs(delta) / step                              # |delta| in grid units
+    tau_h = x / step
+    near = np.clip(rne(tau_h), lo, hi)
+    dead = 2.0 * ad < 1.0
+    vote = (ad > 0.125) & (ad < 0.5)
+    bnd_h = np.abs(np.abs(tau_h - np.floor(tau_h)) - 0.5)
+    if mode == RESQ:
+        target = x + side
+        tau = target / step
+        kappa = np.clip(rne(tau), lo, hi)
+        r = np.clip(target - kappa * step, -step, step)
+        e_val, _, bnd_e = residual_quantize(r, step, kbits)
+        side_new = e_val
+        boundary = np.minimum(np.abs(np.abs(tau - np.floor(tau)) - 0.5), bnd_e)
+        moves = np.zeros_like(x, dtype=bool)
+    elif mode == DIR:
+        T = 2 ** (kbits - 1)
+        ordinary = near != kp
+        sgn = np.sign(delta)
+        c = side + np.where(~ordinary & vote, sgn, 0.0)
+        moves = ~ordinary & vote & (np.abs(c) >= T)
+        kappa = np.where(ordinary, near, np.where(moves, np.clip(kp + sgn, lo, hi), kp))
+        side_new = np.where(ordinary | moves, 0.0, c)
+        tau = tau_h
+        # decisions: the nearest level (half-integers of tau) and the vote band edges
+        boundary = np.minimum(bnd_h, np.minimum(np.abs(ad - 0.125), np.abs(ad - 0.5)))
+    else:
+        raise ValueError(mode)
+    activity = np.array([int(dead.sum()), int((kappa != kp).sum()), int(vote.sum()), int(moves.sum())],
+                        dtype=np.int64)
+    return MemoryRounded(kappa.astype(np.int64), side_new, tau, boundary, activity)
+
+
+def uniform_activity(x, kappa_prev, kappa_new, B: int) -> np.ndarray:
+    """[dead-zone, level changes, votes, 0] of one step under a rule without direction
+    memory (h_t = x; levels entering and leaving the step)."""
+    ad = np.abs(np.asarray(x, np.float64) - np.asarray(kappa_prev, np.float64) * uniform_step(B)) / uniform_step(B)
+    return np.array([int((2.0 * ad < 1.0).sum()), int((np.asarray(kappa_new) != np.asarray(kappa_prev)).sum()),
+                     int(((ad > 0.125) & (ad < 0.5)).sum()), 0], dtype=np.int64)
 
 
 def write_margin(h, q_prev, B: int):

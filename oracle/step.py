@@ -33,8 +33,8 @@ from . import layouts as L
 from .allocation import allocate_head
 from .numerics import f16, f16_bits
 from .philox import sr_draws
-from .quantizers import (EF, SR, affine_metadata, affine_round, levels_n, row_step,
-                         sym_round, uniform_round)
+from .quantizers import (DIR, EF, RESQ, SR, affine_metadata, affine_round, levels_n, row_step,
+                         sym_round, uniform_activity, uniform_memory_round, uniform_round)
 from .recurrence import delta_step
 
 
@@ -47,6 +47,7 @@ class WriteBack:
     meta: dict = field(default_factory=dict)       # metadata as stored
     tau: np.ndarray | None = None  # grid coordinate per element (rounding rows)
     boundary: np.ndarray | None = None
+    activity: np.ndarray | None = None   # UNIFORM: [dead-zone, changes, votes, triggers]
 
 
 def _draws(lay, b, h, t, rows):
@@ -76,11 +77,19 @@ def write_back(lay: L.Layout, X: np.ndarray, e_in, t: int, b: int, h: int,
         c = L.Content(S32=X.astype(np.float32).astype(np.float64))
         wb.region = L.encode_region(lay, c)
         return wb
-    if lay.kind == L.UNIFORM:
+    if lay.kind == L.UNIFORM and mode in (DIR, RESQ):
+        kp = prev.kappa if prev is not None else np.zeros((dk, dv), np.int64)
+        mr = uniform_memory_round(X, lay.bits, mode, kp, e, lay.mem_bits)
+        wb.region = L.encode_region(lay, L.Content(kappa=mr.kappa))
+        tau, bnd, e_new = mr.tau, mr.boundary, mr.side_new
+        wb.activity = mr.activity
+    elif lay.kind == L.UNIFORM:
         r16 = _draws(lay, b, h, t, range(dk)) if mode == SR else None
         rr = uniform_round(X, lay.bits, mode, e, r16)
         wb.region = L.encode_region(lay, L.Content(kappa=rr.kappa))
         tau, bnd, e_new = rr.tau, rr.boundary, rr.e_new
+        if prev is not None:
+            wb.activity = uniform_activity(X, prev.kappa, rr.kappa, lay.bits)
     elif lay.kind in (L.HAD_INT8, L.MIXED):
         G = lay.block
         nb = dv // G
@@ -144,7 +153,7 @@ def write_back(lay: L.Layout, X: np.ndarray, e_in, t: int, b: int, h: int,
     else:
         raise ValueError(lay.kind)
     wb.tau, wb.boundary = tau, bnd
-    if mode == EF:
+    if mode in (EF, DIR, RESQ):
         if lay.kind == L.MIXED:
             e_new[: lay.k_hi] = e[: lay.k_hi]          # float16 rows carry no residual
         wb.e_new = e_new

@@ -124,3 +124,88 @@ def test_symmetric_row_levels():
         assert np.array_equal(sym_round(r.xhat, d2, levels_n(b), "rtn").kappa, r.kappa)
     z = sym_round(np.zeros(8), 0.0, 7, "rtn")
     assert np.all(z.kappa == 0)
+
+
+# ---- temporal-memory rules on the uniform grid (direction / residual memory) ----------
+# The expected values follow the rule text directly: the vote band Delta/8 < |delta| <
+# Delta/2 with strict edges, a one-level move when the counter reaches 2^(k-1), the
+# counter reset at every stored-level change, moves clipped at the rails; the residual
+# of error feedback kept on the k-bit grid j Delta / 2^(k-1), j in [-2^(k-1), 2^(k-1)).
+
+from oracle.quantizers import residual_quantize, uniform_memory_round  # noqa: E402
+
+
+def _dir(x, kp, c, k=2, B=4):
+    return uniform_memory_round(np.array(x, float), B, "dir", np.array(kp), np.array(c, float), k)
+
+
+def test_direction_memory_votes_trigger_and_reset():
+    d = uniform_step(4)                       # 0.125: vote band (0.015625, 0.0625)
+    # one vote up, counter 0 -> 1, no move (T = 2 for k = 2)
+    r = _dir([0.03], [0], [0])
+    assert r.kappa.tolist() == [0] and r.side_new.tolist() == [1.0]
+    # the second same-sign vote reaches T: one level up, counter reset
+    r = _dir([0.03], [0], [1])
+    assert r.kappa.tolist() == [1] and r.side_new.tolist() == [0.0]
+    assert r.activity.tolist() == [1, 1, 1, 1]
+    # an opposite vote takes the counter back, no move
+    r = _dir([-0.03], [0], [1])
+    assert r.kappa.tolist() == [0] and r.side_new.tolist() == [0.0]
+    # below the band: neither vote nor reset
+    r = _dir([0.01], [0], [1])
+    assert r.kappa.tolist() == [0] and r.side_new.tolist() == [1.0]
+    assert r.activity.tolist() == [1, 0, 0, 0]
+    # an ordinary write (nearest level changes) stores it and resets the counter
+    r = _dir([0.07], [0], [-1])
+    assert r.kappa.tolist() == [1] and r.side_new.tolist() == [0.0]
+    assert r.activity.tolist() == [0, 1, 0, 0]
+    # the band edges are excluded: |delta| = Delta/8 and |delta| = Delta/2 (a tie that
+    # rounds back to the even level 0) do not vote
+    r = _dir([d / 8, d / 2, -d / 8], [0, 0, 0], [1, 1, 1])
+    assert r.kappa.tolist() == [0, 0, 0] and r.side_new.tolist() == [1.0, 1.0, 1.0]
+    # proposals relative to a nonzero stored level
+    r = _dir([3 * d + 0.03, -5 * d - 0.03], [3, -5], [1, -1])
+    assert r.kappa.tolist() == [4, -6] and r.side_new.tolist() == [0.0, 0.0]
+
+
+def test_direction_memory_rails_and_counter_range():
+    d = uniform_step(4)
+    # at the upper rail a trigger cannot move the level; the counter still resets
+    r = _dir([7 * d + 0.03, -8 * d - 0.03], [7, -8], [1, -1])
+    assert r.kappa.tolist() == [7, -8] and r.side_new.tolist() == [0.0, 0.0]
+    assert r.activity.tolist() == [2, 0, 2, 2]
+    # k = 3: T = 4, the counter runs through -3 .. 3 before a move
+    c, kp = 0.0, 0
+    seen = []
+    for _ in range(4):
+        r = _dir([kp * d + 0.03], [kp], [c], k=3)
+        kp, c = int(r.kappa[0]), float(r.side_new[0])
+        seen.append((kp, c))
+    assert seen == [(0, 1.0), (0, 2.0), (0, 3.0), (1, 0.0)]
+    for _ in range(3):
+        r = _dir([kp * d - 0.03], [kp], [c], k=3)
+        kp, c = int(r.kappa[0]), float(r.side_new[0])
+    assert (kp, c) == (1, -3.0)
+
+
+def test_residual_memory_grid_and_carry():
+    d = uniform_step(4)
+    # k = 2: residual points {-d, -d/2, 0, d/2}; ties to the even index
+    v, j, _ = residual_quantize(np.array([0.03, 0.04, -d, d, d / 4, 3 * d / 4]), d, 2)
+    assert j.tolist() == [0, 1, -2, 1, 0, 1]
+    assert v.tolist() == [0.0, d / 2, -d, d / 2, 0.0, d / 2]
+    # a sub-threshold proposal is remembered on the k-bit grid and later written
+    x = np.array([0.04])
+    r1 = uniform_memory_round(x, 4, "resq", np.array([0]), np.array([0.0]), 2)
+    assert r1.kappa.tolist() == [0] and r1.side_new.tolist() == [d / 2]
+    r2 = uniform_memory_round(x, 4, "resq", r1.kappa, r1.side_new, 2)
+    assert r2.kappa.tolist() == [1]
+    assert np.isclose(r2.side_new[0], 0.0)           # residual 0.04 + d/2 - d = -0.0225
+    # with many residual bits the rule is error feedback (residual clipped to +-d)
+    rng = np.random.default_rng(3)
+    xs = rng.uniform(-1.2, 1.2, 200)
+    es = rng.uniform(-d, d, 200)
+    r = uniform_memory_round(xs, 4, "resq", np.zeros(200, np.int64), es, 30)
+    ef = uniform_round(xs, 4, "ef", es)
+    assert np.array_equal(r.kappa, ef.kappa)
+    assert np.allclose(r.side_new, ef.e_new, atol=d * 2.0 ** -28)
