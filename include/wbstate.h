@@ -92,27 +92,41 @@ extern "C" {
                           (16*row + col/8, b*H + h, t lo, t hi), column col using word
                           (col%8)/2, low half for even col */
 #define WB_EF 2        /* error feedback: round (h + e), then e = clip(h + e - q, -step, step) */
+#define WB_DIR 3       /* direction memory (UNIFORM only), k = mem_bits: a signed counter c per
+                          element; with q the level entering the step and d = h - q: a change of
+                          the nearest level is written as usual and resets c; otherwise
+                          step/8 < |d| < step/2 adds sign(d) to c and, when |c| reaches 2^(k-1),
+                          the level moves one step that way (clipped at the rails) and c resets
+                          ([WB] "Interventions", "Post-training write-back interventions and
+                          diagnostics", "Trajectory analysis") */
+#define WB_RESQ 4      /* quantized residual memory (UNIFORM only), k = mem_bits: error feedback
+                          whose carried residual clip(h + e - q, -step, step) is itself rounded
+                          to the nearest j * step / 2^(k-1), j in [-2^(k-1), 2^(k-1) - 1], ties
+                          to even j ([WB] "Post-training write-back interventions and
+                          diagnostics": residual widths k = 2, 3, 4) */
 
 #define WB_DECAY_PER_HEAD 0
 #define WB_DECAY_PER_ROW 1
 
 typedef struct wb_layout_desc {
     int32_t kind;    /* WB_FP32 .. WB_BITALLOC */
-    int32_t mode;    /* WB_RTN, WB_SR, WB_EF */
+    int32_t mode;    /* WB_RTN, WB_SR, WB_EF, WB_DIR, WB_RESQ */
     int32_t decay;   /* WB_DECAY_PER_HEAD or WB_DECAY_PER_ROW */
     int32_t B, H, dk, dv;
     int32_t bits;    /* UNIFORM level width: 2, 4 or 8 */
     int32_t block;   /* HAD_INT8 / MIXED affine block length along dv: 32, 64 or 128 */
     int32_t k_hi;    /* MIXED float16 rows: a positive multiple of dk/8 below dk */
     int32_t bbar, bmin, bmax;  /* BITALLOC mean width and clip range, 2 <= bmin <= bbar <= bmax <= 8 */
-    int32_t reserved;          /* must be 0 */
+    int32_t mem_bits;          /* k of WB_DIR / WB_RESQ, 1..8 (the pages evaluate 2, 3, 4); 0 otherwise */
     uint64_t seed;             /* Philox key for WB_SR */
 } wb_layout_desc;
 
 typedef struct wb_state wb_state;   /* opaque host-side handle */
 
-/* Device bytes needed for the state buffer and for the error-feedback side buffer
- * (0 unless mode is WB_EF on a rounding layout). Host only. */
+/* Device bytes needed for the state buffer and for the side buffer of the auxiliary
+ * write-back state -- float32 per element: the error-feedback residual (WB_EF), the
+ * k-bit residual's value (WB_RESQ) or the direction counter (WB_DIR); 0 for the other
+ * rules and for FP32. Host only. */
 int state_bytes(const wb_layout_desc* d, size_t* state_bytes_out, size_t* side_bytes_out);
 
 /* Bind a handle to caller-owned device memory and write the zero state S_0 = 0 with
@@ -148,6 +162,16 @@ int state_step_decode(wb_state* st, const float* q, const float* k, const float*
 int state_prefill_chunk(wb_state* st, const uint16_t* q_bf16, const uint16_t* k_bf16,
                         const uint16_t* v_bf16, const float* beta, const float* s, float* o,
                         int T, int chunk, int C, uint64_t t0, void* stream);
+
+/* UNIFORM only: write-activity counters. With a non-NULL `dev_counters` (uint32
+ * [B*H][4], 16-byte aligned, caller-owned and zeroed by the caller), every following
+ * decode step adds, per head, the number of elements whose write margin
+ * M = 2 |h - q| / step is below 1 (the dead zone), whose stored level changed, whose
+ * proposal lies in the vote band step/8 < |h - q| < step/2, and (WB_DIR) whose counter
+ * triggered a one-level move ([WB] "Methods" diagnostics, "Direction-memory events",
+ * "State diagnostics"; q is the level entering the step, h the updated value). NULL
+ * stops counting. */
+int state_set_activity(wb_state* st, uint32_t* dev_counters);
 
 /* BITALLOC only: recompute per-row widths and clipping-fit indices from the stored
  * state and repack it in place ([LBRS] "Approximate erasure rate", "Range

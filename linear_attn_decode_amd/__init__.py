@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libwbstate.so")
 # layout kinds, write-back rules and decay kinds (values of include/wbstate.h)
 FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC = 0, 1, 2, 3, 4
 KIND_NAMES = {"fp32": FP32, "uniform": UNIFORM, "had_int8": HAD_INT8, "mixed": MIXED, "bitalloc": BITALLOC}
-RTN, SR, EF = 0, 1, 2
-MODE_NAMES = {"rtn": RTN, "sr": SR, "ef": EF}
+RTN, SR, EF, DIR, RESQ = 0, 1, 2, 3, 4
+MODE_NAMES = {"rtn": RTN, "sr": SR, "ef": EF, "dir": DIR, "resq": RESQ}
 DECAY_PER_HEAD, DECAY_PER_ROW = 0, 1
 
 STATUS = {0: "ok", -1: "EINVAL", -2: "ESIZE", -3: "EUNSUPPORTED", -4: "ELAUNCH", -5: "EALIGN"}
@@ -30,7 +30,7 @@ class LayoutDesc(ctypes.Structure):
                 ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("k_hi", ctypes.c_int32),
                 ("bbar", ctypes.c_int32), ("bmin", ctypes.c_int32), ("bmax", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("mem_bits", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 _P = ctypes.c_void_p
@@ -50,6 +50,7 @@ SIGNATURES = {
     "state_quantize": (_I, [_P, _P, _P]),
     "state_export": (_I, [_P, ctypes.POINTER(_P), ctypes.POINTER(_SZ), ctypes.POINTER(_P)]),
     "state_damp_select": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _F, _P, _P, _P]),
+    "state_set_activity": (_I, [_P, _P]),
     "state_status_str": (ctypes.c_char_p, [_I]),
 }
 
@@ -78,12 +79,12 @@ def check(status: int, what: str = "") -> None:
 
 
 def make_desc(kind, mode, B, H, dk=128, dv=128, per_row_decay=True, bits=4, block=32, k_hi=16,
-              bbar=4, bmin=2, bmax=8, seed=0) -> LayoutDesc:
+              bbar=4, bmin=2, bmax=8, seed=0, mem_bits=0) -> LayoutDesc:
     kind = KIND_NAMES.get(kind, kind)
     mode = MODE_NAMES.get(mode, mode)
     return LayoutDesc(kind=kind, mode=mode, decay=DECAY_PER_ROW if per_row_decay else DECAY_PER_HEAD,
                       B=B, H=H, dk=dk, dv=dv, bits=bits, block=block, k_hi=k_hi, bbar=bbar,
-                      bmin=bmin, bmax=bmax, reserved=0, seed=seed)
+                      bmin=bmin, bmax=bmax, mem_bits=mem_bits, seed=seed)
 
 
 def buffer_sizes(desc: LayoutDesc):
@@ -115,11 +116,11 @@ class WriteBackState:
 
     def __init__(self, kind, mode="rtn", B=1, H=1, dk=128, dv=128, per_row_decay=True, bits=4,
                  block=32, k_hi=16, bbar=4, bmin=2, bmax=8, seed=0, perm=None, device="cuda",
-                 stream=None):
+                 stream=None, mem_bits=0):
         import numpy as np
         import torch
         self.desc = make_desc(kind, mode, B, H, dk, dv, per_row_decay, bits, block, k_hi, bbar, bmin,
-                              bmax, seed)
+                              bmax, seed, mem_bits)
         nbytes, side = buffer_sizes(self.desc)
         self.state = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.side = torch.empty(max(side // 4, 4), dtype=torch.float32, device=device)
@@ -194,10 +195,22 @@ class WriteBackState:
         return self.state[: st * self.B * self.H].view(self.B * self.H, st)
 
     def residuals(self):
-        """Error-feedback residuals [B, H, dk, dv] (EF mode) or None."""
+        """The auxiliary write-back state [B, H, dk, dv] -- error-feedback residuals (EF),
+        k-bit residual values (RESQ) or direction counters (DIR) -- or None."""
         if not self.side_bytes:
             return None
         return self.side[: self.side_bytes // 4].view(self.B, self.H, self.dk, self.dv)
+
+    def set_activity(self, counters=None):
+        """Count write activity (UNIFORM): later decode steps add, per head, [dead-zone
+        elements, level changes, vote-band proposals, direction triggers] into
+        ``counters`` (int32 tensor [B, H, 4], zeroed by the caller); None stops."""
+        import torch
+        p = None
+        if counters is not None:
+            p = _ptr(counters, torch.int32, (self.B, self.H, 4), "counters")
+        self._activity = counters
+        check(lib().state_set_activity(self.handle, p), "state_set_activity")
 
 
 def damp_select(samples, s, k_hi=16, block=32, tau=0.01, stream=None):

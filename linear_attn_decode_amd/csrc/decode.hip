@@ -121,7 +121,9 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
     constexpr bool ROT = SM::ROT;
     constexpr int NCG = Sh::NCG, RS = Sh::RS, NT = Sh::NT;
     constexpr int EMODE = (OP == OP_IMPORT) ? WB_RTN : MODE;    // import rounds to nearest
-    constexpr bool USE_SIDE = (MODE == WB_EF) && (KIND != WB_FP32);
+    constexpr bool MEM = MODE == WB_DIR || MODE == WB_RESQ;        // temporal memory (UNIFORM)
+    constexpr bool USE_SIDE = (MODE == WB_EF || MEM) && (KIND != WB_FP32);
+    static_assert(!MEM || KIND == WB_UNIFORM, "temporal-memory rules are defined on the uniform grid");
 
     __shared__ SM sm;
 
@@ -409,6 +411,8 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
         for (int i = tid; i < code_words; i += NT) sm.reg[i] = 0u;
         __syncthreads();
     }
+    // write activity of this lane (UNIFORM decode steps with counters attached)
+    uint32_t n_dead = 0, n_change = 0, n_vote = 0, n_trig = 0;
     if (act) {
         const uint32_t bh = uint32_t(head);
 #pragma unroll
@@ -426,14 +430,68 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             } else if (KIND == WB_UNIFORM) {
                 const int B = A.bits;
                 const Real step = Real(1) / Real(1 << (B - 1));
+                const Real inv_step = Real(1 << (B - 1));
                 const int lo = -(1 << (B - 1)), hi = (1 << (B - 1)) - 1;
+                const size_t boff = ((size_t)row * DV / 8 + cg) * B;
+                // levels entering the step (still stored: this lane writes its fields below)
+                const bool track = OP == OP_STEP && (MEM || A.activity != nullptr);
+                uint64_t prev = 0;
+                if (track) {
+                    if (B == 2) prev = *reinterpret_cast<const uint16_t*>(region + boff);
+                    else if (B == 4) prev = *reinterpret_cast<const uint32_t*>(region + boff);
+                    else prev = *reinterpret_cast<const uint64_t*>(region + boff);
+                }
                 uint64_t fld = 0;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const int kap = round_rule<EMODE, Real>(x[m][c], Real(e[m][c]), step, Real(0), lo, hi, r16[c], &en[c]);
+                    int kp = 0;
+                    if (track) {
+                        kp = int((prev >> (c * B)) & ((1u << B) - 1));
+                        if (kp >= (1 << (B - 1))) kp -= (1 << B);
+                    }
+                    const Real h = x[m][c];
+                    const Real dlt = h - Real(kp) * step;
+                    const Real ad = fabs(dlt);
+                    const bool vote = ad > Real(0.125) * step && ad < Real(0.5) * step;
+                    int kap;
+                    bool trig = false;
+                    if constexpr (EMODE == WB_RESQ) {
+                        // error feedback with the residual kept on the k-bit grid
+                        const Real target = h + Real(e[m][c]);
+                        kap = int(fmin(fmax(rint(target * inv_step), Real(lo)), Real(hi)));
+                        const Real r = fmin(fmax(target - Real(kap) * step, -step), step);
+                        const int hk = 1 << (A.mem_bits - 1);
+                        const Real sub = step / Real(hk);
+                        const Real j = fmin(fmax(rint(r / sub), Real(-hk)), Real(hk - 1));
+                        en[c] = float(j * sub);
+                    } else if constexpr (EMODE == WB_DIR) {
+                        // direction memory: counter in the side buffer
+                        const int near = int(fmin(fmax(rint(h * inv_step), Real(lo)), Real(hi)));
+                        const float cnt = e[m][c];
+                        if (near != kp) {
+                            kap = near;
+                            en[c] = 0.f;
+                        } else if (vote) {
+                            const int sg = dlt > Real(0) ? 1 : -1;
+                            const float c2 = cnt + float(sg);
+                            trig = fabsf(c2) >= float(1 << (A.mem_bits - 1));
+                            kap = trig ? min(max(kp + sg, lo), hi) : kp;
+                            en[c] = trig ? 0.f : c2;
+                        } else {
+                            kap = kp;
+                            en[c] = cnt;
+                        }
+                    } else {
+                        kap = round_rule<EMODE, Real>(h, Real(e[m][c]), step, Real(0), lo, hi, r16[c], &en[c]);
+                    }
+                    if (track) {
+                        n_dead += Real(2) * ad < step;
+                        n_change += kap != kp;
+                        n_vote += vote;
+                        n_trig += trig;
+                    }
                     fld |= uint64_t(uint32_t(kap) & ((1u << B) - 1)) << (c * B);
                 }
-                const size_t boff = ((size_t)row * DV / 8 + cg) * B;
                 if (B == 2) *reinterpret_cast<uint16_t*>(region + boff) = uint16_t(fld);
                 else if (B == 4) *reinterpret_cast<uint32_t*>(region + boff) = uint32_t(fld);
                 else *reinterpret_cast<uint64_t*>(region + boff) = fld;
@@ -516,6 +574,23 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             }
         }
     }
+    if (KIND == WB_UNIFORM && OP == OP_STEP && A.activity != nullptr) {
+        // sum over the wavefront, one atomic add per counter and wavefront
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            n_dead += __shfl_xor(n_dead, d, 64);
+            n_change += __shfl_xor(n_change, d, 64);
+            n_vote += __shfl_xor(n_vote, d, 64);
+            n_trig += __shfl_xor(n_trig, d, 64);
+        }
+        if (lane == 0) {
+            uint32_t* ctr = A.activity + (size_t)head * 4;
+            atomicAdd(ctr + 0, n_dead);
+            atomicAdd(ctr + 1, n_change);
+            atomicAdd(ctr + 2, n_vote);
+            atomicAdd(ctr + 3, n_trig);
+        }
+    }
     if (KIND == WB_BITALLOC) {
         __syncthreads();
         const int total = DK * DV * A.bbar / 8 + 2 * DK;     // codes + Delta (meta unchanged)
@@ -534,6 +609,10 @@ hipError_t launch_one(const KArgs& a, int heads, hipStream_t stream) {
 template <int KIND, int OP, int DK, int DV>
 hipError_t launch_mode(int mode, const KArgs& a, int heads, hipStream_t stream) {
     if (KIND == WB_FP32 || OP == OP_EXPORT) return launch_one<KIND, WB_RTN, OP, DK, DV>(a, heads, stream);
+    if constexpr (KIND == WB_UNIFORM) {
+        if (mode == WB_DIR) return launch_one<KIND, WB_DIR, OP, DK, DV>(a, heads, stream);
+        if (mode == WB_RESQ) return launch_one<KIND, WB_RESQ, OP, DK, DV>(a, heads, stream);
+    }
     switch (mode) {
         case WB_RTN: return launch_one<KIND, WB_RTN, OP, DK, DV>(a, heads, stream);
         case WB_SR: return launch_one<KIND, WB_SR, OP, DK, DV>(a, heads, stream);

@@ -31,6 +31,8 @@ struct KArgs {
     int block = 32;
     int k_hi = 0;
     int bbar = 4;
+    int mem_bits = 0;                 // k of direction / residual memory
+    uint32_t* activity = nullptr;     // [B*H][4] write-activity counters (UNIFORM) or null
 };
 
 // One launch of the decode / import / export kernel for every head of the layout.

@@ -19,6 +19,7 @@ struct wb_state {
     size_t region_stride;
     size_t regions_bytes;
     uint8_t* perm_dev;     // inside the state buffer (MIXED), else null
+    uint32_t* activity;    // caller's write-activity counters (UNIFORM), or null
 };
 
 namespace {
@@ -45,9 +46,11 @@ size_t region_size(const wb_layout_desc& d) {
 int validate(const wb_layout_desc* d) {
     if (!d) return WB_EINVAL;
     if (d->kind < WB_FP32 || d->kind > WB_BITALLOC) return WB_EINVAL;
-    if (d->mode < WB_RTN || d->mode > WB_EF) return WB_EINVAL;
+    if (d->mode < WB_RTN || d->mode > WB_RESQ) return WB_EINVAL;
     if (d->decay != WB_DECAY_PER_HEAD && d->decay != WB_DECAY_PER_ROW) return WB_EINVAL;
-    if (d->reserved != 0) return WB_EINVAL;
+    const bool memory_rule = d->mode == WB_DIR || d->mode == WB_RESQ;
+    if (memory_rule ? (d->mem_bits < 1 || d->mem_bits > 8) : d->mem_bits != 0) return WB_EINVAL;
+    if (memory_rule && d->kind != WB_UNIFORM) return WB_EUNSUPPORTED;
     if (d->B < 1 || d->H < 1) return WB_EINVAL;
     if ((int64_t)d->B * d->H > 0x7FFFFFFF) return WB_EUNSUPPORTED;
     const bool small = d->dk == 16 && d->dv == 16;
@@ -73,7 +76,7 @@ int validate(const wb_layout_desc* d) {
 }
 
 size_t side_size(const wb_layout_desc& d) {
-    if (d.mode != WB_EF || d.kind == WB_FP32) return 0;
+    if ((d.mode != WB_EF && d.mode != WB_DIR && d.mode != WB_RESQ) || d.kind == WB_FP32) return 0;
     return size_t(d.B) * d.H * d.dk * d.dv * 4;
 }
 
@@ -92,6 +95,7 @@ wb::KArgs base_args(const wb_state* st) {
     a.block = st->d.block;
     a.k_hi = st->d.k_hi;
     a.bbar = st->d.bbar;
+    a.mem_bits = st->d.mem_bits;
     return a;
 }
 
@@ -146,6 +150,7 @@ int state_alloc(const wb_layout_desc* d, void* dev_state, size_t state_bytes_in,
     st->region_stride = round256(region_size(*d));
     st->regions_bytes = st->region_stride * size_t(d->B) * size_t(d->H);
     st->perm_dev = d->kind == WB_MIXED ? st->state + st->regions_bytes : nullptr;
+    st->activity = nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // zero state: all layouts but BITALLOC encode S_0 = 0 as zero bytes
@@ -197,7 +202,16 @@ int state_step_decode(wb_state* st, const float* q, const float* k, const float*
     a.s = s;
     a.o = o;
     a.t = t;
+    a.activity = st->activity;
     return hip_status(wb::launch_wb(st->d, wb::OP_STEP, a, static_cast<hipStream_t>(stream)));
+}
+
+int state_set_activity(wb_state* st, uint32_t* dev_counters) {
+    if (!st) return WB_EINVAL;
+    if (st->d.kind != WB_UNIFORM) return WB_EUNSUPPORTED;
+    if (dev_counters && !aligned16(dev_counters)) return WB_EALIGN;
+    st->activity = dev_counters;
+    return WB_OK;
 }
 
 int state_dequant(const wb_state* st, float* S, void* stream) {

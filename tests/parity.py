@@ -186,6 +186,17 @@ def compare_write_back(lay: L.Layout, reg_in, reg_gpu, wb, e_in, e_gpu, t, b, h,
             idx = np.argwhere(~ok)[:3]
             tally.bad.append((where, "codes", idx.tolist(), gc[~ok][:3].tolist(), oc[~ok][:3].tolist(),
                               wb2.boundary[~ok][:3].tolist(), wb2.tau[~ok][:3].tolist()))
+    if lay.mode in ("dir", "resq"):
+        # direction counters / k-bit residual values: exact, except where a decision
+        # (level, vote band edge, residual level) is within the window
+        eg = np.asarray(e_gpu, np.float64)
+        eo = wb2.e_new
+        near_any = wb2.boundary <= window
+        off = (eg != eo) & ~near_any
+        tally.e_worst = max(tally.e_worst, float(np.max(np.where(near_any, 0.0, np.abs(eg - eo)))))
+        if off.any():
+            i = np.unravel_index(np.argmax(off), off.shape)
+            tally.bad.append((where, "memory state", i, eg[i], eo[i], wb2.boundary[i]))
     if lay.mode == "ef":
         eg = np.asarray(e_gpu, np.float64)
         eo = wb2.e_new

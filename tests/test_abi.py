@@ -63,7 +63,8 @@ def test_descriptor_validation():
     ok = wb.make_desc("mixed", "rtn", 2, 2)
     assert _code(ok) == 0
     bad = [
-        (dict(kind=7), -1), (dict(mode=5), -1), (dict(decay=3), -1), (dict(B=0), -1), (dict(reserved=1), -1),
+        (dict(kind=7), -1), (dict(mode=5), -1), (dict(decay=3), -1), (dict(B=0), -1), (dict(mem_bits=1), -1),
+        (dict(mode=3, mem_bits=2), -3), (dict(mode=4, mem_bits=2), -3),
         (dict(dk=64), -3), (dict(dv=64), -3), (dict(block=48), -3), (dict(k_hi=0), -3), (dict(k_hi=128), -3),
         (dict(k_hi=20), -3),
     ]
@@ -80,6 +81,14 @@ def test_descriptor_validation():
     assert _code(d) == -3
     d = wb.make_desc("fp32", "rtn", 1, 1, 32, 32)
     assert _code(d) == -3
+    # temporal-memory rules: uniform grid only, 1 <= k <= 8, a float32 side value per element
+    for mode in ("dir", "resq"):
+        assert _code(wb.make_desc("uniform", mode, 1, 1, 16, 16, mem_bits=0)) == -1
+        assert _code(wb.make_desc("uniform", mode, 1, 1, 16, 16, mem_bits=9)) == -1
+        d = wb.make_desc("uniform", mode, 2, 3, mem_bits=3)
+        assert _code(d) == 0
+        assert wb.buffer_sizes(d)[1] == 2 * 3 * 128 * 128 * 4
+        assert _code(wb.make_desc("bitalloc", mode, 1, 1, mem_bits=2)) == -3
 
 
 def test_alloc_rejects_bad_buffers_without_touching_the_gpu():

@@ -9,7 +9,7 @@ from oracle import layouts as L
 from oracle.allocation import allocate_head
 from oracle.damp import risk_scores, select_permutation
 from oracle.numerics import f16_value
-from oracle.step import allocate_region, export_state, import_state, write_back
+from oracle.step import allocate_region, decode_step, export_state, import_state, write_back
 from synth import decode_inputs
 from tests.parity import Tally, check_head
 
@@ -35,7 +35,7 @@ def _state(lay, perm=None):
     wb = _wb()
     return wb.WriteBackState(lay.kind, lay.mode, lay.B, lay.H, lay.dk, lay.dv, lay.per_row_decay,
                              bits=lay.bits, block=lay.block, k_hi=lay.k_hi, bbar=lay.bbar, bmin=lay.bmin,
-                             bmax=lay.bmax, seed=lay.seed, perm=perm)
+                             bmax=lay.bmax, seed=lay.seed, perm=perm, mem_bits=lay.mem_bits)
 
 
 def _warm_state(rng, B, H, dk, dv):
@@ -101,6 +101,69 @@ def test_tiny_uniform_4bit_rtn_every_step():
 def test_tiny_uniform_4bit_error_feedback_every_step():
     lay = _layout(L.UNIFORM, "ef", 1, 1, 16, bits=4)
     run_decode(lay, 256, warm=False, seed=0)
+
+
+@pytest.mark.parametrize("mode,k", [("dir", 2), ("dir", 3), ("resq", 2), ("resq", 4)])
+def test_tiny_uniform_4bit_temporal_memory_every_step(mode, k):
+    lay = _layout(L.UNIFORM, mode, 1, 1, 16, bits=4, mem_bits=k)
+    run_decode(lay, 256, warm=False, seed=0)
+
+
+@pytest.mark.parametrize("mode,k,bits", [("dir", 2, 4), ("dir", 4, 2), ("resq", 3, 4), ("resq", 2, 8)])
+def test_uniform_temporal_memory_128(mode, k, bits):
+    lay = _layout(L.UNIFORM, mode, 2, 2, 128, bits=bits, mem_bits=k)
+    run_decode(lay, 6, warm=True, seed=14)
+
+
+@pytest.mark.parametrize("mode,k", [("rtn", 0), ("ef", 0), ("dir", 2), ("resq", 3)])
+def test_uniform_write_activity_counters(mode, k):
+    """Per-head write activity summed over the steps, against the oracle's counts on the
+    same stored states (each step starts from the GPU's region and side state); an
+    element may be counted differently only where one of its decisions (write margin 1,
+    vote band edges, level rounding) is within the comparison window."""
+    print(f"\n[case] write activity UNIFORM-4 mode={mode} k={k}", flush=True)
+    from tests.parity import WINDOW
+    B, H, dk, T = 2, 2, 128, 6
+    lay = _layout(L.UNIFORM, mode, B, H, dk, bits=4, mem_bits=k)
+    rng = np.random.default_rng(15)
+    st = _state(lay)
+    inp = decode_inputs(15, B, H, dk, dk, T, True)
+    dev = {key: _to_dev(val) for key, val in inp.items()}
+    st.quantize(_to_dev((_warm_state(rng, B, H, dk, dk) * 0.3).astype(np.float32)))
+    ctr = torch.zeros((B, H, 4), dtype=torch.int32, device="cuda")
+    st.set_activity(ctr)
+    o = torch.zeros((B, H, dk), dtype=torch.float32, device="cuda")
+    expect = np.zeros((B, H, 4), np.int64)
+    slack = np.zeros((B, H), np.int64)
+    step = 2.0 ** -3
+    for t in range(T):
+        torch.cuda.synchronize()
+        regs = st.regions().cpu().numpy()
+        res = st.residuals()
+        e_in = res.cpu().numpy() if res is not None else None
+        st.step_decode(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, t)
+        for b in range(B):
+            for h in range(H):
+                reg_in = regs[b * H + h][: lay.region_size()]
+                r = decode_step(lay, reg_in, None if e_in is None else e_in[b, h], inp["q"][t, b, h],
+                                inp["k"][t, b, h], inp["v"][t, b, h], inp["beta"][t, b, h], inp["s"][b, h],
+                                t, b, h)
+                expect[b, h] += r.wb.activity
+                kp = L.decode_region(lay, reg_in).kappa
+                ad = np.abs(r.wb.X - kp * step) / step
+                near = (np.abs(ad - 0.5) <= WINDOW) | (np.abs(ad - 0.125) <= WINDOW) | (r.wb.boundary <= WINDOW)
+                slack[b, h] += int(near.sum())
+    st.set_activity(None)
+    torch.cuda.synchronize()
+    got = ctr.cpu().numpy().astype(np.int64)
+    print("[activity] gpu", got.sum(axis=(0, 1)).tolist(), "oracle", expect.sum(axis=(0, 1)).tolist(),
+          "near-boundary elements", int(slack.sum()), flush=True)
+    assert np.all(np.abs(got - expect) <= slack[..., None]), (got, expect, slack)
+    assert expect[..., 0].sum() > 0 and expect[..., 2].sum() > 0
+    if mode == "dir":
+        assert expect[..., 3].sum() > 0
+    else:
+        assert got[..., 3].sum() == 0
 
 
 def test_tiny_fp32_identity():
