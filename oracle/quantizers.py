@@ -28,9 +28,24 @@ method"), the readings of this module:
     T = 2^(k-1), the stored level moves one step in that direction (clipped at the grid
     rails) and the counter resets; smaller proposals leave level and counter unchanged.
     The counter therefore takes the 2^k - 1 values -(T-1) .. T-1.
-Write activity of one step (per head): dead-zone elements (write margin M < 1),
-elements whose stored level changed, eligible sub-threshold proposals (Delta_B/8 <
-|delta| < Delta_B/2) and direction-memory triggers (a trigger at a rail moves nothing).
+Write activity of one step (per head; [WB] "Direction-memory events", "Persistence
+metrics", "State diagnostics", "Write-back behavior"), read as eight counts:
+  0 dead-zone elements (write margin M < 1);
+  1 elements whose stored level changed;
+  2 eligible votes: proposals with Delta_B/8 < |delta| < Delta_B/2, signed by delta
+    (counted under every rule, whether or not a direction memory consumes them);
+  3 direction-memory triggers (a trigger at a rail moves nothing);
+  4 sub-threshold writes: M < 1 and the stored level changed anyway;
+  5 / 6 same-sign / opposite-sign vote transitions: an eligible vote whose element
+    also cast an eligible vote on the previous step, with the same / the other sign;
+  7 runs started: an eligible vote that does not continue a run. A run is a string of
+    eligible votes of one sign on consecutive steps; it ends at a reversal, an
+    ineligible step, or a step whose vote changed the stored level or triggered (the
+    ordinary write and the trigger that end runs). Every vote belongs to one run, so
+    the mean run length over a sequence is count 2 / count 7, runs still open at its
+    end included (they end at sequence termination).
+The per-element state this needs between steps is one byte: 0 (no eligible vote),
+1 / 2 (a positive / negative vote, run open), 5 / 6 (the same vote, run closed).
 
 Every grid here is "offset + kappa * step" with integer kappa in [lo, hi]; a rule
 works on the grid coordinate tau = (x - offset) / step.
@@ -130,7 +145,7 @@ class MemoryRounded:
     side_new: np.ndarray    # new residual value (residual memory) or counter (direction memory)
     tau: np.ndarray         # grid coordinate of the value rounded (h or h + e)
     boundary: np.ndarray    # distance (grid units) to the nearest decision boundary
-    activity: np.ndarray    # [dead-zone, level changes, votes, direction-memory triggers]
+    triggers: np.ndarray    # direction-memory triggers (bool)
 
 
 def uniform_memory_round(x, B: int, mode: str, kappa_prev, side, kbits: int) -> MemoryRounded:
@@ -172,17 +187,35 @@ def uniform_memory_round(x, B: int, mode: str, kappa_prev, side, kbits: int) -> 
         boundary = np.minimum(bnd_h, np.minimum(np.abs(ad - 0.125), np.abs(ad - 0.5)))
     else:
         raise ValueError(mode)
-    activity = np.array([int(dead.sum()), int((kappa != kp).sum()), int(vote.sum()), int(moves.sum())],
-                        dtype=np.int64)
-    return MemoryRounded(kappa.astype(np.int64), side_new, tau, boundary, activity)
+    return MemoryRounded(kappa.astype(np.int64), side_new, tau, boundary, moves)
 
 
-def uniform_activity(x, kappa_prev, kappa_new, B: int) -> np.ndarray:
-    """[dead-zone, level changes, votes, 0] of one step under a rule without direction
-    memory (h_t = x; levels entering and leaving the step)."""
-    ad = np.abs(np.asarray(x, np.float64) - np.asarray(kappa_prev, np.float64) * uniform_step(B)) / uniform_step(B)
-    return np.array([int((2.0 * ad < 1.0).sum()), int((np.asarray(kappa_new) != np.asarray(kappa_prev)).sum()),
-                     int(((ad > 0.125) & (ad < 0.5)).sum()), 0], dtype=np.int64)
+def write_activity(x, kappa_prev, kappa_new, B: int, triggers, votes_prev):
+    """The eight write-activity counts of one step on the uniform B-bit grid (h_t = x,
+    levels entering and leaving the step, direction-memory triggers, the vote state of
+    the previous step) and the new vote state; states and counts as described in the
+    module docstring."""
+    x = np.asarray(x, np.float64)
+    kp = np.asarray(kappa_prev, np.int64)
+    kn = np.asarray(kappa_new, np.int64)
+    trig = np.asarray(triggers, bool)
+    vp = np.asarray(votes_prev, np.int64)
+    step = uniform_step(B)
+    delta = x - kp * step
+    ad = np.abs(delta) / step
+    dead = 2.0 * ad < 1.0
+    change = kn != kp
+    vote = (ad > 0.125) & (ad < 0.5)
+    sign = np.where(vote, np.where(delta > 0, 1, 2), 0)
+    prev_sign = vp & 3
+    same = vote & (prev_sign == sign)
+    opposite = vote & (prev_sign != 0) & (prev_sign != sign)
+    continues = vote & (vp == sign)                  # same sign, previous run still open
+    closed = change | trig
+    votes_new = np.where(vote, sign | np.where(closed, 4, 0), 0)
+    counts = np.array([dead.sum(), change.sum(), vote.sum(), trig.sum(), (dead & change).sum(),
+                       same.sum(), opposite.sum(), (vote & ~continues).sum()], dtype=np.int64)
+    return counts, votes_new.astype(np.uint8)
 
 
 def write_margin(h, q_prev, B: int):

@@ -34,7 +34,7 @@ from .allocation import allocate_head
 from .numerics import f16, f16_bits
 from .philox import sr_draws
 from .quantizers import (DIR, EF, RESQ, SR, affine_metadata, affine_round, levels_n, row_step,
-                         sym_round, uniform_activity, uniform_memory_round, uniform_round)
+                         sym_round, uniform_memory_round, uniform_round, write_activity)
 from .recurrence import delta_step
 
 
@@ -47,7 +47,8 @@ class WriteBack:
     meta: dict = field(default_factory=dict)       # metadata as stored
     tau: np.ndarray | None = None  # grid coordinate per element (rounding rows)
     boundary: np.ndarray | None = None
-    activity: np.ndarray | None = None   # UNIFORM: [dead-zone, changes, votes, triggers]
+    activity: np.ndarray | None = None   # UNIFORM: the eight write-activity counts
+    votes_new: np.ndarray | None = None  # UNIFORM: per-element vote state after the step
 
 
 def _draws(lay, b, h, t, rows):
@@ -58,12 +59,14 @@ def _draws(lay, b, h, t, rows):
 
 
 def write_back(lay: L.Layout, X: np.ndarray, e_in, t: int, b: int, h: int,
-               prev: L.Content | None = None, meta_override: dict | None = None) -> WriteBack:
+               prev: L.Content | None = None, meta_override: dict | None = None,
+               votes_in=None) -> WriteBack:
     """Round stored-domain values X (physical rows) into a new region.
 
-    ``prev`` supplies the BITALLOC widths and fit indices; ``meta_override`` (tests)
-    replaces the computed metadata so that X can be re-rounded with another side's
-    metadata.
+    ``prev`` supplies the BITALLOC widths and fit indices and the UNIFORM levels entering
+    the step; ``meta_override`` (tests) replaces the computed metadata so that X can be
+    re-rounded with another side's metadata. ``votes_in`` is the UNIFORM vote state of
+    the previous step (zeros when absent) for the write-activity counts.
     """
     dk, dv = lay.dk, lay.dv
     X = np.asarray(X, dtype=np.float64)
@@ -82,14 +85,16 @@ def write_back(lay: L.Layout, X: np.ndarray, e_in, t: int, b: int, h: int,
         mr = uniform_memory_round(X, lay.bits, mode, kp, e, lay.mem_bits)
         wb.region = L.encode_region(lay, L.Content(kappa=mr.kappa))
         tau, bnd, e_new = mr.tau, mr.boundary, mr.side_new
-        wb.activity = mr.activity
+        wb.activity, wb.votes_new = write_activity(X, kp, mr.kappa, lay.bits, mr.triggers,
+                                                   np.zeros((dk, dv)) if votes_in is None else votes_in)
     elif lay.kind == L.UNIFORM:
         r16 = _draws(lay, b, h, t, range(dk)) if mode == SR else None
         rr = uniform_round(X, lay.bits, mode, e, r16)
         wb.region = L.encode_region(lay, L.Content(kappa=rr.kappa))
         tau, bnd, e_new = rr.tau, rr.boundary, rr.e_new
         if prev is not None:
-            wb.activity = uniform_activity(X, prev.kappa, rr.kappa, lay.bits)
+            wb.activity, wb.votes_new = write_activity(X, prev.kappa, rr.kappa, lay.bits, np.zeros((dk, dv), bool),
+                                                       np.zeros((dk, dv)) if votes_in is None else votes_in)
     elif lay.kind in (L.HAD_INT8, L.MIXED):
         G = lay.block
         nb = dv // G
@@ -169,14 +174,15 @@ class StepResult:
 
 
 def decode_step(lay: L.Layout, region, e_in, q, k, v, beta, s, t: int, b: int, h: int,
-                perm=None) -> StepResult:
-    """One decode token for head (b, h), starting from the given stored region."""
+                perm=None, votes_in=None) -> StepResult:
+    """One decode token for head (b, h), starting from the given stored region (and, for
+    the UNIFORM write-activity counts, the previous step's vote state)."""
     content = L.decode_region(lay, region)
     Y = L.stored_values(lay, content)
     S = L.to_logical(lay, Y, perm)
     S_new, o = delta_step(S, q, k, v, beta, s)
     X = L.to_stored(lay, S_new, perm)
-    wb = write_back(lay, X, e_in, t, b, h, prev=content)
+    wb = write_back(lay, X, e_in, t, b, h, prev=content, votes_in=votes_in)
     return StepResult(wb=wb, o=o, S_prev=S, S_new=S_new)
 
 

@@ -132,11 +132,17 @@ def test_symmetric_row_levels():
 # counter reset at every stored-level change, moves clipped at the rails; the residual
 # of error feedback kept on the k-bit grid j Delta / 2^(k-1), j in [-2^(k-1), 2^(k-1)).
 
-from oracle.quantizers import residual_quantize, uniform_memory_round  # noqa: E402
+from oracle.quantizers import residual_quantize, uniform_memory_round, write_activity  # noqa: E402
 
 
 def _dir(x, kp, c, k=2, B=4):
     return uniform_memory_round(np.array(x, float), B, "dir", np.array(kp), np.array(c, float), k)
+
+
+def _act(x, kp, r, B=4):
+    """[dead-zone, changes, votes, triggers] of one step from no previous vote."""
+    n = len(x)
+    return write_activity(np.array(x, float), np.array(kp), r.kappa, B, r.triggers, np.zeros(n))[0][:4].tolist()
 
 
 def test_direction_memory_votes_trigger_and_reset():
@@ -147,18 +153,18 @@ def test_direction_memory_votes_trigger_and_reset():
     # the second same-sign vote reaches T: one level up, counter reset
     r = _dir([0.03], [0], [1])
     assert r.kappa.tolist() == [1] and r.side_new.tolist() == [0.0]
-    assert r.activity.tolist() == [1, 1, 1, 1]
+    assert _act([0.03], [0], r) == [1, 1, 1, 1]
     # an opposite vote takes the counter back, no move
     r = _dir([-0.03], [0], [1])
     assert r.kappa.tolist() == [0] and r.side_new.tolist() == [0.0]
     # below the band: neither vote nor reset
     r = _dir([0.01], [0], [1])
     assert r.kappa.tolist() == [0] and r.side_new.tolist() == [1.0]
-    assert r.activity.tolist() == [1, 0, 0, 0]
+    assert _act([0.01], [0], r) == [1, 0, 0, 0]
     # an ordinary write (nearest level changes) stores it and resets the counter
     r = _dir([0.07], [0], [-1])
     assert r.kappa.tolist() == [1] and r.side_new.tolist() == [0.0]
-    assert r.activity.tolist() == [0, 1, 0, 0]
+    assert _act([0.07], [0], r) == [0, 1, 0, 0]
     # the band edges are excluded: |delta| = Delta/8 and |delta| = Delta/2 (a tie that
     # rounds back to the even level 0) do not vote
     r = _dir([d / 8, d / 2, -d / 8], [0, 0, 0], [1, 1, 1])
@@ -173,7 +179,7 @@ def test_direction_memory_rails_and_counter_range():
     # at the upper rail a trigger cannot move the level; the counter still resets
     r = _dir([7 * d + 0.03, -8 * d - 0.03], [7, -8], [1, -1])
     assert r.kappa.tolist() == [7, -8] and r.side_new.tolist() == [0.0, 0.0]
-    assert r.activity.tolist() == [2, 0, 2, 2]
+    assert _act([7 * d + 0.03, -8 * d - 0.03], [7, -8], r) == [2, 0, 2, 2]
     # k = 3: T = 4, the counter runs through -3 .. 3 before a move
     c, kp = 0.0, 0
     seen = []
@@ -209,3 +215,67 @@ def test_residual_memory_grid_and_carry():
     ef = uniform_round(xs, 4, "ef", es)
     assert np.array_equal(r.kappa, ef.kappa)
     assert np.allclose(r.side_new, ef.e_new, atol=d * 2.0 ** -28)
+
+
+def _run_sequence(xs_rel, k=3, B=4, mode="dir"):
+    """Drive one element through proposals given relative to its stored level; returns
+    the summed eight counts and the per-step (vote sign, level changed or triggered)."""
+    d = uniform_step(B)
+    kp, side, vs = 0, 0.0, np.zeros(1)
+    total = np.zeros(8, np.int64)
+    events = []
+    for rel in xs_rel:
+        x = np.array([kp * d + rel])
+        if mode in ("dir", "resq"):
+            r = uniform_memory_round(x, B, mode, np.array([kp]), np.array([side]), k)
+            kn, side, trig = r.kappa, float(r.side_new[0]), r.triggers
+        else:
+            rr = uniform_round(x, B, mode, np.array([side]))
+            kn, trig = rr.kappa, np.zeros(1, bool)
+            side = float(rr.e_new[0]) if mode == "ef" else 0.0
+        cnt, vs = write_activity(x, np.array([kp]), kn, B, trig, vs)
+        total += cnt
+        a = abs(rel) / d
+        sign = (1 if rel > 0 else -1) if 0.125 < a < 0.5 else 0
+        events.append((sign, bool(kn[0] != kp or trig[0])))
+        kp = int(kn[0])
+    return total, events
+
+
+def test_vote_persistence_hand_sequence():
+    # k = 3 (T = 4), Delta = 0.125, vote band (0.015625, 0.0625) around the stored level:
+    # + + - (small) + + +(trigger: level 0 -> 1) +
+    total, _ = _run_sequence([0.03, 0.03, -0.03, 0.01, 0.03, 0.03, 0.03, 0.03])
+    # dead 8, changes 1, votes 7, triggers 1, sub-threshold writes 1 (the trigger),
+    # same-sign pairs 4 (steps 1, 5, 6, 7), opposite 1 (step 2), runs 4:
+    # [0, 1], [2], [4, 5, 6], [7] -- the trigger ends the third run
+    assert total.tolist() == [8, 1, 7, 1, 1, 4, 1, 4]
+
+
+def test_vote_persistence_matches_brute_force_runs():
+    """Runs split by a second method: maximal groups of equal nonzero sign on consecutive
+    steps, cut again after every step that changed the level or triggered."""
+    import itertools
+    rng = np.random.default_rng(11)
+    d = uniform_step(4)
+    for mode, k in (("dir", 2), ("dir", 3), ("rtn", 0), ("ef", 0), ("resq", 2)):
+        rel = rng.choice([-0.7, -0.4, -0.03, -0.01, 0.0, 0.01, 0.03, 0.05, 0.4, 0.7], size=400) * d * 8
+        total, ev = _run_sequence(rel, k=max(k, 1), mode=mode)
+        runs = 0
+        for sgn, grp in itertools.groupby(ev, key=lambda e: e[0]):
+            if sgn == 0:
+                continue
+            g = list(grp)
+            runs += 1 + sum(1 for e in g[:-1] if e[1])
+        pairs = list(zip(ev, ev[1:]))
+        same = sum(1 for a, b in pairs if a[0] != 0 and a[0] == b[0])
+        opp = sum(1 for a, b in pairs if a[0] != 0 and b[0] != 0 and a[0] != b[0])
+        votes = sum(1 for e in ev if e[0] != 0)
+        assert (total[2], total[5], total[6], total[7]) == (votes, same, opp, runs), mode
+        assert votes > 50 and runs < votes and opp > 0
+        # nearest-level writing never changes a level below the write margin; under
+        # direction memory only a trigger that is not held at a rail does
+        if mode == "rtn":
+            assert total[4] == 0 and total[3] == 0
+        if mode == "dir":
+            assert 0 < total[4] <= total[3]
