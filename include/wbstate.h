@@ -163,15 +163,26 @@ int state_prefill_chunk(wb_state* st, const uint16_t* q_bf16, const uint16_t* k_
                         const uint16_t* v_bf16, const float* beta, const float* s, float* o,
                         int T, int chunk, int C, uint64_t t0, void* stream);
 
-/* UNIFORM only: write-activity counters. With a non-NULL `dev_counters` (uint32
- * [B*H][4], 16-byte aligned, caller-owned and zeroed by the caller), every following
- * decode step adds, per head, the number of elements whose write margin
- * M = 2 |h - q| / step is below 1 (the dead zone), whose stored level changed, whose
- * proposal lies in the vote band step/8 < |h - q| < step/2, and (WB_DIR) whose counter
- * triggered a one-level move ([WB] "Methods" diagnostics, "Direction-memory events",
- * "State diagnostics"; q is the level entering the step, h the updated value). NULL
- * stops counting. */
-int state_set_activity(wb_state* st, uint32_t* dev_counters);
+/* UNIFORM only: write-activity diagnostics ([WB] "Methods": "Direction-memory events",
+ * "Persistence metrics", "State diagnostics"; "Write-back behavior"). `dev_counters`
+ * (uint32 [B*H][8]) and `dev_votes` (uint8 [B*H][dk][dv], one byte per element) are
+ * device buffers, 16-byte aligned, caller-owned and zeroed by the caller at the start
+ * of a sequence; both non-NULL or both NULL (EINVAL otherwise; NULL stops counting).
+ * With q the level entering a decode step, h the updated value, delta = h - q and
+ * M = 2 |delta| / step, every following decode step adds per head:
+ *   [0] elements with M < 1 (the dead zone);
+ *   [1] elements whose stored level changed;
+ *   [2] eligible votes, step/8 < |delta| < step/2 (under every rule);
+ *   [3] direction-memory triggers (WB_DIR; a trigger at a rail moves nothing);
+ *   [4] sub-threshold writes: M < 1 and the level changed;
+ *   [5] / [6] votes following a vote of the same / the other sign on the previous step;
+ *   [7] runs started: votes that do not continue a run of same-sign votes on
+ *       consecutive steps (a run ends at a reversal, a step without a vote, or a vote
+ *       step that changed the level or triggered). Mean run length = [2] / [7].
+ * `dev_votes` carries, per element, the previous step's vote: 0 none, 1 / 2 a
+ * positive / negative vote whose run is open, 5 / 6 one whose run closed. Prefill
+ * write-backs neither count nor update it. */
+int state_set_activity(wb_state* st, uint32_t* dev_counters, uint8_t* dev_votes);
 
 /* BITALLOC only: recompute per-row widths and clipping-fit indices from the stored
  * state and repack it in place ([LBRS] "Approximate erasure rate", "Range

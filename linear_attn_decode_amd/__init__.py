@@ -50,7 +50,7 @@ SIGNATURES = {
     "state_quantize": (_I, [_P, _P, _P]),
     "state_export": (_I, [_P, ctypes.POINTER(_P), ctypes.POINTER(_SZ), ctypes.POINTER(_P)]),
     "state_damp_select": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _F, _P, _P, _P]),
-    "state_set_activity": (_I, [_P, _P]),
+    "state_set_activity": (_I, [_P, _P, _P]),
     "state_status_str": (ctypes.c_char_p, [_I]),
 }
 
@@ -201,16 +201,21 @@ class WriteBackState:
             return None
         return self.side[: self.side_bytes // 4].view(self.B, self.H, self.dk, self.dv)
 
-    def set_activity(self, counters=None):
+    def set_activity(self, counters=None, votes=None):
         """Count write activity (UNIFORM): later decode steps add, per head, [dead-zone
-        elements, level changes, vote-band proposals, direction triggers] into
-        ``counters`` (int32 tensor [B, H, 4], zeroed by the caller); None stops."""
+        elements, level changes, votes, direction triggers, sub-threshold writes,
+        same-sign vote transitions, opposite-sign vote transitions, runs started] into
+        ``counters`` (int32 [B, H, 8]); ``votes`` (uint8 [B, H, dk, dv]) carries each
+        element's previous vote. Both zeroed by the caller at a sequence start; both
+        None stops."""
         import torch
-        p = None
+        pc = pv = None
         if counters is not None:
-            p = _ptr(counters, torch.int32, (self.B, self.H, 4), "counters")
-        self._activity = counters
-        check(lib().state_set_activity(self.handle, p), "state_set_activity")
+            pc = _ptr(counters, torch.int32, (self.B, self.H, 8), "counters")
+        if votes is not None:
+            pv = _ptr(votes, torch.uint8, (self.B, self.H, self.dk, self.dv), "votes")
+        self._activity = (counters, votes)
+        check(lib().state_set_activity(self.handle, pc, pv), "state_set_activity")
 
 
 def damp_select(samples, s, k_hi=16, block=32, tau=0.01, stream=None):

@@ -411,8 +411,10 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
         for (int i = tid; i < code_words; i += NT) sm.reg[i] = 0u;
         __syncthreads();
     }
-    // write activity of this lane (UNIFORM decode steps with counters attached)
-    uint32_t n_dead = 0, n_change = 0, n_vote = 0, n_trig = 0;
+    // write activity of this lane (UNIFORM decode steps with counters attached): dead-zone,
+    // level changes, votes, triggers, sub-threshold writes, same-sign and opposite-sign
+    // vote transitions, runs started
+    uint32_t nact[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (act) {
         const uint32_t bh = uint32_t(head);
 #pragma unroll
@@ -441,6 +443,12 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     else if (B == 4) prev = *reinterpret_cast<const uint32_t*>(region + boff);
                     else prev = *reinterpret_cast<const uint64_t*>(region + boff);
                 }
+                // vote state of the previous step, one byte per element: 0 none, 1 / 2 a
+                // positive / negative vote with its run open, +4 when the run closed
+                const bool count = OP == OP_STEP && A.activity != nullptr;
+                uint8_t* vptr = count ? A.votes + ((size_t)head * DK + row) * DV + 8 * cg : nullptr;
+                const uint64_t vprev = count ? *reinterpret_cast<const uint64_t*>(vptr) : 0ull;
+                uint64_t vnew = 0;
                 uint64_t fld = 0;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
@@ -484,14 +492,23 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     } else {
                         kap = round_rule<EMODE, Real>(h, Real(e[m][c]), step, Real(0), lo, hi, r16[c], &en[c]);
                     }
-                    if (track) {
-                        n_dead += Real(2) * ad < step;
-                        n_change += kap != kp;
-                        n_vote += vote;
-                        n_trig += trig;
+                    if (count) {
+                        const bool dead = Real(2) * ad < step, change = kap != kp;
+                        const uint32_t vp = uint32_t(vprev >> (8 * c)) & 0xFFu;
+                        const uint32_t sg = vote ? (dlt > Real(0) ? 1u : 2u) : 0u;
+                        nact[0] += dead;
+                        nact[1] += change;
+                        nact[2] += vote;
+                        nact[3] += trig;
+                        nact[4] += dead && change;
+                        nact[5] += vote && (vp & 3u) == sg;
+                        nact[6] += vote && (vp & 3u) != 0u && (vp & 3u) != sg;
+                        nact[7] += vote && vp != sg;
+                        vnew |= uint64_t(sg | ((vote && (change || trig)) ? 4u : 0u)) << (8 * c);
                     }
                     fld |= uint64_t(uint32_t(kap) & ((1u << B) - 1)) << (c * B);
                 }
+                if (count) *reinterpret_cast<uint64_t*>(vptr) = vnew;
                 if (B == 2) *reinterpret_cast<uint16_t*>(region + boff) = uint16_t(fld);
                 else if (B == 4) *reinterpret_cast<uint32_t*>(region + boff) = uint32_t(fld);
                 else *reinterpret_cast<uint64_t*>(region + boff) = fld;
@@ -577,18 +594,14 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
     if (KIND == WB_UNIFORM && OP == OP_STEP && A.activity != nullptr) {
         // sum over the wavefront, one atomic add per counter and wavefront
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            n_dead += __shfl_xor(n_dead, d, 64);
-            n_change += __shfl_xor(n_change, d, 64);
-            n_vote += __shfl_xor(n_vote, d, 64);
-            n_trig += __shfl_xor(n_trig, d, 64);
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) nact[i] += __shfl_xor(nact[i], d, 64);
         }
         if (lane == 0) {
-            uint32_t* ctr = A.activity + (size_t)head * 4;
-            atomicAdd(ctr + 0, n_dead);
-            atomicAdd(ctr + 1, n_change);
-            atomicAdd(ctr + 2, n_vote);
-            atomicAdd(ctr + 3, n_trig);
+            uint32_t* ctr = A.activity + (size_t)head * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) atomicAdd(ctr + i, nact[i]);
         }
     }
     if (KIND == WB_BITALLOC) {

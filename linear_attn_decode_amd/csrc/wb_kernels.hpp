@@ -32,7 +32,8 @@ struct KArgs {
     int k_hi = 0;
     int bbar = 4;
     int mem_bits = 0;                 // k of direction / residual memory
-    uint32_t* activity = nullptr;     // [B*H][4] write-activity counters (UNIFORM) or null
+    uint32_t* activity = nullptr;     // [B*H][8] write-activity counters (UNIFORM) or null
+    uint8_t* votes = nullptr;         // [B*H][DK][DV] vote state, with `activity`
 };
 
 // One launch of the decode / import / export kernel for every head of the layout.

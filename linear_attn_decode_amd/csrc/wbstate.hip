@@ -20,6 +20,7 @@ struct wb_state {
     size_t regions_bytes;
     uint8_t* perm_dev;     // inside the state buffer (MIXED), else null
     uint32_t* activity;    // caller's write-activity counters (UNIFORM), or null
+    uint8_t* votes;        // caller's per-element vote state, set with `activity`
 };
 
 namespace {
@@ -151,6 +152,7 @@ int state_alloc(const wb_layout_desc* d, void* dev_state, size_t state_bytes_in,
     st->regions_bytes = st->region_stride * size_t(d->B) * size_t(d->H);
     st->perm_dev = d->kind == WB_MIXED ? st->state + st->regions_bytes : nullptr;
     st->activity = nullptr;
+    st->votes = nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // zero state: all layouts but BITALLOC encode S_0 = 0 as zero bytes
@@ -203,14 +205,17 @@ int state_step_decode(wb_state* st, const float* q, const float* k, const float*
     a.o = o;
     a.t = t;
     a.activity = st->activity;
+    a.votes = st->votes;
     return hip_status(wb::launch_wb(st->d, wb::OP_STEP, a, static_cast<hipStream_t>(stream)));
 }
 
-int state_set_activity(wb_state* st, uint32_t* dev_counters) {
+int state_set_activity(wb_state* st, uint32_t* dev_counters, uint8_t* dev_votes) {
     if (!st) return WB_EINVAL;
     if (st->d.kind != WB_UNIFORM) return WB_EUNSUPPORTED;
-    if (dev_counters && !aligned16(dev_counters)) return WB_EALIGN;
+    if ((dev_counters == nullptr) != (dev_votes == nullptr)) return WB_EINVAL;
+    if (dev_counters && (!aligned16(dev_counters) || !aligned16(dev_votes))) return WB_EALIGN;
     st->activity = dev_counters;
+    st->votes = dev_votes;
     return WB_OK;
 }
 

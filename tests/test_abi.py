@@ -123,6 +123,7 @@ def test_calls_reject_null_handles_and_pointers():
     assert L_.state_quantize(None, p, None) == -1
     assert L_.state_allocate_bits(None, p, None, None) == -1
     assert L_.state_free(None) == -1
+    assert L_.state_set_activity(None, p, p) == -1
     assert L_.state_prefill_chunk(None, p, p, p, p, p, p, 8, 64, 8, 0, None) == -1
     a, b, c = ctypes.c_void_p(), ctypes.c_size_t(), ctypes.c_void_p()
     assert L_.state_export(None, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == -1

@@ -117,10 +117,11 @@ def test_uniform_temporal_memory_128(mode, k, bits):
 
 @pytest.mark.parametrize("mode,k", [("rtn", 0), ("ef", 0), ("dir", 2), ("resq", 3)])
 def test_uniform_write_activity_counters(mode, k):
-    """Per-head write activity summed over the steps, against the oracle's counts on the
-    same stored states (each step starts from the GPU's region and side state); an
-    element may be counted differently only where one of its decisions (write margin 1,
-    vote band edges, level rounding) is within the comparison window."""
+    """Per-head write activity (all eight counts) summed over the steps, and the vote
+    state after every step, against the oracle on the same stored states (each step
+    starts from the GPU's region, side state and vote state); an element may differ only
+    where one of its decisions (write margin 1, vote band edges, level rounding) is
+    within the comparison window."""
     print(f"\n[case] write activity UNIFORM-4 mode={mode} k={k}", flush=True)
     from tests.parity import WINDOW
     B, H, dk, T = 2, 2, 128, 6
@@ -130,38 +131,46 @@ def test_uniform_write_activity_counters(mode, k):
     inp = decode_inputs(15, B, H, dk, dk, T, True)
     dev = {key: _to_dev(val) for key, val in inp.items()}
     st.quantize(_to_dev((_warm_state(rng, B, H, dk, dk) * 0.3).astype(np.float32)))
-    ctr = torch.zeros((B, H, 4), dtype=torch.int32, device="cuda")
-    st.set_activity(ctr)
+    ctr = torch.zeros((B, H, 8), dtype=torch.int32, device="cuda")
+    votes = torch.zeros((B, H, dk, dk), dtype=torch.uint8, device="cuda")
+    st.set_activity(ctr, votes)
     o = torch.zeros((B, H, dk), dtype=torch.float32, device="cuda")
-    expect = np.zeros((B, H, 4), np.int64)
+    expect = np.zeros((B, H, 8), np.int64)
     slack = np.zeros((B, H), np.int64)
+    vote_bad = 0
     step = 2.0 ** -3
     for t in range(T):
         torch.cuda.synchronize()
         regs = st.regions().cpu().numpy()
         res = st.residuals()
         e_in = res.cpu().numpy() if res is not None else None
+        v_in = votes.cpu().numpy()
         st.step_decode(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, t)
+        torch.cuda.synchronize()
+        v_out = votes.cpu().numpy()
         for b in range(B):
             for h in range(H):
                 reg_in = regs[b * H + h][: lay.region_size()]
                 r = decode_step(lay, reg_in, None if e_in is None else e_in[b, h], inp["q"][t, b, h],
                                 inp["k"][t, b, h], inp["v"][t, b, h], inp["beta"][t, b, h], inp["s"][b, h],
-                                t, b, h)
+                                t, b, h, votes_in=v_in[b, h])
                 expect[b, h] += r.wb.activity
                 kp = L.decode_region(lay, reg_in).kappa
                 ad = np.abs(r.wb.X - kp * step) / step
                 near = (np.abs(ad - 0.5) <= WINDOW) | (np.abs(ad - 0.125) <= WINDOW) | (r.wb.boundary <= WINDOW)
                 slack[b, h] += int(near.sum())
+                vote_bad += int(((v_out[b, h] != r.wb.votes_new) & ~near).sum())
     st.set_activity(None)
     torch.cuda.synchronize()
     got = ctr.cpu().numpy().astype(np.int64)
     print("[activity] gpu", got.sum(axis=(0, 1)).tolist(), "oracle", expect.sum(axis=(0, 1)).tolist(),
-          "near-boundary elements", int(slack.sum()), flush=True)
+          "near-boundary elements", int(slack.sum()), "vote-state mismatches", vote_bad, flush=True)
+    assert vote_bad == 0
     assert np.all(np.abs(got - expect) <= slack[..., None]), (got, expect, slack)
     assert expect[..., 0].sum() > 0 and expect[..., 2].sum() > 0
+    assert expect[..., 5].sum() > 0 and expect[..., 6].sum() > 0 and 0 < expect[..., 7].sum() < expect[..., 2].sum()
     if mode == "dir":
-        assert expect[..., 3].sum() > 0
+        assert expect[..., 3].sum() > 0 and expect[..., 4].sum() > 0
     else:
         assert got[..., 3].sum() == 0
 
