@@ -8,7 +8,10 @@ the rule "mean budget plus half log2 of cost over its geometric mean"):
 
   R_i     row absolute maximum of the currently stored (dequantized) state;
   R~_i    R_i / RMS_j R_j over the normalisation group (one head for KDA);
-  Gamma_i 1 / expm1(2 (s_i + r_i))   (rho_i = 1, C = 1);
+  Gamma_i the persistence factor: 1 / [C expm1(2 (s_i + r_i))] (rho_i = 1) by default,
+          or DAMP's uncapped 1 / (1 - a_i^2), or 1 / (1 - e^{-2 C s_i})
+          ([LBRS] "Choice of persistence factor"); with no decay estimate (online
+          estimators that have seen no token) every row gets the same factor;
   c_i     Gamma_i * R~_i^2;
   b*_i    bbar + 0.5 * log2(c_i / GM(c))  -- the real-valued minimiser of
           sum_i c_i 2^{-2 b_i} at mean bbar (the displayed equation is missing from
@@ -23,8 +26,9 @@ the rule "mean budget plus half log2 of cost over its geometric mean"):
           wins, ties to the larger f ("fit f over 16 values in [1/4, 1] by squared
           error per scale group").
 
-Guards (the pages are silent): every b_i = bbar when all R_i = 0; c_i is floored at
-1e-300 before logarithms; Delta_k = 0 stores level 0.
+Guards (the pages are silent): every b_i = bbar when all R_i = 0; c_i is kept in
+[1e-300, 1e300] before logarithms (an infinite factor, s + r = 0, is the cap);
+Delta_k = 0 stores level 0.
 """
 from __future__ import annotations
 
@@ -32,9 +36,10 @@ import numpy as np
 
 from .numerics import f16, rne
 from .quantizers import fit_fraction, levels_n
-from .recurrence import erasure_rate_approx
+from .recurrence import GAMMA_ERASURE, persistence_factor
 
 C_FLOOR = 1e-300
+C_CAP = 1e300
 
 
 def proxy_cost(c, b):
@@ -63,14 +68,19 @@ def integer_widths(c, bstar, bbar: int, bmin: int, bmax: int):
     return b
 
 
-def row_costs(Y, s_rows, r_rows):
-    """(R, R~, Gamma-hat, c) of one head from its stored values Y [dk][dv]."""
+def row_costs(Y, s_rows, r_rows, factor=GAMMA_ERASURE, C=1):
+    """(R, R~, Gamma-hat, c) of one head from its stored values Y [dk][dv]; s_rows None
+    means no decay estimate (Gamma = 1 for every row)."""
     Y = np.asarray(Y, dtype=np.float64)
     R = np.max(np.abs(Y), axis=1)
     rms = np.sqrt(np.mean(R ** 2))
     Rt = R / rms if rms > 0 else np.zeros_like(R)
-    G = erasure_rate_approx(s_rows, r_rows)
-    return R, Rt, G, G * Rt ** 2
+    if s_rows is None:
+        G = np.ones_like(R)
+    else:
+        with np.errstate(divide="ignore"):
+            G = persistence_factor(s_rows, r_rows, factor, C)
+    return R, Rt, G, np.minimum(G * Rt ** 2, C_CAP)
 
 
 def fit_row(x, R: float, b: int):
@@ -92,11 +102,11 @@ def fit_row(x, R: float, b: int):
     return best, errs
 
 
-def allocate_head(Y, s_rows, r_rows, bbar=4, bmin=2, bmax=8):
+def allocate_head(Y, s_rows, r_rows, bbar=4, bmin=2, bmax=8, factor=GAMMA_ERASURE, C=1):
     """Widths, fit indices and diagnostics for one head's stored values Y."""
     Y = np.asarray(Y, dtype=np.float64)
     dk = Y.shape[0]
-    R, Rt, G, c = row_costs(Y, s_rows, r_rows)
+    R, Rt, G, c = row_costs(Y, s_rows, r_rows, factor, C)
     if np.all(R == 0):
         bstar = np.full(dk, float(bbar))
         b = np.full(dk, bbar, dtype=np.int64)

@@ -83,6 +83,27 @@ def erasure_rate_approx(s, r, rho=1.0, C=1):
     return np.asarray(rho, dtype=np.float64) / (C * np.expm1(2.0 * (s + r)))
 
 
+GAMMA_ERASURE, GAMMA_W1, GAMMA_HC = "erasure", "w1", "hC"
+
+
+def persistence_factor(s, r, kind: str = GAMMA_ERASURE, C: int = 1):
+    """The persistence factor of each row that weights its range in the allocation
+    ([LBRS] "Approximate erasure rate", "Choice of persistence factor", "Related work"):
+      erasure  rho / [C expm1(2 (s + r))]  with rho = 1 (the default);
+      w1       1 / (1 - a^2), a = e^{-s}: DAMP's factor, uncapped;
+      hC       1 / (1 - e^{-2 C s}): the write-back-time factor.
+    w1 and hC do not use r."""
+    s = np.asarray(s, dtype=np.float64)
+    if kind == GAMMA_ERASURE:
+        return erasure_rate_approx(s, r, 1.0, C)
+    a = np.exp(-s)
+    if kind == GAMMA_W1:
+        return 1.0 / (1.0 - a ** 2)
+    if kind == GAMMA_HC:
+        return 1.0 / (1.0 - np.exp(-2.0 * C * s))
+    raise ValueError(kind)
+
+
 def erasure_r(betas, ks):
     """r_i = E[beta (2 - beta) k_i^2] / 2 as a sample mean over a stream of tokens."""
     betas = np.asarray(betas, dtype=np.float64)

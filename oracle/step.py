@@ -201,12 +201,12 @@ def import_state(lay: L.Layout, S, region_prev, perm=None, b=0, h=0) -> np.ndarr
     return write_back(rtn, X, None, 0, b, h, prev=content).region
 
 
-def allocate_region(lay: L.Layout, region, s_rows, r_rows):
+def allocate_region(lay: L.Layout, region, s_rows, r_rows, factor="erasure", C=1):
     """The allocation pass on one BITALLOC head: new widths and fit indices from the
     stored state, then the stored values re-rounded (nearest) at the new widths."""
     content = L.decode_region(lay, region)
     Y = L.stored_values(lay, content)
-    alloc = allocate_head(Y, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax)
+    alloc = allocate_head(Y, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C)
     widths, fits = alloc["widths"], alloc["fit"]
     delta = np.zeros(lay.dk)
     kappa = np.zeros_like(content.kappa)
