@@ -108,6 +108,12 @@ extern "C" {
 #define WB_DECAY_PER_HEAD 0
 #define WB_DECAY_PER_ROW 1
 
+/* persistence factor Gamma_i of the bit allocation ([LBRS] "Approximate erasure rate",
+ * "Choice of persistence factor", "Related work") */
+#define WB_GAMMA_ERASURE 0  /* 1 / (C expm1(2 (s_i + r_i))), the approximate erasure rate */
+#define WB_GAMMA_W1 1       /* 1 / (1 - a_i^2), a_i = e^{-s_i}: DAMP's factor, uncapped */
+#define WB_GAMMA_HC 2       /* 1 / (1 - e^{-2 C s_i}): the write-back-time factor */
+
 typedef struct wb_layout_desc {
     int32_t kind;    /* WB_FP32 .. WB_BITALLOC */
     int32_t mode;    /* WB_RTN, WB_SR, WB_EF, WB_DIR, WB_RESQ */
@@ -184,15 +190,29 @@ int state_prefill_chunk(wb_state* st, const uint16_t* q_bf16, const uint16_t* k_
  * write-backs neither count nor update it. */
 int state_set_activity(wb_state* st, uint32_t* dev_counters, uint8_t* dev_votes);
 
+/* BITALLOC only: online estimators of the decay and erasure terms ([LBRS] "State bit
+ * allocation"). `dev_est` (float32 [B*H][2 dk + 4], 16-byte aligned, caller-owned,
+ * zeroed by the caller at the start of a sequence; NULL detaches) holds per head the
+ * unnormalised span-64 exponential averages (alpha = 2/65 per token) N_a[dk] of
+ * 1 - e^{-2 s_i} and N_r[dk] of beta (2 - beta) k_i^2, then their weight sum W (and
+ * three unused floats). Every following decode step folds its token in:
+ * N <- (1 - alpha) N + alpha x, W <- (1 - alpha) W + alpha. The estimates are
+ * s_i = -1/2 log1p(-N_a / W) and r_i = N_r / (2 W). */
+int state_set_estimators(wb_state* st, float* dev_est);
+
 /* BITALLOC only: recompute per-row widths and clipping-fit indices from the stored
  * state and repack it in place ([LBRS] "Approximate erasure rate", "Range
- * normalization", "State bit allocation", "Levels and storage"; [LBRS-x]):
- * R_i = row max |S|, R~_i = R_i / RMS_j R_j, Gamma_i = 1/expm1(2 (s_i + r_i)),
- * c_i = Gamma_i R~_i^2, b_i = bbar + 0.5 log2(c_i / geomean(c)) rounded (ties even),
+ * normalization", "State bit allocation", "Choice of persistence factor", "Levels and
+ * storage"; [LBRS-x]): R_i = row max |S|, R~_i = R_i / RMS_j R_j, Gamma_i the
+ * persistence factor `factor` (WB_GAMMA_*) at cadence C >= 1, c_i = Gamma_i R~_i^2 kept
+ * in [1e-300, 1e300], b_i = bbar + 0.5 log2(c_i / geomean(c)) rounded (ties even),
  * clipped to [bmin, bmax], adjusted greedily to sum = bbar*dk; f fitted over
  * 1/4 + k/20 by squared error. s, r: float32 [B][H][dk]; r may be NULL for
- * r_i = 1/(3 dk) (E[beta(2-beta)] = 2/3, E[k_i^2] = 1/dk for the synthetic stream). */
-int state_allocate_bits(wb_state* st, const float* s, const float* r, void* stream);
+ * r_i = 1/(3 dk) (E[beta(2-beta)] = 2/3, E[k_i^2] = 1/dk for the synthetic stream).
+ * s NULL (then r must be NULL): s_i and r_i from the attached estimators; a head whose
+ * estimators have seen no token (W = 0) gives every row Gamma = 1. EINVAL for a bad
+ * factor, C < 1, or s NULL without estimators. */
+int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor, int C, void* stream);
 
 /* Export: the stored state dequantized to float32 S [B][H][dk][dv] in the original
  * domain and logical row order (Hadamard rows rotated back, rows un-permuted). */

@@ -20,6 +20,7 @@ FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC = 0, 1, 2, 3, 4
 KIND_NAMES = {"fp32": FP32, "uniform": UNIFORM, "had_int8": HAD_INT8, "mixed": MIXED, "bitalloc": BITALLOC}
 RTN, SR, EF, DIR, RESQ = 0, 1, 2, 3, 4
 MODE_NAMES = {"rtn": RTN, "sr": SR, "ef": EF, "dir": DIR, "resq": RESQ}
+GAMMA_CODES = {"erasure": 0, "w1": 1, "hC": 2}
 DECAY_PER_HEAD, DECAY_PER_ROW = 0, 1
 
 STATUS = {0: "ok", -1: "EINVAL", -2: "ESIZE", -3: "EUNSUPPORTED", -4: "ELAUNCH", -5: "EALIGN"}
@@ -45,7 +46,8 @@ SIGNATURES = {
     "state_free": (_I, [_P]),
     "state_step_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _U64, _P]),
     "state_prefill_chunk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _U64, _P]),
-    "state_allocate_bits": (_I, [_P, _P, _P, _P]),
+    "state_allocate_bits": (_I, [_P, _P, _P, _I, _I, _P]),
+    "state_set_estimators": (_I, [_P, _P]),
     "state_dequant": (_I, [_P, _P, _P]),
     "state_quantize": (_I, [_P, _P, _P]),
     "state_export": (_I, [_P, ctypes.POINTER(_P), ctypes.POINTER(_SZ), ctypes.POINTER(_P)]),
@@ -166,13 +168,23 @@ class WriteBackState:
             _ptr(s, torch.float32, s_shape, "s"), _ptr(o, torch.float32, (B, T, H, dv), "o"),
             T, chunk, C, _U64(t0), _stream(stream)), "state_prefill_chunk")
 
-    def allocate_bits(self, s, r=None, stream=None):
+    def allocate_bits(self, s=None, r=None, factor="erasure", C=1, stream=None):
+        """Allocation pass (BITALLOC). ``s``, ``r``: float32 [B, H, dk]; ``s`` None takes
+        s and r from the attached estimators. ``factor``: "erasure", "w1" or "hC"."""
         import torch
         shape = (self.B, self.H, self.dk)
         check(lib().state_allocate_bits(
-            self.handle, _ptr(s, torch.float32, shape, "s"),
-            None if r is None else _ptr(r, torch.float32, shape, "r"), _stream(stream)),
-            "state_allocate_bits")
+            self.handle, None if s is None else _ptr(s, torch.float32, shape, "s"),
+            None if r is None else _ptr(r, torch.float32, shape, "r"), GAMMA_CODES[factor], int(C),
+            _stream(stream)), "state_allocate_bits")
+
+    def set_estimators(self, est=None):
+        """Attach (or with None detach) the online estimators: float32 [B, H, 2 dk + 4],
+        zeroed by the caller at a sequence start; later decode steps fold their token in."""
+        import torch
+        p = None if est is None else _ptr(est, torch.float32, (self.B, self.H, 2 * self.dk + 4), "est")
+        self._est = est
+        check(lib().state_set_estimators(self.handle, p), "state_set_estimators")
 
     def dequant(self, S, stream=None):
         import torch

@@ -3,7 +3,11 @@
 // [LBRS] "Approximate erasure rate", "Range normalization", "State bit allocation",
 // "Levels and storage"; [LBRS-x] (cost c = Gamma-hat * R~^2 and the width rule):
 //   R_i   = max_j |S_ij| of the stored state;  R~_i = R_i / RMS_j R_j (one head);
-//   Gamma = 1 / expm1(2 (s_i + r_i));  c_i = max(Gamma R~_i^2, 1e-300);
+//   Gamma = the persistence factor ([LBRS] "Choice of persistence factor"): by default
+//   1 / (C expm1(2 (s_i + r_i))), else 1 / (1 - e^{-2 s_i}) (DAMP's, uncapped) or
+//   1 / (1 - e^{-2 C s_i}); s_i, r_i given, or from the online estimators
+//   (s = -1/2 log1p(-N_a / W), r = N_r / (2 W); W = 0: Gamma = 1 for every row);
+//   c_i = Gamma R~_i^2 kept in [1e-300, 1e300];
 //   b*_i  = bbar + 0.5 log2(c_i / GM(c));  b_i = clip(rint(b*_i), bmin, bmax), then one
 //   bit at a time: while short, +1 to the largest (3/4) c 2^{-2b} among b < bmax; while
 //   over, -1 to the smallest 3 c 2^{-2b} among b > bmin; ties to the lower row;
@@ -63,6 +67,13 @@ struct AllocSmem {
     int newfit[DK];
     uint16_t newdelta[DK];
 };
+
+// persistence factor of one row (WB_GAMMA_*); an infinite value is capped by the caller
+__device__ __forceinline__ double persistence(int factor, int C, double s, double r) {
+    if (factor == WB_GAMMA_W1) return 1.0 / -expm1(-2.0 * s);
+    if (factor == WB_GAMMA_HC) return 1.0 / -expm1(-2.0 * double(C) * s);
+    return 1.0 / (double(C) * expm1(2.0 * (s + r)));
+}
 
 // sum over the 16 lanes of a DPP row (the 16 column groups of one state row)
 __device__ __forceinline__ float row16_sum(float v) {
@@ -243,14 +254,27 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         if (sq > 0.0) {
             const double rms = sqrt(sq / double(DK));
             const size_t base = (size_t)head * DK;
-            const double s0 = A.s[base + r0], s1 = A.s[base + r1];
-            const double q0 = A.r ? double(A.r[base + r0]) : double(A.r_default);
-            const double q1 = A.r ? double(A.r[base + r1]) : double(A.r_default);
-            const double g0 = 1.0 / expm1(2.0 * (s0 + q0));
-            const double g1 = 1.0 / expm1(2.0 * (s1 + q1));
+            double s0, s1, q0, q1;
+            bool flat = false;
+            if (A.s) {
+                s0 = A.s[base + r0];
+                s1 = A.s[base + r1];
+                q0 = A.r ? double(A.r[base + r0]) : double(A.r_default);
+                q1 = A.r ? double(A.r[base + r1]) : double(A.r_default);
+            } else {
+                const float* e = A.est + (size_t)head * est_stride(DK);
+                const double W = e[2 * DK];
+                flat = !(W > 0.0);
+                s0 = -0.5 * log1p(-double(e[r0]) / W);
+                s1 = -0.5 * log1p(-double(e[r1]) / W);
+                q0 = 0.5 * double(e[DK + r0]) / W;
+                q1 = 0.5 * double(e[DK + r1]) / W;
+            }
+            const double g0 = flat ? 1.0 : persistence(A.factor, A.cadence, s0, q0);
+            const double g1 = flat ? 1.0 : persistence(A.factor, A.cadence, s1, q1);
             const double rt0 = R0 / rms, rt1 = R1 / rms;
-            c0 = fmax(g0 * (rt0 * rt0), 1e-300);
-            c1 = fmax(g1 * (rt1 * rt1), 1e-300);
+            c0 = fmin(fmax(g0 * (rt0 * rt0), 1e-300), 1e300);
+            c1 = fmin(fmax(g1 * (rt1 * rt1), 1e-300), 1e300);
             const double lsum = wave_sum_f64<1>(log(c0) + log(c1));
             const double gm = exp(lsum / double(DK));
             const double bs0 = double(A.bbar) + 0.5 * log2(c0 / gm);

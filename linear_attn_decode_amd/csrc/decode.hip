@@ -144,6 +144,8 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             sm.q[i] = Real(A.q[(size_t)head * DK + lr]);
             const float sv = A.s_per_row ? A.s[(size_t)head * DK + lr] : A.s[head];
             sm.a[i] = rexp<Real>(-Real(sv));
+            if (KIND == WB_BITALLOC && A.est)
+                ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, i, sv, A.beta[head], A.k[(size_t)head * DK + i]);
         }
     }
 

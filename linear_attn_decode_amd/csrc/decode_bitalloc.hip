@@ -289,6 +289,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         const size_t rb = (size_t)head * DK + trow;
         const float kr = A.k[rb], qr = A.q[rb];
         const float sr = A.s_per_row ? A.s[rb] : A.s[head];
+        if (A.est) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, trow, sr, beta, kr);
         const uint32_t dold = reinterpret_cast<const uint16_t*>(region + code_bytes)[trow];
         const int bw0 = (meta0 & 7) + 1, bw1 = (meta1 & 7) + 1;
         const bool hi_half = wave == 1;

@@ -122,6 +122,22 @@ __device__ __forceinline__ int round_rule(Real x, Real e, Real step, Real offset
     return int(kf);
 }
 
+// ---------------------------------------------------------------------------
+// Online decay / erasure estimators of one head ([LBRS] "State bit allocation"):
+// exponential averages of span 64 (alpha = 2/65 per token) kept unnormalised, as
+// [N_a: dk][N_r: dk][W, pad x3] floats: N_a averages 1 - e^{-2 s_i}, N_r averages
+// beta (2 - beta) k_i^2, W is the weight sum. One call folds one token into one row
+// (and, for row 0, into W).
+constexpr float kEmaAlpha = 2.0f / 65.0f, kEmaKeep = 63.0f / 65.0f;
+__device__ __forceinline__ int est_stride(int dk) { return 2 * dk + 4; }
+__device__ __forceinline__ void ema_fold_row(float* est, int dk, int row, float s, float beta, float k) {
+    const float xa = -expm1f(-2.0f * s);
+    const float xr = beta * (2.0f - beta) * (k * k);
+    est[row] = __builtin_fmaf(est[row], kEmaKeep, kEmaAlpha * xa);
+    est[dk + row] = __builtin_fmaf(est[dk + row], kEmaKeep, kEmaAlpha * xr);
+    if (row == 0) est[2 * dk] = __builtin_fmaf(est[2 * dk], kEmaKeep, kEmaAlpha);
+}
+
 // float64 DPP move inside rows of 16 lanes (both 32-bit halves)
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {

@@ -34,6 +34,7 @@ struct KArgs {
     int mem_bits = 0;                 // k of direction / residual memory
     uint32_t* activity = nullptr;     // [B*H][8] write-activity counters (UNIFORM) or null
     uint8_t* votes = nullptr;         // [B*H][DK][DV] vote state, with `activity`
+    float* est = nullptr;             // [B*H][2 DK + 4] online estimators (BITALLOC) or null
 };
 
 // One launch of the decode / import / export kernel for every head of the layout.
@@ -59,6 +60,9 @@ struct AllocArgs {
     uint8_t* state = nullptr;
     const float* s = nullptr;         // [B*H][dk]
     const float* r = nullptr;         // [B*H][dk] or null
+    const float* est = nullptr;       // [B*H][2 dk + 4] online estimators, used when s is null
+    int factor = 0;                   // WB_GAMMA_*
+    int cadence = 1;                  // C of the persistence factor
     uint64_t region_stride = 0;
     float r_default = 0.f;
     int bbar = 4, bmin = 2, bmax = 8;

@@ -21,6 +21,7 @@ struct wb_state {
     uint8_t* perm_dev;     // inside the state buffer (MIXED), else null
     uint32_t* activity;    // caller's write-activity counters (UNIFORM), or null
     uint8_t* votes;        // caller's per-element vote state, set with `activity`
+    float* est;            // caller's online estimators (BITALLOC), or null
 };
 
 namespace {
@@ -153,6 +154,7 @@ int state_alloc(const wb_layout_desc* d, void* dev_state, size_t state_bytes_in,
     st->perm_dev = d->kind == WB_MIXED ? st->state + st->regions_bytes : nullptr;
     st->activity = nullptr;
     st->votes = nullptr;
+    st->est = nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // zero state: all layouts but BITALLOC encode S_0 = 0 as zero bytes
@@ -206,6 +208,7 @@ int state_step_decode(wb_state* st, const float* q, const float* k, const float*
     a.t = t;
     a.activity = st->activity;
     a.votes = st->votes;
+    a.est = st->est;
     return hip_status(wb::launch_wb(st->d, wb::OP_STEP, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -235,14 +238,27 @@ int state_quantize(wb_state* st, const float* S, void* stream) {
     return hip_status(wb::launch_wb(st->d, wb::OP_IMPORT, a, static_cast<hipStream_t>(stream)));
 }
 
-int state_allocate_bits(wb_state* st, const float* s, const float* r, void* stream) {
-    if (!st || !s) return WB_EINVAL;
+int state_set_estimators(wb_state* st, float* dev_est) {
+    if (!st) return WB_EINVAL;
     if (st->d.kind != WB_BITALLOC) return WB_EUNSUPPORTED;
-    if (!aligned4(s) || (r && !aligned4(r))) return WB_EALIGN;
+    if (dev_est && !aligned16(dev_est)) return WB_EALIGN;
+    st->est = dev_est;
+    return WB_OK;
+}
+
+int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor, int C, void* stream) {
+    if (!st) return WB_EINVAL;
+    if (st->d.kind != WB_BITALLOC) return WB_EUNSUPPORTED;
+    if (factor < WB_GAMMA_ERASURE || factor > WB_GAMMA_HC || C < 1) return WB_EINVAL;
+    if (!s && (r || !st->est)) return WB_EINVAL;
+    if ((s && !aligned4(s)) || (r && !aligned4(r))) return WB_EALIGN;
     wb::AllocArgs a;
     a.state = st->state;
     a.s = s;
     a.r = r;
+    a.est = s ? nullptr : st->est;
+    a.factor = factor;
+    a.cadence = C;
     a.region_stride = st->region_stride;
     a.r_default = float(1.0 / (3.0 * st->d.dk));
     a.bbar = st->d.bbar;

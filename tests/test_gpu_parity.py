@@ -343,6 +343,26 @@ def _alloc_case(case, rng, B, H, dk):
     return S, s
 
 
+def _check_alloc_head(lay, reg_gpu, reg_orc, alloc, tag):
+    """Widths equal except near-ties of the real widths; then fit indices equal except
+    near-equal fit errors; then the repacked bytes equal."""
+    g = L.decode_region(lay, reg_gpu)
+    o = L.decode_region(lay, reg_orc)
+    assert g.widths.sum() == lay.bbar * lay.dk, tag
+    if not np.array_equal(g.widths, o.widths):
+        bad = np.argwhere(g.widths != o.widths).ravel()
+        frac = np.abs(alloc["bstar"][bad] - np.floor(alloc["bstar"][bad]) - 0.5)
+        assert np.all(frac < 1e-5), (tag, bad, alloc["bstar"][bad])
+        return
+    if not np.array_equal(g.fit, o.fit):
+        bad = np.argwhere(g.fit != o.fit).ravel()
+        for i in bad:
+            e = alloc["fit_err"][i]
+            assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (tag, i)
+        return
+    assert np.array_equal(reg_gpu, reg_orc), tag
+
+
 @pytest.mark.parametrize("case", ["warm", "groups", "spread"])
 def test_allocate_bits_matches_oracle(case):
     """Two allocation passes per head: the first from the imported state (every row at
@@ -372,28 +392,93 @@ def test_allocate_bits_matches_oracle(case):
                                                  r[b, h].astype(np.float64))
                 if pas == 1:
                     wide_rows += int((L.decode_region(lay, reg_in).widths >= 6).sum())
-                g = L.decode_region(lay, reg_gpu)
-                o = L.decode_region(lay, reg_orc)
-                assert g.widths.sum() == 512
-                moved += int(np.abs(np.clip(np.rint(alloc["bstar"]), lay.bmin, lay.bmax) - o.widths).sum())
-                if not np.array_equal(g.widths, o.widths):
-                    # only near-ties of the real widths may differ
-                    bad = np.argwhere(g.widths != o.widths).ravel()
-                    frac = np.abs(alloc["bstar"][bad] - np.floor(alloc["bstar"][bad]) - 0.5)
-                    assert np.all(frac < 1e-5), (pas, b, h, bad, alloc["bstar"][bad])
-                    continue
-                if not np.array_equal(g.fit, o.fit):
-                    bad = np.argwhere(g.fit != o.fit).ravel()
-                    for i in bad:
-                        e = alloc["fit_err"][i]
-                        assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (pas, b, h, i)
-                    continue
-                assert np.array_equal(reg_gpu, reg_orc), (pas, b, h)
+                moved += int(np.abs(np.clip(np.rint(alloc["bstar"]), lay.bmin, lay.bmax)
+                                    - L.decode_region(lay, reg_orc).widths).sum())
+                _check_alloc_head(lay, reg_gpu, reg_orc, alloc, (pas, b, h))
     print(f"[alloc] one-bit moves over the heads: {moved}; rows stored with 6+ bits before the second pass: "
           f"{wide_rows}", flush=True)
     if case != "warm":
         assert moved >= 50 * B * H
     assert wide_rows > 0
+
+
+@pytest.mark.parametrize("mode,per_row", [("rtn", True), ("sr", True), ("rtn", False)])
+def test_online_estimators_and_allocation_from_them(mode, per_row):
+    """Span-64 estimators folded in by every decode step (a decay stream that varies per
+    token) against the oracle's recursion; then allocation passes that take s and r
+    from them under each persistence factor, against the oracle fed the GPU's
+    estimator values; a head whose estimators saw no token allocates by range alone."""
+    from oracle.estimators import ema_estimates, ema_fold, ema_init
+    print(f"\n[case] online estimators BITALLOC {mode} per_row={per_row}", flush=True)
+    B, H, dk, T = 2, 3, 128, 40
+    lay = _layout(L.BITALLOC, mode, B, H, dk, per_row=per_row)
+    rng = np.random.default_rng(52)
+    st = _state(lay)
+    inp = decode_inputs(52, B, H, dk, dk, T, per_row)
+    dev = {key: _to_dev(val) for key, val in inp.items()}
+    st.quantize(_to_dev(_warm_state(rng, B, H, dk, dk)))
+    o = torch.zeros((B, H, dk), dtype=torch.float32, device="cuda")
+    # the state never saw a token: every row gets the same factor
+    est = torch.zeros((B, H, 2 * dk + 4), dtype=torch.float32, device="cuda")
+    st.set_estimators(est)
+    before = st.regions().cpu().numpy()
+    st.allocate_bits(None)
+    torch.cuda.synchronize()
+    after = st.regions().cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            reg_in = before[b * H + h][: lay.region_size()]
+            reg_orc, alloc = allocate_region(lay, reg_in, None, None)
+            _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, ("flat", b, h))
+    jit = np.exp(0.4 * rng.standard_normal((T,) + inp["s"].shape)).astype(np.float32)
+    s_t = (inp["s"][None] * jit).astype(np.float32)
+    orc = {(b, h): ema_init(dk) for b in range(B) for h in range(H)}
+    for t in range(T):
+        st.step_decode(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], _to_dev(s_t[t]), o, t)
+        for b in range(B):
+            for h in range(H):
+                srow = s_t[t, b, h] if per_row else np.full(dk, s_t[t, b, h])
+                orc[(b, h)] = ema_fold(orc[(b, h)], srow.astype(np.float64), float(inp["beta"][t, b, h]),
+                                       inp["k"][t, b, h].astype(np.float64))
+    torch.cuda.synchronize()
+    e = est.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            ob = orc[(b, h)]
+            for got, want in ((e[b, h, :dk], ob.Na), (e[b, h, dk:2 * dk], ob.Nr), (e[b, h, 2 * dk], ob.W)):
+                err = np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-30))
+                worst = max(worst, float(err))
+    print(f"[est] worst relative error of the estimators after {T} tokens: {worst:.2e}", flush=True)
+    assert worst < 2e-5
+    st.set_estimators(None)
+    st.set_estimators(est)
+    for factor, C in (("erasure", 1), ("w1", 1), ("hC", 64), ("hC", 4)):
+        torch.cuda.synchronize()
+        before = st.regions().cpu().numpy()
+        st.allocate_bits(None, factor=factor, C=C)
+        torch.cuda.synchronize()
+        after = st.regions().cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                sh, r = ema_estimates(e[b, h, :dk], e[b, h, dk:2 * dk], float(e[b, h, 2 * dk]))
+                reg_in = before[b * H + h][: lay.region_size()]
+                reg_orc, alloc = allocate_region(lay, reg_in, sh, r, factor, C)
+                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h))
+    # explicit decays with the alternative factors
+    s_np = inp["s"] if per_row else np.repeat(inp["s"][..., None], dk, axis=-1).astype(np.float32)
+    for factor, C in (("w1", 1), ("hC", 16)):
+        torch.cuda.synchronize()
+        before = st.regions().cpu().numpy()
+        st.allocate_bits(_to_dev(np.ascontiguousarray(s_np[..., ::-1])), factor=factor, C=C)
+        torch.cuda.synchronize()
+        after = st.regions().cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                reg_in = before[b * H + h][: lay.region_size()]
+                reg_orc, alloc = allocate_region(lay, reg_in, s_np[b, h, ::-1].astype(np.float64),
+                                                 np.full(dk, 1.0 / (3 * dk)), factor, C)
+                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h))
 
 
 def test_allocation_then_decode_full_budget_zero_state():
