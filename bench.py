@@ -30,6 +30,10 @@ PEAK_HBM_GBS = 8000.0
 WORKLOADS = {
     "kda-bitalloc": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
                          extra=dict(bbar=4, bmin=2, bmax=8), kernel="bitalloc_step_kernel"),
+    # the same, with the span-64 decay / erasure estimators folded in by every decode
+    # step and the allocation passes taking s and r from them
+    "kda-bitalloc-online": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
+                                extra=dict(bbar=4, bmin=2, bmax=8), kernel="bitalloc_step_kernel", online=True),
     "kda-mixed": dict(cfg=2, kind="mixed", B=256, H=32, per_row=True, layers=7, alloc_every=0,
                       extra=dict(block=32, k_hi=16), kernel="rot_step_kernel"),
     "gdn-had-int8": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
@@ -74,10 +78,11 @@ def region_bytes(kind, extra):
     return code + 3 * dk, code + 2 * dk          # read: codes + Delta + meta; write: codes + Delta
 
 
-def algorithmic_bytes_per_head(kind, extra, per_row):
+def algorithmic_bytes_per_head(kind, extra, per_row, online=False):
     rd, wr = region_bytes(kind, extra)
     io = 2 * DK * 4 + DV * 4 + 4 + (DK * 4 if per_row else 4) + DV * 4
-    return rd + wr + io
+    est = 2 * (2 * DK * 4 + 4) if online else 0      # estimators read and written
+    return rd + wr + io + est
 
 
 def load_traffic(workload):
@@ -132,6 +137,12 @@ def run_gpu(args, w):
     if w["kind"] == "bitalloc":
         for st in states:
             st.allocate_bits(s_alloc)
+    ests = []
+    if w.get("online"):
+        for st in states:
+            ests.append(torch.zeros((B, H, 2 * DK + 4), dtype=torch.float32, device="cuda"))
+            st.set_estimators(ests[-1])
+        s_alloc = None                                # allocation from the estimators
     torch.cuda.synchronize()
     counts = [0] * len(states)
     alloc_every = w["alloc_every"]
@@ -244,6 +255,7 @@ def cpu_baseline(w, gpu, budget_s):
     except ImportError:
         threadpool_limits = None
     from oracle import layouts as L
+    from oracle.estimators import ema_fold, ema_init
     from oracle.step import decode_step
 
     st = gpu["states"][0]
@@ -271,6 +283,8 @@ def cpu_baseline(w, gpu, budget_s):
             reg = regs[idx].cpu().numpy()[: lay.region_size()]
             decode_step(lay, reg, None, q[b, h], k[b, h], v[b, h], beta[b, h], s[b, h], 0, b, h,
                         None if perm is None else perm[h])
+            if w.get("online"):
+                ema_fold(ema_init(DK), s[b, h], float(beta[b, h]), k[b, h])
             n += 1
             if time.perf_counter() - t0 >= budget_s and n >= 4:
                 break
@@ -336,7 +350,7 @@ def main():
     tokens = B * K
     dec = sorted(gpu["decode_ms"])
     avg_dec_ms = sum(dec) / len(dec)
-    bytes_launch = algorithmic_bytes_per_head(w["kind"], w["extra"], w["per_row"]) * B * H
+    bytes_launch = algorithmic_bytes_per_head(w["kind"], w["extra"], w["per_row"], w.get("online", False)) * B * H
     achieved = bytes_launch / (avg_dec_ms / 1e3) / 1e9
     traffic = load_traffic(args.workload)
     out = {
@@ -355,7 +369,9 @@ def main():
         "config": {"workload": f"{args.workload}: decode write-back, {w['kind']} layout, B={B}, H={H}, "
                                f"dk=dv=128, {'per-row' if w['per_row'] else 'per-head'} decay, RTN, "
                                f"{w['layers']} layer states cycled"
-                               + (f", allocation pass every {w['alloc_every']} tokens per layer" if w["alloc_every"] else ""),
+                               + (f", allocation pass every {w['alloc_every']} tokens per layer" if w["alloc_every"] else "")
+                               + (", span-64 decay/erasure estimators folded in every step, allocation from them"
+                                  if w.get("online") else ""),
                    "global_batch": B, "heads": H, "layers_cycled": w["layers"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
