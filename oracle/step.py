@@ -206,10 +206,27 @@ def allocate_region(lay: L.Layout, region, s_rows, r_rows, factor="erasure", C=1
     stored state, then the stored values re-rounded (nearest) at the new widths."""
     content = L.decode_region(lay, region)
     Y = L.stored_values(lay, content)
+    return _allocate_and_round(lay, Y, s_rows, r_rows, factor, C)
+
+
+def decode_step_alloc(lay: L.Layout, region, q, k, v, beta, s, s_rows, r_rows, factor="erasure", C=1):
+    """One decode token for a BITALLOC head whose write-back allocates ([LBRS] "State
+    bit allocation": widths are chosen at each write-back): the step from the stored
+    state, then widths, fits and Delta chosen for the updated state itself and the
+    state rounded once (nearest) onto that grid. ``s_rows`` / ``r_rows`` feed the
+    allocation (None: no decay estimate). Returns (region, alloc, o, S_new)."""
+    content = L.decode_region(lay, region)
+    Y = L.stored_values(lay, content)
+    S_new, o = delta_step(Y, q, k, v, beta, s)
+    reg, alloc = _allocate_and_round(lay, S_new, s_rows, r_rows, factor, C)
+    return reg, alloc, o, S_new
+
+
+def _allocate_and_round(lay: L.Layout, Y, s_rows, r_rows, factor, C):
     alloc = allocate_head(Y, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C)
     widths, fits = alloc["widths"], alloc["fit"]
     delta = np.zeros(lay.dk)
-    kappa = np.zeros_like(content.kappa)
+    kappa = np.zeros((lay.dk, lay.dv), np.int64)
     for i in range(lay.dk):
         delta[i], _ = row_step(alloc["R"][i], int(widths[i]), int(fits[i]))
         n = levels_n(int(widths[i]))

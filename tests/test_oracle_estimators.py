@@ -115,3 +115,39 @@ def test_infinite_factor_is_capped():
     s[3] = 0.0
     a = allocate_head(Y, s, 0.0)               # s + r = 0 on row 3: factor infinite
     assert np.all(np.isfinite(a["bstar"])) and a["widths"][3] == 8 and a["widths"].sum() == 128
+
+
+def test_step_with_allocation_reduces_to_its_parts():
+    """A token that changes nothing (beta = 0, s = 0) makes the allocating write-back the
+    allocation pass; any token's readout is the plain step's; the grid and codes are
+    the rounding of the updated state at the widths the allocation chose for it."""
+    from oracle import layouts as L
+    from oracle.quantizers import levels_n, sym_round
+    from oracle.step import allocate_region, decode_step, decode_step_alloc, import_state
+    rng = np.random.default_rng(8)
+    dk = dv = 32
+    lay = L.Layout(kind=L.BITALLOC, B=1, H=1, dk=dk, dv=dv, mode="rtn", per_row_decay=True, bbar=4, bmin=2, bmax=8)
+    S = rng.standard_normal((dk, dv)) * np.exp(rng.uniform(-3, 0.5, (dk, 1)))
+    s_rows = np.exp(rng.uniform(np.log(1e-3), 0.0, dk))
+    # a stored state with mixed widths: the zero state at the mean width, S imported
+    # into it, then one allocation pass
+    start = L.encode_region(lay, L.Content(kappa=np.zeros((dk, dv), np.int64), widths=np.full(dk, 4),
+                                           fit=np.zeros(dk, np.int64), delta_bits=np.zeros(dk, np.uint16)))
+    reg0, _ = allocate_region(lay, import_state(lay, S, start), s_rows, 0.01)
+    assert L.decode_region(lay, reg0).widths.max() > 4
+    k = rng.standard_normal(dk)
+    k /= np.linalg.norm(k)
+    q = rng.standard_normal(dk)
+    q /= np.linalg.norm(q)
+    v = rng.standard_normal(dv)
+    reg_a, alloc_a, o_a, _ = decode_step_alloc(lay, reg0, q, k, v, 0.0, np.zeros(dk), s_rows, 0.01, "w1")
+    reg_p, _ = allocate_region(lay, reg0, s_rows, 0.01, "w1")
+    assert np.array_equal(reg_a, reg_p)
+    reg_b, alloc_b, o_b, S_new = decode_step_alloc(lay, reg0, q, k, v, 0.7, s_rows, s_rows, 0.01)
+    ref = decode_step(lay, reg0, None, q, k, v, 0.7, s_rows, 0, 0, 0)
+    assert np.allclose(o_b, ref.o, rtol=1e-13, atol=1e-15) and np.allclose(S_new, ref.S_new, rtol=0, atol=0)
+    c = L.decode_region(lay, reg_b)
+    assert c.widths.sum() == 4 * dk and np.array_equal(c.widths, alloc_b["widths"])
+    for i in range(dk):
+        n = levels_n(int(c.widths[i]))
+        assert np.array_equal(c.kappa[i], sym_round(S_new[i], float(c.delta[i]), n, "rtn").kappa)
