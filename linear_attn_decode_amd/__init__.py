@@ -48,6 +48,7 @@ SIGNATURES = {
     "state_prefill_chunk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _U64, _P]),
     "state_allocate_bits": (_I, [_P, _P, _P, _I, _I, _P]),
     "state_set_estimators": (_I, [_P, _P]),
+    "state_step_decode_alloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
     "state_dequant": (_I, [_P, _P, _P]),
     "state_quantize": (_I, [_P, _P, _P]),
     "state_export": (_I, [_P, ctypes.POINTER(_P), ctypes.POINTER(_SZ), ctypes.POINTER(_P)]),
@@ -156,6 +157,18 @@ class WriteBackState:
             self.handle, _ptr(q, f, (B, H, dk), "q"), _ptr(k, f, (B, H, dk), "k"),
             _ptr(v, f, (B, H, dv), "v"), _ptr(beta, f, (B, H), "beta"), _ptr(s, f, s_shape, "s"),
             _ptr(o, f, (B, H, dv), "o"), _U64(t), _stream(stream)), "state_step_decode")
+
+    def step_decode_alloc(self, q, k, v, beta, s, o, factor="erasure", C=1, stream=None):
+        """One decode token whose write-back allocates widths for the updated state
+        (BITALLOC, RTN)."""
+        import torch
+        B, H, dk, dv = self.B, self.H, self.dk, self.dv
+        s_shape = (B, H, dk) if self.desc.decay == DECAY_PER_ROW else (B, H)
+        f = torch.float32
+        check(lib().state_step_decode_alloc(
+            self.handle, _ptr(q, f, (B, H, dk), "q"), _ptr(k, f, (B, H, dk), "k"),
+            _ptr(v, f, (B, H, dv), "v"), _ptr(beta, f, (B, H), "beta"), _ptr(s, f, s_shape, "s"),
+            _ptr(o, f, (B, H, dv), "o"), GAMMA_CODES[factor], int(C), _stream(stream)), "state_step_decode_alloc")
 
     def prefill(self, q, k, v, beta, s, o, T: int, chunk: int = 64, C: int = 8, t0: int = 0, stream=None):
         import torch

@@ -162,8 +162,20 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
 }
 
+// STEP = false: the allocation pass on the stored state. STEP = true: one decode token
+// whose write-back allocates: the stored state is dequantized, the delta-rule step
+// (u = k^T D S, w = beta (v - u), S' = D S + k w^T, o = S'^T q) runs in float32, the
+// token is folded into the estimators, and the widths, fits and codes are chosen
+// for S' (every row through the 16-candidate fit: S' is not on the old grid).
+template <bool STEP>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) allocate_kernel(const AllocArgs A) {
     __shared__ AllocSmem sm;
+    // decode-step scratch, in the candidate table (filled only after the step)
+    float* const fk = reinterpret_cast<float*>(&sm.cand[0][0]);
+    float* const fq = fk + DK;
+    float* const fa = fq + DK;
+    float* const red = fa + DK;                   // [4 wavefronts][DV]
+    static_assert(sizeof(sm.cand) >= sizeof(float) * (3 * DK + 4 * DV), "step scratch");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int head = blockIdx.x;
     const int cg = tid % NCG, rg = tid / NCG;
@@ -173,6 +185,16 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
 
     for (int i = tid; i * 16 < total; i += NT)
         reinterpret_cast<uint4*>(sm.reg)[i] = reinterpret_cast<const uint4*>(region)[i];
+    if constexpr (STEP) {
+        if (tid < DK) {
+            const size_t rb = (size_t)head * DK + tid;
+            const float sv = A.s_per_row ? A.sd[rb] : A.sd[head];
+            fk[tid] = A.k[rb];
+            fq[tid] = A.q[rb];
+            fa[tid] = expf(-sv);
+            if (A.est) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, tid, sv, A.beta[head], fk[tid]);
+        }
+    }
     __syncthreads();
     const uint8_t* bytes = reinterpret_cast<const uint8_t*>(sm.reg);
     if (wave == 0) {
@@ -227,19 +249,72 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         uint64_t fld = (uint64_t(sm.reg[wi]) | (uint64_t(sm.reg[wi + 1]) << 32)) >> sh;
         if (sh) fld |= uint64_t(sm.reg[wi + 2]) << (64 - sh);
         const float dl = sm.delta[row];
-        float R = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const int kap = int((fld >> (c * bw)) & ((1ull << bw) - 1)) - n;
             x[m][c] = float(kap) * dl;
-            R = fmaxf(R, fabsf(x[m][c]));
         }
-        // maximum over the row's 16 lanes (a DPP row; non-negative values)
+    }
+    if constexpr (STEP) {
+        // u_j = sum_i k_i a_i S_ij: this thread's 8 rows, then the 4 row groups of the
+        // wavefront (lanes 16 and 32 apart), then the 4 wavefronts through LDS
+        float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int row = sm.order[rg + RS * m];
+            const float ka = fk[row] * fa[row];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) u[c] = __builtin_fmaf(ka, x[m][c], u[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) u[c] = add_xor32_f32(add_xor16_f32(u[c]));
+        if (lane < 16) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) red[wave * DV + 8 * cg + c] = u[c];
+        }
+        __syncthreads();
+        const float beta = A.beta[head];
+        float w[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int col = 8 * cg + c;
+            const float uj = (red[col] + red[DV + col]) + (red[2 * DV + col] + red[3 * DV + col]);
+            w[c] = beta * (A.v[(size_t)head * DV + col] - uj);
+        }
+        __syncthreads();
+        // S' = D S + k w^T and o_j = sum_i q_i S'_ij
+        float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int row = sm.order[rg + RS * m];
+            const float a = fa[row], kk = fk[row], qq = fq[row];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                x[m][c] = __builtin_fmaf(kk, w[c], a * x[m][c]);
+                p[c] = __builtin_fmaf(qq, x[m][c], p[c]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) p[c] = add_xor32_f32(add_xor16_f32(p[c]));
+        if (lane < 16) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) red[wave * DV + 8 * cg + c] = p[c];
+        }
+        __syncthreads();
+        if (tid < DV)
+            A.o[(size_t)head * DV + tid] = (red[tid] + red[DV + tid]) + (red[2 * DV + tid] + red[3 * DV + tid]);
+    }
+    // row maxima, over the row's 16 lanes (a DPP row; non-negative values)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        float R = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) R = fmaxf(R, fabsf(x[m][c]));
         R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0xB1, 0xF, 0xF, false)));
         R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x4E, 0xF, 0xF, false)));
         R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x141, 0xF, 0xF, false)));
         R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x140, 0xF, 0xF, false)));
-        if (cg == 0) sm.R[row] = double(R);
+        if (cg == 0) sm.R[sm.order[rg + RS * m]] = double(R);
     }
     __syncthreads();
 
@@ -261,6 +336,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
                 s1 = A.s[base + r1];
                 q0 = A.r ? double(A.r[base + r0]) : double(A.r_default);
                 q1 = A.r ? double(A.r[base + r1]) : double(A.r_default);
+            } else if (STEP && !A.est) {
+                // the decode token's own decays
+                s0 = A.s_per_row ? A.sd[base + r0] : A.sd[head];
+                s1 = A.s_per_row ? A.sd[base + r1] : A.sd[head];
+                q0 = q1 = double(A.r_default);
             } else {
                 const float* e = A.est + (size_t)head * est_stride(DK);
                 const double W = e[2 * DK];
@@ -410,9 +490,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         const float lo = kMagic - float(n), hi = kMagic + float(n);
         const int bwo = sm.width[row];
         int best;
-        if (bwo <= 5) {
+        if (!STEP && bwo <= 5) {
             best = level_fit<1>(x[m], sm.delta[row], (1 << (bwo - 1)) - 1, sm.cand[row][cg], lo, hi, cg);
-        } else if (bwo == 6) {
+        } else if (!STEP && bwo == 6) {
             best = level_fit<2>(x[m], sm.delta[row], (1 << (bwo - 1)) - 1, sm.cand[row][cg], lo, hi, cg);
         } else {
             float err[16];
@@ -482,7 +562,12 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
 }  // namespace
 
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(allocate_kernel, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL(allocate_kernel<false>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(allocate_kernel<true>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -164,6 +164,16 @@ __device__ __forceinline__ double add_xor16_f64(double v) {
            __longlong_as_double((long long)((uint64_t(hi[1]) << 32) | lo[1]));
 }
 
+// float32 v + the value of the lane 32 / 16 apart (one lane swap)
+__device__ __forceinline__ float add_xor32_f32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor16_f32(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Sum over the lanes of the wavefront that are equal modulo NB (1 or 4), returned in
 // every lane: DPP inside rows of 16 lanes (xor 1, xor 2; rotations by 8 and 4 combine
 // the four lanes of a residue class), then the rows by lane swaps.

@@ -60,14 +60,19 @@ struct AllocArgs {
     uint8_t* state = nullptr;
     const float* s = nullptr;         // [B*H][dk]
     const float* r = nullptr;         // [B*H][dk] or null
-    const float* est = nullptr;       // [B*H][2 dk + 4] online estimators, used when s is null
+    float* est = nullptr;             // [B*H][2 dk + 4] online estimators, used when s is null
     int factor = 0;                   // WB_GAMMA_*
     int cadence = 1;                  // C of the persistence factor
+    // decode step whose write-back allocates (launch_step_allocate): the token's inputs
+    const float *q = nullptr, *k = nullptr, *v = nullptr, *beta = nullptr, *sd = nullptr;
+    float* o = nullptr;
+    int s_per_row = 1;
     uint64_t region_stride = 0;
     float r_default = 0.f;
     int bbar = 4, bmin = 2, bmax = 8;
 };
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
+hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
 
 struct DampArgs {
     const float* samples = nullptr;   // [N][H][dk][dv]

@@ -267,6 +267,33 @@ int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor
     return hip_status(wb::launch_allocate_bits(st->d, a, static_cast<hipStream_t>(stream)));
 }
 
+int state_step_decode_alloc(wb_state* st, const float* q, const float* k, const float* v, const float* beta,
+                            const float* s, float* o, int factor, int C, void* stream) {
+    if (!st || !q || !k || !v || !beta || !s || !o) return WB_EINVAL;
+    if (st->d.kind != WB_BITALLOC || st->d.mode != WB_RTN) return WB_EUNSUPPORTED;
+    if (factor < WB_GAMMA_ERASURE || factor > WB_GAMMA_HC || C < 1) return WB_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(beta) || !aligned4(s))
+        return WB_EALIGN;
+    wb::AllocArgs a;
+    a.state = st->state;
+    a.region_stride = st->region_stride;
+    a.r_default = float(1.0 / (3.0 * st->d.dk));
+    a.bbar = st->d.bbar;
+    a.bmin = st->d.bmin;
+    a.bmax = st->d.bmax;
+    a.est = st->est;
+    a.factor = factor;
+    a.cadence = C;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.sd = s;
+    a.o = o;
+    a.s_per_row = st->d.decay == WB_DECAY_PER_ROW;
+    return hip_status(wb::launch_step_allocate(st->d, a, static_cast<hipStream_t>(stream)));
+}
+
 int state_prefill_chunk(wb_state* st, const uint16_t* q_bf16, const uint16_t* k_bf16, const uint16_t* v_bf16,
                         const float* beta, const float* s, float* o, int T, int chunk, int C, uint64_t t0,
                         void* stream) {

@@ -215,3 +215,52 @@ def compare_write_back(lay: L.Layout, reg_in, reg_gpu, wb, e_in, e_gpu, t, b, h,
         if np.any(err > 0):
             i = np.unravel_index(np.argmax(err), err.shape)
             tally.bad.append((where, "residual", i, eg[i], eo[i]))
+
+
+def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: Tally, where,
+                             window=WINDOW, meta_rel=META_REL):
+    """Compare a write-back that allocated (BITALLOC) with the oracle's on the same
+    updated state X. Widths: equal, or an allocation of the same budget whose proxy
+    cost under the oracle's costs is within 1e-6 of the oracle's (the float32 state
+    moves near-tied costs). Rows of equal width: fit indices equal or of equal squared
+    error within 1e-6; rows of equal width and fit: Delta equal or the adjacent float16
+    where the pre-rounding value is within ``meta_rel`` of the midpoint; rows of equal
+    width, fit and Delta: codes equal or one apart within ``window`` steps of a
+    rounding boundary. Returns the number of rows left out of the code comparison."""
+    from oracle.quantizers import fit_fraction, levels_n, sym_round
+    g = L.decode_region(lay, np.asarray(reg_gpu, np.uint8)[: lay.region_size()])
+    o = L.decode_region(lay, np.asarray(reg_orc, np.uint8)[: lay.region_size()])
+    if g.widths.sum() != lay.bbar * lay.dk or g.widths.min() < lay.bmin or g.widths.max() > lay.bmax:
+        tally.bad.append((where, "width budget", int(g.widths.sum())))
+        return lay.dk
+    c = alloc["c"]
+    same_w = g.widths == o.widths
+    if not same_w.all():
+        cg = float(np.sum(c * 2.0 ** (-2.0 * g.widths)))
+        co = float(np.sum(c * 2.0 ** (-2.0 * o.widths)))
+        if cg > co * (1 + 1e-6) or (~same_w).sum() > 8:
+            tally.bad.append((where, "widths", np.argwhere(~same_w).ravel()[:6].tolist(), cg, co))
+    same_f = same_w & (g.fit == o.fit)
+    for i in np.argwhere(same_w & ~same_f).ravel():
+        e = alloc["fit_err"][i]
+        if abs(e[g.fit[i]] - e[o.fit[i]]) > 1e-6 * max(e[o.fit[i]], 1e-300):
+            tally.bad.append((where, "fit", int(i), int(g.fit[i]), int(o.fit[i])))
+    rows = np.argwhere(same_f).ravel()
+    pre = np.array([fit_fraction(int(o.fit[i])) * alloc["R"][i] / levels_n(int(o.widths[i])) for i in rows])
+    _meta_ok(g.delta_bits[rows], o.delta_bits[rows], pre, tally, (where, "delta"), meta_rel)
+    skipped = lay.dk - rows.size
+    for i in rows:
+        if g.delta_bits[i] != o.delta_bits[i]:
+            skipped += 1
+            continue
+        n = levels_n(int(g.widths[i]))
+        rr = sym_round(X[i], float(g.delta[i]), n, "rtn")
+        tally.elems += lay.dv
+        diff = g.kappa[i] != rr.kappa
+        if diff.any():
+            tally.mismatch += int(diff.sum())
+            ok = ~diff | ((np.abs(g.kappa[i] - rr.kappa) == 1) & (rr.boundary <= window))
+            if not ok.all():
+                j = np.argwhere(~ok).ravel()[:3]
+                tally.bad.append((where, "codes", int(i), j.tolist(), g.kappa[i][j].tolist(), rr.kappa[j].tolist()))
+    return skipped

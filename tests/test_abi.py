@@ -123,6 +123,7 @@ def test_calls_reject_null_handles_and_pointers():
     assert L_.state_quantize(None, p, None) == -1
     assert L_.state_allocate_bits(None, p, None, 0, 1, None) == -1
     assert L_.state_set_estimators(None, p) == -1
+    assert L_.state_step_decode_alloc(None, p, p, p, p, p, p, 0, 1, None) == -1
     assert L_.state_free(None) == -1
     assert L_.state_set_activity(None, p, p) == -1
     assert L_.state_prefill_chunk(None, p, p, p, p, p, p, 8, 64, 8, 0, None) == -1

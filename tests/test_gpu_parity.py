@@ -481,6 +481,69 @@ def test_online_estimators_and_allocation_from_them(mode, per_row):
                 _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h))
 
 
+@pytest.mark.parametrize("case", ["est-erasure", "est-hC64", "decays-w1", "per-head-est"])
+def test_decode_step_with_allocation(case):
+    """Decode tokens whose write-back allocates (teacher-forced: each token starts from
+    the GPU's stored region and estimators) against the oracle's plain step, allocation
+    on the updated state and single rounding; readout within 1e-4 relative."""
+    from oracle.estimators import EmaState, ema_estimates, ema_fold
+    from oracle.step import decode_step_alloc
+    from tests.parity import O_REL, Tally, compare_alloc_write_back
+    print(f"\n[case] decode step with allocation {case}", flush=True)
+    B, H, dk, T = 2, 3, 128, 5
+    per_row = case != "per-head-est"
+    use_est = case != "decays-w1"
+    factor, C = {"est-erasure": ("erasure", 1), "est-hC64": ("hC", 64), "decays-w1": ("w1", 1),
+                 "per-head-est": ("erasure", 1)}[case]
+    lay = _layout(L.BITALLOC, "rtn", B, H, dk, per_row=per_row)
+    rng = np.random.default_rng(61)
+    st = _state(lay)
+    inp = decode_inputs(61, B, H, dk, dk, T, per_row)
+    dev = {key: _to_dev(val) for key, val in inp.items()}
+    st.quantize(_to_dev(_warm_state(rng, B, H, dk, dk)))
+    o = torch.zeros((B, H, dk), dtype=torch.float32, device="cuda")
+    est = None
+    if use_est:
+        est = torch.zeros((B, H, 2 * dk + 4), dtype=torch.float32, device="cuda")
+        # a few ordinary tokens first, so that the estimators hold a history
+        st.set_estimators(est)
+        for t in range(3):
+            st.step_decode(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, t)
+    tally = Tally()
+    skipped = 0
+    for t in range(T):
+        torch.cuda.synchronize()
+        regs_in = st.regions().cpu().numpy()
+        e_in = est.cpu().numpy().astype(np.float64) if use_est else None
+        st.step_decode_alloc(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, factor, C)
+        torch.cuda.synchronize()
+        regs = st.regions().cpu().numpy()
+        o_np = o.cpu().numpy()
+        e_out = est.cpu().numpy().astype(np.float64) if use_est else None
+        for b in range(B):
+            for h in range(H):
+                s_bh = inp["s"][b, h].astype(np.float64)
+                s_rows = s_bh if per_row else np.full(dk, float(s_bh))
+                beta = float(inp["beta"][t, b, h])
+                if use_est:
+                    es = EmaState(Na=e_in[b, h, :dk], Nr=e_in[b, h, dk:2 * dk], W=float(e_in[b, h, 2 * dk]))
+                    es = ema_fold(es, s_rows, beta, inp["k"][t, b, h].astype(np.float64))
+                    for got, want in ((e_out[b, h, :dk], es.Na), (e_out[b, h, dk:2 * dk], es.Nr)):
+                        assert np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-30)) < 1e-5
+                    sa, ra = ema_estimates(es.Na, es.Nr, es.W)
+                else:
+                    sa, ra = s_rows, np.full(dk, 1.0 / (3 * dk))
+                reg_orc, alloc, o_orc, X = decode_step_alloc(
+                    lay, regs_in[b * H + h], inp["q"][t, b, h], inp["k"][t, b, h], inp["v"][t, b, h], beta,
+                    s_bh, sa, ra, factor, C)
+                skipped += compare_alloc_write_back(lay, regs[b * H + h], reg_orc, alloc, X, tally, (t, b, h))
+                err = np.linalg.norm(o_np[b, h] - o_orc) / max(np.linalg.norm(o_orc), 1e-30)
+                tally.o_worst = max(tally.o_worst, float(err))
+    print("[tally]", tally.summary(), "rows left out of the code comparison:", skipped, flush=True)
+    assert tally.ok(), tally.summary()
+    assert skipped <= 0.01 * T * B * H * dk
+
+
 def test_allocation_then_decode_full_budget_zero_state():
     # a zero state keeps every row at the mean width
     lay = _layout(L.BITALLOC, "rtn", 1, 2, 128)
