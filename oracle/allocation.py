@@ -121,6 +121,39 @@ def allocate_head(Y, s_rows, r_rows, bbar=4, bmin=2, bmax=8, factor=GAMMA_ERASUR
             "R": R, "Rt": Rt, "Gamma": G, "fit_err": errs}
 
 
+def allocate_layer(Ys, s_rows, r_rows, bbar=4, bmin=2, bmax=8, factor=GAMMA_ERASURE, C=1):
+    """Widths and fit indices for the heads of one layer of one sequence under the
+    layer-wise mean budget ([LBRS] "State bit allocation": "at layer-wise mean budget
+    bbar"; "Range normalization": R~ within each output group, one head). Costs per
+    head as in ``allocate_head``; the geometric mean, the rounding and the one-bit
+    adjustments run over all rows of the layer (sum b = bbar * rows, ties to the
+    lower (head, row)); every row keeps bbar only when the whole layer is zero.
+    ``Ys`` [H][dk][dv]; ``s_rows`` / ``r_rows`` per head (None: no decay estimate).
+    Returns one dict per head, as ``allocate_head``."""
+    H = len(Ys)
+    parts = [row_costs(Ys[h], None if s_rows is None else s_rows[h], None if r_rows is None else r_rows[h],
+                       factor, C) for h in range(H)]
+    dk = len(parts[0][0])
+    c_all = np.concatenate([p[3] for p in parts])
+    if all(np.all(p[0] == 0) for p in parts):
+        bstar = np.full(H * dk, float(bbar))
+        b = np.full(H * dk, bbar, dtype=np.int64)
+    else:
+        bstar = real_widths(c_all, bbar)
+        b = integer_widths(c_all, bstar, bbar, bmin, bmax)
+    out = []
+    for h in range(H):
+        R, Rt, G, c = parts[h]
+        bh = b[h * dk:(h + 1) * dk]
+        fits = np.zeros(dk, dtype=np.int64)
+        errs = np.zeros((dk, 16))
+        for i in range(dk):
+            fits[i], errs[i] = fit_row(np.asarray(Ys[h][i], np.float64), R[i], int(bh[i]))
+        out.append({"widths": bh.copy(), "fit": fits, "bstar": bstar[h * dk:(h + 1) * dk],
+                    "c": np.maximum(c, C_FLOOR), "R": R, "Rt": Rt, "Gamma": G, "fit_err": errs})
+    return out
+
+
 def default_r(dk: int) -> float:
     """Closed form of r_i for the synthetic stream: beta ~ U(0,1) and unit keys of
     isotropic direction give E[beta (2 - beta)] = 2/3 and E[k_i^2] = 1/dk, so

@@ -22,9 +22,11 @@ MIXED     static mixed precision ([DAMP] "Risk scoring and selection",
 BITALLOC  decay-aware per-row widths ([LBRS] "State bit allocation", "Levels and
           storage": prefix sums of widths give row offsets): row i's codes start at
           byte (dv/8) * sum_{i'<i} b_i', element j at bits [j b_i, (j+1) b_i),
-          stored as kappa + n_i; the code area is dk*dv*bbar/8 bytes (the head's
-          budget is fixed); then f16 Delta [dk]; then u8 meta [dk] =
-          (b_i - 1) | (k_i << 4), k_i the clipping-fit index.
+          stored as kappa + n_i; the code area holds dk*dv*b_cap/8 bytes, b_cap = bbar
+          when the budget is per head (the area is exactly full) and b_cap = bmax when
+          the budget is per layer (a head's widths may sum to anything up to bmax*dk;
+          the bytes after its last row are zero); then f16 Delta [dk]; then u8 meta
+          [dk] = (b_i - 1) | (k_i << 4), k_i the clipping-fit index.
 """
 from __future__ import annotations
 
@@ -56,11 +58,17 @@ class Layout:
     mode: str = "rtn"
     seed: int = 0
     mem_bits: int = 0      # k of the temporal-memory rules (direction / residual memory)
+    budget: str = "head"   # BITALLOC width budget: "head" or "layer" (all heads of a sequence)
     extra: dict = field(default_factory=dict)
 
     @property
     def int8_rows(self) -> int:
         return self.dk - self.k_hi if self.kind == MIXED else self.dk
+
+    @property
+    def code_capacity(self) -> int:
+        """BITALLOC code-area bytes of one head."""
+        return self.dk * self.dv * (self.bmax if self.budget == "layer" else self.bbar) // 8
 
     def region_size(self) -> int:
         dk, dv = self.dk, self.dv
@@ -74,7 +82,7 @@ class Layout:
             q = dk - self.k_hi
             return self.k_hi * dv * 2 + q * dv + q * (dv // self.block) * 4
         if self.kind == BITALLOC:
-            return dk * dv * self.bbar // 8 + 2 * dk + dk
+            return self.code_capacity + 2 * dk + dk
         raise ValueError(self.kind)
 
     def region_stride(self) -> int:
@@ -135,7 +143,7 @@ def decode_region(lay: Layout, region: np.ndarray) -> Content:
         c.zero = f16_value(c.zero_bits)
         return c
     if lay.kind == BITALLOC:
-        cbytes = dk * dv * lay.bbar // 8
+        cbytes = lay.code_capacity
         dbits = r[cbytes: cbytes + 2 * dk].view(np.uint16).copy()
         meta = r[cbytes + 2 * dk: cbytes + 3 * dk].astype(np.int64)
         widths = (meta & 7) + 1
@@ -186,8 +194,11 @@ def encode_region(lay: Layout, c: Content) -> np.ndarray:
             data = pack_fields(np.asarray(c.kappa[i], dtype=np.int64) + n, b)
             out[off: off + data.size] = data
             off += data.size
-        cbytes = dk * dv * lay.bbar // 8
-        assert off == cbytes, "widths do not meet the head budget"
+        cbytes = lay.code_capacity
+        if lay.budget == "layer":
+            assert off <= cbytes, "widths exceed the head's code capacity"
+        else:
+            assert off == cbytes, "widths do not meet the head budget"
         out[cbytes: cbytes + 2 * dk] = np.asarray(c.delta_bits, np.uint16).view(np.uint8)
         meta = (np.asarray(c.widths, np.int64) - 1) | (np.asarray(c.fit, np.int64) << 4)
         out[cbytes + 2 * dk: cbytes + 3 * dk] = meta.astype(np.uint8)

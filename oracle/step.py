@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import layouts as L
-from .allocation import allocate_head
+from .allocation import allocate_head, allocate_layer
 from .numerics import f16, f16_bits
 from .philox import sr_draws
 from .quantizers import (DIR, EF, RESQ, SR, affine_metadata, affine_round, levels_n, row_step,
@@ -209,6 +209,15 @@ def allocate_region(lay: L.Layout, region, s_rows, r_rows, factor="erasure", C=1
     return _allocate_and_round(lay, Y, s_rows, r_rows, factor, C)
 
 
+def allocate_layer_regions(lay: L.Layout, regions, s_rows, r_rows, factor="erasure", C=1):
+    """The allocation pass over the H heads of one sequence under the layer-wise budget
+    (``lay.budget == "layer"``): widths from the stored states of all heads, then each
+    head's stored values re-rounded (nearest) at its new widths."""
+    Ys = [L.stored_values(lay, L.decode_region(lay, reg)) for reg in regions]
+    allocs = allocate_layer(Ys, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C)
+    return [_round_at(lay, Ys[h], allocs[h]) for h in range(len(regions))], allocs
+
+
 def decode_step_alloc(lay: L.Layout, region, q, k, v, beta, s, s_rows, r_rows, factor="erasure", C=1):
     """One decode token for a BITALLOC head whose write-back allocates ([LBRS] "State
     bit allocation": widths are chosen at each write-back): the step from the stored
@@ -224,6 +233,10 @@ def decode_step_alloc(lay: L.Layout, region, q, k, v, beta, s, s_rows, r_rows, f
 
 def _allocate_and_round(lay: L.Layout, Y, s_rows, r_rows, factor, C):
     alloc = allocate_head(Y, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C)
+    return _round_at(lay, Y, alloc), alloc
+
+
+def _round_at(lay: L.Layout, Y, alloc):
     widths, fits = alloc["widths"], alloc["fit"]
     delta = np.zeros(lay.dk)
     kappa = np.zeros((lay.dk, lay.dv), np.int64)
@@ -233,7 +246,7 @@ def _allocate_and_round(lay: L.Layout, Y, s_rows, r_rows, factor, C):
         rr = sym_round(Y[i], delta[i], n, "rtn")
         kappa[i] = rr.kappa
     c = L.Content(kappa=kappa, widths=widths, fit=fits, delta_bits=f16_bits(delta))
-    return L.encode_region(lay, c), alloc
+    return L.encode_region(lay, c)
 
 
 def prefill(lay: L.Layout, region, e_in, q, k, v, beta, s, t0: int, C: int, b: int, h: int,

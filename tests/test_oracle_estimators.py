@@ -151,3 +151,85 @@ def test_step_with_allocation_reduces_to_its_parts():
     for i in range(dk):
         n = levels_n(int(c.widths[i]))
         assert np.array_equal(c.kappa[i], sym_round(S_new[i], float(c.delta[i]), n, "rtn").kappa)
+
+
+# ---------------------------------------------------------------- layer-wise budget
+
+def _heads(rng, H, dk=16, dv=8):
+    return [rng.standard_normal((dk, dv)) * np.exp(rng.uniform(-3, 0.5, (dk, 1))) for _ in range(H)]
+
+
+def test_layer_budget_with_one_head_is_the_head_budget():
+    from oracle.allocation import allocate_layer
+    rng = np.random.default_rng(21)
+    Y = _heads(rng, 1)
+    s = np.exp(rng.uniform(np.log(1e-3), 0.0, 16))
+    a = allocate_layer(Y, [s], [0.01])[0]
+    b = allocate_head(Y[0], s, 0.01)
+    assert np.array_equal(a["widths"], b["widths"]) and np.array_equal(a["fit"], b["fit"])
+
+
+def test_layer_budget_identical_heads_and_decay_across_heads():
+    from oracle.allocation import allocate_layer
+    rng = np.random.default_rng(22)
+    Y = _heads(rng, 1)[0]
+    s = np.exp(rng.uniform(np.log(1e-3), 0.0, 16))
+    per_head = allocate_head(Y, s, 0.01)["widths"]
+    for a in allocate_layer([Y, Y, Y], [s, s, s], [0.01] * 3):
+        assert np.array_equal(a["widths"], per_head)
+    # equal ranges, head 1 decays faster on every row: head 0 takes bits from head 1
+    a0, a1 = allocate_layer([Y, Y], [s, s + 1.0], [0.01, 0.01])
+    assert a0["widths"].sum() > 4 * 16 > a1["widths"].sum()
+    assert a0["widths"].sum() + a1["widths"].sum() == 2 * 4 * 16
+
+
+def test_layer_budget_is_the_brute_force_optimum_on_tiny_layers():
+    import itertools
+    from oracle.allocation import allocate_layer, proxy_cost
+    rng = np.random.default_rng(23)
+    for _ in range(20):
+        Y = _heads(rng, 2, dk=2, dv=4)
+        s = [np.exp(rng.uniform(np.log(1e-3), 0.0, 2)) for _ in range(2)]
+        al = allocate_layer(Y, s, [0.01, 0.01], bbar=4, bmin=2, bmax=8)
+        b = np.concatenate([a["widths"] for a in al])
+        c = np.concatenate([a["c"] for a in al])
+        best = min(proxy_cost(c, np.array(w)) for w in itertools.product(range(2, 9), repeat=4) if sum(w) == 16)
+        assert b.sum() == 16 and np.isclose(proxy_cost(c, b), best, rtol=1e-12)
+
+
+def test_layer_budget_zero_heads():
+    from oracle.allocation import allocate_layer
+    rng = np.random.default_rng(24)
+    Z = np.zeros((16, 8))
+    s = np.full(16, 0.05)
+    for a in allocate_layer([Z, Z], [s, s], [0.01, 0.01]):
+        assert np.all(a["widths"] == 4)
+    Y = _heads(rng, 1)[0]
+    a0, a1 = allocate_layer([Y, Z], [s, s], [0.01, 0.01])
+    assert np.all(a1["widths"] == 2) and a0["widths"].sum() == 2 * 4 * 16 - 2 * 16
+
+
+def test_layer_capacity_region_round_trip():
+    from oracle import layouts as L
+    from oracle.allocation import allocate_layer
+    from oracle.step import allocate_layer_regions
+    rng = np.random.default_rng(25)
+    dk, dv, H = 16, 16, 3
+    lay = L.Layout(kind=L.BITALLOC, B=1, H=H, dk=dk, dv=dv, bbar=4, bmin=2, bmax=8, budget="layer")
+    assert lay.region_size() == dk * dv + 3 * dk
+    s = [np.exp(rng.uniform(np.log(1e-3), 0.0, dk)) for _ in range(H)]
+    s[2] = s[2] + 1.0
+    start = [L.initial_region(lay) for _ in range(H)]
+    Ys = _heads(rng, H, dk, dv)
+    from oracle.step import import_state
+    regs = [import_state(lay, Ys[h], start[h]) for h in range(H)]
+    new, allocs = allocate_layer_regions(lay, regs, s, [0.01] * H)
+    used = []
+    for h in range(H):
+        c = L.decode_region(lay, new[h])
+        assert np.array_equal(c.widths, allocs[h]["widths"])
+        u = int(c.widths.sum()) * dv // 8
+        used.append(u)
+        assert np.all(new[h][u: lay.code_capacity] == 0)
+        assert np.array_equal(L.encode_region(lay, c), new[h])
+    assert sum(used) == H * dk * dv * 4 // 8 and used[2] < used[0]
