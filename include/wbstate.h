@@ -114,6 +114,12 @@ extern "C" {
 #define WB_GAMMA_W1 1       /* 1 / (1 - a_i^2), a_i = e^{-s_i}: DAMP's factor, uncapped */
 #define WB_GAMMA_HC 2       /* 1 / (1 - e^{-2 C s_i}): the write-back-time factor */
 
+/* BITALLOC width budget ([LBRS] "State bit allocation": a layer-wise mean budget) */
+#define WB_BUDGET_HEAD 0    /* each head's widths sum to bbar * dk; code area exactly full */
+#define WB_BUDGET_LAYER 1   /* the widths of all H heads of a sequence sum to bbar * H * dk;
+                             * each head's code area holds bmax * dk * dv / 8 bytes, zero
+                             * after the head's last row */
+
 typedef struct wb_layout_desc {
     int32_t kind;    /* WB_FP32 .. WB_BITALLOC */
     int32_t mode;    /* WB_RTN, WB_SR, WB_EF, WB_DIR, WB_RESQ */
@@ -124,6 +130,7 @@ typedef struct wb_layout_desc {
     int32_t k_hi;    /* MIXED float16 rows: a positive multiple of dk/8 below dk */
     int32_t bbar, bmin, bmax;  /* BITALLOC mean width and clip range, 2 <= bmin <= bbar <= bmax <= 8 */
     int32_t mem_bits;          /* k of WB_DIR / WB_RESQ, 1..8 (the pages evaluate 2, 3, 4); 0 otherwise */
+    int32_t budget;            /* WB_BUDGET_HEAD or WB_BUDGET_LAYER (BITALLOC, H * dk <= 4096); 0 otherwise */
     uint64_t seed;             /* Philox key for WB_SR */
 } wb_layout_desc;
 

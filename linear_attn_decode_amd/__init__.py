@@ -21,6 +21,7 @@ KIND_NAMES = {"fp32": FP32, "uniform": UNIFORM, "had_int8": HAD_INT8, "mixed": M
 RTN, SR, EF, DIR, RESQ = 0, 1, 2, 3, 4
 MODE_NAMES = {"rtn": RTN, "sr": SR, "ef": EF, "dir": DIR, "resq": RESQ}
 GAMMA_CODES = {"erasure": 0, "w1": 1, "hC": 2}
+BUDGET_CODES = {"head": 0, "layer": 1}
 DECAY_PER_HEAD, DECAY_PER_ROW = 0, 1
 
 STATUS = {0: "ok", -1: "EINVAL", -2: "ESIZE", -3: "EUNSUPPORTED", -4: "ELAUNCH", -5: "EALIGN"}
@@ -31,7 +32,7 @@ class LayoutDesc(ctypes.Structure):
                 ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("k_hi", ctypes.c_int32),
                 ("bbar", ctypes.c_int32), ("bmin", ctypes.c_int32), ("bmax", ctypes.c_int32),
-                ("mem_bits", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("mem_bits", ctypes.c_int32), ("budget", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 _P = ctypes.c_void_p
@@ -82,12 +83,12 @@ def check(status: int, what: str = "") -> None:
 
 
 def make_desc(kind, mode, B, H, dk=128, dv=128, per_row_decay=True, bits=4, block=32, k_hi=16,
-              bbar=4, bmin=2, bmax=8, seed=0, mem_bits=0) -> LayoutDesc:
+              bbar=4, bmin=2, bmax=8, seed=0, mem_bits=0, budget="head") -> LayoutDesc:
     kind = KIND_NAMES.get(kind, kind)
     mode = MODE_NAMES.get(mode, mode)
     return LayoutDesc(kind=kind, mode=mode, decay=DECAY_PER_ROW if per_row_decay else DECAY_PER_HEAD,
                       B=B, H=H, dk=dk, dv=dv, bits=bits, block=block, k_hi=k_hi, bbar=bbar,
-                      bmin=bmin, bmax=bmax, mem_bits=mem_bits, seed=seed)
+                      bmin=bmin, bmax=bmax, mem_bits=mem_bits, budget=BUDGET_CODES.get(budget, budget), seed=seed)
 
 
 def buffer_sizes(desc: LayoutDesc):
@@ -119,11 +120,11 @@ class WriteBackState:
 
     def __init__(self, kind, mode="rtn", B=1, H=1, dk=128, dv=128, per_row_decay=True, bits=4,
                  block=32, k_hi=16, bbar=4, bmin=2, bmax=8, seed=0, perm=None, device="cuda",
-                 stream=None, mem_bits=0):
+                 stream=None, mem_bits=0, budget="head"):
         import numpy as np
         import torch
         self.desc = make_desc(kind, mode, B, H, dk, dv, per_row_decay, bits, block, k_hi, bbar, bmin,
-                              bmax, seed, mem_bits)
+                              bmax, seed, mem_bits, budget)
         nbytes, side = buffer_sizes(self.desc)
         self.state = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.side = torch.empty(max(side // 4, 4), dtype=torch.float32, device=device)
@@ -210,9 +211,16 @@ class WriteBackState:
                                    _stream(stream)), "state_quantize")
 
     def region_stride(self) -> int:
-        import numpy as np
-        regions = self.state.numel() - (((self.H * self.dk + 255) // 256) * 256 if self.desc.kind == MIXED else 0)
-        return regions // (self.B * self.H)
+        """Bytes between heads: the state buffer less what follows the regions (the
+        MIXED permutation table; the layer-budget allocation workspace)."""
+        def r256(n):
+            return (n + 255) // 256 * 256
+        tail = 0
+        if self.desc.kind == MIXED:
+            tail = r256(self.H * self.dk)
+        elif self.desc.kind == BITALLOC and self.desc.budget == BUDGET_CODES["layer"]:
+            tail = r256(self.B * self.H * self.dk * 9)
+        return (self.state.numel() - tail) // (self.B * self.H)
 
     def regions(self):
         """The stored bytes as a [B*H, region_stride] uint8 tensor view."""

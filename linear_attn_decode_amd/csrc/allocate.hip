@@ -167,8 +167,16 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 // (u = k^T D S, w = beta (v - u), S' = D S + k w^T, o = S'^T q) runs in float32, the
 // token is folded into the estimators, and the widths, fits and codes are chosen
 // for S' (every row through the 16-candidate fit: S' is not on the old grid).
-template <bool STEP>
+enum { kHead = 0, kStep = 1, kCost = 2, kPack = 3 };
+
+// MODE kHead: the allocation pass on the stored state (per-head budget). kStep: one
+// decode token whose write-back allocates (see below). Layer-wise budget: kCost writes
+// each row's cost c_i (0 for a head whose rows are all zero) to the workspace and
+// stops; kPack takes the widths the per-sequence pass left in the workspace, then
+// fits and repacks as kHead does.
+template <int MODE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) allocate_kernel(const AllocArgs A) {
+    constexpr bool STEP = MODE == kStep;
     __shared__ AllocSmem sm;
     // decode-step scratch, in the candidate table (filled only after the step)
     float* const fk = reinterpret_cast<float*>(&sm.cand[0][0]);
@@ -180,7 +188,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     const int head = blockIdx.x;
     const int cg = tid % NCG, rg = tid / NCG;
     uint8_t* region = A.state + (size_t)head * A.region_stride;
-    const int code_bytes = DK * DV * A.bbar / 8;
+    const int code_bytes = A.code_cap;         // Delta and meta follow the code area
     const int total = code_bytes + 3 * DK;
 
     for (int i = tid; i * 16 < total; i += NT)
@@ -326,7 +334,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         const double sq = wave_sum_f64<1>(R0 * R0 + R1 * R1);
         int b0 = A.bbar, b1 = A.bbar;
         double c0 = 0.0, c1 = 0.0;
-        if (sq > 0.0) {
+        if (MODE != kPack && sq > 0.0) {
             const double rms = sqrt(sq / double(DK));
             const size_t base = (size_t)head * DK;
             double s0, s1, q0, q1;
@@ -355,6 +363,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             const double rt0 = R0 / rms, rt1 = R1 / rms;
             c0 = fmin(fmax(g0 * (rt0 * rt0), 1e-300), 1e300);
             c1 = fmin(fmax(g1 * (rt1 * rt1), 1e-300), 1e300);
+            if constexpr (MODE == kCost) {
+                A.ws_c[base + r0] = c0;
+                A.ws_c[base + r1] = c1;
+            } else {
             const double lsum = wave_sum_f64<1>(log(c0) + log(c1));
             const double gm = exp(lsum / double(DK));
             const double bs0 = double(A.bbar) + 0.5 * log2(c0 / gm);
@@ -453,6 +465,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
                 b0 += grow ? a0 : -a0;
                 b1 += grow ? a1 : -a1;
             }
+            }
+        } else if constexpr (MODE == kCost) {
+            A.ws_c[(size_t)head * DK + r0] = 0.0;        // a head whose rows are all zero
+            A.ws_c[(size_t)head * DK + r1] = 0.0;
+        }
+        if constexpr (MODE == kPack) {
+            b0 = A.ws_w[(size_t)head * DK + r0];
+            b1 = A.ws_w[(size_t)head * DK + r1];
         }
         sm.newwidth[r0] = b0;
         sm.newwidth[r1] = b1;
@@ -466,6 +486,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         sm.newoff[r0] = incl - local;
         sm.newoff[r1] = incl - local + b0 * (DV / 8);
     }
+    if constexpr (MODE == kCost) return;
     __syncthreads();
 
     // candidate steps: thread t fills fit index t % 16 of rows t / 16 + 16 m
@@ -559,15 +580,196 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         reinterpret_cast<uint4*>(region)[i] = reinterpret_cast<const uint4*>(sm.reg)[i];
 }
 
+// ---------------------------------------------------------------------------------
+// Widths of one sequence's layer under the layer-wise budget ([LBRS] "State bit
+// allocation": a layer-wise mean budget; "Range normalization": costs normalised per
+// head, computed by the kCost pass): the geometric mean, the rounding, the clip and the
+// one-bit adjustments of the per-head rule taken over all H*dk rows of the sequence,
+// ties to the lower (head, row); when every head of the layer is zero every row keeps
+// bbar. One workgroup per sequence; thread t owns the contiguous rows t*rpt ..
+// t*rpt + rpt - 1, so that a row's rank among tied rows follows the thread order.
+constexpr int LNT = 512, LMAX = 4096, LW = LNT / 64;   // up to 4096 rows
+
+struct LayerSmem {
+    double v0[LMAX];          // first candidate value of each row
+    int8_t lim[LMAX];         // its number of candidates (one-bit steps)
+    uint8_t bw[LMAX];         // widths
+    double partd[2][LW];
+    int parti[2][LW];
+    uint32_t low_word;
+};
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+// block sums, summed over the wavefronts in a fixed order; `ph` alternates between
+// the two slots so that one barrier per sum suffices
+__device__ __forceinline__ double block_sum_f64(double v, LayerSmem& sm, int& ph) {
+    v = wave_sum_f64<1>(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sm.partd[ph][wave] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < LW; ++w) t += sm.partd[ph][w];
+    ph ^= 1;
+    return t;
+}
+__device__ __forceinline__ int block_sum_i32(int v, LayerSmem& sm, int& ph) {
+    v = wave_sum_i32(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sm.parti[ph][wave] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < LW; ++w) t += sm.parti[ph][w];
+    ph ^= 1;
+    return t;
+}
+
+__global__ void __launch_bounds__(LNT) layer_widths_kernel(const AllocArgs A) {
+    __shared__ LayerSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = A.H * DK;
+    const int rpt = (n + LNT - 1) / LNT;
+    const int row0 = min(tid * rpt, n), row1 = min(row0 + rpt, n);
+    const size_t base = (size_t)blockIdx.x * n;
+    int ph = 0;
+    int nz = 0;
+    for (int r = row0; r < row1; ++r) {
+        const double c = A.ws_c[base + r];
+        sm.v0[r] = c;
+        sm.bw[r] = uint8_t(A.bbar);
+        nz += c != 0.0;
+    }
+    if (block_sum_i32(nz, sm, ph) > 0) {
+        double lsum = 0.0;
+        for (int r = row0; r < row1; ++r) {
+            sm.v0[r] = fmax(sm.v0[r], 1e-300);
+            lsum += log(sm.v0[r]);
+        }
+        const double gm = exp(block_sum_f64(lsum, sm, ph) / double(n));
+        int tot = 0;
+        for (int r = row0; r < row1; ++r) {
+            const double bs = double(A.bbar) + 0.5 * log2(sm.v0[r] / gm);
+            const int b = int(fmin(fmax(rint(bs), double(A.bmin)), double(A.bmax)));
+            sm.bw[r] = uint8_t(b);
+            tot += b;
+        }
+        const int target = A.bbar * n;
+        tot = block_sum_i32(tot, sm, ph);
+        const bool grow = tot < target;
+        const int moves = grow ? target - tot : tot - target;
+        if (moves > 0) {
+            // candidates (row, step): the per-head rule's keys (gain bits, or the
+            // complement of the loss bits), the `moves` largest taken; a row's
+            // successive values scale exactly by `scale`
+            const double scale = grow ? 0.25 : 4.0;
+            for (int r = row0; r < row1; ++r) {
+                const int b = sm.bw[r];
+                const double c = sm.v0[r];
+                sm.lim[r] = int8_t(grow ? A.bmax - b : b - A.bmin);
+                sm.v0[r] = grow ? (0.75 * c) * exp2(-2.0 * b) : (3.0 * c) * exp2(-2.0 * b);
+            }
+            auto for_keys = [&](int r, auto f) {
+                double v = sm.v0[r];
+                const int lim = sm.lim[r];
+                for (int st = 0; st < lim; ++st) {
+                    const uint64_t bits = uint64_t(__double_as_longlong(v));
+                    f(grow ? bits : ~bits);
+                    v *= scale;
+                }
+            };
+            auto count_if = [&](auto pred) {
+                int cnt = 0;
+                for (int r = row0; r < row1; ++r) for_keys(r, [&](uint64_t k) { cnt += pred(k); });
+                return block_sum_i32(cnt, sm, ph);
+            };
+            uint32_t Hw = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = Hw | (1u << bit);
+                if (count_if([&](uint64_t k) { return int(uint32_t(k >> 32) >= cand); }) >= moves) Hw = cand;
+            }
+            const uint64_t hiT = (uint64_t(Hw) << 32) | 0xFFFFFFFFull;
+            const int need = moves - count_if([&](uint64_t k) { return int(k > hiT); });
+            const int neq = count_if([&](uint64_t k) { return int(uint32_t(k >> 32) == Hw); });
+            uint32_t Lw = 0;
+            if (neq > 1) {
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t cand = Lw | (1u << bit);
+                    if (count_if([&](uint64_t k) { return int(uint32_t(k >> 32) == Hw && uint32_t(k) >= cand); }) >= need)
+                        Lw = cand;
+                }
+            } else {
+                // the one key with that high word: its low word
+                for (int r = row0; r < row1; ++r)
+                    for_keys(r, [&](uint64_t k) {
+                        if (uint32_t(k >> 32) == Hw) sm.low_word = uint32_t(k);
+                    });
+                __syncthreads();
+                Lw = sm.low_word;
+            }
+            const uint64_t T = (uint64_t(Hw) << 32) | Lw;
+            const int rem = moves - count_if([&](uint64_t k) { return int(k > T); });
+            // this thread's tied rows (a row has at most one candidate equal to T: its
+            // successive values differ by a factor of 4) and their rank in row order
+            int ties = 0;
+            for (int r = row0; r < row1; ++r) {
+                bool t = false;
+                for_keys(r, [&](uint64_t k) { t |= k == T; });
+                ties += t;
+            }
+            int incl = ties;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int o = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += o;
+            }
+            if (lane == 63) sm.parti[ph][wave] = incl;
+            __syncthreads();
+            int before = incl - ties;
+            for (int w = 0; w < wave; ++w) before += sm.parti[ph][w];
+            for (int r = row0; r < row1; ++r) {
+                int a = 0;
+                bool t = false;
+                for_keys(r, [&](uint64_t k) {
+                    a += k > T;
+                    t |= k == T;
+                });
+                if (t) {
+                    if (before < rem) ++a;
+                    ++before;
+                }
+                sm.bw[r] = uint8_t(int(sm.bw[r]) + (grow ? a : -a));
+            }
+        }
+    }
+    for (int r = row0; r < row1; ++r) A.ws_w[base + r] = sm.bw[r];
+}
+
 }  // namespace
 
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(allocate_kernel<false>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL(allocate_kernel<kHead>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(allocate_kernel<true>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL(allocate_kernel<kStep>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_allocate_layer(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(allocate_kernel<kCost>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(layer_widths_kernel, dim3(d.B), dim3(LNT), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(allocate_kernel<kPack>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -111,6 +111,7 @@ struct Smem {
     int fit[KIND == WB_BITALLOC ? DK : 1];
     int off[KIND == WB_BITALLOC ? DK : 1];
     float delta[KIND == WB_BITALLOC ? DK : 1];
+    int used;                       // BITALLOC code bytes of the head (sum of widths * DV / 8)
 };
 
 template <int KIND, int MODE, int OP, int DK, int DV>
@@ -151,10 +152,14 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
 
     // ---- BITALLOC: stage the region in LDS, derive widths and row offsets --------
     if (KIND == WB_BITALLOC) {
-        const int code_bytes = DK * DV * A.bbar / 8;
+        // Delta and meta follow the code area (A.code_cap bytes); under the per-head
+        // budget the codes fill it and the whole region is staged at once, under the
+        // layer budget the metadata is staged first and the codes up to the head's
+        // last row after the widths are known (below)
+        const int code_bytes = A.code_cap;
         const int total = code_bytes + 3 * DK;
         const uint4* src = reinterpret_cast<const uint4*>(region);
-        for (int i = tid; i * 16 < total; i += NT) {
+        for (int i = A.layer ? code_bytes / 16 + tid : tid; i * 16 < total; i += NT) {
             reinterpret_cast<uint4*>(sm.reg)[i] = src[i];
         }
         __syncthreads();
@@ -192,6 +197,12 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                 if (row < DK) sm.off[row] = run;
                 run += wv[r];
             }
+            if (lane == 63) sm.used = incl;
+        }
+        if (A.layer) {
+            __syncthreads();
+            const int used = sm.used;
+            for (int i = tid; i * 16 < used; i += NT) reinterpret_cast<uint4*>(sm.reg)[i] = src[i];
         }
     }
     __syncthreads();
@@ -409,7 +420,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
     if (KIND == WB_BITALLOC) {
         // clear the code area of the LDS copy; codes are OR-ed in, then copied out
         __syncthreads();
-        const int code_words = DK * DV * A.bbar / 32;
+        const int code_words = sm.used / 4;
         for (int i = tid; i < code_words; i += NT) sm.reg[i] = 0u;
         __syncthreads();
     }
@@ -582,8 +593,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     if (top) atomicOr(&sm.reg[wi + 2], top);
                 }
                 if (cg == 0) {
-                    const int code_bytes = DK * DV * A.bbar / 8;
-                    reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(sm.reg) + code_bytes)[row] = dbits;
+                    reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(sm.reg) + A.code_cap)[row] = dbits;
                 }
             }
             if (USE_SIDE) {
@@ -608,9 +618,12 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
     }
     if (KIND == WB_BITALLOC) {
         __syncthreads();
-        const int total = DK * DV * A.bbar / 8 + 2 * DK;     // codes + Delta (meta unchanged)
+        // codes up to the head's last row, then Delta (meta unchanged)
         uint4* dst = reinterpret_cast<uint4*>(region);
-        for (int i = tid; i * 16 < total; i += NT) dst[i] = reinterpret_cast<const uint4*>(sm.reg)[i];
+        const uint4* lds = reinterpret_cast<const uint4*>(sm.reg);
+        const int used = sm.used;
+        for (int i = tid; i * 16 < used; i += NT) dst[i] = lds[i];
+        for (int i = tid; i * 16 < 2 * DK; i += NT) dst[A.code_cap / 16 + i] = lds[A.code_cap / 16 + i];
     }
 }
 
@@ -650,24 +663,26 @@ __global__ void fill_kernel(uint8_t* dst, size_t n, uint4 p0, int period) {
         dst[i] = pat[i % period];
 }
 
-__global__ void init_bitalloc_kernel(uint8_t* state, uint64_t stride, int code_bytes, uint4 p0, int period,
-                                    int dk, uint8_t meta) {
+// codes of the zero state on [0, code_bytes) (the rest of the code area keeps the zero
+// fill), Delta = 0 and the meta bytes after the code area of `cap` bytes
+__global__ void init_bitalloc_kernel(uint8_t* state, uint64_t stride, int code_bytes, int cap, uint4 p0,
+                                     int period, int dk, uint8_t meta) {
     const uint8_t* pat = reinterpret_cast<const uint8_t*>(&p0);
     uint8_t* reg = state + (size_t)blockIdx.x * stride;
     for (int i = threadIdx.x; i < code_bytes; i += blockDim.x) reg[i] = pat[i % period];
-    for (int i = threadIdx.x; i < 2 * dk; i += blockDim.x) reg[code_bytes + i] = 0;
-    for (int i = threadIdx.x; i < dk; i += blockDim.x) reg[code_bytes + 2 * dk + i] = meta;
+    for (int i = threadIdx.x; i < 2 * dk; i += blockDim.x) reg[cap + i] = 0;
+    for (int i = threadIdx.x; i < dk; i += blockDim.x) reg[cap + 2 * dk + i] = meta;
 }
 
 }  // namespace
 
-hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes, const uint8_t* pattern,
-                                int period, int dk, uint8_t meta, hipStream_t stream) {
+hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes, int cap,
+                                const uint8_t* pattern, int period, int dk, uint8_t meta, hipStream_t stream) {
     uint4 p{0, 0, 0, 0};
     uint8_t* pb = reinterpret_cast<uint8_t*>(&p);
     for (int i = 0; i < period && i < 16; ++i) pb[i] = pattern[i];
-    hipLaunchKernelGGL(init_bitalloc_kernel, dim3(heads), dim3(256), 0, stream, state, stride, code_bytes, p, period,
-                       dk, meta);
+    hipLaunchKernelGGL(init_bitalloc_kernel, dim3(heads), dim3(256), 0, stream, state, stride, code_bytes, cap, p,
+                       period, dk, meta);
     return hipGetLastError();
 }
 
@@ -688,7 +703,7 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
             if (op == OP_STEP && rot_step_supported(d)) return launch_rot_step(d, a, stream);
             return launch_op<WB_MIXED, 128, 128>(op, d.mode, a, heads, stream);
         default:
-            if (op == OP_STEP && d.mode == WB_RTN) return launch_bitalloc_step(d, a, stream);
+            if (op == OP_STEP && d.mode == WB_RTN && d.budget == WB_BUDGET_HEAD) return launch_bitalloc_step(d, a, stream);
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
     }
 }

@@ -32,6 +32,8 @@ struct KArgs {
     int k_hi = 0;
     int bbar = 4;
     int mem_bits = 0;                 // k of direction / residual memory
+    int code_cap = 0;                 // BITALLOC code-area bytes of a head (meta follows)
+    int layer = 0;                    // BITALLOC layer budget: the used code bytes vary per head
     uint32_t* activity = nullptr;     // [B*H][8] write-activity counters (UNIFORM) or null
     uint8_t* votes = nullptr;         // [B*H][DK][DV] vote state, with `activity`
     float* est = nullptr;             // [B*H][2 DK + 4] online estimators (BITALLOC) or null
@@ -52,8 +54,9 @@ hipError_t launch_rot_step(const wb_layout_desc& d, const KArgs& a, hipStream_t 
 hipError_t launch_fill(void* dst, size_t n, const uint8_t* pattern, int period, hipStream_t stream);
 
 // Writes the zero state of every BITALLOC region: codes of width bbar holding level 0
-// (the `period`-byte pattern), Delta = 0 and the given meta byte.
-hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes,
+// (the `period`-byte pattern) on [0, code_bytes), Delta = 0 and the given meta byte
+// after the code area of `cap` bytes.
+hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes, int cap,
                                 const uint8_t* pattern, int period, int dk, uint8_t meta, hipStream_t stream);
 
 struct AllocArgs {
@@ -70,9 +73,16 @@ struct AllocArgs {
     uint64_t region_stride = 0;
     float r_default = 0.f;
     int bbar = 4, bmin = 2, bmax = 8;
+    // layer-wise budget: code-area bytes and the workspace of costs and widths
+    int code_cap = 0;
+    int H = 1;
+    double* ws_c = nullptr;           // [B*H*dk]
+    uint8_t* ws_w = nullptr;          // [B*H*dk]
 };
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
 hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
+// layer-wise budget: costs per head, widths per sequence, then fits and repack per head
+hipError_t launch_allocate_layer(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
 
 struct DampArgs {
     const float* samples = nullptr;   // [N][H][dk][dv]

@@ -31,6 +31,12 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
+// BITALLOC code-area bytes of one head: exactly the budget (per-head budget) or room
+// for every row at bmax (layer budget)
+size_t code_capacity(const wb_layout_desc& d) {
+    return size_t(d.dk) * d.dv * size_t(d.budget == WB_BUDGET_LAYER ? d.bmax : d.bbar) / 8;
+}
+
 size_t region_size(const wb_layout_desc& d) {
     const size_t dk = d.dk, dv = d.dv;
     switch (d.kind) {
@@ -41,8 +47,15 @@ size_t region_size(const wb_layout_desc& d) {
             const size_t qr = dk - size_t(d.k_hi);
             return size_t(d.k_hi) * dv * 2 + qr * dv + qr * (dv / d.block) * 4;
         }
-        default: return dk * dv * size_t(d.bbar) / 8 + 3 * dk;
+        default: return code_capacity(d) + 3 * dk;
     }
+}
+
+// workspace of the layer-wise allocation, after the regions: float64 costs and u8
+// widths of every row
+size_t layer_ws_size(const wb_layout_desc& d) {
+    if (d.kind != WB_BITALLOC || d.budget != WB_BUDGET_LAYER) return 0;
+    return round256(size_t(d.B) * d.H * d.dk * 9);
 }
 
 int validate(const wb_layout_desc* d) {
@@ -74,6 +87,8 @@ int validate(const wb_layout_desc* d) {
     if (d->kind == WB_BITALLOC) {
         if (d->bmin < 2 || d->bmin > d->bbar || d->bbar > d->bmax || d->bmax > 8) return WB_EUNSUPPORTED;
     }
+    if (d->budget != WB_BUDGET_HEAD && d->budget != WB_BUDGET_LAYER) return WB_EINVAL;
+    if (d->budget == WB_BUDGET_LAYER && (d->kind != WB_BITALLOC || d->H * d->dk > 4096)) return WB_EUNSUPPORTED;
     return WB_OK;
 }
 
@@ -98,6 +113,8 @@ wb::KArgs base_args(const wb_state* st) {
     a.k_hi = st->d.k_hi;
     a.bbar = st->d.bbar;
     a.mem_bits = st->d.mem_bits;
+    a.code_cap = int(code_capacity(st->d));
+    a.layer = st->d.kind == WB_BITALLOC && st->d.budget == WB_BUDGET_LAYER;
     return a;
 }
 
@@ -112,6 +129,7 @@ int state_bytes(const wb_layout_desc* d, size_t* state_bytes_out, size_t* side_b
     const size_t stride = round256(region_size(*d));
     size_t total = stride * size_t(d->B) * size_t(d->H);
     if (d->kind == WB_MIXED) total += round256(size_t(d->H) * d->dk);
+    total += layer_ws_size(*d);
     *state_bytes_out = total;
     *side_bytes_out = side_size(*d);
     return WB_OK;
@@ -171,8 +189,8 @@ int state_alloc(const wb_layout_desc* d, void* dev_state, size_t state_bytes_in,
         for (int i = 0; i < bb; ++i) pat[i] = uint8_t(fields >> (8 * i));
         const int code_bytes = d->dk * d->dv * bb / 8;
         const uint8_t meta = uint8_t((bb - 1) | (15 << 4));
-        e = wb::launch_init_bitalloc(st->state, st->region_stride, d->B * d->H, code_bytes, pat, bb, d->dk,
-                                     meta, s);
+        e = wb::launch_init_bitalloc(st->state, st->region_stride, d->B * d->H, code_bytes, int(code_capacity(*d)),
+                                     pat, bb, d->dk, meta, s);
     }
     if (e == hipSuccess && st->side) e = wb::launch_fill(st->side, need_side, &zero, 1, s);
     if (e == hipSuccess && st->perm_dev) {
@@ -259,18 +277,26 @@ int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor
     a.est = s ? nullptr : st->est;
     a.factor = factor;
     a.cadence = C;
+    a.code_cap = int(code_capacity(st->d));
     a.region_stride = st->region_stride;
     a.r_default = float(1.0 / (3.0 * st->d.dk));
     a.bbar = st->d.bbar;
     a.bmin = st->d.bmin;
     a.bmax = st->d.bmax;
+    if (st->d.budget == WB_BUDGET_LAYER) {
+        a.H = st->d.H;
+        a.ws_c = reinterpret_cast<double*>(st->state + st->regions_bytes);
+        a.ws_w = st->state + st->regions_bytes + size_t(st->d.B) * st->d.H * st->d.dk * 8;
+        return hip_status(wb::launch_allocate_layer(st->d, a, static_cast<hipStream_t>(stream)));
+    }
     return hip_status(wb::launch_allocate_bits(st->d, a, static_cast<hipStream_t>(stream)));
 }
 
 int state_step_decode_alloc(wb_state* st, const float* q, const float* k, const float* v, const float* beta,
                             const float* s, float* o, int factor, int C, void* stream) {
     if (!st || !q || !k || !v || !beta || !s || !o) return WB_EINVAL;
-    if (st->d.kind != WB_BITALLOC || st->d.mode != WB_RTN) return WB_EUNSUPPORTED;
+    if (st->d.kind != WB_BITALLOC || st->d.mode != WB_RTN || st->d.budget != WB_BUDGET_HEAD)
+        return WB_EUNSUPPORTED;
     if (factor < WB_GAMMA_ERASURE || factor > WB_GAMMA_HC || C < 1) return WB_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(beta) || !aligned4(s))
         return WB_EALIGN;
@@ -291,6 +317,7 @@ int state_step_decode_alloc(wb_state* st, const float* q, const float* k, const 
     a.sd = s;
     a.o = o;
     a.s_per_row = st->d.decay == WB_DECAY_PER_ROW;
+    a.code_cap = int(code_capacity(st->d));
     return hip_status(wb::launch_step_allocate(st->d, a, static_cast<hipStream_t>(stream)));
 }
 

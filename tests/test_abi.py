@@ -89,6 +89,18 @@ def test_descriptor_validation():
         assert _code(d) == 0
         assert wb.buffer_sizes(d)[1] == 2 * 3 * 128 * 128 * 4
         assert _code(wb.make_desc("bitalloc", mode, 1, 1, mem_bits=2)) == -3
+    # layer-wise width budget: BITALLOC only, at most 4096 rows per sequence; regions
+    # sized for every row at bmax, then the allocation workspace (float64 cost and u8
+    # width per row)
+    assert _code(wb.make_desc("bitalloc", "rtn", 1, 1, budget=2)) == -1
+    assert _code(wb.make_desc("mixed", "rtn", 1, 1, budget="layer")) == -3
+    assert _code(wb.make_desc("bitalloc", "rtn", 1, 33, budget="layer")) == -3
+    d = wb.make_desc("bitalloc", "rtn", 3, 32, budget="layer", bbar=4, bmax=6)
+    assert _code(d) == 0
+    stride = -(-(128 * 128 * 6 // 8 + 3 * 128) // 256) * 256
+    assert wb.buffer_sizes(d)[0] == 3 * 32 * stride + -(-(3 * 32 * 128 * 9) // 256) * 256
+    d = wb.make_desc("bitalloc", "rtn", 3, 32, bbar=4, bmax=6)
+    assert wb.buffer_sizes(d)[0] == 3 * 32 * -(-(128 * 128 * 4 // 8 + 3 * 128) // 256) * 256
 
 
 def test_alloc_rejects_bad_buffers_without_touching_the_gpu():

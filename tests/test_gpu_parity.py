@@ -35,7 +35,7 @@ def _state(lay, perm=None):
     wb = _wb()
     return wb.WriteBackState(lay.kind, lay.mode, lay.B, lay.H, lay.dk, lay.dv, lay.per_row_decay,
                              bits=lay.bits, block=lay.block, k_hi=lay.k_hi, bbar=lay.bbar, bmin=lay.bmin,
-                             bmax=lay.bmax, seed=lay.seed, perm=perm, mem_bits=lay.mem_bits)
+                             bmax=lay.bmax, seed=lay.seed, perm=perm, mem_bits=lay.mem_bits, budget=lay.budget)
 
 
 def _warm_state(rng, B, H, dk, dv):
@@ -183,7 +183,7 @@ def test_tiny_fp32_identity():
 CASES = [
     (L.FP32, {}), (L.UNIFORM, {"bits": 4}), (L.UNIFORM, {"bits": 2}), (L.UNIFORM, {"bits": 8}),
     (L.HAD_INT8, {"block": 128}), (L.HAD_INT8, {"block": 32}), (L.MIXED, {"block": 32, "k_hi": 16}),
-    (L.BITALLOC, {}),
+    (L.BITALLOC, {}), (L.BITALLOC, {"budget": "layer"}),
 ]
 
 
@@ -205,6 +205,15 @@ def test_bitalloc_after_allocation_rtn_and_sr():
     for mode in ("rtn", "sr"):
         lay = _layout(L.BITALLOC, mode, 2, 2, 128)
         run_decode(lay, 7, warm=True, seed=13, alloc_every=3)
+
+
+@pytest.mark.parametrize("mode", ["rtn", "ef"])
+def test_bitalloc_layer_budget_decode_after_allocation(mode):
+    """Decode steps on heads whose widths differ under the layer-wise budget (each
+    head's codes end at its own length inside the code area)."""
+    print(f"\n[case] layer-budget BITALLOC decode {mode}", flush=True)
+    lay = _layout(L.BITALLOC, mode, 2, 4, 128, budget="layer")
+    run_decode(lay, 7, warm=True, seed=17, alloc_every=3)
 
 
 # ---------------------------------------------------------------------------- import / export
@@ -542,6 +551,65 @@ def test_decode_step_with_allocation(case):
     print("[tally]", tally.summary(), "rows left out of the code comparison:", skipped, flush=True)
     assert tally.ok(), tally.summary()
     assert skipped <= 0.01 * T * B * H * dk
+
+
+@pytest.mark.parametrize("case", ["warm", "spread"])
+def test_allocate_bits_layer_budget_matches_oracle(case):
+    """The layer-wise allocation (costs per head, widths over every row of a sequence,
+    fits and repack per head) against the oracle on two passes, the second with the
+    decays reversed across rows and the states of half the heads scaled down, from the
+    widths the first pass left; whole regions compared (the code area is zero after
+    each head's last row)."""
+    from oracle.step import allocate_layer_regions
+    print(f"\n[case] allocate_bits layer budget {case} B=2 H=8", flush=True)
+    B, H, dk = 2, 8, 128
+    lay = _layout(L.BITALLOC, "rtn", B, H, dk, budget="layer")
+    rng = np.random.default_rng(37)
+    st = _state(lay)
+    S, s = _alloc_case(case, rng, B, H, dk)
+    # heads of a sequence differ: decays shifted per head
+    s = (s * np.exp(rng.uniform(-2.0, 1.0, (B, H, 1)))).astype(np.float32)
+    st.quantize(_to_dev(S))
+    r = np.full((B, H, dk), 1.0 / (3 * dk), dtype=np.float32)
+    spread = 0
+    for pas, s_pass in enumerate((s, np.ascontiguousarray(s[..., ::-1]))):
+        if pas == 1:
+            torch.cuda.synchronize()
+            out = torch.zeros((B, H, dk, dk), dtype=torch.float32, device="cuda")
+            st.dequant(out)
+            out[:, ::2] *= 0.01
+            st.quantize(out.contiguous())
+        torch.cuda.synchronize()
+        before = st.regions().cpu().numpy()
+        st.allocate_bits(_to_dev(s_pass), _to_dev(r))
+        torch.cuda.synchronize()
+        after = st.regions().cpu().numpy()
+        for b in range(B):
+            regs_in = [before[b * H + h][: lay.region_size()] for h in range(H)]
+            orc, allocs = allocate_layer_regions(lay, regs_in, [s_pass[b, h].astype(np.float64) for h in range(H)],
+                                                 [r[b, h].astype(np.float64) for h in range(H)])
+            g_w = [L.decode_region(lay, after[b * H + h][: lay.region_size()]).widths for h in range(H)]
+            assert sum(int(w.sum()) for w in g_w) == lay.bbar * H * dk
+            sums = [int(w.sum()) for w in g_w]
+            spread = max(spread, max(sums) - min(sums))
+            for h in range(H):
+                reg_gpu = after[b * H + h][: lay.region_size()]
+                o_w = allocs[h]["widths"]
+                if not np.array_equal(g_w[h], o_w):
+                    bad = np.argwhere(g_w[h] != o_w).ravel()
+                    frac = np.abs(allocs[h]["bstar"][bad] - np.floor(allocs[h]["bstar"][bad]) - 0.5)
+                    assert np.all(frac < 1e-5), (pas, b, h, bad, allocs[h]["bstar"][bad])
+                    continue
+                g = L.decode_region(lay, reg_gpu)
+                o = L.decode_region(lay, orc[h])
+                if not np.array_equal(g.fit, o.fit):
+                    for i in np.argwhere(g.fit != o.fit).ravel():
+                        e = allocs[h]["fit_err"][i]
+                        assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (pas, b, h, i)
+                    continue
+                assert np.array_equal(reg_gpu, orc[h]), (pas, b, h)
+    print(f"[alloc-layer] largest difference of head bit totals within a sequence: {spread}", flush=True)
+    assert spread > 0
 
 
 def test_allocation_then_decode_full_budget_zero_state():
