@@ -154,6 +154,54 @@ def allocate_layer(Ys, s_rows, r_rows, bbar=4, bmin=2, bmax=8, factor=GAMMA_ERAS
     return out
 
 
+def allocate_heads(Ys, s_rows, r_rows, bbar=4, bmin=2, bmax=8, factor=GAMMA_ERASURE, C=1, group=32):
+    """One width per head for the heads of one sequence's layer ([LBRS] "Allocation
+    units": per-head decay and normalisation give each head one width and block scales;
+    R~ = 1, so decay alone sets the widths; "at layer-wise mean budget"). Reading: under
+    one width the head's proxy cost is sum_i c_i 2^{-2b} with c_i = Gamma_i (R~ = 1), so
+    the head's cost is c_h = sum_i Gamma_i (kept in [1e-300, 1e300]); widths by the same
+    rule as rows (geometric mean, rounding, clip, one-bit adjustments over the heads, ties
+    to the lower head). Then for each scale group (``group`` rows of one column): the
+    clipping fit over the 16 fractions at the head's new width, Delta = f16(f R / n) and
+    the nearest levels. Returns widths [H], and per head fit / delta [dk/group][dv] and
+    kappa [dk][dv]."""
+    H = len(Ys)
+    c = np.zeros(H)
+    for h in range(H):
+        with np.errstate(divide="ignore"):
+            G = persistence_factor(s_rows[h], r_rows[h], factor, C)
+        c[h] = min(float(np.sum(G)), C_CAP)
+    bstar = real_widths(c, bbar)
+    b = integer_widths(c, bstar, bbar, bmin, bmax)
+    fits, deltas, kappas, errs = [], [], [], []
+    for h in range(H):
+        Y = np.asarray(Ys[h], np.float64)
+        dk, dv = Y.shape
+        ng = dk // group
+        n = levels_n(int(b[h]))
+        fk = np.zeros((ng, dv), np.int64)
+        dl = np.zeros((ng, dv))
+        er = np.zeros((ng, dv, 16))
+        for g in range(ng):
+            for j in range(dv):
+                x = Y[g * group:(g + 1) * group, j]
+                R = float(np.max(np.abs(x)))
+                fk[g, j], er[g, j] = fit_row(x, R, int(b[h]))
+                dl[g, j] = float(f16(fit_fraction(int(fk[g, j])) * R / n))
+        kap = np.zeros((dk, dv), np.int64)
+        for g in range(ng):
+            for j in range(dv):
+                x = Y[g * group:(g + 1) * group, j]
+                kap[g * group:(g + 1) * group, j] = (np.zeros(group, np.int64) if dl[g, j] == 0.0 else
+                                                     np.clip(rne(x / dl[g, j]), -n, n).astype(np.int64))
+        fits.append(fk)
+        deltas.append(dl)
+        kappas.append(kap)
+        errs.append(er)
+    return {"widths": b, "bstar": bstar, "c": np.maximum(c, C_FLOOR), "fit": fits, "delta": deltas,
+            "kappa": kappas, "fit_err": errs}
+
+
 def default_r(dk: int) -> float:
     """Closed form of r_i for the synthetic stream: beta ~ U(0,1) and unit keys of
     isotropic direction give E[beta (2 - beta)] = 2/3 and E[k_i^2] = 1/dk, so

@@ -27,6 +27,12 @@ BITALLOC  decay-aware per-row widths ([LBRS] "State bit allocation", "Levels and
           the budget is per layer (a head's widths may sum to anything up to bmax*dk;
           the bytes after its last row are zero); then f16 Delta [dk]; then u8 meta
           [dk] = (b_i - 1) | (k_i << 4), k_i the clipping-fit index.
+HEADALLOC per-head widths with block scales ([LBRS] "Allocation units": for per-head
+          decay and normalisation one width per head and a scale per block of 32 key
+          channels; "Levels and storage"): element (i, j) at bits [(i dv + j) b, +b)
+          as kappa + n, n = 2^(b-1) - 1, in a code area of dk*dv*bmax/8 bytes (zero after
+          the last element); then f16 Delta [dk/32][dv] (one per 32 rows of a column);
+          then u8 clipping-fit index [dk/32][dv]; then u8 (b - 1) and 15 zero bytes.
 """
 from __future__ import annotations
 
@@ -37,8 +43,9 @@ import numpy as np
 from .hadamard import sylvester
 from .numerics import f16_bits, f16_value, pack_fields, unpack_fields
 
-FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC = "fp32", "uniform", "had_int8", "mixed", "bitalloc"
-KINDS = (FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC)
+FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC, HEADALLOC = "fp32", "uniform", "had_int8", "mixed", "bitalloc", "headalloc"
+KINDS = (FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC, HEADALLOC)
+HA_GROUP = 32              # HEADALLOC: key channels (rows) per scale group
 
 
 @dataclass
@@ -67,7 +74,9 @@ class Layout:
 
     @property
     def code_capacity(self) -> int:
-        """BITALLOC code-area bytes of one head."""
+        """BITALLOC / HEADALLOC code-area bytes of one head."""
+        if self.kind == HEADALLOC:
+            return self.dk * self.dv * self.bmax // 8
         return self.dk * self.dv * (self.bmax if self.budget == "layer" else self.bbar) // 8
 
     def region_size(self) -> int:
@@ -83,6 +92,9 @@ class Layout:
             return self.k_hi * dv * 2 + q * dv + q * (dv // self.block) * 4
         if self.kind == BITALLOC:
             return self.code_capacity + 2 * dk + dk
+        if self.kind == HEADALLOC:
+            ng = dk // HA_GROUP
+            return self.code_capacity + 3 * ng * dv + 16
         raise ValueError(self.kind)
 
     def region_stride(self) -> int:
@@ -113,6 +125,7 @@ class Content:
     widths: np.ndarray | None = None     # BITALLOC b_i
     fit: np.ndarray | None = None        # BITALLOC k_i
     delta: np.ndarray | None = None      # BITALLOC f16 Delta values
+    width: int | None = None             # HEADALLOC b of the head
     delta_bits: np.ndarray | None = None
 
 
@@ -158,6 +171,14 @@ def decode_region(lay: Layout, region: np.ndarray) -> Content:
             off += nbytes
         return Content(kappa=kappa, widths=widths, fit=fit, delta=f16_value(dbits),
                        delta_bits=dbits)
+    if lay.kind == HEADALLOC:
+        ng = dk // HA_GROUP
+        cap = lay.code_capacity
+        dbits = r[cap: cap + 2 * ng * dv].view(np.uint16).reshape(ng, dv).copy()
+        fit = r[cap + 2 * ng * dv: cap + 3 * ng * dv].astype(np.int64).reshape(ng, dv)
+        b = int(r[cap + 3 * ng * dv]) + 1
+        u = unpack_fields(r[: dk * dv * b // 8], b, dk * dv).reshape(dk, dv)
+        return Content(kappa=u - (2 ** (b - 1) - 1), width=b, fit=fit, delta=f16_value(dbits), delta_bits=dbits)
     raise ValueError(lay.kind)
 
 
@@ -203,6 +224,17 @@ def encode_region(lay: Layout, c: Content) -> np.ndarray:
         meta = (np.asarray(c.widths, np.int64) - 1) | (np.asarray(c.fit, np.int64) << 4)
         out[cbytes + 2 * dk: cbytes + 3 * dk] = meta.astype(np.uint8)
         return out
+    if lay.kind == HEADALLOC:
+        ng = dk // HA_GROUP
+        cap = lay.code_capacity
+        b = int(c.width)
+        data = pack_fields(np.asarray(c.kappa, dtype=np.int64).reshape(-1) + (2 ** (b - 1) - 1), b)
+        assert data.size <= cap
+        out[: data.size] = data
+        out[cap: cap + 2 * ng * dv] = np.asarray(c.delta_bits, np.uint16).reshape(-1).view(np.uint8)
+        out[cap + 2 * ng * dv: cap + 3 * ng * dv] = np.asarray(c.fit, np.int64).reshape(-1).astype(np.uint8)
+        out[cap + 3 * ng * dv] = b - 1
+        return out
     raise ValueError(lay.kind)
 
 
@@ -229,6 +261,8 @@ def stored_values(lay: Layout, c: Content) -> np.ndarray:
         return np.concatenate([f16_value(c.hi_bits), y], axis=0)
     if lay.kind == BITALLOC:
         return c.kappa.astype(np.float64) * c.delta[:, None]
+    if lay.kind == HEADALLOC:
+        return c.kappa.astype(np.float64) * np.repeat(c.delta, HA_GROUP, axis=0)
     raise ValueError(lay.kind)
 
 
@@ -282,10 +316,15 @@ def initial_region(lay: Layout) -> np.ndarray:
         c = Content(kappa=np.zeros((dk, dv), np.int64), widths=np.full(dk, lay.bbar),
                     fit=np.full(dk, 15), delta_bits=np.zeros(dk, np.uint16))
         return encode_region(lay, c)
+    if lay.kind == HEADALLOC:
+        ng = dk // HA_GROUP
+        c = Content(kappa=np.zeros((dk, dv), np.int64), width=lay.bbar, fit=np.full((ng, dv), 15),
+                    delta_bits=np.zeros((ng, dv), np.uint16))
+        return encode_region(lay, c)
     return np.zeros(lay.region_size(), dtype=np.uint8)
 
 
-__all__ = ["Layout", "Content", "decode_region", "encode_region", "stored_values",
+__all__ = ["Layout", "Content", "decode_region", "encode_region", "stored_values", "HEADALLOC", "HA_GROUP",
            "to_logical", "to_stored", "rotated_rows", "initial_region", "f16_bits",
            "KINDS", "FP32", "UNIFORM", "HAD_INT8", "MIXED", "BITALLOC",
            "bits_per_value_stored"]

@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import layouts as L
-from .allocation import allocate_head, allocate_layer
+from .allocation import allocate_head, allocate_heads, allocate_layer
 from .numerics import f16, f16_bits
 from .philox import sr_draws
 from .quantizers import (DIR, EF, RESQ, SR, affine_metadata, affine_round, levels_n, row_step,
@@ -155,6 +155,28 @@ def write_back(lay: L.Layout, X: np.ndarray, e_in, t: int, b: int, h: int,
         wb.meta_pre = {"delta": dpre, "R": R}
         wb.meta = {"delta": delta}
         wb.region = L.encode_region(lay, c)
+    elif lay.kind == L.HEADALLOC:
+        # the head's width and each group's fit index stay; Delta of a group (32 rows
+        # of one column) from its maximum
+        bw, fits = int(prev.width), prev.fit
+        G = L.HA_GROUP
+        ng = dk // G
+        n = levels_n(bw)
+        Rg = np.max(np.abs(X.reshape(ng, G, dv)), axis=1)
+        delta = np.zeros((ng, dv))
+        dpre = np.zeros((ng, dv))
+        for g in range(ng):
+            for j in range(dv):
+                delta[g, j], dpre[g, j] = row_step(Rg[g, j], bw, int(fits[g, j]))
+        if meta_override is not None:
+            delta = meta_override["delta"]
+        r16 = _draws(lay, b, h, t, range(dk)) if mode == SR else None
+        rr = sym_round(X, np.repeat(delta, G, axis=0), n, mode, e, r16)
+        kappa, tau, bnd, e_new = rr.kappa, rr.tau, rr.boundary, rr.e_new
+        c = L.Content(kappa=kappa, width=bw, fit=fits, delta_bits=f16_bits(delta))
+        wb.meta_pre = {"delta": dpre, "R": Rg}
+        wb.meta = {"delta": delta}
+        wb.region = L.encode_region(lay, c)
     else:
         raise ValueError(lay.kind)
     wb.tau, wb.boundary = tau, bnd
@@ -216,6 +238,20 @@ def allocate_layer_regions(lay: L.Layout, regions, s_rows, r_rows, factor="erasu
     Ys = [L.stored_values(lay, L.decode_region(lay, reg)) for reg in regions]
     allocs = allocate_layer(Ys, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C)
     return [_round_at(lay, Ys[h], allocs[h]) for h in range(len(regions))], allocs
+
+
+def allocate_headalloc_regions(lay: L.Layout, regions, s_rows, r_rows, factor="erasure", C=1):
+    """The allocation pass over the H heads of one sequence for the per-head unit
+    (HEADALLOC): one width per head from decay alone, clipping fits per scale group at
+    the new width, the stored values re-rounded (nearest)."""
+    Ys = [L.stored_values(lay, L.decode_region(lay, reg)) for reg in regions]
+    al = allocate_heads(Ys, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C, L.HA_GROUP)
+    out = []
+    for h, Y in enumerate(Ys):
+        c = L.Content(kappa=al["kappa"][h], width=int(al["widths"][h]), fit=al["fit"][h],
+                      delta_bits=f16_bits(al["delta"][h]))
+        out.append(L.encode_region(lay, c))
+    return out, al
 
 
 def decode_step_alloc(lay: L.Layout, region, q, k, v, beta, s, s_rows, r_rows, factor="erasure", C=1):
