@@ -60,6 +60,11 @@ def test_encode_decode_roundtrip(kind):
                       scale_bits=f16_bits(rng.random((nq, nb))),
                       zero_bits=f16_bits(rng.standard_normal((nq, nb))),
                       hi_bits=f16_bits(rng.standard_normal((la.k_hi, dv))) if kind == L.MIXED else None)
+    elif kind == L.HEADALLOC:
+        b = 5
+        ng = dk // L.HA_GROUP
+        c = L.Content(kappa=rng.integers(-(2 ** (b - 1) - 1), 2 ** (b - 1), (dk, dv)), width=b,
+                      fit=rng.integers(0, 16, (ng, dv)), delta_bits=f16_bits(rng.random((ng, dv))))
     else:
         w = np.full(dk, 4)
         w[:8] = [2, 8, 3, 5, 6, 2, 3, 3]        # sums to 32: same as eight rows of 4
@@ -165,6 +170,9 @@ def test_step_rounds_within_half_a_step(kind, mode):
         step[q0:] += 2 * zero_err
         if kind == L.MIXED:
             step[:q0] = np.abs(r.wb.X[:q0]) * 2 ** -10 + 2 ** -24
+    elif kind == L.HEADALLOC:
+        c = L.decode_region(la, r.wb.region)
+        step = np.repeat(c.delta, L.HA_GROUP, axis=0)
     else:
         c = L.decode_region(la, r.wb.region)
         step = np.repeat(c.delta[:, None], dv, axis=1)
@@ -174,9 +182,11 @@ def test_step_rounds_within_half_a_step(kind, mode):
     if kind == L.BITALLOC:
         n = (2 ** (c.widths - 1) - 1)[:, None]
         unclipped &= np.abs(r.wb.X) <= n * step
+    if kind == L.HEADALLOC:
+        unclipped &= np.abs(r.wb.X) <= (2 ** (c.width - 1) - 1) * step
     bound = step * (1.0 if mode == "sr" else 0.5) + (step if mode == "ef" else 0)
     assert np.all(err[unclipped] <= bound[unclipped] * (1 + 1e-9) + 1e-12)
-    assert rot.sum() == (0 if kind in (L.FP32, L.UNIFORM, L.BITALLOC) else la.int8_rows)
+    assert rot.sum() == (0 if kind in (L.FP32, L.UNIFORM, L.BITALLOC, L.HEADALLOC) else la.int8_rows)
 
 
 def test_prefill_with_cadence_one_equals_decode_steps():
