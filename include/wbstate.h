@@ -82,6 +82,12 @@ extern "C" {
 #define WB_HAD_INT8 2  /* Hadamard rows, per-block asymmetric affine INT8 */
 #define WB_MIXED 3     /* k_hi float16 rows + Hadamard INT8 rows, static permutation */
 #define WB_BITALLOC 4  /* decay-aware per-row widths, packed mixed-width codes */
+#define WB_HEADALLOC 5 /* decay-aware per-head width, a float16 scale per 32 key channels of a
+                        * column ([LBRS] "Allocation units"): element (i, j) at bits
+                        * [(i dv + j) b, +b) as kappa + n, n = 2^(b-1) - 1, in a code area of
+                        * dk*dv*bmax/8 bytes; then f16 Delta [dk/32][dv]; then u8 clipping-fit
+                        * index [dk/32][dv]; then u8 (b - 1) and 15 zero bytes. Widths are
+                        * budgeted over the heads of a sequence (budget must be 0). */
 
 /* write-back rules ([WB] "Post-training write-back interventions and diagnostics";
  * [WB-zh] "Error feedback and stochastic rounding"). FP32 ignores the rule.

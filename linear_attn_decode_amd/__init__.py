@@ -16,8 +16,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwbstate.so")
 
 # layout kinds, write-back rules and decay kinds (values of include/wbstate.h)
-FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC = 0, 1, 2, 3, 4
-KIND_NAMES = {"fp32": FP32, "uniform": UNIFORM, "had_int8": HAD_INT8, "mixed": MIXED, "bitalloc": BITALLOC}
+FP32, UNIFORM, HAD_INT8, MIXED, BITALLOC, HEADALLOC = 0, 1, 2, 3, 4, 5
+KIND_NAMES = {"fp32": FP32, "uniform": UNIFORM, "had_int8": HAD_INT8, "mixed": MIXED, "bitalloc": BITALLOC,
+              "headalloc": HEADALLOC}
 RTN, SR, EF, DIR, RESQ = 0, 1, 2, 3, 4
 MODE_NAMES = {"rtn": RTN, "sr": SR, "ef": EF, "dir": DIR, "resq": RESQ}
 GAMMA_CODES = {"erasure": 0, "w1": 1, "hC": 2}
@@ -220,6 +221,8 @@ class WriteBackState:
             tail = r256(self.H * self.dk)
         elif self.desc.kind == BITALLOC and self.desc.budget == BUDGET_CODES["layer"]:
             tail = r256(self.B * self.H * self.dk * 9)
+        elif self.desc.kind == HEADALLOC:
+            tail = r256(self.B * self.H * 9)
         return (self.state.numel() - tail) // (self.B * self.H)
 
     def regions(self):

@@ -633,7 +633,7 @@ __device__ __forceinline__ int block_sum_i32(int v, LayerSmem& sm, int& ph) {
 __global__ void __launch_bounds__(LNT) layer_widths_kernel(const AllocArgs A) {
     __shared__ LayerSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = A.H * DK;
+    const int n = A.rows_per_seq;
     const int rpt = (n + LNT - 1) / LNT;
     const int row0 = min(tid * rpt, n), row1 = min(row0 + rpt, n);
     const size_t base = (size_t)blockIdx.x * n;
@@ -750,6 +750,125 @@ __global__ void __launch_bounds__(LNT) layer_widths_kernel(const AllocArgs A) {
     for (int r = row0; r < row1; ++r) A.ws_w[base + r] = sm.bw[r];
 }
 
+// ---------------------------------------------------------------------------------
+// Per-head allocation unit (HEADALLOC; [LBRS] "Allocation units": per-head decay and
+// normalisation give each head one width and a scale per block of 32 key channels,
+// R~ = 1, so decay alone sets the widths). The head's cost is the sum of its rows'
+// persistence factors (under one width its proxy cost is sum_i Gamma_i 2^{-2b});
+// the widths over the heads of a sequence come from layer_widths_kernel.
+__global__ void __launch_bounds__(64) head_cost_kernel(const AllocArgs A) {
+    const int head = blockIdx.x, lane = threadIdx.x;
+    const size_t base = (size_t)head * DK;
+    double g = 0.0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int row = 2 * lane + k;
+        double s, q;
+        bool flat = false;
+        if (A.s) {
+            s = A.s[base + row];
+            q = A.r ? double(A.r[base + row]) : double(A.r_default);
+        } else {
+            const float* e = A.est + (size_t)head * est_stride(DK);
+            const double W = e[2 * DK];
+            flat = !(W > 0.0);
+            s = -0.5 * log1p(-double(e[row]) / W);
+            q = 0.5 * double(e[DK + row]) / W;
+        }
+        g += flat ? 1.0 : persistence(A.factor, A.cadence, s, q);
+    }
+    g = wave_sum_f64<1>(g);
+    if (lane == 0) A.ws_c[head] = fmin(g, 1e300);
+}
+
+constexpr int HNG = DK / 32;                   // scale groups (32 rows) per column
+
+struct HeadPackSmem {
+    uint32_t old_codes[DK * DV / 4 + 4];
+    uint32_t new_codes[DK * DV / 4 + 4];
+    uint16_t scale[HNG * DV];
+    uint8_t fit[HNG * DV];
+    int old_width;
+};
+
+// Repack one head at the width the sequence pass chose: for each group (32 rows of one
+// column, one thread) the clipping fit over f_k = 1/4 + k/20 at the new width (smallest
+// squared error, ties to the larger f), Delta = f16(f R / n), the nearest levels.
+__global__ void __launch_bounds__(NT) headalloc_pack_kernel(const AllocArgs A) {
+    __shared__ HeadPackSmem sm;
+    const int tid = threadIdx.x;
+    const int head = blockIdx.x;
+    uint8_t* region = A.state + (size_t)head * A.region_stride;
+    const int cap = A.code_cap;
+    if (tid == 0) sm.old_width = int(region[cap + 3 * HNG * DV]) + 1;
+    for (int i = tid; i < HNG * DV / 8; i += NT)
+        reinterpret_cast<uint4*>(sm.scale)[i] = reinterpret_cast<const uint4*>(region + cap)[i];
+    for (int i = tid; i < DK * DV / 4 + 4; i += NT) sm.new_codes[i] = 0u;
+    __syncthreads();
+    const int bo = sm.old_width, bn = int(A.ws_w[head]);
+    const int old_used = DK * DV * bo / 8, new_used = DK * DV * bn / 8;
+    for (int i = tid; i * 16 < old_used; i += NT)
+        reinterpret_cast<uint4*>(sm.old_codes)[i] = reinterpret_cast<const uint4*>(region)[i];
+    if (tid < 4) sm.old_codes[old_used / 4 + tid] = 0u;
+    __syncthreads();
+    const int no = (1 << (bo - 1)) - 1, nn = (1 << (bn - 1)) - 1;
+    for (int gi = tid; gi < HNG * DV; gi += NT) {
+        const int g = gi / DV, col = gi - g * DV;
+        const float dlo = f16_bits_to_f32(sm.scale[gi]);
+        float x[32];
+        float R = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 32; ++rr) {
+            const int bit = ((32 * g + rr) * DV + col) * bo;
+            const uint64_t w = uint64_t(sm.old_codes[bit >> 5]) | (uint64_t(sm.old_codes[(bit >> 5) + 1]) << 32);
+            const int field = int((w >> (bit & 31)) & ((1u << bo) - 1));
+            x[rr] = float(field - no) * dlo;                 // exact: |level| <= 127 times a float16
+            R = fmaxf(R, fabsf(x[rr]));
+        }
+        int best = 15;
+        float be = 0.f;
+        for (int k = 15; k >= 0; --k) {
+            const float d = f16_bits_to_f32(f64_to_f16_rto(kFit.f[k] * double(R) / double(nn)));
+            const float inv = d > 0.f ? 1.f / d : 0.f;
+            float e = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 32; ++rr) {
+                const float q = fminf(fmaxf(rintf(x[rr] * inv), -float(nn)), float(nn));
+                const float r = __builtin_fmaf(-d, q, x[rr]);
+                e = __builtin_fmaf(r, r, e);
+            }
+            if (k == 15 || e < be) {                          // ties keep the larger f
+                be = e;
+                best = k;
+            }
+        }
+        const uint16_t dbits = f64_to_f16_rto(kFit.f[best] * double(R) / double(nn));
+        const double d = double(f16_bits_to_f32(dbits));
+#pragma unroll
+        for (int rr = 0; rr < 32; ++rr) {
+            const int lev = d > 0.0 ? int(fmin(fmax(rint(double(x[rr]) / d), -double(nn)), double(nn))) : 0;
+            const uint32_t field = uint32_t(lev + nn);
+            const int bit = ((32 * g + rr) * DV + col) * bn;
+            const int sh = bit & 31;
+            atomicOr(&sm.new_codes[bit >> 5], field << sh);
+            if (sh + bn > 32) atomicOr(&sm.new_codes[(bit >> 5) + 1], field >> (32 - sh));
+        }
+        sm.scale[gi] = dbits;
+        sm.fit[gi] = uint8_t(best);
+    }
+    __syncthreads();
+    // codes up to the longer of the old and the new length (the rest stays zero), then
+    // the scales, the fit indices and the width
+    const int span = old_used > new_used ? old_used : new_used;
+    for (int i = tid; i * 16 < span; i += NT)
+        reinterpret_cast<uint4*>(region)[i] = reinterpret_cast<const uint4*>(sm.new_codes)[i];
+    for (int i = tid; i < HNG * DV / 8; i += NT)
+        reinterpret_cast<uint4*>(region + cap)[i] = reinterpret_cast<const uint4*>(sm.scale)[i];
+    for (int i = tid; i < HNG * DV / 16; i += NT)
+        reinterpret_cast<uint4*>(region + cap + 2 * HNG * DV)[i] = reinterpret_cast<const uint4*>(sm.fit)[i];
+    if (tid == 0) region[cap + 3 * HNG * DV] = uint8_t(bn - 1);
+}
+
 }  // namespace
 
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
@@ -759,6 +878,17 @@ hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hip
 
 hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(allocate_kernel<kStep>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_allocate_heads(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(head_cost_kernel, dim3(d.B * d.H), dim3(64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(layer_widths_kernel, dim3(d.B), dim3(LNT), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(headalloc_pack_kernel, dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -99,7 +99,11 @@ struct Smem {
     static constexpr bool ROT = KIND == WB_HAD_INT8 || KIND == WB_MIXED;
     using Real = typename std::conditional<ROT, double, float>::type;
     static constexpr int NQ = ROT ? 4 : 2;             // reduced quantities: uP, pP (, uQ, pQ)
-    static constexpr int BA_WORDS = (KIND == WB_BITALLOC) ? (DK * DV + 3 * DK) / 4 + 4 : 1;
+    // BITALLOC (and HEADALLOC, run by the same instantiations): codes up to 8 bits per
+    // value, then the larger of the two metadata blocks
+    static constexpr int HA_META = 3 * (DK / 32) * DV + 16;
+    static constexpr int BA_WORDS = (KIND == WB_BITALLOC) ? (DK * DV + (HA_META > 3 * DK ? HA_META : 3 * DK)) / 4 + 4 : 1;
+    static constexpr int HA_N = (KIND == WB_BITALLOC) ? (DK / 32) * DV : 1;
     Real k[DK], q[DK], a[DK];
     Real red[Shape<DK, DV>::NW][NQ][DV];
     Real vec[NQ][DV];
@@ -112,6 +116,9 @@ struct Smem {
     int off[KIND == WB_BITALLOC ? DK : 1];
     float delta[KIND == WB_BITALLOC ? DK : 1];
     int used;                       // BITALLOC code bytes of the head (sum of widths * DV / 8)
+    // HEADALLOC: group maxima per wavefront, then the groups' Delta
+    float gred[KIND == WB_BITALLOC ? 4 : 1][HA_N];
+    float gdelta[HA_N];
 };
 
 template <int KIND, int MODE, int OP, int DK, int DV>
@@ -157,7 +164,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
         // layer budget the metadata is staged first and the codes up to the head's
         // last row after the widths are known (below)
         const int code_bytes = A.code_cap;
-        const int total = code_bytes + 3 * DK;
+        const int total = code_bytes + (A.head_unit ? SM::HA_META : 3 * DK);
         const uint4* src = reinterpret_cast<const uint4*>(region);
         for (int i = A.layer ? code_bytes / 16 + tid : tid; i * 16 < total; i += NT) {
             reinterpret_cast<uint4*>(sm.reg)[i] = src[i];
@@ -172,7 +179,11 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             for (int r = 0; r < RPL; ++r) {
                 const int row = lane * RPL + r;
                 int wdt = 0;
-                if (row < DK) {
+                if (row < DK && A.head_unit) {
+                    // one width for the head; the group scales stay in the staged bytes
+                    wdt = int(bytes[code_bytes + 3 * (DK / 32) * DV]) + 1;
+                    sm.width[row] = wdt;
+                } else if (row < DK) {
                     const int meta = bytes[code_bytes + 2 * DK + row];
                     wdt = (meta & 7) + 1;
                     sm.width[row] = wdt;
@@ -285,10 +296,13 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                 if (sh) fld |= uint64_t(sm.reg[wi + 2]) << (64 - sh);
                 const float dl = sm.delta[row];
                 const uint64_t mask = (1ull << bw) - 1;
+                // HEADALLOC: the scale of (row / 32, column)
+                const uint16_t* gs = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sm.reg) +
+                                                                       A.code_cap) + (row >> 5) * DV + 8 * cg;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const int kap = int((fld >> (c * bw)) & mask) - n;
-                    x[m][c] = Real(float(kap) * dl);
+                    x[m][c] = Real(float(kap) * (A.head_unit ? f16_bits_to_f32(gs[c]) : dl));
                 }
             }
             if (USE_SIDE && OP == OP_STEP && !(KIND == WB_MIXED && m < mhi)) {
@@ -423,6 +437,41 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
         const int code_words = sm.used / 4;
         for (int i = tid; i < code_words; i += NT) sm.reg[i] = 0u;
         __syncthreads();
+        if constexpr (KIND == WB_BITALLOC && DK == 128) if (A.head_unit) {
+            // HEADALLOC: Delta of each group (32 rows of one column) from its maximum and
+            // its stored fit index. Rows rg + 16 m: the lane's rows of group g are m = 2g,
+            // 2g + 1; the group's other rows sit in the lanes 16 and 32 apart and in the
+            // other wavefronts.
+            constexpr int NGR = DK / 32;
+            float gm[NGR][8];
+#pragma unroll
+            for (int g = 0; g < NGR; ++g)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    float v = fmaxf(fabsf(float(x[2 * g][c])), fabsf(float(x[2 * g + 1][c])));
+                    auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                    v = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+                    auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                    gm[g][c] = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+                }
+            if (lane < 16) {
+#pragma unroll
+                for (int g = 0; g < NGR; ++g)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) sm.gred[wave][g * DV + 8 * cg + c] = gm[g][c];
+            }
+            __syncthreads();
+            const int n = (1 << (sm.width[0] - 1)) - 1;
+            uint8_t* lb = reinterpret_cast<uint8_t*>(sm.reg);
+            for (int i = tid; i < NGR * DV; i += NT) {
+                const float R = fmaxf(fmaxf(sm.gred[0][i], sm.gred[1][i]), fmaxf(sm.gred[2][i], sm.gred[3][i]));
+                const double f = 0.25 + double(lb[A.code_cap + 2 * NGR * DV + i]) / 20.0;
+                const uint16_t dbits = f64_to_f16_bits(f * double(R) / double(n));
+                sm.gdelta[i] = f16_bits_to_f32(dbits);
+                reinterpret_cast<uint16_t*>(lb + A.code_cap)[i] = dbits;      // for the write-back
+            }
+            __syncthreads();
+        }
     }
     // write activity of this lane (UNIFORM decode steps with counters attached): dead-zone,
     // level changes, votes, triggers, sub-threshold writes, same-sign and opposite-sign
@@ -569,18 +618,23 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             } else if (KIND == WB_BITALLOC) {
                 const int bw = sm.width[row];
                 const int n = (1 << (bw - 1)) - 1;
-                float R = 0.f;
+                uint16_t dbits = 0;
+                float dl = 0.f;
+                if (!A.head_unit) {
+                    float R = 0.f;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) R = fmaxf(R, fabsf(float(x[m][c])));
+                    for (int c = 0; c < 8; ++c) R = fmaxf(R, fabsf(float(x[m][c])));
 #pragma unroll
-                for (int d = 1; d < NCG; d <<= 1) R = fmaxf(R, xor_shfl(R, d));
-                const double f = 0.25 + double(sm.fit[row]) / 20.0;
-                const uint16_t dbits = f64_to_f16_bits(f * double(R) / double(n));
-                const float dl = f16_bits_to_f32(dbits);
+                    for (int d = 1; d < NCG; d <<= 1) R = fmaxf(R, xor_shfl(R, d));
+                    const double f = 0.25 + double(sm.fit[row]) / 20.0;
+                    dbits = f64_to_f16_bits(f * double(R) / double(n));
+                    dl = f16_bits_to_f32(dbits);
+                }
                 uint64_t fld = 0;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const int kap = round_rule<EMODE, float>(float(x[m][c]), e[m][c], dl, 0.f, -n, n, r16[c], &en[c]);
+                    const float dc = A.head_unit ? sm.gdelta[(row >> 5) * DV + 8 * cg + c] : dl;
+                    const int kap = round_rule<EMODE, float>(float(x[m][c]), e[m][c], dc, 0.f, -n, n, r16[c], &en[c]);
                     fld |= uint64_t(uint32_t(kap + n)) << (c * bw);
                 }
                 const int off = sm.off[row] + cg * bw;
@@ -592,7 +646,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     const uint32_t top = uint32_t(fld >> (64 - sh));
                     if (top) atomicOr(&sm.reg[wi + 2], top);
                 }
-                if (cg == 0) {
+                if (cg == 0 && !A.head_unit) {
                     reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(sm.reg) + A.code_cap)[row] = dbits;
                 }
             }
@@ -623,7 +677,8 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
         const uint4* lds = reinterpret_cast<const uint4*>(sm.reg);
         const int used = sm.used;
         for (int i = tid; i * 16 < used; i += NT) dst[i] = lds[i];
-        for (int i = tid; i * 16 < 2 * DK; i += NT) dst[A.code_cap / 16 + i] = lds[A.code_cap / 16 + i];
+        const int delta_bytes = A.head_unit ? 2 * (DK / 32) * DV : 2 * DK;
+        for (int i = tid; i * 16 < delta_bytes; i += NT) dst[A.code_cap / 16 + i] = lds[A.code_cap / 16 + i];
     }
 }
 
@@ -686,6 +741,26 @@ hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int 
     return hipGetLastError();
 }
 
+__global__ void init_headalloc_kernel(uint8_t* state, uint64_t stride, int code_bytes, int cap, uint4 p0,
+                                      int period, int groups, uint8_t wbyte) {
+    const uint8_t* pat = reinterpret_cast<const uint8_t*>(&p0);
+    uint8_t* reg = state + (size_t)blockIdx.x * stride;
+    for (int i = threadIdx.x; i < code_bytes; i += blockDim.x) reg[i] = pat[i % period];
+    for (int i = threadIdx.x; i < 2 * groups; i += blockDim.x) reg[cap + i] = 0;
+    for (int i = threadIdx.x; i < groups; i += blockDim.x) reg[cap + 2 * groups + i] = 15;
+    if (threadIdx.x == 0) reg[cap + 3 * groups] = wbyte;
+}
+
+hipError_t launch_init_headalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes, int cap,
+                                 const uint8_t* pattern, int period, int groups, uint8_t wbyte, hipStream_t stream) {
+    uint4 p{0, 0, 0, 0};
+    uint8_t* pb = reinterpret_cast<uint8_t*>(&p);
+    for (int i = 0; i < period && i < 16; ++i) pb[i] = pattern[i];
+    hipLaunchKernelGGL(init_headalloc_kernel, dim3(heads), dim3(256), 0, stream, state, stride, code_bytes, cap, p,
+                       period, groups, wbyte);
+    return hipGetLastError();
+}
+
 hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_t stream) {
     const int heads = d.B * d.H;
     const bool small = d.dk == 16;
@@ -702,6 +777,8 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
         case WB_MIXED:
             if (op == OP_STEP && rot_step_supported(d)) return launch_rot_step(d, a, stream);
             return launch_op<WB_MIXED, 128, 128>(op, d.mode, a, heads, stream);
+        case WB_HEADALLOC:
+            return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
         default:
             if (op == OP_STEP && d.mode == WB_RTN && d.budget == WB_BUDGET_HEAD) return launch_bitalloc_step(d, a, stream);
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);

@@ -34,6 +34,7 @@ struct KArgs {
     int mem_bits = 0;                 // k of direction / residual memory
     int code_cap = 0;                 // BITALLOC code-area bytes of a head (meta follows)
     int layer = 0;                    // BITALLOC layer budget: the used code bytes vary per head
+    int head_unit = 0;                // HEADALLOC (run by the BITALLOC kernels): one width, group scales
     uint32_t* activity = nullptr;     // [B*H][8] write-activity counters (UNIFORM) or null
     uint8_t* votes = nullptr;         // [B*H][DK][DV] vote state, with `activity`
     float* est = nullptr;             // [B*H][2 DK + 4] online estimators (BITALLOC) or null
@@ -58,6 +59,10 @@ hipError_t launch_fill(void* dst, size_t n, const uint8_t* pattern, int period, 
 // after the code area of `cap` bytes.
 hipError_t launch_init_bitalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes, int cap,
                                 const uint8_t* pattern, int period, int dk, uint8_t meta, hipStream_t stream);
+// The same for HEADALLOC regions: codes, `groups` zero f16 scales, fit index 15 per
+// group, the width byte.
+hipError_t launch_init_headalloc(uint8_t* state, uint64_t stride, int heads, int code_bytes, int cap,
+                                 const uint8_t* pattern, int period, int groups, uint8_t wbyte, hipStream_t stream);
 
 struct AllocArgs {
     uint8_t* state = nullptr;
@@ -76,13 +81,16 @@ struct AllocArgs {
     // layer-wise budget: code-area bytes and the workspace of costs and widths
     int code_cap = 0;
     int H = 1;
-    double* ws_c = nullptr;           // [B*H*dk]
-    uint8_t* ws_w = nullptr;          // [B*H*dk]
+    int rows_per_seq = 0;             // allocation units of a sequence: H*dk rows, or H heads
+    double* ws_c = nullptr;           // [B*rows_per_seq]
+    uint8_t* ws_w = nullptr;          // [B*rows_per_seq]
 };
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
 hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
 // layer-wise budget: costs per head, widths per sequence, then fits and repack per head
 hipError_t launch_allocate_layer(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
+// per-head unit (HEADALLOC): head costs, widths per sequence, then group fits and repack
+hipError_t launch_allocate_heads(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream);
 
 struct DampArgs {
     const float* samples = nullptr;   // [N][H][dk][dv]

@@ -34,7 +34,8 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // BITALLOC code-area bytes of one head: exactly the budget (per-head budget) or room
 // for every row at bmax (layer budget)
 size_t code_capacity(const wb_layout_desc& d) {
-    return size_t(d.dk) * d.dv * size_t(d.budget == WB_BUDGET_LAYER ? d.bmax : d.bbar) / 8;
+    const bool room = d.budget == WB_BUDGET_LAYER || d.kind == WB_HEADALLOC;
+    return size_t(d.dk) * d.dv * size_t(room ? d.bmax : d.bbar) / 8;
 }
 
 size_t region_size(const wb_layout_desc& d) {
@@ -47,6 +48,7 @@ size_t region_size(const wb_layout_desc& d) {
             const size_t qr = dk - size_t(d.k_hi);
             return size_t(d.k_hi) * dv * 2 + qr * dv + qr * (dv / d.block) * 4;
         }
+        case WB_HEADALLOC: return code_capacity(d) + 3 * (dk / 32) * dv + 16;
         default: return code_capacity(d) + 3 * dk;
     }
 }
@@ -54,13 +56,14 @@ size_t region_size(const wb_layout_desc& d) {
 // workspace of the layer-wise allocation, after the regions: float64 costs and u8
 // widths of every row
 size_t layer_ws_size(const wb_layout_desc& d) {
+    if (d.kind == WB_HEADALLOC) return round256(size_t(d.B) * d.H * 9);      // one "row" per head
     if (d.kind != WB_BITALLOC || d.budget != WB_BUDGET_LAYER) return 0;
     return round256(size_t(d.B) * d.H * d.dk * 9);
 }
 
 int validate(const wb_layout_desc* d) {
     if (!d) return WB_EINVAL;
-    if (d->kind < WB_FP32 || d->kind > WB_BITALLOC) return WB_EINVAL;
+    if (d->kind < WB_FP32 || d->kind > WB_HEADALLOC) return WB_EINVAL;
     if (d->mode < WB_RTN || d->mode > WB_RESQ) return WB_EINVAL;
     if (d->decay != WB_DECAY_PER_HEAD && d->decay != WB_DECAY_PER_ROW) return WB_EINVAL;
     const bool memory_rule = d->mode == WB_DIR || d->mode == WB_RESQ;
@@ -84,9 +87,10 @@ int validate(const wb_layout_desc* d) {
         const int rs = d->dk / 8;
         if (d->k_hi <= 0 || d->k_hi >= d->dk || d->k_hi % rs) return WB_EUNSUPPORTED;
     }
-    if (d->kind == WB_BITALLOC) {
+    if (d->kind == WB_BITALLOC || d->kind == WB_HEADALLOC) {
         if (d->bmin < 2 || d->bmin > d->bbar || d->bbar > d->bmax || d->bmax > 8) return WB_EUNSUPPORTED;
     }
+    if (d->kind == WB_HEADALLOC && d->H > 4096) return WB_EUNSUPPORTED;
     if (d->budget != WB_BUDGET_HEAD && d->budget != WB_BUDGET_LAYER) return WB_EINVAL;
     if (d->budget == WB_BUDGET_LAYER && (d->kind != WB_BITALLOC || d->H * d->dk > 4096)) return WB_EUNSUPPORTED;
     return WB_OK;
@@ -114,7 +118,8 @@ wb::KArgs base_args(const wb_state* st) {
     a.bbar = st->d.bbar;
     a.mem_bits = st->d.mem_bits;
     a.code_cap = int(code_capacity(st->d));
-    a.layer = st->d.kind == WB_BITALLOC && st->d.budget == WB_BUDGET_LAYER;
+    a.head_unit = st->d.kind == WB_HEADALLOC;
+    a.layer = (st->d.kind == WB_BITALLOC && st->d.budget == WB_BUDGET_LAYER) || a.head_unit;
     return a;
 }
 
@@ -192,6 +197,17 @@ int state_alloc(const wb_layout_desc* d, void* dev_state, size_t state_bytes_in,
         e = wb::launch_init_bitalloc(st->state, st->region_stride, d->B * d->H, code_bytes, int(code_capacity(*d)),
                                      pat, bb, d->dk, meta, s);
     }
+    if (e == hipSuccess && d->kind == WB_HEADALLOC) {
+        // every element at width bbar holding level 0 (n), Delta = 0, fit indices 15
+        const int bb = d->bbar;
+        const uint64_t n = (1ull << (bb - 1)) - 1;
+        uint64_t fields = 0;
+        for (int c = 0; c < 8; ++c) fields |= n << (c * bb);
+        uint8_t pat[8];
+        for (int i = 0; i < bb; ++i) pat[i] = uint8_t(fields >> (8 * i));
+        e = wb::launch_init_headalloc(st->state, st->region_stride, d->B * d->H, d->dk * d->dv * bb / 8,
+                                      int(code_capacity(*d)), pat, bb, (d->dk / 32) * d->dv, uint8_t(bb - 1), s);
+    }
     if (e == hipSuccess && st->side) e = wb::launch_fill(st->side, need_side, &zero, 1, s);
     if (e == hipSuccess && st->perm_dev) {
         e = hipMemcpyAsync(st->perm_dev, perm, size_t(d->H) * d->dk, hipMemcpyHostToDevice, s);
@@ -258,7 +274,7 @@ int state_quantize(wb_state* st, const float* S, void* stream) {
 
 int state_set_estimators(wb_state* st, float* dev_est) {
     if (!st) return WB_EINVAL;
-    if (st->d.kind != WB_BITALLOC) return WB_EUNSUPPORTED;
+    if (st->d.kind != WB_BITALLOC && st->d.kind != WB_HEADALLOC) return WB_EUNSUPPORTED;
     if (dev_est && !aligned16(dev_est)) return WB_EALIGN;
     st->est = dev_est;
     return WB_OK;
@@ -266,7 +282,7 @@ int state_set_estimators(wb_state* st, float* dev_est) {
 
 int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor, int C, void* stream) {
     if (!st) return WB_EINVAL;
-    if (st->d.kind != WB_BITALLOC) return WB_EUNSUPPORTED;
+    if (st->d.kind != WB_BITALLOC && st->d.kind != WB_HEADALLOC) return WB_EUNSUPPORTED;
     if (factor < WB_GAMMA_ERASURE || factor > WB_GAMMA_HC || C < 1) return WB_EINVAL;
     if (!s && (r || !st->est)) return WB_EINVAL;
     if ((s && !aligned4(s)) || (r && !aligned4(r))) return WB_EALIGN;
@@ -283,8 +299,16 @@ int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor
     a.bbar = st->d.bbar;
     a.bmin = st->d.bmin;
     a.bmax = st->d.bmax;
+    if (st->d.kind == WB_HEADALLOC) {
+        a.H = st->d.H;
+        a.rows_per_seq = st->d.H;
+        a.ws_c = reinterpret_cast<double*>(st->state + st->regions_bytes);
+        a.ws_w = st->state + st->regions_bytes + size_t(st->d.B) * st->d.H * 8;
+        return hip_status(wb::launch_allocate_heads(st->d, a, static_cast<hipStream_t>(stream)));
+    }
     if (st->d.budget == WB_BUDGET_LAYER) {
         a.H = st->d.H;
+        a.rows_per_seq = st->d.H * st->d.dk;
         a.ws_c = reinterpret_cast<double*>(st->state + st->regions_bytes);
         a.ws_w = st->state + st->regions_bytes + size_t(st->d.B) * st->d.H * st->d.dk * 8;
         return hip_status(wb::launch_allocate_layer(st->d, a, static_cast<hipStream_t>(stream)));

@@ -133,6 +133,11 @@ def compare_write_back(lay: L.Layout, reg_in, reg_gpu, wb, e_in, e_gpu, t, b, h,
             tally.bad.append((where, "widths/fit changed by a decode step"))
         _meta_ok(g.delta_bits, owb.delta_bits, wb.meta_pre["delta"], tally, (where, "delta"), meta_rel)
         override = {"delta": g.delta}
+    elif lay.kind == L.HEADALLOC:
+        if not (g.width == cin.width and np.array_equal(g.fit, cin.fit)):
+            tally.bad.append((where, "width/fit changed by a decode step"))
+        _meta_ok(g.delta_bits, owb.delta_bits, wb.meta_pre["delta"], tally, (where, "delta"), meta_rel)
+        override = {"delta": g.delta}
     wb2 = write_back(lay, X, e_in, t, b, h, prev=cin, meta_override=override)
     req = L.decode_region(lay, wb2.region)
     if lay.kind == L.UNIFORM:
@@ -141,6 +146,9 @@ def compare_write_back(lay: L.Layout, reg_in, reg_gpu, wb, e_in, e_gpu, t, b, h,
     elif lay.kind == L.BITALLOC:
         gc, oc = g.kappa, req.kappa
         step = np.repeat(g.delta[:, None], lay.dv, axis=1)
+    elif lay.kind == L.HEADALLOC:
+        gc, oc = g.kappa, req.kappa
+        step = np.repeat(g.delta, L.HA_GROUP, axis=0)
     else:
         q0 = lay.dk - lay.int8_rows
         gc = np.zeros(X.shape, np.int64)

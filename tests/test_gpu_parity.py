@@ -49,13 +49,15 @@ def _to_dev(a):
 
 
 def run_decode(lay, T, heads=None, warm=True, seed=1, perm=None, steps_checked=None, alloc_every=None,
-               edit=None):
+               edit=None, state=None):
+    """Teacher-forced decode steps against the oracle (``state``: continue an existing
+    state instead of a fresh one)."""
     print(f"\n[case] kind={lay.kind} mode={lay.mode} B={lay.B} H={lay.H} dk={lay.dk} T={T}", flush=True)
     B, H, dk, dv = lay.B, lay.H, lay.dk, lay.dv
     rng = np.random.default_rng(seed)
     if lay.kind == L.MIXED and perm is None:
         perm = np.stack([rng.permutation(dk) for _ in range(H)])
-    st = _state(lay, perm)
+    st = _state(lay, perm) if state is None else state
     inp = decode_inputs(seed, B, H, dk, dv, T, lay.per_row_decay)
     if edit is not None:
         edit(inp)
@@ -183,7 +185,7 @@ def test_tiny_fp32_identity():
 CASES = [
     (L.FP32, {}), (L.UNIFORM, {"bits": 4}), (L.UNIFORM, {"bits": 2}), (L.UNIFORM, {"bits": 8}),
     (L.HAD_INT8, {"block": 128}), (L.HAD_INT8, {"block": 32}), (L.MIXED, {"block": 32, "k_hi": 16}),
-    (L.BITALLOC, {}), (L.BITALLOC, {"budget": "layer"}),
+    (L.BITALLOC, {}), (L.BITALLOC, {"budget": "layer"}), (L.HEADALLOC, {}),
 ]
 
 
@@ -258,7 +260,7 @@ def test_import_export(kind, kw):
                 _meta_ok(g.scale_bits, oc.scale_bits, orc.meta_pre["scale"], tally, ("scale", b, h))
                 _meta_ok(g.zero_bits, oc.zero_bits, orc.meta_pre["zero"], tally, ("zero", b, h))
                 override = {"scale": g.scale, "zero": g.zero}
-            elif kind == L.BITALLOC:
+            elif kind in (L.BITALLOC, L.HEADALLOC):
                 from tests.parity import _meta_ok
                 oc = L.decode_region(lay, o_reg)
                 _meta_ok(g.delta_bits, oc.delta_bits, orc.meta_pre["delta"], tally, ("delta", b, h))
@@ -610,6 +612,59 @@ def test_allocate_bits_layer_budget_matches_oracle(case):
                 assert np.array_equal(reg_gpu, orc[h]), (pas, b, h)
     print(f"[alloc-layer] largest difference of head bit totals within a sequence: {spread}", flush=True)
     assert spread > 0
+
+
+@pytest.mark.parametrize("per_row", [False, True])
+def test_headalloc_allocation_matches_oracle_and_decode_after(per_row):
+    """The per-head unit: widths over the heads of each sequence from the summed row
+    factors, group fits and repack against the oracle on two passes (the second with the
+    decays permuted across heads), whole regions compared; then decode steps on the
+    heads of different widths."""
+    from oracle.step import allocate_headalloc_regions
+    print(f"\n[case] headalloc allocation per_row={per_row} B=2 H=8", flush=True)
+    B, H, dk = 2, 8, 128
+    lay = _layout(L.HEADALLOC, "rtn", B, H, dk, per_row=per_row)
+    rng = np.random.default_rng(43)
+    st = _state(lay)
+    st.quantize(_to_dev(_warm_state(rng, B, H, dk, dk)))
+    s_head = np.exp(rng.uniform(np.log(1e-3), 0.0, (B, H)))
+    s = np.repeat(s_head[..., None], dk, axis=-1)
+    if per_row:
+        s = s * np.exp(rng.uniform(-1.0, 1.0, (B, H, dk)))
+    s = s.astype(np.float32)
+    r = np.full((B, H, dk), 1.0 / (3 * dk), dtype=np.float32)
+    spread = 0
+    for pas, s_pass in enumerate((s, np.ascontiguousarray(s[:, ::-1]))):
+        torch.cuda.synchronize()
+        before = st.regions().cpu().numpy()
+        st.allocate_bits(_to_dev(s_pass), _to_dev(r))
+        torch.cuda.synchronize()
+        after = st.regions().cpu().numpy()
+        for b in range(B):
+            regs_in = [before[b * H + h][: lay.region_size()] for h in range(H)]
+            orc, al = allocate_headalloc_regions(lay, regs_in, [s_pass[b, h].astype(np.float64) for h in range(H)],
+                                                 [r[b, h].astype(np.float64) for h in range(H)])
+            gw = np.array([L.decode_region(lay, after[b * H + h][: lay.region_size()]).width for h in range(H)])
+            assert gw.sum() == lay.bbar * H
+            spread = max(spread, int(gw.max() - gw.min()))
+            if not np.array_equal(gw, al["widths"]):
+                bad = np.argwhere(gw != al["widths"]).ravel()
+                frac = np.abs(al["bstar"][bad] - np.floor(al["bstar"][bad]) - 0.5)
+                assert np.all(frac < 1e-5), (pas, b, bad, al["bstar"][bad])
+                continue
+            for h in range(H):
+                reg_gpu = after[b * H + h][: lay.region_size()]
+                g = L.decode_region(lay, reg_gpu)
+                if not np.array_equal(g.fit, al["fit"][h]):
+                    for gi in np.argwhere(g.fit != al["fit"][h]):
+                        e = al["fit_err"][h][gi[0], gi[1]]
+                        gf, of = g.fit[gi[0], gi[1]], al["fit"][h][gi[0], gi[1]]
+                        assert abs(e[gf] - e[of]) <= 1e-6 * max(e[of], 1e-300), (pas, b, h, gi)
+                    continue
+                assert np.array_equal(reg_gpu, orc[h]), (pas, b, h)
+    print(f"[headalloc] largest width difference between heads of a sequence: {spread}", flush=True)
+    assert spread >= 2
+    run_decode(lay, 4, warm=False, seed=44, state=st)
 
 
 def test_allocation_then_decode_full_budget_zero_state():
