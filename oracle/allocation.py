@@ -35,7 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 from .numerics import f16, rne
-from .quantizers import fit_fraction, levels_n
+from .quantizers import fit_fraction, levels_n, one_bit_round, one_bit_step
 from .recurrence import GAMMA_ERASURE, persistence_factor
 
 C_FLOOR = 1e-300
@@ -84,8 +84,13 @@ def row_costs(Y, s_rows, r_rows, factor=GAMMA_ERASURE, C=1):
 
 
 def fit_row(x, R: float, b: int):
-    """Clipping-fit index k and the row's squared errors for all 16 candidates."""
+    """Clipping-fit index k and the row's squared errors for all 16 candidates; a
+    one-bit row has no fit (sign times mean |x|): every candidate carries its error and
+    k = 15 is kept."""
     x = np.asarray(x, dtype=np.float64)
+    if b == 1:
+        d, _ = one_bit_step(x)
+        return 15, np.full(16, float(np.sum((x - d * one_bit_round(x, d, "rtn").kappa) ** 2)))
     n = levels_n(b)
     errs = np.zeros(16)
     for k in range(16):

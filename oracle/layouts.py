@@ -167,7 +167,8 @@ def decode_region(lay: Layout, region: np.ndarray) -> Content:
             b = int(widths[i])
             nbytes = dv * b // 8
             u = unpack_fields(r[off: off + nbytes], b, dv)
-            kappa[i] = u - (2 ** (b - 1) - 1)
+            # b = 1: the field is kappa' in {0, 1} for the levels -Delta, +Delta
+            kappa[i] = 2 * u - 1 if b == 1 else u - (2 ** (b - 1) - 1)
             off += nbytes
         return Content(kappa=kappa, widths=widths, fit=fit, delta=f16_value(dbits),
                        delta_bits=dbits)
@@ -212,7 +213,8 @@ def encode_region(lay: Layout, c: Content) -> np.ndarray:
         for i in range(dk):
             b = int(c.widths[i])
             n = 2 ** (b - 1) - 1
-            data = pack_fields(np.asarray(c.kappa[i], dtype=np.int64) + n, b)
+            k = np.asarray(c.kappa[i], dtype=np.int64)
+            data = pack_fields((k + 1) // 2 if b == 1 else k + n, b)
             out[off: off + data.size] = data
             off += data.size
         cbytes = lay.code_capacity

@@ -258,5 +258,21 @@ def row_step(R: float, b: int, kfit: int):
     return float(f16(pre)), pre
 
 
+def one_bit_step(x):
+    """One-bit row ([LBRS] "Levels and storage": one bit stores the sign times the mean
+    absolute value): Delta = f16(mean |x|) and its float64 pre-rounding value."""
+    pre = float(np.mean(np.abs(np.asarray(x, np.float64))))
+    return float(f16(pre)), pre
+
+
+def one_bit_round(x, step, mode, e=None, r16=None) -> Rounded:
+    """The rules on the two levels -Delta, +Delta: the grid -Delta + kappa' * 2 Delta,
+    kappa' in {0, 1} (RTN: the sign, an exact zero being the half-step tie that goes to
+    the even index, -Delta). Returns kappa = 2 kappa' - 1 in {-1, +1}."""
+    step = np.broadcast_to(np.asarray(step, dtype=np.float64), np.shape(x))
+    rr = round_on_grid(x, 2.0 * step, -step, 0, 1, mode, e, r16)
+    return Rounded(kappa=2 * rr.kappa - 1, xhat=rr.xhat, e_new=rr.e_new, tau=rr.tau, boundary=rr.boundary)
+
+
 def sym_round(x, step, n, mode, e=None, r16=None) -> Rounded:
     return round_on_grid(x, step, 0.0, -n, n, mode, e, r16)

@@ -33,8 +33,9 @@ from . import layouts as L
 from .allocation import allocate_head, allocate_heads, allocate_layer
 from .numerics import f16, f16_bits
 from .philox import sr_draws
-from .quantizers import (DIR, EF, RESQ, SR, affine_metadata, affine_round, levels_n, row_step,
-                         sym_round, uniform_memory_round, uniform_round, write_activity)
+from .quantizers import (DIR, EF, RESQ, SR, affine_metadata, affine_round, levels_n, one_bit_round,
+                         one_bit_step, row_step, sym_round, uniform_memory_round, uniform_round,
+                         write_activity)
 from .recurrence import delta_step
 
 
@@ -142,14 +143,19 @@ def write_back(lay: L.Layout, X: np.ndarray, e_in, t: int, b: int, h: int,
         delta = np.zeros(dk)
         dpre = np.zeros(dk)
         for i in range(dk):
-            delta[i], dpre[i] = row_step(R[i], int(widths[i]), int(fits[i]))
+            if widths[i] == 1:
+                delta[i], dpre[i] = one_bit_step(X[i])
+            else:
+                delta[i], dpre[i] = row_step(R[i], int(widths[i]), int(fits[i]))
         if meta_override is not None:
             delta = meta_override["delta"]
         r16 = _draws(lay, b, h, t, range(dk)) if mode == SR else None
         kappa = np.zeros((dk, dv), np.int64)
         for i in range(dk):
             n = levels_n(int(widths[i]))
-            rr = sym_round(X[i], delta[i], n, mode, e[i], None if r16 is None else r16[i])
+            ri = None if r16 is None else r16[i]
+            rr = (one_bit_round(X[i], delta[i], mode, e[i], ri) if widths[i] == 1 else
+                  sym_round(X[i], delta[i], n, mode, e[i], ri))
             kappa[i], tau[i], bnd[i], e_new[i] = rr.kappa, rr.tau, rr.boundary, rr.e_new
         c = L.Content(kappa=kappa, widths=widths, fit=fits, delta_bits=f16_bits(delta))
         wb.meta_pre = {"delta": dpre, "R": R}
@@ -277,6 +283,10 @@ def _round_at(lay: L.Layout, Y, alloc):
     delta = np.zeros(lay.dk)
     kappa = np.zeros((lay.dk, lay.dv), np.int64)
     for i in range(lay.dk):
+        if widths[i] == 1:
+            delta[i], _ = one_bit_step(Y[i])
+            kappa[i] = one_bit_round(Y[i], delta[i], "rtn").kappa
+            continue
         delta[i], _ = row_step(alloc["R"][i], int(widths[i]), int(fits[i]))
         n = levels_n(int(widths[i]))
         rr = sym_round(Y[i], delta[i], n, "rtn")
