@@ -174,7 +174,8 @@ enum { kHead = 0, kStep = 1, kCost = 2, kPack = 3 };
 // each row's cost c_i (0 for a head whose rows are all zero) to the workspace and
 // stops; kPack takes the widths the per-sequence pass left in the workspace, then
 // fits and repacks as kHead does.
-template <int MODE>
+// OB: rows may be one bit wide (bmin = 1); without it that path is not compiled.
+template <int MODE, bool OB>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) allocate_kernel(const AllocArgs A) {
     constexpr bool STEP = MODE == kStep;
     __shared__ AllocSmem sm;
@@ -259,7 +260,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         const float dl = sm.delta[row];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const int kap = int((fld >> (c * bw)) & ((1ull << bw) - 1)) - n;
+            const int field = int((fld >> (c * bw)) & ((1ull << bw) - 1));
+            const int kap = (OB && bw == 1) ? 2 * field - 1 : field - n;    // one-bit rows: -1, +1
             x[m][c] = float(kap) * dl;
         }
     }
@@ -492,8 +494,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     // candidate steps: thread t fills fit index t % 16 of rows t / 16 + 16 m
     for (int i = tid; i < DK * 16; i += NT) {
         const int row = i >> 4, kf = i & 15;
-        const int n = (1 << (sm.newwidth[row] - 1)) - 1;
-        const float d = f16_bits_to_f32(f64_to_f16_rto(kFit.f[kf] * sm.R[row] / n));
+        const int n = (1 << (sm.newwidth[row] - 1)) - 1;      // 0: a one-bit row, no fit
+        const float d = n ? f16_bits_to_f32(f64_to_f16_rto(kFit.f[kf] * sm.R[row] / n)) : 0.f;
         // reciprocal refined by one Newton step: it only orders candidate errors and
         // pre-rounds the repack, which falls back to an exact quotient near half-integers
         float r = __builtin_amdgcn_rcpf(d);
@@ -510,11 +512,31 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         const int n = (1 << (bw - 1)) - 1;
         const float lo = kMagic - float(n), hi = kMagic + float(n);
         const int bwo = sm.width[row];
-        int best;
+        const int nold = (OB && bwo == 1) ? 1 : (1 << (bwo - 1)) - 1;    // one-bit rows hold levels -1, +1
+        int best = 15;
+        uint16_t dbits = 0;
+        uint64_t fld = 0;
+        if (OB && bw == 1) {
+            // one-bit row ([LBRS] "Levels and storage"): Delta = f16(mean |x|), the sign
+            // (nearest of -Delta, +Delta: an exact zero is the tie and takes -Delta); the
+            // sum is exact in float64 for values on the old grid
+            double sa = 0.0;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sa += fabs(double(x[m][c]));
+            sa += dpp_f64<0xB1>(sa);
+            sa += dpp_f64<0x4E>(sa);
+            sa += dpp_f64<0x141>(sa);
+            sa += dpp_f64<0x140>(sa);
+            dbits = f64_to_f16_rto(sa / double(DV));
+            if (dbits) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) fld |= uint64_t(x[m][c] > 0.f) << c;
+            }
+        } else {
         if (!STEP && bwo <= 5) {
-            best = level_fit<1>(x[m], sm.delta[row], (1 << (bwo - 1)) - 1, sm.cand[row][cg], lo, hi, cg);
+            best = level_fit<1>(x[m], sm.delta[row], nold, sm.cand[row][cg], lo, hi, cg);
         } else if (!STEP && bwo == 6) {
-            best = level_fit<2>(x[m], sm.delta[row], (1 << (bwo - 1)) - 1, sm.cand[row][cg], lo, hi, cg);
+            best = level_fit<2>(x[m], sm.delta[row], nold, sm.cand[row][cg], lo, hi, cg);
         } else {
             float err[16];
 #pragma unroll
@@ -539,8 +561,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
                 }
         }
         const float2 dk = sm.cand[row][best];
-        const uint16_t dbits = f32_to_f16_bits(dk.x);
-        uint64_t fld = 0;
+        dbits = f32_to_f16_bits(dk.x);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             // nearest level, ties to even, of the exact quotient x / Delta: x / Delta +
@@ -554,6 +575,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             q = __builtin_amdgcn_fmed3f(q, lo, hi);
             const uint32_t code = __float_as_uint(q) - (kMagicBits - uint32_t(n));   // level + n
             fld |= uint64_t(code) << (c * bw);
+        }
         }
         const int off = sm.newoff[row] + cg * bw;
         const int wi = off >> 2, sh = (off & 3) * 8;
@@ -872,12 +894,14 @@ __global__ void __launch_bounds__(NT) headalloc_pack_kernel(const AllocArgs A) {
 }  // namespace
 
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(allocate_kernel<kHead>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kHead, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<kHead, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(allocate_kernel<kStep>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kStep, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<kStep, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -893,13 +917,15 @@ hipError_t launch_allocate_heads(const wb_layout_desc& d, const AllocArgs& a, hi
 }
 
 hipError_t launch_allocate_layer(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(allocate_kernel<kCost>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kCost, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<kCost, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(layer_widths_kernel, dim3(d.B), dim3(LNT), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(allocate_kernel<kPack>, dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kPack, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<kPack, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -301,7 +301,8 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                                                                        A.code_cap) + (row >> 5) * DV + 8 * cg;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const int kap = int((fld >> (c * bw)) & mask) - n;
+                    const int field = int((fld >> (c * bw)) & mask);
+                    const int kap = bw == 1 ? 2 * field - 1 : field - n;   // one-bit rows: -1, +1
                     x[m][c] = Real(float(kap) * (A.head_unit ? f16_bits_to_f32(gs[c]) : dl));
                 }
             }
@@ -620,7 +621,16 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                 const int n = (1 << (bw - 1)) - 1;
                 uint16_t dbits = 0;
                 float dl = 0.f;
-                if (!A.head_unit) {
+                if (bw == 1) {
+                    // one-bit row: Delta = f16(mean |x|); the rule on -Delta + k' 2 Delta
+                    double sa = 0.0;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) sa += fabs(double(x[m][c]));
+#pragma unroll
+                    for (int d = 1; d < NCG; d <<= 1) sa += xor_shfl(sa, d);
+                    dbits = f64_to_f16_bits(sa / double(DV));
+                    dl = f16_bits_to_f32(dbits);
+                } else if (!A.head_unit) {
                     float R = 0.f;
 #pragma unroll
                     for (int c = 0; c < 8; ++c) R = fmaxf(R, fabsf(float(x[m][c])));
@@ -634,6 +644,11 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const float dc = A.head_unit ? sm.gdelta[(row >> 5) * DV + 8 * cg + c] : dl;
+                    if (bw == 1) {
+                        const int k1 = round_rule<EMODE, float>(float(x[m][c]), e[m][c], 2.f * dl, -dl, 0, 1, r16[c], &en[c]);
+                        fld |= uint64_t(uint32_t(k1)) << c;
+                        continue;
+                    }
                     const int kap = round_rule<EMODE, float>(float(x[m][c]), e[m][c], dc, 0.f, -n, n, r16[c], &en[c]);
                     fld |= uint64_t(uint32_t(kap + n)) << (c * bw);
                 }
@@ -780,7 +795,8 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
         case WB_HEADALLOC:
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
         default:
-            if (op == OP_STEP && d.mode == WB_RTN && d.budget == WB_BUDGET_HEAD) return launch_bitalloc_step(d, a, stream);
+            if (op == OP_STEP && d.mode == WB_RTN && d.budget == WB_BUDGET_HEAD && d.bmin >= 2)
+                return launch_bitalloc_step(d, a, stream);
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
     }
 }

@@ -88,7 +88,9 @@ int validate(const wb_layout_desc* d) {
         if (d->k_hi <= 0 || d->k_hi >= d->dk || d->k_hi % rs) return WB_EUNSUPPORTED;
     }
     if (d->kind == WB_BITALLOC || d->kind == WB_HEADALLOC) {
-        if (d->bmin < 2 || d->bmin > d->bbar || d->bbar > d->bmax || d->bmax > 8) return WB_EUNSUPPORTED;
+        // one-bit rows (bmin = 1) for the per-row unit only: a one-bit head is excluded
+        const int floor = d->kind == WB_BITALLOC ? 1 : 2;
+        if (d->bmin < floor || d->bmin > d->bbar || d->bbar > d->bmax || d->bmax > 8) return WB_EUNSUPPORTED;
     }
     if (d->kind == WB_HEADALLOC && d->H > 4096) return WB_EUNSUPPORTED;
     if (d->budget != WB_BUDGET_HEAD && d->budget != WB_BUDGET_LAYER) return WB_EINVAL;

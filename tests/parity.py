@@ -235,7 +235,7 @@ def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: T
     where the pre-rounding value is within ``meta_rel`` of the midpoint; rows of equal
     width, fit and Delta: codes equal or one apart within ``window`` steps of a
     rounding boundary. Returns the number of rows left out of the code comparison."""
-    from oracle.quantizers import fit_fraction, levels_n, sym_round
+    from oracle.quantizers import fit_fraction, levels_n, one_bit_round, sym_round
     g = L.decode_region(lay, np.asarray(reg_gpu, np.uint8)[: lay.region_size()])
     o = L.decode_region(lay, np.asarray(reg_orc, np.uint8)[: lay.region_size()])
     if g.widths.sum() != lay.bbar * lay.dk or g.widths.min() < lay.bmin or g.widths.max() > lay.bmax:
@@ -254,7 +254,8 @@ def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: T
         if abs(e[g.fit[i]] - e[o.fit[i]]) > 1e-6 * max(e[o.fit[i]], 1e-300):
             tally.bad.append((where, "fit", int(i), int(g.fit[i]), int(o.fit[i])))
     rows = np.argwhere(same_f).ravel()
-    pre = np.array([fit_fraction(int(o.fit[i])) * alloc["R"][i] / levels_n(int(o.widths[i])) for i in rows])
+    pre = np.array([float(np.mean(np.abs(X[i]))) if o.widths[i] == 1 else
+                    fit_fraction(int(o.fit[i])) * alloc["R"][i] / levels_n(int(o.widths[i])) for i in rows])
     _meta_ok(g.delta_bits[rows], o.delta_bits[rows], pre, tally, (where, "delta"), meta_rel)
     skipped = lay.dk - rows.size
     for i in rows:
@@ -262,7 +263,8 @@ def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: T
             skipped += 1
             continue
         n = levels_n(int(g.widths[i]))
-        rr = sym_round(X[i], float(g.delta[i]), n, "rtn")
+        rr = (one_bit_round(X[i], float(g.delta[i]), "rtn") if g.widths[i] == 1 else
+              sym_round(X[i], float(g.delta[i]), n, "rtn"))
         tally.elems += lay.dv
         diff = g.kappa[i] != rr.kappa
         if diff.any():

@@ -75,8 +75,12 @@ def test_descriptor_validation():
         assert _code(d) == code, fields
     d = wb.make_desc("uniform", "rtn", 1, 1, 16, 16, bits=3)
     assert _code(d) == -3
-    d = wb.make_desc("bitalloc", "rtn", 1, 1, bbar=4, bmin=1)
-    assert _code(d) == -3
+    # one-bit rows: bmin = 1 for the per-row unit; the per-head unit keeps a two-bit floor
+    assert _code(wb.make_desc("bitalloc", "rtn", 1, 1, bbar=4, bmin=1)) == 0
+    assert _code(wb.make_desc("bitalloc", "rtn", 1, 1, bbar=4, bmin=0)) == -3
+    assert _code(wb.make_desc("headalloc", "rtn", 1, 1, bbar=4, bmin=1)) == -3
+    assert _code(wb.make_desc("headalloc", "rtn", 1, 4, bbar=4, bmin=2)) == 0
+    assert _code(wb.make_desc("headalloc", "rtn", 1, 1, bbar=4, budget="layer")) == -3
     d = wb.make_desc("bitalloc", "rtn", 1, 1, bbar=4, bmax=9)
     assert _code(d) == -3
     d = wb.make_desc("fp32", "rtn", 1, 1, 32, 32)

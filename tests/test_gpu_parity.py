@@ -209,6 +209,45 @@ def test_bitalloc_after_allocation_rtn_and_sr():
         run_decode(lay, 7, warm=True, seed=13, alloc_every=3)
 
 
+@pytest.mark.parametrize("mode", ["rtn", "sr", "ef"])
+def test_bitalloc_one_bit_rows_decode_after_allocation(mode):
+    """Decode steps with rows one bit wide (bmin = 1, mean width 3: the allocation
+    passes leave slow rows wide and fast rows at sign times mean |x|)."""
+    print(f"\n[case] one-bit rows BITALLOC decode {mode}", flush=True)
+    lay = _layout(L.BITALLOC, mode, 2, 2, 128, bbar=3, bmin=1)
+    run_decode(lay, 7, warm=True, seed=19, alloc_every=3)
+
+
+@pytest.mark.parametrize("case", ["warm", "spread"])
+def test_allocate_bits_one_bit_rows_matches_oracle(case):
+    """The allocation pass with a one-bit floor (bmin = 1, mean width 3) on two passes,
+    the second from the widths the first left (one-bit rows read as -Delta, +Delta)."""
+    print(f"\n[case] allocate_bits one-bit floor {case}", flush=True)
+    B, H, dk = 2, 4, 128
+    lay = _layout(L.BITALLOC, "rtn", B, H, dk, bbar=3, bmin=1)
+    rng = np.random.default_rng(47)
+    st = _state(lay)
+    S, s = _alloc_case(case, rng, B, H, dk)
+    st.quantize(_to_dev(S))
+    r = np.full((B, H, dk), 1.0 / (3 * dk), dtype=np.float32)
+    ones = 0
+    for pas, s_pass in enumerate((s, np.ascontiguousarray(s[..., ::-1]))):
+        torch.cuda.synchronize()
+        before = st.regions().cpu().numpy()
+        st.allocate_bits(_to_dev(s_pass), _to_dev(r))
+        torch.cuda.synchronize()
+        after = st.regions().cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                reg_in = before[b * H + h][: lay.region_size()]
+                reg_orc, alloc = allocate_region(lay, reg_in, s_pass[b, h].astype(np.float64),
+                                                 r[b, h].astype(np.float64))
+                ones += int((alloc["widths"] == 1).sum())
+                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (pas, b, h))
+    print(f"[alloc-1bit] one-bit rows chosen over both passes: {ones}", flush=True)
+    assert ones > 0
+
+
 @pytest.mark.parametrize("mode", ["rtn", "ef"])
 def test_bitalloc_layer_budget_decode_after_allocation(mode):
     """Decode steps on heads whose widths differ under the layer-wise budget (each
@@ -492,7 +531,7 @@ def test_online_estimators_and_allocation_from_them(mode, per_row):
                 _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h))
 
 
-@pytest.mark.parametrize("case", ["est-erasure", "est-hC64", "decays-w1", "per-head-est"])
+@pytest.mark.parametrize("case", ["est-erasure", "est-hC64", "decays-w1", "per-head-est", "one-bit-floor"])
 def test_decode_step_with_allocation(case):
     """Decode tokens whose write-back allocates (teacher-forced: each token starts from
     the GPU's stored region and estimators) against the oracle's plain step, allocation
@@ -505,8 +544,9 @@ def test_decode_step_with_allocation(case):
     per_row = case != "per-head-est"
     use_est = case != "decays-w1"
     factor, C = {"est-erasure": ("erasure", 1), "est-hC64": ("hC", 64), "decays-w1": ("w1", 1),
-                 "per-head-est": ("erasure", 1)}[case]
-    lay = _layout(L.BITALLOC, "rtn", B, H, dk, per_row=per_row)
+                 "per-head-est": ("erasure", 1), "one-bit-floor": ("erasure", 1)}[case]
+    kw = dict(bbar=3, bmin=1) if case == "one-bit-floor" else {}
+    lay = _layout(L.BITALLOC, "rtn", B, H, dk, per_row=per_row, **kw)
     rng = np.random.default_rng(61)
     st = _state(lay)
     inp = decode_inputs(61, B, H, dk, dk, T, per_row)
