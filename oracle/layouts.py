@@ -19,6 +19,9 @@ MIXED     static mixed precision ([DAMP] "Risk scoring and selection",
           holds logical row perm[p]; physical rows 0..k_hi-1 are float16 values
           [k_hi][dv] (unrotated); the remaining rows are Hadamard INT8 as above:
           u8 codes [dk-k_hi][dv], then (f16 scale, f16 zero) [dk-k_hi][dv/G][2].
+          With the INT4 tier (int_bits = 4; [DAMP] "Quantization & calibration details"
+          gives b = 4 beside b = 8) the codes are 4 bits, two a byte, low nibble first,
+          and the affine grid has 15 steps.
 BITALLOC  decay-aware per-row widths ([LBRS] "State bit allocation", "Levels and
           storage": prefix sums of widths give row offsets): row i's codes start at
           byte (dv/8) * sum_{i'<i} b_i', element j at bits [j b_i, (j+1) b_i),
@@ -66,6 +69,7 @@ class Layout:
     seed: int = 0
     mem_bits: int = 0      # k of the temporal-memory rules (direction / residual memory)
     budget: str = "head"   # BITALLOC width budget: "head" or "layer" (all heads of a sequence)
+    int_bits: int = 8      # HAD_INT8 / MIXED integer tier: 8 (INT8) or 4 (INT4, two codes a byte)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -86,10 +90,10 @@ class Layout:
         if self.kind == UNIFORM:
             return dk * dv * self.bits // 8
         if self.kind == HAD_INT8:
-            return dk * dv + dk * (dv // self.block) * 4
+            return dk * dv * self.int_bits // 8 + dk * (dv // self.block) * 4
         if self.kind == MIXED:
             q = dk - self.k_hi
-            return self.k_hi * dv * 2 + q * dv + q * (dv // self.block) * 4
+            return self.k_hi * dv * 2 + q * dv * self.int_bits // 8 + q * (dv // self.block) * 4
         if self.kind == BITALLOC:
             return self.code_capacity + 2 * dk + dk
         if self.kind == HEADALLOC:
@@ -147,8 +151,12 @@ def decode_region(lay: Layout, region: np.ndarray) -> Content:
         if lay.kind == MIXED:
             c.hi_bits = r[: lay.k_hi * dv * 2].view(np.uint16).reshape(lay.k_hi, dv).copy()
             off = lay.k_hi * dv * 2
-        c.codes = r[off: off + nq * dv].reshape(nq, dv).astype(np.int64)
-        off += nq * dv
+        cb = nq * dv * lay.int_bits // 8
+        if lay.int_bits == 8:
+            c.codes = r[off: off + cb].reshape(nq, dv).astype(np.int64)
+        else:
+            c.codes = unpack_fields(r[off: off + cb], lay.int_bits, nq * dv).reshape(nq, dv)
+        off += cb
         pairs = r[off: off + nq * nb * 4].view(np.uint16).reshape(nq, nb, 2)
         c.scale_bits = pairs[:, :, 0].copy()
         c.zero_bits = pairs[:, :, 1].copy()
@@ -201,7 +209,10 @@ def encode_region(lay: Layout, c: Content) -> np.ndarray:
             hb = np.asarray(c.hi_bits, dtype=np.uint16).reshape(-1).view(np.uint8)
             out[: hb.size] = hb
             off = hb.size
-        cd = np.asarray(c.codes, dtype=np.uint8).reshape(-1)
+        if lay.int_bits == 8:
+            cd = np.asarray(c.codes, dtype=np.uint8).reshape(-1)
+        else:
+            cd = pack_fields(np.asarray(c.codes, dtype=np.int64).reshape(-1), lay.int_bits)
         out[off: off + cd.size] = cd
         off += cd.size
         pairs = np.stack([np.asarray(c.scale_bits, np.uint16), np.asarray(c.zero_bits, np.uint16)],

@@ -226,18 +226,19 @@ def write_margin(h, q_prev, B: int):
 
 # ----- per-block asymmetric affine INT8 ---------------------------------------
 
-def affine_metadata(x_block):
+def affine_metadata(x_block, bits: int = 8):
     """Returns (scale, zero, scale_pre, zero_pre): float16 values and their float64
-    pre-rounding values, for one block of values."""
+    pre-rounding values, for one block of values; b-bit codes 0 .. 2^b - 1 ([DAMP]
+    "Quantization & calibration details": b = 8 for INT8, b = 4 for INT4)."""
     x_block = np.asarray(x_block, dtype=np.float64)
     mn = float(np.min(x_block))
     mx = float(np.max(x_block))
-    scale_pre = max(mx - mn, 0.0) / 255.0
+    scale_pre = max(mx - mn, 0.0) / float(2 ** bits - 1)
     return float(f16(scale_pre)), float(f16(mn)), scale_pre, mn
 
 
-def affine_round(x, scale, zero, mode, e=None, r16=None) -> Rounded:
-    return round_on_grid(x, scale, zero, 0, 255, mode, e, r16)
+def affine_round(x, scale, zero, mode, e=None, r16=None, bits: int = 8) -> Rounded:
+    return round_on_grid(x, scale, zero, 0, 2 ** bits - 1, mode, e, r16)
 
 
 # ----- symmetric per-row levels (decay-aware allocation) ---------------------

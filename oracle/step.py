@@ -110,12 +110,12 @@ def write_back(lay: L.Layout, X: np.ndarray, e_in, t: int, b: int, h: int,
         for p in range(nq):
             for g in range(nb):
                 blk = X[q0 + p, g * G:(g + 1) * G]
-                scale[p, g], zero[p, g], spre[p, g], zpre[p, g] = affine_metadata(blk)
+                scale[p, g], zero[p, g], spre[p, g], zpre[p, g] = affine_metadata(blk, lay.int_bits)
         if meta_override is not None:
             scale, zero = meta_override["scale"], meta_override["zero"]
         r16 = _draws(lay, b, h, t, range(q0, dk)) if mode == SR else None
         rr = affine_round(X[q0:], np.repeat(scale, G, axis=1), np.repeat(zero, G, axis=1),
-                          mode, e[q0:], r16)
+                          mode, e[q0:], r16, lay.int_bits)
         c.codes = rr.kappa
         c.scale_bits = f16_bits(scale)
         c.zero_bits = f16_bits(zero)
