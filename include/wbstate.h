@@ -137,6 +137,9 @@ typedef struct wb_layout_desc {
     int32_t bbar, bmin, bmax;  /* BITALLOC mean width and clip range, 2 <= bmin <= bbar <= bmax <= 8 */
     int32_t mem_bits;          /* k of WB_DIR / WB_RESQ, 1..8 (the pages evaluate 2, 3, 4); 0 otherwise */
     int32_t budget;            /* WB_BUDGET_HEAD or WB_BUDGET_LAYER (BITALLOC, H * dk <= 4096); 0 otherwise */
+    int32_t int_bits;          /* HAD_INT8 / MIXED integer tier ([DAMP] "Quantization & calibration
+                                * details"): 0 or 8 for INT8, 4 for INT4 (codes two a byte, low nibble
+                                * first, 15 affine steps); 0 for the other layouts */
     uint64_t seed;             /* Philox key for WB_SR */
 } wb_layout_desc;
 

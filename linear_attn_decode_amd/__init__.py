@@ -33,7 +33,8 @@ class LayoutDesc(ctypes.Structure):
                 ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("k_hi", ctypes.c_int32),
                 ("bbar", ctypes.c_int32), ("bmin", ctypes.c_int32), ("bmax", ctypes.c_int32),
-                ("mem_bits", ctypes.c_int32), ("budget", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("mem_bits", ctypes.c_int32), ("budget", ctypes.c_int32), ("int_bits", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
 
 
 _P = ctypes.c_void_p
@@ -84,12 +85,13 @@ def check(status: int, what: str = "") -> None:
 
 
 def make_desc(kind, mode, B, H, dk=128, dv=128, per_row_decay=True, bits=4, block=32, k_hi=16,
-              bbar=4, bmin=2, bmax=8, seed=0, mem_bits=0, budget="head") -> LayoutDesc:
+              bbar=4, bmin=2, bmax=8, seed=0, mem_bits=0, budget="head", int_bits=0) -> LayoutDesc:
     kind = KIND_NAMES.get(kind, kind)
     mode = MODE_NAMES.get(mode, mode)
     return LayoutDesc(kind=kind, mode=mode, decay=DECAY_PER_ROW if per_row_decay else DECAY_PER_HEAD,
                       B=B, H=H, dk=dk, dv=dv, bits=bits, block=block, k_hi=k_hi, bbar=bbar,
-                      bmin=bmin, bmax=bmax, mem_bits=mem_bits, budget=BUDGET_CODES.get(budget, budget), seed=seed)
+                      bmin=bmin, bmax=bmax, mem_bits=mem_bits, budget=BUDGET_CODES.get(budget, budget),
+                      int_bits=int_bits, seed=seed)
 
 
 def buffer_sizes(desc: LayoutDesc):
@@ -121,11 +123,11 @@ class WriteBackState:
 
     def __init__(self, kind, mode="rtn", B=1, H=1, dk=128, dv=128, per_row_decay=True, bits=4,
                  block=32, k_hi=16, bbar=4, bmin=2, bmax=8, seed=0, perm=None, device="cuda",
-                 stream=None, mem_bits=0, budget="head"):
+                 stream=None, mem_bits=0, budget="head", int_bits=0):
         import numpy as np
         import torch
         self.desc = make_desc(kind, mode, B, H, dk, dv, per_row_decay, bits, block, k_hi, bbar, bmin,
-                              bmax, seed, mem_bits, budget)
+                              bmax, seed, mem_bits, budget, int_bits)
         nbytes, side = buffer_sizes(self.desc)
         self.state = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.side = torch.empty(max(side // 4, 4), dtype=torch.float32, device=device)

@@ -273,9 +273,13 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             } else if (ROT) {
                 const int k_hi = (KIND == WB_MIXED) ? A.k_hi : 0;
                 const int qrow = row - k_hi;
+                const int ib = A.int_bits;                // 8, or 4: codes two a byte
                 const size_t code_base = (size_t)k_hi * DV * 2;
-                const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV;
-                const uint2 raw = *reinterpret_cast<const uint2*>(region + code_base + (size_t)qrow * DV + 8 * cg);
+                const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV * ib / 8;
+                const uint8_t* cp = region + code_base + ((size_t)qrow * DV + 8 * cg) * ib / 8;
+                uint2 raw;
+                if (ib == 8) raw = *reinterpret_cast<const uint2*>(cp);
+                else raw = make_uint2(*reinterpret_cast<const uint32_t*>(cp), 0u);
                 const int nb = DV / A.block;
                 const int g = (8 * cg) / A.block;
                 const uint32_t sz = *reinterpret_cast<const uint32_t*>(region + meta_base + ((size_t)qrow * nb + g) * 4);
@@ -283,7 +287,8 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                 const Real zero = Real(f16_bits_to_f32(sz >> 16));
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const uint32_t code = ((c < 4 ? raw.x : raw.y) >> ((c & 3) * 8)) & 0xFFu;
+                    const uint32_t code = ib == 8 ? ((c < 4 ? raw.x : raw.y) >> ((c & 3) * 8)) & 0xFFu
+                                                  : (raw.x >> (c * 4)) & 0xFu;
                     x[m][c] = zero + Real(code) * scale;
                 }
             } else if (KIND == WB_BITALLOC) {
@@ -584,8 +589,10 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             } else if (ROT) {
                 const int k_hi = (KIND == WB_MIXED) ? A.k_hi : 0;
                 const int qrow = row - k_hi;
+                const int ib = A.int_bits;
+                const int top = (1 << ib) - 1;            // 255 or 15
                 const size_t code_base = (size_t)k_hi * DV * 2;
-                const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV;
+                const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV * ib / 8;
                 const int LB = A.block / 8;               // lanes per block
                 Real mn = x[m][0], mx = x[m][0];
 #pragma unroll
@@ -597,7 +604,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     mn = fmin(mn, xor_shfl(mn, d));
                     mx = fmax(mx, xor_shfl(mx, d));
                 }
-                const Real spre = fmax(mx - mn, Real(0)) / Real(255);
+                const Real spre = fmax(mx - mn, Real(0)) / Real(top);
                 const uint16_t sbits = to_f16_bits<Real>(spre);
                 const uint16_t zbits = to_f16_bits<Real>(mn);
                 const Real scale = Real(f16_bits_to_f32(sbits));
@@ -605,11 +612,14 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                 uint32_t lo4 = 0, hi4 = 0;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const int code = round_rule<EMODE, Real>(x[m][c], Real(e[m][c]), scale, zero, 0, 255, r16[c], &en[c]);
-                    if (c < 4) lo4 |= uint32_t(code) << (c * 8);
+                    const int code = round_rule<EMODE, Real>(x[m][c], Real(e[m][c]), scale, zero, 0, top, r16[c], &en[c]);
+                    if (ib == 4) lo4 |= uint32_t(code) << (c * 4);
+                    else if (c < 4) lo4 |= uint32_t(code) << (c * 8);
                     else hi4 |= uint32_t(code) << ((c - 4) * 8);
                 }
-                *reinterpret_cast<uint2*>(region + code_base + (size_t)qrow * DV + 8 * cg) = make_uint2(lo4, hi4);
+                uint8_t* cp = region + code_base + ((size_t)qrow * DV + 8 * cg) * ib / 8;
+                if (ib == 8) *reinterpret_cast<uint2*>(cp) = make_uint2(lo4, hi4);
+                else *reinterpret_cast<uint32_t*>(cp) = lo4;
                 if ((cg % LB) == 0) {
                     const int nb = DV / A.block;
                     const int g = (8 * cg) / A.block;

@@ -397,7 +397,7 @@ hipError_t launch_rot(const wb_layout_desc& d, const KArgs& a, hipStream_t strea
 }  // namespace
 
 bool rot_step_supported(const wb_layout_desc& d) {
-    if (d.mode != WB_RTN || d.dk != DK || d.dv != DV) return false;
+    if (d.mode != WB_RTN || d.dk != DK || d.dv != DV || d.int_bits == 4) return false;
     if (d.kind == WB_HAD_INT8) return d.block == 32 || d.block == 128;
     if (d.kind == WB_MIXED) return d.k_hi == 16 && d.block == 32;
     return false;

@@ -577,7 +577,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
 }  // namespace
 
 hipError_t launch_prefill(const wb_layout_desc& d, const PrefillArgs& a, hipStream_t stream) {
-    if (d.dk != 128 || d.dv != 128 || d.mode != WB_RTN) return hipErrorNotSupported;
+    if (d.dk != 128 || d.dv != 128 || d.mode != WB_RTN || d.int_bits == 4) return hipErrorNotSupported;
     const dim3 grid(d.B * d.H), block(NT);
     switch (d.kind) {
         case WB_FP32: hipLaunchKernelGGL(prefill_kernel<WB_FP32>, grid, block, 0, stream, a); break;

@@ -35,6 +35,7 @@ struct KArgs {
     int code_cap = 0;                 // BITALLOC code-area bytes of a head (meta follows)
     int layer = 0;                    // BITALLOC layer budget: the used code bytes vary per head
     int head_unit = 0;                // HEADALLOC (run by the BITALLOC kernels): one width, group scales
+    int int_bits = 8;                 // HAD_INT8 / MIXED integer tier: 8 or 4
     uint32_t* activity = nullptr;     // [B*H][8] write-activity counters (UNIFORM) or null
     uint8_t* votes = nullptr;         // [B*H][DK][DV] vote state, with `activity`
     float* est = nullptr;             // [B*H][2 DK + 4] online estimators (BITALLOC) or null

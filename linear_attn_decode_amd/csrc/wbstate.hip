@@ -38,15 +38,18 @@ size_t code_capacity(const wb_layout_desc& d) {
     return size_t(d.dk) * d.dv * size_t(room ? d.bmax : d.bbar) / 8;
 }
 
+// width of the integer tier of the Hadamard layouts
+size_t int_bits(const wb_layout_desc& d) { return d.int_bits == 4 ? 4 : 8; }
+
 size_t region_size(const wb_layout_desc& d) {
     const size_t dk = d.dk, dv = d.dv;
     switch (d.kind) {
         case WB_FP32: return 4 * dk * dv;
         case WB_UNIFORM: return dk * dv * size_t(d.bits) / 8;
-        case WB_HAD_INT8: return dk * dv + dk * (dv / d.block) * 4;
+        case WB_HAD_INT8: return dk * dv * int_bits(d) / 8 + dk * (dv / d.block) * 4;
         case WB_MIXED: {
             const size_t qr = dk - size_t(d.k_hi);
-            return size_t(d.k_hi) * dv * 2 + qr * dv + qr * (dv / d.block) * 4;
+            return size_t(d.k_hi) * dv * 2 + qr * dv * int_bits(d) / 8 + qr * (dv / d.block) * 4;
         }
         case WB_HEADALLOC: return code_capacity(d) + 3 * (dk / 32) * dv + 16;
         default: return code_capacity(d) + 3 * dk;
@@ -93,6 +96,8 @@ int validate(const wb_layout_desc* d) {
         if (d->bmin < floor || d->bmin > d->bbar || d->bbar > d->bmax || d->bmax > 8) return WB_EUNSUPPORTED;
     }
     if (d->kind == WB_HEADALLOC && d->H > 4096) return WB_EUNSUPPORTED;
+    const bool hadamard = d->kind == WB_HAD_INT8 || d->kind == WB_MIXED;
+    if (hadamard ? (d->int_bits != 0 && d->int_bits != 8 && d->int_bits != 4) : d->int_bits != 0) return WB_EINVAL;
     if (d->budget != WB_BUDGET_HEAD && d->budget != WB_BUDGET_LAYER) return WB_EINVAL;
     if (d->budget == WB_BUDGET_LAYER && (d->kind != WB_BITALLOC || d->H * d->dk > 4096)) return WB_EUNSUPPORTED;
     return WB_OK;
@@ -120,6 +125,7 @@ wb::KArgs base_args(const wb_state* st) {
     a.bbar = st->d.bbar;
     a.mem_bits = st->d.mem_bits;
     a.code_cap = int(code_capacity(st->d));
+    a.int_bits = int(int_bits(st->d));
     a.head_unit = st->d.kind == WB_HEADALLOC;
     a.layer = (st->d.kind == WB_BITALLOC && st->d.budget == WB_BUDGET_LAYER) || a.head_unit;
     return a;

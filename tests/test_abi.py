@@ -81,6 +81,14 @@ def test_descriptor_validation():
     assert _code(wb.make_desc("headalloc", "rtn", 1, 1, bbar=4, bmin=1)) == -3
     assert _code(wb.make_desc("headalloc", "rtn", 1, 4, bbar=4, bmin=2)) == 0
     assert _code(wb.make_desc("headalloc", "rtn", 1, 1, bbar=4, budget="layer")) == -3
+    # INT4 tier of the Hadamard layouts: codes two a byte
+    assert _code(wb.make_desc("had_int8", "rtn", 1, 1, block=32, int_bits=3)) == -1
+    assert _code(wb.make_desc("uniform", "rtn", 1, 1, int_bits=4)) == -1
+    d = wb.make_desc("had_int8", "rtn", 2, 3, block=32, int_bits=4)
+    assert _code(d) == 0
+    assert wb.buffer_sizes(d)[0] == 2 * 3 * -(-(128 * 128 // 2 + 128 * 4 * 4) // 256) * 256
+    d = wb.make_desc("mixed", "ef", 1, 2, block=32, k_hi=16, int_bits=4)
+    assert wb.buffer_sizes(d)[0] == 2 * -(-(16 * 128 * 2 + 112 * 64 + 112 * 4 * 4) // 256) * 256 + 256
     d = wb.make_desc("bitalloc", "rtn", 1, 1, bbar=4, bmax=9)
     assert _code(d) == -3
     d = wb.make_desc("fp32", "rtn", 1, 1, 32, 32)

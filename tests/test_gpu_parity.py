@@ -35,7 +35,8 @@ def _state(lay, perm=None):
     wb = _wb()
     return wb.WriteBackState(lay.kind, lay.mode, lay.B, lay.H, lay.dk, lay.dv, lay.per_row_decay,
                              bits=lay.bits, block=lay.block, k_hi=lay.k_hi, bbar=lay.bbar, bmin=lay.bmin,
-                             bmax=lay.bmax, seed=lay.seed, perm=perm, mem_bits=lay.mem_bits, budget=lay.budget)
+                             bmax=lay.bmax, seed=lay.seed, perm=perm, mem_bits=lay.mem_bits, budget=lay.budget,
+                             int_bits=0 if lay.int_bits == 8 else lay.int_bits)
 
 
 def _warm_state(rng, B, H, dk, dv):
@@ -186,6 +187,7 @@ CASES = [
     (L.FP32, {}), (L.UNIFORM, {"bits": 4}), (L.UNIFORM, {"bits": 2}), (L.UNIFORM, {"bits": 8}),
     (L.HAD_INT8, {"block": 128}), (L.HAD_INT8, {"block": 32}), (L.MIXED, {"block": 32, "k_hi": 16}),
     (L.BITALLOC, {}), (L.BITALLOC, {"budget": "layer"}), (L.HEADALLOC, {}),
+    (L.HAD_INT8, {"block": 32, "int_bits": 4}), (L.MIXED, {"block": 32, "k_hi": 16, "int_bits": 4}),
 ]
 
 
