@@ -258,11 +258,21 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         uint64_t fld = (uint64_t(sm.reg[wi]) | (uint64_t(sm.reg[wi + 1]) << 32)) >> sh;
         if (sh) fld |= uint64_t(sm.reg[wi + 2]) << (64 - sh);
         const float dl = sm.delta[row];
+        float R = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const int field = int((fld >> (c * bw)) & ((1ull << bw) - 1));
             const int kap = (OB && bw == 1) ? 2 * field - 1 : field - n;    // one-bit rows: -1, +1
             x[m][c] = float(kap) * dl;
+            R = fmaxf(R, fabsf(x[m][c]));
+        }
+        if constexpr (!STEP) {
+            // maximum over the row's 16 lanes (a DPP row; non-negative values)
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0xB1, 0xF, 0xF, false)));
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x4E, 0xF, 0xF, false)));
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x141, 0xF, 0xF, false)));
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x140, 0xF, 0xF, false)));
+            if (cg == 0) sm.R[row] = double(R);
         }
     }
     if constexpr (STEP) {
@@ -314,17 +324,19 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         if (tid < DV)
             A.o[(size_t)head * DV + tid] = (red[tid] + red[DV + tid]) + (red[2 * DV + tid] + red[3 * DV + tid]);
     }
-    // row maxima, over the row's 16 lanes (a DPP row; non-negative values)
+    if constexpr (STEP) {
+        // row maxima of the updated state, over the row's 16 lanes (a DPP row)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        float R = 0.f;
+        for (int m = 0; m < 8; ++m) {
+            float R = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) R = fmaxf(R, fabsf(x[m][c]));
-        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0xB1, 0xF, 0xF, false)));
-        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x4E, 0xF, 0xF, false)));
-        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x141, 0xF, 0xF, false)));
-        R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x140, 0xF, 0xF, false)));
-        if (cg == 0) sm.R[sm.order[rg + RS * m]] = double(R);
+            for (int c = 0; c < 8; ++c) R = fmaxf(R, fabsf(x[m][c]));
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0xB1, 0xF, 0xF, false)));
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x4E, 0xF, 0xF, false)));
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x141, 0xF, 0xF, false)));
+            R = fmaxf(R, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), 0x140, 0xF, 0xF, false)));
+            if (cg == 0) sm.R[sm.order[rg + RS * m]] = double(R);
+        }
     }
     __syncthreads();
 

@@ -256,6 +256,9 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
 }
 
+// EST: fold the token into the attached online estimators (a second instantiation,
+// so that the plain step carries no trace of it)
+template <bool EST>
 __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     extern __shared__ __align__(16) uint8_t smraw[];
     BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw);
@@ -289,7 +292,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         const size_t rb = (size_t)head * DK + trow;
         const float kr = A.k[rb], qr = A.q[rb];
         const float sr = A.s_per_row ? A.s[rb] : A.s[head];
-        if (A.est) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, trow, sr, beta, kr);
+        if constexpr (EST) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, trow, sr, beta, kr);
         const uint32_t dold = reinterpret_cast<const uint16_t*>(region + code_bytes)[trow];
         const int bw0 = (meta0 & 7) + 1, bw1 = (meta1 & 7) + 1;
         const bool hi_half = wave == 1;
@@ -465,7 +468,8 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
 hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
     const size_t region = size_t(DK) * DV * d.bbar / 8 + 3 * DK;
     const size_t smem = kRegOffset + (region + 15) / 16 * 16 + 16;
-    hipLaunchKernelGGL(bitalloc_step_kernel, dim3(d.B * d.H), dim3(NT), smem, stream, a);
+    if (a.est) hipLaunchKernelGGL(bitalloc_step_kernel<true>, dim3(d.B * d.H), dim3(NT), smem, stream, a);
+    else hipLaunchKernelGGL(bitalloc_step_kernel<false>, dim3(d.B * d.H), dim3(NT), smem, stream, a);
     return hipGetLastError();
 }
 
