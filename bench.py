@@ -42,6 +42,25 @@ WORKLOADS = {
                      kernel="wb_kernel"),
     "kda-prefill": dict(cfg=4, kind="mixed", B=8, H=32, per_row=True, layers=1, alloc_every=0, T=8192, C=8,
                         extra=dict(block=32, k_hi=16)),
+    # the widened rows, timed the same way: temporal-memory write-back, write-activity
+    # counters, allocation at every write-back, the layer budget, one-bit rows, the
+    # per-head unit and the INT4 tier (every one but the allocating step runs in the
+    # generic decode kernel)
+    "kda-uniform4-dir": dict(cfg=None, kind="uniform", mode="dir", B=256, H=32, per_row=True, layers=3,
+                             alloc_every=0, extra=dict(bits=4, mem_bits=2), kernel="wb_kernel"),
+    "kda-uniform4-activity": dict(cfg=None, kind="uniform", B=256, H=32, per_row=True, layers=3, alloc_every=0,
+                                  extra=dict(bits=4), kernel="wb_kernel", activity=True),
+    "kda-bitalloc-alloc-each": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=0,
+                                    extra=dict(bbar=4, bmin=2, bmax=8), kernel="allocate_kernel", online=True,
+                                    alloc_each=True),
+    "kda-bitalloc-layer": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=8, alloc_every=64,
+                               extra=dict(bbar=4, bmin=2, bmax=8, budget="layer"), kernel="wb_kernel"),
+    "kda-bitalloc-1bit": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
+                              extra=dict(bbar=4, bmin=1, bmax=8), kernel="wb_kernel"),
+    "gdn-headalloc": dict(cfg=1, kind="headalloc", B=64, H=16, per_row=False, layers=60, alloc_every=64,
+                          extra=dict(bbar=4, bmin=2, bmax=8), kernel="wb_kernel"),
+    "gdn-had-int4": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
+                         extra=dict(block=128, int_bits=4), kernel="wb_kernel"),
 }
 PEAK_FP32_MFMA_TFLOPS = 157.3
 
@@ -64,25 +83,35 @@ DK = DV = 128
 
 
 def region_bytes(kind, extra):
+    """(read, written) bytes of one head's stored state in one decode step."""
     dk, dv = DK, DV
+    ib = extra.get("int_bits") or 8
     if kind == "fp32":
         return 4 * dk * dv, 4 * dk * dv
+    if kind == "uniform":
+        n = dk * dv * extra["bits"] // 8
+        return n, n
     if kind == "had_int8":
-        n = dk * dv + dk * (dv // extra["block"]) * 4
+        n = dk * dv * ib // 8 + dk * (dv // extra["block"]) * 4
         return n, n
     if kind == "mixed":
         qr = dk - extra["k_hi"]
-        n = extra["k_hi"] * dv * 2 + qr * dv + qr * (dv // extra["block"]) * 4
+        n = extra["k_hi"] * dv * 2 + qr * dv * ib // 8 + qr * (dv // extra["block"]) * 4
         return n, n
-    code = dk * dv * extra["bbar"] // 8
+    code = dk * dv * extra["bbar"] // 8              # the mean width's codes
+    if kind == "headalloc":
+        groups = (dk // 32) * dv
+        return code + 3 * groups + 16, code + 2 * groups     # read: + scales, fits, width; write: + scales
     return code + 3 * dk, code + 2 * dk          # read: codes + Delta + meta; write: codes + Delta
 
 
-def algorithmic_bytes_per_head(kind, extra, per_row, online=False):
+def algorithmic_bytes_per_head(kind, extra, per_row, online=False, mode="rtn", activity=False):
     rd, wr = region_bytes(kind, extra)
     io = 2 * DK * 4 + DV * 4 + 4 + (DK * 4 if per_row else 4) + DV * 4
     est = 2 * (2 * DK * 4 + 4) if online else 0      # estimators read and written
-    return rd + wr + io + est
+    side = 2 * 4 * DK * DV if mode in ("ef", "dir", "resq") else 0     # float32 side value per element
+    votes = 2 * DK * DV + 8 * 4 if activity else 0   # vote state read and written, the counters
+    return rd + wr + io + est + side + votes
 
 
 def load_traffic(workload):
@@ -110,8 +139,8 @@ def warm_states(wb, torch, w, seed):
         perm = np.stack([rng.permutation(DK) for _ in range(H)])
     states = []
     for layer in range(w["layers"]):
-        st = wb.WriteBackState(w["kind"], "rtn", B, H, DK, DV, w["per_row"], seed=seed + layer, perm=perm,
-                               **w["extra"])
+        st = wb.WriteBackState(w["kind"], w.get("mode", "rtn"), B, H, DK, DV, w["per_row"], seed=seed + layer,
+                               perm=perm, **w["extra"])
         scale = torch.exp(torch.rand((B, H, DK, 1), generator=g, device="cuda") * 3.5 - 3.0)
         S = torch.randn((B, H, DK, DV), generator=g, device="cuda") * scale
         st.quantize(S.contiguous())
@@ -131,12 +160,17 @@ def run_gpu(args, w):
     R = 64
     inp = device_inputs(args.seed, B, H, DK, DV, R, w["per_row"])
     s_ring = inp["s"].unsqueeze(0).expand((R,) + tuple(inp["s"].shape)).contiguous()
-    s_alloc = inp["s"] if w["per_row"] else None
+    # the allocation takes a decay per row (a per-head decay repeated over the rows)
+    s_alloc = inp["s"] if w["per_row"] else inp["s"].unsqueeze(-1).expand(B, H, DK).contiguous()
     o_ring = torch.zeros((R, B, H, DV), dtype=torch.float32, device="cuda")
     states = warm_states(wb, torch, w, args.seed)
-    if w["kind"] == "bitalloc":
+    if w["kind"] in ("bitalloc", "headalloc"):
         for st in states:
             st.allocate_bits(s_alloc)
+    if w.get("activity"):
+        for st in states:
+            st.set_activity(torch.zeros((B, H, 8), dtype=torch.int32, device="cuda"),
+                            torch.zeros((B, H, DK, DV), dtype=torch.uint8, device="cuda"))
     ests = []
     if w.get("online"):
         for st in states:
@@ -151,7 +185,11 @@ def run_gpu(args, w):
         layer = i % len(states)
         r = i % R
         st = states[layer]
-        st.step_decode(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r], counts[layer])
+        if w.get("alloc_each"):
+            st.step_decode_alloc(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r])
+        else:
+            st.step_decode(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r],
+                           counts[layer])
         counts[layer] += 1
         if alloc_every and counts[layer] % alloc_every == 0:
             if ev_alloc is not None:
@@ -350,7 +388,8 @@ def main():
     tokens = B * K
     dec = sorted(gpu["decode_ms"])
     avg_dec_ms = sum(dec) / len(dec)
-    bytes_launch = algorithmic_bytes_per_head(w["kind"], w["extra"], w["per_row"], w.get("online", False)) * B * H
+    bytes_launch = algorithmic_bytes_per_head(w["kind"], w["extra"], w["per_row"], w.get("online", False),
+                                              w.get("mode", "rtn"), w.get("activity", False)) * B * H
     achieved = bytes_launch / (avg_dec_ms / 1e3) / 1e9
     traffic = load_traffic(args.workload)
     out = {
@@ -364,10 +403,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w["kind"] in ("bitalloc", "fp32") else "f64",
+        "dtype": "f64" if w["kind"] in ("had_int8", "mixed") else "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: decode write-back, {w['kind']} layout, B={B}, H={H}, "
-                               f"dk=dv=128, {'per-row' if w['per_row'] else 'per-head'} decay, RTN, "
+                               f"dk=dv=128, {'per-row' if w['per_row'] else 'per-head'} decay, "
+                               f"{w.get('mode', 'rtn').upper()}, "
                                f"{w['layers']} layer states cycled"
                                + (f", allocation pass every {w['alloc_every']} tokens per layer" if w["alloc_every"] else "")
                                + (", span-64 decay/erasure estimators folded in every step, allocation from them"
