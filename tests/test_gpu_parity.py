@@ -709,6 +709,67 @@ def test_headalloc_allocation_matches_oracle_and_decode_after(per_row):
     run_decode(lay, 4, warm=False, seed=44, state=st)
 
 
+@pytest.mark.parametrize("unit", ["layer", "headalloc"])
+def test_allocation_from_estimators_layer_and_head_units(unit):
+    """The layer-budget and per-head allocations taking s and r from the online
+    estimators (folded in by the decode steps, here through the generic kernel), against
+    the oracle fed the GPU's estimator values."""
+    from oracle.estimators import ema_estimates
+    from oracle.step import allocate_headalloc_regions, allocate_layer_regions
+    print(f"\n[case] allocation from estimators: {unit}", flush=True)
+    B, H, dk, T = 2, 4, 128, 12
+    kind, kw = (L.BITALLOC, dict(budget="layer")) if unit == "layer" else (L.HEADALLOC, {})
+    lay = _layout(kind, "rtn", B, H, dk, **kw)
+    rng = np.random.default_rng(71)
+    st = _state(lay)
+    inp = decode_inputs(71, B, H, dk, dk, T, True)
+    dev = {key: _to_dev(val) for key, val in inp.items()}
+    st.quantize(_to_dev(_warm_state(rng, B, H, dk, dk)))
+    est = torch.zeros((B, H, 2 * dk + 4), dtype=torch.float32, device="cuda")
+    st.set_estimators(est)
+    o = torch.zeros((B, H, dk), dtype=torch.float32, device="cuda")
+    # per-head decay shifts so that heads differ
+    s_t = (inp["s"] * np.exp(rng.uniform(-1.5, 1.5, (B, H, 1)))).astype(np.float32)
+    for t in range(T):
+        st.step_decode(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], _to_dev(s_t), o, t)
+    torch.cuda.synchronize()
+    e = est.cpu().numpy().astype(np.float64)
+    before = st.regions().cpu().numpy()
+    st.allocate_bits(None, factor="hC", C=16)
+    torch.cuda.synchronize()
+    after = st.regions().cpu().numpy()
+    for b in range(B):
+        sr = [ema_estimates(e[b, h, :dk], e[b, h, dk:2 * dk], float(e[b, h, 2 * dk])) for h in range(H)]
+        regs_in = [before[b * H + h][: lay.region_size()] for h in range(H)]
+        if unit == "layer":
+            orc, al = allocate_layer_regions(lay, regs_in, [x[0] for x in sr], [x[1] for x in sr], "hC", 16)
+            widths_o = [a["widths"] for a in al]
+            bstar = np.concatenate([a["bstar"] for a in al])
+            gw = [L.decode_region(lay, after[b * H + h][: lay.region_size()]).widths for h in range(H)]
+        else:
+            orc, al = allocate_headalloc_regions(lay, regs_in, [x[0] for x in sr], [x[1] for x in sr], "hC", 16)
+            widths_o = [np.array([w]) for w in al["widths"]]
+            bstar = al["bstar"]
+            gw = [np.array([L.decode_region(lay, after[b * H + h][: lay.region_size()]).width]) for h in range(H)]
+        go, oo = np.concatenate(gw), np.concatenate(widths_o)
+        if not np.array_equal(go, oo):
+            bad = np.argwhere(go != oo).ravel()
+            assert np.all(np.abs(bstar[bad] - np.floor(bstar[bad]) - 0.5) < 1e-5), (b, bad)
+            continue
+        for h in range(H):
+            reg_gpu = after[b * H + h][: lay.region_size()]
+            g = L.decode_region(lay, reg_gpu)
+            o_fit = al[h]["fit"] if unit == "layer" else al["fit"][h]
+            if not np.array_equal(g.fit, o_fit):
+                # only fits whose squared errors tie within 1e-6 may differ
+                for idx in np.argwhere(g.fit != o_fit):
+                    idx = tuple(idx)
+                    e = al[h]["fit_err"][idx] if unit == "layer" else al["fit_err"][h][idx]
+                    assert abs(e[g.fit[idx]] - e[o_fit[idx]]) <= 1e-6 * max(e[o_fit[idx]], 1e-300), (b, h, idx)
+                continue
+            assert np.array_equal(reg_gpu, orc[h]), (b, h)
+
+
 def test_allocation_then_decode_full_budget_zero_state():
     # a zero state keeps every row at the mean width
     lay = _layout(L.BITALLOC, "rtn", 1, 2, 128)
