@@ -32,19 +32,21 @@ namespace {
 constexpr int DK = 128, DV = 128, NT = 256;
 constexpr double kInvSqrt128 = 0.08838834764831844055;
 
-template <int KHI, int BLOCK>
+// IB: bits of the integer tier's codes (8, or 4 with two codes a byte, low nibble first)
+template <int KHI, int BLOCK, int IB = 8>
 struct RotLayout {
-    static constexpr int NQ = DK - KHI;                     // INT8 rows
-    static constexpr int NB = DV / BLOCK;                   // blocks per INT8 row
+    static constexpr int NQ = DK - KHI;                     // integer rows
+    static constexpr int NB = DV / BLOCK;                   // blocks per integer row
+    static constexpr int TOP = (1 << IB) - 1;               // largest code
     static constexpr int CODE_BASE = KHI * DV * 2;
-    static constexpr int META_BASE = CODE_BASE + NQ * DV;
+    static constexpr int META_BASE = CODE_BASE + NQ * DV * IB / 8;
     static constexpr int REGION = META_BASE + NQ * NB * 4;  // bytes (a multiple of 16)
     static_assert(REGION % 16 == 0, "region must be a whole number of 16-byte words");
 };
 
-template <int KHI, int BLOCK>
+template <int KHI, int BLOCK, int IB>
 struct RotSmem {
-    using LY = RotLayout<KHI, BLOCK>;
+    using LY = RotLayout<KHI, BLOCK, IB>;
     // (uP, pP, uQ, pQ) of the second half, then the sums; before the contraction its
     // first half holds (k a, q a) per physical row
     double part[4][DV];
@@ -137,10 +139,10 @@ __device__ __forceinline__ void wht128(double& a0, double& a1, int lane) {
     a1 = y * kInvSqrt128;
 }
 
-template <int KHI, int BLOCK>
+template <int KHI, int BLOCK, int IB>
 __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
-    using LY = RotLayout<KHI, BLOCK>;
-    __shared__ RotSmem<KHI, BLOCK> sm;
+    using LY = RotLayout<KHI, BLOCK, IB>;
+    __shared__ RotSmem<KHI, BLOCK, IB> sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int head = blockIdx.x;
@@ -148,7 +150,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     uint8_t* region = A.state + (size_t)head * A.region_stride;
     uint8_t* lb = reinterpret_cast<uint8_t*>(sm.reg);
     double2* kq = reinterpret_cast<double2*>(&sm.part[0][0]);
-    constexpr int kZW = RotSmem<KHI, BLOCK>::ZW;     // wavefronts that hold INT8 blocks
+    constexpr int kZW = RotSmem<KHI, BLOCK, IB>::ZW;     // wavefronts that hold INT8 blocks
 
     // v and beta for the vector phase, requested first
     float v_lo = 0.f, v_hi = 0.f, beta_in = 0.f;
@@ -229,8 +231,14 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             static_assert(LY::NQ % 4 == 0, "rows are taken two at a time per half");
 #pragma unroll 4
             for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); qr += 2) {
-                const double code0 = double(lb[LY::CODE_BASE + qr * DV + j]);
-                const double code1 = double(lb[LY::CODE_BASE + (qr + 1) * DV + j]);
+                double code0, code1;
+                if constexpr (IB == 8) {
+                    code0 = double(lb[LY::CODE_BASE + qr * DV + j]);
+                    code1 = double(lb[LY::CODE_BASE + (qr + 1) * DV + j]);
+                } else {
+                    code0 = double((lb[LY::CODE_BASE + (qr * DV + j) / 2] >> ((j & 1) * 4)) & 15u);
+                    code1 = double((lb[LY::CODE_BASE + ((qr + 1) * DV + j) / 2] >> ((j & 1) * 4)) & 15u);
+                }
                 const double2 c0 = sm.kqs[qr * LY::NB + g];         // (k a step, q a step)
                 const double2 c1 = sm.kqs[(qr + 1) * LY::NB + g];
                 uQ = fma(c0.x, code0, uQ);
@@ -324,16 +332,24 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             }
             const int qr = p - KHI;
             const int g = (16 * cg) / BLOCK;
-            uint4* ptr = reinterpret_cast<uint4*>(lb + LY::CODE_BASE + qr * DV + 16 * cg);
-            const uint4 raw = *ptr;
-            const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+            // the lane's 16 codes: 16 bytes, or 8 bytes of nibbles
+            uint8_t* cptr = lb + LY::CODE_BASE + (qr * DV + 16 * cg) * IB / 8;
+            uint32_t rw[4];
+            if constexpr (IB == 8) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(cptr);
+                rw[0] = raw.x; rw[1] = raw.y; rw[2] = raw.z; rw[3] = raw.w;
+            } else {
+                const uint2 raw = *reinterpret_cast<const uint2*>(cptr);
+                rw[0] = raw.x; rw[1] = raw.y; rw[2] = 0u; rw[3] = 0u;
+            }
             const float2 s = sm.sz[qr * LY::NB + g];
             // a (zero + code * scale) + k (H w)_c = code * (a scale) + (a zero + k (H w)_c)
             const double as = ak.x * double(s.x), az = ak.x * double(s.y);
             double y[16];
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
-                const uint32_t code = (rw[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+                const uint32_t code = IB == 8 ? (rw[c >> 2] >> ((c & 3) * 8)) & 0xFFu
+                                              : (rw[c >> 3] >> ((c & 7) * 4)) & 0xFu;
                 y[c] = fma(double(code), as, fma(ak.y, hwv[c], az));
             }
             double mn = y[0], mx = y[0];
@@ -343,9 +359,9 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                 mx = fmax(mx, y[c]);
             }
             block_minmax<BLOCK>(mn, mx);
-            // (a product with 1/255 instead of the quotient: the two differ by at most one
+            // (a product with 1/TOP instead of the quotient: the two differ by at most one
             // float64 unit, which moves a float16 rounding only at a midpoint)
-            const uint16_t sbits = f64_to_f16_rto(fmax(mx - mn, 0.0) * (1.0 / 255.0));
+            const uint16_t sbits = f64_to_f16_rto(fmax(mx - mn, 0.0) * (1.0 / double(LY::TOP)));
             const uint16_t zbits = f64_to_f16_rto(mn);
             const double scale = f16_to_f64(sbits), zero = f16_to_f64(zbits);
             uint32_t o4[4] = {0, 0, 0, 0};
@@ -359,22 +375,25 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                 const double span = fmax(fabs(mx - zero), fabs(mn - zero)) * inv;
                 if (span < 1073741824.0) {
                     // t + 1.5 * 2^52 rounds t to the nearest integer (ties to even); its
-                    // low 32 bits are that integer, clamped to [0, 255] in integer form
+                    // low 32 bits are that integer, clamped to [0, TOP] in integer form
 #pragma unroll
                     for (int c = 0; c < 16; ++c) {
                         const double r = fma(y[c], inv, nz) + 6755399441055744.0;
-                        const int kk = min(max(int(uint32_t(__double_as_longlong(r))), 0), 255);
-                        o4[c >> 2] |= uint32_t(kk) << ((c & 3) * 8);
+                        const int kk = min(max(int(uint32_t(__double_as_longlong(r))), 0), LY::TOP);
+                        if constexpr (IB == 8) o4[c >> 2] |= uint32_t(kk) << ((c & 3) * 8);
+                        else o4[c >> 3] |= uint32_t(kk) << ((c & 7) * 4);
                     }
                 } else {
 #pragma unroll
                     for (int c = 0; c < 16; ++c) {
-                        const double kf = fmin(fmax(rint((y[c] - zero) / scale), 0.0), 255.0);
-                        o4[c >> 2] |= uint32_t(kf) << ((c & 3) * 8);
+                        const double kf = fmin(fmax(rint((y[c] - zero) / scale), 0.0), double(LY::TOP));
+                        if constexpr (IB == 8) o4[c >> 2] |= uint32_t(kf) << ((c & 3) * 8);
+                        else o4[c >> 3] |= uint32_t(kf) << ((c & 7) * 4);
                     }
                 }
             }
-            *ptr = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            if constexpr (IB == 8) *reinterpret_cast<uint4*>(cptr) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            else *reinterpret_cast<uint2*>(cptr) = make_uint2(o4[0], o4[1]);
             if ((cg % LPB) == 0)
                 sm.reg[LY::META_BASE / 4 + qr * LY::NB + g] = uint32_t(sbits) | (uint32_t(zbits) << 16);
         }
@@ -390,14 +409,15 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
 
 template <int KHI, int BLOCK>
 hipError_t launch_rot(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool rot_step_supported(const wb_layout_desc& d) {
-    if (d.mode != WB_RTN || d.dk != DK || d.dv != DV || d.int_bits == 4) return false;
+    if (d.mode != WB_RTN || d.dk != DK || d.dv != DV) return false;
     if (d.kind == WB_HAD_INT8) return d.block == 32 || d.block == 128;
     if (d.kind == WB_MIXED) return d.k_hi == 16 && d.block == 32;
     return false;

@@ -187,7 +187,8 @@ CASES = [
     (L.FP32, {}), (L.UNIFORM, {"bits": 4}), (L.UNIFORM, {"bits": 2}), (L.UNIFORM, {"bits": 8}),
     (L.HAD_INT8, {"block": 128}), (L.HAD_INT8, {"block": 32}), (L.MIXED, {"block": 32, "k_hi": 16}),
     (L.BITALLOC, {}), (L.BITALLOC, {"budget": "layer"}), (L.HEADALLOC, {}),
-    (L.HAD_INT8, {"block": 32, "int_bits": 4}), (L.MIXED, {"block": 32, "k_hi": 16, "int_bits": 4}),
+    (L.HAD_INT8, {"block": 32, "int_bits": 4}), (L.HAD_INT8, {"block": 128, "int_bits": 4}),
+    (L.MIXED, {"block": 32, "k_hi": 16, "int_bits": 4}),
 ]
 
 
@@ -814,6 +815,7 @@ def test_damp_select_matches_oracle():
 
 FULL = [
     ("gdn-had-int8", dict(kind=L.HAD_INT8, B=64, H=16, per_row=False, block=128), ["rtn"]),
+    ("gdn-had-int4", dict(kind=L.HAD_INT8, B=64, H=16, per_row=False, block=128, int_bits=4), ["rtn"]),
     ("kda-mixed", dict(kind=L.MIXED, B=256, H=32, per_row=True, block=32, k_hi=16), ["rtn"]),
     ("kda-bitalloc", dict(kind=L.BITALLOC, B=256, H=32, per_row=True), ["rtn", "sr"]),
 ]
