@@ -805,8 +805,7 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
         case WB_HEADALLOC:
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
         default:
-            if (op == OP_STEP && d.mode == WB_RTN && d.budget == WB_BUDGET_HEAD && d.bmin >= 2)
-                return launch_bitalloc_step(d, a, stream);
+            if (op == OP_STEP && bitalloc_step_supported(d)) return launch_bitalloc_step(d, a, stream);
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
     }
 }

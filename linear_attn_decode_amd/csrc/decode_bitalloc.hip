@@ -27,6 +27,10 @@
 //   * the packed codes of a lane (8 elements = b bytes) go to a staging copy of the
 //     region in LDS at their final byte offset, then the region is written to HBM with
 //     16-byte stores.
+// Two more instantiations widen it: the layer-wise budget (the code area holds every
+// row at b_max; the widths are read first and only the codes in use are staged and
+// written back, so the zero tail is never touched) and one-bit rows (the two levels
+// -Delta, +Delta: the code is the sign, Delta = f16(mean |x|) from a row sum).
 // Layout citations: [LBRS] "State bit allocation", "Levels and storage".
 #include "wb_device.hpp"
 #include "wb_kernels.hpp"
@@ -130,6 +134,15 @@ __device__ __forceinline__ uint32_t lshl_add(uint32_t y, int s, uint32_t a) {
 // B-bit codes (B bytes) at byte `boff` of the staging copy.
 template <int B>
 __device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8], float inv) {
+    if constexpr (B == 1) {
+        // one-bit row, round to nearest on -Delta + k 2 Delta: k = 1 exactly where x > 0
+        // (an exact zero is the tie, which goes to the even index 0; a zero step stores 0)
+        uint32_t w = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w |= uint32_t(x[c] * inv > 0.f) << c;
+        reinterpret_cast<uint8_t*>(reg)[boff] = uint8_t(w);
+        return;
+    }
     constexpr float n = float((1 << (B - 1)) - 1);
     uint32_t y[8];
 #pragma unroll
@@ -190,6 +203,7 @@ __device__ __forceinline__ void unpack8_any(const Raw& raw, int boff, int bw, fl
     for (int c = 0; c < 8; ++c) code[c] = float(uint32_t(fld >> (c * bw)) & mask);
 }
 
+template <bool OB>
 __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const float x[8], float inv) {
     const float n = float((1 << (bw - 1)) - 1);
     uint64_t fld = 0;
@@ -197,7 +211,9 @@ __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const
     for (int c = 0; c < 8; ++c) {
         const uint32_t y =
             __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
-        fld |= uint64_t(y - kMagicBits) << (c * bw);
+        uint32_t code = y - kMagicBits;
+        if (OB && bw == 1) code = x[c] * inv > 0.f;
+        fld |= uint64_t(code) << (c * bw);
     }
     uint8_t* bytes = reinterpret_cast<uint8_t*>(reg);
 #pragma unroll
@@ -209,9 +225,14 @@ __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const
 // handled together are adjacent in the width order, so this is the common case), the
 // width is a scalar and the specialised code is chosen by a scalar branch; otherwise
 // the generic per-lane code runs.
+template <bool OB>
 __device__ __forceinline__ void unpack_rows(const Raw& raw, int boff, int bw, float code[8]) {
     const int bu = __builtin_amdgcn_readfirstlane(bw);
     if (__ballot(bw != bu) == 0ull) {
+        if (OB && bu == 1) {
+            unpack8<1>(raw, boff, code);
+            return;
+        }
         switch (bu) {
             case 2: unpack8<2>(raw, boff, code); break;
             case 3: unpack8<3>(raw, boff, code); break;
@@ -226,9 +247,14 @@ __device__ __forceinline__ void unpack_rows(const Raw& raw, int boff, int bw, fl
     }
 }
 
+template <bool OB>
 __device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const float x[8], float inv) {
     const int bu = __builtin_amdgcn_readfirstlane(bw);
     if (__ballot(bw != bu) == 0ull) {
+        if (OB && bu == 1) {
+            pack8<1>(reg, boff, x, inv);
+            return;
+        }
         switch (bu) {
             case 2: pack8<2>(reg, boff, x, inv); break;
             case 3: pack8<3>(reg, boff, x, inv); break;
@@ -239,7 +265,7 @@ __device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const
             default: pack8<8>(reg, boff, x, inv); break;
         }
     } else {
-        pack8_any(reg, boff, bw, x, inv);
+        pack8_any<OB>(reg, boff, bw, x, inv);
     }
 }
 
@@ -252,13 +278,35 @@ __device__ __forceinline__ uint32_t rowmax16_bits(uint32_t v) {
     return v;
 }
 
+// sum over the 16 lanes of a DPP row (the same butterfly as the maximum)
+__device__ __forceinline__ float rowsum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
+// sum over the wavefront, returned as a scalar (DPP inside rows of 16 lanes, then the
+// four row sums)
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
 }
 
-// EST: fold the token into the attached online estimators (a second instantiation,
-// so that the plain step carries no trace of it)
-template <bool EST>
+// EST: fold the token into the attached online estimators; LAYER: the layer-wise budget
+// layout (code area of b_max bits per element, codes in use first, then a zero tail);
+// OB: one-bit rows may occur. Each is its own instantiation, so that the plain step
+// carries no trace of the others.
+template <bool EST, bool LAYER, bool OB>
 __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     extern __shared__ __align__(16) uint8_t smraw[];
     BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw);
@@ -268,16 +316,36 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     const int head = blockIdx.x;
     const int cg = lane & 15, rq = lane >> 4;
     uint8_t* region = A.state + (size_t)head * A.region_stride;
-    const int code_bytes = DK * DV * A.bbar / 8;
-    const int nvec = (code_bytes + 3 * DK) / 16;
+    // the code area: the head's codes (per-head budget), or room for every row at b_max
+    // with the codes in use first (layer budget); Delta and the width / fit bytes follow
+    const int code_bytes = LAYER ? A.code_cap : DK * DV * A.bbar / 8;
+    constexpr int kMetaVec = 3 * DK / 16;
+    const uint8_t* meta = region + code_bytes + 2 * DK;
 
     // ---- loads: the region (staged through registers), metadata, per-row inputs ------
-    uint4 pf0 = make_uint4(0, 0, 0, 0), pf1 = pf0, pf2 = pf0;
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(region);
+    // Per-head budget: the region in one piece. Layer budget: the codes every head holds
+    // (b_min bits per element) and the metadata, then, once the widths are summed, the
+    // rest of the codes in use.
+    uint4 pf0 = make_uint4(0, 0, 0, 0), pf1 = pf0, pf2 = pf0, pfm = pf0;
+    const uint4* src = reinterpret_cast<const uint4*>(region);
+    int nvec = 0, nmin = 0, ncode = 0;
+    int meta0 = 0, meta1 = 0;
+    if constexpr (!LAYER) {
+        nvec = (code_bytes + 3 * DK) / 16;
         if (tid < nvec) pf0 = src[tid];
         if (tid + NT < nvec) pf1 = src[tid + NT];
         if (tid + 2 * NT < nvec) pf2 = src[tid + 2 * NT];
+    } else {
+        nmin = min(A.bmin * (DK * DV / 8 / 16), NT);
+        if (tid < nmin) pf0 = src[tid];
+        if (tid < kMetaVec) pfm = src[code_bytes / 16 + tid];
+        meta0 = meta[lane];
+        meta1 = meta[lane + 64];
+        // 16-byte vectors of codes in use: sum of the widths times DV / 128 (at most the
+        // code area)
+        ncode = min(wave_sum_i32((meta0 & 7) + (meta1 & 7) + 2) * (DV / 128), code_bytes / 16);
+        if (nmin + tid < ncode) pf1 = src[nmin + tid];
+        if (nmin + tid + NT < ncode) pf2 = src[nmin + tid + NT];
     }
     const float vj = A.v[(size_t)head * DV + (tid & (DV - 1))];
     const float beta = A.beta[head];
@@ -286,8 +354,10 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     // The width order, the byte offsets and the ranks come from ballots over the width
     // bytes of all 128 rows, which both wavefronts read.
     if (wave < 2) {
-        const uint8_t* meta = region + code_bytes + 2 * DK;
-        const int meta0 = meta[lane], meta1 = meta[lane + 64];
+        if constexpr (!LAYER) {
+            meta0 = meta[lane];
+            meta1 = meta[lane + 64];
+        }
         const int trow = lane + 64 * wave;
         const size_t rb = (size_t)head * DK + trow;
         const float kr = A.k[rb], qr = A.q[rb];
@@ -299,7 +369,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         const int bwt = hi_half ? bw1 : bw0;
         int off = 0, pos = 0, before = 0, sum_lo = 0;
 #pragma unroll
-        for (int v = 2; v <= 8; ++v) {
+        for (int v = OB ? 1 : 2; v <= 8; ++v) {
             const unsigned long long ma = __ballot(bw0 == v), mb = __ballot(bw1 == v);
             const int ca = __popcll(ma), cb = __popcll(mb);
             const int bt = lanes_below(hi_half ? mb : ma);
@@ -312,7 +382,9 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         const int fit = (hi_half ? meta1 : meta0) >> 4;
         const float n = float((1 << (bwt - 1)) - 1);
         const float ad = expf(-sr) * f16_bits_to_f32(dold);
-        sm.ta[pos] = TabA{ad, -n * ad, kr, qr};
+        // a one-bit row's levels are -Delta, +Delta: code * 2 a Delta - a Delta
+        if (OB && bwt == 1) sm.ta[pos] = TabA{2.f * ad, -ad, kr, qr};
+        else sm.ta[pos] = TabA{ad, -n * ad, kr, qr};
         sm.tb[pos] = TabB{kFn.v[fit][bwt], uint32_t(off * (DV / 8)) | (uint32_t(bwt) << 16) | (uint32_t(trow) << 24)};
         // q . k over the wavefront's 64 rows: DPP sums inside each row of 16 lanes, then
         // the four row sums
@@ -330,9 +402,16 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     }
     {
         uint4* dst = reinterpret_cast<uint4*>(reg);
-        if (tid < nvec) dst[tid] = pf0;
-        if (tid + NT < nvec) dst[tid + NT] = pf1;
-        if (tid + 2 * NT < nvec) dst[tid + 2 * NT] = pf2;
+        if constexpr (!LAYER) {
+            if (tid < nvec) dst[tid] = pf0;
+            if (tid + NT < nvec) dst[tid + NT] = pf1;
+            if (tid + 2 * NT < nvec) dst[tid + 2 * NT] = pf2;
+        } else {
+            if (tid < nmin) dst[tid] = pf0;
+            if (tid < kMetaVec) dst[code_bytes / 16 + tid] = pfm;
+            if (nmin + tid < ncode) dst[nmin + tid] = pf1;
+            if (nmin + tid + NT < ncode) dst[nmin + tid + NT] = pf2;
+        }
     }
     __syncthreads();
 
@@ -361,7 +440,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         if (m + 2 < MR) loc_next = sm.tb[NG * (m + 2) + 4 * wave + rq].loc;
         const TabA ta = sm.ta[NG * m + 4 * wave + rq];
         float code[8];
-        unpack_rows(raw, boff_of(loc), int((loc >> 16) & 15u), code);
+        unpack_rows<OB>(raw, boff_of(loc), int((loc >> 16) & 15u), code);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             x[m][c] = __builtin_fmaf(code[c], ta.alpha, ta.beta0);
@@ -440,7 +519,18 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         mx = fmaxf(fmaxf(mx, fabsf(x[m][5])), fabsf(x[m][6]));
         mx = fmaxf(mx, fabsf(x[m][7]));
         const float R = __uint_as_float(rowmax16_bits(__float_as_uint(mx)));
-        const uint16_t dbits = f32_to_f16_bits(R * tb.fn);
+        uint16_t dbits = f32_to_f16_bits(R * tb.fn);
+        if constexpr (OB) {
+            // one-bit row: Delta = f16(mean |x|), the row sum by a pairwise sum in the lane
+            // and a DPP butterfly (relative error below 7 float32 roundings)
+            const bool one = ((tb.loc >> 16) & 15u) == 1u;
+            if (__ballot(one) != 0ull) {
+                float sa = ((fabsf(x[m][0]) + fabsf(x[m][1])) + (fabsf(x[m][2]) + fabsf(x[m][3]))) +
+                           ((fabsf(x[m][4]) + fabsf(x[m][5])) + (fabsf(x[m][6]) + fabsf(x[m][7])));
+                sa = rowsum16(sa);
+                if (one) dbits = f32_to_f16_bits(sa * (1.f / float(DV)));
+            }
+        }
         const float dl = f16_bits_to_f32(dbits);
         // reciprocal refined by one Newton step (near correctly rounded)
         float r = __builtin_amdgcn_rcpf(dl);
@@ -452,24 +542,56 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         const uint32_t l = sm.tb[NG * m + 4 * wave + rq].loc;
-        pack_rows(reg, boff_of(l), int((l >> 16) & 15u), x[m], inv[m]);
+        pack_rows<OB>(reg, boff_of(l), int((l >> 16) & 15u), x[m], inv[m]);
     }
     __syncthreads();
     {
-        const int out_vec = (code_bytes + 2 * DK) / 16;
         uint4* dst = reinterpret_cast<uint4*>(region);
-        const uint4* src = reinterpret_cast<const uint4*>(reg);
-        for (int i = tid; i < out_vec; i += NT) dst[i] = src[i];
+        const uint4* lsrc = reinterpret_cast<const uint4*>(reg);
+        if constexpr (!LAYER) {
+            const int out_vec = (code_bytes + 2 * DK) / 16;
+            for (int i = tid; i < out_vec; i += NT) dst[i] = lsrc[i];
+        } else {
+            // the codes in use, then Delta (the tail and the width / fit bytes are unchanged)
+            for (int i = tid; i < ncode + 2 * DK / 16; i += NT) {
+                const int vi = i < ncode ? i : code_bytes / 16 + (i - ncode);
+                dst[vi] = lsrc[vi];
+            }
+        }
     }
 }
 
 }  // namespace
 
+namespace {
+template <bool EST, bool LAYER, bool OB>
+void launch_variant(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
+    hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB>), dim3(d.B * d.H), dim3(NT), smem, stream, a);
+}
+template <bool EST, bool LAYER>
+void launch_ob(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
+    if (d.bmin == 1) launch_variant<EST, LAYER, true>(d, a, smem, stream);
+    else launch_variant<EST, LAYER, false>(d, a, smem, stream);
+}
+template <bool EST>
+void launch_layer(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
+    if (a.layer) launch_ob<EST, true>(d, a, smem, stream);
+    else launch_ob<EST, false>(d, a, smem, stream);
+}
+}  // namespace
+
+bool bitalloc_step_supported(const wb_layout_desc& d) {
+    return d.dk == DK && d.dv == DV && d.mode == WB_RTN && d.bmin >= 1 && d.bmax <= 8 &&
+           (d.budget == WB_BUDGET_HEAD || d.budget == WB_BUDGET_LAYER);
+}
+
 hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
-    const size_t region = size_t(DK) * DV * d.bbar / 8 + 3 * DK;
-    const size_t smem = kRegOffset + (region + 15) / 16 * 16 + 16;
-    if (a.est) hipLaunchKernelGGL(bitalloc_step_kernel<true>, dim3(d.B * d.H), dim3(NT), smem, stream, a);
-    else hipLaunchKernelGGL(bitalloc_step_kernel<false>, dim3(d.B * d.H), dim3(NT), smem, stream, a);
+    // the staged region: the code area (per head: b-bar bits per element; layer budget:
+    // b_max), Delta and the width / fit bytes
+    const size_t code_area = size_t(a.layer ? a.code_cap : DK * DV * d.bbar / 8);
+    const size_t smem = kRegOffset + (code_area + 3 * DK + 15) / 16 * 16 + 16;
+    if (a.est) launch_layer<true>(d, a, smem, stream);
+    else launch_layer<false>(d, a, smem, stream);
     return hipGetLastError();
 }
 

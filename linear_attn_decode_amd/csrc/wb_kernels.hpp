@@ -31,6 +31,7 @@ struct KArgs {
     int block = 32;
     int k_hi = 0;
     int bbar = 4;
+    int bmin = 2;                     // BITALLOC smallest row width
     int mem_bits = 0;                 // k of direction / residual memory
     int code_cap = 0;                 // BITALLOC code-area bytes of a head (meta follows)
     int layer = 0;                    // BITALLOC layer budget: the used code bytes vary per head
@@ -44,7 +45,9 @@ struct KArgs {
 // One launch of the decode / import / export kernel for every head of the layout.
 hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_t stream);
 
-// Decode step of the BITALLOC layout with round-to-nearest (the tuned kernel).
+// Decode step of the BITALLOC layout with round-to-nearest (the tuned kernel), for the
+// layouts bitalloc_step_supported() accepts (either budget, one-bit rows included).
+bool bitalloc_step_supported(const wb_layout_desc& d);
 hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
 
 // Decode step of the Hadamard-rotated layouts with round-to-nearest (the tuned kernel),

@@ -123,6 +123,7 @@ wb::KArgs base_args(const wb_state* st) {
     a.block = st->d.block;
     a.k_hi = st->d.k_hi;
     a.bbar = st->d.bbar;
+    a.bmin = st->d.bmin;
     a.mem_bits = st->d.mem_bits;
     a.code_cap = int(code_capacity(st->d));
     a.int_bits = int(int_bits(st->d));

@@ -221,6 +221,55 @@ def test_bitalloc_one_bit_rows_decode_after_allocation(mode):
     run_decode(lay, 7, warm=True, seed=19, alloc_every=3)
 
 
+def _width_patterns(rng, lay, n):
+    """Row-width patterns for `n` heads that put every width the layout allows next to
+    every other inside the groups of rows a wavefront handles together: all rows at the
+    narrowest and (layer budget) the widest width, rows in random order, widths falling
+    with the row index, and alternating extremes; under the per-head budget each pattern
+    is brought to the budget's total by moving single bits between random rows."""
+    dk, lo, hi = lay.dk, lay.bmin, lay.bmax
+    pats = [np.full(dk, lo), np.full(dk, hi) if lay.budget == "layer" else rng.integers(lo, hi + 1, dk),
+            rng.integers(lo, hi + 1, dk), np.sort(rng.integers(lo, hi + 1, dk))[::-1],
+            np.where(np.arange(dk) % 2 == 0, lo, hi)]
+    out = []
+    for i in range(n):
+        w = np.array(pats[i % len(pats)] if i < len(pats) else rng.integers(lo, hi + 1, dk), np.int64)
+        if lay.budget != "layer":
+            total = lay.bbar * dk
+            while w.sum() != total:
+                j = int(rng.integers(dk))
+                if w.sum() > total and w[j] > lo:
+                    w[j] -= 1
+                elif w.sum() < total and w[j] < hi:
+                    w[j] += 1
+        out.append(w)
+    return out
+
+
+@pytest.mark.parametrize("budget,bmin", [("head", 2), ("head", 1), ("layer", 2), ("layer", 1)])
+@pytest.mark.parametrize("mode", ["rtn", "sr"])
+def test_bitalloc_decode_arbitrary_widths(budget, bmin, mode):
+    """Decode steps from regions written by the oracle's encoder with arbitrary row widths
+    (every width next to every other, heads at the narrowest and widest totals under the
+    layer budget, one-bit rows among them), random levels, fit indices and steps."""
+    print(f"\n[case] arbitrary widths BITALLOC budget={budget} bmin={bmin} {mode}", flush=True)
+    B, H, dk = 2, 4, 128
+    lay = _layout(L.BITALLOC, mode, B, H, dk, bbar=3 if bmin == 1 else 4, bmin=bmin, budget=budget)
+    rng = np.random.default_rng(61 + bmin)
+    st = _state(lay)
+    regs = st.regions()
+    size = lay.region_size()
+    for i, w in enumerate(_width_patterns(rng, lay, B * H)):
+        n = 2 ** (w - 1) - 1
+        kappa = np.where((w == 1)[:, None], 2 * rng.integers(0, 2, (dk, dk)) - 1,
+                         rng.integers(-n[:, None], n[:, None] + 1, (dk, dk)))
+        delta = (10.0 ** rng.uniform(-3, -1, dk)).astype(np.float16)
+        c = L.Content(kappa=kappa, widths=w, fit=rng.integers(0, 16, dk), delta_bits=delta.view(np.uint16))
+        regs[i, :size].copy_(torch.from_numpy(L.encode_region(lay, c)))
+    torch.cuda.synchronize()
+    run_decode(lay, 3, warm=False, seed=62, state=st)
+
+
 @pytest.mark.parametrize("case", ["warm", "spread"])
 def test_allocate_bits_one_bit_rows_matches_oracle(case):
     """The allocation pass with a one-bit floor (bmin = 1, mean width 3) on two passes,
@@ -818,6 +867,8 @@ FULL = [
     ("gdn-had-int4", dict(kind=L.HAD_INT8, B=64, H=16, per_row=False, block=128, int_bits=4), ["rtn"]),
     ("kda-mixed", dict(kind=L.MIXED, B=256, H=32, per_row=True, block=32, k_hi=16), ["rtn"]),
     ("kda-bitalloc", dict(kind=L.BITALLOC, B=256, H=32, per_row=True), ["rtn", "sr"]),
+    ("kda-bitalloc-layer", dict(kind=L.BITALLOC, B=256, H=32, per_row=True, budget="layer"), ["rtn"]),
+    ("kda-bitalloc-1bit", dict(kind=L.BITALLOC, B=256, H=32, per_row=True, bmin=1), ["rtn"]),
 ]
 
 
