@@ -45,8 +45,8 @@ WORKLOADS = {
     # the widened rows, timed the same way: temporal-memory write-back, write-activity
     # counters, allocation at every write-back, the layer budget, one-bit rows, the
     # per-head unit and the INT4 tier (the layer budget and one-bit rows run in the tuned
-    # BITALLOC kernel, the INT4 tier in the rotated-domain kernel, the rest in the generic
-    # decode kernel)
+    # BITALLOC kernel, the per-head unit in its own tuned kernel, the INT4 tier in the
+    # rotated-domain kernel, the rest in the generic decode kernel)
     "kda-uniform4-dir": dict(cfg=None, kind="uniform", mode="dir", B=256, H=32, per_row=True, layers=3,
                              alloc_every=0, extra=dict(bits=4, mem_bits=2), kernel="wb_kernel"),
     "kda-uniform4-activity": dict(cfg=None, kind="uniform", B=256, H=32, per_row=True, layers=3, alloc_every=0,
@@ -59,7 +59,7 @@ WORKLOADS = {
     "kda-bitalloc-1bit": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
                               extra=dict(bbar=4, bmin=1, bmax=8), kernel="bitalloc_step_kernel"),
     "gdn-headalloc": dict(cfg=1, kind="headalloc", B=64, H=16, per_row=False, layers=60, alloc_every=64,
-                          extra=dict(bbar=4, bmin=2, bmax=8), kernel="wb_kernel"),
+                          extra=dict(bbar=4, bmin=2, bmax=8), kernel="headalloc_step_kernel"),
     "gdn-had-int4": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
                          extra=dict(block=128, int_bits=4), kernel="rot_step_kernel"),
 }

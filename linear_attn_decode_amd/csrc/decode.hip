@@ -803,6 +803,7 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
             if (op == OP_STEP && rot_step_supported(d)) return launch_rot_step(d, a, stream);
             return launch_op<WB_MIXED, 128, 128>(op, d.mode, a, heads, stream);
         case WB_HEADALLOC:
+            if (op == OP_STEP && headalloc_step_supported(d)) return launch_headalloc_step(d, a, stream);
             return launch_op<WB_BITALLOC, 128, 128>(op, d.mode, a, heads, stream);
         default:
             if (op == OP_STEP && bitalloc_step_supported(d)) return launch_bitalloc_step(d, a, stream);

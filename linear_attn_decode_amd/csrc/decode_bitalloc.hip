@@ -130,16 +130,26 @@ __device__ __forceinline__ uint32_t lshl_add(uint32_t y, int s, uint32_t a) {
     return r;
 }
 
-// Round 8 values on the row grid (magic-number FMA, med3 clamp) and write the packed
-// B-bit codes (B bytes) at byte `boff` of the staging copy.
-template <int B>
-__device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8], float inv) {
+// 1 / Delta of the 8 values of a lane: one per row (InvOne) or one per column (InvCol)
+struct InvOne {
+    float v;
+    __device__ __forceinline__ float operator[](int) const { return v; }
+};
+struct InvCol {
+    const float* p;
+    __device__ __forceinline__ float operator[](int c) const { return p[c]; }
+};
+
+// Round 8 values on the grid (magic-number FMA, med3 clamp) and write the packed B-bit
+// codes (B bytes) at byte `boff` of the staging copy.
+template <int B, typename Inv = InvOne>
+__device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8], Inv inv) {
     if constexpr (B == 1) {
         // one-bit row, round to nearest on -Delta + k 2 Delta: k = 1 exactly where x > 0
         // (an exact zero is the tie, which goes to the even index 0; a zero step stores 0)
         uint32_t w = 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) w |= uint32_t(x[c] * inv > 0.f) << c;
+        for (int c = 0; c < 8; ++c) w |= uint32_t(x[c] * inv[c] > 0.f) << c;
         reinterpret_cast<uint8_t*>(reg)[boff] = uint8_t(w);
         return;
     }
@@ -147,7 +157,7 @@ __device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8],
     uint32_t y[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-        y[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
+        y[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv[c], kMagic + n), kMagic, kMagic + 2.f * n));
     // the constant high bits of every shifted y are removed once per word
     uint32_t g0 = 0, g1 = 0;
 #pragma unroll
@@ -252,17 +262,17 @@ __device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const
     const int bu = __builtin_amdgcn_readfirstlane(bw);
     if (__ballot(bw != bu) == 0ull) {
         if (OB && bu == 1) {
-            pack8<1>(reg, boff, x, inv);
+            pack8<1>(reg, boff, x, InvOne{inv});
             return;
         }
         switch (bu) {
-            case 2: pack8<2>(reg, boff, x, inv); break;
-            case 3: pack8<3>(reg, boff, x, inv); break;
-            case 4: pack8<4>(reg, boff, x, inv); break;
-            case 5: pack8<5>(reg, boff, x, inv); break;
-            case 6: pack8<6>(reg, boff, x, inv); break;
-            case 7: pack8<7>(reg, boff, x, inv); break;
-            default: pack8<8>(reg, boff, x, inv); break;
+            case 2: pack8<2>(reg, boff, x, InvOne{inv}); break;
+            case 3: pack8<3>(reg, boff, x, InvOne{inv}); break;
+            case 4: pack8<4>(reg, boff, x, InvOne{inv}); break;
+            case 5: pack8<5>(reg, boff, x, InvOne{inv}); break;
+            case 6: pack8<6>(reg, boff, x, InvOne{inv}); break;
+            case 7: pack8<7>(reg, boff, x, InvOne{inv}); break;
+            default: pack8<8>(reg, boff, x, InvOne{inv}); break;
         }
     } else {
         pack8_any<OB>(reg, boff, bw, x, inv);
@@ -519,7 +529,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         mx = fmaxf(fmaxf(mx, fabsf(x[m][5])), fabsf(x[m][6]));
         mx = fmaxf(mx, fabsf(x[m][7]));
         const float R = __uint_as_float(rowmax16_bits(__float_as_uint(mx)));
-        uint16_t dbits = f32_to_f16_bits(R * tb.fn);
+        uint32_t dbits = f16_bits_of_product(R, tb.fn);
         if constexpr (OB) {
             // one-bit row: Delta = f16(mean |x|), the row sum by a pairwise sum in the lane
             // and a DPP butterfly (relative error below 7 float32 roundings)
@@ -528,7 +538,8 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
                 float sa = ((fabsf(x[m][0]) + fabsf(x[m][1])) + (fabsf(x[m][2]) + fabsf(x[m][3]))) +
                            ((fabsf(x[m][4]) + fabsf(x[m][5])) + (fabsf(x[m][6]) + fabsf(x[m][7])));
                 sa = rowsum16(sa);
-                if (one) dbits = f32_to_f16_bits(sa * (1.f / float(DV)));
+                const uint32_t d1 = f16_bits_of_product(sa, 1.f / float(DV));
+                if (one) dbits = d1;
             }
         }
         const float dl = f16_bits_to_f32(dbits);
@@ -536,7 +547,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         float r = __builtin_amdgcn_rcpf(dl);
         r = __builtin_fmaf(__builtin_fmaf(-dl, r, 1.f), r, r);
         inv[m] = dl > 0.f ? r : 0.f;
-        if (cg == 0) dout[tb.loc >> 24] = dbits;
+        if (cg == 0) dout[tb.loc >> 24] = uint16_t(dbits);
     }
     // ... then the rounding and packing, specialised per width
 #pragma unroll
@@ -583,6 +594,256 @@ void launch_layer(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStrea
 bool bitalloc_step_supported(const wb_layout_desc& d) {
     return d.dk == DK && d.dv == DV && d.mode == WB_RTN && d.bmin >= 1 && d.bmax <= 8 &&
            (d.budget == WB_BUDGET_HEAD || d.budget == WB_BUDGET_LAYER);
+}
+
+// ---------------------------------------------------------------------------
+// Decode write-back step of the per-head allocation unit (HEADALLOC) with round to
+// nearest ([LBRS] "Allocation units"): one width b for the whole head, and a float16 step
+// per group of 32 key rows and value column with its own fit index. Four wavefronts per
+// head, one per row group: lane (cg, rq) of wavefront g holds rows 32 g + 8 rq .. + 7 and
+// columns 8 cg .. 8 cg + 7, so a column's group maximum is the maximum over the lane's 8
+// rows and the 4 lanes 16 apart, and every step a lane reads or rounds with belongs to
+// its own group. The width is the same for every row of a head, so the body is
+// specialised per width and chosen once per workgroup.
+namespace {
+
+constexpr int HNW = 4, HNT = 64 * HNW;         // one wavefront per row group
+constexpr int HGR = DK / 32;                   // row groups
+constexpr int HMR = 8;                         // rows per lane
+constexpr int kHaCodeMax = DK * DV;            // code bytes at 8 bits per value
+
+struct HaSmem {
+    float4 row[DK];                             // a_i, k_i a_i, q_i a_i, k_i
+    float2 g[HGR * DV];                         // stored Delta and -n Delta per (group, column)
+    float fn[HGR * DV];                         // f / n per (group, column)
+    float ginv[HGR * DV];                       // 1 / new Delta (0 for a zero step)
+    float red[2][HNW][DV];                      // u / p partials of the wavefronts
+    float w[DV];
+    float qk[2];
+    uint32_t reg[(kHaCodeMax + 2 * HGR * DV) / 4 + 4];   // staged codes, then the new Delta bits
+};
+
+template <int B>
+__device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
+    constexpr int n = (1 << (B - 1)) - 1;
+    constexpr int NVEC = DK * DV * B / 8 / 16;           // 16-byte vectors of codes in use
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int head = blockIdx.x;
+    const int cg = lane & 15, rq = lane >> 4;
+    uint8_t* region = A.state + (size_t)head * A.region_stride;
+    const int cap = A.code_cap;
+    const uint4* src = reinterpret_cast<const uint4*>(region);
+
+    uint4 pf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[i] = (tid + HNT * i < NVEC) ? src[tid + HNT * i] : make_uint4(0, 0, 0, 0);
+    const float vj = A.v[(size_t)head * DV + (tid & (DV - 1))];
+    const float beta = A.beta[head];
+
+    // per-row constants (wavefronts 0 and 1) and q . k
+    if (tid < DK) {
+        const size_t rb = (size_t)head * DK + tid;
+        const float kr = A.k[rb], qr = A.q[rb];
+        const float sr = A.s_per_row ? A.s[rb] : A.s[head];
+        if (A.est) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, tid, sr, beta, kr);
+        const float a = expf(-sr);
+        sm.row[tid] = make_float4(a, kr * a, qr * a, kr);
+        float pq = qr * kr;
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0xB1, 0xF, 0xF, false));
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x4E, 0xF, 0xF, false));
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x141, 0xF, 0xF, false));
+        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x140, 0xF, 0xF, false));
+        const float qsum = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 0)) +
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 16))) +
+                           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 32)) +
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 48)));
+        if (lane == 0) sm.qk[wave] = qsum;
+    }
+    // stored steps and fit fractions per (group, column): thread owns t and t + 256
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = tid + HNT * i;
+        const float dold = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(region + cap)[t]);
+        const int fit = region[cap + 2 * HGR * DV + t] & 15;
+        sm.g[t] = make_float2(dold, -float(n) * dold);     // exact: 11 + 7 significant bits
+        sm.fn[t] = kFn.v[fit][B];
+    }
+    {
+        uint4* dst = reinterpret_cast<uint4*>(sm.reg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (tid + HNT * i < NVEC) dst[tid + HNT * i] = pf[i];
+    }
+    __syncthreads();
+
+    // ---- dequantize the lane's 8 rows x 8 columns (group `wave`); u, p partials -------
+    // x0 = Delta (code - n) is exact; the decay is folded into the row weights of u and
+    // p and into the update.
+    const int row0 = 32 * wave + HMR * rq;
+    float gd[8], gn[8];
+    {
+        const float4* gp = reinterpret_cast<const float4*>(&sm.g[wave * DV + 8 * cg]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = gp[i];
+            gd[2 * i] = v.x;
+            gn[2 * i] = v.y;
+            gd[2 * i + 1] = v.z;
+            gn[2 * i + 1] = v.w;
+        }
+    }
+    float x[HMR][8], up[8], pp[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        up[c] = 0.f;
+        pp[c] = 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < HMR; ++m) {
+        const int boff = (row0 + m) * (DV / 8) * B + cg * B;
+        float code[8];
+        unpack8<B>(load_raw(sm.reg, boff), boff, code);
+        const float4 tr = sm.row[row0 + m];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            x[m][c] = __builtin_fmaf(code[c], gd[c], gn[c]);
+            up[c] = __builtin_fmaf(tr.y, x[m][c], up[c]);
+            pp[c] = __builtin_fmaf(tr.z, x[m][c], pp[c]);
+        }
+    }
+    // the four row blocks of the wavefront summed by lane swaps (as in the per-row
+    // kernel): lane (cg, rq) then holds quantity rq / 2 of columns 8 cg + 4 (rq % 2) + 0..3
+    {
+        float t[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(up[c]), __float_as_uint(pp[c]), false,
+                                                            false);
+            t[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        float s4[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t[c]), __float_as_uint(t[c + 4]), false,
+                                                            false);
+            s4[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        *reinterpret_cast<float4*>(&sm.red[rq >> 1][wave][8 * cg + 4 * (rq & 1)]) =
+            make_float4(s4[0], s4[1], s4[2], s4[3]);
+    }
+    __syncthreads();
+
+    // ---- w = beta (v - u) (threads 0..127); p summed by threads 128..255 for o --------
+    const int jq = tid >> 7, j = tid & (DV - 1);
+    float pj = 0.f;
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < HNW; ++g) acc += sm.red[jq][g][j];
+        if (jq == 0) sm.w[j] = beta * (vj - acc);
+        else pj = acc;
+    }
+    __syncthreads();
+    if (jq == 1) A.o[(size_t)head * DV + j] = __builtin_fmaf(sm.qk[0] + sm.qk[1], sm.w[j], pj);
+
+    // ---- update and group maxima ---------------------------------------------------------
+    float wv[8], mx[8];
+    {
+        const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[8 * cg]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[8 * cg + 4]);
+        wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+        wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) mx[c] = 0.f;
+#pragma unroll
+    for (int m = 0; m < HMR; ++m) {
+        const float4 tr = sm.row[row0 + m];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            x[m][c] = __builtin_fmaf(tr.x, x[m][c], tr.w * wv[c]);
+            mx[c] = fmaxf(mx[c], fabsf(x[m][c]));
+        }
+    }
+    // over the group's other rows: the lanes 16 and 32 apart
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[c]), __float_as_uint(mx[c]), false, false);
+        const float v = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+        const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        mx[c] = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    }
+    // new steps: lane (cg, rq) derives columns 8 cg + 2 rq and 8 cg + 2 rq + 1
+    {
+        float R0 = mx[0], R1 = mx[1];
+        if (rq == 1) { R0 = mx[2]; R1 = mx[3]; }
+        if (rq == 2) { R0 = mx[4]; R1 = mx[5]; }
+        if (rq == 3) { R0 = mx[6]; R1 = mx[7]; }
+        uint16_t* dnew = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(sm.reg) + kHaCodeMax);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int t = wave * DV + 8 * cg + 2 * rq + e;
+            const uint32_t dbits = f16_bits_of_product(e ? R1 : R0, sm.fn[t]);
+            const float dl = f16_bits_to_f32(dbits);
+            float r = __builtin_amdgcn_rcpf(dl);
+            r = __builtin_fmaf(__builtin_fmaf(-dl, r, 1.f), r, r);
+            sm.ginv[t] = dl > 0.f ? r : 0.f;
+            dnew[t] = uint16_t(dbits);
+        }
+    }
+    __syncthreads();
+
+    // ---- round to nearest on each column's grid and pack into the staging copy ---------
+    float gi[8];
+    {
+        const float4 i0 = *reinterpret_cast<const float4*>(&sm.ginv[wave * DV + 8 * cg]);
+        const float4 i1 = *reinterpret_cast<const float4*>(&sm.ginv[wave * DV + 8 * cg + 4]);
+        gi[0] = i0.x; gi[1] = i0.y; gi[2] = i0.z; gi[3] = i0.w;
+        gi[4] = i1.x; gi[5] = i1.y; gi[6] = i1.z; gi[7] = i1.w;
+    }
+#pragma unroll
+    for (int m = 0; m < HMR; ++m) pack8<B>(sm.reg, (row0 + m) * (DV / 8) * B + cg * B, x[m], InvCol{gi});
+    __syncthreads();
+
+    // ---- the codes, then the new steps (the fit bytes and the width byte are unchanged)
+    {
+        uint4* dst = reinterpret_cast<uint4*>(region);
+        const uint4* ls = reinterpret_cast<const uint4*>(sm.reg);
+        constexpr int NOUT = NVEC + 2 * HGR * DV / 16;
+        for (int i = tid; i < NOUT; i += HNT) {
+            if (i < NVEC) dst[i] = ls[i];
+            else dst[cap / 16 + (i - NVEC)] = ls[kHaCodeMax / 16 + (i - NVEC)];
+        }
+    }
+}
+
+__global__ void __launch_bounds__(HNT) headalloc_step_kernel(const KArgs A) {
+    __shared__ HaSmem sm;
+    const uint8_t* region = A.state + (size_t)blockIdx.x * A.region_stride;
+    // the head's width byte follows the steps and fit indices; kept inside [2, b_max]
+    int b = int(region[A.code_cap + 3 * HGR * DV]) + 1;
+    b = __builtin_amdgcn_readfirstlane(min(max(b, 2), A.code_cap / (DK * DV / 8)));
+    switch (b) {
+        case 2: headalloc_body<2>(A, sm); break;
+        case 3: headalloc_body<3>(A, sm); break;
+        case 4: headalloc_body<4>(A, sm); break;
+        case 5: headalloc_body<5>(A, sm); break;
+        case 6: headalloc_body<6>(A, sm); break;
+        case 7: headalloc_body<7>(A, sm); break;
+        default: headalloc_body<8>(A, sm); break;
+    }
+}
+
+}  // namespace
+
+bool headalloc_step_supported(const wb_layout_desc& d) {
+    return d.kind == WB_HEADALLOC && d.dk == DK && d.dv == DV && d.mode == WB_RTN && d.bmax <= 8;
+}
+
+hipError_t launch_headalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(headalloc_step_kernel, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {

@@ -490,7 +490,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                         mn = fminf(mn, x[c]);
                         mx = fmaxf(mx, x[c]);
                     }
-                    const uint16_t sb = f32_to_f16_bits(fmaxf(mx - mn, 0.f) * (1.f / 255.f));
+                    const uint32_t sb = f16_bits_of_product(fmaxf(mx - mn, 0.f), 1.f / 255.f);
                     const uint16_t zb = f32_to_f16_bits(mn);
                     const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
                     // levels in magic-number form (1.5 * 2^23 + level); level 0 if the

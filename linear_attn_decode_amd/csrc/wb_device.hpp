@@ -78,6 +78,17 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
     return __half2float(__ushort_as_half(uint16_t(bits)));
 }
 
+// float16 bits of the product p * q. The bits are made opaque before anything else reads
+// them, so that a stored float16 step and the step used for rounding are one value: the
+// compiler may fuse the multiply into the conversion (one rounding) or not (two), and
+// without the barrier it has been seen to do one for the stored bits and the other for
+// the value derived from them.
+__device__ __forceinline__ uint32_t f16_bits_of_product(float p, float q) {
+    uint32_t b = f32_to_f16_bits(p * q);
+    asm volatile("" : "+v"(b));
+    return b;
+}
+
 template <typename Real>
 __device__ __forceinline__ uint16_t to_f16_bits(Real x);
 template <>

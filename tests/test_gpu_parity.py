@@ -270,6 +270,32 @@ def test_bitalloc_decode_arbitrary_widths(budget, bmin, mode):
     run_decode(lay, 3, warm=False, seed=62, state=st)
 
 
+@pytest.mark.parametrize("per_row", [False, True])
+@pytest.mark.parametrize("mode", ["rtn", "sr"])
+def test_headalloc_decode_arbitrary_widths(mode, per_row):
+    """Decode steps of the per-head unit from regions written by the oracle's encoder:
+    every width from 2 to 8 among the heads, random levels, fit indices and group steps
+    (some steps zero)."""
+    print(f"\n[case] arbitrary widths HEADALLOC {mode} per_row={per_row}", flush=True)
+    B, H, dk = 2, 4, 128
+    lay = _layout(L.HEADALLOC, mode, B, H, dk, per_row=per_row)
+    rng = np.random.default_rng(71)
+    st = _state(lay)
+    regs = st.regions()
+    size = lay.region_size()
+    ng = dk // L.HA_GROUP
+    for i in range(B * H):
+        w = [2, 3, 4, 5, 6, 7, 8, int(rng.integers(2, 9))][i]
+        n = 2 ** (w - 1) - 1
+        delta = (10.0 ** rng.uniform(-3, -1, (ng, dk))).astype(np.float16)
+        delta[rng.random((ng, dk)) < 0.02] = 0
+        c = L.Content(kappa=rng.integers(-n, n + 1, (dk, dk)), width=w, fit=rng.integers(0, 16, (ng, dk)),
+                      delta_bits=delta.view(np.uint16))
+        regs[i, :size].copy_(torch.from_numpy(L.encode_region(lay, c)))
+    torch.cuda.synchronize()
+    run_decode(lay, 3, warm=False, seed=72, state=st)
+
+
 @pytest.mark.parametrize("case", ["warm", "spread"])
 def test_allocate_bits_one_bit_rows_matches_oracle(case):
     """The allocation pass with a one-bit floor (bmin = 1, mean width 3) on two passes,
@@ -869,6 +895,7 @@ FULL = [
     ("kda-bitalloc", dict(kind=L.BITALLOC, B=256, H=32, per_row=True), ["rtn", "sr"]),
     ("kda-bitalloc-layer", dict(kind=L.BITALLOC, B=256, H=32, per_row=True, budget="layer"), ["rtn"]),
     ("kda-bitalloc-1bit", dict(kind=L.BITALLOC, B=256, H=32, per_row=True, bmin=1), ["rtn"]),
+    ("gdn-headalloc", dict(kind=L.HEADALLOC, B=64, H=16, per_row=False), ["rtn"]),
 ]
 
 
@@ -883,4 +910,5 @@ def test_full_size_sampled_heads(name, cfg, modes):
         kind, B, H, per_row = c.pop("kind"), c.pop("B"), c.pop("H"), c.pop("per_row")
         lay = _layout(kind, mode, B, H, 128, per_row=per_row, **c)
         picks = sorted({(int(rng.integers(B)), int(rng.integers(H))) for _ in range(12)})
-        run_decode(lay, 4, heads=picks, warm=True, seed=52, steps_checked={1, 3}, alloc_every=1 if kind == L.BITALLOC else None)
+        run_decode(lay, 4, heads=picks, warm=True, seed=52, steps_checked={1, 3},
+                   alloc_every=1 if kind == L.BITALLOC else None)
