@@ -34,6 +34,10 @@ WORKLOADS = {
     # step and the allocation passes taking s and r from them
     "kda-bitalloc-online": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
                                 extra=dict(bbar=4, bmin=2, bmax=8), kernel="bitalloc_step_kernel", online=True),
+    # the same decode step under Philox stochastic rounding (the second rule of the
+    # decay-aware configuration)
+    "kda-bitalloc-sr": dict(cfg=3, kind="bitalloc", mode="sr", B=256, H=32, per_row=True, layers=15, alloc_every=64,
+                            extra=dict(bbar=4, bmin=2, bmax=8), kernel="bitalloc_step_kernel"),
     "kda-mixed": dict(cfg=2, kind="mixed", B=256, H=32, per_row=True, layers=7, alloc_every=0,
                       extra=dict(block=32, k_hi=16), kernel="rot_step_kernel"),
     "gdn-had-int8": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,

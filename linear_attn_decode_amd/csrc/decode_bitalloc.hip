@@ -140,24 +140,17 @@ struct InvCol {
     __device__ __forceinline__ float operator[](int c) const { return p[c]; }
 };
 
-// Round 8 values on the grid (magic-number FMA, med3 clamp) and write the packed B-bit
-// codes (B bytes) at byte `boff` of the staging copy.
-template <int B, typename Inv = InvOne>
-__device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8], Inv inv) {
+// Write 8 codes of `B` bits, given in magic-number form (the bits of 1.5 * 2^23 + code),
+// packed at byte `boff` of the staging copy (B bytes).
+template <int B>
+__device__ __forceinline__ void store8(uint32_t* reg, int boff, const uint32_t y[8]) {
     if constexpr (B == 1) {
-        // one-bit row, round to nearest on -Delta + k 2 Delta: k = 1 exactly where x > 0
-        // (an exact zero is the tie, which goes to the even index 0; a zero step stores 0)
         uint32_t w = 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) w |= uint32_t(x[c] * inv[c] > 0.f) << c;
+        for (int c = 0; c < 8; ++c) w |= (y[c] - kMagicBits) << c;
         reinterpret_cast<uint8_t*>(reg)[boff] = uint8_t(w);
         return;
     }
-    constexpr float n = float((1 << (B - 1)) - 1);
-    uint32_t y[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-        y[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv[c], kMagic + n), kMagic, kMagic + 2.f * n));
     // the constant high bits of every shifted y are removed once per word
     uint32_t g0 = 0, g1 = 0;
 #pragma unroll
@@ -202,6 +195,46 @@ __device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8],
     }
 }
 
+// Round 8 values to the nearest level (magic-number FMA, med3 clamp) and store them.
+template <int B, typename Inv = InvOne>
+__device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8], Inv inv) {
+    uint32_t y[8];
+    if constexpr (B == 1) {
+        // one-bit row, round to nearest on -Delta + k 2 Delta: k = 1 exactly where x > 0
+        // (an exact zero is the tie, which goes to the even index 0; a zero step stores 0)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] = kMagicBits + uint32_t(x[c] * inv[c] > 0.f);
+    } else {
+        constexpr float n = float((1 << (B - 1)) - 1);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            y[c] = __float_as_uint(
+                __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv[c], kMagic + n), kMagic, kMagic + 2.f * n));
+    }
+    store8<B>(reg, boff, y);
+}
+
+// Stochastic rounding of one value on the grid of the row (level index in [0, 2n], or
+// [0, 1] for a one-bit row on -Delta + k 2 Delta): floor(tau) + [u < frac(tau)] with u the
+// 16-bit draw over 2^16, clamped at the rails; a zero step stores level 0 (offset n).
+__device__ __forceinline__ uint32_t sr_level(float x, float inv, int bw, uint32_t r16) {
+    const bool one = bw == 1;
+    const float n = one ? 0.f : float((1 << (bw - 1)) - 1);
+    const float tau = one ? (inv > 0.f ? __builtin_fmaf(x, 0.5f * inv, 0.5f) : 0.f) : x * inv;
+    const float fl = floorf(tau);
+    float k = fl + ((float(r16) < (tau - fl) * 65536.f) ? 1.f : 0.f);
+    k = one ? __builtin_amdgcn_fmed3f(k, 0.f, 1.f) : __builtin_amdgcn_fmed3f(k, -n, n);
+    return __float_as_uint(kMagic + (k + n));
+}
+
+template <int B>
+__device__ __forceinline__ void pack8_sr(uint32_t* reg, int boff, const float x[8], float inv, const uint32_t r16[8]) {
+    uint32_t y[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) y[c] = sr_level(x[c], inv, B, r16[c]);
+    store8<B>(reg, boff, y);
+}
+
 // Generic unpack / pack for a per-lane width (a group of rows of mixed widths).
 __device__ __forceinline__ void unpack8_any(const Raw& raw, int boff, int bw, float code[8]) {
     const int sh = (boff & 3) * 8;
@@ -213,16 +246,22 @@ __device__ __forceinline__ void unpack8_any(const Raw& raw, int boff, int bw, fl
     for (int c = 0; c < 8; ++c) code[c] = float(uint32_t(fld >> (c * bw)) & mask);
 }
 
-template <bool OB>
-__device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const float x[8], float inv) {
+template <bool OB, bool SR>
+__device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const float x[8], float inv,
+                                          const uint32_t r16[8]) {
     const float n = float((1 << (bw - 1)) - 1);
     uint64_t fld = 0;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        const uint32_t y =
-            __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
-        uint32_t code = y - kMagicBits;
-        if (OB && bw == 1) code = x[c] * inv > 0.f;
+        uint32_t code;
+        if constexpr (SR) {
+            code = sr_level(x[c], inv, bw, r16[c]) - kMagicBits;
+        } else {
+            const uint32_t y = __float_as_uint(
+                __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
+            code = y - kMagicBits;
+            if (OB && bw == 1) code = x[c] * inv > 0.f;
+        }
         fld |= uint64_t(code) << (c * bw);
     }
     uint8_t* bytes = reinterpret_cast<uint8_t*>(reg);
@@ -257,25 +296,32 @@ __device__ __forceinline__ void unpack_rows(const Raw& raw, int boff, int bw, fl
     }
 }
 
-template <bool OB>
-__device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const float x[8], float inv) {
+template <int B, bool SR>
+__device__ __forceinline__ void pack8_rule(uint32_t* reg, int boff, const float x[8], float inv, const uint32_t r16[8]) {
+    if constexpr (SR) pack8_sr<B>(reg, boff, x, inv, r16);
+    else pack8<B>(reg, boff, x, InvOne{inv});
+}
+
+template <bool OB, bool SR>
+__device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const float x[8], float inv,
+                                          const uint32_t r16[8]) {
     const int bu = __builtin_amdgcn_readfirstlane(bw);
     if (__ballot(bw != bu) == 0ull) {
         if (OB && bu == 1) {
-            pack8<1>(reg, boff, x, InvOne{inv});
+            pack8_rule<1, SR>(reg, boff, x, inv, r16);
             return;
         }
         switch (bu) {
-            case 2: pack8<2>(reg, boff, x, InvOne{inv}); break;
-            case 3: pack8<3>(reg, boff, x, InvOne{inv}); break;
-            case 4: pack8<4>(reg, boff, x, InvOne{inv}); break;
-            case 5: pack8<5>(reg, boff, x, InvOne{inv}); break;
-            case 6: pack8<6>(reg, boff, x, InvOne{inv}); break;
-            case 7: pack8<7>(reg, boff, x, InvOne{inv}); break;
-            default: pack8<8>(reg, boff, x, InvOne{inv}); break;
+            case 2: pack8_rule<2, SR>(reg, boff, x, inv, r16); break;
+            case 3: pack8_rule<3, SR>(reg, boff, x, inv, r16); break;
+            case 4: pack8_rule<4, SR>(reg, boff, x, inv, r16); break;
+            case 5: pack8_rule<5, SR>(reg, boff, x, inv, r16); break;
+            case 6: pack8_rule<6, SR>(reg, boff, x, inv, r16); break;
+            case 7: pack8_rule<7, SR>(reg, boff, x, inv, r16); break;
+            default: pack8_rule<8, SR>(reg, boff, x, inv, r16); break;
         }
     } else {
-        pack8_any<OB>(reg, boff, bw, x, inv);
+        pack8_any<OB, SR>(reg, boff, bw, x, inv, r16);
     }
 }
 
@@ -314,9 +360,10 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 
 // EST: fold the token into the attached online estimators; LAYER: the layer-wise budget
 // layout (code area of b_max bits per element, codes in use first, then a zero tail);
-// OB: one-bit rows may occur. Each is its own instantiation, so that the plain step
+// OB: one-bit rows may occur; SR: stochastic rounding with the Philox draws of the
+// element (row, 8 columns) instead of round to nearest. Each is its own instantiation, so that the plain step
 // carries no trace of the others.
-template <bool EST, bool LAYER, bool OB>
+template <bool EST, bool LAYER, bool OB, bool SR>
 __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     extern __shared__ __align__(16) uint8_t smraw[];
     BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw);
@@ -553,7 +600,9 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         const uint32_t l = sm.tb[NG * m + 4 * wave + rq].loc;
-        pack_rows<OB>(reg, boff_of(l), int((l >> 16) & 15u), x[m], inv[m]);
+        uint32_t r16[8];
+        if constexpr (SR) sr_draws8(A.seed, uint32_t(head), A.t, int(l >> 24), cg, r16);
+        pack_rows<OB, SR>(reg, boff_of(l), int((l >> 16) & 15u), x[m], inv[m], r16);
     }
     __syncthreads();
     {
@@ -577,7 +626,10 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
 namespace {
 template <bool EST, bool LAYER, bool OB>
 void launch_variant(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
-    hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB>), dim3(d.B * d.H), dim3(NT), smem, stream, a);
+    if (d.mode == WB_SR)
+        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, true>), dim3(d.B * d.H), dim3(NT), smem, stream, a);
+    else
+        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, false>), dim3(d.B * d.H), dim3(NT), smem, stream, a);
 }
 template <bool EST, bool LAYER>
 void launch_ob(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
@@ -592,7 +644,7 @@ void launch_layer(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStrea
 }  // namespace
 
 bool bitalloc_step_supported(const wb_layout_desc& d) {
-    return d.dk == DK && d.dv == DV && d.mode == WB_RTN && d.bmin >= 1 && d.bmax <= 8 &&
+    return d.dk == DK && d.dv == DV && (d.mode == WB_RTN || d.mode == WB_SR) && d.bmin >= 1 && d.bmax <= 8 &&
            (d.budget == WB_BUDGET_HEAD || d.budget == WB_BUDGET_LAYER);
 }
 
