@@ -220,14 +220,10 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
 
     // ---- load the lane's tile (stored domain) ------------------------------------
     Real x[8][8];
-    float e[8][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            x[m][c] = Real(0);
-            e[m][c] = 0.f;
-        }
+        for (int c = 0; c < 8; ++c) x[m][c] = Real(0);
     }
     if (act) {
 #pragma unroll
@@ -310,13 +306,6 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     const int kap = bw == 1 ? 2 * field - 1 : field - n;   // one-bit rows: -1, +1
                     x[m][c] = Real(float(kap) * (A.head_unit ? f16_bits_to_f32(gs[c]) : dl));
                 }
-            }
-            if (USE_SIDE && OP == OP_STEP && !(KIND == WB_MIXED && m < mhi)) {
-                const float* src = A.side + ((size_t)head * DK + row) * DV + 8 * cg;
-                const float4 v0 = reinterpret_cast<const float4*>(src)[0];
-                const float4 v1 = reinterpret_cast<const float4*>(src)[1];
-                e[m][0] = v0.x; e[m][1] = v0.y; e[m][2] = v0.z; e[m][3] = v0.w;
-                e[m][4] = v1.x; e[m][5] = v1.y; e[m][6] = v1.z; e[m][7] = v1.w;
             }
         }
     }
@@ -490,6 +479,17 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
             const int row = rg + RS * m;
             uint32_t r16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             const bool hi_row = (KIND == WB_MIXED && m < mhi);
+            // the side value of the lane's 8 elements of this row (residual, counter or
+            // residual value), read here rather than with the codes so that it does not
+            // hold registers through the contractions
+            float em[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (USE_SIDE && OP == OP_STEP && !hi_row) {
+                const float* src = A.side + ((size_t)head * DK + row) * DV + 8 * cg;
+                const float4 v0 = reinterpret_cast<const float4*>(src)[0];
+                const float4 v1 = reinterpret_cast<const float4*>(src)[1];
+                em[0] = v0.x; em[1] = v0.y; em[2] = v0.z; em[3] = v0.w;
+                em[4] = v1.x; em[5] = v1.y; em[6] = v1.z; em[7] = v1.w;
+            }
             if (EMODE == WB_SR && KIND != WB_FP32 && !hi_row) sr_draws8(A.seed, bh, A.t, row, cg, r16);
             float en[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             if (KIND == WB_FP32) {
@@ -533,7 +533,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     bool trig = false;
                     if constexpr (EMODE == WB_RESQ) {
                         // error feedback with the residual kept on the k-bit grid
-                        const Real target = h + Real(e[m][c]);
+                        const Real target = h + Real(em[c]);
                         kap = int(fmin(fmax(rint(target * inv_step), Real(lo)), Real(hi)));
                         const Real r = fmin(fmax(target - Real(kap) * step, -step), step);
                         const int hk = 1 << (A.mem_bits - 1);
@@ -543,7 +543,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                     } else if constexpr (EMODE == WB_DIR) {
                         // direction memory: counter in the side buffer
                         const int near = int(fmin(fmax(rint(h * inv_step), Real(lo)), Real(hi)));
-                        const float cnt = e[m][c];
+                        const float cnt = em[c];
                         if (near != kp) {
                             kap = near;
                             en[c] = 0.f;
@@ -558,7 +558,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                             en[c] = cnt;
                         }
                     } else {
-                        kap = round_rule<EMODE, Real>(h, Real(e[m][c]), step, Real(0), lo, hi, r16[c], &en[c]);
+                        kap = round_rule<EMODE, Real>(h, Real(em[c]), step, Real(0), lo, hi, r16[c], &en[c]);
                     }
                     if (count) {
                         const bool dead = Real(2) * ad < step, change = kap != kp;
@@ -612,7 +612,7 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                 uint32_t lo4 = 0, hi4 = 0;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const int code = round_rule<EMODE, Real>(x[m][c], Real(e[m][c]), scale, zero, 0, top, r16[c], &en[c]);
+                    const int code = round_rule<EMODE, Real>(x[m][c], Real(em[c]), scale, zero, 0, top, r16[c], &en[c]);
                     if (ib == 4) lo4 |= uint32_t(code) << (c * 4);
                     else if (c < 4) lo4 |= uint32_t(code) << (c * 8);
                     else hi4 |= uint32_t(code) << ((c - 4) * 8);
@@ -655,11 +655,11 @@ __global__ void __launch_bounds__((Shape<DK, DV>::NT)) wb_kernel(const KArgs A) 
                 for (int c = 0; c < 8; ++c) {
                     const float dc = A.head_unit ? sm.gdelta[(row >> 5) * DV + 8 * cg + c] : dl;
                     if (bw == 1) {
-                        const int k1 = round_rule<EMODE, float>(float(x[m][c]), e[m][c], 2.f * dl, -dl, 0, 1, r16[c], &en[c]);
+                        const int k1 = round_rule<EMODE, float>(float(x[m][c]), em[c], 2.f * dl, -dl, 0, 1, r16[c], &en[c]);
                         fld |= uint64_t(uint32_t(k1)) << c;
                         continue;
                     }
-                    const int kap = round_rule<EMODE, float>(float(x[m][c]), e[m][c], dc, 0.f, -n, n, r16[c], &en[c]);
+                    const int kap = round_rule<EMODE, float>(float(x[m][c]), em[c], dc, 0.f, -n, n, r16[c], &en[c]);
                     fld |= uint64_t(uint32_t(kap + n)) << (c * bw);
                 }
                 const int off = sm.off[row] + cg * bw;
