@@ -650,7 +650,7 @@ bool bitalloc_step_supported(const wb_layout_desc& d) {
 
 // ---------------------------------------------------------------------------
 // Decode write-back step of the per-head allocation unit (HEADALLOC) with round to
-// nearest ([LBRS] "Allocation units"): one width b for the whole head, and a float16 step
+// nearest or stochastic rounding ([LBRS] "Allocation units"): one width b for the whole head, and a float16 step
 // per group of 32 key rows and value column with its own fit index. Four wavefronts per
 // head, one per row group: lane (cg, rq) of wavefront g holds rows 32 g + 8 rq .. + 7 and
 // columns 8 cg .. 8 cg + 7, so a column's group maximum is the maximum over the lane's 8
@@ -675,7 +675,7 @@ struct HaSmem {
     uint32_t reg[(kHaCodeMax + 2 * HGR * DV) / 4 + 4];   // staged codes, then the new Delta bits
 };
 
-template <int B>
+template <int B, bool SR>
 __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
     constexpr int n = (1 << (B - 1)) - 1;
     constexpr int NVEC = DK * DV * B / 8 / 16;           // 16-byte vectors of codes in use
@@ -855,7 +855,19 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
         gi[4] = i1.x; gi[5] = i1.y; gi[6] = i1.z; gi[7] = i1.w;
     }
 #pragma unroll
-    for (int m = 0; m < HMR; ++m) pack8<B>(sm.reg, (row0 + m) * (DV / 8) * B + cg * B, x[m], InvCol{gi});
+    for (int m = 0; m < HMR; ++m) {
+        const int boff = (row0 + m) * (DV / 8) * B + cg * B;
+        if constexpr (SR) {
+            // stochastic rounding with the element's Philox draws (row, column group)
+            uint32_t r16[8], y[8];
+            sr_draws8(A.seed, uint32_t(head), A.t, row0 + m, cg, r16);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) y[c] = sr_level(x[m][c], gi[c], B, r16[c]);
+            store8<B>(sm.reg, boff, y);
+        } else {
+            pack8<B>(sm.reg, boff, x[m], InvCol{gi});
+        }
+    }
     __syncthreads();
 
     // ---- the codes, then the new steps (the fit bytes and the width byte are unchanged)
@@ -870,6 +882,7 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
     }
 }
 
+template <bool SR>
 __global__ void __launch_bounds__(HNT) headalloc_step_kernel(const KArgs A) {
     __shared__ HaSmem sm;
     const uint8_t* region = A.state + (size_t)blockIdx.x * A.region_stride;
@@ -877,24 +890,26 @@ __global__ void __launch_bounds__(HNT) headalloc_step_kernel(const KArgs A) {
     int b = int(region[A.code_cap + 3 * HGR * DV]) + 1;
     b = __builtin_amdgcn_readfirstlane(min(max(b, 2), A.code_cap / (DK * DV / 8)));
     switch (b) {
-        case 2: headalloc_body<2>(A, sm); break;
-        case 3: headalloc_body<3>(A, sm); break;
-        case 4: headalloc_body<4>(A, sm); break;
-        case 5: headalloc_body<5>(A, sm); break;
-        case 6: headalloc_body<6>(A, sm); break;
-        case 7: headalloc_body<7>(A, sm); break;
-        default: headalloc_body<8>(A, sm); break;
+        case 2: headalloc_body<2, SR>(A, sm); break;
+        case 3: headalloc_body<3, SR>(A, sm); break;
+        case 4: headalloc_body<4, SR>(A, sm); break;
+        case 5: headalloc_body<5, SR>(A, sm); break;
+        case 6: headalloc_body<6, SR>(A, sm); break;
+        case 7: headalloc_body<7, SR>(A, sm); break;
+        default: headalloc_body<8, SR>(A, sm); break;
     }
 }
 
 }  // namespace
 
 bool headalloc_step_supported(const wb_layout_desc& d) {
-    return d.kind == WB_HEADALLOC && d.dk == DK && d.dv == DV && d.mode == WB_RTN && d.bmax <= 8;
+    return d.kind == WB_HEADALLOC && d.dk == DK && d.dv == DV && (d.mode == WB_RTN || d.mode == WB_SR) &&
+           d.bmax <= 8;
 }
 
 hipError_t launch_headalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(headalloc_step_kernel, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
+    if (d.mode == WB_SR) hipLaunchKernelGGL(headalloc_step_kernel<true>, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
+    else hipLaunchKernelGGL(headalloc_step_kernel<false>, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -50,7 +50,8 @@ hipError_t launch_wb(const wb_layout_desc& d, int op, const KArgs& a, hipStream_
 bool bitalloc_step_supported(const wb_layout_desc& d);
 hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
 
-// Decode step of the per-head allocation unit (HEADALLOC) with round-to-nearest.
+// Decode step of the per-head allocation unit (HEADALLOC) with round-to-nearest or
+// stochastic rounding.
 bool headalloc_step_supported(const wb_layout_desc& d);
 hipError_t launch_headalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
 
