@@ -59,6 +59,10 @@ struct BaFixed {
     float red[2][NW][DV];                      // u / p partials of the wavefronts
     float w[DV];
     float qk[4];
+    float bias[2][2];                          // per table wavefront: sum k beta0, sum q beta0
+    // bfloat16 limbs of the matrix-core row weights k_i alpha_i and q_i alpha_i, by
+    // [wavefront][row group][row step][quantity * 4 + limb] (limb 3 is zero)
+    uint16_t alimb[NW][4][MR][8];
 };
 // the staged region follows BaFixed in dynamic LDS
 constexpr int kRegOffset = (int(sizeof(BaFixed)) + 15) / 16 * 16;
@@ -325,24 +329,6 @@ __device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const
     }
 }
 
-// max over the 16 lanes of a DPP row, of non-negative floats given as bit patterns
-__device__ __forceinline__ uint32_t rowmax16_bits(uint32_t v) {
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));   // xor 1
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));   // xor 2
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));  // half mirror
-    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));  // mirror
-    return v;
-}
-
-// sum over the 16 lanes of a DPP row (the same butterfly as the maximum)
-__device__ __forceinline__ float rowsum16(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    return v;
-}
-
 // sum over the wavefront, returned as a scalar (DPP inside rows of 16 lanes, then the
 // four row sums)
 __device__ __forceinline__ int wave_sum_i32(int v) {
@@ -354,8 +340,73 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
            (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
+// float sum over the wavefront, returned as a scalar (DPP inside rows of 16 lanes, then
+// the four row sums read with every lane active)
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+}
+
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+}
+
+// Three bfloat16 limbs whose sum is the float32 c exactly: each limb keeps the leading
+// 8 significant bits of what the previous ones left (truncation), and 3 x 8 bits cover
+// the 24-bit significand. Returned as (limb0 | limb1 << 16, limb2).
+__device__ __forceinline__ uint2 bf16_limbs3(float c) {
+    const uint32_t h0 = __float_as_uint(c) & 0xFFFF0000u;
+    const float r1 = c - __uint_as_float(h0);
+    const uint32_t h1 = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(h1);
+    return make_uint2((h0 >> 16) | h1, __float_as_uint(r2) >> 16);
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D = A B on the matrix cores (16 x 16 output, K = 32, bfloat16 operands, float32
+// accumulation); the operands are four 32-bit registers of two bfloat16 each
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(const uint32_t a[4], const uint32_t b[4]) {
+    const uint4 av = make_uint4(a[0], a[1], a[2], a[3]), bv = make_uint4(b[0], b[1], b[2], b[3]);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
+                                                   f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
+// DPP moves inside rows of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Row maxima (non-negative floats as bit patterns) of the 4 rows a lane holds, reduced
+// over the 16 lanes of its DPP row and scattered: lane cg ends with the maximum of row
+// ((cg & 1) << 1) | ((cg >> 1) & 1), the four rows spread over every quad.
+__device__ __forceinline__ uint32_t rowmax4_scatter(const uint32_t m[4], int cg) {
+    const bool odd = cg & 1, hi = cg & 2;
+    const uint32_t k0 = odd ? m[2] : m[0], k1 = odd ? m[3] : m[1];
+    const uint32_t s0 = odd ? m[0] : m[2], s1 = odd ? m[1] : m[3];
+    const uint32_t n0 = max(k0, dpp_u32<0xB1>(s0)), n1 = max(k1, dpp_u32<0xB1>(s1));   // xor 1
+    uint32_t v = max(hi ? n1 : n0, dpp_u32<0x4E>(hi ? n0 : n1));                         // xor 2
+    v = max(v, dpp_u32<0x124>(v));                                                      // row_ror:4
+    return max(v, dpp_u32<0x128>(v));                                                   // row_ror:8
+}
+// the same for sums of floats
+__device__ __forceinline__ float rowsum4_scatter(const float m[4], int cg) {
+    const bool odd = cg & 1, hi = cg & 2;
+    const float k0 = odd ? m[2] : m[0], k1 = odd ? m[3] : m[1];
+    const float s0 = odd ? m[0] : m[2], s1 = odd ? m[1] : m[3];
+    const float n0 = k0 + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(s0)));
+    const float n1 = k1 + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(s1)));
+    float v = (hi ? n1 : n0) + __uint_as_float(dpp_u32<0x4E>(__float_as_uint(hi ? n0 : n1)));
+    v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));
+    return v + __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
 }
 
 // EST: fold the token into the attached online estimators; LAYER: the layer-wise budget
@@ -364,7 +415,7 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 // element (row, 8 columns) instead of round to nearest. Each is its own instantiation, so that the plain step
 // carries no trace of the others.
 template <bool EST, bool LAYER, bool OB, bool SR>
-__global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
+__global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KArgs A) {
     extern __shared__ __align__(16) uint8_t smraw[];
     BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw);
     uint32_t* reg = reinterpret_cast<uint32_t*>(smraw + kRegOffset);
@@ -439,23 +490,25 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         const int fit = (hi_half ? meta1 : meta0) >> 4;
         const float n = float((1 << (bwt - 1)) - 1);
         const float ad = expf(-sr) * f16_bits_to_f32(dold);
-        // a one-bit row's levels are -Delta, +Delta: code * 2 a Delta - a Delta
-        if (OB && bwt == 1) sm.ta[pos] = TabA{2.f * ad, -ad, kr, qr};
-        else sm.ta[pos] = TabA{ad, -n * ad, kr, qr};
+        // dequantize + decay: x = code * alpha + beta0 (a one-bit row's levels are -Delta,
+        // +Delta: code * 2 a Delta - a Delta)
+        const bool one = OB && bwt == 1;
+        const float alpha = one ? 2.f * ad : ad, beta0 = one ? -ad : -n * ad;
+        sm.ta[pos] = TabA{alpha, beta0, kr, qr};
         sm.tb[pos] = TabB{kFn.v[fit][bwt], uint32_t(off * (DV / 8)) | (uint32_t(bwt) << 16) | (uint32_t(trow) << 24)};
-        // q . k over the wavefront's 64 rows: DPP sums inside each row of 16 lanes, then
-        // the four row sums
-        float pq = qr * kr;
-        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0xB1, 0xF, 0xF, false));
-        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x4E, 0xF, 0xF, false));
-        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x141, 0xF, 0xF, false));
-        pq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pq), 0x140, 0xF, 0xF, false));
-        // (read the row sums with every lane active; only the store is predicated)
-        const float qsum = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 0)) +
-                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 16))) +
-                           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 32)) +
-                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 48)));
-        if (lane == 0) sm.qk[wave] = qsum;
+        // u and p on the matrix cores: u_j = sum_i (k_i alpha_i) code_ij + sum_i k_i beta0_i
+        // (p with q_i); the row weights as exact bfloat16 limbs, the constant terms summed here
+        const uint2 lu = bf16_limbs3(kr * alpha), lp = bf16_limbs3(qr * alpha);
+        *reinterpret_cast<uint4*>(&sm.alimb[(pos % NG) >> 2][pos & 3][pos / NG][0]) =
+            make_uint4(lu.x, lu.y, lp.x, lp.y);
+        // q . k and the constant terms over the wavefront's 64 rows
+        const float qsum = wave_sum_f32(qr * kr);
+        const float bu = wave_sum_f32(kr * beta0), bp = wave_sum_f32(qr * beta0);
+        if (lane == 0) {
+            sm.qk[wave] = qsum;
+            sm.bias[wave][0] = bu;
+            sm.bias[wave][1] = bp;
+        }
     }
     {
         uint4* dst = reinterpret_cast<uint4*>(reg);
@@ -472,17 +525,16 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     }
     __syncthreads();
 
-    // ---- dequantize the lane's 4 rows x 8 columns; u, p partial sums ------------------
+    // ---- dequantize the lane's 4 rows x 8 columns; u, p on the matrix cores -----------
     // The code words of row m + 1 are requested (and the location of row m + 2 read)
     // before row m is unpacked, so their LDS latency overlaps the arithmetic.
+    // Matrix-core operands (16 x 16 x 32, bfloat16): the K slots of lane group rq are the
+    // lane's rows m = 0..3 times the two columns of a column pair; B for column pair cp
+    // holds the codes (exact in bfloat16), A the limbs of the row weights; output row
+    // 8 s + 4 q + limb of lane column cg is the partial of quantity q (u, p) for column
+    // 8 cg + 2 cp + s over the wavefront's 16 rows.
     auto boff_of = [&](uint32_t l) { return int(l & 0xFFFFu) + cg * int((l >> 16) & 15u); };
-    float x[MR][8];
-    float up[8], pp[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        up[c] = 0.f;
-        pp[c] = 0.f;
-    }
+    uint32_t bop[4][MR];                       // B operands: [column pair][row]
     uint32_t loc_cur = sm.tb[4 * wave + rq].loc;
     uint32_t loc_next = sm.tb[NG + 4 * wave + rq].loc;
     Raw raw_next = load_raw(reg, boff_of(loc_cur));
@@ -495,45 +547,31 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
             loc_cur = loc_next;
         }
         if (m + 2 < MR) loc_next = sm.tb[NG * (m + 2) + 4 * wave + rq].loc;
-        const TabA ta = sm.ta[NG * m + 4 * wave + rq];
         float code[8];
         unpack_rows<OB>(raw, boff_of(loc), int((loc >> 16) & 15u), code);
+        // the codes are integers below 2^8, so a float's high half is its exact bfloat16
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            x[m][c] = __builtin_fmaf(code[c], ta.alpha, ta.beta0);
-            up[c] = __builtin_fmaf(ta.k, x[m][c], up[c]);
-            pp[c] = __builtin_fmaf(ta.q, x[m][c], pp[c]);
-        }
+        for (int cp = 0; cp < 4; ++cp)
+            bop[cp][m] = __builtin_amdgcn_perm(__float_as_uint(code[2 * cp + 1]), __float_as_uint(code[2 * cp]),
+                                               0x07060302u);
         // finish this row here (keeps the codes of one row live at a time)
-        asm volatile("" ::"v"(x[m][0]), "v"(x[m][1]), "v"(x[m][2]), "v"(x[m][3]), "v"(x[m][4]), "v"(x[m][5]),
-                     "v"(x[m][6]), "v"(x[m][7]));
-        asm volatile("" ::"v"(up[0]), "v"(up[1]), "v"(up[2]), "v"(up[3]), "v"(up[4]), "v"(up[5]), "v"(up[6]),
-                     "v"(up[7]), "v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(pp[4]), "v"(pp[5]), "v"(pp[6]),
-                     "v"(pp[7]));
+        asm volatile("" ::"v"(bop[0][m]), "v"(bop[1][m]), "v"(bop[2][m]), "v"(bop[3][m]));
     }
-    // Sum the four row groups of the wavefront in registers (a reduce-scatter by lane
-    // swaps): exchanging lanes 32..63 of u with lanes 0..31 of p and adding leaves the
-    // u sums over row groups (0, 2) and (1, 3) in the low half and the p sums in the
-    // high half; exchanging odd 16-lane rows of columns c with even rows of columns
-    // c + 4 and adding completes the sums. Lane (cg, rq) then holds quantity rq / 2 of
-    // columns 8 cg + 4 (rq % 2) + 0..3.
     {
-        float t[8];
+        // A operand of lane (g = rq, output row mo = cg): the limb of quantity (mo / 4) % 2
+        // for each row m in the slot of column parity mo / 8 (limb 3 reads a zero)
+        const int mo = cg;
+        const uint16_t* al = &sm.alimb[wave][rq][0][((mo >> 2) & 1) * 4 + (mo & 3)];
+        uint32_t aop[MR];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(up[c]), __float_as_uint(pp[c]), false,
-                                                            false);
-            t[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-        }
-        float s4[4];
+        for (int m = 0; m < MR; ++m) aop[m] = uint32_t(al[8 * m]) << (16 * (mo >> 3));
+        // lane (rq, cg) receives quantity rq % 2 of column 8 cg + 2 cp + rq / 2
+        float* red = &sm.red[rq & 1][wave][8 * cg + (rq >> 1)];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t[c]), __float_as_uint(t[c + 4]), false,
-                                                            false);
-            s4[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        for (int cp = 0; cp < 4; ++cp) {
+            const f32x4_t d = mfma_bf16_16x16x32(aop, bop[cp]);
+            red[2 * cp] = (d[0] + d[1]) + d[2];
         }
-        *reinterpret_cast<float4*>(&sm.red[rq >> 1][wave][8 * cg + 4 * (rq & 1)]) =
-            make_float4(s4[0], s4[1], s4[2], s4[3]);
     }
     __syncthreads();
 
@@ -541,7 +579,7 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
     const int jq = tid >> 7, j = tid & (DV - 1);
     float pj = 0.f;
     if (jq < 2) {
-        float acc = 0.f;
+        float acc = sm.bias[0][jq] + sm.bias[1][jq];
 #pragma unroll
         for (int g = 0; g < NW; ++g) acc += sm.red[jq][g][j];
         if (jq == 0) sm.w[j] = beta * (vj - acc);
@@ -562,39 +600,57 @@ __global__ void __launch_bounds__(NT) bitalloc_step_kernel(const KArgs A) {
         wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
     }
     uint16_t* dout = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(reg) + code_bytes);
-    // row maxima and steps first (no branches, so the lane's rows interleave) ...
-    float inv[MR];
+    // update and in-lane maxima of |x| of the lane's rows, then the row maxima over the
+    // 16 lanes of each row reduced and scattered (each lane ends with one of the 4 rows),
+    // so that every step is derived once per 4 lanes and handed back by quad broadcasts
+    // dequantize + decay from the codes kept in the B operands (x = code alpha + beta0),
+    // then the update
+    float x[MR][8];
+    uint32_t mxb[MR];
+    float sab[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-        const int pos = NG * m + 4 * wave + rq;
-        const float kk = sm.ta[pos].k;
-        const TabB tb = sm.tb[pos];
+        const TabA ta = sm.ta[NG * m + 4 * wave + rq];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) x[m][c] = __builtin_fmaf(kk, wv[c], x[m][c]);
+        for (int cp = 0; cp < 4; ++cp) {
+            x[m][2 * cp] = __builtin_fmaf(__uint_as_float(bop[cp][m] << 16), ta.alpha, ta.beta0);
+            x[m][2 * cp + 1] = __builtin_fmaf(__uint_as_float(bop[cp][m] & 0xFFFF0000u), ta.alpha, ta.beta0);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[m][c] = __builtin_fmaf(ta.k, wv[c], x[m][c]);
         float mx = fmaxf(fmaxf(fabsf(x[m][0]), fabsf(x[m][1])), fabsf(x[m][2]));
         mx = fmaxf(fmaxf(mx, fabsf(x[m][3])), fabsf(x[m][4]));
         mx = fmaxf(fmaxf(mx, fabsf(x[m][5])), fabsf(x[m][6]));
-        mx = fmaxf(mx, fabsf(x[m][7]));
-        const float R = __uint_as_float(rowmax16_bits(__float_as_uint(mx)));
+        mxb[m] = __float_as_uint(fmaxf(mx, fabsf(x[m][7])));
+        if constexpr (OB)
+            sab[m] = ((fabsf(x[m][0]) + fabsf(x[m][1])) + (fabsf(x[m][2]) + fabsf(x[m][3]))) +
+                     ((fabsf(x[m][4]) + fabsf(x[m][5])) + (fabsf(x[m][6]) + fabsf(x[m][7])));
+    }
+    float inv[MR];
+    {
+        // this lane's row: ms = ((cg & 1) << 1) | ((cg >> 1) & 1)
+        const int ms = ((cg & 1) << 1) | ((cg >> 1) & 1);
+        const TabB tb = sm.tb[NG * ms + 4 * wave + rq];
+        const float R = __uint_as_float(rowmax4_scatter(mxb, cg));
         uint32_t dbits = f16_bits_of_product(R, tb.fn);
         if constexpr (OB) {
             // one-bit row: Delta = f16(mean |x|), the row sum by a pairwise sum in the lane
-            // and a DPP butterfly (relative error below 7 float32 roundings)
-            const bool one = ((tb.loc >> 16) & 15u) == 1u;
-            if (__ballot(one) != 0ull) {
-                float sa = ((fabsf(x[m][0]) + fabsf(x[m][1])) + (fabsf(x[m][2]) + fabsf(x[m][3]))) +
-                           ((fabsf(x[m][4]) + fabsf(x[m][5])) + (fabsf(x[m][6]) + fabsf(x[m][7])));
-                sa = rowsum16(sa);
-                const uint32_t d1 = f16_bits_of_product(sa, 1.f / float(DV));
-                if (one) dbits = d1;
-            }
+            // and four DPP steps (relative error below 7 float32 roundings)
+            const float sa = rowsum4_scatter(sab, cg);
+            const uint32_t d1 = f16_bits_of_product(sa, 1.f / float(DV));
+            if (((tb.loc >> 16) & 15u) == 1u) dbits = d1;
         }
         const float dl = f16_bits_to_f32(dbits);
         // reciprocal refined by one Newton step (near correctly rounded)
         float r = __builtin_amdgcn_rcpf(dl);
         r = __builtin_fmaf(__builtin_fmaf(-dl, r, 1.f), r, r);
-        inv[m] = dl > 0.f ? r : 0.f;
-        if (cg == 0) dout[tb.loc >> 24] = uint16_t(dbits);
+        const uint32_t ib = __float_as_uint(dl > 0.f ? r : 0.f);
+        if (cg < 4) dout[tb.loc >> 24] = uint16_t(dbits);
+        // row m sits in quad lane ((m & 1) << 1) | (m >> 1)
+        inv[0] = __uint_as_float(dpp_u32<0x00>(ib));
+        inv[1] = __uint_as_float(dpp_u32<0xAA>(ib));
+        inv[2] = __uint_as_float(dpp_u32<0x55>(ib));
+        inv[3] = __uint_as_float(dpp_u32<0xFF>(ib));
     }
     // ... then the rounding and packing, specialised per width
 #pragma unroll
