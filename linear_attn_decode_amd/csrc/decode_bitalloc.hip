@@ -19,10 +19,11 @@
 //     constants, byte offset, width) sit in LDS tables indexed by sorted position;
 //   * dequantize + decay is one FMA: a_i Delta_i (code - n_i) = code * (a_i Delta_i) +
 //     (-n_i a_i Delta_i);
-//   * rounding to the nearest level adds 1.5 * 2^23 + n_i in the same FMA as the scaling
-//     (x * (1/Delta) + magic rounds the exact product once, ties to even), clamps with
-//     one med3, and packs with shift-adds whose constant high bits are removed once per
-//     32-bit word;
+//   * rounding to the nearest level adds 1.5 * 2^23 in the same FMA as the scaling
+//     (x * (1/Delta) + magic rounds the exact product once, ties to the even level),
+//     clamps with one med3 to [magic - n_i, magic + n_i], and packs with shift-adds whose
+//     constant high bits (those of magic - n_i, so the field is level + n_i) are removed
+//     once per 32-bit word;
 //   * row maxima use DPP integer max on the bits of |x| (ordered like the values);
 //   * the packed codes of a lane (8 elements = b bytes) go to a staging copy of the
 //     region in LDS at their final byte offset, then the region is written to HBM with
@@ -144,14 +145,17 @@ struct InvCol {
     __device__ __forceinline__ float operator[](int c) const { return p[c]; }
 };
 
-// Write 8 codes of `B` bits, given in magic-number form (the bits of 1.5 * 2^23 + code),
+// Write 8 codes of `B` bits, given in magic-number form (the bits of 1.5 * 2^23 + level,
+// level in [-n, n]; the stored field is level + n, n = 2^(B-1) - 1, and 0 / 1 for B = 1),
 // packed at byte `boff` of the staging copy (B bytes).
 template <int B>
 __device__ __forceinline__ void store8(uint32_t* reg, int boff, const uint32_t y[8]) {
+    // bits of 1.5 * 2^23 - n: subtracting them leaves level + n
+    constexpr uint32_t base = kMagicBits - uint32_t(B == 1 ? 0 : (1 << (B - 1)) - 1);
     if constexpr (B == 1) {
         uint32_t w = 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) w |= (y[c] - kMagicBits) << c;
+        for (int c = 0; c < 8; ++c) w |= (y[c] - base) << c;
         reinterpret_cast<uint8_t*>(reg)[boff] = uint8_t(w);
         return;
     }
@@ -160,8 +164,8 @@ __device__ __forceinline__ void store8(uint32_t* reg, int boff, const uint32_t y
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int p = c * B;
-        if (p + B <= 32) g0 += kMagicBits << p;
-        else if (p >= 32) g1 += kMagicBits << (p - 32);
+        if (p + B <= 32) g0 += base << p;
+        else if (p >= 32) g1 += base << (p - 32);
     }
     uint32_t w0 = y[0] - g0, w1 = 0u - g1;
     bool w1_started = false;
@@ -175,7 +179,7 @@ __device__ __forceinline__ void store8(uint32_t* reg, int boff, const uint32_t y
             else w1 = lshl_add(y[c], p - 32, w1);
             w1_started = true;
         } else {
-            const uint32_t code = y[c] - kMagicBits;
+            const uint32_t code = y[c] - base;
             w0 = lshl_add(code, p, w0);
             w1 += code >> (32 - p);
             w1_started = true;
@@ -209,18 +213,20 @@ __device__ __forceinline__ void pack8(uint32_t* reg, int boff, const float x[8],
 #pragma unroll
         for (int c = 0; c < 8; ++c) y[c] = kMagicBits + uint32_t(x[c] * inv[c] > 0.f);
     } else {
+        // the level itself is rounded (ties to even), then clamped to [-n, n]
         constexpr float n = float((1 << (B - 1)) - 1);
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             y[c] = __float_as_uint(
-                __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv[c], kMagic + n), kMagic, kMagic + 2.f * n));
+                __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv[c], kMagic), kMagic - n, kMagic + n));
     }
     store8<B>(reg, boff, y);
 }
 
 // Stochastic rounding of one value on the grid of the row (level index in [0, 2n], or
 // [0, 1] for a one-bit row on -Delta + k 2 Delta): floor(tau) + [u < frac(tau)] with u the
-// 16-bit draw over 2^16, clamped at the rails; a zero step stores level 0 (offset n).
+// 16-bit draw over 2^16, clamped at the rails; a zero step stores level 0. Returned in
+// magic-number form, 1.5 * 2^23 + level (level in [-n, n], or k for a one-bit row).
 __device__ __forceinline__ uint32_t sr_level(float x, float inv, int bw, uint32_t r16) {
     const bool one = bw == 1;
     const float n = one ? 0.f : float((1 << (bw - 1)) - 1);
@@ -228,7 +234,7 @@ __device__ __forceinline__ uint32_t sr_level(float x, float inv, int bw, uint32_
     const float fl = floorf(tau);
     float k = fl + ((float(r16) < (tau - fl) * 65536.f) ? 1.f : 0.f);
     k = one ? __builtin_amdgcn_fmed3f(k, 0.f, 1.f) : __builtin_amdgcn_fmed3f(k, -n, n);
-    return __float_as_uint(kMagic + (k + n));
+    return __float_as_uint(kMagic + k);
 }
 
 template <int B>
@@ -253,17 +259,19 @@ __device__ __forceinline__ void unpack8_any(const Raw& raw, int boff, int bw, fl
 template <bool OB, bool SR>
 __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const float x[8], float inv,
                                           const uint32_t r16[8]) {
-    const float n = float((1 << (bw - 1)) - 1);
+    const int ni = (OB && bw == 1) ? 0 : (1 << (bw - 1)) - 1;
+    const float n = float(ni);
+    const uint32_t base = kMagicBits - uint32_t(ni);     // the field is level + n
     uint64_t fld = 0;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         uint32_t code;
         if constexpr (SR) {
-            code = sr_level(x[c], inv, bw, r16[c]) - kMagicBits;
+            code = sr_level(x[c], inv, bw, r16[c]) - base;
         } else {
             const uint32_t y = __float_as_uint(
-                __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic + n), kMagic, kMagic + 2.f * n));
-            code = y - kMagicBits;
+                __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic), kMagic - n, kMagic + n));
+            code = y - base;
             if (OB && bw == 1) code = x[c] * inv > 0.f;
         }
         fld |= uint64_t(code) << (c * bw);

@@ -274,3 +274,23 @@ def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: T
                 j = np.argwhere(~ok).ravel()[:3]
                 tally.bad.append((where, "codes", int(i), j.tolist(), g.kappa[i][j].tolist(), rr.kappa[j].tolist()))
     return skipped
+
+
+def check_heads_chunk(args):
+    """Worker of the full-layer comparison: check heads [lo, hi) of one teacher-forced
+    step from arrays saved by the caller (numpy only, so that it runs in a spawned
+    process). Returns the chunk's tally."""
+    import os
+    (d, lay_kw, lo, hi, t) = args
+    lay = L.Layout(**lay_kw)
+    ld = lambda n: np.load(os.path.join(d, n + ".npy"), mmap_mode="r")
+    reg_in, reg_out, o = ld("reg_in"), ld("reg_out"), ld("o")
+    q, k, v, beta, s = ld("q"), ld("k"), ld("v"), ld("beta"), ld("s")
+    perm = ld("perm") if os.path.exists(os.path.join(d, "perm.npy")) else None
+    H = lay.H
+    tally = Tally()
+    for idx in range(lo, hi):
+        b, h = divmod(idx, H)
+        check_head(lay, reg_in[idx], reg_out[idx], None, None, o[b, h], q[b, h], k[b, h], v[b, h], beta[b, h],
+                   s[b, h], t, b, h, None if perm is None else perm[h], tally)
+    return tally

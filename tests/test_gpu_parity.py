@@ -321,7 +321,7 @@ def test_allocate_bits_one_bit_rows_matches_oracle(case):
                 reg_orc, alloc = allocate_region(lay, reg_in, s_pass[b, h].astype(np.float64),
                                                  r[b, h].astype(np.float64))
                 ones += int((alloc["widths"] == 1).sum())
-                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (pas, b, h))
+                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (pas, b, h), reg_in)
     print(f"[alloc-1bit] one-bit rows chosen over both passes: {ones}", flush=True)
     assert ones > 0
 
@@ -471,24 +471,52 @@ def _alloc_case(case, rng, B, H, dk):
     return S, s
 
 
-def _check_alloc_head(lay, reg_gpu, reg_orc, alloc, tag):
-    """Widths equal except near-ties of the real widths; then fit indices equal except
-    near-equal fit errors; then the repacked bytes equal."""
+def _check_alloc_head(lay, reg_gpu, reg_orc, alloc, tag, reg_in):
+    """Widths equal except near-ties of the real widths (b* within 1e-5 of a .5 boundary,
+    the budget kept); fit indices equal except near-equal fit errors; then, for every row
+    and whatever the widths and fits agreed on, the GPU's Delta against the oracle's step
+    for the GPU's width and fit (equal, or the adjacent float16 within 1e-6 of a
+    midpoint), and the GPU's codes against the oracle's rounding of the stored values Y
+    on the GPU's grid (equal, or one step apart within 1e-5 of a step of a boundary).
+    When every choice agrees the repacked bytes must also be equal."""
+    from oracle.numerics import f16_bits
+    from oracle.quantizers import levels_n, one_bit_round, one_bit_step, row_step, sym_round
+    from tests.parity import _meta_ok
     g = L.decode_region(lay, reg_gpu)
     o = L.decode_region(lay, reg_orc)
     assert g.widths.sum() == lay.bbar * lay.dk, tag
-    if not np.array_equal(g.widths, o.widths):
-        bad = np.argwhere(g.widths != o.widths).ravel()
-        frac = np.abs(alloc["bstar"][bad] - np.floor(alloc["bstar"][bad]) - 0.5)
-        assert np.all(frac < 1e-5), (tag, bad, alloc["bstar"][bad])
+    bad_w = np.argwhere(g.widths != o.widths).ravel()
+    if bad_w.size:
+        frac = np.abs(alloc["bstar"][bad_w] - np.floor(alloc["bstar"][bad_w]) - 0.5)
+        assert np.all(frac < 1e-5), (tag, bad_w, alloc["bstar"][bad_w])
+    same_w = g.widths == o.widths
+    for i in np.argwhere(same_w & (g.fit != o.fit)).ravel():
+        e = alloc["fit_err"][i]
+        assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (tag, i)
+    if bad_w.size == 0 and np.array_equal(g.fit, o.fit):
+        assert np.array_equal(reg_gpu, reg_orc), tag
         return
-    if not np.array_equal(g.fit, o.fit):
-        bad = np.argwhere(g.fit != o.fit).ravel()
-        for i in bad:
-            e = alloc["fit_err"][i]
-            assert abs(e[g.fit[i]] - e[o.fit[i]]) <= 1e-6 * max(e[o.fit[i]], 1e-300), (tag, i)
-        return
-    assert np.array_equal(reg_gpu, reg_orc), tag
+    # re-round every row of the stored values with the GPU's widths and fits
+    Y = L.stored_values(lay, L.decode_region(lay, reg_in))
+    tally = Tally()
+    for i in range(lay.dk):
+        b = int(g.widths[i])
+        if b == 1:
+            d, pre = one_bit_step(Y[i])
+        else:
+            d, pre = row_step(float(alloc["R"][i]), b, int(g.fit[i]))
+        _meta_ok(g.delta_bits[i:i + 1], f16_bits(np.array([d])), np.array([pre]), tally, (tag, "delta", i))
+        if g.delta_bits[i] != f16_bits(np.array([d]))[0]:
+            continue
+        rr = one_bit_round(Y[i], d, "rtn") if b == 1 else sym_round(Y[i], d, levels_n(b), "rtn")
+        diff = g.kappa[i] != rr.kappa
+        tally.elems += lay.dv
+        if diff.any():
+            tally.mismatch += int(diff.sum())
+            ok = ~diff | ((np.abs(g.kappa[i] - rr.kappa) == 1) & (rr.boundary <= 1e-5))
+            if not ok.all():
+                tally.bad.append((tag, "codes", i, np.argwhere(~ok).ravel()[:3].tolist()))
+    assert tally.ok(), (tag, tally.summary())
 
 
 @pytest.mark.parametrize("case", ["warm", "groups", "spread"])
@@ -522,7 +550,7 @@ def test_allocate_bits_matches_oracle(case):
                     wide_rows += int((L.decode_region(lay, reg_in).widths >= 6).sum())
                 moved += int(np.abs(np.clip(np.rint(alloc["bstar"]), lay.bmin, lay.bmax)
                                     - L.decode_region(lay, reg_orc).widths).sum())
-                _check_alloc_head(lay, reg_gpu, reg_orc, alloc, (pas, b, h))
+                _check_alloc_head(lay, reg_gpu, reg_orc, alloc, (pas, b, h), reg_in)
     print(f"[alloc] one-bit moves over the heads: {moved}; rows stored with 6+ bits before the second pass: "
           f"{wide_rows}", flush=True)
     if case != "warm":
@@ -557,7 +585,7 @@ def test_online_estimators_and_allocation_from_them(mode, per_row):
         for h in range(H):
             reg_in = before[b * H + h][: lay.region_size()]
             reg_orc, alloc = allocate_region(lay, reg_in, None, None)
-            _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, ("flat", b, h))
+            _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, ("flat", b, h), reg_in)
     jit = np.exp(0.4 * rng.standard_normal((T,) + inp["s"].shape)).astype(np.float32)
     s_t = (inp["s"][None] * jit).astype(np.float32)
     orc = {(b, h): ema_init(dk) for b in range(B) for h in range(H)}
@@ -592,7 +620,7 @@ def test_online_estimators_and_allocation_from_them(mode, per_row):
                 sh, r = ema_estimates(e[b, h, :dk], e[b, h, dk:2 * dk], float(e[b, h, 2 * dk]))
                 reg_in = before[b * H + h][: lay.region_size()]
                 reg_orc, alloc = allocate_region(lay, reg_in, sh, r, factor, C)
-                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h))
+                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h), reg_in)
     # explicit decays with the alternative factors
     s_np = inp["s"] if per_row else np.repeat(inp["s"][..., None], dk, axis=-1).astype(np.float32)
     for factor, C in (("w1", 1), ("hC", 16)):
@@ -606,7 +634,7 @@ def test_online_estimators_and_allocation_from_them(mode, per_row):
                 reg_in = before[b * H + h][: lay.region_size()]
                 reg_orc, alloc = allocate_region(lay, reg_in, s_np[b, h, ::-1].astype(np.float64),
                                                  np.full(dk, 1.0 / (3 * dk)), factor, C)
-                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h))
+                _check_alloc_head(lay, after[b * H + h][: lay.region_size()], reg_orc, alloc, (factor, C, b, h), reg_in)
 
 
 @pytest.mark.parametrize("case", ["est-erasure", "est-hC64", "decays-w1", "per-head-est", "one-bit-floor"])
