@@ -67,7 +67,7 @@ WORKLOADS = {
     "gdn-had-int4": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
                          extra=dict(block=128, int_bits=4), kernel="rot_step_kernel"),
 }
-PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP64_MFMA_TFLOPS = 78.6     # the prefill's state path runs on float64 matrix cores
 
 
 def prefill_flops_per_segment(L=8):
@@ -183,8 +183,10 @@ def run_gpu(args, w):
             st.set_estimators(ests[-1])
         s_alloc = None                                # allocation from the estimators
     torch.cuda.synchronize()
-    counts = [0] * len(states)
     alloc_every = w["alloc_every"]
+    # each layer's token counter starts at its own phase of the allocation cadence, so
+    # that over the run the passes fall at the steady rate of one per `alloc_every` steps
+    counts = [(layer * alloc_every) // len(states) if alloc_every else 0 for layer in range(len(states))]
 
     def one(i, ev_alloc=None):
         layer = i % len(states)
@@ -240,8 +242,20 @@ def run_gpu(args, w):
     clean = [(a.elapsed_time(b), n) for a, b, n, d in groups if not d]
     dec_ms = [t / n for t, n in clean for _ in range(n)]
     alloc_ms = [a.elapsed_time(b) for a, b in alloc_evs]
-    return {"total_ms": total_ms, "wall_s": wall, "decode_ms": dec_ms, "alloc_ms": alloc_ms, "states": states,
-            "inputs": inp}
+    in_window = len(alloc_ms)
+    if alloc_every and in_window < 3:
+        # a short run holds fewer passes than it should at the cadence: time a few more
+        # (after the window) for the per-pass cost that is amortised into the result
+        for i in range(3 - in_window):
+            ae = (ev(), ev())
+            ae[0].record()
+            states[i % len(states)].allocate_bits(s_alloc)
+            ae[1].record()
+            alloc_evs.append(ae)
+        torch.cuda.synchronize()
+        alloc_ms = [a.elapsed_time(b) for a, b in alloc_evs]
+    return {"total_ms": total_ms, "wall_s": wall, "decode_ms": dec_ms, "alloc_ms": alloc_ms,
+            "alloc_in_window": in_window, "states": states, "inputs": inp}
 
 
 def run_prefill(args, w):
@@ -397,14 +411,23 @@ def main():
                                               w.get("mode", "rtn"), w.get("activity", False)) * B * H
     achieved = bytes_launch / (avg_dec_ms / 1e3) / 1e9
     traffic = load_traffic(args.workload)
+    # Whole-job time: the timed window, with the allocation passes counted at their
+    # cadence (one per `alloc_every` layer tokens): the passes inside the window are in
+    # it; the difference to the steady-rate count K / alloc_every is added (or taken
+    # away) at the measured per-pass time.
+    alloc_ms = gpu["alloc_ms"]
+    pass_ms = sum(alloc_ms) / len(alloc_ms) if alloc_ms else 0.0
+    n_in = gpu["alloc_in_window"]
+    expected = K / w["alloc_every"] if w["alloc_every"] else 0.0
+    job_s = total_s + (expected - n_in) * pass_ms / 1e3
     out = {
         "metric": "write-back decode tokens/s + effective HBM GB/s (% peak), 32h x 128x128, B=256",
-        "value": tokens / total_s,
+        "value": tokens / job_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": gpu["total_ms"] / K,
+        "ms_per_step": job_s * 1e3 / K,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -423,8 +446,11 @@ def main():
                      "kernel": w["kernel"], "bytes_per_launch": bytes_launch,
                      "avg_launch_us": avg_dec_ms * 1e3, "median_launch_us": dec[len(dec) // 2] * 1e3,
                      "timing": "HIP events around groups of 16 back-to-back decode launches"},
-        "allocation_pass": {"launches": len(gpu["alloc_ms"]),
-                            "avg_us": (sum(gpu["alloc_ms"]) / len(gpu["alloc_ms"]) * 1e3) if gpu["alloc_ms"] else None},
+        "allocation_pass": {"every_tokens_per_layer": w["alloc_every"] or None,
+                            "launches_in_window": n_in, "launches_at_cadence": expected,
+                            "avg_us": pass_ms * 1e3 if alloc_ms else None,
+                            "amortised_us_per_step": (pass_ms * 1e3 / w["alloc_every"]) if w["alloc_every"] else 0.0,
+                            "window_tokens_per_s": tokens / total_s},
         "wall_s": gpu["wall_s"],
     }
     if not args.no_cpu:
@@ -446,12 +472,12 @@ def main_prefill(args, w):
         "value": B * T / (avg / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": avg,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": {"workload": f"kda-prefill: B={B}, H={H}, T={T}, dk=dv=128, per-row decay, mixed layout "
                                f"(16 float16 rows + Hadamard INT8, 32-value blocks), write-back every {C} tokens",
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None, "kernel": "prefill_kernel",
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP64_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP64_MFMA_TFLOPS, "traffic": None, "kernel": "prefill_kernel",
                      "flops_per_launch": total, "mfma_flops_per_launch": mfma_flops * seg * B * H,
                      "avg_launch_us": avg * 1e3},
         "wall_s": gpu["wall_s"],

@@ -2,33 +2,45 @@
 //
 // [LBRS] "Accumulated readout error": write-back happens once every C tokens (per
 // prefill chunk, per token in decode, or deferred with C = 8); outputs are read from
-// the unquantized state before each write-back. Between two write-backs the state
-// evolves exactly, so each call is cut into segments of at most 8 tokens that end at
-// every write-back point; a segment of L tokens starting from state S_0 is evaluated
-// in closed form (a WY-style rewrite of L delta-rule steps):
+// the unquantized state before each write-back; [LBRS] "Protocol": each write-back is
+// quantized and dequantized before the state is used again. Between two write-backs the
+// state evolves exactly, so each call is cut into segments that end at every
+// write-back point (and at most min(chunk, 8) tokens long); a segment of L tokens
+// starting from state S_0 is evaluated in closed form (a WY-style rewrite of L
+// delta-rule steps):
 //   g_t = sum_{tau<=t} s_tau (per key row), Gamma_t = e^{-g_t};
 //   k^_t = Gamma_t k_t,  q^_t = Gamma_t q_t,  k-_t = k_t / Gamma_t;
 //   w_t  = beta_t (v_t - S_0^T k^_t - sum_{tau<t} (k^_t . k-_tau) w_tau)   (forward solve)
 //   o_t  = S_0^T q^_t + sum_{tau<=t} (q^_t . k-_tau) w_tau
 //   S_L  = Gamma_L S_0 + sum_tau (Gamma_L k-_tau) w_tau^T.
 // The dense contractions [k^; q^] S_0 (16 x 128 x 128) and the rank-8 update run on
-// v_mfma_f32_16x16x4_f32 in float32 (inputs q, k, v are bfloat16); the triangular
-// solve and the small dot products run on the vector ALUs.
+// the matrix cores; the Gram matrices, the triangular solve and the transforms on the
+// vector ALUs.
 //
-// State placement: the 128 x 128 state lives in registers in the MFMA accumulator
-// layout. Wave w owns columns 32w .. 32w+31 (2 column tiles of 16) and all 8 row tiles;
-// lane l holds rows 16*rt + 4*(l/16) + r (r = 0..3) of columns 32w + 16*ct + l%16. The
+// Precision: the state path runs in float64 (v_mfma_f64_16x16x4_f64 for both
+// contractions, float64 decay factors, Gram matrices, solve and transforms). A
+// write-back decides a stored code to within 1e-5 of a step; on 8-bit grids and float16
+// rows that is below one float32 ulp of the value, so a float32 state path flips codes
+// the float64 recurrence does not, and the trajectories of a long call diverge. Outputs
+// are stored as float32.
+//
+// State placement: the 128 x 128 state lives in registers in the float64 MFMA
+// accumulator layout. Wave w owns columns 32w .. 32w+31 (2 column tiles of 16) and all
+// 8 row tiles; register r of lane l holds row 16*rt + l/16 + 4*r (r = 0..3) of column
+// 32w + 16*ct + l%16 (the float64 16 x 16 result interleaves its rows over the four lane
+// groups, unlike the float32 one, which gives each lane group 4 consecutive rows). The
 // same registers serve as the B operand of the [k^; q^] S_0 contraction (K index =
 // row), so no state data moves between waves. Hadamard rows stay rotated (Y = S H):
 // the contraction over rotated rows is transformed back with one 128-point transform
 // per output vector, and rotated rows are updated with H w.
 //
-// Write-back (every C tokens and after the last token) rounds the register state in
-// place: float16 rows to nearest float16; Hadamard INT8 rows per block of 32 columns
-// (= one wave's columns) with an asymmetric affine grid ([DAMP] "Quantization &
-// calibration details"); uniform rows on the B-bit grid. The last write-back is also
-// encoded into the stored region. Supported here: FP32, UNIFORM, HAD_INT8 and MIXED
-// with affine blocks of 32 values, round-to-nearest.
+// Write-back (every C tokens and after the last token) rounds the state in place,
+// through LDS in two halves of 64 rows (one thread per 32-value row block): float16
+// rows to the nearest float16; Hadamard INT8 rows per block of 32 columns (= one wave's
+// columns) on an asymmetric affine grid ([DAMP] "Quantization & calibration details");
+// uniform rows on the B-bit grid. The last write-back is also encoded into the stored
+// region. Supported here: FP32, UNIFORM, HAD_INT8 and MIXED with affine blocks of 32
+// values, round-to-nearest.
 #include "wb_device.hpp"
 #include "wb_kernels.hpp"
 
@@ -36,74 +48,111 @@ namespace wb {
 namespace {
 
 constexpr int DK = 128, DV = 128, NT = 256, SEG = 8;
-typedef float f32x4 __attribute__((ext_vector_type(4)));   // MFMA accumulator fragment
-constexpr float kInvSqrt128f = 0.08838834764831845f;
+typedef double f64x4 __attribute__((ext_vector_type(4)));   // MFMA accumulator fragment
+constexpr double kInvSqrt128 = 0.088388347648318440550;     // 1 / sqrt(128)
 
+// LDS strides (in doubles) chosen against bank conflicts of 64-bit accesses, taken per
+// half wavefront (32 lanes, 32 double-wide bank pairs):
+//   * PS:  rows of k^, q^, k- as 4 parts of 32 rows padded to 33 (the Gram quads read
+//          part x token pairs: slots 4 token + part, all distinct);
+//   * VS:  vectors over the value axis read by two lane groups at once (rows 16 apart
+//          in slots: 128 + 16);
+//   * KQS: the transposed [k^; q^] (odd, so a row's 16 entries and the next row's
+//          do not collide);
+//   * WBS: the write-back copy, row blocks of 32 padded to 33 and rows to 148 (= 20 mod
+//          32): the per-block threads (8 rows x 4 blocks per half wavefront) read
+//          distinct slots.
+constexpr int PS = 4 * 33, VS = DV + 16, KQS = 17, WBS = 148;
+__device__ __forceinline__ int pidx(int row) { return (row >> 5) * 33 + (row & 31); }    // row in a PS row
+__device__ __forceinline__ int widx(int col) { return (col >> 5) * 33 + (col & 31); }    // column in a WBS row
+
+// per-segment staging (dead while the write-back uses the same storage)
+struct PfStage {
+    double khat[SEG][PS];
+    double qhat[SEG][PS];
+    double kbar[SEG][PS];      // k_tau / Gamma_tau
+    double kbarL[SEG][VS];     // Gamma_L k_tau / Gamma_tau
+    double kqt[DK][KQS];       // [k^; q^] transposed (16 used): the MFMA A operand
+    double ks[2 * SEG][VS];    // [k^; q^] S_0 over the unrotated rows, then the whole contraction
+    double ksq[2 * SEG][VS];   // the same over the rotated rows
+};
 struct PfSmem {
-    float khat[SEG][DK];      // rows 0..7 of the contraction operand
-    float qhat[SEG][DK];      // rows 8..15 (must follow khat)
-    float kbar[SEG][DK];      // k_tau / Gamma_tau
-    float kbarL[SEG][DK];     // Gamma_L k_tau / Gamma_tau
-    float gl[DK];             // Gamma_L per row
-    float kqt[DK][20];        // [k^; q^] transposed (16 used): the MFMA A operand, read
-                              // without bank conflicts (row stride 20 floats)
+    union {
+        PfStage st;
+        double wbuf[DK / 2][WBS];   // half of the state, row-major, for the write-back
+    } u;
     float v[SEG][DV];
-    float ks[2 * SEG][DV];    // [k^; q^] S_0 over the unrotated rows, then the whole contraction
-    float ksq[2 * SEG][DV];   // the same over the rotated rows
-    float w[SEG][DV];
-    float hw[SEG][DV];
-    float A[SEG][SEG], QK[SEG][SEG];
-    float beta[SEG];
+    double w[SEG][VS];
+    double hw[SEG][VS];
+    double gl[DK];             // Gamma_L per row
+    double A[SEG][SEG], QK[SEG][SEG];
+    double beta[SEG];
     int perm[DK];
-    float wbuf[DK][DV + 4];   // the state in row-major order for the write-back (row stride
-                              // padded to 132 floats: both transposes are conflict-free)
 };
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// DPP move of a float64 inside rows of 16 lanes (both halves)
+template <int CTRL>
+__device__ __forceinline__ double mov_dpp_f64(double v) {
+    const uint64_t b = uint64_t(__double_as_longlong(v));
+    const uint32_t lo = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(b)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false));
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
 
 // Butterfly partner at lane ^ d for d = 1, 2, 4, 8 (DPP inside a row of 16 lanes),
 // 16 and 32 (lane swaps of the odd and even rows or of the two halves: swapping a
 // register with itself leaves the even rows' (low half's) values in the first result
 // and the odd rows' (high half's) in the second, everywhere).
 template <int D>
-__device__ __forceinline__ float xor_partner(float v, int lane) {
-    const int b = __float_as_int(v);
-    if constexpr (D == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false));
-    if constexpr (D == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false));
+__device__ __forceinline__ double xor_partner(double v, int lane) {
+    if constexpr (D == 1) return mov_dpp_f64<0xB1>(v);
+    if constexpr (D == 2) return mov_dpp_f64<0x4E>(v);
     if constexpr (D == 4) {
         // row_ror:n hands lane i the value of lane i - n (mod 16)
-        const int up = __builtin_amdgcn_mov_dpp(b, 0x12C, 0xF, 0xF, false);     // row_ror:12 (i + 4)
-        const int dn = __builtin_amdgcn_mov_dpp(b, 0x124, 0xF, 0xF, false);     // row_ror:4  (i - 4)
-        return __int_as_float((lane & 4) ? dn : up);
+        const double up = mov_dpp_f64<0x12C>(v);     // row_ror:12 (i + 4)
+        const double dn = mov_dpp_f64<0x124>(v);     // row_ror:4  (i - 4)
+        return (lane & 4) ? dn : up;
     }
-    if constexpr (D == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, false));   // row_ror:8
+    if constexpr (D == 8) return mov_dpp_f64<0x128>(v);   // row_ror:8
+    const uint64_t b = uint64_t(__double_as_longlong(v));
     if constexpr (D == 16) {
-        const auto r = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
-        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+        const auto lo = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+        const bool up = lane & 16;
+        return __longlong_as_double((long long)((uint64_t(up ? hi[0] : hi[1]) << 32) | (up ? lo[0] : lo[1])));
     }
-    const auto r = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
-    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+    const bool up = lane & 32;
+    return __longlong_as_double((long long)((uint64_t(up ? hi[0] : hi[1]) << 32) | (up ? lo[0] : lo[1])));
 }
 
 template <int D>
-__device__ __forceinline__ void butterfly(float& x, float& y, int lane) {
-    const float sg = (lane & D) ? -1.f : 1.f;     // lane with bit D set: partner - self
-    const float ox = xor_partner<D>(x, lane), oy = xor_partner<D>(y, lane);
-    x = __builtin_fmaf(sg, x, ox);
-    y = __builtin_fmaf(sg, y, oy);
+__device__ __forceinline__ void butterfly(double& x, double& y, int lane) {
+    const double ox = xor_partner<D>(x, lane), oy = xor_partner<D>(y, lane);
+    // lane with bit D set: partner - self
+    if (lane & D) {
+        x = ox - x;
+        y = oy - y;
+    } else {
+        x = x + ox;
+        y = y + oy;
+    }
 }
 
 // 128-point orthonormal transform of a vector held by one wavefront as v[lane], v[lane + 64]
-__device__ __forceinline__ void wave_wht128(float& a0, float& a1, int lane) {
-    float x = a0 + a1, y = a0 - a1;
+__device__ __forceinline__ void wave_wht128(double& a0, double& a1, int lane) {
+    double x = a0 + a1, y = a0 - a1;
     butterfly<1>(x, y, lane);
     butterfly<2>(x, y, lane);
     butterfly<4>(x, y, lane);
     butterfly<8>(x, y, lane);
     butterfly<16>(x, y, lane);
     butterfly<32>(x, y, lane);
-    a0 = x * kInvSqrt128f;
-    a1 = y * kInvSqrt128f;
+    a0 = x * kInvSqrt128;
+    a1 = y * kInvSqrt128;
 }
 
 template <int KIND>
@@ -157,13 +206,16 @@ __device__ __forceinline__ void load_segment(const PrefillArgs& P, int b, int h,
     in.beta = (tid < SEG && tid < L) ? P.beta[((size_t)b * T + t + tid) * H + h] : 0.f;
 }
 
-// length of the segment starting at t: up to SEG tokens, ending at the next
+// length of the segment starting at t: up to min(chunk, 8) tokens, ending at the next
 // write-back point or the last token
-__device__ __forceinline__ int segment_length(int t, int T, int C) {
+__device__ __forceinline__ int segment_length(int t, int T, int C, int chunk) {
     const int to_wb = C - (t % C);
-    int L = SEG < to_wb ? SEG : to_wb;
+    int L = chunk < SEG ? chunk : SEG;
+    L = L < to_wb ? L : to_wb;
     return L > T - t ? T - t : L;
 }
+
+__device__ __forceinline__ double f16d(uint32_t bits) { return double(f16_bits_to_f32(bits)); }
 
 template <int KIND>
 __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
@@ -180,52 +232,52 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
     const size_t code_base = (size_t)k_hi * DV * 2;
     const size_t meta_base = code_base + (size_t)(DK - k_hi) * DV;
     const int ub = A.bits;
-    const float ustep = 1.f / float(1 << (ub - 1));
+    const double ustep = 1.0 / double(1 << (ub - 1));
 
     for (int i = tid; i < DK; i += NT) sm.perm[i] = (KIND == WB_MIXED) ? int(A.perm[h * DK + i]) : i;
 
     // ---- load and dequantize the stored state into the accumulator layout ----------
-    f32x4 S[8][2];
+    f64x4 S[8][2];
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            float e[4];
+            double e[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * rt + 4 * lg + r;
+                const int row = 16 * rt + lg + 4 * r;
                 const int col = 32 * wave + 16 * ct + lc;
-                float x = 0.f;
+                double x = 0.0;
                 if (KIND == WB_FP32) {
-                    x = reinterpret_cast<const float*>(region)[row * DV + col];
+                    x = double(reinterpret_cast<const float*>(region)[row * DV + col]);
                 } else if (KIND == WB_UNIFORM) {
                     const int bit = (row * DV + col) * ub;
                     const uint32_t byte = region[bit >> 3];
                     int kap = int((byte >> (bit & 7)) & ((1u << ub) - 1));
                     if (kap >= (1 << (ub - 1))) kap -= (1 << ub);
-                    x = float(kap) * ustep;
+                    x = double(kap) * ustep;
                 } else if (KIND == WB_MIXED && row < k_hi) {
-                    x = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(region)[row * DV + col]);
+                    x = f16d(reinterpret_cast<const uint16_t*>(region)[row * DV + col]);
                 } else {
                     const int qrow = row - k_hi;
                     const uint32_t code = region[code_base + (size_t)qrow * DV + col];
                     const uint32_t sz = *reinterpret_cast<const uint32_t*>(
                         region + meta_base + ((size_t)qrow * (DV / 32) + col / 32) * 4);
-                    x = f16_bits_to_f32(sz >> 16) + float(code) * f16_bits_to_f32(sz & 0xFFFFu);
+                    x = f16d(sz >> 16) + double(code) * f16d(sz & 0xFFFFu);
                 }
                 e[r] = x;
             }
-            S[rt][ct] = f32x4{e[0], e[1], e[2], e[3]};
+            S[rt][ct] = f64x4{e[0], e[1], e[2], e[3]};
         }
     __syncthreads();
 
     const int T = P.T;
     const int my_lr = sm.perm[tid & (DK - 1)];
     SegIn nxt;
-    load_segment(P, b, h, 0, segment_length(0, T, P.C), tid, my_lr, nxt);
+    load_segment(P, b, h, 0, segment_length(0, T, P.C, P.chunk), tid, my_lr, nxt);
     int t = 0;
     while (t < T) {
-        const int L = segment_length(t, T, P.C);
+        const int L = segment_length(t, T, P.C, P.chunk);
         const bool write_back = ((t + L) % P.C == 0) || (t + L == T);
         const SegIn cur = nxt;
 
@@ -235,32 +287,34 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             const int i = tid + n * NT, tt = i / DV, j = i - tt * DV;
             sm.v[tt][j] = bf16f(cur.vv[n]);
         }
-        if (tid < SEG) sm.beta[tid] = cur.beta;
+        if (tid < SEG) sm.beta[tid] = double(cur.beta);
         {
             // thread t: row t % 128, tokens 4 (t / 128) .. +3
             const int p = tid & (DK - 1), half = tid / DK;
-            float g[SEG];
-            float acc = 0.f;
+            double g[SEG];
+            double acc = 0.0;
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
-                acc += cur.sv[tt];
+                acc += double(cur.sv[tt]);
                 g[tt] = acc;
             }
-            const float gL = g[L - 1];
-            const float decL = expf(-gL);
+            const double decL = exp(-g[L - 1]);
 #pragma unroll
             for (int t4 = 0; t4 < SEG / 2; ++t4) {
                 const int tt = (SEG / 2) * half + t4;
-                const float gt = half ? g[SEG / 2 + t4] : g[t4];
-                const float kk = bf16f(cur.kk[t4]), qq = bf16f(cur.qq[t4]);
-                const float dec = __expf(-gt);       // hardware exp2 of the scaled argument
-                const float inc = __builtin_amdgcn_rcpf(dec);      // e^{g}, within an ulp or two
-                sm.khat[tt][p] = kk * dec;
-                sm.qhat[tt][p] = qq * dec;
-                sm.kqt[p][tt] = kk * dec;
-                sm.kqt[p][SEG + tt] = qq * dec;
-                sm.kbar[tt][p] = kk * inc;
-                sm.kbarL[tt][p] = kk * (inc * decL);
+                const double gt = half ? g[SEG / 2 + t4] : g[t4];
+                const double kk = double(bf16f(cur.kk[t4])), qq = double(bf16f(cur.qq[t4]));
+                const double dec = exp(-gt);
+                // e^{g}: reciprocal refined by two Newton steps (within an ulp)
+                double inc = __builtin_amdgcn_rcp(dec);
+                inc = fma(fma(-dec, inc, 1.0), inc, inc);
+                inc = fma(fma(-dec, inc, 1.0), inc, inc);
+                sm.u.st.khat[tt][pidx(p)] = kk * dec;
+                sm.u.st.qhat[tt][pidx(p)] = qq * dec;
+                sm.u.st.kqt[p][tt] = kk * dec;
+                sm.u.st.kqt[p][SEG + tt] = qq * dec;
+                sm.u.st.kbar[tt][pidx(p)] = kk * inc;
+                sm.u.st.kbarL[tt][p] = kk * (inc * decL);
             }
             if (half == 0) sm.gl[p] = decL;
         }
@@ -270,65 +324,57 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         {
             const int pair = tid >> 2, part = tid & 3;
             const int tt = pair / SEG, ta = pair - tt * SEG;
-            float a = 0.f, q = 0.f;
+            double a = 0.0, q = 0.0;
             if (ta <= tt && tt < L) {
-                const float4* kh = reinterpret_cast<const float4*>(&sm.khat[tt][32 * part]);
-                const float4* qh = reinterpret_cast<const float4*>(&sm.qhat[tt][32 * part]);
-                const float4* kb = reinterpret_cast<const float4*>(&sm.kbar[ta][32 * part]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float4 x = kh[i], y = qh[i], z = kb[i];
-                    a = __builtin_fmaf(x.x, z.x, a); a = __builtin_fmaf(x.y, z.y, a);
-                    a = __builtin_fmaf(x.z, z.z, a); a = __builtin_fmaf(x.w, z.w, a);
-                    q = __builtin_fmaf(y.x, z.x, q); q = __builtin_fmaf(y.y, z.y, q);
-                    q = __builtin_fmaf(y.z, z.z, q); q = __builtin_fmaf(y.w, z.w, q);
+                const double* kh = &sm.u.st.khat[tt][33 * part];
+                const double* qh = &sm.u.st.qhat[tt][33 * part];
+                const double* kb = &sm.u.st.kbar[ta][33 * part];
+#pragma unroll 8
+                for (int i = 0; i < 32; ++i) {
+                    a = fma(kh[i], kb[i], a);
+                    q = fma(qh[i], kb[i], q);
                 }
             }
-            a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false));
-            q += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(q), 0xB1, 0xF, 0xF, false));
-            a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false));
-            q += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(q), 0x4E, 0xF, 0xF, false));
+            a += mov_dpp_f64<0xB1>(a);
+            q += mov_dpp_f64<0xB1>(q);
+            a += mov_dpp_f64<0x4E>(a);
+            q += mov_dpp_f64<0x4E>(q);
             if (part == 0) {
-                sm.A[tt][ta] = (ta < tt) ? a : 0.f;
-                sm.QK[tt][ta] = (ta <= tt) ? q : 0.f;
+                sm.A[tt][ta] = (ta < tt) ? a : 0.0;
+                sm.QK[tt][ta] = (ta <= tt) ? q : 0.0;
             }
         }
 
         // ---- [k^; q^] S_0 on MFMA (16 x 32 per wave), rotated rows kept apart --------
-        f32x4 accP[2], accQ[2];
+        f64x4 accP[2], accQ[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            accP[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accP[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
             accQ[ct] = accP[ct];
         }
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float a = sm.kqt[16 * rt + 4 * lg + r][lc];
+                const double a = sm.u.st.kqt[16 * rt + lg + 4 * r][lc];
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    const float bv = (r == 0) ? S[rt][ct].x : (r == 1) ? S[rt][ct].y : (r == 2) ? S[rt][ct].z : S[rt][ct].w;
+                    const double bv = S[rt][ct][r];
                     if (LY::rotated(rt))
-                        accQ[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, accQ[ct], 0, 0, 0);
+                        accQ[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, accQ[ct], 0, 0, 0);
                     else
-                        accP[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, accP[ct], 0, 0, 0);
+                        accP[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, accP[ct], 0, 0, 0);
                 }
             }
         }
-        // accumulator element (M = 4*lg + r, column 32w + 16ct + lc)
+        // accumulator element (M = lg + 4r, column 32w + 16ct + lc)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const int col = 32 * wave + 16 * ct + lc;
-            sm.ks[4 * lg + 0][col] = accP[ct].x;
-            sm.ks[4 * lg + 1][col] = accP[ct].y;
-            sm.ks[4 * lg + 2][col] = accP[ct].z;
-            sm.ks[4 * lg + 3][col] = accP[ct].w;
-            if (LY::ROT) {
-                sm.ksq[4 * lg + 0][col] = accQ[ct].x;
-                sm.ksq[4 * lg + 1][col] = accQ[ct].y;
-                sm.ksq[4 * lg + 2][col] = accQ[ct].z;
-                sm.ksq[4 * lg + 3][col] = accQ[ct].w;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sm.u.st.ks[lg + 4 * r][col] = accP[ct][r];
+                if (LY::ROT) sm.u.st.ksq[lg + 4 * r][col] = accQ[ct][r];
             }
         }
         __syncthreads();
@@ -338,10 +384,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv) {
                 const int m = 4 * wave + vv;
-                float a0 = sm.ksq[m][lane], a1 = sm.ksq[m][lane + 64];
+                double a0 = sm.u.st.ksq[m][lane], a1 = sm.u.st.ksq[m][lane + 64];
                 wave_wht128(a0, a1, lane);
-                sm.ks[m][lane] += a0;
-                sm.ks[m][lane + 64] += a1;
+                sm.u.st.ks[m][lane] += a0;
+                sm.u.st.ks[m][lane + 64] += a1;
             }
             __syncthreads();
         }
@@ -349,32 +395,32 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         // ---- per column: forward solve for w (threads 0..127) ------------------------
         if (tid < DV) {
             const int j = tid;
-            float wv[SEG];
+            double wv[SEG];
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
-                float u = sm.v[tt][j] - sm.ks[tt][j];
+                double u = double(sm.v[tt][j]) - sm.u.st.ks[tt][j];
 #pragma unroll
-                for (int ta = 0; ta < tt; ++ta) u = __builtin_fmaf(-sm.A[tt][ta], wv[ta], u);
+                for (int ta = 0; ta < tt; ++ta) u = fma(-sm.A[tt][ta], wv[ta], u);
                 wv[tt] = sm.beta[tt] * u;
                 sm.w[tt][j] = wv[tt];
             }
         }
         // inputs of the next segment (requested before this segment's output stores)
-        if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C), tid, my_lr, nxt);
+        if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C, P.chunk), tid, my_lr, nxt);
         __syncthreads();
         // ---- outputs o (threads 128..255) beside H w (threads 0..127) ------------------
         if (tid >= NT - DV) {
             const int j = tid - (NT - DV);
-            float wv[SEG];
+            double wv[SEG];
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) wv[tt] = sm.w[tt][j];
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) {
                 if (tt < L) {
-                    float o = sm.ks[SEG + tt][j];
+                    double o = sm.u.st.ks[SEG + tt][j];
 #pragma unroll
-                    for (int ta = 0; ta <= tt; ++ta) o = __builtin_fmaf(sm.QK[tt][ta], wv[ta], o);
-                    P.o[(((size_t)b * T + t + tt) * H + h) * DV + j] = o;
+                    for (int ta = 0; ta <= tt; ++ta) o = fma(sm.QK[tt][ta], wv[ta], o);
+                    P.o[(((size_t)b * T + t + tt) * H + h) * DV + j] = float(o);
                 }
             }
         } else if (LY::ROT) {
@@ -382,7 +428,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv) {
                 const int m = 4 * wave + vv;
-                float a0 = sm.w[m][lane], a1 = sm.w[m][lane + 64];
+                double a0 = sm.w[m][lane], a1 = sm.w[m][lane + 64];
                 wave_wht128(a0, a1, lane);
                 sm.hw[m][lane] = a0;
                 sm.hw[m][lane + 64] = a1;
@@ -393,164 +439,164 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         // ---- S_L = Gamma_L S_0 + sum_tau (Gamma_L k-_tau) w_tau^T  (MFMA, K = 8) ------
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
-            const float g0 = sm.gl[16 * rt + 4 * lg + 0], g1 = sm.gl[16 * rt + 4 * lg + 1];
-            const float g2 = sm.gl[16 * rt + 4 * lg + 2], g3 = sm.gl[16 * rt + 4 * lg + 3];
-            const float* wsrc = LY::rotated(rt) ? &sm.hw[0][0] : &sm.w[0][0];
+            const double* wsrc = LY::rotated(rt) ? &sm.hw[0][0] : &sm.w[0][0];
+            double gv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gv[r] = sm.gl[16 * rt + lg + 4 * r];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                f32x4 c = S[rt][ct];
-                c.x *= g0;
-                c.y *= g1;
-                c.z *= g2;
-                c.w *= g3;
+                f64x4 c = S[rt][ct];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) c[r] *= gv[r];
                 const int col = 32 * wave + 16 * ct + lc;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const int tok = 4 * kk + lg;
-                    const float a = sm.kbarL[tok][16 * rt + lc];
-                    const float bv = wsrc[tok * DV + col];
-                    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, c, 0, 0, 0);
+                    const double a = sm.u.st.kbarL[tok][16 * rt + lc];
+                    const double bv = wsrc[tok * VS + col];
+                    c = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, c, 0, 0, 0);
                 }
                 S[rt][ct] = c;
             }
         }
 
         // ---- write-back ---------------------------------------------------------------
-        // The state goes through LDS in row-major order: each thread then rounds two
-        // whole 32-value row blocks (one INT8 block each: extrema, float16 metadata and
-        // levels without cross-lane steps), and the call's last write-back stores its
-        // codes contiguously.
+        // The state goes through LDS in row-major order, 64 rows at a time: each thread
+        // then rounds one whole 32-value row block (one INT8 block: extrema, float16
+        // metadata and levels without cross-lane steps), and the call's last write-back
+        // stores its codes contiguously.
         if (write_back && KIND != WB_FP32) {
             const bool last = (t + L == T);
+            __syncthreads();      // every wave is done with the staging area
 #pragma unroll
-            for (int rt = 0; rt < 8; ++rt)
+            for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const int col = 32 * wave + 16 * ct + lc;
-                    const f32x4 v = S[rt][ct];
-                    sm.wbuf[16 * rt + 4 * lg + 0][col] = v.x;
-                    sm.wbuf[16 * rt + 4 * lg + 1][col] = v.y;
-                    sm.wbuf[16 * rt + 4 * lg + 2][col] = v.z;
-                    sm.wbuf[16 * rt + 4 * lg + 3][col] = v.w;
-                }
-            __syncthreads();
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int rt = 4 * hv + rq;
 #pragma unroll
-            for (int unit = 0; unit < 2; ++unit) {
-                const int u = tid + NT * unit;
-                const int row = u >> 2, cb = u & 3;          // row block: columns 32 cb .. +31
-                float4* rp = reinterpret_cast<float4*>(&sm.wbuf[row][32 * cb]);
-                float x[32];
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const int col = 32 * wave + 16 * ct + lc;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float4 f = rp[i];
-                    x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
-                }
-                if (KIND == WB_UNIFORM) {
-                    const float lo = -float(1 << (ub - 1)), hi = float((1 << (ub - 1)) - 1);
-                    const float inv = float(1 << (ub - 1));
-                    float kv[32];
-#pragma unroll
-                    for (int c = 0; c < 32; ++c) {
-                        kv[c] = fminf(fmaxf(rintf(x[c] * inv), lo), hi);
-                        x[c] = kv[c] * ustep;
+                        for (int r = 0; r < 4; ++r) sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)] = S[rt][ct][r];
                     }
-                    if (last) {
-                        // codes are packed only where they are stored
-                        uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // 32 fields of ub <= 8 bits
+                }
+                __syncthreads();
+                {
+                    const int lrow = tid >> 2, cb = tid & 3;        // row block: columns 32 cb .. +31
+                    const int row = 64 * hv + lrow;
+                    double* rp = &sm.u.wbuf[lrow][33 * cb];
+                    double x[32];
+#pragma unroll
+                    for (int c = 0; c < 32; ++c) x[c] = rp[c];
+                    if (KIND == WB_UNIFORM) {
+                        const double lo = -double(1 << (ub - 1)), hi = double((1 << (ub - 1)) - 1);
+                        const double inv = double(1 << (ub - 1));
+                        double kv[32];
 #pragma unroll
                         for (int c = 0; c < 32; ++c) {
-                            const int bit = c * ub;
-                            wd[bit >> 5] |= (uint32_t(int(kv[c])) & ((1u << ub) - 1)) << (bit & 31);
+                            kv[c] = fmin(fmax(rint(x[c] * inv), lo), hi);
+                            x[c] = kv[c] * ustep;
                         }
-                        // element (row, col) at bit ub (row DV + col): this block is 4 ub
-                        // contiguous bytes, 4-byte aligned
-                        uint32_t* dst = reinterpret_cast<uint32_t*>(region + ((row * DV + 32 * cb) * ub) / 8);
-                        for (int i = 0; i < ub; ++i) dst[i] = wd[i];
-                    }
-                } else if (KIND == WB_MIXED && row < k_hi) {
-                    uint32_t hw2[16];
+                        if (last) {
+                            // codes are packed only where they are stored
+                            uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // 32 fields of ub <= 8 bits
 #pragma unroll
-                    for (int c = 0; c < 32; c += 2) {
-                        const uint16_t h0 = f32_to_f16_bits(x[c]), h1 = f32_to_f16_bits(x[c + 1]);
-                        x[c] = f16_bits_to_f32(h0);
-                        x[c + 1] = f16_bits_to_f32(h1);
-                        hw2[c >> 1] = uint32_t(h0) | (uint32_t(h1) << 16);
-                    }
-                    if (last) {
-                        uint4* dst = reinterpret_cast<uint4*>(region + (row * DV + 32 * cb) * 2);
+                            for (int c = 0; c < 32; ++c) {
+                                const int bit = c * ub;
+                                wd[bit >> 5] |= (uint32_t(int(kv[c])) & ((1u << ub) - 1)) << (bit & 31);
+                            }
+                            // element (row, col) at bit ub (row DV + col): this block is 4 ub
+                            // contiguous bytes, 4-byte aligned
+                            uint32_t* dst = reinterpret_cast<uint32_t*>(region + ((row * DV + 32 * cb) * ub) / 8);
+                            for (int i = 0; i < ub; ++i) dst[i] = wd[i];
+                        }
+                    } else if (KIND == WB_MIXED && row < k_hi) {
+                        // float16 rows: one correctly rounded conversion per value
+                        uint32_t hw2[16];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            dst[i] = make_uint4(hw2[4 * i], hw2[4 * i + 1], hw2[4 * i + 2], hw2[4 * i + 3]);
-                    }
-                } else {
-                    // affine INT8 block of 32 values
-                    float mn = x[0], mx = x[0];
+                        for (int c = 0; c < 32; c += 2) {
+                            const uint16_t h0 = f64_to_f16_bits(x[c]), h1 = f64_to_f16_bits(x[c + 1]);
+                            x[c] = f16d(h0);
+                            x[c + 1] = f16d(h1);
+                            hw2[c >> 1] = uint32_t(h0) | (uint32_t(h1) << 16);
+                        }
+                        if (last) {
+                            uint4* dst = reinterpret_cast<uint4*>(region + (row * DV + 32 * cb) * 2);
 #pragma unroll
-                    for (int c = 1; c < 32; ++c) {
-                        mn = fminf(mn, x[c]);
-                        mx = fmaxf(mx, x[c]);
-                    }
-                    const uint32_t sb = f16_bits_of_product(fmaxf(mx - mn, 0.f), 1.f / 255.f);
-                    const uint16_t zb = f32_to_f16_bits(mn);
-                    const float sc = f16_bits_to_f32(sb), ze = f16_bits_to_f32(zb);
-                    // levels in magic-number form (1.5 * 2^23 + level); level 0 if the
-                    // block is constant
-                    constexpr float M = 12582912.0f;
-                    float yv[32];
-                    if (sc > 0.f) {
-                        // reciprocal refined by one Newton step; rounding by adding 1.5 * 2^23
-                        // (ties to even), clamp by med3
-                        float inv = __builtin_amdgcn_rcpf(sc);
-                        inv = __builtin_fmaf(__builtin_fmaf(-sc, inv, 1.f), inv, inv);
-#pragma unroll
-                        for (int c = 0; c < 32; ++c) {
-                            yv[c] = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c] - ze, inv, M), M, M + 255.f);
-                            x[c] = __builtin_fmaf(yv[c] - M, sc, ze);
+                            for (int i = 0; i < 4; ++i)
+                                dst[i] = make_uint4(hw2[4 * i], hw2[4 * i + 1], hw2[4 * i + 2], hw2[4 * i + 3]);
                         }
                     } else {
+                        // affine INT8 block of 32 values: scale = f16((max - min) / 255) and
+                        // zero = f16(min), each rounded once from float64; the level is
+                        // (x - zero) / scale rounded to nearest (ties to even), clamped to [0, 255]
+                        double mn = x[0], mx = x[0];
 #pragma unroll
-                        for (int c = 0; c < 32; ++c) {
-                            yv[c] = M;
-                            x[c] = ze;
+                        for (int c = 1; c < 32; ++c) {
+                            mn = fmin(mn, x[c]);
+                            mx = fmax(mx, x[c]);
+                        }
+                        const uint16_t sb = f64_to_f16_bits(fmax(mx - mn, 0.0) / 255.0);
+                        const uint16_t zb = f64_to_f16_bits(mn);
+                        const double sc = f16d(sb), ze = f16d(zb);
+                        uint32_t cw4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                        if (sc > 0.0) {
+                            const double inv = 1.0 / sc;
+#pragma unroll
+                            for (int c = 0; c < 32; ++c) {
+                                const double lev = fmin(fmax(rint((x[c] - ze) * inv), 0.0), 255.0);
+                                x[c] = fma(lev, sc, ze);
+                                cw4[c >> 2] |= uint32_t(lev) << (8 * (c & 3));
+                            }
+                        } else {
+#pragma unroll
+                            for (int c = 0; c < 32; ++c) x[c] = ze;
+                        }
+                        if (last) {
+                            const int qrow = row - k_hi;
+                            uint4* dst = reinterpret_cast<uint4*>(region + code_base + (size_t)qrow * DV + 32 * cb);
+                            dst[0] = make_uint4(cw4[0], cw4[1], cw4[2], cw4[3]);
+                            dst[1] = make_uint4(cw4[4], cw4[5], cw4[6], cw4[7]);
+                            *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + cb) * 4) =
+                                uint32_t(sb) | (uint32_t(zb) << 16);
                         }
                     }
-                    if (last) {
-                        // codes are packed only where they are stored
-                        uint32_t cw4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                        for (int c = 0; c < 32; ++c) cw4[c >> 2] |= (__float_as_uint(yv[c]) & 0xFFu) << (8 * (c & 3));
-                        const int qrow = row - k_hi;
-                        uint4* dst = reinterpret_cast<uint4*>(region + code_base + (size_t)qrow * DV + 32 * cb);
-                        dst[0] = make_uint4(cw4[0], cw4[1], cw4[2], cw4[3]);
-                        dst[1] = make_uint4(cw4[4], cw4[5], cw4[6], cw4[7]);
-                        *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + cb) * 4) =
-                            uint32_t(sb) | (uint32_t(zb) << 16);
+                    for (int c = 0; c < 32; ++c) rp[c] = x[c];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int rt = 4 * hv + rq;
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const int col = 32 * wave + 16 * ct + lc;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) S[rt][ct][r] = sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)];
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) rp[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+                __syncthreads();
             }
-            __syncthreads();
+        }
+        if (KIND == WB_FP32 && write_back) {
+            // identity write-back: the state continues from its float32 copy
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const int col = 32 * wave + 16 * ct + lc;
-                    S[rt][ct] = f32x4{sm.wbuf[16 * rt + 4 * lg + 0][col], sm.wbuf[16 * rt + 4 * lg + 1][col],
-                                      sm.wbuf[16 * rt + 4 * lg + 2][col], sm.wbuf[16 * rt + 4 * lg + 3][col]};
-                }
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[rt][ct][r] = double(float(S[rt][ct][r]));
         }
         if (KIND == WB_FP32 && t + L == T) {
+            // the stored float32 state
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     const int col = 32 * wave + 16 * ct + lc;
                     float* dst = reinterpret_cast<float*>(region);
-                    dst[(16 * rt + 4 * lg + 0) * DV + col] = S[rt][ct].x;
-                    dst[(16 * rt + 4 * lg + 1) * DV + col] = S[rt][ct].y;
-                    dst[(16 * rt + 4 * lg + 2) * DV + col] = S[rt][ct].z;
-                    dst[(16 * rt + 4 * lg + 3) * DV + col] = S[rt][ct].w;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(16 * rt + lg + 4 * r) * DV + col] = float(S[rt][ct][r]);
                 }
         }
         __syncthreads();

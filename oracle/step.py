@@ -296,11 +296,12 @@ def _round_at(lay: L.Layout, Y, alloc):
 
 
 def prefill(lay: L.Layout, region, e_in, q, k, v, beta, s, t0: int, C: int, b: int, h: int,
-            perm=None, return_last=False):
+            perm=None, return_last=False, records=None):
     """Token-by-token prefill of one head with write-back after every C-th token of
     the call and after the last one. q, k, v, beta, s are per-token arrays for this
     head ([T][d], [T], [T][dk] or [T]). Returns (region, e, outputs [T][dv]) and, with
-    ``return_last``, the record of the last write-back (its pre-rounding values)."""
+    ``return_last``, the record of the last write-back (its pre-rounding values);
+    ``records`` (a list) receives (token index, record) of every write-back."""
     T = len(beta)
     content = L.decode_region(lay, region)
     S = L.to_logical(lay, L.stored_values(lay, content), perm)
@@ -312,6 +313,8 @@ def prefill(lay: L.Layout, region, e_in, q, k, v, beta, s, t0: int, C: int, b: i
         if (i + 1) % C == 0 or i == T - 1:
             X = L.to_stored(lay, S, perm)
             wb = write_back(lay, X, e, t0 + i, b, h, prev=content)
+            if records is not None:
+                records.append((i, wb))
             region = wb.region
             e = wb.e_new
             content = L.decode_region(lay, region)
