@@ -32,21 +32,6 @@ constexpr int DK = 128, DV = 128, NT = 256, NCG = 16, RS = 16;
 constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
 constexpr uint32_t kMagicBits = 0x4B400000u;
 
-// float64 -> float16 bits, correctly rounded (nearest, ties to even): rounding to odd
-// at float32 precision, then the hardware conversion (Boldo & Melquiond, IEEE Trans.
-// Computers 2008: a rounding to odd with at least two more bits than the target
-// followed by the final rounding is the correct rounding)
-__device__ __forceinline__ uint16_t f64_to_f16_rto(double x) {
-    const float f = float(x);
-    uint32_t fb = __float_as_uint(f);
-    const double back = double(f);
-    if (back != x) {
-        if (fabs(back) > fabs(x)) fb -= 1u;   // one step toward zero: the truncation
-        fb |= 1u;                             // sticky bit: round to odd
-    }
-    return __half_as_ushort(__float2half_rn(__uint_as_float(fb)));
-}
-
 // fit fractions f_k = 1/4 + k/20 in float64 (the same operations, at compile time)
 struct FitTable {
     double f[16];
@@ -507,7 +492,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     for (int i = tid; i < DK * 16; i += NT) {
         const int row = i >> 4, kf = i & 15;
         const int n = (1 << (sm.newwidth[row] - 1)) - 1;      // 0: a one-bit row, no fit
-        const float d = n ? f16_bits_to_f32(f64_to_f16_rto(kFit.f[kf] * sm.R[row] / n)) : 0.f;
+        const float d = n ? f16_bits_to_f32(f64_to_f16_bits(kFit.f[kf] * sm.R[row] / n)) : 0.f;
         // reciprocal refined by one Newton step: it only orders candidate errors and
         // pre-rounds the repack, which falls back to an exact quotient near half-integers
         float r = __builtin_amdgcn_rcpf(d);
@@ -539,7 +524,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             sa += dpp_f64<0x4E>(sa);
             sa += dpp_f64<0x141>(sa);
             sa += dpp_f64<0x140>(sa);
-            dbits = f64_to_f16_rto(sa / double(DV));
+            dbits = f64_to_f16_bits(sa / double(DV));
             if (dbits) {
 #pragma unroll
                 for (int c = 0; c < 8; ++c) fld |= uint64_t(x[m][c] > 0.f) << c;
@@ -862,7 +847,7 @@ __global__ void __launch_bounds__(NT) headalloc_pack_kernel(const AllocArgs A) {
         int best = 15;
         float be = 0.f;
         for (int k = 15; k >= 0; --k) {
-            const float d = f16_bits_to_f32(f64_to_f16_rto(kFit.f[k] * double(R) / double(nn)));
+            const float d = f16_bits_to_f32(f64_to_f16_bits(kFit.f[k] * double(R) / double(nn)));
             const float inv = d > 0.f ? 1.f / d : 0.f;
             float e = 0.f;
 #pragma unroll
@@ -876,7 +861,7 @@ __global__ void __launch_bounds__(NT) headalloc_pack_kernel(const AllocArgs A) {
                 best = k;
             }
         }
-        const uint16_t dbits = f64_to_f16_rto(kFit.f[best] * double(R) / double(nn));
+        const uint16_t dbits = f64_to_f16_bits(kFit.f[best] * double(R) / double(nn));
         const double d = double(f16_bits_to_f32(dbits));
 #pragma unroll
         for (int rr = 0; rr < 32; ++rr) {

@@ -61,17 +61,6 @@ struct RotSmem {
     uint32_t reg[LY::REGION / 4];
 };
 
-__device__ __forceinline__ uint16_t f64_to_f16_rto(double x) {
-    const float f = float(x);
-    uint32_t fb = __float_as_uint(f);
-    const double back = double(f);
-    if (back != x) {
-        if (fabs(back) > fabs(x)) fb -= 1u;   // one step toward zero: the truncation
-        fb |= 1u;                             // sticky bit: round to odd
-    }
-    return __half_as_ushort(__float2half_rn(__uint_as_float(fb)));
-}
-
 __device__ __forceinline__ double f16_to_f64(uint32_t bits) { return double(f16_bits_to_f32(bits)); }
 
 // min and max over the lanes of one block (BLOCK / 16 consecutive lanes of a DPP row)
@@ -324,7 +313,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                     for (int c = 0; c < 8; ++c) {
                         const double x = f16_to_f64((w4[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu);
                         const double xn = fma(ak.x, x, ak.y * sm.w[16 * cg + 8 * hv + c]);
-                        o4[c >> 1] |= uint32_t(f64_to_f16_rto(xn)) << ((c & 1) * 16);
+                        o4[c >> 1] |= uint32_t(f64_to_f16_bits(xn)) << ((c & 1) * 16);
                     }
                     ptr[hv] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
                 }
@@ -361,8 +350,8 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             block_minmax<BLOCK>(mn, mx);
             // (a product with 1/TOP instead of the quotient: the two differ by at most one
             // float64 unit, which moves a float16 rounding only at a midpoint)
-            const uint16_t sbits = f64_to_f16_rto(fmax(mx - mn, 0.0) * (1.0 / double(LY::TOP)));
-            const uint16_t zbits = f64_to_f16_rto(mn);
+            const uint16_t sbits = f64_to_f16_bits(fmax(mx - mn, 0.0) * (1.0 / double(LY::TOP)));
+            const uint16_t zbits = f64_to_f16_bits(mn);
             const double scale = f16_to_f64(sbits), zero = f16_to_f64(zbits);
             uint32_t o4[4] = {0, 0, 0, 0};
             if (scale != 0.0) {

@@ -25,19 +25,20 @@
 // are stored as float32.
 //
 // State placement: the 128 x 128 state lives in registers in the float64 MFMA
-// accumulator layout. Wave w owns columns 32w .. 32w+31 (2 column tiles of 16) and all
-// 8 row tiles; register r of lane l holds row 16*rt + l/16 + 4*r (r = 0..3) of column
-// 32w + 16*ct + l%16 (the float64 16 x 16 result interleaves its rows over the four lane
-// groups, unlike the float32 one, which gives each lane group 4 consecutive rows). The
+// accumulator layout, over 8 wavefronts (2 per SIMD, so that one hides the other's
+// latency). Wave w owns columns 16w .. 16w+15 (one column tile) and all 8 row tiles;
+// register r of lane l holds row 16*rt + l/16 + 4*r (r = 0..3) of column 16w + l%16
+// (the float64 16 x 16 result interleaves its rows over the four lane groups, unlike
+// the float32 one, which gives each lane group 4 consecutive rows). The
 // same registers serve as the B operand of the [k^; q^] S_0 contraction (K index =
 // row), so no state data moves between waves. Hadamard rows stay rotated (Y = S H):
 // the contraction over rotated rows is transformed back with one 128-point transform
 // per output vector, and rotated rows are updated with H w.
 //
 // Write-back (every C tokens and after the last token) rounds the state in place,
-// through LDS in two halves of 64 rows (one thread per 32-value row block): float16
-// rows to the nearest float16; Hadamard INT8 rows per block of 32 columns (= one wave's
-// columns) on an asymmetric affine grid ([DAMP] "Quantization & calibration details");
+// through LDS in two halves of 64 rows (two threads per 32-value row block): float16
+// rows to the nearest float16; Hadamard INT8 rows per block of 32 columns on an
+// asymmetric affine grid ([DAMP] "Quantization & calibration details");
 // uniform rows on the B-bit grid. The last write-back is also encoded into the stored
 // region. Supported here: FP32, UNIFORM, HAD_INT8 and MIXED with affine blocks of 32
 // values, round-to-nearest.
@@ -47,23 +48,23 @@
 namespace wb {
 namespace {
 
-constexpr int DK = 128, DV = 128, NT = 256, SEG = 8;
+constexpr int DK = 128, DV = 128, NW = 8, NT = 64 * NW, SEG = 8;
 typedef double f64x4 __attribute__((ext_vector_type(4)));   // MFMA accumulator fragment
 constexpr double kInvSqrt128 = 0.088388347648318440550;     // 1 / sqrt(128)
 
 // LDS strides (in doubles) chosen against bank conflicts of 64-bit accesses, taken per
 // half wavefront (32 lanes, 32 double-wide bank pairs):
-//   * PS:  rows of k^, q^, k- as 4 parts of 32 rows padded to 33 (the Gram quads read
-//          part x token pairs: slots 4 token + part, all distinct);
+//   * PS:  rows of k^, q^, k- as 8 parts of 16 rows padded to 17 (the Gram threads read
+//          4 tokens x 8 parts per half wavefront: slots 8 token + 17 part, all distinct);
 //   * VS:  vectors over the value axis read by two lane groups at once (rows 16 apart
 //          in slots: 128 + 16);
 //   * KQS: the transposed [k^; q^] (odd, so a row's 16 entries and the next row's
 //          do not collide);
-//   * WBS: the write-back copy, row blocks of 32 padded to 33 and rows to 148 (= 20 mod
-//          32): the per-block threads (8 rows x 4 blocks per half wavefront) read
+//   * WBS: the write-back copy, row blocks of 32 padded to 33 (132 = 4 mod 32): the
+//          block threads (4 rows x 4 blocks x 2 halves per half wavefront) read
 //          distinct slots.
-constexpr int PS = 4 * 33, VS = DV + 16, KQS = 17, WBS = 148;
-__device__ __forceinline__ int pidx(int row) { return (row >> 5) * 33 + (row & 31); }    // row in a PS row
+constexpr int PS = 8 * 17, VS = DV + 16, KQS = 17, WBS = 4 * 33;
+__device__ __forceinline__ int pidx(int row) { return (row >> 4) * 17 + (row & 15); }    // row in a PS row
 __device__ __forceinline__ int widx(int col) { return (col >> 5) * 33 + (col & 31); }    // column in a WBS row
 
 // per-segment staging (dead while the write-back uses the same storage)
@@ -91,6 +92,7 @@ struct PfSmem {
 };
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ double f16d(uint32_t bits) { return double(f16_bits_to_f32(bits)); }
 
 // DPP move of a float64 inside rows of 16 lanes (both halves)
 template <int CTRL>
@@ -164,11 +166,12 @@ struct PfLayout {
 };
 
 // One segment's inputs as this thread reads them: thread t owns physical row t % 128
-// for the tokens 4 (t / 128) .. +3 (k and q; the decays of all the segment's tokens),
-// every thread owns 4 values of v, and threads 0..7 one beta each. Loaded a segment
+// for the tokens 2 (t / 128), +1 (k and q; the decays of all the segment's tokens),
+// every thread owns 2 values of v, and threads 0..7 one beta each. Loaded a segment
 // ahead into registers.
+constexpr int TPT = SEG * DK / NT;     // tokens per thread in the staging
 struct SegIn {
-    uint16_t kk[SEG / 2], qq[SEG / 2];
+    uint16_t kk[TPT], qq[TPT];
     float sv[SEG];
     uint16_t vv[SEG * DV / NT];
     float beta;
@@ -178,7 +181,7 @@ __device__ __forceinline__ void load_segment(const PrefillArgs& P, int b, int h,
                                              SegIn& in) {
     const KArgs& A = P.base;
     const int H = A.H, T = P.T;
-    const int half = tid / DK;
+    const int quarter = tid / DK;
 #pragma unroll
     for (int tt = 0; tt < SEG; ++tt) {
         in.sv[tt] = 0.f;
@@ -188,14 +191,14 @@ __device__ __forceinline__ void load_segment(const PrefillArgs& P, int b, int h,
         }
     }
 #pragma unroll
-    for (int t4 = 0; t4 < SEG / 2; ++t4) {
-        const int tt = (SEG / 2) * half + t4;
-        in.kk[t4] = 0;
-        in.qq[t4] = 0;
+    for (int i = 0; i < TPT; ++i) {
+        const int tt = TPT * quarter + i;
+        in.kk[i] = 0;
+        in.qq[i] = 0;
         if (tt < L) {
             const size_t base = ((size_t)b * T + t + tt) * H + h;
-            in.kk[t4] = P.k[base * DK + lr];
-            in.qq[t4] = P.q[base * DK + lr];
+            in.kk[i] = P.k[base * DK + lr];
+            in.qq[i] = P.q[base * DK + lr];
         }
     }
 #pragma unroll
@@ -215,8 +218,6 @@ __device__ __forceinline__ int segment_length(int t, int T, int C, int chunk) {
     return L > T - t ? T - t : L;
 }
 
-__device__ __forceinline__ double f16d(uint32_t bits) { return double(f16_bits_to_f32(bits)); }
-
 template <int KIND>
 __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
     __shared__ PfSmem sm;
@@ -227,6 +228,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
     const int H = A.H;
     const int b = head / H, h = head - b * H;
     const int lc = lane & 15, lg = lane >> 4;          // column within tile, row group
+    const int col = 16 * wave + lc;                     // this lane's state column
     uint8_t* region = A.state + (size_t)head * A.region_stride;
     const int k_hi = (KIND == WB_MIXED) ? A.k_hi : 0;
     const size_t code_base = (size_t)k_hi * DV * 2;
@@ -237,38 +239,35 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
     for (int i = tid; i < DK; i += NT) sm.perm[i] = (KIND == WB_MIXED) ? int(A.perm[h * DK + i]) : i;
 
     // ---- load and dequantize the stored state into the accumulator layout ----------
-    f64x4 S[8][2];
+    f64x4 S[8];
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int rt = 0; rt < 8; ++rt) {
+        double e[4];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            double e[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * rt + lg + 4 * r;
-                const int col = 32 * wave + 16 * ct + lc;
-                double x = 0.0;
-                if (KIND == WB_FP32) {
-                    x = double(reinterpret_cast<const float*>(region)[row * DV + col]);
-                } else if (KIND == WB_UNIFORM) {
-                    const int bit = (row * DV + col) * ub;
-                    const uint32_t byte = region[bit >> 3];
-                    int kap = int((byte >> (bit & 7)) & ((1u << ub) - 1));
-                    if (kap >= (1 << (ub - 1))) kap -= (1 << ub);
-                    x = double(kap) * ustep;
-                } else if (KIND == WB_MIXED && row < k_hi) {
-                    x = f16d(reinterpret_cast<const uint16_t*>(region)[row * DV + col]);
-                } else {
-                    const int qrow = row - k_hi;
-                    const uint32_t code = region[code_base + (size_t)qrow * DV + col];
-                    const uint32_t sz = *reinterpret_cast<const uint32_t*>(
-                        region + meta_base + ((size_t)qrow * (DV / 32) + col / 32) * 4);
-                    x = f16d(sz >> 16) + double(code) * f16d(sz & 0xFFFFu);
-                }
-                e[r] = x;
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rt + lg + 4 * r;
+            double x = 0.0;
+            if (KIND == WB_FP32) {
+                x = double(reinterpret_cast<const float*>(region)[row * DV + col]);
+            } else if (KIND == WB_UNIFORM) {
+                const int bit = (row * DV + col) * ub;
+                const uint32_t byte = region[bit >> 3];
+                int kap = int((byte >> (bit & 7)) & ((1u << ub) - 1));
+                if (kap >= (1 << (ub - 1))) kap -= (1 << ub);
+                x = double(kap) * ustep;
+            } else if (KIND == WB_MIXED && row < k_hi) {
+                x = f16d(reinterpret_cast<const uint16_t*>(region)[row * DV + col]);
+            } else {
+                const int qrow = row - k_hi;
+                const uint32_t code = region[code_base + (size_t)qrow * DV + col];
+                const uint32_t sz = *reinterpret_cast<const uint32_t*>(
+                    region + meta_base + ((size_t)qrow * (DV / 32) + col / 32) * 4);
+                x = f16d(sz >> 16) + double(code) * f16d(sz & 0xFFFFu);
             }
-            S[rt][ct] = f64x4{e[0], e[1], e[2], e[3]};
+            e[r] = x;
         }
+        S[rt] = f64x4{e[0], e[1], e[2], e[3]};
+    }
     __syncthreads();
 
     const int T = P.T;
@@ -289,8 +288,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         }
         if (tid < SEG) sm.beta[tid] = double(cur.beta);
         {
-            // thread t: row t % 128, tokens 4 (t / 128) .. +3
-            const int p = tid & (DK - 1), half = tid / DK;
+            // thread t: row t % 128, tokens 2 (t / 128), +1
+            const int p = tid & (DK - 1), quarter = tid / DK;
             double g[SEG];
             double acc = 0.0;
 #pragma unroll
@@ -300,11 +299,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
             }
             const double decL = exp(-g[L - 1]);
 #pragma unroll
-            for (int t4 = 0; t4 < SEG / 2; ++t4) {
-                const int tt = (SEG / 2) * half + t4;
-                const double gt = half ? g[SEG / 2 + t4] : g[t4];
-                const double kk = double(bf16f(cur.kk[t4])), qq = double(bf16f(cur.qq[t4]));
-                const double dec = exp(-gt);
+            for (int i = 0; i < TPT; ++i) {
+                const int tt = TPT * quarter + i;
+                const double kk = double(bf16f(cur.kk[i])), qq = double(bf16f(cur.qq[i]));
+                const double dec = exp(-g[tt]);
                 // e^{g}: reciprocal refined by two Newton steps (within an ulp)
                 double inc = __builtin_amdgcn_rcp(dec);
                 inc = fma(fma(-dec, inc, 1.0), inc, inc);
@@ -316,74 +314,63 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 sm.u.st.kbar[tt][pidx(p)] = kk * inc;
                 sm.u.st.kbarL[tt][p] = kk * (inc * decL);
             }
-            if (half == 0) sm.gl[p] = decL;
+            if (quarter == 0) sm.gl[p] = decL;
         }
         __syncthreads();
         // small Gram matrices: A[t][tau] = k^_t . k-_tau (tau < t), QK[t][tau] (tau <= t);
-        // four lanes (a DPP quad) per entry, 32 rows each
+        // eight lanes per entry, 16 rows each
         {
-            const int pair = tid >> 2, part = tid & 3;
+            const int pair = tid >> 3, part = tid & 7;
             const int tt = pair / SEG, ta = pair - tt * SEG;
             double a = 0.0, q = 0.0;
             if (ta <= tt && tt < L) {
-                const double* kh = &sm.u.st.khat[tt][33 * part];
-                const double* qh = &sm.u.st.qhat[tt][33 * part];
-                const double* kb = &sm.u.st.kbar[ta][33 * part];
-#pragma unroll 8
-                for (int i = 0; i < 32; ++i) {
+                const double* kh = &sm.u.st.khat[tt][17 * part];
+                const double* qh = &sm.u.st.qhat[tt][17 * part];
+                const double* kb = &sm.u.st.kbar[ta][17 * part];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
                     a = fma(kh[i], kb[i], a);
                     q = fma(qh[i], kb[i], q);
                 }
             }
-            a += mov_dpp_f64<0xB1>(a);
+            a += mov_dpp_f64<0xB1>(a);      // xor 1
             q += mov_dpp_f64<0xB1>(q);
-            a += mov_dpp_f64<0x4E>(a);
+            a += mov_dpp_f64<0x4E>(a);      // xor 2
             q += mov_dpp_f64<0x4E>(q);
+            a += mov_dpp_f64<0x141>(a);     // half mirror: the other quad of the 8 lanes
+            q += mov_dpp_f64<0x141>(q);
             if (part == 0) {
                 sm.A[tt][ta] = (ta < tt) ? a : 0.0;
                 sm.QK[tt][ta] = (ta <= tt) ? q : 0.0;
             }
         }
 
-        // ---- [k^; q^] S_0 on MFMA (16 x 32 per wave), rotated rows kept apart --------
-        f64x4 accP[2], accQ[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            accP[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
-            accQ[ct] = accP[ct];
-        }
+        // ---- [k^; q^] S_0 on MFMA (16 x 16 per wave), rotated rows kept apart --------
+        f64x4 accP = f64x4{0.0, 0.0, 0.0, 0.0}, accQ = accP;
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const double a = sm.u.st.kqt[16 * rt + lg + 4 * r][lc];
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const double bv = S[rt][ct][r];
-                    if (LY::rotated(rt))
-                        accQ[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, accQ[ct], 0, 0, 0);
-                    else
-                        accP[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, accP[ct], 0, 0, 0);
-                }
+                if (LY::rotated(rt))
+                    accQ = __builtin_amdgcn_mfma_f64_16x16x4f64(a, S[rt][r], accQ, 0, 0, 0);
+                else
+                    accP = __builtin_amdgcn_mfma_f64_16x16x4f64(a, S[rt][r], accP, 0, 0, 0);
             }
         }
-        // accumulator element (M = lg + 4r, column 32w + 16ct + lc)
+        // accumulator element (M = lg + 4r, column 16w + lc)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int col = 32 * wave + 16 * ct + lc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sm.u.st.ks[lg + 4 * r][col] = accP[ct][r];
-                if (LY::ROT) sm.u.st.ksq[lg + 4 * r][col] = accQ[ct][r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            sm.u.st.ks[lg + 4 * r][col] = accP[r];
+            if (LY::ROT) sm.u.st.ksq[lg + 4 * r][col] = accQ[r];
         }
         __syncthreads();
         if (LY::ROT) {
-            // wave w transforms vectors 4w .. 4w+3 back from the rotated domain and adds
+            // wave w transforms vectors 2w, 2w + 1 back from the rotated domain and adds
             // the unrotated part
 #pragma unroll
-            for (int vv = 0; vv < 4; ++vv) {
-                const int m = 4 * wave + vv;
+            for (int vv = 0; vv < 2; ++vv) {
+                const int m = 2 * wave + vv;
                 double a0 = sm.u.st.ksq[m][lane], a1 = sm.u.st.ksq[m][lane + 64];
                 wave_wht128(a0, a1, lane);
                 sm.u.st.ks[m][lane] += a0;
@@ -408,9 +395,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         // inputs of the next segment (requested before this segment's output stores)
         if (t + L < T) load_segment(P, b, h, t + L, segment_length(t + L, T, P.C, P.chunk), tid, my_lr, nxt);
         __syncthreads();
-        // ---- outputs o (threads 128..255) beside H w (threads 0..127) ------------------
-        if (tid >= NT - DV) {
-            const int j = tid - (NT - DV);
+        // ---- outputs o (threads 128..255) beside H w (waves 4..7) ----------------------
+        if (tid >= DV && tid < 2 * DV) {
+            const int j = tid - DV;
             double wv[SEG];
 #pragma unroll
             for (int tt = 0; tt < SEG; ++tt) wv[tt] = sm.w[tt][j];
@@ -423,11 +410,11 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                     P.o[(((size_t)b * T + t + tt) * H + h) * DV + j] = float(o);
                 }
             }
-        } else if (LY::ROT) {
-            // H w for the rotated rows: four vectors per wave
+        } else if (LY::ROT && wave >= 4) {
+            // H w for the rotated rows: two vectors per wave
 #pragma unroll
-            for (int vv = 0; vv < 4; ++vv) {
-                const int m = 4 * wave + vv;
+            for (int vv = 0; vv < 2; ++vv) {
+                const int m = 2 * (wave - 4) + vv;
                 double a0 = sm.w[m][lane], a1 = sm.w[m][lane + 64];
                 wave_wht128(a0, a1, lane);
                 sm.hw[m][lane] = a0;
@@ -440,91 +427,74 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
             const double* wsrc = LY::rotated(rt) ? &sm.hw[0][0] : &sm.w[0][0];
-            double gv[4];
+            f64x4 c = S[rt];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gv[r] = sm.gl[16 * rt + lg + 4 * r];
+            for (int r = 0; r < 4; ++r) c[r] *= sm.gl[16 * rt + lg + 4 * r];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                f64x4 c = S[rt][ct];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) c[r] *= gv[r];
-                const int col = 32 * wave + 16 * ct + lc;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int tok = 4 * kk + lg;
-                    const double a = sm.u.st.kbarL[tok][16 * rt + lc];
-                    const double bv = wsrc[tok * VS + col];
-                    c = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, c, 0, 0, 0);
-                }
-                S[rt][ct] = c;
+            for (int kk = 0; kk < 2; ++kk) {
+                const int tok = 4 * kk + lg;
+                const double a = sm.u.st.kbarL[tok][16 * rt + lc];
+                const double bv = wsrc[tok * VS + col];
+                c = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, c, 0, 0, 0);
             }
+            S[rt] = c;
         }
 
         // ---- write-back ---------------------------------------------------------------
-        // The state goes through LDS in row-major order, 64 rows at a time: each thread
-        // then rounds one whole 32-value row block (one INT8 block: extrema, float16
-        // metadata and levels without cross-lane steps), and the call's last write-back
-        // stores its codes contiguously.
+        // The state goes through LDS in row-major order, 64 rows at a time: two threads
+        // then round one 32-value row block (an INT8 block: extrema exchanged between
+        // the pair, float16 metadata and levels), and the call's last write-back stores
+        // its codes contiguously.
         if (write_back && KIND != WB_FP32) {
             const bool last = (t + L == T);
             __syncthreads();      // every wave is done with the staging area
 #pragma unroll
             for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int rt = 4 * hv + rq;
+                for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const int col = 32 * wave + 16 * ct + lc;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)] = S[rt][ct][r];
-                    }
-                }
+                    for (int r = 0; r < 4; ++r) sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)] = S[4 * hv + rq][r];
                 __syncthreads();
                 {
-                    const int lrow = tid >> 2, cb = tid & 3;        // row block: columns 32 cb .. +31
+                    // thread: row lrow, block cb (columns 32 cb .. +31), half hf (16 columns)
+                    const int lrow = tid >> 3, cb = (tid >> 1) & 3, hf = tid & 1;
                     const int row = 64 * hv + lrow;
-                    double* rp = &sm.u.wbuf[lrow][33 * cb];
-                    double x[32];
+                    double* rp = &sm.u.wbuf[lrow][33 * cb + 16 * hf];
+                    double x[16];
 #pragma unroll
-                    for (int c = 0; c < 32; ++c) x[c] = rp[c];
+                    for (int c = 0; c < 16; ++c) x[c] = rp[c];
+                    const int col0 = 32 * cb + 16 * hf;
                     if (KIND == WB_UNIFORM) {
                         const double lo = -double(1 << (ub - 1)), hi = double((1 << (ub - 1)) - 1);
                         const double inv = double(1 << (ub - 1));
-                        double kv[32];
+                        uint32_t wd[4] = {0, 0, 0, 0};           // 16 fields of ub <= 8 bits
 #pragma unroll
-                        for (int c = 0; c < 32; ++c) {
-                            kv[c] = fmin(fmax(rint(x[c] * inv), lo), hi);
-                            x[c] = kv[c] * ustep;
+                        for (int c = 0; c < 16; ++c) {
+                            const double kv = fmin(fmax(rint(x[c] * inv), lo), hi);
+                            x[c] = kv * ustep;
+                            const int bit = c * ub;
+                            wd[bit >> 5] |= (uint32_t(int(kv)) & ((1u << ub) - 1)) << (bit & 31);
                         }
                         if (last) {
-                            // codes are packed only where they are stored
-                            uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // 32 fields of ub <= 8 bits
-#pragma unroll
-                            for (int c = 0; c < 32; ++c) {
-                                const int bit = c * ub;
-                                wd[bit >> 5] |= (uint32_t(int(kv[c])) & ((1u << ub) - 1)) << (bit & 31);
-                            }
-                            // element (row, col) at bit ub (row DV + col): this block is 4 ub
-                            // contiguous bytes, 4-byte aligned
-                            uint32_t* dst = reinterpret_cast<uint32_t*>(region + ((row * DV + 32 * cb) * ub) / 8);
-                            for (int i = 0; i < ub; ++i) dst[i] = wd[i];
+                            // element (row, col) at bit ub (row DV + col): these 16 fields are
+                            // 2 ub contiguous bytes, 2-byte aligned
+                            uint16_t* dst = reinterpret_cast<uint16_t*>(region + ((row * DV + col0) * ub) / 8);
+                            for (int i = 0; i < ub; ++i) dst[i] = uint16_t(wd[i >> 1] >> (16 * (i & 1)));
                         }
                     } else if (KIND == WB_MIXED && row < k_hi) {
                         // float16 rows: one correctly rounded conversion per value
-                        uint32_t hw2[16];
+                        uint32_t hw2[8];
 #pragma unroll
-                        for (int c = 0; c < 32; c += 2) {
+                        for (int c = 0; c < 16; c += 2) {
                             const uint16_t h0 = f64_to_f16_bits(x[c]), h1 = f64_to_f16_bits(x[c + 1]);
                             x[c] = f16d(h0);
                             x[c + 1] = f16d(h1);
                             hw2[c >> 1] = uint32_t(h0) | (uint32_t(h1) << 16);
                         }
                         if (last) {
-                            uint4* dst = reinterpret_cast<uint4*>(region + (row * DV + 32 * cb) * 2);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                dst[i] = make_uint4(hw2[4 * i], hw2[4 * i + 1], hw2[4 * i + 2], hw2[4 * i + 3]);
+                            uint4* dst = reinterpret_cast<uint4*>(region + (row * DV + col0) * 2);
+                            dst[0] = make_uint4(hw2[0], hw2[1], hw2[2], hw2[3]);
+                            dst[1] = make_uint4(hw2[4], hw2[5], hw2[6], hw2[7]);
                         }
                     } else {
                         // affine INT8 block of 32 values: scale = f16((max - min) / 255) and
@@ -532,49 +502,45 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                         // (x - zero) / scale rounded to nearest (ties to even), clamped to [0, 255]
                         double mn = x[0], mx = x[0];
 #pragma unroll
-                        for (int c = 1; c < 32; ++c) {
+                        for (int c = 1; c < 16; ++c) {
                             mn = fmin(mn, x[c]);
                             mx = fmax(mx, x[c]);
                         }
+                        mn = fmin(mn, mov_dpp_f64<0xB1>(mn));     // the pair's other half
+                        mx = fmax(mx, mov_dpp_f64<0xB1>(mx));
                         const uint16_t sb = f64_to_f16_bits(fmax(mx - mn, 0.0) / 255.0);
                         const uint16_t zb = f64_to_f16_bits(mn);
                         const double sc = f16d(sb), ze = f16d(zb);
-                        uint32_t cw4[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                        uint32_t cw4[4] = {0, 0, 0, 0};
                         if (sc > 0.0) {
                             const double inv = 1.0 / sc;
 #pragma unroll
-                            for (int c = 0; c < 32; ++c) {
+                            for (int c = 0; c < 16; ++c) {
                                 const double lev = fmin(fmax(rint((x[c] - ze) * inv), 0.0), 255.0);
                                 x[c] = fma(lev, sc, ze);
                                 cw4[c >> 2] |= uint32_t(lev) << (8 * (c & 3));
                             }
                         } else {
 #pragma unroll
-                            for (int c = 0; c < 32; ++c) x[c] = ze;
+                            for (int c = 0; c < 16; ++c) x[c] = ze;
                         }
                         if (last) {
                             const int qrow = row - k_hi;
-                            uint4* dst = reinterpret_cast<uint4*>(region + code_base + (size_t)qrow * DV + 32 * cb);
-                            dst[0] = make_uint4(cw4[0], cw4[1], cw4[2], cw4[3]);
-                            dst[1] = make_uint4(cw4[4], cw4[5], cw4[6], cw4[7]);
-                            *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + cb) * 4) =
-                                uint32_t(sb) | (uint32_t(zb) << 16);
+                            *reinterpret_cast<uint4*>(region + code_base + (size_t)qrow * DV + col0) =
+                                make_uint4(cw4[0], cw4[1], cw4[2], cw4[3]);
+                            if (hf == 0)
+                                *reinterpret_cast<uint32_t*>(region + meta_base + ((size_t)qrow * (DV / 32) + cb) * 4) =
+                                    uint32_t(sb) | (uint32_t(zb) << 16);
                         }
                     }
 #pragma unroll
-                    for (int c = 0; c < 32; ++c) rp[c] = x[c];
+                    for (int c = 0; c < 16; ++c) rp[c] = x[c];
                 }
                 __syncthreads();
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int rt = 4 * hv + rq;
+                for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const int col = 32 * wave + 16 * ct + lc;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) S[rt][ct][r] = sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)];
-                    }
-                }
+                    for (int r = 0; r < 4; ++r) S[4 * hv + rq][r] = sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)];
                 __syncthreads();
             }
         }
@@ -583,21 +549,15 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) S[rt][ct][r] = double(float(S[rt][ct][r]));
+                for (int r = 0; r < 4; ++r) S[rt][r] = double(float(S[rt][r]));
         }
         if (KIND == WB_FP32 && t + L == T) {
             // the stored float32 state
+            float* dst = reinterpret_cast<float*>(region);
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const int col = 32 * wave + 16 * ct + lc;
-                    float* dst = reinterpret_cast<float*>(region);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[(16 * rt + lg + 4 * r) * DV + col] = float(S[rt][ct][r]);
-                }
+                for (int r = 0; r < 4; ++r) dst[(16 * rt + lg + 4 * r) * DV + col] = float(S[rt][r]);
         }
         __syncthreads();
         t += L;

@@ -47,27 +47,24 @@ __device__ __forceinline__ void sr_draws8(uint64_t seed, uint32_t bh, uint64_t t
 }
 
 // ---------------------------------------------------------------------------
-// float16 conversions. float64 -> float16 is rounded once, to nearest with ties to
-// even, by integer arithmetic on the float64 fields (a float64 -> float32 -> float16
-// chain can round twice and land on the wrong side of a float16 midpoint).
+// float16 conversions. float64 -> float16 must round once, to nearest with ties to
+// even: a float64 -> float32 -> float16 chain of two nearest roundings can land on the
+// wrong side of a float16 midpoint. The float32 step is therefore rounded to odd
+// (truncate, then set the last bit if anything was dropped), which keeps enough
+// information for the final nearest rounding to float16 to be the correct rounding of
+// the float64 value (Boldo & Melquiond, "Emulation of FMA and correctly rounded sums:
+// proved algorithms using rounding to odd", IEEE Trans. Computers 57(4), 2008: 24 >=
+// 11 + 2 bits). Overflow goes to infinity, values below half the smallest float16
+// subnormal to zero.
 __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
-    const uint64_t bits = (uint64_t)__double_as_longlong(x);
-    const uint16_t sign = uint16_t((bits >> 48) & 0x8000u);
-    const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
-    if (mag >= 0x7FF0000000000000ull) return sign | (mag > 0x7FF0000000000000ull ? 0x7E00u : 0x7C00u);
-    const int biased = int(mag >> 52);
-    if (biased == 0) return sign;                       // float64 subnormal: far below float16
-    const int e = biased - 1023;
-    if (e >= 16) return sign | 0x7C00u;                 // overflow to infinity
-    const uint64_t m = (mag & 0xFFFFFFFFFFFFFull) | (1ull << 52);
-    const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
-    if (shift >= 64) return sign;
-    uint64_t q = m >> shift;
-    const uint64_t rem = m & ((1ull << shift) - 1);
-    const uint64_t half = 1ull << (shift - 1);
-    if (rem > half || (rem == half && (q & 1))) ++q;
-    const uint32_t h = (e >= -14) ? (uint32_t(e + 14) << 10) + uint32_t(q) : uint32_t(q);
-    return uint16_t(sign | h);
+    const float f = float(x);
+    uint32_t fb = __float_as_uint(f);
+    const double back = double(f);
+    if (back != x) {
+        if (fabs(back) > fabs(x)) fb -= 1u;   // one step toward zero: the truncation
+        fb |= 1u;                             // sticky bit: round to odd
+    }
+    return __half_as_ushort(__float2half_rn(__uint_as_float(fb)));
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
