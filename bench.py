@@ -58,6 +58,11 @@ WORKLOADS = {
     "kda-bitalloc-alloc-each": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=0,
                                     extra=dict(bbar=4, bmin=2, bmax=8), kernel="allocate_kernel", online=True,
                                     alloc_each=True),
+    # allocation at every write-back under the layer budget, rounding stochastically:
+    # three launches per step (costs, widths per sequence, rounding at those widths)
+    "kda-bitalloc-layer-sr-alloc-each": dict(cfg=3, kind="bitalloc", mode="sr", B=256, H=32, per_row=True, layers=8,
+                                             alloc_every=0, extra=dict(bbar=4, bmin=2, bmax=8, budget="layer"),
+                                             kernel="allocate_kernel", online=True, alloc_each=True),
     "kda-bitalloc-layer": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=8, alloc_every=64,
                                extra=dict(bbar=4, bmin=2, bmax=8, budget="layer"), kernel="bitalloc_step_kernel"),
     "kda-bitalloc-1bit": dict(cfg=3, kind="bitalloc", B=256, H=32, per_row=True, layers=15, alloc_every=64,
@@ -193,7 +198,8 @@ def run_gpu(args, w):
         r = i % R
         st = states[layer]
         if w.get("alloc_each"):
-            st.step_decode_alloc(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r])
+            st.step_decode_alloc(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r],
+                                 counts[layer])
         else:
             st.step_decode(inp["q"][r], inp["k"][r], inp["v"][r], inp["beta"][r], s_ring[r], o_ring[r],
                            counts[layer])

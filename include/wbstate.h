@@ -206,16 +206,21 @@ int state_prefill_chunk(wb_state* st, const uint16_t* q_bf16, const uint16_t* k_
  * write-backs neither count nor update it. */
 int state_set_activity(wb_state* st, uint32_t* dev_counters, uint8_t* dev_votes);
 
-/* BITALLOC, RTN only: one decode token (inputs as state_step_decode) whose write-back
- * first allocates ([LBRS] "State bit allocation": widths are set at each write-back;
- * "Levels and storage"): the step runs from the stored state, the token is folded
- * into the attached estimators (if any), then widths, clipping fits and Delta_i are
- * chosen as in state_allocate_bits but for the updated state S_t itself, and S_t is
- * rounded once (nearest) onto the new grid. The allocation takes s_i and r_i from the
- * estimators when attached, else this token's decays and r_i = 1/(3 dk). o as in
- * state_step_decode. EUNSUPPORTED for other layouts or rules. */
+/* BITALLOC, RTN or SR: one decode token (inputs as state_step_decode) whose write-back
+ * first allocates ([LBRS] "State bit allocation": widths are set at each write-back,
+ * at the state's budget, per head or layer-wise; "Levels and storage"): the step runs
+ * from the stored state, the token is folded into the attached estimators (if any),
+ * then widths, clipping fits and Delta_i are chosen as in state_allocate_bits but for
+ * the updated state S_t itself, and S_t is rounded once onto the new grid: to nearest
+ * (RTN) or stochastically with the Philox draws of token t (SR, as state_step_decode).
+ * Layer-wise budget: the widths of a sequence's rows come from all its H heads, so the
+ * call runs three launches on `stream` (costs of every head's updated state, the
+ * widths per sequence, then the step once more with the fits and the rounding); the
+ * workspace is the state's own. The allocation takes s_i and r_i from the estimators
+ * when attached, else this token's decays and r_i = 1/(3 dk). o as in
+ * state_step_decode. EUNSUPPORTED for other layouts and for EF. */
 int state_step_decode_alloc(wb_state* st, const float* q, const float* k, const float* v, const float* beta,
-                            const float* s, float* o, int factor, int C, void* stream);
+                            const float* s, float* o, uint64_t t, int factor, int C, void* stream);
 
 /* BITALLOC only: online estimators of the decay and erasure terms ([LBRS] "State bit
  * allocation"). `dev_est` (float32 [B*H][2 dk + 4], 16-byte aligned, caller-owned,

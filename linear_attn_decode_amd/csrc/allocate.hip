@@ -152,17 +152,26 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 // (u = k^T D S, w = beta (v - u), S' = D S + k w^T, o = S'^T q) runs in float32, the
 // token is folded into the estimators, and the widths, fits and codes are chosen
 // for S' (every row through the 16-candidate fit: S' is not on the old grid).
-enum { kHead = 0, kStep = 1, kCost = 2, kPack = 3 };
+enum { kHead = 0, kStep = 1, kCost = 2, kPack = 3, kStepCost = 4, kStepPack = 5 };
 
 // MODE kHead: the allocation pass on the stored state (per-head budget). kStep: one
 // decode token whose write-back allocates (see below). Layer-wise budget: kCost writes
 // each row's cost c_i (0 for a head whose rows are all zero) to the workspace and
 // stops; kPack takes the widths the per-sequence pass left in the workspace, then
-// fits and repacks as kHead does.
+// fits and repacks as kHead does. kStepCost / kStepPack are the same two halves for a
+// decode token whose write-back allocates under the layer budget: both run the token's
+// step from the stored state (the same operations, so the same updated state), the
+// first writes the outputs, folds the token into the estimators and leaves the costs
+// of the updated state, the second fits and rounds it at the widths of the layer.
 // OB: rows may be one bit wide (bmin = 1); without it that path is not compiled.
-template <int MODE, bool OB>
+// SR: the allocating write-back rounds stochastically (Philox draws of the element:
+// row, column group of 8, head, token), as the decode write-back does.
+template <int MODE, bool OB, bool SR>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) allocate_kernel(const AllocArgs A) {
-    constexpr bool STEP = MODE == kStep;
+    constexpr bool STEP = MODE == kStep || MODE == kStepCost || MODE == kStepPack;
+    constexpr bool COST = MODE == kCost || MODE == kStepCost;
+    constexpr bool PACK = MODE == kPack || MODE == kStepPack;
+    static_assert(STEP || !SR, "stochastic rounding is a rule of the decode write-back");
     __shared__ AllocSmem sm;
     // decode-step scratch, in the candidate table (filled only after the step)
     float* const fk = reinterpret_cast<float*>(&sm.cand[0][0]);
@@ -186,7 +195,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             fk[tid] = A.k[rb];
             fq[tid] = A.q[rb];
             fa[tid] = expf(-sv);
-            if (A.est) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, tid, sv, A.beta[head], fk[tid]);
+            if (MODE != kStepPack && A.est)
+                ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, tid, sv, A.beta[head], fk[tid]);
         }
     }
     __syncthreads();
@@ -306,7 +316,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             for (int c = 0; c < 8; ++c) red[wave * DV + 8 * cg + c] = p[c];
         }
         __syncthreads();
-        if (tid < DV)
+        if (MODE != kStepPack && tid < DV)
             A.o[(size_t)head * DV + tid] = (red[tid] + red[DV + tid]) + (red[2 * DV + tid] + red[3 * DV + tid]);
     }
     if constexpr (STEP) {
@@ -333,7 +343,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         const double sq = wave_sum_f64<1>(R0 * R0 + R1 * R1);
         int b0 = A.bbar, b1 = A.bbar;
         double c0 = 0.0, c1 = 0.0;
-        if (MODE != kPack && sq > 0.0) {
+        if (!PACK && sq > 0.0) {
             const double rms = sqrt(sq / double(DK));
             const size_t base = (size_t)head * DK;
             double s0, s1, q0, q1;
@@ -362,7 +372,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             const double rt0 = R0 / rms, rt1 = R1 / rms;
             c0 = fmin(fmax(g0 * (rt0 * rt0), 1e-300), 1e300);
             c1 = fmin(fmax(g1 * (rt1 * rt1), 1e-300), 1e300);
-            if constexpr (MODE == kCost) {
+            if constexpr (COST) {
                 A.ws_c[base + r0] = c0;
                 A.ws_c[base + r1] = c1;
             } else {
@@ -465,11 +475,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
                 b1 += grow ? a1 : -a1;
             }
             }
-        } else if constexpr (MODE == kCost) {
+        } else if constexpr (COST) {
             A.ws_c[(size_t)head * DK + r0] = 0.0;        // a head whose rows are all zero
             A.ws_c[(size_t)head * DK + r1] = 0.0;
         }
-        if constexpr (MODE == kPack) {
+        if constexpr (PACK) {
             b0 = A.ws_w[(size_t)head * DK + r0];
             b1 = A.ws_w[(size_t)head * DK + r1];
         }
@@ -485,7 +495,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         sm.newoff[r0] = incl - local;
         sm.newoff[r1] = incl - local + b0 * (DV / 8);
     }
-    if constexpr (MODE == kCost) return;
+    if constexpr (COST) return;
     __syncthreads();
 
     // candidate steps: thread t fills fit index t % 16 of rows t / 16 + 16 m
@@ -513,6 +523,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         int best = 15;
         uint16_t dbits = 0;
         uint64_t fld = 0;
+        uint32_t r16[8];
+        if constexpr (SR) sr_draws8(A.seed, uint32_t(head), A.t, row, cg, r16);
         if (OB && bw == 1) {
             // one-bit row ([LBRS] "Levels and storage"): Delta = f16(mean |x|), the sign
             // (nearest of -Delta, +Delta: an exact zero is the tie and takes -Delta); the
@@ -526,8 +538,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
             sa += dpp_f64<0x140>(sa);
             dbits = f64_to_f16_bits(sa / double(DV));
             if (dbits) {
+                if constexpr (SR) {
+                    // the levels -Delta + k 2 Delta, k = floor(tau) + [u < frac(tau)],
+                    // tau = (x + Delta) / (2 Delta), clamped to [0, 1]
+                    const float d = f16_bits_to_f32(dbits);
+                    const float h = 0.5f / d;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) fld |= uint64_t(x[m][c] > 0.f) << c;
+                    for (int c = 0; c < 8; ++c) {
+                        const float tau = __builtin_fmaf(x[m][c], h, 0.5f);
+                        const float fl = floorf(tau);
+                        const float k = fminf(fmaxf(fl + ((float(r16[c]) < (tau - fl) * 65536.f) ? 1.f : 0.f), 0.f), 1.f);
+                        fld |= uint64_t(k > 0.f) << c;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) fld |= uint64_t(x[m][c] > 0.f) << c;
+                }
             }
         } else {
         if (!STEP && bwo <= 5) {
@@ -559,6 +585,18 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         }
         const float2 dk = sm.cand[row][best];
         dbits = f32_to_f16_bits(dk.x);
+        if constexpr (SR) {
+            // floor(tau) + [u < frac(tau)] with tau = x / Delta and u the element's 16-bit
+            // draw over 2^16, clamped to [-n, n]; a zero step stores level 0
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float tau = x[m][c] * dk.y;
+                const float fl = floorf(tau);
+                const float k = fminf(fmaxf(fl + ((float(r16[c]) < (tau - fl) * 65536.f) ? 1.f : 0.f), -float(n)),
+                                      float(n));
+                fld |= uint64_t(uint32_t(int(k) + n)) << (c * bw);
+            }
+        } else
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             // nearest level, ties to even, of the exact quotient x / Delta: x / Delta +
@@ -891,15 +929,37 @@ __global__ void __launch_bounds__(NT) headalloc_pack_kernel(const AllocArgs A) {
 }  // namespace
 
 hipError_t launch_allocate_bits(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kHead, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((allocate_kernel<kHead, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kHead, true, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<kHead, false, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int MODE, bool SR>
+void launch_alloc_ob(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<MODE, true, SR>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<MODE, false, SR>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+}
+
+template <bool SR>
+hipError_t step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
+    if (d.budget != WB_BUDGET_LAYER) {
+        launch_alloc_ob<kStep, SR>(d, a, stream);
+        return hipGetLastError();
+    }
+    // layer budget: step and costs, the widths of each sequence, then the step again
+    // with the fit and the rounding at those widths
+    launch_alloc_ob<kStepCost, SR>(d, a, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(layer_widths_kernel, dim3(d.B), dim3(LNT), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_alloc_ob<kStepPack, SR>(d, a, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_step_allocate(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kStep, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((allocate_kernel<kStep, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
-    return hipGetLastError();
+    return d.mode == WB_SR ? step_allocate<true>(d, a, stream) : step_allocate<false>(d, a, stream);
 }
 
 hipError_t launch_allocate_heads(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
@@ -914,15 +974,15 @@ hipError_t launch_allocate_heads(const wb_layout_desc& d, const AllocArgs& a, hi
 }
 
 hipError_t launch_allocate_layer(const wb_layout_desc& d, const AllocArgs& a, hipStream_t stream) {
-    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kCost, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((allocate_kernel<kCost, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kCost, true, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<kCost, false, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(layer_widths_kernel, dim3(d.B), dim3(LNT), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kPack, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((allocate_kernel<kPack, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    if (d.bmin == 1) hipLaunchKernelGGL((allocate_kernel<kPack, true, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((allocate_kernel<kPack, false, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -83,6 +83,8 @@ struct AllocArgs {
     // decode step whose write-back allocates (launch_step_allocate): the token's inputs
     const float *q = nullptr, *k = nullptr, *v = nullptr, *beta = nullptr, *sd = nullptr;
     float* o = nullptr;
+    uint64_t t = 0;                   // the token index (stochastic rounding draws)
+    uint64_t seed = 0;
     int s_per_row = 1;
     uint64_t region_stride = 0;
     float r_default = 0.f;

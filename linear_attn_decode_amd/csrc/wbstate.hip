@@ -326,10 +326,9 @@ int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor
 }
 
 int state_step_decode_alloc(wb_state* st, const float* q, const float* k, const float* v, const float* beta,
-                            const float* s, float* o, int factor, int C, void* stream) {
+                            const float* s, float* o, uint64_t t, int factor, int C, void* stream) {
     if (!st || !q || !k || !v || !beta || !s || !o) return WB_EINVAL;
-    if (st->d.kind != WB_BITALLOC || st->d.mode != WB_RTN || st->d.budget != WB_BUDGET_HEAD)
-        return WB_EUNSUPPORTED;
+    if (st->d.kind != WB_BITALLOC || st->d.mode == WB_EF) return WB_EUNSUPPORTED;
     if (factor < WB_GAMMA_ERASURE || factor > WB_GAMMA_HC || C < 1) return WB_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(beta) || !aligned4(s))
         return WB_EALIGN;
@@ -351,6 +350,14 @@ int state_step_decode_alloc(wb_state* st, const float* q, const float* k, const 
     a.o = o;
     a.s_per_row = st->d.decay == WB_DECAY_PER_ROW;
     a.code_cap = int(code_capacity(st->d));
+    a.t = t;
+    a.seed = st->d.seed;
+    if (st->d.budget == WB_BUDGET_LAYER) {
+        a.H = st->d.H;
+        a.rows_per_seq = st->d.H * st->d.dk;
+        a.ws_c = reinterpret_cast<double*>(st->state + st->regions_bytes);
+        a.ws_w = st->state + st->regions_bytes + size_t(st->d.B) * st->d.H * st->d.dk * 8;
+    }
     return hip_status(wb::launch_step_allocate(st->d, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -260,17 +260,38 @@ def allocate_headalloc_regions(lay: L.Layout, regions, s_rows, r_rows, factor="e
     return out, al
 
 
-def decode_step_alloc(lay: L.Layout, region, q, k, v, beta, s, s_rows, r_rows, factor="erasure", C=1):
+def decode_step_alloc(lay: L.Layout, region, q, k, v, beta, s, s_rows, r_rows, factor="erasure", C=1,
+                      t: int = 0, b: int = 0, h: int = 0):
     """One decode token for a BITALLOC head whose write-back allocates ([LBRS] "State
     bit allocation": widths are chosen at each write-back): the step from the stored
     state, then widths, fits and Delta chosen for the updated state itself and the
-    state rounded once (nearest) onto that grid. ``s_rows`` / ``r_rows`` feed the
-    allocation (None: no decay estimate). Returns (region, alloc, o, S_new)."""
+    state rounded once onto that grid, by the layout's rule (RTN; SR with the draws of
+    token t of head (b, h)). ``s_rows`` / ``r_rows`` feed the allocation (None: no
+    decay estimate). Returns (region, alloc, o, S_new)."""
     content = L.decode_region(lay, region)
     Y = L.stored_values(lay, content)
     S_new, o = delta_step(Y, q, k, v, beta, s)
-    reg, alloc = _allocate_and_round(lay, S_new, s_rows, r_rows, factor, C)
-    return reg, alloc, o, S_new
+    alloc = allocate_head(S_new, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C)
+    return _round_at(lay, S_new, alloc, lay.mode, t, b, h), alloc, o, S_new
+
+
+def decode_step_alloc_layer(lay: L.Layout, regions, q, k, v, beta, s, s_rows, r_rows, factor="erasure", C=1,
+                            t: int = 0, b: int = 0):
+    """One decode token for the H heads of one sequence under the layer-wise budget
+    ([LBRS] "State bit allocation": widths at each write-back, "at layer-wise mean
+    budget bbar"): each head's step from its stored state, then the widths over every
+    row of the H updated states (``allocate_layer``), and each head rounded once at its
+    widths by the layout's rule. Per-head inputs are indexed [h]; ``s_rows`` /
+    ``r_rows`` [H][dk] or None. Returns (regions, allocs, outputs, updated states)."""
+    Ss, outs = [], []
+    for h, reg in enumerate(regions):
+        Y = L.stored_values(lay, L.decode_region(lay, reg))
+        S_new, o = delta_step(Y, q[h], k[h], v[h], beta[h], s[h])
+        Ss.append(S_new)
+        outs.append(o)
+    allocs = allocate_layer(Ss, s_rows, r_rows, lay.bbar, lay.bmin, lay.bmax, factor, C)
+    regs = [_round_at(lay, Ss[h], allocs[h], lay.mode, t, b, h) for h in range(len(regions))]
+    return regs, allocs, outs, Ss
 
 
 def _allocate_and_round(lay: L.Layout, Y, s_rows, r_rows, factor, C):
@@ -278,18 +299,22 @@ def _allocate_and_round(lay: L.Layout, Y, s_rows, r_rows, factor, C):
     return _round_at(lay, Y, alloc), alloc
 
 
-def _round_at(lay: L.Layout, Y, alloc):
+def _round_at(lay: L.Layout, Y, alloc, mode: str = "rtn", t: int = 0, b: int = 0, h: int = 0):
+    """Round Y at the allocation's widths and fits by ``mode`` (SR: the draws of token
+    t, head (b, h)). The allocation pass alone re-rounds to nearest; a decode write-back
+    that allocates uses the layout's rule."""
     widths, fits = alloc["widths"], alloc["fit"]
     delta = np.zeros(lay.dk)
     kappa = np.zeros((lay.dk, lay.dv), np.int64)
     for i in range(lay.dk):
+        r16 = _draws(lay, b, h, t, [i])[0] if mode == "sr" else None
         if widths[i] == 1:
             delta[i], _ = one_bit_step(Y[i])
-            kappa[i] = one_bit_round(Y[i], delta[i], "rtn").kappa
+            kappa[i] = one_bit_round(Y[i], delta[i], mode, r16=r16).kappa
             continue
         delta[i], _ = row_step(alloc["R"][i], int(widths[i]), int(fits[i]))
         n = levels_n(int(widths[i]))
-        rr = sym_round(Y[i], delta[i], n, "rtn")
+        rr = sym_round(Y[i], delta[i], n, mode, r16=r16)
         kappa[i] = rr.kappa
     c = L.Content(kappa=kappa, widths=widths, fit=fits, delta_bits=f16_bits(delta))
     return L.encode_region(lay, c)

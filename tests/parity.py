@@ -226,24 +226,28 @@ def compare_write_back(lay: L.Layout, reg_in, reg_gpu, wb, e_in, e_gpu, t, b, h,
 
 
 def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: Tally, where,
-                             window=WINDOW, meta_rel=META_REL):
+                             window=WINDOW, meta_rel=META_REL, draws=None, layer=False):
     """Compare a write-back that allocated (BITALLOC) with the oracle's on the same
     updated state X. Widths: equal, or an allocation of the same budget whose proxy
     cost under the oracle's costs is within 1e-6 of the oracle's (the float32 state
-    moves near-tied costs). Rows of equal width: fit indices equal or of equal squared
-    error within 1e-6; rows of equal width and fit: Delta equal or the adjacent float16
-    where the pre-rounding value is within ``meta_rel`` of the midpoint; rows of equal
-    width, fit and Delta: codes equal or one apart within ``window`` steps of a
-    rounding boundary. Returns the number of rows left out of the code comparison."""
+    moves near-tied costs; ``layer``: the budget and the cost are the sequence's, which
+    the caller checks with ``compare_layer_widths``). Rows of equal width: fit indices
+    equal or of equal squared error within 1e-6; rows of equal width and fit: Delta
+    equal or the adjacent float16 where the pre-rounding value is within ``meta_rel``
+    of the midpoint; rows of equal width, fit and Delta: codes equal or one apart within
+    ``window`` steps of a rounding boundary (``draws``: row -> 16-bit draws, for
+    stochastic rounding, whose boundary is the draw). Returns the number of rows left
+    out of the code comparison."""
     from oracle.quantizers import fit_fraction, levels_n, one_bit_round, sym_round
     g = L.decode_region(lay, np.asarray(reg_gpu, np.uint8)[: lay.region_size()])
     o = L.decode_region(lay, np.asarray(reg_orc, np.uint8)[: lay.region_size()])
-    if g.widths.sum() != lay.bbar * lay.dk or g.widths.min() < lay.bmin or g.widths.max() > lay.bmax:
+    if ((not layer and g.widths.sum() != lay.bbar * lay.dk) or g.widths.min() < lay.bmin or
+            g.widths.max() > lay.bmax):
         tally.bad.append((where, "width budget", int(g.widths.sum())))
         return lay.dk
     c = alloc["c"]
     same_w = g.widths == o.widths
-    if not same_w.all():
+    if not same_w.all() and not layer:
         cg = float(np.sum(c * 2.0 ** (-2.0 * g.widths)))
         co = float(np.sum(c * 2.0 ** (-2.0 * o.widths)))
         if cg > co * (1 + 1e-6) or (~same_w).sum() > 8:
@@ -263,8 +267,9 @@ def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: T
             skipped += 1
             continue
         n = levels_n(int(g.widths[i]))
-        rr = (one_bit_round(X[i], float(g.delta[i]), "rtn") if g.widths[i] == 1 else
-              sym_round(X[i], float(g.delta[i]), n, "rtn"))
+        mode, r16 = ("rtn", None) if draws is None else ("sr", draws(i))
+        rr = (one_bit_round(X[i], float(g.delta[i]), mode, r16=r16) if g.widths[i] == 1 else
+              sym_round(X[i], float(g.delta[i]), n, mode, r16=r16))
         tally.elems += lay.dv
         diff = g.kappa[i] != rr.kappa
         if diff.any():
@@ -274,6 +279,24 @@ def compare_alloc_write_back(lay: L.Layout, reg_gpu, reg_orc, alloc, X, tally: T
                 j = np.argwhere(~ok).ravel()[:3]
                 tally.bad.append((where, "codes", int(i), j.tolist(), g.kappa[i][j].tolist(), rr.kappa[j].tolist()))
     return skipped
+
+
+def compare_layer_widths(lay: L.Layout, regs_gpu, allocs, tally: Tally, where):
+    """The widths of one sequence's heads after a layer-budget allocation: the sum over
+    the H heads is bbar H dk, and where they differ from the oracle's the allocation's
+    proxy cost under the oracle's costs is within 1e-6 of the oracle's, on at most 8
+    rows (the float32 state moves near-tied costs)."""
+    gw = np.concatenate([L.decode_region(lay, np.asarray(r, np.uint8)[: lay.region_size()]).widths for r in regs_gpu])
+    ow = np.concatenate([a["widths"] for a in allocs])
+    c = np.concatenate([a["c"] for a in allocs])
+    if gw.sum() != lay.bbar * lay.dk * len(allocs):
+        tally.bad.append((where, "layer width budget", int(gw.sum())))
+        return
+    if not np.array_equal(gw, ow):
+        cg = float(np.sum(c * 2.0 ** (-2.0 * gw)))
+        co = float(np.sum(c * 2.0 ** (-2.0 * ow)))
+        if cg > co * (1 + 1e-6) or int(np.sum(gw != ow)) > 8:
+            tally.bad.append((where, "layer widths", np.argwhere(gw != ow).ravel()[:6].tolist(), cg, co))
 
 
 def check_heads_chunk(args):

@@ -672,7 +672,7 @@ def test_decode_step_with_allocation(case):
         torch.cuda.synchronize()
         regs_in = st.regions().cpu().numpy()
         e_in = est.cpu().numpy().astype(np.float64) if use_est else None
-        st.step_decode_alloc(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, factor, C)
+        st.step_decode_alloc(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, t, factor, C)
         torch.cuda.synchronize()
         regs = st.regions().cpu().numpy()
         o_np = o.cpu().numpy()
@@ -695,6 +695,87 @@ def test_decode_step_with_allocation(case):
                     s_bh, sa, ra, factor, C)
                 skipped += compare_alloc_write_back(lay, regs[b * H + h], reg_orc, alloc, X, tally, (t, b, h))
                 err = np.linalg.norm(o_np[b, h] - o_orc) / max(np.linalg.norm(o_orc), 1e-30)
+                tally.o_worst = max(tally.o_worst, float(err))
+    print("[tally]", tally.summary(), "rows left out of the code comparison:", skipped, flush=True)
+    assert tally.ok(), tally.summary()
+    assert skipped <= 0.01 * T * B * H * dk
+
+
+@pytest.mark.parametrize("case", ["layer-rtn", "layer-sr", "head-sr", "layer-sr-one-bit", "layer-rtn-decays-hC"])
+def test_decode_step_with_allocation_layer_budget_and_sr(case):
+    """Allocating decode tokens at the layer-wise budget and/or with stochastic rounding
+    (teacher-forced from the GPU's stored regions and estimators) against the oracle:
+    each head's plain step, the widths over the sequence's H updated states (layer) or
+    the head's own (head), and one rounding by the layout's rule with the draws of the
+    token. Readout within 1e-4 relative; widths per sequence within the proxy-cost
+    tolerance; codes to the decode bound."""
+    from oracle.estimators import EmaState, ema_estimates, ema_fold
+    from oracle.step import decode_step_alloc, decode_step_alloc_layer
+    from oracle.philox import sr_draws
+    from tests.parity import Tally, compare_alloc_write_back, compare_layer_widths
+    print(f"\n[case] decode step with allocation {case}", flush=True)
+    B, H, dk, T = 2, 4, 128, 4
+    layer = case.startswith("layer")
+    mode = "sr" if "-sr" in case else "rtn"
+    use_est = "decays" not in case
+    factor, C = ("hC", 64) if "hC" in case else ("erasure", 1)
+    kw = dict(bbar=3, bmin=1) if "one-bit" in case else {}
+    lay = _layout(L.BITALLOC, mode, B, H, dk, budget="layer" if layer else "head", **kw)
+    rng = np.random.default_rng(67)
+    st = _state(lay)
+    inp = decode_inputs(67, B, H, dk, dk, T + 2, True)
+    dev = {key: _to_dev(val) for key, val in inp.items()}
+    S0 = _warm_state(rng, B, H, dk, dk) * np.exp(rng.uniform(-1.5, 1.5, (B, H, 1, 1))).astype(np.float32)
+    st.quantize(_to_dev(S0))
+    o = torch.zeros((B, H, dk), dtype=torch.float32, device="cuda")
+    est = None
+    if use_est:
+        est = torch.zeros((B, H, 2 * dk + 4), dtype=torch.float32, device="cuda")
+        st.set_estimators(est)
+        for t in range(2):
+            st.step_decode(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, t)
+    tally = Tally()
+    skipped = 0
+    for t in range(2, T + 2):
+        torch.cuda.synchronize()
+        regs_in = st.regions().cpu().numpy()
+        e_in = est.cpu().numpy().astype(np.float64) if use_est else None
+        st.step_decode_alloc(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], dev["s"], o, t, factor, C)
+        torch.cuda.synchronize()
+        regs = st.regions().cpu().numpy()
+        o_np = o.cpu().numpy()
+        for b in range(B):
+            sa_h, ra_h = [], []
+            for h in range(H):
+                s_rows = inp["s"][b, h].astype(np.float64)
+                if use_est:
+                    es = EmaState(Na=e_in[b, h, :dk], Nr=e_in[b, h, dk:2 * dk], W=float(e_in[b, h, 2 * dk]))
+                    es = ema_fold(es, s_rows, float(inp["beta"][t, b, h]), inp["k"][t, b, h].astype(np.float64))
+                    sa, ra = ema_estimates(es.Na, es.Nr, es.W)
+                else:
+                    sa, ra = s_rows, np.full(dk, 1.0 / (3 * dk))
+                sa_h.append(sa)
+                ra_h.append(ra)
+            args = [[inp[n][t, b, h] for h in range(H)] for n in ("q", "k", "v")]
+            betas = [float(inp["beta"][t, b, h]) for h in range(H)]
+            ss = [inp["s"][b, h].astype(np.float64) for h in range(H)]
+            rin = [regs_in[b * H + h] for h in range(H)]
+            if layer:
+                regs_o, allocs, outs, Xs = decode_step_alloc_layer(lay, rin, *args, betas, ss, sa_h, ra_h, factor,
+                                                                   C, t, b)
+                compare_layer_widths(lay, [regs[b * H + h] for h in range(H)], allocs, tally, (t, b))
+            else:
+                res = [decode_step_alloc(lay, rin[h], args[0][h], args[1][h], args[2][h], betas[h], ss[h],
+                                         sa_h[h], ra_h[h], factor, C, t, b, h) for h in range(H)]
+                regs_o, allocs, outs, Xs = (list(x) for x in zip(*res))
+            for h in range(H):
+                draws = None
+                if mode == "sr":
+                    draws = (lambda bb, hh: (lambda i: np.asarray(sr_draws(lay.seed, bb, hh, H, t, int(i), dk),
+                                                                  np.float64)))(b, h)
+                skipped += compare_alloc_write_back(lay, regs[b * H + h], regs_o[h], allocs[h], Xs[h], tally,
+                                                    (t, b, h), draws=draws, layer=layer)
+                err = np.linalg.norm(o_np[b, h] - outs[h]) / max(np.linalg.norm(outs[h]), 1e-30)
                 tally.o_worst = max(tally.o_worst, float(err))
     print("[tally]", tally.summary(), "rows left out of the code comparison:", skipped, flush=True)
     assert tally.ok(), tally.summary()

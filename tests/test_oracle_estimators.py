@@ -153,6 +153,100 @@ def test_step_with_allocation_reduces_to_its_parts():
         assert np.array_equal(c.kappa[i], sym_round(S_new[i], float(c.delta[i]), n, "rtn").kappa)
 
 
+def _alloc_case(rng, dk, dv, H, **kw):
+    from oracle import layouts as L
+    from oracle.step import allocate_layer_regions, import_state
+    args = dict(kind=L.BITALLOC, B=1, H=H, dk=dk, dv=dv, per_row_decay=True, bbar=4, bmin=2, bmax=8,
+                budget="layer")
+    lay = L.Layout(**{**args, **kw})
+    start = L.encode_region(lay, L.Content(kappa=np.zeros((dk, dv), np.int64), widths=np.full(dk, 4),
+                                           fit=np.zeros(dk, np.int64), delta_bits=np.zeros(dk, np.uint16)))
+    regs = [import_state(lay, rng.standard_normal((dk, dv)) * np.exp(rng.uniform(-3, 0.5, (dk, 1))) * 3.0 ** h,
+                         start) for h in range(H)]
+    s_rows = [np.exp(rng.uniform(np.log(1e-3), 0.0, dk)) for _ in range(H)]
+    regs, _ = allocate_layer_regions(lay, regs, s_rows, [0.01] * H)
+    unit = lambda x: x / np.linalg.norm(x)
+    tok = dict(q=[unit(rng.standard_normal(dk)) for _ in range(H)], k=[unit(rng.standard_normal(dk)) for _ in range(H)],
+               v=[rng.standard_normal(dv) for _ in range(H)], beta=[0.6] * H,
+               s=[np.exp(rng.uniform(np.log(1e-3), 0.0, dk)) for _ in range(H)])
+    return lay, regs, s_rows, tok
+
+
+def test_layer_step_with_allocation_reduces_to_its_parts():
+    """The allocating token under the layer-wise budget: each head's readout and updated
+    state are the plain step's; the widths of the H updated states are the layer
+    allocation of those states (sum = bbar H dk) and every head is rounded to nearest
+    on its new grid; with one head it is the per-head allocating token, byte for byte."""
+    from oracle import layouts as L
+    from oracle.allocation import allocate_layer
+    from oracle.quantizers import levels_n, one_bit_round, sym_round
+    from oracle.step import decode_step, decode_step_alloc, decode_step_alloc_layer
+    rng = np.random.default_rng(81)
+    dk, dv, H = 32, 8, 3
+    lay, regs, s_rows, tok = _alloc_case(rng, dk, dv, H, bmin=1)
+    new, allocs, outs, Ss = decode_step_alloc_layer(lay, regs, tok["q"], tok["k"], tok["v"], tok["beta"], tok["s"],
+                                                    s_rows, [0.01] * H)
+    ref_w = allocate_layer(Ss, s_rows, [0.01] * H, 4, 1, 8)
+    total = 0
+    for h in range(H):
+        ref = decode_step(lay, regs[h], None, tok["q"][h], tok["k"][h], tok["v"][h], 0.6, tok["s"][h], 0, 0, h)
+        assert np.array_equal(Ss[h], ref.S_new) and np.allclose(outs[h], ref.o, rtol=1e-13, atol=1e-15)
+        c = L.decode_region(lay, new[h])
+        assert np.array_equal(c.widths, ref_w[h]["widths"]) and np.array_equal(c.fit, ref_w[h]["fit"])
+        total += int(c.widths.sum())
+        for i in range(dk):
+            if c.widths[i] == 1:
+                want = one_bit_round(Ss[h][i], float(c.delta[i]), "rtn").kappa
+            else:
+                want = sym_round(Ss[h][i], float(c.delta[i]), levels_n(int(c.widths[i])), "rtn").kappa
+            assert np.array_equal(c.kappa[i], want)
+    assert total == 4 * H * dk
+    one, *_ = decode_step_alloc_layer(lay, regs[:1], tok["q"][:1], tok["k"][:1], tok["v"][:1], [0.6], tok["s"][:1],
+                                      s_rows[:1], [0.01])
+    head, *_ = decode_step_alloc(lay, regs[0], tok["q"][0], tok["k"][0], tok["v"][0], 0.6, tok["s"][0],
+                                 s_rows[0], 0.01)
+    assert np.array_equal(one[0], head)
+
+
+def test_allocating_write_back_stochastic_rounding():
+    """SR on the allocated grid: each level is the floor or the ceiling of x / Delta
+    (clipped; one-bit rows: of (x + Delta) / (2 Delta)), the draws depend on the token
+    (two tokens give different codes) and, away from the rails, the levels average to
+    the value over many tokens (E[xhat] = x) within 5 sigma of the mean of N draws
+    (sigma <= Delta / 2 per draw)."""
+    from oracle import layouts as L
+    from oracle.step import _round_at, decode_step_alloc_layer
+    rng = np.random.default_rng(82)
+    dk, dv, H, N = 32, 8, 2, 256
+    lay, regs, s_rows, tok = _alloc_case(rng, dk, dv, H, bmin=1, mode="sr", seed=0x5EED)
+    new, allocs, outs, Ss = decode_step_alloc_layer(lay, regs, tok["q"], tok["k"], tok["v"], tok["beta"], tok["s"],
+                                                    s_rows, [0.01] * H, t=7, b=0)
+    for h in range(H):
+        c = L.decode_region(lay, new[h])
+        assert np.any(c.widths == 1)
+        d = c.delta.astype(np.float64)[:, None]
+        one = (c.widths == 1)[:, None]
+        n = np.where(c.widths == 1, 1, (1 << (c.widths - 1)) - 1)[:, None].astype(np.float64)
+        tau = np.where(one, (Ss[h] + d) / (2 * d), Ss[h] / np.where(d == 0, 1, d))
+        lev = np.where(one, (c.kappa + 1) // 2, c.kappa)
+        lo = np.where(one, 0, np.maximum(np.floor(tau), -n))
+        hi = np.where(one, 1, np.minimum(np.ceil(tau), n))
+        lo = np.where(one, np.clip(np.floor(tau), 0, 1), lo)
+        hi = np.where(one, np.clip(np.ceil(tau), 0, 1), hi)
+        assert np.all((lev >= lo) & (lev <= hi))
+        acc = np.zeros((dk, dv))
+        for t in range(N):
+            reg = _round_at(lay, Ss[h], allocs[h], "sr", t, 0, h)
+            acc += L.stored_values(lay, L.decode_region(lay, reg))
+            if t == 1:
+                assert not np.array_equal(reg, _round_at(lay, Ss[h], allocs[h], "sr", 0, 0, h))
+        inside = np.where(one, np.abs(Ss[h]) <= d, np.abs(Ss[h]) <= n * d) & (d > 0)
+        err = np.abs(acc / N - Ss[h])
+        bound = 5 * np.broadcast_to(np.where(one, 2 * d, d), err.shape) / (2 * np.sqrt(N))
+        assert inside.sum() > 0.75 * dk * dv
+        assert np.all(err[inside] <= bound[inside])
+
+
 # ---------------------------------------------------------------- layer-wise budget
 
 def _heads(rng, H, dk=16, dv=8):
