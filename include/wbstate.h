@@ -75,6 +75,8 @@ extern "C" {
 #define WB_EUNSUPPORTED (-3)  /* shape / layout / mode combination not built */
 #define WB_ELAUNCH (-4)       /* the HIP runtime refused a launch or copy */
 #define WB_EALIGN (-5)        /* a device pointer is not 16-byte aligned */
+#define WB_ESCRATCH (-6)      /* the work exceeds the library's static scratch (see
+                               * state_allocate_bits_static) */
 
 /* storage layouts */
 #define WB_FP32 0      /* identity write-back, q_t = h_t */
@@ -245,6 +247,20 @@ int state_set_estimators(wb_state* st, float* dev_est);
  * estimators have seen no token (W = 0) gives every row Gamma = 1. EINVAL for a bad
  * factor, C < 1, or s NULL without estimators. */
 int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor, int C, void* stream);
+
+/* For callers that cannot allocate device memory or must not touch the state buffer's
+ * workspace (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): state_allocate_bits with the same arguments and results, whose
+ * workspace (layer-wise budget and HEADALLOC: a float64 cost and a uint8 width per row
+ * of the layer, 9 * B * H * dk bytes, HEADALLOC 9 * B * H) is a static device array of
+ * the library, 16 MiB per GPU (B * H <= 14563 heads at dk = 128 under the layer
+ * budget), held by each GPU the library runs on until the process ends. Nothing is
+ * allocated, by the library or by any routine it calls. WB_ESCRATCH if the workspace
+ * exceeds the array; WB_ELAUNCH if its device address could not be found when the
+ * handle was made. Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (several streams, several threads) race and must be ordered by
+ * the caller. A per-head budget uses no workspace and runs as state_allocate_bits. */
+int state_allocate_bits_static(wb_state* st, const float* s, const float* r, int factor, int C, void* stream);
 
 /* Export: the stored state dequantized to float32 S [B][H][dk][dv] in the original
  * domain and logical row order (Hadamard rows rotated back, rows un-permuted). */

@@ -25,7 +25,7 @@ GAMMA_CODES = {"erasure": 0, "w1": 1, "hC": 2}
 BUDGET_CODES = {"head": 0, "layer": 1}
 DECAY_PER_HEAD, DECAY_PER_ROW = 0, 1
 
-STATUS = {0: "ok", -1: "EINVAL", -2: "ESIZE", -3: "EUNSUPPORTED", -4: "ELAUNCH", -5: "EALIGN"}
+STATUS = {0: "ok", -1: "EINVAL", -2: "ESIZE", -3: "EUNSUPPORTED", -4: "ELAUNCH", -5: "EALIGN", -6: "ESCRATCH"}
 
 
 class LayoutDesc(ctypes.Structure):
@@ -50,6 +50,7 @@ SIGNATURES = {
     "state_step_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _U64, _P]),
     "state_prefill_chunk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _U64, _P]),
     "state_allocate_bits": (_I, [_P, _P, _P, _I, _I, _P]),
+    "state_allocate_bits_static": (_I, [_P, _P, _P, _I, _I, _P]),
     "state_set_estimators": (_I, [_P, _P]),
     "state_step_decode_alloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _U64, _I, _I, _P]),
     "state_dequant": (_I, [_P, _P, _P]),
@@ -195,6 +196,16 @@ class WriteBackState:
             self.handle, None if s is None else _ptr(s, torch.float32, shape, "s"),
             None if r is None else _ptr(r, torch.float32, shape, "r"), GAMMA_CODES[factor], int(C),
             _stream(stream)), "state_allocate_bits")
+
+    def allocate_bits_static(self, s=None, r=None, factor="erasure", C=1, stream=None):
+        """``allocate_bits`` with the workspace in the library's static device scratch
+        (no allocation; calls on one GPU must not overlap)."""
+        import torch
+        shape = (self.B, self.H, self.dk)
+        check(lib().state_allocate_bits_static(
+            self.handle, None if s is None else _ptr(s, torch.float32, shape, "s"),
+            None if r is None else _ptr(r, torch.float32, shape, "r"), GAMMA_CODES[factor], int(C),
+            _stream(stream)), "state_allocate_bits_static")
 
     def set_estimators(self, est=None):
         """Attach (or with None detach) the online estimators: float32 [B, H, 2 dk + 4],

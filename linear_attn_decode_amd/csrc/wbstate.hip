@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "wb_kernels.hpp"
@@ -22,9 +23,36 @@ struct wb_state {
     uint32_t* activity;    // caller's write-activity counters (UNIFORM), or null
     uint8_t* votes;        // caller's per-element vote state, set with `activity`
     float* est;            // caller's online estimators (BITALLOC), or null
+    uint8_t* scratch;      // device address of this GPU's `scratch` array, or null
 };
 
 namespace {
+
+// Scratch of state_allocate_bits_static: the workspace the allocation passes of the
+// layer-wise budget and the per-head unit otherwise keep after the regions (a float64
+// cost and a uint8 width per row of the layer: 9 bytes per row). Each GPU the library
+// runs on holds its own copy until the process ends. Nothing in it has to start at
+// zero: every pass writes each row's cost and width before reading them.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The array's device address on each GPU, looked up once per device with that device
+// current. In host code `scratch` names a host-side stand-in, never the device memory.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+uint8_t* scratch_addr[kMaxDevices] = {};
+
+uint8_t* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_addr[dev] = static_cast<uint8_t*>(p);
+    }
+    return scratch_addr[dev];
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -187,6 +215,9 @@ int state_alloc(const wb_layout_desc* d, void* dev_state, size_t state_bytes_in,
     st->activity = nullptr;
     st->votes = nullptr;
     st->est = nullptr;
+    // the static scratch of this device (null if the lookup failed: then only
+    // state_allocate_bits_static refuses, with WB_ELAUNCH)
+    st->scratch = scratch_for_current_device();
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // zero state: all layouts but BITALLOC encode S_0 = 0 as zero bytes
@@ -289,12 +320,13 @@ int state_set_estimators(wb_state* st, float* dev_est) {
     return WB_OK;
 }
 
-int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor, int C, void* stream) {
-    if (!st) return WB_EINVAL;
-    if (st->d.kind != WB_BITALLOC && st->d.kind != WB_HEADALLOC) return WB_EUNSUPPORTED;
-    if (factor < WB_GAMMA_ERASURE || factor > WB_GAMMA_HC || C < 1) return WB_EINVAL;
-    if (!s && (r || !st->est)) return WB_EINVAL;
-    if ((s && !aligned4(s)) || (r && !aligned4(r))) return WB_EALIGN;
+}  // extern "C"
+
+namespace {
+
+// The allocation pass; `ws` is the workspace of the layer-wise budget and the per-head
+// unit: the state buffer's tail, or the static scratch (state_allocate_bits_static).
+int allocate_bits(wb_state* st, const float* s, const float* r, int factor, int C, void* stream, uint8_t* ws) {
     wb::AllocArgs a;
     a.state = st->state;
     a.s = s;
@@ -311,18 +343,46 @@ int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor
     if (st->d.kind == WB_HEADALLOC) {
         a.H = st->d.H;
         a.rows_per_seq = st->d.H;
-        a.ws_c = reinterpret_cast<double*>(st->state + st->regions_bytes);
-        a.ws_w = st->state + st->regions_bytes + size_t(st->d.B) * st->d.H * 8;
+        a.ws_c = reinterpret_cast<double*>(ws);
+        a.ws_w = ws + size_t(st->d.B) * st->d.H * 8;
         return hip_status(wb::launch_allocate_heads(st->d, a, static_cast<hipStream_t>(stream)));
     }
     if (st->d.budget == WB_BUDGET_LAYER) {
         a.H = st->d.H;
         a.rows_per_seq = st->d.H * st->d.dk;
-        a.ws_c = reinterpret_cast<double*>(st->state + st->regions_bytes);
-        a.ws_w = st->state + st->regions_bytes + size_t(st->d.B) * st->d.H * st->d.dk * 8;
+        a.ws_c = reinterpret_cast<double*>(ws);
+        a.ws_w = ws + size_t(st->d.B) * st->d.H * st->d.dk * 8;
         return hip_status(wb::launch_allocate_layer(st->d, a, static_cast<hipStream_t>(stream)));
     }
     return hip_status(wb::launch_allocate_bits(st->d, a, static_cast<hipStream_t>(stream)));
+}
+
+int allocate_bits_check(const wb_state* st, const float* s, const float* r, int factor, int C) {
+    if (!st) return WB_EINVAL;
+    if (st->d.kind != WB_BITALLOC && st->d.kind != WB_HEADALLOC) return WB_EUNSUPPORTED;
+    if (factor < WB_GAMMA_ERASURE || factor > WB_GAMMA_HC || C < 1) return WB_EINVAL;
+    if (!s && (r || !st->est)) return WB_EINVAL;
+    if ((s && !aligned4(s)) || (r && !aligned4(r))) return WB_EALIGN;
+    return WB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int state_allocate_bits(wb_state* st, const float* s, const float* r, int factor, int C, void* stream) {
+    const int v = allocate_bits_check(st, s, r, factor, C);
+    if (v) return v;
+    return allocate_bits(st, s, r, factor, C, stream, st->state + st->regions_bytes);
+}
+
+int state_allocate_bits_static(wb_state* st, const float* s, const float* r, int factor, int C, void* stream) {
+    const int v = allocate_bits_check(st, s, r, factor, C);
+    if (v) return v;
+    // the same bytes the state's own workspace holds, which must fit the static array
+    if (layer_ws_size(st->d) > kScratchBytes) return WB_ESCRATCH;
+    if (!st->scratch) return WB_ELAUNCH;
+    return allocate_bits(st, s, r, factor, C, stream, st->scratch);
 }
 
 int state_step_decode_alloc(wb_state* st, const float* q, const float* k, const float* v, const float* beta,
@@ -422,6 +482,7 @@ const char* state_status_str(int status) {
         case WB_EUNSUPPORTED: return "unsupported shape, layout or mode";
         case WB_ELAUNCH: return "HIP launch or copy failed";
         case WB_EALIGN: return "device pointer not 16-byte aligned";
+        case WB_ESCRATCH: return "layer workspace larger than the library's static scratch (16 MiB)";
         default: return "unknown status";
     }
 }

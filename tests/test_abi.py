@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert wb.lib().state_status_str(code)
     assert wb.lib().state_status_str(-99) == b"unknown status"
 
@@ -146,6 +146,7 @@ def test_calls_reject_null_handles_and_pointers():
     assert L_.state_dequant(None, p, None) == -1
     assert L_.state_quantize(None, p, None) == -1
     assert L_.state_allocate_bits(None, p, None, 0, 1, None) == -1
+    assert L_.state_allocate_bits_static(None, p, None, 0, 1, None) == -1
     assert L_.state_set_estimators(None, p) == -1
     assert L_.state_step_decode_alloc(None, p, p, p, p, p, p, 0, 0, 1, None) == -1
     assert L_.state_free(None) == -1
