@@ -441,24 +441,40 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
         }
 
         // ---- write-back ---------------------------------------------------------------
-        // The state goes through LDS in row-major order, 64 rows at a time: two threads
-        // then round one 32-value row block (an INT8 block: extrema exchanged between
-        // the pair, float16 metadata and levels), and the call's last write-back stores
-        // its codes contiguously.
+        // Element-wise rows (the float16 rows of MIXED) round in registers. Rows with
+        // per-block metadata (and UNIFORM rows, whose codes are packed across columns)
+        // go through LDS in row-major order, up to four row tiles at a time: two
+        // threads then round one 32-value row block (an INT8 block: extrema exchanged
+        // between the pair, float16 metadata and levels), and the call's last
+        // write-back stores its codes contiguously.
         if (write_back && KIND != WB_FP32) {
             const bool last = (t + L == T);
+            if (KIND == WB_MIXED) {
+                // row tile 0: physical rows 0..15, the float16 rows (k_hi = 16)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint16_t hb = f64_to_f16_bits(S[0][r]);
+                    S[0][r] = f16d(hb);
+                    if (last) reinterpret_cast<uint16_t*>(region)[(lg + 4 * r) * DV + col] = hb;
+                }
+            }
+            constexpr int RT0 = KIND == WB_MIXED ? 1 : 0;
             __syncthreads();      // every wave is done with the staging area
 #pragma unroll
             for (int hv = 0; hv < 2; ++hv) {
+                const int g0 = RT0 + 4 * hv;                   // first row tile of this pass
+                const int nrows = 16 * (8 - g0 < 4 ? 8 - g0 : 4);
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq)
+                    if (RT0 + 4 * hv + rq < 8)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)] = S[4 * hv + rq][r];
+                        for (int r = 0; r < 4; ++r)
+                            sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)] = S[(RT0 + 4 * hv + rq) & 7][r];
                 __syncthreads();
-                {
-                    // thread: row lrow, block cb (columns 32 cb .. +31), half hf (16 columns)
-                    const int lrow = tid >> 3, cb = (tid >> 1) & 3, hf = tid & 1;
-                    const int row = 64 * hv + lrow;
+                // thread: row lrow, block cb (columns 32 cb .. +31), half hf (16 columns)
+                const int lrow = tid >> 3, cb = (tid >> 1) & 3, hf = tid & 1;
+                if (lrow < nrows) {
+                    const int row = 16 * g0 + lrow;
                     double* rp = &sm.u.wbuf[lrow][33 * cb + 16 * hf];
                     double x[16];
 #pragma unroll
@@ -481,25 +497,12 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                             uint16_t* dst = reinterpret_cast<uint16_t*>(region + ((row * DV + col0) * ub) / 8);
                             for (int i = 0; i < ub; ++i) dst[i] = uint16_t(wd[i >> 1] >> (16 * (i & 1)));
                         }
-                    } else if (KIND == WB_MIXED && row < k_hi) {
-                        // float16 rows: one correctly rounded conversion per value
-                        uint32_t hw2[8];
-#pragma unroll
-                        for (int c = 0; c < 16; c += 2) {
-                            const uint16_t h0 = f64_to_f16_bits(x[c]), h1 = f64_to_f16_bits(x[c + 1]);
-                            x[c] = f16d(h0);
-                            x[c + 1] = f16d(h1);
-                            hw2[c >> 1] = uint32_t(h0) | (uint32_t(h1) << 16);
-                        }
-                        if (last) {
-                            uint4* dst = reinterpret_cast<uint4*>(region + (row * DV + col0) * 2);
-                            dst[0] = make_uint4(hw2[0], hw2[1], hw2[2], hw2[3]);
-                            dst[1] = make_uint4(hw2[4], hw2[5], hw2[6], hw2[7]);
-                        }
                     } else {
                         // affine INT8 block of 32 values: scale = f16((max - min) / 255) and
                         // zero = f16(min), each rounded once from float64; the level is
-                        // (x - zero) / scale rounded to nearest (ties to even), clamped to [0, 255]
+                        // (x - zero) / scale rounded to nearest (ties to even), clamped to
+                        // [0, 255]: rounded by adding 1.5 * 2^52 (the integer lands in the
+                        // low word), clamped as an integer, and rebuilt exactly from it
                         double mn = x[0], mx = x[0];
 #pragma unroll
                         for (int c = 1; c < 16; ++c) {
@@ -514,10 +517,13 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                         uint32_t cw4[4] = {0, 0, 0, 0};
                         if (sc > 0.0) {
                             const double inv = 1.0 / sc;
+                            constexpr double kM = 6755399441055744.0;          // 1.5 * 2^52
+                            const int mhi = int(uint64_t(__double_as_longlong(kM)) >> 32);
 #pragma unroll
                             for (int c = 0; c < 16; ++c) {
-                                const double lev = fmin(fmax(rint((x[c] - ze) * inv), 0.0), 255.0);
-                                x[c] = fma(lev, sc, ze);
+                                const double tm = (x[c] - ze) * inv + kM;
+                                const int lev = min(max(int(uint32_t(__double_as_longlong(tm))), 0), 255);
+                                x[c] = fma(__hiloint2double(mhi, lev) - kM, sc, ze);
                                 cw4[c >> 2] |= uint32_t(lev) << (8 * (c & 3));
                             }
                         } else {
@@ -539,8 +545,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                 __syncthreads();
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq)
+                    if (RT0 + 4 * hv + rq < 8)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[4 * hv + rq][r] = sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)];
+                        for (int r = 0; r < 4; ++r)
+                            S[(RT0 + 4 * hv + rq) & 7][r] = sm.u.wbuf[16 * rq + lg + 4 * r][widx(col)];
                 __syncthreads();
             }
         }
