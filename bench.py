@@ -125,7 +125,7 @@ def algorithmic_bytes_per_head(kind, extra, per_row, online=False, mode="rtn", a
 
 
 def load_traffic(workload):
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{WORKLOADS[workload]['kernel']}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
