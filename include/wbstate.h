@@ -181,8 +181,12 @@ int state_step_decode(wb_state* st, const float* q, const float* k, const float*
  * bfloat16 bit patterns [B][T][H][d]; beta float32 [B][T][H]; s float32 [B][T][H][dk]
  * or [B][T][H]; o float32 [B][T][H][dv]. The state is written back after tokens
  * t0 + i with (i + 1) % C == 0 and after the last token; outputs come from the
- * unquantized running state. `chunk` is the intra-chunk length of the dense
- * contractions (64; T need not be a multiple). */
+ * unquantized running state. The call is evaluated in segments that end at every
+ * write-back point and are at most min(chunk, 8) tokens long (chunk >= 1, EINVAL
+ * otherwise; the result does not depend on it: the recurrence is exact between
+ * write-backs). The state path runs in float64. Supported: FP32, UNIFORM, HAD_INT8 and
+ * MIXED (k_hi = 16) with 32-value blocks and 8-bit codes, round to nearest, dk = dv =
+ * 128 (EUNSUPPORTED otherwise). */
 int state_prefill_chunk(wb_state* st, const uint16_t* q_bf16, const uint16_t* k_bf16,
                         const uint16_t* v_bf16, const float* beta, const float* s, float* o,
                         int T, int chunk, int C, uint64_t t0, void* stream);
