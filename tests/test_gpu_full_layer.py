@@ -1,12 +1,14 @@
 """Every head of a full layer, one teacher-forced decode step, against the oracle.
 
-The mixed layout at B = 256, H = 32 (round to nearest) and the decay-aware per-row
-widths at the same shape (round to nearest and Philox stochastic rounding, after an
-allocation pass), in the launch configuration the benchmark times: all 8,192 head
-states of the layer are compared, not a sample, so that the parity bound (codes
-bit-equal except at most 1e-4 of the elements, each one step apart and within 1e-5 of
-a step of the boundary; outputs within 1e-4 relative L2 per head) is checked at scale.
-The oracle runs in 16 spawned processes over arrays saved to a temporary directory.
+The mixed layout at B = 256, H = 32 (round to nearest), the decay-aware per-row widths
+at the same shape (round to nearest and Philox stochastic rounding, after an allocation
+pass; and under the layer-wise budget), the Hadamard INT8 layout at B = 64, H = 16 with
+per-head decay and the per-head allocation unit at that shape, in the launch
+configurations the benchmark times: every head state of the layer is compared, not a
+sample, so that the parity bound (codes bit-equal except at most 1e-4 of the elements,
+each one step apart and within 1e-5 of a step of the boundary; outputs within 1e-4
+relative L2 per head) is checked at scale. The oracle runs in 16 spawned processes over
+arrays saved to a temporary directory.
 """
 import multiprocessing as mp
 import os
@@ -31,26 +33,37 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-@pytest.mark.parametrize("kind,mode", [(L.MIXED, "rtn"), (L.BITALLOC, "rtn"), (L.BITALLOC, "sr")],
-                         ids=["mixed-rtn", "bitalloc-rtn", "bitalloc-sr"])
-def test_full_layer_every_head(kind, mode):
+CASES = {
+    "mixed-rtn": dict(kind=L.MIXED, mode="rtn", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
+    "bitalloc-rtn": dict(kind=L.BITALLOC, mode="rtn", B=256, H=32, per_row=True, kw={}),
+    "bitalloc-sr": dict(kind=L.BITALLOC, mode="sr", B=256, H=32, per_row=True, kw={}),
+    "bitalloc-layer-rtn": dict(kind=L.BITALLOC, mode="rtn", B=256, H=32, per_row=True, kw=dict(budget="layer")),
+    "had-int8-rtn-gdn": dict(kind=L.HAD_INT8, mode="rtn", B=64, H=16, per_row=False, kw=dict(block=128)),
+    "headalloc-rtn-gdn": dict(kind=L.HEADALLOC, mode="rtn", B=64, H=16, per_row=False, kw={}),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_full_layer_every_head(case):
     import linear_attn_decode_amd as wb
-    B, H, d = 256, 32, 128
-    kw = dict(block=32, k_hi=16) if kind == L.MIXED else {}
-    lay_kw = dict(kind=kind, B=B, H=H, dk=d, dv=d, mode=mode, seed=0x5EED_1234_ABCD, **kw)
-    print(f"\n[case] full layer {kind} {mode} B={B} H={H}", flush=True)
+    c = CASES[case]
+    kind, mode, B, H, per_row, kw = c["kind"], c["mode"], c["B"], c["H"], c["per_row"], c["kw"]
+    d = 128
+    lay_kw = dict(kind=kind, B=B, H=H, dk=d, dv=d, mode=mode, per_row_decay=per_row, seed=0x5EED_1234_ABCD, **kw)
+    print(f"\n[case] full layer {case} B={B} H={H}", flush=True)
     rng = np.random.default_rng(61)
     perm = np.stack([rng.permutation(d) for _ in range(H)]) if kind == L.MIXED else None
-    st = wb.WriteBackState(kind, mode, B, H, d, d, True, seed=lay_kw["seed"], perm=perm, **kw)
+    st = wb.WriteBackState(kind, mode, B, H, d, d, per_row, seed=lay_kw["seed"], perm=perm, **kw)
     scale = np.exp(rng.uniform(-3.0, 0.5, (B, H, d, 1)))
     S0 = (rng.standard_normal((B, H, d, d)) * scale).astype(np.float32)
     st.quantize(_dev(S0))
     del S0
-    inp = decode_inputs(62, B, H, d, d, 2, True)
+    inp = decode_inputs(62, B, H, d, d, 2, per_row)
     dev = {n: _dev(a) for n, a in inp.items()}
     o = torch.zeros((B, H, d), dtype=torch.float32, device="cuda")
-    if kind == L.BITALLOC:
-        st.allocate_bits(dev["s"])
+    if kind in (L.BITALLOC, L.HEADALLOC):
+        s_rows = dev["s"] if per_row else dev["s"][:, :, None].expand(B, H, d).contiguous()
+        st.allocate_bits(s_rows)
     # one untimed step, so that the compared step starts from a state the kernel wrote
     st.step_decode(dev["q"][0], dev["k"][0], dev["v"][0], dev["beta"][0], dev["s"], o, 0)
     torch.cuda.synchronize()
