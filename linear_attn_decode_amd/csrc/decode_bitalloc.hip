@@ -50,8 +50,10 @@ struct TabA {                                   // dequantize constants, by sort
     float alpha, beta0, k, q;                   // a Delta, -n a Delta, k_i, q_i
 };
 struct TabB {                                   // requantize constants, by sorted position
+    uint32_t off;                               // byte offset of the row's codes
+    uint32_t bw;                                // width (off, bw: one 8-byte read)
     float fn;                                   // f / n
-    uint32_t loc;                               // byte offset | width << 16 | row << 24
+    uint32_t row;                               // row index
 };
 
 struct BaFixed {
@@ -65,18 +67,22 @@ struct BaFixed {
     // [wavefront][row group][row step][quantity * 4 + limb] (limb 3 is zero)
     uint16_t alimb[NW][4][MR][8];
 };
-// the staged region follows BaFixed in dynamic LDS
-constexpr int kRegOffset = (int(sizeof(BaFixed)) + 15) / 16 * 16;
+// LDS: the staged region first (at most the code area at 8 bits per element, Delta and
+// the width / fit bytes, and 16 bytes that the last row's 3-word read may touch), then
+// BaFixed; one static size, so that the compiler folds the bases into the instruction
+// offsets
+constexpr int kCodeAreaMax = DK * DV;
+constexpr int kFixedOffset = (kCodeAreaMax + 3 * DK + 16 + 15) / 16 * 16;
+constexpr int kSmemBytes = kFixedOffset + int(sizeof(BaFixed));
 
-// f_k / n_b for fit index k (f_k = 1/4 + k/20) and width b (n_b = 2^(b-1) - 1)
-struct FnTable {
-    float v[16][9];
-    constexpr FnTable() : v() {
-        for (int k = 0; k < 16; ++k)
-            for (int b = 2; b <= 8; ++b) v[k][b] = (0.25f + 0.05f * float(k)) / float((1 << (b - 1)) - 1);
-    }
-};
-__constant__ FnTable kFn = FnTable();
+// f_k / n_b for fit index k (f_k = 1/4 + k/20) and width b (n_b = 2^(b-1) - 1), each
+// step rounded once in float32 (the multiply and add kept apart, the division correctly
+// rounded); computed in registers, so that no memory lookup sits on the table path.
+// One-bit rows (b = 1, no fit) get 0.
+__device__ __forceinline__ float fn_of(int k, int b) {
+    const float f = __fadd_rn(0.25f, __fmul_rn(0.05f, float(k)));
+    return b > 1 ? __fdiv_rn(f, float((1 << (b - 1)) - 1)) : 0.f;
+}
 
 // The three 32-bit words of the staged region that hold a lane's 8 codes (at most 64
 // bits starting anywhere in the first word).
@@ -253,7 +259,7 @@ __device__ __forceinline__ void unpack8_any(const Raw& raw, int boff, int bw, fl
     const uint64_t fld = uint64_t(lo) | (uint64_t(hi) << 32);
     const uint32_t mask = (1u << bw) - 1;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) code[c] = float(uint32_t(fld >> (c * bw)) & mask);
+    for (int c = 0; c < 8; ++c) code[c] = float(uint32_t(fld >> __umul24(uint32_t(c), uint32_t(bw))) & mask);
 }
 
 template <bool OB, bool SR>
@@ -274,7 +280,7 @@ __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const
             code = y - base;
             if (OB && bw == 1) code = x[c] * inv > 0.f;
         }
-        fld |= uint64_t(code) << (c * bw);
+        fld |= uint64_t(code) << __umul24(uint32_t(c), uint32_t(bw));
     }
     uint8_t* bytes = reinterpret_cast<uint8_t*>(reg);
 #pragma unroll
@@ -286,26 +292,38 @@ __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const
 // handled together are adjacent in the width order, so this is the common case), the
 // width is a scalar and the specialised code is chosen by a scalar branch; otherwise
 // the generic per-lane code runs.
+// The floats are pinned inside each specialised branch (an empty asm that takes them as
+// operands), so the conversions stay next to the width-specific field extraction (byte
+// conversions for widths 4 and 8) instead of being merged after the branches.
+template <int B>
+__device__ __forceinline__ void unpack8_pinned(const Raw& raw, int boff, float code[8]) {
+    unpack8<B>(raw, boff, code);
+    asm volatile("" : "+v"(code[0]), "+v"(code[1]), "+v"(code[2]), "+v"(code[3]), "+v"(code[4]), "+v"(code[5]),
+                 "+v"(code[6]), "+v"(code[7]));
+}
+
+// Returns the width as a scalar when the lanes share it, else 0 (the pack reuses it).
 template <bool OB>
-__device__ __forceinline__ void unpack_rows(const Raw& raw, int boff, int bw, float code[8]) {
+__device__ __forceinline__ int unpack_rows(const Raw& raw, int boff, int bw, float code[8]) {
     const int bu = __builtin_amdgcn_readfirstlane(bw);
     if (__ballot(bw != bu) == 0ull) {
         if (OB && bu == 1) {
-            unpack8<1>(raw, boff, code);
-            return;
+            unpack8_pinned<1>(raw, boff, code);
+            return bu;
         }
         switch (bu) {
-            case 2: unpack8<2>(raw, boff, code); break;
-            case 3: unpack8<3>(raw, boff, code); break;
-            case 4: unpack8<4>(raw, boff, code); break;
-            case 5: unpack8<5>(raw, boff, code); break;
-            case 6: unpack8<6>(raw, boff, code); break;
-            case 7: unpack8<7>(raw, boff, code); break;
-            default: unpack8<8>(raw, boff, code); break;
+            case 2: unpack8_pinned<2>(raw, boff, code); break;
+            case 3: unpack8_pinned<3>(raw, boff, code); break;
+            case 4: unpack8_pinned<4>(raw, boff, code); break;
+            case 5: unpack8_pinned<5>(raw, boff, code); break;
+            case 6: unpack8_pinned<6>(raw, boff, code); break;
+            case 7: unpack8_pinned<7>(raw, boff, code); break;
+            default: unpack8_pinned<8>(raw, boff, code); break;
         }
-    } else {
-        unpack8_any(raw, boff, bw, code);
+        return bu;
     }
+    unpack8_any(raw, boff, bw, code);
+    return 0;
 }
 
 template <int B, bool SR>
@@ -314,11 +332,12 @@ __device__ __forceinline__ void pack8_rule(uint32_t* reg, int boff, const float 
     else pack8<B>(reg, boff, x, InvOne{inv});
 }
 
+// bu: the shared width from unpack_rows (0: the lanes' widths differ; the per-lane
+// width is then read from *bw)
 template <bool OB, bool SR>
-__device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const float x[8], float inv,
-                                          const uint32_t r16[8]) {
-    const int bu = __builtin_amdgcn_readfirstlane(bw);
-    if (__ballot(bw != bu) == 0ull) {
+__device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bu, const uint32_t* bw, const float x[8],
+                                          float inv, const uint32_t r16[8]) {
+    if (bu != 0) {
         if (OB && bu == 1) {
             pack8_rule<1, SR>(reg, boff, x, inv, r16);
             return;
@@ -333,7 +352,7 @@ __device__ __forceinline__ void pack_rows(uint32_t* reg, int boff, int bw, const
             default: pack8_rule<8, SR>(reg, boff, x, inv, r16); break;
         }
     } else {
-        pack8_any<OB, SR>(reg, boff, bw, x, inv, r16);
+        pack8_any<OB, SR>(reg, boff, int(*bw), x, inv, r16);
     }
 }
 
@@ -363,6 +382,14 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+}
+
+// 16 bytes from global memory straight into LDS (no registers): lane l of the wavefront
+// writes bytes [16 l, 16 l + 16) after `wave_dst`, which must be the same for every lane
+// of the wavefront (the hardware takes it from a scalar register).
+__device__ __forceinline__ void lds_load16(const uint4* src, uint32_t* wave_dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
 }
 
 // Three bfloat16 limbs whose sum is the float32 c exactly: each limb keeps the leading
@@ -424,9 +451,9 @@ __device__ __forceinline__ float rowsum4_scatter(const float m[4], int cg) {
 // carries no trace of the others.
 template <bool EST, bool LAYER, bool OB, bool SR>
 __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KArgs A) {
-    extern __shared__ __align__(16) uint8_t smraw[];
-    BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw);
-    uint32_t* reg = reinterpret_cast<uint32_t*>(smraw + kRegOffset);
+    __shared__ __align__(16) uint8_t smraw[kSmemBytes];
+    BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw + kFixedOffset);
+    uint32_t* reg = reinterpret_cast<uint32_t*>(smraw);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int head = blockIdx.x;
@@ -438,48 +465,63 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
     constexpr int kMetaVec = 3 * DK / 16;
     const uint8_t* meta = region + code_bytes + 2 * DK;
 
-    // ---- loads: the region (staged through registers), metadata, per-row inputs ------
-    // Per-head budget: the region in one piece. Layer budget: the codes every head holds
-    // (b_min bits per element) and the metadata, then, once the widths are summed, the
-    // rest of the codes in use.
-    uint4 pf0 = make_uint4(0, 0, 0, 0), pf1 = pf0, pf2 = pf0, pfm = pf0;
-    const uint4* src = reinterpret_cast<const uint4*>(region);
-    int nvec = 0, nmin = 0, ncode = 0;
-    int meta0 = 0, meta1 = 0;
-    if constexpr (!LAYER) {
-        nvec = (code_bytes + 3 * DK) / 16;
-        if (tid < nvec) pf0 = src[tid];
-        if (tid + NT < nvec) pf1 = src[tid + NT];
-        if (tid + 2 * NT < nvec) pf2 = src[tid + 2 * NT];
-    } else {
-        nmin = min(A.bmin * (DK * DV / 8 / 16), NT);
-        if (tid < nmin) pf0 = src[tid];
-        if (tid < kMetaVec) pfm = src[code_bytes / 16 + tid];
-        meta0 = meta[lane];
-        meta1 = meta[lane + 64];
-        // 16-byte vectors of codes in use: sum of the widths times DV / 128 (at most the
-        // code area)
-        ncode = min(wave_sum_i32((meta0 & 7) + (meta1 & 7) + 2) * (DV / 128), code_bytes / 16);
-        if (nmin + tid < ncode) pf1 = src[nmin + tid];
-        if (nmin + tid + NT < ncode) pf2 = src[nmin + tid + NT];
-    }
+    // ---- loads: per-row inputs, the region (straight into LDS) ------------------------
+    // Wavefronts 0 and 1 build the per-row tables: they load the rows' inputs only, so
+    // that their wait covers nothing else. Wavefronts 2..7 copy the region: per-head
+    // budget, the region in one piece; layer budget, the codes every head holds (b_min
+    // bits per element) and the metadata, then, once the widths are summed, the rest of
+    // the codes in use. Vector i of the region goes to vector i of the staging copy.
     const float vj = A.v[(size_t)head * DV + (tid & (DV - 1))];
     const float beta = A.beta[head];
+    const int trow = lane + 64 * (wave & 1);
+    const size_t rb = (size_t)head * DK + trow;
+    int meta0 = 0, meta1 = 0;
+    float kr = 0.f, qr = 0.f, sr = 0.f;
+    uint32_t dold = 0;
+    int ncode = 0;
+    if (LAYER || wave < 2) {
+        meta0 = meta[lane];
+        meta1 = meta[lane + 64];
+    }
+    // layer budget: the 16-byte vectors of codes in use, the sum of the widths times
+    // DV / 128 (at most the code area)
+    if constexpr (LAYER) ncode = min(wave_sum_i32((meta0 & 7) + (meta1 & 7) + 2) * (DV / 128), code_bytes / 16);
+    if (wave < 2) {
+        kr = A.k[rb];
+        qr = A.q[rb];
+        sr = A.s_per_row ? A.s[rb] : A.s[head];
+        dold = reinterpret_cast<const uint16_t*>(region + code_bytes)[trow];
+    } else {
+        const uint4* src = reinterpret_cast<const uint4*>(region);
+        constexpr int NS = NT - 128;                    // copying threads
+        const int st = tid - 128, sw0 = 64 * (wave - 2);
+        // vectors [v0, v1): thread st copies v0 + st, v0 + st + NS, ...; the wavefront's
+        // first vector of each round is a scalar (the LDS destination comes from it)
+        auto copy = [&](int v0, int v1) {
+            for (int r = 0; v0 + r + st < v1; r += NS) lds_load16(src + v0 + r + st, reg + 4 * (v0 + r + sw0));
+        };
+        if constexpr (!LAYER) {
+            copy(0, (code_bytes + 3 * DK) / 16);
+        } else {
+            const int nmin = A.bmin * (DK * DV / 8 / 16);
+            copy(0, nmin);
+            copy(code_bytes / 16, code_bytes / 16 + kMetaVec);
+            copy(nmin, ncode);
+        }
+    }
 
     // ---- per-row tables: wavefronts 0 and 1 own rows lane and lane + 64 ---------------
     // The width order, the byte offsets and the ranks come from ballots over the width
     // bytes of all 128 rows, which both wavefronts read.
     if (wave < 2) {
-        if constexpr (!LAYER) {
-            meta0 = meta[lane];
-            meta1 = meta[lane + 64];
-        }
-        const int trow = lane + 64 * wave;
-        const size_t rb = (size_t)head * DK + trow;
-        const float kr = A.k[rb], qr = A.q[rb];
-        const float sr = A.s_per_row ? A.s[rb] : A.s[head];
+        // The rest of the workgroup waits for these two wavefronts: they run at a raised
+        // issue priority until the tables are written (other workgroups on the compute
+        // unit fill the gaps).
+        __builtin_amdgcn_s_setprio(3);
+        // (opaque from here on, so that no use of the row inputs is placed among the loads
+        // and makes the wavefront wait for them before the loads are all issued)
+        asm volatile("" : "+v"(meta0), "+v"(meta1), "+v"(kr), "+v"(qr), "+v"(sr), "+v"(dold));
         if constexpr (EST) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, trow, sr, beta, kr);
-        const uint32_t dold = reinterpret_cast<const uint16_t*>(region + code_bytes)[trow];
         const int bw0 = (meta0 & 7) + 1, bw1 = (meta1 & 7) + 1;
         const bool hi_half = wave == 1;
         const int bwt = hi_half ? bw1 : bw0;
@@ -503,7 +545,7 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
         const bool one = OB && bwt == 1;
         const float alpha = one ? 2.f * ad : ad, beta0 = one ? -ad : -n * ad;
         sm.ta[pos] = TabA{alpha, beta0, kr, qr};
-        sm.tb[pos] = TabB{kFn.v[fit][bwt], uint32_t(off * (DV / 8)) | (uint32_t(bwt) << 16) | (uint32_t(trow) << 24)};
+        sm.tb[pos] = TabB{uint32_t(off * (DV / 8)), uint32_t(bwt), fn_of(fit, bwt), uint32_t(trow)};
         // u and p on the matrix cores: u_j = sum_i (k_i alpha_i) code_ij + sum_i k_i beta0_i
         // (p with q_i); the row weights as exact bfloat16 limbs, the constant terms summed here
         const uint2 lu = bf16_limbs3(kr * alpha), lp = bf16_limbs3(qr * alpha);
@@ -517,19 +559,7 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
             sm.bias[wave][0] = bu;
             sm.bias[wave][1] = bp;
         }
-    }
-    {
-        uint4* dst = reinterpret_cast<uint4*>(reg);
-        if constexpr (!LAYER) {
-            if (tid < nvec) dst[tid] = pf0;
-            if (tid + NT < nvec) dst[tid + NT] = pf1;
-            if (tid + 2 * NT < nvec) dst[tid + 2 * NT] = pf2;
-        } else {
-            if (tid < nmin) dst[tid] = pf0;
-            if (tid < kMetaVec) dst[code_bytes / 16 + tid] = pfm;
-            if (nmin + tid < ncode) dst[nmin + tid] = pf1;
-            if (nmin + tid + NT < ncode) dst[nmin + tid + NT] = pf2;
-        }
+        __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
 
@@ -541,29 +571,29 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
     // holds the codes (exact in bfloat16), A the limbs of the row weights; output row
     // 8 s + 4 q + limb of lane column cg is the partial of quantity q (u, p) for column
     // 8 cg + 2 cp + s over the wavefront's 16 rows.
-    auto boff_of = [&](uint32_t l) { return int(l & 0xFFFFu) + cg * int((l >> 16) & 15u); };
-    uint32_t bop[4][MR];                       // B operands: [column pair][row]
-    uint32_t loc_cur = sm.tb[4 * wave + rq].loc;
-    uint32_t loc_next = sm.tb[NG + 4 * wave + rq].loc;
+    // (byte offset, width) of the lane's row at step m; the lane's codes start at
+    // offset + cg * width
+    // the wavefront's table entries: sorted positions NG m + 4 wave + rq
+    const TabA* taw = &sm.ta[4 * wave];
+    const TabB* tbw = &sm.tb[4 * wave];
+    auto loc_of = [&](int m) { return *reinterpret_cast<const uint2*>(&tbw[NG * m + rq].off); };
+    auto boff_of = [&](uint2 l) { return int(__umul24(uint32_t(cg), l.y) + l.x); };
+    // the codes as floats, row m column 8 cg + c; later the updated state in place
+    float x[MR][8];
+    int bus[MR];                                // shared widths, kept for the pack
+    uint2 loc_cur = loc_of(0);
+    uint2 loc_next = loc_of(1);
     Raw raw_next = load_raw(reg, boff_of(loc_cur));
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         const Raw raw = raw_next;
-        const uint32_t loc = loc_cur;
+        const uint2 loc = loc_cur;
         if (m + 1 < MR) {
             raw_next = load_raw(reg, boff_of(loc_next));
             loc_cur = loc_next;
         }
-        if (m + 2 < MR) loc_next = sm.tb[NG * (m + 2) + 4 * wave + rq].loc;
-        float code[8];
-        unpack_rows<OB>(raw, boff_of(loc), int((loc >> 16) & 15u), code);
-        // the codes are integers below 2^8, so a float's high half is its exact bfloat16
-#pragma unroll
-        for (int cp = 0; cp < 4; ++cp)
-            bop[cp][m] = __builtin_amdgcn_perm(__float_as_uint(code[2 * cp + 1]), __float_as_uint(code[2 * cp]),
-                                               0x07060302u);
-        // finish this row here (keeps the codes of one row live at a time)
-        asm volatile("" ::"v"(bop[0][m]), "v"(bop[1][m]), "v"(bop[2][m]), "v"(bop[3][m]));
+        if (m + 2 < MR) loc_next = loc_of(m + 2);
+        bus[m] = unpack_rows<OB>(raw, boff_of(loc), int(loc.y), x[m]);
     }
     {
         // A operand of lane (g = rq, output row mo = cg): the limb of quantity (mo / 4) % 2
@@ -577,7 +607,13 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
         float* red = &sm.red[rq & 1][wave][8 * cg + (rq >> 1)];
 #pragma unroll
         for (int cp = 0; cp < 4; ++cp) {
-            const f32x4_t d = mfma_bf16_16x16x32(aop, bop[cp]);
+            // the codes are integers below 2^8, so a float's high half is its exact bfloat16
+            uint32_t bop[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                bop[m] = __builtin_amdgcn_perm(__float_as_uint(x[m][2 * cp + 1]), __float_as_uint(x[m][2 * cp]),
+                                               0x07060302u);
+            const f32x4_t d = mfma_bf16_16x16x32(aop, bop);
             red[2 * cp] = (d[0] + d[1]) + d[2];
         }
     }
@@ -611,21 +647,15 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
     // update and in-lane maxima of |x| of the lane's rows, then the row maxima over the
     // 16 lanes of each row reduced and scattered (each lane ends with one of the 4 rows),
     // so that every step is derived once per 4 lanes and handed back by quad broadcasts
-    // dequantize + decay from the codes kept in the B operands (x = code alpha + beta0),
-    // then the update
-    float x[MR][8];
+    // dequantize + decay from the codes kept as floats (x = code alpha + beta0), then the
+    // update
     uint32_t mxb[MR];
     float sab[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-        const TabA ta = sm.ta[NG * m + 4 * wave + rq];
+        const TabA ta = taw[NG * m + rq];
 #pragma unroll
-        for (int cp = 0; cp < 4; ++cp) {
-            x[m][2 * cp] = __builtin_fmaf(__uint_as_float(bop[cp][m] << 16), ta.alpha, ta.beta0);
-            x[m][2 * cp + 1] = __builtin_fmaf(__uint_as_float(bop[cp][m] & 0xFFFF0000u), ta.alpha, ta.beta0);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[m][c] = __builtin_fmaf(ta.k, wv[c], x[m][c]);
+        for (int c = 0; c < 8; ++c) x[m][c] = __builtin_fmaf(ta.k, wv[c], __builtin_fmaf(x[m][c], ta.alpha, ta.beta0));
         float mx = fmaxf(fmaxf(fabsf(x[m][0]), fabsf(x[m][1])), fabsf(x[m][2]));
         mx = fmaxf(fmaxf(mx, fabsf(x[m][3])), fabsf(x[m][4]));
         mx = fmaxf(fmaxf(mx, fabsf(x[m][5])), fabsf(x[m][6]));
@@ -638,7 +668,7 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
     {
         // this lane's row: ms = ((cg & 1) << 1) | ((cg >> 1) & 1)
         const int ms = ((cg & 1) << 1) | ((cg >> 1) & 1);
-        const TabB tb = sm.tb[NG * ms + 4 * wave + rq];
+        const TabB tb = tbw[NG * ms + rq];
         const float R = __uint_as_float(rowmax4_scatter(mxb, cg));
         uint32_t dbits = f16_bits_of_product(R, tb.fn);
         if constexpr (OB) {
@@ -646,14 +676,14 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
             // and four DPP steps (relative error below 7 float32 roundings)
             const float sa = rowsum4_scatter(sab, cg);
             const uint32_t d1 = f16_bits_of_product(sa, 1.f / float(DV));
-            if (((tb.loc >> 16) & 15u) == 1u) dbits = d1;
+            if (tb.bw == 1u) dbits = d1;
         }
         const float dl = f16_bits_to_f32(dbits);
         // reciprocal refined by one Newton step (near correctly rounded)
         float r = __builtin_amdgcn_rcpf(dl);
         r = __builtin_fmaf(__builtin_fmaf(-dl, r, 1.f), r, r);
         const uint32_t ib = __float_as_uint(dl > 0.f ? r : 0.f);
-        if (cg < 4) dout[tb.loc >> 24] = uint16_t(dbits);
+        if (cg < 4) dout[tb.row] = uint16_t(dbits);
         // row m sits in quad lane ((m & 1) << 1) | (m >> 1)
         inv[0] = __uint_as_float(dpp_u32<0x00>(ib));
         inv[1] = __uint_as_float(dpp_u32<0xAA>(ib));
@@ -663,10 +693,10 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
     // ... then the rounding and packing, specialised per width
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-        const uint32_t l = sm.tb[NG * m + 4 * wave + rq].loc;
+        const TabB* tb = &tbw[NG * m + rq];
         uint32_t r16[8];
-        if constexpr (SR) sr_draws8(A.seed, uint32_t(head), A.t, int(l >> 24), cg, r16);
-        pack_rows<OB, SR>(reg, boff_of(l), int((l >> 16) & 15u), x[m], inv[m], r16);
+        if constexpr (SR) sr_draws8(A.seed, uint32_t(head), A.t, int(tb->row), cg, r16);
+        pack_rows<OB, SR>(reg, boff_of(loc_of(m)), bus[m], &tb->bw, x[m], inv[m], r16);
     }
     __syncthreads();
     {
@@ -689,21 +719,21 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
 
 namespace {
 template <bool EST, bool LAYER, bool OB>
-void launch_variant(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
+void launch_variant(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
     if (d.mode == WB_SR)
-        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, true>), dim3(d.B * d.H), dim3(NT), smem, stream, a);
+        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     else
-        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, false>), dim3(d.B * d.H), dim3(NT), smem, stream, a);
+        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
 }
 template <bool EST, bool LAYER>
-void launch_ob(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
-    if (d.bmin == 1) launch_variant<EST, LAYER, true>(d, a, smem, stream);
-    else launch_variant<EST, LAYER, false>(d, a, smem, stream);
+void launch_ob(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
+    if (d.bmin == 1) launch_variant<EST, LAYER, true>(d, a, stream);
+    else launch_variant<EST, LAYER, false>(d, a, stream);
 }
 template <bool EST>
-void launch_layer(const wb_layout_desc& d, const KArgs& a, size_t smem, hipStream_t stream) {
-    if (a.layer) launch_ob<EST, true>(d, a, smem, stream);
-    else launch_ob<EST, false>(d, a, smem, stream);
+void launch_layer(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
+    if (a.layer) launch_ob<EST, true>(d, a, stream);
+    else launch_ob<EST, false>(d, a, stream);
 }
 }  // namespace
 
@@ -783,7 +813,7 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
         const float dold = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(region + cap)[t]);
         const int fit = region[cap + 2 * HGR * DV + t] & 15;
         sm.g[t] = make_float2(dold, -float(n) * dold);     // exact: 11 + 7 significant bits
-        sm.fn[t] = kFn.v[fit][B];
+        sm.fn[t] = fn_of(fit, B);
     }
     {
         uint4* dst = reinterpret_cast<uint4*>(sm.reg);
@@ -981,9 +1011,9 @@ hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStre
     // the staged region: the code area (per head: b-bar bits per element; layer budget:
     // b_max), Delta and the width / fit bytes
     const size_t code_area = size_t(a.layer ? a.code_cap : DK * DV * d.bbar / 8);
-    const size_t smem = kRegOffset + (code_area + 3 * DK + 15) / 16 * 16 + 16;
-    if (a.est) launch_layer<true>(d, a, smem, stream);
-    else launch_layer<false>(d, a, smem, stream);
+    if (code_area > size_t(kCodeAreaMax)) return hipErrorInvalidValue;
+    if (a.est) launch_layer<true>(d, a, stream);
+    else launch_layer<false>(d, a, stream);
     return hipGetLastError();
 }
 
