@@ -367,17 +367,17 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
            (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
-// float sum over the wavefront, returned as a scalar (DPP inside rows of 16 lanes, then
-// the four row sums read with every lane active)
-__device__ __forceinline__ float wave_sum_f32(float v) {
+// float sum over the wavefront, left in lane 63: DPP inside rows of 16 lanes, then
+// each row's sum carried into the next by row broadcasts (lane 15 of row r to row r + 1,
+// lane 31 to rows 2 and 3)
+__device__ __forceinline__ float wave_sum_f32_last(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
-           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return v;
 }
 
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
@@ -552,9 +552,9 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
         *reinterpret_cast<uint4*>(&sm.alimb[(pos % NG) >> 2][pos & 3][pos / NG][0]) =
             make_uint4(lu.x, lu.y, lp.x, lp.y);
         // q . k and the constant terms over the wavefront's 64 rows
-        const float qsum = wave_sum_f32(qr * kr);
-        const float bu = wave_sum_f32(kr * beta0), bp = wave_sum_f32(qr * beta0);
-        if (lane == 0) {
+        const float qsum = wave_sum_f32_last(qr * kr);
+        const float bu = wave_sum_f32_last(kr * beta0), bp = wave_sum_f32_last(qr * beta0);
+        if (lane == 63) {
             sm.qk[wave] = qsum;
             sm.bias[wave][0] = bu;
             sm.bias[wave][1] = bp;

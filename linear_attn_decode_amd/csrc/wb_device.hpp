@@ -29,9 +29,14 @@ __device__ __forceinline__ Ctr4 philox4x32_10(Ctr4 c, uint32_t k0, uint32_t k1) 
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = Ctr4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        // each 32 x 32 -> 64-bit product as one multiply (low and high words together)
+        const uint64_t p0 = uint64_t(0xD2511F53u) * c.x, p1 = uint64_t(0xCD9E8D57u) * c.z;
+        const uint32_t lo0 = uint32_t(p0), hi0 = uint32_t(p0 >> 32);
+        const uint32_t lo1 = uint32_t(p1), hi1 = uint32_t(p1 >> 32);
+        // (three-input exclusive or: truth table 0x96)
+        const uint32_t x0 = uint32_t(__builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96));
+        const uint32_t x2 = uint32_t(__builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96));
+        c = Ctr4{x0, lo1, x2, lo0};
     }
     return c;
 }
