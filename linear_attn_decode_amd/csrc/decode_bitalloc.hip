@@ -384,14 +384,6 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
 }
 
-// 16 bytes from global memory straight into LDS (no registers): lane l of the wavefront
-// writes bytes [16 l, 16 l + 16) after `wave_dst`, which must be the same for every lane
-// of the wavefront (the hardware takes it from a scalar register).
-__device__ __forceinline__ void lds_load16(const uint4* src, uint32_t* wave_dst) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
-}
-
 // Three bfloat16 limbs whose sum is the float32 c exactly: each limb keeps the leading
 // 8 significant bits of what the previous ones left (truncation), and 3 x 8 bits cover
 // the 24-bit significand. Returned as (limb0 | limb1 << 16, limb2).

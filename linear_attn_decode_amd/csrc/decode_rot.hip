@@ -7,8 +7,9 @@
 // Same computation as the generic decode kernel (rotated domain: u = sum_P k a S +
 // H sum_Q k a Y, w = beta (v - u), S_P' = a S_P + k w, Y_Q' = a Y_Q + k (H w),
 // o = sum_P q a S + H sum_Q q a Y + (q . k) w), organised for throughput:
-//   * the region is staged in LDS with 16-byte loads, updated there, and written back
-//     with 16-byte stores;
+//   * the region is staged in LDS by global-to-LDS 16-byte loads (two wavefronts; the
+//     other two build the per-row tables meanwhile); each updated row is written back to
+//     HBM by the lanes that requantized it, with 16-byte stores;
 //   * u and p (contractions over rows) run column-parallel: thread (j, half) walks
 //     half of the rows of column j, so the only cross-thread step is adding two
 //     halves; the float64 step and offset of every INT8 block are tabulated once;
@@ -141,33 +142,38 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     double2* kq = reinterpret_cast<double2*>(&sm.part[0][0]);
     constexpr int kZW = RotSmem<KHI, BLOCK, IB>::ZW;     // wavefronts that hold INT8 blocks
 
-    // v and beta for the vector phase, requested first
+    // ---- per-row tables in physical row order (wavefronts 0, 1); the region staged in
+    // LDS (wavefronts 2, 3) -------------------------------------------------------------
+    // The table wavefronts load only their own inputs, so that their waits cover nothing
+    // else; the other two issue the whole region as global-to-LDS loads at once.
     float v_lo = 0.f, v_hi = 0.f, beta_in = 0.f;
-    if (wave == 0) {
-        v_lo = A.v[(size_t)head * DV + lane];
-        v_hi = A.v[(size_t)head * DV + lane + 64];
-        beta_in = A.beta[head];
-    }
-
-    // ---- stage the region; per-row tables in physical row order -----------------------
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(region);
-        uint4* dst = reinterpret_cast<uint4*>(sm.reg);
-#pragma unroll
-        for (int i = tid; i < LY::REGION / 16; i += NT) dst[i] = src[i];
-    }
     if (wave < 2) {
+        // v and beta for the vector phase (wavefront 0)
+        if (wave == 0) {
+            v_lo = A.v[(size_t)head * DV + lane];
+            v_hi = A.v[(size_t)head * DV + lane + 64];
+            beta_in = A.beta[head];
+        }
         const int p = tid;
         const int lr = KHI > 0 ? int(A.perm[h * DK + p]) : p;
-        const double kd = double(A.k[(size_t)head * DK + lr]);
-        const double qd = double(A.q[(size_t)head * DK + lr]);
+        const float kf = A.k[(size_t)head * DK + lr], qf = A.q[(size_t)head * DK + lr];
         const float sv = A.s_per_row ? A.s[(size_t)head * DK + lr] : A.s[head];
+        // The rest of the workgroup waits for these two wavefronts: they run at a raised
+        // issue priority until the tables are written.
+        __builtin_amdgcn_s_setprio(3);
+        const double kd = double(kf), qd = double(qf);
         const double ad = exp(-double(sv));
         kq[p] = make_double2(kd * ad, qd * ad);
         sm.ak[p] = make_double2(ad, kd);
         double pq = qd * kd;
         pq = wave_sum_f64<1>(pq);
         if (lane == 0) sm.qk[wave] = pq;
+        __builtin_amdgcn_s_setprio(0);
+    } else {
+        // vectors i0 + lane of the region, i0 = 64 (wave - 2) + 128 r (a scalar)
+        const uint4* src = reinterpret_cast<const uint4*>(region);
+        for (int i0 = 64 * (wave - 2); i0 < LY::REGION / 16; i0 += 128)
+            if (i0 + lane < LY::REGION / 16) lds_load16(src + i0 + lane, &sm.reg[4 * i0]);
     }
     __syncthreads();
     // The contraction over rows folds each INT8 block's step into the row weights:
@@ -264,6 +270,9 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     // ---- w = beta (v - u), o = p + (q . k) w, H w (one wavefront) ----------------------
     // (wavefront 0: u, w and H w; wavefront 1: p, in parallel; o after the barrier)
     if (wave == 0) {
+        // (v and beta opaque until here, so that their conversions are not placed among
+        // the loads at the start, where they would make the wavefront wait for them)
+        asm volatile("" : "+v"(v_lo), "+v"(v_hi), "+v"(beta_in));
         double uq0 = sm.part[2][lane], uq1 = sm.part[2][lane + 64];
         wht128(uq0, uq1, lane);
         const double u0 = sm.part[0][lane] + uq0, u1 = sm.part[0][lane + 64] + uq1;
@@ -315,7 +324,8 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                         const double xn = fma(ak.x, x, ak.y * sm.w[16 * cg + 8 * hv + c]);
                         o4[c >> 1] |= uint32_t(f64_to_f16_bits(xn)) << ((c & 1) * 16);
                     }
-                    ptr[hv] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+                    // straight to the stored region (nothing reads the staged copy again)
+                    reinterpret_cast<uint4*>(region + (p * DV + 16 * cg) * 2)[hv] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
                 }
                 continue;
             }
@@ -381,18 +391,15 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                     }
                 }
             }
-            if constexpr (IB == 8) *reinterpret_cast<uint4*>(cptr) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-            else *reinterpret_cast<uint2*>(cptr) = make_uint2(o4[0], o4[1]);
+            // straight to the stored region (nothing reads the staged copy again), so the
+            // stores overlap the rest of the update
+            uint8_t* gptr = region + LY::CODE_BASE + (qr * DV + 16 * cg) * IB / 8;
+            if constexpr (IB == 8) *reinterpret_cast<uint4*>(gptr) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            else *reinterpret_cast<uint2*>(gptr) = make_uint2(o4[0], o4[1]);
             if ((cg % LPB) == 0)
-                sm.reg[LY::META_BASE / 4 + qr * LY::NB + g] = uint32_t(sbits) | (uint32_t(zbits) << 16);
+                reinterpret_cast<uint32_t*>(region + LY::META_BASE)[qr * LY::NB + g] =
+                    uint32_t(sbits) | (uint32_t(zbits) << 16);
         }
-    }
-    __syncthreads();
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(sm.reg);
-        uint4* dst = reinterpret_cast<uint4*>(region);
-#pragma unroll
-        for (int i = tid; i < LY::REGION / 16; i += NT) dst[i] = src[i];
     }
 }
 

@@ -51,6 +51,15 @@ __device__ __forceinline__ void sr_draws8(uint64_t seed, uint32_t bh, uint64_t t
     for (int c = 0; c < 8; ++c) r16[c] = (c & 1) ? (ws[c >> 1] >> 16) : (ws[c >> 1] & 0xFFFFu);
 }
 
+// 16 bytes from global memory straight into LDS (no registers): lane l of the wavefront
+// writes bytes [16 l, 16 l + 16) after `wave_dst`, which must be the same for every lane
+// of the wavefront (the hardware takes it from a scalar register). The wavefront's
+// s_waitcnt vmcnt covers the write; a workgroup barrier after that wait publishes it.
+__device__ __forceinline__ void lds_load16(const void* src, void* wave_dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // float16 conversions. float64 -> float16 must round once, to nearest with ties to
 // even: a float64 -> float32 -> float16 chain of two nearest roundings can land on the
