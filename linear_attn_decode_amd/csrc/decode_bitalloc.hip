@@ -758,7 +758,7 @@ struct HaSmem {
     float red[2][HNW][DV];                      // u / p partials of the wavefronts
     float w[DV];
     float qk[2];
-    uint32_t reg[(kHaCodeMax + 2 * HGR * DV) / 4 + 4];   // staged codes, then the new Delta bits
+    alignas(16) uint32_t reg[(kHaCodeMax + 2 * HGR * DV) / 4 + 4];   // staged codes, then the new Delta bits
 };
 
 template <int B, bool SR>
@@ -773,17 +773,26 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
     const int cap = A.code_cap;
     const uint4* src = reinterpret_cast<const uint4*>(region);
 
-    uint4 pf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pf[i] = (tid + HNT * i < NVEC) ? src[tid + HNT * i] : make_uint4(0, 0, 0, 0);
-    const float vj = A.v[(size_t)head * DV + (tid & (DV - 1))];
-    const float beta = A.beta[head];
-
-    // per-row constants (wavefronts 0 and 1) and q . k
-    if (tid < DK) {
+    // Wavefronts 0 and 1 load the per-row inputs and the stored steps and fit bytes and
+    // build the tables (at a raised issue priority: the rest of the workgroup waits for
+    // them); wavefronts 2 and 3 copy the codes into LDS with global-to-LDS loads, so
+    // that neither pair's waits include the other's loads.
+    float vj = 0.f, beta = 0.f;
+    if (wave < 2) {
+        vj = A.v[(size_t)head * DV + tid];
+        beta = A.beta[head];
         const size_t rb = (size_t)head * DK + tid;
         const float kr = A.k[rb], qr = A.q[rb];
         const float sr = A.s_per_row ? A.s[rb] : A.s[head];
+        uint32_t dbits[4], fbyte[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = tid + 2 * 64 * i;
+            dbits[i] = reinterpret_cast<const uint16_t*>(region + cap)[t];
+            fbyte[i] = region[cap + 2 * HGR * DV + t];
+        }
+        __builtin_amdgcn_s_setprio(3);
+        // per-row constants and q . k
         if (A.est) ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, tid, sr, beta, kr);
         const float a = expf(-sr);
         sm.row[tid] = make_float4(a, kr * a, qr * a, kr);
@@ -797,21 +806,18 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
                            (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 32)) +
                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 48)));
         if (lane == 0) sm.qk[wave] = qsum;
-    }
-    // stored steps and fit fractions per (group, column): thread owns t and t + 256
+        // stored steps and fit fractions per (group, column): thread owns t = tid + 128 i
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = tid + HNT * i;
-        const float dold = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(region + cap)[t]);
-        const int fit = region[cap + 2 * HGR * DV + t] & 15;
-        sm.g[t] = make_float2(dold, -float(n) * dold);     // exact: 11 + 7 significant bits
-        sm.fn[t] = fn_of(fit, B);
-    }
-    {
-        uint4* dst = reinterpret_cast<uint4*>(sm.reg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tid + HNT * i < NVEC) dst[tid + HNT * i] = pf[i];
+        for (int i = 0; i < 4; ++i) {
+            const int t = tid + 2 * 64 * i;
+            const float dold = f16_bits_to_f32(dbits[i]);
+            sm.g[t] = make_float2(dold, -float(n) * dold);     // exact: 11 + 7 significant bits
+            sm.fn[t] = fn_of(int(fbyte[i] & 15u), B);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    } else {
+        // vectors i0 + lane of the codes, i0 = 64 (wave - 2) + 128 r (a scalar)
+        for (int i0 = 64 * (wave - 2); i0 < NVEC; i0 += 128) lds_load16(src + i0 + lane, &sm.reg[4 * i0]);
     }
     __syncthreads();
 
