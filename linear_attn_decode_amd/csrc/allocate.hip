@@ -186,8 +186,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     const int code_bytes = A.code_cap;         // Delta and meta follow the code area
     const int total = code_bytes + 3 * DK;
 
-    for (int i = tid; i * 16 < total; i += NT)
-        reinterpret_cast<uint4*>(sm.reg)[i] = reinterpret_cast<const uint4*>(region)[i];
+    // the region straight into LDS (global-to-LDS loads, all issued at once): vectors
+    // i0 + lane, i0 = 64 wave + 256 r (a scalar)
+    for (int i0 = 64 * wave; i0 * 16 < total; i0 += NT)
+        if ((i0 + lane) * 16 < total) lds_load16(reinterpret_cast<const uint4*>(region) + i0 + lane, &sm.reg[4 * i0]);
     if constexpr (STEP) {
         if (tid < DK) {
             const size_t rb = (size_t)head * DK + tid;
@@ -202,6 +204,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     __syncthreads();
     const uint8_t* bytes = reinterpret_cast<const uint8_t*>(sm.reg);
     if (wave == 0) {
+        // (the rest of the workgroup waits for this wavefront: raised issue priority)
+        __builtin_amdgcn_s_setprio(3);
         int wv[2], local = 0;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
@@ -236,6 +240,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         }
         sm.order[pos0] = 2 * lane;
         sm.order[pos1] = 2 * lane + 1;
+        __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
 
@@ -335,8 +340,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
     }
     __syncthreads();
 
-    // widths (one wavefront; lane l owns rows 2l and 2l+1)
+    // widths (one wavefront, at raised issue priority; lane l owns rows 2l and 2l+1)
     if (wave == 0) {
+        __builtin_amdgcn_s_setprio(3);
         const int r0 = 2 * lane, r1 = r0 + 1;
         const double R0 = sm.R[r0], R1 = sm.R[r1];
         // (the squares of float32 maxima cannot underflow in float64: some R > 0 iff sq > 0)
@@ -494,6 +500,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
         }
         sm.newoff[r0] = incl - local;
         sm.newoff[r1] = incl - local + b0 * (DV / 8);
+        __builtin_amdgcn_s_setprio(0);
     }
     if constexpr (COST) return;
     __syncthreads();
