@@ -268,7 +268,9 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     }
 
     // ---- w = beta (v - u), o = p + (q . k) w, H w (one wavefront) ----------------------
-    // (wavefront 0: u, w and H w; wavefront 1: p, in parallel; o after the barrier)
+    // (wavefront 0: u, w and H w; wavefront 1: p, in parallel; o after the barrier; the
+    // other two wait, so these two run at raised issue priority)
+    if (wave < 2) __builtin_amdgcn_s_setprio(3);
     if (wave == 0) {
         // (v and beta opaque until here, so that their conversions are not placed among
         // the loads at the start, where they would make the wavefront wait for them)
@@ -290,6 +292,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         sm.part[3][lane] = sm.part[1][lane] + pq0;
         sm.part[3][lane + 64] = sm.part[1][lane + 64] + pq1;
     }
+    if (wave < 2) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     if (tid >= NT - DV) {
         const int j = tid - (NT - DV);
