@@ -201,6 +201,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) al
                 ema_fold_row(A.est + (size_t)head * est_stride(DK), DK, tid, sv, A.beta[head], fk[tid]);
         }
     }
+    lds_loads_wait();
     __syncthreads();
     const uint8_t* bytes = reinterpret_cast<const uint8_t*>(sm.reg);
     if (wave == 0) {

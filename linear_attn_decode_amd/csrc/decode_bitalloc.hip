@@ -500,6 +500,7 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
             copy(code_bytes / 16, code_bytes / 16 + kMetaVec);
             copy(nmin, ncode);
         }
+        lds_loads_wait();
     }
 
     // ---- per-row tables: wavefronts 0 and 1 own rows lane and lane + 64 ---------------
@@ -818,6 +819,7 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
     } else {
         // vectors i0 + lane of the codes, i0 = 64 (wave - 2) + 128 r (a scalar)
         for (int i0 = 64 * (wave - 2); i0 < NVEC; i0 += 128) lds_load16(src + i0 + lane, &sm.reg[4 * i0]);
+        lds_loads_wait();
     }
     __syncthreads();
 

@@ -174,6 +174,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         const uint4* src = reinterpret_cast<const uint4*>(region);
         for (int i0 = 64 * (wave - 2); i0 < LY::REGION / 16; i0 += 128)
             if (i0 + lane < LY::REGION / 16) lds_load16(src + i0 + lane, &sm.reg[4 * i0]);
+        lds_loads_wait();
     }
     __syncthreads();
     // The contraction over rows folds each INT8 block's step into the row weights:

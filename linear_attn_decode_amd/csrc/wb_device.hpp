@@ -53,12 +53,15 @@ __device__ __forceinline__ void sr_draws8(uint64_t seed, uint32_t bh, uint64_t t
 
 // 16 bytes from global memory straight into LDS (no registers): lane l of the wavefront
 // writes bytes [16 l, 16 l + 16) after `wave_dst`, which must be the same for every lane
-// of the wavefront (the hardware takes it from a scalar register). The wavefront's
-// s_waitcnt vmcnt covers the write; a workgroup barrier after that wait publishes it.
+// of the wavefront (the hardware takes it from a scalar register). The write completes
+// with the wavefront's vector-memory counter; the compiler does not order later LDS
+// reads after it, so a wavefront that issued such loads calls lds_loads_wait() before
+// the workgroup barrier that publishes the data.
 __device__ __forceinline__ void lds_load16(const void* src, void* wave_dst) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
 }
+__device__ __forceinline__ void lds_loads_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // float16 conversions. float64 -> float16 must round once, to nearest with ties to
