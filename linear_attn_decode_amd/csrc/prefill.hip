@@ -511,12 +511,19 @@ __global__ void __launch_bounds__(NT) prefill_kernel(const PrefillArgs P) {
                         }
                         mn = fmin(mn, mov_dpp_f64<0xB1>(mn));     // the pair's other half
                         mx = fmax(mx, mov_dpp_f64<0xB1>(mx));
-                        const uint16_t sb = f64_to_f16_bits(fmax(mx - mn, 0.0) / 255.0);
+                        // (a product with 1/255 in place of the quotient: the two differ by
+                        // at most one float64 unit, which moves a float16 rounding only at
+                        // a midpoint)
+                        const uint16_t sb = f64_to_f16_bits(fmax(mx - mn, 0.0) * (1.0 / 255.0));
                         const uint16_t zb = f64_to_f16_bits(mn);
                         const double sc = f16d(sb), ze = f16d(zb);
                         uint32_t cw4[4] = {0, 0, 0, 0};
                         if (sc > 0.0) {
-                            const double inv = 1.0 / sc;
+                            // reciprocal of the step refined by one Newton step (within a
+                            // float64 unit of 1 / sc: a level moves only within ~1e-13 of a
+                            // half-integer)
+                            double inv = __builtin_amdgcn_rcp(sc);
+                            inv = fma(fma(-sc, inv, 1.0), inv, inv);
                             constexpr double kM = 6755399441055744.0;          // 1.5 * 2^52
                             const int mhi = int(uint64_t(__double_as_longlong(kM)) >> 32);
 #pragma unroll
