@@ -7,16 +7,20 @@
 //   * rows are visited in order of increasing width, so the 4 rows a wavefront handles
 //     per step nearly always share one width; that width is read into a scalar register
 //     and the unpack / pack code is chosen by a scalar branch and specialised per width
-//     (static bit positions); a group of mixed widths is walked one width at a time;
+//     (static bit positions); a group of mixed widths takes a generic per-lane path;
 //   * eight wavefronts per head; a lane holds 4 rows x 8 columns of the state (32
-//     values, which keeps the register count low enough for 6 wavefronts per SIMD), and
-//     the u / p partial sums of a wavefront are combined in registers by lane swaps
-//     before one LDS store;
+//     values as floats, 64 VGPRs: 8 wavefronts per SIMD);
+//   * six wavefronts copy the region into LDS with global-to-LDS loads while the other
+//     two load the rows' inputs and build the per-row tables, at a raised issue
+//     priority (the workgroup waits for them);
 //   * the sort, the byte offsets of the rows and their ranks come from wavefront ballots
 //     (each of the two wavefronts that build the tables reads the widths of all 128
 //     rows, so no cross-wave scan is needed);
-//   * per-row constants (decayed step, offset term, k_i, q_i, f_i / n_i, rounding
-//     constants, byte offset, width) sit in LDS tables indexed by sorted position;
+//   * per-row constants (decayed step, offset term, k_i, q_i, f_i / n_i, byte offset,
+//     width) sit in LDS tables indexed by sorted position;
+//   * u and p run on the bfloat16 matrix cores with exact operands (the integer codes,
+//     and the row weights split into three bfloat16 limbs); a wavefront's partial sums
+//     go to LDS once;
 //   * dequantize + decay is one FMA: a_i Delta_i (code - n_i) = code * (a_i Delta_i) +
 //     (-n_i a_i Delta_i);
 //   * rounding to the nearest level adds 1.5 * 2^23 in the same FMA as the scaling
@@ -25,7 +29,7 @@
 //     constant high bits (those of magic - n_i, so the field is level + n_i) are removed
 //     once per 32-bit word;
 //   * row maxima use DPP integer max on the bits of |x| (ordered like the values);
-//   * the packed codes of a lane (8 elements = b bytes) go to a staging copy of the
+//   * the packed codes of a lane (8 elements = b bytes) go to the staged copy of the
 //     region in LDS at their final byte offset, then the region is written to HBM with
 //     16-byte stores.
 // Two more instantiations widen it: the layer-wise budget (the code area holds every
