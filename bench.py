@@ -398,8 +398,9 @@ def main():
                          "(no timing, no JSON result line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported on this build "
-              f"(every head state is independent, see the design notes on sharding).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the write-back runs on one GPU's "
+              f"share of the heads (every head state is independent, so several GPUs would each take a "
+              f"disjoint set of (sequence, head) pairs with no communication).", file=sys.stderr)
         sys.exit(2)
     w = WORKLOADS[args.workload]
     if args.profile_steps:
