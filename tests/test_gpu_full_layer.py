@@ -2,9 +2,10 @@
 
 The mixed layout at B = 256, H = 32 (round to nearest), the decay-aware per-row widths
 at the same shape (round to nearest and Philox stochastic rounding, after an allocation
-pass; and under the layer-wise budget), the Hadamard INT8 layout at B = 64, H = 16 with
-per-head decay and the per-head allocation unit at that shape, in the launch
-configurations the benchmark times: every head state of the layer is compared, not a
+pass; under the layer-wise budget; with one-bit rows allowed), the Hadamard INT8 layout
+and its INT4 tier at B = 64, H = 16 with per-head decay and the per-head allocation unit
+at that shape (round to nearest and stochastic rounding), in the launch configurations
+the benchmark times: every head state of the layer is compared, not a
 sample, so that the parity bound (codes bit-equal except at most 1e-4 of the elements,
 each one step apart and within 1e-5 of a step of the boundary; outputs within 1e-4
 relative L2 per head) is checked at scale. The oracle runs in 16 spawned processes over
@@ -40,6 +41,9 @@ CASES = {
     "bitalloc-layer-rtn": dict(kind=L.BITALLOC, mode="rtn", B=256, H=32, per_row=True, kw=dict(budget="layer")),
     "had-int8-rtn-gdn": dict(kind=L.HAD_INT8, mode="rtn", B=64, H=16, per_row=False, kw=dict(block=128)),
     "headalloc-rtn-gdn": dict(kind=L.HEADALLOC, mode="rtn", B=64, H=16, per_row=False, kw={}),
+    "had-int4-rtn-gdn": dict(kind=L.HAD_INT8, mode="rtn", B=64, H=16, per_row=False, kw=dict(block=128, int_bits=4)),
+    "bitalloc-1bit-rtn": dict(kind=L.BITALLOC, mode="rtn", B=256, H=32, per_row=True, kw=dict(bmin=1)),
+    "headalloc-sr-gdn": dict(kind=L.HEADALLOC, mode="sr", B=64, H=16, per_row=False, kw={}),
 }
 
 
