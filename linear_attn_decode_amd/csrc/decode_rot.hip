@@ -57,10 +57,15 @@ struct RotSmem {
     double2 kqs[LY::NQ * LY::NB];    // (k a step, q a step) of every INT8 block
     double zsum[4][LY::NB][2];       // per wavefront and block column: (sum k a offset, sum q a offset)
     static constexpr int ZW = (LY::NQ * LY::NB + 63) / 64 < 4 ? (LY::NQ * LY::NB + 63) / 64 : 4;
-    double w[DV], hw[DV];
+    // w and H w, 16-value groups padded to 18 (the update's lanes read group cg at 144 cg
+    // bytes: eight lanes of one pass hit eight different bank quadruples)
+    double w[DV / 16 * 18], hw[DV / 16 * 18];
     double qk[2];
     uint32_t reg[LY::REGION / 4];
 };
+
+// index of value j in a 16-value-group array padded to 18 per group
+__device__ __forceinline__ int pad18(int j) { return j + 2 * (j >> 4); }
 
 __device__ __forceinline__ double f16_to_f64(uint32_t bits) { return double(f16_bits_to_f32(bits)); }
 
@@ -281,12 +286,12 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         const double u0 = sm.part[0][lane] + uq0, u1 = sm.part[0][lane + 64] + uq1;
         const double w0 = double(beta_in) * (double(v_lo) - u0);
         const double w1 = double(beta_in) * (double(v_hi) - u1);
-        sm.w[lane] = w0;
-        sm.w[lane + 64] = w1;
+        sm.w[pad18(lane)] = w0;
+        sm.w[pad18(lane + 64)] = w1;
         double r0 = w0, r1 = w1;
         wht128(r0, r1, lane);
-        sm.hw[lane] = r0;
-        sm.hw[lane + 64] = r1;
+        sm.hw[pad18(lane)] = r0;
+        sm.hw[pad18(lane + 64)] = r1;
     } else if (wave == 1) {
         double pq0 = sm.part[3][lane], pq1 = sm.part[3][lane + 64];
         wht128(pq0, pq1, lane);
@@ -297,7 +302,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     __syncthreads();
     if (tid >= NT - DV) {
         const int j = tid - (NT - DV);
-        A.o[(size_t)head * DV + j] = float(sm.part[3][j] + (sm.qk[0] + sm.qk[1]) * sm.w[j]);
+        A.o[(size_t)head * DV + j] = float(sm.part[3][j] + (sm.qk[0] + sm.qk[1]) * sm.w[pad18(j)]);
     }
 
     // ---- update and requantize in place (lane = 4 rows x 16 columns) -------------------
@@ -308,7 +313,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         constexpr int LPB = BLOCK / 16;                     // lanes per block
         double hwv[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) hwv[c] = sm.hw[16 * cg + c];
+        for (int c = 0; c < 16; ++c) hwv[c] = sm.hw[18 * cg + c];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int p = rg + 32 * m;
@@ -325,7 +330,7 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
                         const double x = f16_to_f64((w4[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu);
-                        const double xn = fma(ak.x, x, ak.y * sm.w[16 * cg + 8 * hv + c]);
+                        const double xn = fma(ak.x, x, ak.y * sm.w[18 * cg + 8 * hv + c]);
                         o4[c >> 1] |= uint32_t(f64_to_f16_bits(xn)) << ((c & 1) * 16);
                     }
                     // straight to the stored region (nothing reads the staged copy again)
