@@ -7,14 +7,16 @@
 // Same computation as the generic decode kernel (rotated domain: u = sum_P k a S +
 // H sum_Q k a Y, w = beta (v - u), S_P' = a S_P + k w, Y_Q' = a Y_Q + k (H w),
 // o = sum_P q a S + H sum_Q q a Y + (q . k) w), organised for throughput:
-//   * the region is staged in LDS by global-to-LDS 16-byte loads (two wavefronts; the
-//     other two build the per-row tables meanwhile); each updated row is written back to
-//     HBM by the lanes that requantized it, with 16-byte stores;
+//   * the region is staged in LDS by global-to-LDS 16-byte loads (two wavefronts, or
+//     one where the other forms H v; the remaining two build the per-row tables
+//     meanwhile); each updated row is written back to HBM by the lanes that requantized
+//     it, with 16-byte stores;
 //   * u and p (contractions over rows) run column-parallel: thread (j, half) walks
 //     half of the rows of column j, so the only cross-thread step is adding two
 //     halves; the float64 step and offset of every INT8 block are tabulated once;
-//   * the three 128-point transforms run on wavefronts (H uQ then H w on one, H pQ on
-//     another);
+//   * the 128-point transforms run on wavefronts (H uQ then H w on one, H pQ on
+//     another); without float16 rows u = H uQ, so H w = beta (H v - uQ) needs no
+//     transform after the contraction (H H = I) and H v is formed during the loads;
 //   * the update and the requantization run row-parallel (lane = 4 rows x 16 columns,
 //     so a block of 32 values spans 2 lanes) with float64 element arithmetic and the
 //     block minimum / maximum by DPP;
@@ -60,6 +62,7 @@ struct RotSmem {
     // w and H w, 16-value groups padded to 18 (the update's lanes read group cg at 144 cg
     // bytes: eight lanes of one pass hit eight different bank quadruples)
     double w[DV / 16 * 18], hw[DV / 16 * 18];
+    double hv[KHI == 0 ? DV : 1];    // H v (layouts without float16 rows)
     double qk[2];
     uint32_t reg[LY::REGION / 4];
 };
@@ -174,10 +177,20 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         pq = wave_sum_f64<1>(pq);
         if (lane == 0) sm.qk[wave] = pq;
         __builtin_amdgcn_s_setprio(0);
+    } else if (KHI == 0 && wave == 2) {
+        // Without float16 rows u = H uQ, so H w = beta (H v - uQ) (H H = I): H v is formed
+        // here, while the region is in flight, and the vector phase needs one transform
+        // (of uQ) on its critical path instead of two
+        double x = double(A.v[(size_t)head * DV + lane]), y = double(A.v[(size_t)head * DV + lane + 64]);
+        wht128(x, y, lane);
+        sm.hv[lane] = x;
+        sm.hv[lane + 64] = y;
     } else {
-        // vectors i0 + lane of the region, i0 = 64 (wave - 2) + 128 r (a scalar)
+        // vectors i0 + lane of the region, i0 = 64 (wave - c0) + 64 nc r (a scalar): both
+        // wavefronts copy, or wavefront 3 alone where wavefront 2 forms H v
+        constexpr int c0 = KHI == 0 ? 3 : 2, nc = 4 - c0;
         const uint4* src = reinterpret_cast<const uint4*>(region);
-        for (int i0 = 64 * (wave - 2); i0 < LY::REGION / 16; i0 += 128)
+        for (int i0 = 64 * (wave - c0); i0 < LY::REGION / 16; i0 += 64 * nc)
             if (i0 + lane < LY::REGION / 16) lds_load16(src + i0 + lane, &sm.reg[4 * i0]);
         lds_loads_wait();
     }
@@ -274,24 +287,31 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     }
 
     // ---- w = beta (v - u), o = p + (q . k) w, H w (one wavefront) ----------------------
-    // (wavefront 0: u, w and H w; wavefront 1: p, in parallel; o after the barrier; the
-    // other two wait, so these two run at raised issue priority)
+    // (wavefront 0: H w (from H v, without float16 rows), u, w and else H w; wavefront 1:
+    // p, in parallel; o after the barrier; the other two wait, so these two run at raised
+    // issue priority)
     if (wave < 2) __builtin_amdgcn_s_setprio(3);
     if (wave == 0) {
         // (v and beta opaque until here, so that their conversions are not placed among
         // the loads at the start, where they would make the wavefront wait for them)
         asm volatile("" : "+v"(v_lo), "+v"(v_hi), "+v"(beta_in));
         double uq0 = sm.part[2][lane], uq1 = sm.part[2][lane + 64];
+        if constexpr (KHI == 0) {
+            sm.hw[pad18(lane)] = double(beta_in) * (sm.hv[lane] - uq0);
+            sm.hw[pad18(lane + 64)] = double(beta_in) * (sm.hv[lane + 64] - uq1);
+        }
         wht128(uq0, uq1, lane);
         const double u0 = sm.part[0][lane] + uq0, u1 = sm.part[0][lane + 64] + uq1;
         const double w0 = double(beta_in) * (double(v_lo) - u0);
         const double w1 = double(beta_in) * (double(v_hi) - u1);
         sm.w[pad18(lane)] = w0;
         sm.w[pad18(lane + 64)] = w1;
-        double r0 = w0, r1 = w1;
-        wht128(r0, r1, lane);
-        sm.hw[pad18(lane)] = r0;
-        sm.hw[pad18(lane + 64)] = r1;
+        if constexpr (KHI > 0) {
+            double r0 = w0, r1 = w1;
+            wht128(r0, r1, lane);
+            sm.hw[pad18(lane)] = r0;
+            sm.hw[pad18(lane + 64)] = r1;
+        }
     } else if (wave == 1) {
         double pq0 = sm.part[3][lane], pq1 = sm.part[3][lane + 64];
         wht128(pq0, pq1, lane);
