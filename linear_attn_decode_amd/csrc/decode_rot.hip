@@ -26,6 +26,8 @@
 // Float64 is used wherever a stored code or float16 value is decided: the codes must
 // agree with a float64 evaluation to within 1e-5 of a step, and float16 rows to within
 // 1e-5 of a float16 spacing.
+#include <utility>
+
 #include "wb_device.hpp"
 #include "wb_kernels.hpp"
 
@@ -66,6 +68,32 @@ struct RotSmem {
     double qk[2];
     uint32_t reg[LY::REGION / 4];
 };
+
+// acc += (w of lane K of this lane's 16-lane row) * c: a float64 multiply-add whose first
+// operand is broadcast within each row of 16 lanes (DPP row_newbcast). A DPP source must
+// not have been written by a vector instruction in the two preceding wait states: the
+// weights are read from LDS once, well before, and each group of 16 starts with a nop.
+// (Not volatile: the statement has no effect beyond its output, so the compiler may
+// schedule the code loads around it.)
+template <int K>
+__device__ __forceinline__ void fmac_rowbcast(double& acc, double w, double c) {
+    if constexpr (K == 0)
+        asm("s_nop 1\n\tv_fmac_f64_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf"
+            : "+v"(acc) : "v"(w), "v"(c));
+    else
+        asm("v_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(w), "v"(c),
+            "n"(K));
+}
+
+// f(std::integral_constant<int, 0>) .. f(std::integral_constant<int, N - 1>)
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 // index of value j in a 16-value-group array padded to 18 per group
 __device__ __forceinline__ int pad18(int j) { return j + 2 * (j >> 4); }
@@ -240,26 +268,48 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         }
         const int g = j / BLOCK;
         {
-            // two interleaved partial sums per quantity (shorter dependency chains)
-            double uQ1 = 0.0, pQ1 = 0.0;
-            static_assert(LY::NQ % 4 == 0, "rows are taken two at a time per half");
-#pragma unroll 4
-            for (int qr = half * (LY::NQ / 2); qr < (half + 1) * (LY::NQ / 2); qr += 2) {
-                double code0, code1;
-                if constexpr (IB == 8) {
-                    code0 = double(lb[LY::CODE_BASE + qr * DV + j]);
-                    code1 = double(lb[LY::CODE_BASE + (qr + 1) * DV + j]);
-                } else {
-                    code0 = double((lb[LY::CODE_BASE + (qr * DV + j) / 2] >> ((j & 1) * 4)) & 15u);
-                    code1 = double((lb[LY::CODE_BASE + ((qr + 1) * DV + j) / 2] >> ((j & 1) * 4)) & 15u);
-                }
-                const double2 c0 = sm.kqs[qr * LY::NB + g];         // (k a step, q a step)
-                const double2 c1 = sm.kqs[(qr + 1) * LY::NB + g];
-                uQ = fma(c0.x, code0, uQ);
-                pQ = fma(c0.y, code0, pQ);
-                uQ1 = fma(c1.x, code1, uQ1);
-                pQ1 = fma(c1.y, code1, pQ1);
+            // The row weights come from registers, not from LDS: lane l holds the
+            // (k a step, q a step) of rows 16 i + l % 16 of its half, and row 16 i + K is
+            // multiplied with the weight broadcast from lane K of each 16-lane row (the 16
+            // lanes of a row are 16 columns of one block). Two partial sums per quantity
+            // (even and odd rows) keep the dependency chains short.
+            constexpr int RH = LY::NQ / 2;                     // rows per half
+            constexpr int NG = (RH + 15) / 16;                 // groups of 16 rows
+            static_assert(RH % 2 == 0, "rows are taken two at a time per half");
+            const int qb = half * RH;
+            double2 wk[NG];
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int r = 16 * i + (lane & 15);
+                wk[i] = r < RH ? sm.kqs[(qb + r) * LY::NB + g] : make_double2(0.0, 0.0);
             }
+            double uQ1 = 0.0, pQ1 = 0.0;
+            auto code_of = [&](int qr) -> uint32_t {
+                if constexpr (IB == 8) return lb[LY::CODE_BASE + qr * DV + j];
+                else return (lb[LY::CODE_BASE + (qr * DV + j) / 2] >> ((j & 1) * 4)) & 15u;
+            };
+            static_for<NG>([&](auto gi) {
+                constexpr int i = decltype(gi)::value;
+                // the group's 16 codes are requested before the first multiply-add
+                uint32_t cb[16];
+                static_for<16>([&](auto ki) {
+                    constexpr int K = decltype(ki)::value;
+                    if constexpr (16 * i + K < RH) cb[K] = code_of(qb + 16 * i + K);
+                });
+                static_for<16>([&](auto ki) {
+                    constexpr int K = decltype(ki)::value;
+                    if constexpr (16 * i + K < RH) {
+                        const double code = double(cb[K]);
+                        if constexpr (K % 2 == 0) {
+                            fmac_rowbcast<K>(uQ, wk[i].x, code);
+                            fmac_rowbcast<K>(pQ, wk[i].y, code);
+                        } else {
+                            fmac_rowbcast<K>(uQ1, wk[i].x, code);
+                            fmac_rowbcast<K>(pQ1, wk[i].y, code);
+                        }
+                    }
+                });
+            });
             uQ += uQ1;
             pQ += pQ1;
         }
