@@ -257,14 +257,19 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
         const int j = tid & (DV - 1), half = tid >> 7;
         double uP = 0.0, pP = 0.0, uQ = 0.0, pQ = 0.0;
         if constexpr (KHI > 0) {
+            // the float16 rows of this half, weights broadcast from registers as below
+            static_assert(KHI / 2 <= 16, "one group of float16 rows per half");
             const uint16_t* f16rows = reinterpret_cast<const uint16_t*>(lb);
-#pragma unroll 4
-            for (int p = half * (KHI / 2); p < (half + 1) * (KHI / 2); ++p) {
-                const double x = f16_to_f64(f16rows[p * DV + j]);
-                const double2 c = sm.kqh[p];
-                uP = fma(c.x, x, uP);
-                pP = fma(c.y, x, pP);
-            }
+            const int pb = half * (KHI / 2);
+            const double2 wh = (lane & 15) < KHI / 2 ? sm.kqh[pb + (lane & 15)] : make_double2(0.0, 0.0);
+            uint32_t hb[KHI / 2];
+            static_for<KHI / 2>([&](auto ki) { hb[decltype(ki)::value] = f16rows[(pb + decltype(ki)::value) * DV + j]; });
+            static_for<KHI / 2>([&](auto ki) {
+                constexpr int K = decltype(ki)::value;
+                const double x = f16_to_f64(hb[K]);
+                fmac_rowbcast<K>(uP, wh.x, x);
+                fmac_rowbcast<K>(pP, wh.y, x);
+            });
         }
         const int g = j / BLOCK;
         {
