@@ -159,7 +159,8 @@ struct InvCol {
 // level in [-n, n]; the stored field is level + n, n = 2^(B-1) - 1, and 0 / 1 for B = 1),
 // packed at byte `boff` of the staging copy (B bytes).
 template <int B>
-__device__ __forceinline__ void store8(uint32_t* reg, int boff, const uint32_t y[8]) {
+__device__ __forceinline__ void store8(uint32_t* reg, int boff_i, const uint32_t y[8]) {
+    const uint32_t boff = uint32_t(boff_i);     // (unsigned: a scalar base plus a 32-bit lane offset)
     // bits of 1.5 * 2^23 - n: subtracting them leaves level + n
     constexpr uint32_t base = kMagicBits - uint32_t(B == 1 ? 0 : (1 << (B - 1)) - 1);
     if constexpr (B == 1) {
@@ -209,7 +210,7 @@ __device__ __forceinline__ void store8(uint32_t* reg, int boff, const uint32_t y
         hw[2] = uint16_t(w1);
     } else {
 #pragma unroll
-        for (int i = 0; i < B; ++i) bytes[boff + i] = uint8_t(i < 4 ? (w0 >> (8 * i)) : (w1 >> (8 * (i - 4))));
+        for (int i = 0; i < B; ++i) (bytes + boff)[i] = uint8_t(i < 4 ? (w0 >> (8 * i)) : (w1 >> (8 * (i - 4))));
     }
 }
 
@@ -286,10 +287,10 @@ __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const
         }
         fld |= uint64_t(code) << __umul24(uint32_t(c), uint32_t(bw));
     }
-    uint8_t* bytes = reinterpret_cast<uint8_t*>(reg);
+    uint8_t* bytes = reinterpret_cast<uint8_t*>(reg) + uint32_t(boff);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        if (i < bw) bytes[boff + i] = uint8_t(fld >> (8 * i));
+        if (i < bw) bytes[i] = uint8_t(fld >> (8 * i));
 }
 
 // Unpack / pack with the width held per lane. When the lanes share one width (rows
@@ -640,7 +641,10 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
         wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
         wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
     }
-    uint16_t* dout = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(reg) + code_bytes);
+    // the new codes and steps go straight to the region in HBM (the rows keep their
+    // offsets: a decode step changes no width), each lane storing what it rounded
+    uint32_t* gout = reinterpret_cast<uint32_t*>(region);
+    uint16_t* dout = reinterpret_cast<uint16_t*>(region + code_bytes);
     // update and in-lane maxima of |x| of the lane's rows, then the row maxima over the
     // 16 lanes of each row reduced and scattered (each lane ends with one of the 4 rows),
     // so that every step is derived once per 4 lanes and handed back by quad broadcasts
@@ -693,22 +697,7 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
         const TabB* tb = &tbw[NG * m + rq];
         uint32_t r16[8];
         if constexpr (SR) sr_draws8(A.seed, uint32_t(head), A.t, int(tb->row), cg, r16);
-        pack_rows<OB, SR>(reg, boff_of(loc_of(m)), bus[m], &tb->bw, x[m], inv[m], r16);
-    }
-    __syncthreads();
-    {
-        uint4* dst = reinterpret_cast<uint4*>(region);
-        const uint4* lsrc = reinterpret_cast<const uint4*>(reg);
-        if constexpr (!LAYER) {
-            const int out_vec = (code_bytes + 2 * DK) / 16;
-            for (int i = tid; i < out_vec; i += NT) dst[i] = lsrc[i];
-        } else {
-            // the codes in use, then Delta (the tail and the width / fit bytes are unchanged)
-            for (int i = tid; i < ncode + 2 * DK / 16; i += NT) {
-                const int vi = i < ncode ? i : code_bytes / 16 + (i - ncode);
-                dst[vi] = lsrc[vi];
-            }
-        }
+        pack_rows<OB, SR>(gout, boff_of(loc_of(m)), bus[m], &tb->bw, x[m], inv[m], r16);
     }
 }
 
