@@ -752,7 +752,7 @@ struct HaSmem {
     float red[2][HNW][DV];                      // u / p partials of the wavefronts
     float w[DV];
     float qk[2];
-    alignas(16) uint32_t reg[(kHaCodeMax + 2 * HGR * DV) / 4 + 4];   // staged codes, then the new Delta bits
+    alignas(16) uint32_t reg[kHaCodeMax / 4 + 4];   // staged codes (+16 bytes a row's 3-word read may touch)
 };
 
 template <int B, bool SR>
@@ -919,7 +919,7 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
         if (rq == 1) { R0 = mx[2]; R1 = mx[3]; }
         if (rq == 2) { R0 = mx[4]; R1 = mx[5]; }
         if (rq == 3) { R0 = mx[6]; R1 = mx[7]; }
-        uint16_t* dnew = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(sm.reg) + kHaCodeMax);
+        uint16_t* dnew = reinterpret_cast<uint16_t*>(region + cap);     // straight to HBM
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int t = wave * DV + 8 * cg + 2 * rq + e;
@@ -933,7 +933,8 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
     }
     __syncthreads();
 
-    // ---- round to nearest on each column's grid and pack into the staging copy ---------
+    // ---- round on each column's grid and pack; each lane stores its codes in HBM --------
+    uint32_t* gout = reinterpret_cast<uint32_t*>(region);
     float gi[8];
     {
         const float4 i0 = *reinterpret_cast<const float4*>(&sm.ginv[wave * DV + 8 * cg]);
@@ -950,23 +951,12 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
             sr_draws8(A.seed, uint32_t(head), A.t, row0 + m, cg, r16);
 #pragma unroll
             for (int c = 0; c < 8; ++c) y[c] = sr_level(x[m][c], gi[c], B, r16[c]);
-            store8<B>(sm.reg, boff, y);
+            store8<B>(gout, boff, y);
         } else {
-            pack8<B>(sm.reg, boff, x[m], InvCol{gi});
+            pack8<B>(gout, boff, x[m], InvCol{gi});
         }
     }
-    __syncthreads();
-
-    // ---- the codes, then the new steps (the fit bytes and the width byte are unchanged)
-    {
-        uint4* dst = reinterpret_cast<uint4*>(region);
-        const uint4* ls = reinterpret_cast<const uint4*>(sm.reg);
-        constexpr int NOUT = NVEC + 2 * HGR * DV / 16;
-        for (int i = tid; i < NOUT; i += HNT) {
-            if (i < NVEC) dst[i] = ls[i];
-            else dst[cap / 16 + (i - NVEC)] = ls[kHaCodeMax / 16 + (i - NVEC)];
-        }
-    }
+    // (the fit bytes and the width byte are unchanged)
 }
 
 template <bool SR>
