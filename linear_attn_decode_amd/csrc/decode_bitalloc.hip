@@ -29,12 +29,12 @@
 //     constant high bits (those of magic - n_i, so the field is level + n_i) are removed
 //     once per 32-bit word;
 //   * row maxima use DPP integer max on the bits of |x| (ordered like the values);
-//   * the packed codes of a lane (8 elements = b bytes) go to the staged copy of the
-//     region in LDS at their final byte offset, then the region is written to HBM with
-//     16-byte stores.
+//   * the packed codes of a lane (8 elements = b bytes) and each row's new Delta go
+//     straight to the region in HBM at their final byte offsets (a decode step changes
+//     no width, so rows keep their offsets), with no staging copy or final barrier.
 // Two more instantiations widen it: the layer-wise budget (the code area holds every
 // row at b_max; the widths are read first and only the codes in use are staged and
-// written back, so the zero tail is never touched) and one-bit rows (the two levels
+// stored, so the zero tail is never touched) and one-bit rows (the two levels
 // -Delta, +Delta: the code is the sign, Delta = f16(mean |x|) from a row sum).
 // Layout citations: [LBRS] "State bit allocation", "Levels and storage".
 #include "wb_device.hpp"
@@ -157,7 +157,7 @@ struct InvCol {
 
 // Write 8 codes of `B` bits, given in magic-number form (the bits of 1.5 * 2^23 + level,
 // level in [-n, n]; the stored field is level + n, n = 2^(B-1) - 1, and 0 / 1 for B = 1),
-// packed at byte `boff` of the staging copy (B bytes).
+// packed at byte `boff` of `reg` (B bytes; the region in HBM, or a staging copy in LDS).
 template <int B>
 __device__ __forceinline__ void store8(uint32_t* reg, int boff_i, const uint32_t y[8]) {
     const uint32_t boff = uint32_t(boff_i);     // (unsigned: a scalar base plus a 32-bit lane offset)
@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
         A.o[(size_t)head * DV + j] = __builtin_fmaf(qk, sm.w[j], pj);
     }
 
-    // ---- update and requantize into the staging copy -----------------------------------
+    // ---- update, requantize and store ---------------------------------------------------
     float wv[8];
     {
         const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[8 * cg]);
