@@ -157,12 +157,13 @@ struct InvCol {
 
 // Write 8 codes of `B` bits, given in magic-number form (the bits of 1.5 * 2^23 + level,
 // level in [-n, n]; the stored field is level + n, n = 2^(B-1) - 1, and 0 / 1 for B = 1),
-// packed at byte `boff` of `reg` (B bytes; the region in HBM, or a staging copy in LDS).
-template <int B>
+// or, with FIELD, as the stored fields themselves, packed at byte `boff` of `reg` (B bytes;
+// the region in HBM, or a staging copy in LDS).
+template <int B, bool FIELD = false>
 __device__ __forceinline__ void store8(uint32_t* reg, int boff_i, const uint32_t y[8]) {
     const uint32_t boff = uint32_t(boff_i);     // (unsigned: a scalar base plus a 32-bit lane offset)
     // bits of 1.5 * 2^23 - n: subtracting them leaves level + n
-    constexpr uint32_t base = kMagicBits - uint32_t(B == 1 ? 0 : (1 << (B - 1)) - 1);
+    constexpr uint32_t base = FIELD ? 0u : kMagicBits - uint32_t(B == 1 ? 0 : (1 << (B - 1)) - 1);
     if constexpr (B == 1) {
         uint32_t w = 0;
 #pragma unroll
@@ -248,12 +249,38 @@ __device__ __forceinline__ uint32_t sr_level(float x, float inv, int bw, uint32_
     return __float_as_uint(kMagic + k);
 }
 
+// The same rounding for B >= 2 bits in integer form, returning the stored field level + n.
+// With tau = x / Delta, F = floor(tau) and g = frac(tau) 2^16, a 16-bit integer draw u has
+// u < g exactly when u < ceil(g), so floor(tau) + [u < g] = F + [ceil(g) + 2^16 - 1 - u >=
+// 2^16], which is floor((ceil(tau 2^16) + 2^16 - 1 - u) / 2^16) because ceil(tau 2^16) =
+// F 2^16 + ceil(g). tau 2^16 is the rounded product scaled by a power of two (exact), its
+// ceiling is minus one floor conversion of x * (-2^16 / Delta) (`ninv16`), and the field
+// comes out of one arithmetic shift, n 2^16 added before it, clamped to [0, 2n]. A zero
+// step (ninv16 = 0) gives the field n, level 0.
+__device__ __forceinline__ int cvt_floor_i32(float v) {
+    int r;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ uint32_t sr_field_int(float x, float ninv16, int n, uint32_t r16) {
+    const int z = cvt_floor_i32(x * ninv16);                     // -ceil(tau 2^16)
+    const int l = ((n << 16) + 65535 - z - int(r16)) >> 16;      // level + n
+    return uint32_t(min(max(l, 0), 2 * n));
+}
+// Either form for one element of a B-bit row (B = 1: the one-bit grid of sr_level).
+template <int B>
+__device__ __forceinline__ uint32_t sr_field(float x, float inv, float ninv16, uint32_t r16) {
+    if constexpr (B == 1) return sr_level(x, inv, 1, r16) - kMagicBits;
+    else return sr_field_int(x, ninv16, (1 << (B - 1)) - 1, r16);
+}
+
 template <int B>
 __device__ __forceinline__ void pack8_sr(uint32_t* reg, int boff, const float x[8], float inv, const uint32_t r16[8]) {
+    const float ninv16 = inv * -65536.f;
     uint32_t y[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) y[c] = sr_level(x[c], inv, B, r16[c]);
-    store8<B>(reg, boff, y);
+    for (int c = 0; c < 8; ++c) y[c] = sr_field<B>(x[c], inv, ninv16, r16[c]);
+    store8<B, true>(reg, boff, y);
 }
 
 // Generic unpack / pack for a per-lane width (a group of rows of mixed widths).
@@ -278,7 +305,8 @@ __device__ __forceinline__ void pack8_any(uint32_t* reg, int boff, int bw, const
     for (int c = 0; c < 8; ++c) {
         uint32_t code;
         if constexpr (SR) {
-            code = sr_level(x[c], inv, bw, r16[c]) - base;
+            code = (OB && bw == 1) ? sr_level(x[c], inv, 1, r16[c]) - kMagicBits
+                                   : sr_field_int(x[c], inv * -65536.f, ni, r16[c]);
         } else {
             const uint32_t y = __float_as_uint(
                 __builtin_amdgcn_fmed3f(__builtin_fmaf(x[c], inv, kMagic), kMagic - n, kMagic + n));
@@ -950,8 +978,8 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
             uint32_t r16[8], y[8];
             sr_draws8(A.seed, uint32_t(head), A.t, row0 + m, cg, r16);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) y[c] = sr_level(x[m][c], gi[c], B, r16[c]);
-            store8<B>(gout, boff, y);
+            for (int c = 0; c < 8; ++c) y[c] = sr_field<B>(x[m][c], gi[c], gi[c] * -65536.f, r16[c]);
+            store8<B, true>(gout, boff, y);
         } else {
             pack8<B>(gout, boff, x[m], InvCol{gi});
         }
