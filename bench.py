@@ -71,6 +71,11 @@ WORKLOADS = {
                           extra=dict(bbar=4, bmin=2, bmax=8), kernel="headalloc_step_kernel"),
     "gdn-had-int4": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
                          extra=dict(block=128, int_bits=4), kernel="rot_step_kernel"),
+    # the rotated layouts under Philox stochastic rounding (the tuned rotated-domain kernel)
+    "kda-mixed-sr": dict(cfg=2, kind="mixed", mode="sr", B=256, H=32, per_row=True, layers=7, alloc_every=0,
+                         extra=dict(block=32, k_hi=16), kernel="rot_step_kernel"),
+    "gdn-had-int8-sr": dict(cfg=1, kind="had_int8", mode="sr", B=64, H=16, per_row=False, layers=60,
+                            alloc_every=0, extra=dict(block=128), kernel="rot_step_kernel"),
 }
 PEAK_FP64_MFMA_TFLOPS = 78.6     # the prefill's state path runs on float64 matrix cores
 

@@ -1,6 +1,7 @@
-// Decode write-back step of the Hadamard-rotated layouts, round to nearest: HAD_INT8
-// (every row in the rotated domain, per-block affine INT8) and MIXED (the first k_hi
-// physical rows in float16, the rest Hadamard INT8, rows permuted per head).
+// Decode write-back step of the Hadamard-rotated layouts, round to nearest or stochastic
+// rounding: HAD_INT8 (every row in the rotated domain, per-block affine INT8) and MIXED
+// (the first k_hi physical rows in float16, the rest Hadamard INT8, rows permuted per
+// head).
 // [DAMP] "Implementation" (reconstruct, update, re-quantize, write back), "Key
 // Points" (transform along the value dimension); [LBRS] "Accumulated readout error".
 //
@@ -20,6 +21,9 @@
 //   * the update and the requantization run row-parallel (lane = 4 rows x 16 columns,
 //     so a block of 32 values spans 2 lanes) with float64 element arithmetic and the
 //     block minimum / maximum by DPP;
+//   * stochastic rounding draws each INT8 element's 16-bit uniform from Philox4x32-10
+//     keyed by (physical row, 8-column group, head, token), as every decode kernel does,
+//     and takes floor(t) + [u < frac(t) 2^16] in integer form (one floor of -t 2^16);
 //   * float64 -> float16 goes through float32 rounded to odd, then the hardware
 //     conversion: rounding to odd at 24 bits followed by a rounding to 11 bits gives
 //     the correctly rounded result (Boldo & Melquiond, IEEE Trans. Computers 2008).
@@ -165,7 +169,7 @@ __device__ __forceinline__ void wht128(double& a0, double& a1, int lane) {
     a1 = y * kInvSqrt128;
 }
 
-template <int KHI, int BLOCK, int IB>
+template <int KHI, int BLOCK, int IB, bool SR>
 __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
     using LY = RotLayout<KHI, BLOCK, IB>;
     __shared__ RotSmem<KHI, BLOCK, IB> sm;
@@ -448,15 +452,39 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             const uint16_t zbits = f64_to_f16_bits(mn);
             const double scale = f16_to_f64(sbits), zero = f16_to_f64(zbits);
             uint32_t o4[4] = {0, 0, 0, 0};
+            // stochastic rounding: the 16-bit draws of the lane's two 8-column groups
+            uint32_t r16[16];
+            if constexpr (SR) {
+                sr_draws8(A.seed, uint32_t(head), A.t, p, 2 * cg, r16);
+                sr_draws8(A.seed, uint32_t(head), A.t, p, 2 * cg + 1, r16 + 8);
+            }
             if (scale != 0.0) {
                 // reciprocal of the step refined by one Newton step
                 double inv = __builtin_amdgcn_rcp(scale);
                 inv = fma(fma(-scale, inv, 1.0), inv, inv);
                 const double nz = -zero * inv;
-                // levels t = (y - zero) / scale lie within +-2^30 unless the offset is far
+                // levels t = (y - zero) / scale lie within +-2^30 (+-2^14 under stochastic
+                // rounding, whose integer form holds t 2^16) unless the offset is far
                 // outside the block's range (then the float64 path below is taken)
                 const double span = fmax(fabs(mx - zero), fabs(mn - zero)) * inv;
-                if (span < 1073741824.0) {
+                if (SR && span < 16384.0) {
+                    // floor(t) + [u < frac(t) 2^16] = floor((ceil(t 2^16) + 2^16 - 1 - u) / 2^16)
+                    // for an integer draw u (u < g exactly when u < ceil(g)); t 2^16 is the
+                    // product of the nearest-rounding path scaled by 2^16 (exact), and its
+                    // ceiling is minus the floor of its negation
+                    const double inv16 = inv * 65536.0, nz16 = nz * 65536.0;
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) {
+                        const int zc = int(floor(-fma(y[c], inv16, nz16)));          // -ceil(t 2^16)
+                        int kk = min(max((65535 - zc - int(r16[c])) >> 16, 0), LY::TOP);
+                        // (opaque, so that the shift, clamp and byte packing are not merged
+                        // into v_ashr_pk_u8_i32: with it the upper two bytes of each packed
+                        // word came out with stray bits set)
+                        asm volatile("" : "+v"(kk));
+                        if constexpr (IB == 8) o4[c >> 2] |= uint32_t(kk) << ((c & 3) * 8);
+                        else o4[c >> 3] |= uint32_t(kk) << ((c & 7) * 4);
+                    }
+                } else if (!SR && span < 1073741824.0) {
                     // t + 1.5 * 2^52 rounds t to the nearest integer (ties to even); its
                     // low 32 bits are that integer, clamped to [0, TOP] in integer form
 #pragma unroll
@@ -469,7 +497,15 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                 } else {
 #pragma unroll
                     for (int c = 0; c < 16; ++c) {
-                        const double kf = fmin(fmax(rint((y[c] - zero) / scale), 0.0), double(LY::TOP));
+                        const double t = (y[c] - zero) / scale;
+                        double kf;
+                        if constexpr (SR) {
+                            const double fl = floor(t);
+                            kf = fl + ((double(r16[c]) < (t - fl) * 65536.0) ? 1.0 : 0.0);
+                        } else {
+                            kf = rint(t);
+                        }
+                        kf = fmin(fmax(kf, 0.0), double(LY::TOP));
                         if constexpr (IB == 8) o4[c >> 2] |= uint32_t(kf) << ((c & 3) * 8);
                         else o4[c >> 3] |= uint32_t(kf) << ((c & 7) * 4);
                     }
@@ -489,15 +525,21 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
 
 template <int KHI, int BLOCK>
 hipError_t launch_rot(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
-    if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    const dim3 grid(d.B * d.H), block(NT);
+    if (d.mode == WB_SR) {
+        if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8, true>), grid, block, 0, stream, a);
+    } else {
+        if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4, false>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool rot_step_supported(const wb_layout_desc& d) {
-    if (d.mode != WB_RTN || d.dk != DK || d.dv != DV) return false;
+    if ((d.mode != WB_RTN && d.mode != WB_SR) || d.dk != DK || d.dv != DV) return false;
     if (d.kind == WB_HAD_INT8) return d.block == 32 || d.block == 128;
     if (d.kind == WB_MIXED) return d.k_hi == 16 && d.block == 32;
     return false;

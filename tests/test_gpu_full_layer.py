@@ -1,9 +1,9 @@
 """Every head of a full layer, one teacher-forced decode step, against the oracle.
 
-The mixed layout at B = 256, H = 32 (round to nearest), the decay-aware per-row widths
+The mixed layout at B = 256, H = 32 (round to nearest and stochastic rounding), the decay-aware per-row widths
 at the same shape (round to nearest and Philox stochastic rounding, after an allocation
 pass; under the layer-wise budget; with one-bit rows allowed), the Hadamard INT8 layout
-and its INT4 tier at B = 64, H = 16 with per-head decay and the per-head allocation unit
+(both rules) and its INT4 tier at B = 64, H = 16 with per-head decay and the per-head allocation unit
 at that shape (round to nearest and stochastic rounding), in the launch configurations
 the benchmark times: every head state of the layer is compared, not a
 sample, so that the parity bound (codes bit-equal except at most 1e-4 of the elements,
@@ -44,6 +44,8 @@ CASES = {
     "had-int4-rtn-gdn": dict(kind=L.HAD_INT8, mode="rtn", B=64, H=16, per_row=False, kw=dict(block=128, int_bits=4)),
     "bitalloc-1bit-rtn": dict(kind=L.BITALLOC, mode="rtn", B=256, H=32, per_row=True, kw=dict(bmin=1)),
     "headalloc-sr-gdn": dict(kind=L.HEADALLOC, mode="sr", B=64, H=16, per_row=False, kw={}),
+    "mixed-sr": dict(kind=L.MIXED, mode="sr", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
+    "had-int8-sr-gdn": dict(kind=L.HAD_INT8, mode="sr", B=64, H=16, per_row=False, kw=dict(block=128)),
 }
 
 
