@@ -71,10 +71,15 @@ WORKLOADS = {
                           extra=dict(bbar=4, bmin=2, bmax=8), kernel="headalloc_step_kernel"),
     "gdn-had-int4": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
                          extra=dict(block=128, int_bits=4), kernel="rot_step_kernel"),
-    # the rotated layouts under Philox stochastic rounding (the tuned rotated-domain kernel)
+    # the rotated layouts under Philox stochastic rounding (the tuned rotated-domain kernel) ...
     "kda-mixed-sr": dict(cfg=2, kind="mixed", mode="sr", B=256, H=32, per_row=True, layers=7, alloc_every=0,
                          extra=dict(block=32, k_hi=16), kernel="rot_step_kernel"),
     "gdn-had-int8-sr": dict(cfg=1, kind="had_int8", mode="sr", B=64, H=16, per_row=False, layers=60,
+                            alloc_every=0, extra=dict(block=128), kernel="rot_step_kernel"),
+    # ... and under error feedback (a float32 residual per INT8 element read and written)
+    "kda-mixed-ef": dict(cfg=2, kind="mixed", mode="ef", B=256, H=32, per_row=True, layers=7, alloc_every=0,
+                         extra=dict(block=32, k_hi=16), kernel="rot_step_kernel"),
+    "gdn-had-int8-ef": dict(cfg=1, kind="had_int8", mode="ef", B=64, H=16, per_row=False, layers=60,
                             alloc_every=0, extra=dict(block=128), kernel="rot_step_kernel"),
 }
 PEAK_FP64_MFMA_TFLOPS = 78.6     # the prefill's state path runs on float64 matrix cores
@@ -124,7 +129,9 @@ def algorithmic_bytes_per_head(kind, extra, per_row, online=False, mode="rtn", a
     rd, wr = region_bytes(kind, extra)
     io = 2 * DK * 4 + DV * 4 + 4 + (DK * 4 if per_row else 4) + DV * 4
     est = 2 * (2 * DK * 4 + 4) if online else 0      # estimators read and written
-    side = 2 * 4 * DK * DV if mode in ("ef", "dir", "resq") else 0     # float32 side value per element
+    # float32 side value per element, read and written (not for the float16 rows of MIXED)
+    side_rows = DK - extra.get("k_hi", 0) if kind == "mixed" else DK
+    side = 2 * 4 * side_rows * DV if mode in ("ef", "dir", "resq") else 0
     votes = 2 * DK * DV + 8 * 4 if activity else 0   # vote state read and written, the counters
     return rd + wr + io + est + side + votes
 

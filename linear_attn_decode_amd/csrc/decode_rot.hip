@@ -1,5 +1,5 @@
-// Decode write-back step of the Hadamard-rotated layouts, round to nearest or stochastic
-// rounding: HAD_INT8 (every row in the rotated domain, per-block affine INT8) and MIXED
+// Decode write-back step of the Hadamard-rotated layouts under each write-back rule
+// (round to nearest, stochastic rounding, error feedback): HAD_INT8 (every row in the rotated domain, per-block affine INT8) and MIXED
 // (the first k_hi physical rows in float16, the rest Hadamard INT8, rows permuted per
 // head).
 // [DAMP] "Implementation" (reconstruct, update, re-quantize, write back), "Key
@@ -24,6 +24,9 @@
 //   * stochastic rounding draws each INT8 element's 16-bit uniform from Philox4x32-10
 //     keyed by (physical row, 8-column group, head, token), as every decode kernel does,
 //     and takes floor(t) + [u < frac(t) 2^16] in integer form (one floor of -t 2^16);
+//   * error feedback reads each INT8 element's float32 residual (physical rows, rotated
+//     domain) with the lane's codes, rounds y + e on the grid derived from y, and stores
+//     e' = clip(y + e - q, -step, step) beside the codes; float16 rows have no residual;
 //   * float64 -> float16 goes through float32 rounded to odd, then the hardware
 //     conversion: rounding to odd at 24 bits followed by a rounding to 11 bits gives
 //     the correctly rounded result (Boldo & Melquiond, IEEE Trans. Computers 2008).
@@ -169,8 +172,17 @@ __device__ __forceinline__ void wht128(double& a0, double& a1, int lane) {
     a1 = y * kInvSqrt128;
 }
 
-template <int KHI, int BLOCK, int IB, bool SR>
+// largest |e| of a lane's 16 residuals
+__device__ __forceinline__ float emax16(const float e[16]) {
+    float m = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) m = fmaxf(m, fabsf(e[c]));
+    return m;
+}
+
+template <int KHI, int BLOCK, int IB, int MODE>
 __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
+    constexpr bool SR = MODE == WB_SR, EF = MODE == WB_EF;
     using LY = RotLayout<KHI, BLOCK, IB>;
     __shared__ RotSmem<KHI, BLOCK, IB> sm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -419,6 +431,17 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
             }
             const int qr = p - KHI;
             const int g = (16 * cg) / BLOCK;
+            // error feedback: the residuals of the lane's 16 elements (requested first, so
+            // that their latency overlaps the update)
+            float* eptr = EF ? A.side + ((size_t)head * DK + p) * DV + 16 * cg : nullptr;
+            float e16[16];
+            if constexpr (EF) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 v = reinterpret_cast<const float4*>(eptr)[i];
+                    e16[4 * i] = v.x; e16[4 * i + 1] = v.y; e16[4 * i + 2] = v.z; e16[4 * i + 3] = v.w;
+                }
+            }
             // the lane's 16 codes: 16 bytes, or 8 bytes of nibbles
             uint8_t* cptr = lb + LY::CODE_BASE + (qr * DV + 16 * cg) * IB / 8;
             uint32_t rw[4];
@@ -484,7 +507,20 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                         if constexpr (IB == 8) o4[c >> 2] |= uint32_t(kk) << ((c & 3) * 8);
                         else o4[c >> 3] |= uint32_t(kk) << ((c & 7) * 4);
                     }
-                } else if (!SR && span < 1073741824.0) {
+                } else if (EF && span + double(emax16(e16)) * inv < 1073741824.0) {
+                    // y + e on the grid of y: nearest level as below, then the residual
+                    // y + e - (zero + level scale), clipped to one step, in float32
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) {
+                        const double tc = y[c] + double(e16[c]);
+                        const double r = fma(tc, inv, nz) + 6755399441055744.0;
+                        const int kk = min(max(int(uint32_t(__double_as_longlong(r))), 0), LY::TOP);
+                        const double xh = fma(double(kk), scale, zero);
+                        e16[c] = float(fmin(fmax(tc - xh, -scale), scale));
+                        if constexpr (IB == 8) o4[c >> 2] |= uint32_t(kk) << ((c & 3) * 8);
+                        else o4[c >> 3] |= uint32_t(kk) << ((c & 7) * 4);
+                    }
+                } else if (MODE == WB_RTN && span < 1073741824.0) {
                     // t + 1.5 * 2^52 rounds t to the nearest integer (ties to even); its
                     // low 32 bits are that integer, clamped to [0, TOP] in integer form
 #pragma unroll
@@ -497,7 +533,8 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                 } else {
 #pragma unroll
                     for (int c = 0; c < 16; ++c) {
-                        const double t = (y[c] - zero) / scale;
+                        const double tc = EF ? y[c] + double(e16[c]) : y[c];
+                        const double t = (tc - zero) / scale;
                         double kf;
                         if constexpr (SR) {
                             const double fl = floor(t);
@@ -506,10 +543,21 @@ __global__ void __launch_bounds__(NT) rot_step_kernel(const KArgs A) {
                             kf = rint(t);
                         }
                         kf = fmin(fmax(kf, 0.0), double(LY::TOP));
+                        if constexpr (EF) e16[c] = float(fmin(fmax(tc - (zero + kf * scale), -scale), scale));
                         if constexpr (IB == 8) o4[c >> 2] |= uint32_t(kf) << ((c & 3) * 8);
                         else o4[c >> 3] |= uint32_t(kf) << ((c & 7) * 4);
                     }
                 }
+            }
+            if constexpr (EF) {
+                // a zero step stores level 0 and a zero residual
+                if (scale == 0.0) {
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) e16[c] = 0.f;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    reinterpret_cast<float4*>(eptr)[i] = make_float4(e16[4 * i], e16[4 * i + 1], e16[4 * i + 2], e16[4 * i + 3]);
             }
             // straight to the stored region (nothing reads the staged copy again), so the
             // stores overlap the rest of the update
@@ -527,11 +575,15 @@ template <int KHI, int BLOCK>
 hipError_t launch_rot(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
     const dim3 grid(d.B * d.H), block(NT);
     if (d.mode == WB_SR) {
-        if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8, true>), grid, block, 0, stream, a);
+        if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4, WB_SR>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8, WB_SR>), grid, block, 0, stream, a);
+    } else if (d.mode == WB_EF) {
+        if (a.side == nullptr) return hipErrorInvalidValue;
+        if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4, WB_EF>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8, WB_EF>), grid, block, 0, stream, a);
     } else {
-        if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4, false>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8, false>), grid, block, 0, stream, a);
+        if (d.int_bits == 4) hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 4, WB_RTN>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((rot_step_kernel<KHI, BLOCK, 8, WB_RTN>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -539,7 +591,7 @@ hipError_t launch_rot(const wb_layout_desc& d, const KArgs& a, hipStream_t strea
 }  // namespace
 
 bool rot_step_supported(const wb_layout_desc& d) {
-    if ((d.mode != WB_RTN && d.mode != WB_SR) || d.dk != DK || d.dv != DV) return false;
+    if ((d.mode != WB_RTN && d.mode != WB_SR && d.mode != WB_EF) || d.dk != DK || d.dv != DV) return false;
     if (d.kind == WB_HAD_INT8) return d.block == 32 || d.block == 128;
     if (d.kind == WB_MIXED) return d.k_hi == 16 && d.block == 32;
     return false;

@@ -55,9 +55,9 @@ hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStre
 bool headalloc_step_supported(const wb_layout_desc& d);
 hipError_t launch_headalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
 
-// Decode step of the Hadamard-rotated layouts with round-to-nearest or stochastic
-// rounding (the tuned kernel),
-// for the shapes rot_step_supported() accepts.
+// Decode step of the Hadamard-rotated layouts under round-to-nearest, stochastic
+// rounding or error feedback (the tuned kernel), for the shapes rot_step_supported()
+// accepts.
 bool rot_step_supported(const wb_layout_desc& d);
 hipError_t launch_rot_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream);
 

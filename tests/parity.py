@@ -310,10 +310,14 @@ def check_heads_chunk(args):
     reg_in, reg_out, o = ld("reg_in"), ld("reg_out"), ld("o")
     q, k, v, beta, s = ld("q"), ld("k"), ld("v"), ld("beta"), ld("s")
     perm = ld("perm") if os.path.exists(os.path.join(d, "perm.npy")) else None
+    # error-feedback residuals before and after the step, when the caller saved them
+    e_in = ld("e_in") if os.path.exists(os.path.join(d, "e_in.npy")) else None
+    e_out = ld("e_out") if os.path.exists(os.path.join(d, "e_out.npy")) else None
     H = lay.H
     tally = Tally()
     for idx in range(lo, hi):
         b, h = divmod(idx, H)
-        check_head(lay, reg_in[idx], reg_out[idx], None, None, o[b, h], q[b, h], k[b, h], v[b, h], beta[b, h],
-                   s[b, h], t, b, h, None if perm is None else perm[h], tally)
+        check_head(lay, reg_in[idx], reg_out[idx], None if e_in is None else np.asarray(e_in[b, h]),
+                   None if e_out is None else np.asarray(e_out[b, h]), o[b, h], q[b, h], k[b, h], v[b, h],
+                   beta[b, h], s[b, h], t, b, h, None if perm is None else perm[h], tally)
     return tally

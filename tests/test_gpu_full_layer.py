@@ -1,9 +1,10 @@
 """Every head of a full layer, one teacher-forced decode step, against the oracle.
 
-The mixed layout at B = 256, H = 32 (round to nearest and stochastic rounding), the decay-aware per-row widths
+The mixed layout at B = 256, H = 32 (round to nearest, stochastic rounding and error
+feedback, its residuals compared too), the decay-aware per-row widths
 at the same shape (round to nearest and Philox stochastic rounding, after an allocation
 pass; under the layer-wise budget; with one-bit rows allowed), the Hadamard INT8 layout
-(both rules) and its INT4 tier at B = 64, H = 16 with per-head decay and the per-head allocation unit
+(all three rules) and its INT4 tier at B = 64, H = 16 with per-head decay and the per-head allocation unit
 at that shape (round to nearest and stochastic rounding), in the launch configurations
 the benchmark times: every head state of the layer is compared, not a
 sample, so that the parity bound (codes bit-equal except at most 1e-4 of the elements,
@@ -46,6 +47,8 @@ CASES = {
     "headalloc-sr-gdn": dict(kind=L.HEADALLOC, mode="sr", B=64, H=16, per_row=False, kw={}),
     "mixed-sr": dict(kind=L.MIXED, mode="sr", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
     "had-int8-sr-gdn": dict(kind=L.HAD_INT8, mode="sr", B=64, H=16, per_row=False, kw=dict(block=128)),
+    "mixed-ef": dict(kind=L.MIXED, mode="ef", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
+    "had-int8-ef-gdn": dict(kind=L.HAD_INT8, mode="ef", B=64, H=16, per_row=False, kw=dict(block=128)),
 }
 
 
@@ -74,12 +77,16 @@ def test_full_layer_every_head(case):
     st.step_decode(dev["q"][0], dev["k"][0], dev["v"][0], dev["beta"][0], dev["s"], o, 0)
     torch.cuda.synchronize()
     reg_in = st.regions().cpu().numpy()[:, : L.Layout(**lay_kw).region_size()]
+    e_in = st.residuals().cpu().numpy() if mode == "ef" else None
     st.step_decode(dev["q"][1], dev["k"][1], dev["v"][1], dev["beta"][1], dev["s"], o, 1)
     torch.cuda.synchronize()
     reg_out = st.regions().cpu().numpy()[:, : reg_in.shape[1]]
     with tempfile.TemporaryDirectory(dir="/tmp") as tmp:
         arrays = dict(reg_in=reg_in, reg_out=reg_out, o=o.cpu().numpy(), q=inp["q"][1], k=inp["k"][1],
                       v=inp["v"][1], beta=inp["beta"][1], s=inp["s"])
+        if mode == "ef":
+            arrays["e_in"] = e_in
+            arrays["e_out"] = st.residuals().cpu().numpy()
         if perm is not None:
             arrays["perm"] = perm
         for n, a in arrays.items():
