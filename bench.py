@@ -38,6 +38,9 @@ WORKLOADS = {
     # decay-aware configuration)
     "kda-bitalloc-sr": dict(cfg=3, kind="bitalloc", mode="sr", B=256, H=32, per_row=True, layers=15, alloc_every=64,
                             extra=dict(bbar=4, bmin=2, bmax=8), kernel="bitalloc_step_kernel"),
+    # ... and under error feedback (a float32 residual per element read and written)
+    "kda-bitalloc-ef": dict(cfg=3, kind="bitalloc", mode="ef", B=256, H=32, per_row=True, layers=15, alloc_every=64,
+                            extra=dict(bbar=4, bmin=2, bmax=8), kernel="bitalloc_step_kernel"),
     "kda-mixed": dict(cfg=2, kind="mixed", B=256, H=32, per_row=True, layers=7, alloc_every=0,
                       extra=dict(block=32, k_hi=16), kernel="rot_step_kernel"),
     "gdn-had-int8": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,

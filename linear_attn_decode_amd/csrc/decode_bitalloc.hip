@@ -445,6 +445,62 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Error feedback on a row of step `dl` (1 / dl = `inv`): y + e rounded to the nearest level
+// (magic-number form, as pack8), x-hat = level * dl, and the new residual
+// clip(y + e - x-hat, -step, step) left in e. A one-bit row's levels are -dl, +dl (step
+// 2 dl: the level is 1 exactly where y + e > 0). A zero step gives level 0 and residual 0.
+template <bool OB>
+__device__ __forceinline__ void ef_round8(const float x[8], float e[8], float inv, float dl, int bw, uint32_t y[8]) {
+    if (OB && bw == 1) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float t = x[c] + e[c];
+            const bool k = t * inv > 0.f;
+            y[c] = kMagicBits + uint32_t(k);
+            e[c] = fminf(fmaxf(t - (k ? dl : -dl), -2.f * dl), 2.f * dl);
+        }
+    } else {
+        const float n = float((1 << (bw - 1)) - 1);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float t = x[c] + e[c];
+            const float yf = __builtin_amdgcn_fmed3f(__builtin_fmaf(t, inv, kMagic), kMagic - n, kMagic + n);
+            y[c] = __float_as_uint(yf);
+            e[c] = fminf(fmaxf(t - (yf - kMagic) * dl, -dl), dl);
+        }
+    }
+}
+
+// Pack 8 levels in magic-number form at the row's width: specialised when the lanes share
+// it (bu, a scalar), else per lane (bw).
+template <bool OB>
+__device__ __forceinline__ void store_rows(uint32_t* reg, int boff, int bu, int bw, const uint32_t y[8]) {
+    if (bu != 0) {
+        if (OB && bu == 1) {
+            store8<1>(reg, boff, y);
+            return;
+        }
+        switch (bu) {
+            case 2: store8<2>(reg, boff, y); break;
+            case 3: store8<3>(reg, boff, y); break;
+            case 4: store8<4>(reg, boff, y); break;
+            case 5: store8<5>(reg, boff, y); break;
+            case 6: store8<6>(reg, boff, y); break;
+            case 7: store8<7>(reg, boff, y); break;
+            default: store8<8>(reg, boff, y); break;
+        }
+        return;
+    }
+    const uint32_t base = kMagicBits - uint32_t((OB && bw == 1) ? 0 : (1 << (bw - 1)) - 1);
+    uint64_t fld = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fld |= uint64_t(y[c] - base) << __umul24(uint32_t(c), uint32_t(bw));
+    uint8_t* bytes = reinterpret_cast<uint8_t*>(reg) + uint32_t(boff);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < bw) bytes[i] = uint8_t(fld >> (8 * i));
+}
+
 // Row maxima (non-negative floats as bit patterns) of the 4 rows a lane holds, reduced
 // over the 16 lanes of its DPP row and scattered: lane cg ends with the maximum of row
 // ((cg & 1) << 1) | ((cg >> 1) & 1), the four rows spread over every quad.
@@ -471,11 +527,13 @@ __device__ __forceinline__ float rowsum4_scatter(const float m[4], int cg) {
 
 // EST: fold the token into the attached online estimators; LAYER: the layer-wise budget
 // layout (code area of b_max bits per element, codes in use first, then a zero tail);
-// OB: one-bit rows may occur; SR: stochastic rounding with the Philox draws of the
-// element (row, 8 columns) instead of round to nearest. Each is its own instantiation, so that the plain step
-// carries no trace of the others.
-template <bool EST, bool LAYER, bool OB, bool SR>
-__global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KArgs A) {
+// OB: one-bit rows may occur; RULE: round to nearest, stochastic rounding with the
+// Philox draws of the element (row, 8 columns), or error feedback with the element's
+// float32 residual (physical rows, read and written at the row's rounding). Each is its
+// own instantiation, so that the plain step carries no trace of the others.
+template <bool EST, bool LAYER, bool OB, int RULE>
+__global__ void __launch_bounds__(NT, RULE == WB_RTN ? 8 : 6) bitalloc_step_kernel(const KArgs A) {
+    constexpr bool SR = RULE == WB_SR, EF = RULE == WB_EF;
     __shared__ __align__(16) uint8_t smraw[kSmemBytes];
     BaFixed& sm = *reinterpret_cast<BaFixed*>(smraw + kFixedOffset);
     uint32_t* reg = reinterpret_cast<uint32_t*>(smraw);
@@ -694,6 +752,7 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
                      ((fabsf(x[m][4]) + fabsf(x[m][5])) + (fabsf(x[m][6]) + fabsf(x[m][7])));
     }
     float inv[MR];
+    float dls[MR];                              // error feedback: the rows' steps
     {
         // this lane's row: ms = ((cg & 1) << 1) | ((cg >> 1) & 1)
         const int ms = ((cg & 1) << 1) | ((cg >> 1) & 1);
@@ -718,14 +777,33 @@ __global__ void __launch_bounds__(NT, SR ? 6 : 8) bitalloc_step_kernel(const KAr
         inv[1] = __uint_as_float(dpp_u32<0xAA>(ib));
         inv[2] = __uint_as_float(dpp_u32<0x55>(ib));
         inv[3] = __uint_as_float(dpp_u32<0xFF>(ib));
+        if constexpr (EF) {
+            const uint32_t db = __float_as_uint(dl);
+            dls[0] = __uint_as_float(dpp_u32<0x00>(db));
+            dls[1] = __uint_as_float(dpp_u32<0xAA>(db));
+            dls[2] = __uint_as_float(dpp_u32<0x55>(db));
+            dls[3] = __uint_as_float(dpp_u32<0xFF>(db));
+        }
     }
     // ... then the rounding and packing, specialised per width
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         const TabB* tb = &tbw[NG * m + rq];
-        uint32_t r16[8];
-        if constexpr (SR) sr_draws8(A.seed, uint32_t(head), A.t, int(tb->row), cg, r16);
-        pack_rows<OB, SR>(gout, boff_of(loc_of(m)), bus[m], &tb->bw, x[m], inv[m], r16);
+        if constexpr (EF) {
+            float4* ep = reinterpret_cast<float4*>(A.side + ((size_t)head * DK + tb->row) * DV + 8 * cg);
+            const float4 e0 = ep[0], e1 = ep[1];
+            float e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+            uint32_t y[8];
+            const int bw = int(tb->bw);
+            ef_round8<OB>(x[m], e, inv[m], dls[m], bw, y);
+            ep[0] = make_float4(e[0], e[1], e[2], e[3]);
+            ep[1] = make_float4(e[4], e[5], e[6], e[7]);
+            store_rows<OB>(gout, boff_of(loc_of(m)), bus[m], bw, y);
+        } else {
+            uint32_t r16[8];
+            if constexpr (SR) sr_draws8(A.seed, uint32_t(head), A.t, int(tb->row), cg, r16);
+            pack_rows<OB, SR>(gout, boff_of(loc_of(m)), bus[m], &tb->bw, x[m], inv[m], r16);
+        }
     }
 }
 
@@ -735,9 +813,11 @@ namespace {
 template <bool EST, bool LAYER, bool OB>
 void launch_variant(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
     if (d.mode == WB_SR)
-        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, true>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, WB_SR>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+    else if (d.mode == WB_EF)
+        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, WB_EF>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
     else
-        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, false>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
+        hipLaunchKernelGGL((bitalloc_step_kernel<EST, LAYER, OB, WB_RTN>), dim3(d.B * d.H), dim3(NT), 0, stream, a);
 }
 template <bool EST, bool LAYER>
 void launch_ob(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
@@ -752,8 +832,8 @@ void launch_layer(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool bitalloc_step_supported(const wb_layout_desc& d) {
-    return d.dk == DK && d.dv == DV && (d.mode == WB_RTN || d.mode == WB_SR) && d.bmin >= 1 && d.bmax <= 8 &&
-           (d.budget == WB_BUDGET_HEAD || d.budget == WB_BUDGET_LAYER);
+    return d.dk == DK && d.dv == DV && (d.mode == WB_RTN || d.mode == WB_SR || d.mode == WB_EF) && d.bmin >= 1 &&
+           d.bmax <= 8 && (d.budget == WB_BUDGET_HEAD || d.budget == WB_BUDGET_LAYER);
 }
 
 // ---------------------------------------------------------------------------
@@ -1023,6 +1103,7 @@ hipError_t launch_bitalloc_step(const wb_layout_desc& d, const KArgs& a, hipStre
     // b_max), Delta and the width / fit bytes
     const size_t code_area = size_t(a.layer ? a.code_cap : DK * DV * d.bbar / 8);
     if (code_area > size_t(kCodeAreaMax)) return hipErrorInvalidValue;
+    if (d.mode == WB_EF && a.side == nullptr) return hipErrorInvalidValue;
     if (a.est) launch_layer<true>(d, a, stream);
     else launch_layer<false>(d, a, stream);
     return hipGetLastError();

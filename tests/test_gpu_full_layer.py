@@ -2,8 +2,8 @@
 
 The mixed layout at B = 256, H = 32 (round to nearest, stochastic rounding and error
 feedback, its residuals compared too), the decay-aware per-row widths
-at the same shape (round to nearest and Philox stochastic rounding, after an allocation
-pass; under the layer-wise budget; with one-bit rows allowed), the Hadamard INT8 layout
+at the same shape (round to nearest, Philox stochastic rounding and error feedback, after
+an allocation pass; under the layer-wise budget; with one-bit rows allowed), the Hadamard INT8 layout
 (all three rules) and its INT4 tier at B = 64, H = 16 with per-head decay and the per-head allocation unit
 at that shape (round to nearest and stochastic rounding), in the launch configurations
 the benchmark times: every head state of the layer is compared, not a
@@ -47,6 +47,7 @@ CASES = {
     "headalloc-sr-gdn": dict(kind=L.HEADALLOC, mode="sr", B=64, H=16, per_row=False, kw={}),
     "mixed-sr": dict(kind=L.MIXED, mode="sr", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
     "had-int8-sr-gdn": dict(kind=L.HAD_INT8, mode="sr", B=64, H=16, per_row=False, kw=dict(block=128)),
+    "bitalloc-ef": dict(kind=L.BITALLOC, mode="ef", B=256, H=32, per_row=True, kw={}),
     "mixed-ef": dict(kind=L.MIXED, mode="ef", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
     "had-int8-ef-gdn": dict(kind=L.HAD_INT8, mode="ef", B=64, H=16, per_row=False, kw=dict(block=128)),
 }

@@ -247,7 +247,7 @@ def _width_patterns(rng, lay, n):
 
 
 @pytest.mark.parametrize("budget,bmin", [("head", 2), ("head", 1), ("layer", 2), ("layer", 1)])
-@pytest.mark.parametrize("mode", ["rtn", "sr"])
+@pytest.mark.parametrize("mode", ["rtn", "sr", "ef"])
 def test_bitalloc_decode_arbitrary_widths(budget, bmin, mode):
     """Decode steps from regions written by the oracle's encoder with arbitrary row widths
     (every width next to every other, heads at the narrowest and widest totals under the
