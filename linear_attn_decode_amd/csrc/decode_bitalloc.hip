@@ -753,6 +753,17 @@ __global__ void __launch_bounds__(NT, RULE == WB_RTN ? 8 : 6) bitalloc_step_kern
     }
     float inv[MR];
     float dls[MR];                              // error feedback: the rows' steps
+    // error feedback: the residuals of the lane's rows, one row ahead of their rounding
+    // (the first requested before the steps are derived, so that its latency overlaps it)
+    auto eptr_of = [&](int m) {
+        return reinterpret_cast<float4*>(A.side + ((size_t)head * DK + tbw[NG * m + rq].row) * DV + 8 * cg);
+    };
+    float4 epre[2];
+    if constexpr (EF) {
+        const float4* ep = eptr_of(0);
+        epre[0] = ep[0];
+        epre[1] = ep[1];
+    }
     {
         // this lane's row: ms = ((cg & 1) << 1) | ((cg >> 1) & 1)
         const int ms = ((cg & 1) << 1) | ((cg >> 1) & 1);
@@ -790,8 +801,13 @@ __global__ void __launch_bounds__(NT, RULE == WB_RTN ? 8 : 6) bitalloc_step_kern
     for (int m = 0; m < MR; ++m) {
         const TabB* tb = &tbw[NG * m + rq];
         if constexpr (EF) {
-            float4* ep = reinterpret_cast<float4*>(A.side + ((size_t)head * DK + tb->row) * DV + 8 * cg);
-            const float4 e0 = ep[0], e1 = ep[1];
+            float4* ep = eptr_of(m);
+            const float4 e0 = epre[0], e1 = epre[1];
+            if (m + 1 < MR) {
+                const float4* en = eptr_of(m + 1);
+                epre[0] = en[0];
+                epre[1] = en[1];
+            }
             float e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
             uint32_t y[8];
             const int bw = int(tb->bw);
