@@ -72,6 +72,8 @@ WORKLOADS = {
                               extra=dict(bbar=4, bmin=1, bmax=8), kernel="bitalloc_step_kernel"),
     "gdn-headalloc": dict(cfg=1, kind="headalloc", B=64, H=16, per_row=False, layers=60, alloc_every=64,
                           extra=dict(bbar=4, bmin=2, bmax=8), kernel="headalloc_step_kernel"),
+    "gdn-headalloc-ef": dict(cfg=1, kind="headalloc", mode="ef", B=64, H=16, per_row=False, layers=60, alloc_every=64,
+                             extra=dict(bbar=4, bmin=2, bmax=8), kernel="headalloc_step_kernel"),
     "gdn-had-int4": dict(cfg=1, kind="had_int8", B=64, H=16, per_row=False, layers=60, alloc_every=0,
                          extra=dict(block=128, int_bits=4), kernel="rot_step_kernel"),
     # the rotated layouts under Philox stochastic rounding (the tuned rotated-domain kernel) ...

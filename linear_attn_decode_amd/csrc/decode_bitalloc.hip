@@ -854,7 +854,7 @@ bool bitalloc_step_supported(const wb_layout_desc& d) {
 
 // ---------------------------------------------------------------------------
 // Decode write-back step of the per-head allocation unit (HEADALLOC) with round to
-// nearest or stochastic rounding ([LBRS] "Allocation units"): one width b for the whole head, and a float16 step
+// nearest, stochastic rounding or error feedback ([LBRS] "Allocation units"): one width b for the whole head, and a float16 step
 // per group of 32 key rows and value column with its own fit index. Four wavefronts per
 // head, one per row group: lane (cg, rq) of wavefront g holds rows 32 g + 8 rq .. + 7 and
 // columns 8 cg .. 8 cg + 7, so a column's group maximum is the maximum over the lane's 8
@@ -879,8 +879,9 @@ struct HaSmem {
     alignas(16) uint32_t reg[kHaCodeMax / 4 + 4];   // staged codes (+16 bytes a row's 3-word read may touch)
 };
 
-template <int B, bool SR>
+template <int B, int RULE>
 __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
+    constexpr bool SR = RULE == WB_SR, EF = RULE == WB_EF;
     constexpr int n = (1 << (B - 1)) - 1;
     constexpr int NVEC = DK * DV * B / 8 / 16;           // 16-byte vectors of codes in use
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1052,6 +1053,9 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
             float r = __builtin_amdgcn_rcpf(dl);
             r = __builtin_fmaf(__builtin_fmaf(-dl, r, 1.f), r, r);
             sm.ginv[t] = dl > 0.f ? r : 0.f;
+            // error feedback: the new step itself, in the slot of the stored one (read
+            // only by the unpack, before the partial-sum barrier)
+            if constexpr (EF) sm.g[t].x = dl;
             dnew[t] = uint16_t(dbits);
         }
     }
@@ -1066,10 +1070,33 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
         gi[0] = i0.x; gi[1] = i0.y; gi[2] = i0.z; gi[3] = i0.w;
         gi[4] = i1.x; gi[5] = i1.y; gi[6] = i1.z; gi[7] = i1.w;
     }
+    float gdl[8];
+    if constexpr (EF) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) gdl[c] = sm.g[wave * DV + 8 * cg + c].x;
+    }
 #pragma unroll
     for (int m = 0; m < HMR; ++m) {
         const int boff = (row0 + m) * (DV / 8) * B + cg * B;
-        if constexpr (SR) {
+        if constexpr (EF) {
+            // error feedback: y + e to the nearest level of the column's grid, the residual
+            // y + e - level Delta clipped to one step (a zero step: level 0, residual 0)
+            float4* ep = reinterpret_cast<float4*>(A.side + ((size_t)head * DK + row0 + m) * DV + 8 * cg);
+            const float4 e0 = ep[0], e1 = ep[1];
+            float e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+            uint32_t y[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float t = x[m][c] + e[c];
+                const float yf = __builtin_amdgcn_fmed3f(__builtin_fmaf(t, gi[c], kMagic), kMagic - float(n),
+                                                         kMagic + float(n));
+                y[c] = __float_as_uint(yf);
+                e[c] = fminf(fmaxf(t - (yf - kMagic) * gdl[c], -gdl[c]), gdl[c]);
+            }
+            ep[0] = make_float4(e[0], e[1], e[2], e[3]);
+            ep[1] = make_float4(e[4], e[5], e[6], e[7]);
+            store8<B>(gout, boff, y);
+        } else if constexpr (SR) {
             // stochastic rounding with the element's Philox draws (row, column group)
             uint32_t r16[8], y[8];
             sr_draws8(A.seed, uint32_t(head), A.t, row0 + m, cg, r16);
@@ -1083,7 +1110,7 @@ __device__ __forceinline__ void headalloc_body(const KArgs& A, HaSmem& sm) {
     // (the fit bytes and the width byte are unchanged)
 }
 
-template <bool SR>
+template <int RULE>
 __global__ void __launch_bounds__(HNT) headalloc_step_kernel(const KArgs A) {
     __shared__ HaSmem sm;
     const uint8_t* region = A.state + (size_t)blockIdx.x * A.region_stride;
@@ -1091,26 +1118,29 @@ __global__ void __launch_bounds__(HNT) headalloc_step_kernel(const KArgs A) {
     int b = int(region[A.code_cap + 3 * HGR * DV]) + 1;
     b = __builtin_amdgcn_readfirstlane(min(max(b, 2), A.code_cap / (DK * DV / 8)));
     switch (b) {
-        case 2: headalloc_body<2, SR>(A, sm); break;
-        case 3: headalloc_body<3, SR>(A, sm); break;
-        case 4: headalloc_body<4, SR>(A, sm); break;
-        case 5: headalloc_body<5, SR>(A, sm); break;
-        case 6: headalloc_body<6, SR>(A, sm); break;
-        case 7: headalloc_body<7, SR>(A, sm); break;
-        default: headalloc_body<8, SR>(A, sm); break;
+        case 2: headalloc_body<2, RULE>(A, sm); break;
+        case 3: headalloc_body<3, RULE>(A, sm); break;
+        case 4: headalloc_body<4, RULE>(A, sm); break;
+        case 5: headalloc_body<5, RULE>(A, sm); break;
+        case 6: headalloc_body<6, RULE>(A, sm); break;
+        case 7: headalloc_body<7, RULE>(A, sm); break;
+        default: headalloc_body<8, RULE>(A, sm); break;
     }
 }
 
 }  // namespace
 
 bool headalloc_step_supported(const wb_layout_desc& d) {
-    return d.kind == WB_HEADALLOC && d.dk == DK && d.dv == DV && (d.mode == WB_RTN || d.mode == WB_SR) &&
-           d.bmax <= 8;
+    return d.kind == WB_HEADALLOC && d.dk == DK && d.dv == DV &&
+           (d.mode == WB_RTN || d.mode == WB_SR || d.mode == WB_EF) && d.bmax <= 8;
 }
 
 hipError_t launch_headalloc_step(const wb_layout_desc& d, const KArgs& a, hipStream_t stream) {
-    if (d.mode == WB_SR) hipLaunchKernelGGL(headalloc_step_kernel<true>, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
-    else hipLaunchKernelGGL(headalloc_step_kernel<false>, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
+    if (d.mode == WB_SR) hipLaunchKernelGGL(headalloc_step_kernel<WB_SR>, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
+    else if (d.mode == WB_EF) {
+        if (a.side == nullptr) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(headalloc_step_kernel<WB_EF>, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
+    } else hipLaunchKernelGGL(headalloc_step_kernel<WB_RTN>, dim3(d.B * d.H), dim3(HNT), 0, stream, a);
     return hipGetLastError();
 }
 

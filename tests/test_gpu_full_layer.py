@@ -5,7 +5,7 @@ feedback, its residuals compared too), the decay-aware per-row widths
 at the same shape (round to nearest, Philox stochastic rounding and error feedback, after
 an allocation pass; under the layer-wise budget; with one-bit rows allowed), the Hadamard INT8 layout
 (all three rules) and its INT4 tier at B = 64, H = 16 with per-head decay and the per-head allocation unit
-at that shape (round to nearest and stochastic rounding), in the launch configurations
+at that shape (all three rules), in the launch configurations
 the benchmark times: every head state of the layer is compared, not a
 sample, so that the parity bound (codes bit-equal except at most 1e-4 of the elements,
 each one step apart and within 1e-5 of a step of the boundary; outputs within 1e-4
@@ -48,6 +48,7 @@ CASES = {
     "mixed-sr": dict(kind=L.MIXED, mode="sr", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
     "had-int8-sr-gdn": dict(kind=L.HAD_INT8, mode="sr", B=64, H=16, per_row=False, kw=dict(block=128)),
     "bitalloc-ef": dict(kind=L.BITALLOC, mode="ef", B=256, H=32, per_row=True, kw={}),
+    "headalloc-ef-gdn": dict(kind=L.HEADALLOC, mode="ef", B=64, H=16, per_row=False, kw={}),
     "mixed-ef": dict(kind=L.MIXED, mode="ef", B=256, H=32, per_row=True, kw=dict(block=32, k_hi=16)),
     "had-int8-ef-gdn": dict(kind=L.HAD_INT8, mode="ef", B=64, H=16, per_row=False, kw=dict(block=128)),
 }

@@ -271,7 +271,7 @@ def test_bitalloc_decode_arbitrary_widths(budget, bmin, mode):
 
 
 @pytest.mark.parametrize("per_row", [False, True])
-@pytest.mark.parametrize("mode", ["rtn", "sr"])
+@pytest.mark.parametrize("mode", ["rtn", "sr", "ef"])
 def test_headalloc_decode_arbitrary_widths(mode, per_row):
     """Decode steps of the per-head unit from regions written by the oracle's encoder:
     every width from 2 to 8 among the heads, random levels, fit indices and group steps
